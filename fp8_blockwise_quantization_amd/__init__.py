@@ -1,0 +1,29 @@
+"""MI355X (gfx950) FP8 blockwise-quantized W8A8 linear layer.
+
+Python face of ``libfp8rl.so``: 128x128 weight re-quantization, 1x128 per-token activation
+quantization, the blockwise-scaled FP8 GEMM and its grouped-expert (MoE) form. Tensors live on
+the GPU; the functions only marshal arguments into the C ABI (include/fp8rl.h).
+"""
+
+from ._lib import (  # noqa: F401
+    EXPORTED,
+    FP8RL_OP_GEMM,
+    FP8RL_OP_GROUPED_GEMM,
+    FP8RL_OUT_BF16,
+    FP8RL_OUT_F32,
+    Fp8rlError,
+    fp8rl_encode_e4m3_f32,
+    fp8rl_gemm_w8a8_blockscaled,
+    fp8rl_grouped_gemm_w8a8,
+    fp8rl_quant_act_tok128,
+    fp8rl_quant_weight_blk128,
+    fp8rl_workspace_bytes,
+    lib,
+)
+
+# Short aliases.
+quant_weight = fp8rl_quant_weight_blk128
+quant_act = fp8rl_quant_act_tok128
+gemm = fp8rl_gemm_w8a8_blockscaled
+grouped_gemm = fp8rl_grouped_gemm_w8a8
+encode_e4m3 = fp8rl_encode_e4m3_f32

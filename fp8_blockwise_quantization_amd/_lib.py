@@ -1,0 +1,227 @@
+"""ctypes binding of ``libfp8rl.so`` (the C ABI declared in include/fp8rl.h).
+
+Argument marshalling only: every function here checks that the tensors are what the C call
+expects (device, dtype, row-major with unit column stride), passes raw device pointers, row
+pitches and the current HIP stream, and turns a non-zero status into ``Fp8rlError``. All of the
+arithmetic runs in the library's HIP kernels. There is no fallback: if the library is missing or
+cannot be loaded, every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+from .build import LIB_PATH
+
+FP8RL_OUT_BF16 = 0
+FP8RL_OUT_F32 = 1
+FP8RL_OP_GEMM = 0
+FP8RL_OP_GROUPED_GEMM = 1
+
+_lock = threading.Lock()
+_lib = None
+
+
+class Fp8rlError(RuntimeError):
+    def __init__(self, status: int, func: str):
+        self.status = status
+        msg = lib().fp8rl_status_string(status).decode() if _lib is not None else str(status)
+        super().__init__(f"{func} failed with status {status}: {msg}")
+
+
+def lib() -> ctypes.CDLL:
+    """Load the HIP library (once). Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m fp8_blockwise_quantization_amd.build`"
+            )
+        L = ctypes.CDLL(LIB_PATH)
+        i64, vp, i32, sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        sig = {
+            "fp8rl_encode_e4m3_f32": (ctypes.c_int, [vp, i64, vp, vp]),
+            "fp8rl_quant_weight_blk128": (ctypes.c_int, [vp, i64, i64, i64, vp, i64, vp, vp]),
+            "fp8rl_quant_act_tok128": (ctypes.c_int, [vp, i64, i64, i64, vp, i64, vp, vp]),
+            "fp8rl_gemm_w8a8_blockscaled": (
+                ctypes.c_int, [vp, vp, vp, vp, i64, i64, i64, vp, ctypes.c_int, i64, vp, sz, vp]),
+            "fp8rl_grouped_gemm_w8a8": (
+                ctypes.c_int, [vp, vp, vp, vp, vp, i32, i64, i64, i64, vp, ctypes.c_int, vp, sz, vp]),
+            "fp8rl_workspace_bytes": (sz, [ctypes.c_int, i64, i64, i64, i32]),
+            "fp8rl_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+            "fp8rl_version": (ctypes.c_int, []),
+        }
+        for name, (res, args) in sig.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+        return L
+
+
+EXPORTED = (
+    "fp8rl_encode_e4m3_f32",
+    "fp8rl_quant_weight_blk128",
+    "fp8rl_quant_act_tok128",
+    "fp8rl_gemm_w8a8_blockscaled",
+    "fp8rl_grouped_gemm_w8a8",
+    "fp8rl_workspace_bytes",
+    "fp8rl_status_string",
+    "fp8rl_version",
+)
+
+
+def _check(status: int, func: str) -> None:
+    if status != 0:
+        raise Fp8rlError(status, func)
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _rows(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: int = 2):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device (cuda) tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must be {ndim}-D")
+    if t.stride(-1) != 1 and t.shape[-1] > 1:
+        raise ValueError(f"{name} must have unit stride along its last dimension")
+    return t.stride(-2) if ndim >= 2 else t.numel()
+
+
+def _dense(t: torch.Tensor, name: str, dtype: torch.dtype):
+    if not t.is_cuda or t.dtype != dtype or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous cuda {dtype} tensor")
+
+
+# ---------------------------------------------------------------------------------------------
+# One Python function per C entry point, same name, tensors in place of pointers.
+# ---------------------------------------------------------------------------------------------
+
+
+def fp8rl_encode_e4m3_f32(v: torch.Tensor, out: torch.Tensor | None = None, stream=None):
+    _dense(v, "v", torch.float32)
+    if out is None:
+        out = torch.empty(v.shape, dtype=torch.uint8, device=v.device)
+    _dense(out, "out", torch.uint8)
+    _check(lib().fp8rl_encode_e4m3_f32(_ptr(v), v.numel(), _ptr(out), _stream(stream)),
+           "fp8rl_encode_e4m3_f32")
+    return out
+
+
+def fp8rl_quant_weight_blk128(w: torch.Tensor, wq: torch.Tensor | None = None,
+                              sw: torch.Tensor | None = None, stream=None):
+    """bf16 W[N][K] -> (Wq uint8 [N][K], sw float32 [N/128][K/128])."""
+    ld_w = _rows(w, "w", torch.bfloat16)
+    N, K = w.shape
+    if wq is None:
+        wq = torch.empty((N, K), dtype=torch.uint8, device=w.device)
+    if sw is None:
+        sw = torch.empty((N // 128, K // 128), dtype=torch.float32, device=w.device)
+    ld_wq = _rows(wq, "wq", torch.uint8)
+    _dense(sw, "sw", torch.float32)
+    if tuple(wq.shape) != (N, K) or sw.numel() != (N // 128) * (K // 128):
+        raise ValueError("output shapes do not match the weight")
+    _check(lib().fp8rl_quant_weight_blk128(_ptr(w), N, K, ld_w, _ptr(wq), ld_wq, _ptr(sw),
+                                           _stream(stream)), "fp8rl_quant_weight_blk128")
+    return wq, sw
+
+
+def fp8rl_quant_act_tok128(x: torch.Tensor, xq: torch.Tensor | None = None,
+                           sa: torch.Tensor | None = None, stream=None):
+    """bf16 X[M][K] -> (Xq uint8 [M][K], sa float32 [M][K/128])."""
+    ld_x = _rows(x, "x", torch.bfloat16)
+    M, K = x.shape
+    if xq is None:
+        xq = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    if sa is None:
+        sa = torch.empty((M, K // 128), dtype=torch.float32, device=x.device)
+    ld_xq = _rows(xq, "xq", torch.uint8)
+    _dense(sa, "sa", torch.float32)
+    if tuple(xq.shape) != (M, K) or sa.numel() != M * (K // 128):
+        raise ValueError("output shapes do not match the activation")
+    _check(lib().fp8rl_quant_act_tok128(_ptr(x), M, K, ld_x, _ptr(xq), ld_xq, _ptr(sa),
+                                        _stream(stream)), "fp8rl_quant_act_tok128")
+    return xq, sa
+
+
+def fp8rl_workspace_bytes(op: int, M: int, N: int, K: int, E: int = 0) -> int:
+    return int(lib().fp8rl_workspace_bytes(op, M, N, K, E))
+
+
+def _out_code(dtype) -> int:
+    if dtype == torch.bfloat16:
+        return FP8RL_OUT_BF16
+    if dtype == torch.float32:
+        return FP8RL_OUT_F32
+    raise TypeError("output dtype must be torch.bfloat16 or torch.float32")
+
+
+def fp8rl_gemm_w8a8_blockscaled(xq, sa, wq, sw, out_dtype=torch.bfloat16, y=None,
+                                workspace=None, stream=None):
+    """Y[M][N] = blockscaled Xq Wq^T (bf16 or float32)."""
+    _dense(xq, "xq", torch.uint8)
+    _dense(wq, "wq", torch.uint8)
+    _dense(sa, "sa", torch.float32)
+    _dense(sw, "sw", torch.float32)
+    M, K = xq.shape
+    N = wq.shape[0]
+    if wq.shape[1] != K:
+        raise ValueError("K mismatch between xq and wq")
+    if y is None:
+        y = torch.empty((M, N), dtype=out_dtype, device=xq.device)
+    ld_y = _rows(y, "y", y.dtype)
+    need = fp8rl_workspace_bytes(FP8RL_OP_GEMM, M, N, K)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=xq.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().fp8rl_gemm_w8a8_blockscaled(_ptr(xq), _ptr(sa), _ptr(wq), _ptr(sw), M, N, K,
+                                             _ptr(y), _out_code(y.dtype), ld_y, _ptr(workspace),
+                                             ws_bytes, _stream(stream)),
+           "fp8rl_gemm_w8a8_blockscaled")
+    return y
+
+
+def fp8rl_grouped_gemm_w8a8(xq, sa, wq, sw, expert_offsets, out_dtype=torch.bfloat16, y=None,
+                            workspace=None, stream=None):
+    """Per-expert blockscaled GEMM over row segments given by device int32 ``expert_offsets``."""
+    _dense(xq, "xq", torch.uint8)
+    _dense(wq, "wq", torch.uint8)
+    _dense(sa, "sa", torch.float32)
+    _dense(sw, "sw", torch.float32)
+    _dense(expert_offsets, "expert_offsets", torch.int32)
+    M, K = xq.shape
+    E, N, K2 = wq.shape
+    if K2 != K or expert_offsets.numel() != E + 1:
+        raise ValueError("shape mismatch between xq, wq and expert_offsets")
+    if y is None:
+        y = torch.empty((M, N), dtype=out_dtype, device=xq.device)
+    _dense(y, "y", y.dtype)
+    need = fp8rl_workspace_bytes(FP8RL_OP_GROUPED_GEMM, M, N, K, E)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=xq.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().fp8rl_grouped_gemm_w8a8(_ptr(xq), _ptr(sa), _ptr(wq), _ptr(sw),
+                                         _ptr(expert_offsets), E, M, N, K, _ptr(y),
+                                         _out_code(y.dtype), _ptr(workspace), ws_bytes,
+                                         _stream(stream)), "fp8rl_grouped_gemm_w8a8")
+    return y

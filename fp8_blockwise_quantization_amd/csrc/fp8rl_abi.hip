@@ -1,0 +1,135 @@
+// C ABI entry points: argument validation (host only, before any HIP call) and dispatch.
+#include <stdint.h>
+
+#include "../../include/fp8rl.h"
+#include "launch.hpp"
+
+namespace {
+
+constexpr int64_t kMaxDim = (int64_t{1} << 31) - 1;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? FP8RL_OK : FP8RL_ERR_HIP; }
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+int check_dims(int64_t a, int64_t b, int64_t c) {
+  if (a < 0 || b < 0 || c < 0) return FP8RL_ERR_SHAPE;
+  if (a > kMaxDim || b > kMaxDim || c > kMaxDim) return FP8RL_ERR_SHAPE;
+  return FP8RL_OK;
+}
+
+// Shared checks of the dense and grouped GEMMs' operands.
+int check_gemm_common(const uint8_t* xq, const float* sa, const uint8_t* wq, const float* sw,
+                      int64_t N, int64_t K, const void* y, int y_dtype, int64_t ld_y) {
+  if (!xq || !sa || !wq || !sw || !y) return FP8RL_ERR_NULL;
+  if (N == 0 || K == 0 || N % 128 || K % 128) return FP8RL_ERR_SHAPE;
+  if (y_dtype != FP8RL_OUT_BF16 && y_dtype != FP8RL_OUT_F32) return FP8RL_ERR_DTYPE;
+  if (ld_y < N) return FP8RL_ERR_SHAPE;
+  const int64_t ybytes = y_dtype == FP8RL_OUT_F32 ? 4 : 2;
+  if (!aligned(xq, 16) || !aligned(wq, 16) || !aligned(y, 16) || !aligned(sa, 4) ||
+      !aligned(sw, 4) || (ld_y * ybytes) % 16)
+    return FP8RL_ERR_ALIGN;
+  return FP8RL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fp8rl_version(void) { return 100; }  // 0.1.0
+
+const char* fp8rl_status_string(int s) {
+  switch (s) {
+    case FP8RL_OK: return "ok";
+    case FP8RL_ERR_NULL: return "a required pointer is NULL";
+    case FP8RL_ERR_SHAPE: return "invalid shape (negative, too large, or not a multiple of 128)";
+    case FP8RL_ERR_ALIGN: return "pointer or row pitch not aligned as required";
+    case FP8RL_ERR_DTYPE: return "unknown output dtype";
+    case FP8RL_ERR_WORKSPACE: return "workspace too small";
+    case FP8RL_ERR_HIP: return "HIP kernel launch failed";
+    case FP8RL_ERR_ARG: return "invalid argument";
+    default: return "unknown status";
+  }
+}
+
+int fp8rl_encode_e4m3_f32(const float* v, int64_t n, uint8_t* out, void* stream) {
+  if (n < 0 || n > (int64_t{1} << 33)) return FP8RL_ERR_SHAPE;
+  if (n == 0) return FP8RL_OK;
+  if (!v || !out) return FP8RL_ERR_NULL;
+  if (!aligned(v, 16) || !aligned(out, 16)) return FP8RL_ERR_ALIGN;
+  return hip_status(fp8rl::launch_encode(v, n, out, as_stream(stream)));
+}
+
+int fp8rl_quant_weight_blk128(const uint16_t* w, int64_t N, int64_t K, int64_t ld_w, uint8_t* wq,
+                              int64_t ld_wq, float* sw, void* stream) {
+  if (int s = check_dims(N, K, 0)) return s;
+  if (N == 0 || K == 0) return FP8RL_OK;
+  if (!w || !wq || !sw) return FP8RL_ERR_NULL;
+  if (N % 128 || K % 128 || ld_w < K || ld_wq < K) return FP8RL_ERR_SHAPE;
+  if ((N / 128) * (K / 128) >= (int64_t{1} << 24)) return FP8RL_ERR_SHAPE;  // grid limit
+  if (!aligned(w, 16) || !aligned(wq, 16) || !aligned(sw, 4) || (ld_w * 2) % 16 || ld_wq % 16)
+    return FP8RL_ERR_ALIGN;
+  return hip_status(fp8rl::launch_quant_weight(w, N, K, ld_w, wq, ld_wq, sw, as_stream(stream)));
+}
+
+int fp8rl_quant_act_tok128(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x, uint8_t* xq,
+                           int64_t ld_xq, float* sa, void* stream) {
+  if (int s = check_dims(M, K, 0)) return s;
+  if (M == 0 || K == 0) return FP8RL_OK;
+  if (!x || !xq || !sa) return FP8RL_ERR_NULL;
+  if (K % 128 || ld_x < K || ld_xq < K) return FP8RL_ERR_SHAPE;
+  if (M * (K / 128) >= (int64_t{1} << 30)) return FP8RL_ERR_SHAPE;  // grid limit
+  if (!aligned(x, 16) || !aligned(xq, 16) || !aligned(sa, 4) || (ld_x * 2) % 16 || ld_xq % 16)
+    return FP8RL_ERR_ALIGN;
+  return hip_status(fp8rl::launch_quant_act(x, M, K, ld_x, xq, ld_xq, sa, as_stream(stream)));
+}
+
+size_t fp8rl_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int32_t E) {
+  if (M <= 0 || N <= 0 || K <= 0 || N % 128 || K % 128) return 0;
+  if (op == FP8RL_OP_GEMM) return fp8rl::plan_gemm(M, N, K).workspace_bytes;
+  if (op == FP8RL_OP_GROUPED_GEMM) return fp8rl::plan_grouped_gemm(M, N, K, E).workspace_bytes;
+  return 0;
+}
+
+int fp8rl_gemm_w8a8_blockscaled(const uint8_t* xq, const float* sa, const uint8_t* wq,
+                                const float* sw, int64_t M, int64_t N, int64_t K, void* y,
+                                int y_dtype, int64_t ld_y, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  if (int s = check_dims(M, N, K)) return s;
+  if (M == 0) return FP8RL_OK;
+  if (int s = check_gemm_common(xq, sa, wq, sw, N, K, y, y_dtype, ld_y)) return s;
+  if (((M + 127) / 128) * (N / 64) >= (int64_t{1} << 22)) return FP8RL_ERR_SHAPE;  // grid limit
+  const fp8rl::GemmPlan plan = fp8rl::plan_gemm(M, N, K);
+  if (plan.workspace_bytes > 0) {
+    if (!workspace || workspace_bytes < plan.workspace_bytes) return FP8RL_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return FP8RL_ERR_ALIGN;
+  }
+  return hip_status(fp8rl::launch_gemm(xq, sa, wq, sw, M, N, K, y, y_dtype == FP8RL_OUT_F32, ld_y,
+                                       workspace, plan, as_stream(stream)));
+}
+
+int fp8rl_grouped_gemm_w8a8(const uint8_t* xq, const float* sa, const uint8_t* wq, const float* sw,
+                            const int32_t* expert_offsets, int32_t E, int64_t M_total, int64_t N,
+                            int64_t K, void* y, int y_dtype, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  if (int s = check_dims(M_total, N, K)) return s;
+  if (E < 1 || E > 1024) return FP8RL_ERR_ARG;
+  if (M_total == 0) return FP8RL_OK;
+  if (!expert_offsets) return FP8RL_ERR_NULL;
+  if (int s = check_gemm_common(xq, sa, wq, sw, N, K, y, y_dtype, N)) return s;
+  if (!aligned(expert_offsets, 4)) return FP8RL_ERR_ALIGN;
+  if (((M_total + 127) / 128 + E) * (N / 128) >= (int64_t{1} << 22)) return FP8RL_ERR_SHAPE;
+  if ((int64_t)E * N * K >= (int64_t{1} << 40)) return FP8RL_ERR_SHAPE;
+  const fp8rl::GemmPlan plan = fp8rl::plan_grouped_gemm(M_total, N, K, E);
+  if (plan.workspace_bytes > 0) {
+    if (!workspace || workspace_bytes < plan.workspace_bytes) return FP8RL_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return FP8RL_ERR_ALIGN;
+  }
+  return hip_status(fp8rl::launch_grouped_gemm(xq, sa, wq, sw, expert_offsets, E, M_total, N, K, y,
+                                               y_dtype == FP8RL_OUT_F32, workspace, plan,
+                                               as_stream(stream)));
+}
+
+}  // extern "C"

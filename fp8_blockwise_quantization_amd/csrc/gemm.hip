@@ -1,0 +1,482 @@
+// Blockwise-scaled W8A8 GEMM and its grouped (MoE) form on gfx950 FP8 matrix cores.
+//
+//   Y[m][n] = sum_kb sa[m][kb] * sw[n/128][kb] * P_kb[m][n],
+//   P_kb[m][n] = sum over the 128 k of slice kb of dec(Xq[m][k]) * dec(Wq[n][k])
+//
+// (NeMo RL blog, "FP8 for linear layers in RL", Table 1: [1,128] activation and [128,128] weight
+// scales in FP32; FP8-RL write-up, section 1.) One K step of the kernel is exactly one 128-wide
+// scale slice, and one v_mfma_f32_16x16x128_f8f6f4 covers it for a 16x16 output tile, so P_kb
+// comes out of the matrix core as a float32 tile that is then scaled by sa*sw and added into a
+// float32 accumulator with one FMA per element.
+//
+// Data flow per workgroup: Xq and Wq tiles of one K slice (BM x 128 and BN x 128 bytes) are
+// copied global -> registers -> LDS with a double buffer (the next slice's global loads are in
+// flight while the current slice is multiplied), the activation scales of the slice go to LDS
+// beside them, and the weight scale of a wave's 128-column block is a wave-uniform load.
+// LDS rows are 128 bytes; the 16-byte chunk c of row r is stored at chunk c ^ (r & 7), so the
+// fragment reads of 8 consecutive rows at the same k hit 8 different bank groups.
+#include <atomic>
+
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace fp8rl {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+template <int BM_, int BN_, int WM_, int WN_>
+struct Tile {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+  static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
+  static constexpr int WAVES = WAVES_M * WAVES_N;
+  static constexpr int NT = WAVES * 64;
+  static constexpr int TM = WM / 16, TN = WN / 16;
+  static constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;
+  static constexpr int STAGE_BYTES = A_BYTES + B_BYTES + BM * 4;
+  static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
+  static constexpr int A_LOADS = BM * 8 / NT;
+  static constexpr int B_LOADS = BN * 8 / NT;
+  static_assert((BM * 8) % NT == 0 && (BN * 8) % NT == 0, "tile must split into 16-byte loads");
+  static_assert(BM <= NT, "one scale load per tile row");
+  static_assert(128 % WN == 0, "a wave's columns must share one weight-scale block");
+};
+
+using TileLarge = Tile<128, 128, 64, 64>;  // prefill-sized M
+using TileSmall = Tile<64, 64, 32, 32>;    // decode-sized M
+
+struct GemmArgs {
+  const uint8_t* xq;
+  const float* sa;
+  const uint8_t* wq;
+  const float* sw;
+  int M, N, K, KB;
+  void* y;
+  int64_t ldy;
+  int out_f32;
+  float* ws;  // split-K partials [splits][M][N], or null
+  int splits, kb_per_split;
+  // grouped form
+  const int32_t* offsets;
+  int E;
+  int64_t wq_stride, sw_stride;  // per expert
+  int tiles_n;
+};
+
+template <class T>
+struct Prefetch {
+  uint4 a[T::A_LOADS];
+  uint4 b[T::B_LOADS];
+  float s;
+};
+
+__device__ __forceinline__ uint4 ldg16(const uint8_t* p) {
+  return *reinterpret_cast<const uint4*>(p);
+}
+
+template <class T>
+__device__ __forceinline__ void load_slice(Prefetch<T>& st, const uint8_t* A, int m_valid,
+                                           const uint8_t* B, int n_valid, int64_t ld, const float* SA,
+                                           int KB, int kb, int tid) {
+  const int64_t koff = (int64_t)kb * 128;
+#pragma unroll
+  for (int i = 0; i < T::A_LOADS; ++i) {
+    const int c = tid + i * T::NT, row = c >> 3, cc = c & 7;
+    st.a[i] = row < m_valid ? ldg16(A + row * ld + koff + cc * 16) : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < T::B_LOADS; ++i) {
+    const int c = tid + i * T::NT, row = c >> 3, cc = c & 7;
+    st.b[i] = row < n_valid ? ldg16(B + row * ld + koff + cc * 16) : make_uint4(0, 0, 0, 0);
+  }
+  st.s = (tid < T::BM && tid < m_valid) ? SA[(int64_t)tid * KB + kb] : 0.f;
+}
+
+template <class T>
+__device__ __forceinline__ void store_slice(const Prefetch<T>& st, uint8_t* stage, int tid) {
+  uint8_t* sA = stage;
+  uint8_t* sB = stage + T::A_BYTES;
+  float* sS = reinterpret_cast<float*>(stage + T::A_BYTES + T::B_BYTES);
+#pragma unroll
+  for (int i = 0; i < T::A_LOADS; ++i) {
+    const int c = tid + i * T::NT, row = c >> 3, cc = c & 7;
+    *reinterpret_cast<uint4*>(sA + row * 128 + ((cc ^ (row & 7)) << 4)) = st.a[i];
+  }
+#pragma unroll
+  for (int i = 0; i < T::B_LOADS; ++i) {
+    const int c = tid + i * T::NT, row = c >> 3, cc = c & 7;
+    *reinterpret_cast<uint4*>(sB + row * 128 + ((cc ^ (row & 7)) << 4)) = st.b[i];
+  }
+  if (tid < T::BM) sS[tid] = st.s;
+}
+
+// Fragment of a 16x128 operand tile for v_mfma_f32_16x16x128_f8f6f4: lane l holds row l % 16 and
+// the 32 consecutive k of quarter l / 16. A and B use the same k assignment, so the product sums
+// every k of the slice exactly once.
+__device__ __forceinline__ v8i load_frag(const uint8_t* s, int row, int kq) {
+  const uint8_t* p = s + row * 128;
+  const int sw = row & 7;
+  const uint4 lo = *reinterpret_cast<const uint4*>(p + (((2 * kq) ^ sw) << 4));
+  const uint4 hi = *reinterpret_cast<const uint4*>(p + (((2 * kq + 1) ^ sw) << 4));
+  v8i f;
+  f[0] = (int)lo.x; f[1] = (int)lo.y; f[2] = (int)lo.z; f[3] = (int)lo.w;
+  f[4] = (int)hi.x; f[5] = (int)hi.y; f[6] = (int)hi.z; f[7] = (int)hi.w;
+  return f;
+}
+
+template <class T>
+__device__ __forceinline__ void mma_slice(const uint8_t* stage, float swv, int wm, int wn, int lane,
+                                          v4f (&acc)[T::TM][T::TN]) {
+  const uint8_t* sA = stage;
+  const uint8_t* sB = stage + T::A_BYTES;
+  const float* sS = reinterpret_cast<const float*>(stage + T::A_BYTES + T::B_BYTES);
+  const int r16 = lane & 15, kq = lane >> 4;
+  v8i af[T::TM], bf[T::TN];
+  v4f sc[T::TM];
+#pragma unroll
+  for (int i = 0; i < T::TM; ++i) af[i] = load_frag(sA, wm * T::WM + i * 16 + r16, kq);
+#pragma unroll
+  for (int j = 0; j < T::TN; ++j) bf[j] = load_frag(sB, wn * T::WN + j * 16 + r16, kq);
+#pragma unroll
+  for (int i = 0; i < T::TM; ++i) {
+    // output rows of this lane in sub-tile i: 4 * kq + v, v = 0..3
+    sc[i] = *reinterpret_cast<const v4f*>(sS + wm * T::WM + i * 16 + 4 * kq) * swv;
+  }
+  const v4f zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < T::TM; ++i) {
+#pragma unroll
+    for (int j = 0; j < T::TN; ++j) {
+      const v4f p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i], bf[j], zero, 0, 0, 0, 0,
+                                                                      0, 0);
+      acc[i][j] += p * sc[i];
+    }
+  }
+}
+
+// One output tile over K slices [kb0, kb1). A/SA start at the tile's first row, B at its first
+// column (weight row); SW is the weight-scale matrix [N/128][KB] of the current expert.
+template <class T>
+__device__ __forceinline__ void run_tile(const uint8_t* A, const float* SA, int m_valid,
+                                         const uint8_t* B, const float* SW, int n0, int n_valid,
+                                         int64_t ld, int KB, int kb0, int kb1, uint8_t* smem,
+                                         v4f (&acc)[T::TM][T::TN]) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / T::WAVES_N, wn = wave % T::WAVES_N;
+  const float* swrow = SW + (int64_t)((n0 + wn * T::WN) >> 7) * KB;
+
+#pragma unroll
+  for (int i = 0; i < T::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < T::TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+  if (kb0 >= kb1) return;
+
+  Prefetch<T> st;
+  load_slice<T>(st, A, m_valid, B, n_valid, ld, SA, KB, kb0, tid);
+  store_slice<T>(st, smem, tid);
+  __syncthreads();
+  for (int kb = kb0; kb < kb1; ++kb) {
+    const int cur = (kb - kb0) & 1;
+    const bool more = kb + 1 < kb1;
+    if (more) load_slice<T>(st, A, m_valid, B, n_valid, ld, SA, KB, kb + 1, tid);
+    const float swv = swrow[kb];
+    mma_slice<T>(smem + cur * T::STAGE_BYTES, swv, wm, wn, lane, acc);
+    if (more) store_slice<T>(st, smem + (cur ^ 1) * T::STAGE_BYTES, tid);
+    __syncthreads();
+  }
+}
+
+// Write a finished tile: rows [m0, m0 + m_valid) of Y (or of split-K partial `split`).
+template <class T>
+__device__ __forceinline__ void store_tile(const GemmArgs& p, int64_t row0, int m_valid, int n0,
+                                           int split, const v4f (&acc)[T::TM][T::TN]) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / T::WAVES_N, wn = wave % T::WAVES_N;
+  const int r16 = lane & 15, kq = lane >> 4;
+#pragma unroll
+  for (int i = 0; i < T::TM; ++i) {
+#pragma unroll
+    for (int j = 0; j < T::TN; ++j) {
+      const int col = n0 + wn * T::WN + j * 16 + r16;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int r = wm * T::WM + i * 16 + 4 * kq + v;
+        if (r >= m_valid) continue;
+        const int64_t row = row0 + r;
+        const float val = acc[i][j][v];
+        if (p.ws) {
+          p.ws[((int64_t)split * p.M + row) * p.N + col] = val;
+        } else if (p.out_f32) {
+          reinterpret_cast<float*>(p.y)[row * p.ldy + col] = val;
+        } else {
+          reinterpret_cast<uint16_t*>(p.y)[row * p.ldy + col] = f32_to_bf16_rne(val);
+        }
+      }
+    }
+  }
+}
+
+// Map a linear workgroup id to (tile_m, tile_n). Ids are first regrouped so that each of the
+// 8 XCDs (which receive workgroups round-robin) owns a contiguous range, then tiles are ordered in
+// column groups of 8 m-tiles so that concurrently running workgroups on one XCD share A rows and
+// B columns in that XCD's L2.
+__device__ __forceinline__ void tile_coords(int pid, int total, int tiles_m, int tiles_n, int& tm,
+                                            int& tn) {
+  if ((total & 7) == 0) pid = (pid & 7) * (total >> 3) + (pid >> 3);
+  constexpr int G = 8;
+  const int per_group = G * tiles_n;
+  const int group = pid / per_group;
+  const int first_m = group * G;
+  const int gsize = min(tiles_m - first_m, G);
+  const int in_group = pid - group * per_group;
+  tm = first_m + in_group % gsize;
+  tn = in_group / gsize;
+}
+
+template <class T>
+__global__ __launch_bounds__(T::NT) void gemm_kernel(GemmArgs p) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int tiles_m = (p.M + T::BM - 1) / T::BM;
+  const int tiles_n = p.N / T::BN;
+  int tm, tn;
+  tile_coords(blockIdx.x, tiles_m * tiles_n, tiles_m, tiles_n, tm, tn);
+  const int split = blockIdx.y;
+  const int kb0 = split * p.kb_per_split;
+  const int kb1 = min(p.KB, kb0 + p.kb_per_split);
+  const int m0 = tm * T::BM, n0 = tn * T::BN;
+  const int m_valid = min(T::BM, p.M - m0);
+  v4f acc[T::TM][T::TN];
+  run_tile<T>(p.xq + (int64_t)m0 * p.K, p.sa + (int64_t)m0 * p.KB, m_valid,
+              p.wq + (int64_t)n0 * p.K, p.sw, n0, T::BN, p.K, p.KB, kb0, kb1, smem, acc);
+  store_tile<T>(p, m0, m_valid, n0, split, acc);
+}
+
+// Deterministic split-K reduction: partials are summed in split order.
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ ws,
+                                                            int splits, int64_t M, int N, void* y,
+                                                            int64_t ldy, int out_f32) {
+  const int64_t i4 = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t total4 = M * N / 4;
+  if (i4 >= total4) return;
+  const int64_t e = i4 * 4;
+  const int64_t row = e / N, col = e - (e / N) * N;
+  float4 s = reinterpret_cast<const float4*>(ws)[i4];
+  for (int k = 1; k < splits; ++k) {
+    const float4 t = reinterpret_cast<const float4*>(ws + (int64_t)k * M * N)[i4];
+    s.x += t.x;
+    s.y += t.y;
+    s.z += t.z;
+    s.w += t.w;
+  }
+  if (out_f32) {
+    *reinterpret_cast<float4*>(reinterpret_cast<float*>(y) + row * ldy + col) = s;
+  } else {
+    uint16_t* o = reinterpret_cast<uint16_t*>(y) + row * ldy + col;
+    const uint32_t lo = f32_to_bf16_rne(s.x) | ((uint32_t)f32_to_bf16_rne(s.y) << 16);
+    const uint32_t hi = f32_to_bf16_rne(s.z) | ((uint32_t)f32_to_bf16_rne(s.w) << 16);
+    *reinterpret_cast<uint2*>(o) = make_uint2(lo, hi);
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Grouped GEMM. The grid enumerates (m-tile, n-tile) pairs up to the bound
+// sum_e ceil(rows_e / BM) <= M_total / BM + E; each workgroup reads the offsets, forms the
+// per-expert tile counts and their prefix sums in LDS, finds which expert its m-tile belongs to
+// and exits if it is past the last real tile. No host round trip and no workspace are needed.
+// ---------------------------------------------------------------------------------------------
+constexpr int kMaxExperts = 1024;
+
+template <class T>
+__global__ __launch_bounds__(T::NT) void grouped_gemm_kernel(GemmArgs p) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  int* s_scan = reinterpret_cast<int*>(smem + T::LDS_BYTES);  // [NT] scan scratch
+  __shared__ int s_expert, s_row0, s_rows;
+
+  const int tid = threadIdx.x;
+  const int tm_lin = blockIdx.x / p.tiles_n;
+  const int tn = blockIdx.x - tm_lin * p.tiles_n;
+
+  if (tid == 0) s_expert = -1;
+  // exclusive scan of per-expert m-tile counts, NT experts per pass, carried across passes
+  int carry = 0;
+  for (int base = 0; base < p.E; base += T::NT) {
+    const int e = base + tid;
+    int lo = 0, hi = 0, cnt = 0;
+    if (e < p.E) {
+      lo = min(max(p.offsets[e], 0), p.M);
+      hi = min(max(p.offsets[e + 1], lo), p.M);
+      cnt = (hi - lo + T::BM - 1) / T::BM;
+    }
+    s_scan[tid] = cnt;
+    __syncthreads();
+    for (int d = 1; d < T::NT; d <<= 1) {
+      const int v = tid >= d ? s_scan[tid - d] : 0;
+      __syncthreads();
+      s_scan[tid] += v;
+      __syncthreads();
+    }
+    const int incl = s_scan[tid] + carry;
+    const int excl = incl - cnt;
+    if (e < p.E && cnt > 0 && tm_lin >= excl && tm_lin < incl) {
+      s_expert = e;
+      s_row0 = lo + (tm_lin - excl) * T::BM;
+      s_rows = min(T::BM, hi - s_row0);
+    }
+    carry += s_scan[T::NT - 1];
+    __syncthreads();
+  }
+  const int e = s_expert;
+  if (e < 0) return;  // past the last real tile (uniform across the workgroup)
+  const int row0 = s_row0, m_valid = s_rows;
+  const int n0 = tn * T::BN;
+  v4f acc[T::TM][T::TN];
+  run_tile<T>(p.xq + (int64_t)row0 * p.K, p.sa + (int64_t)row0 * p.KB, m_valid,
+              p.wq + e * p.wq_stride + (int64_t)n0 * p.K, p.sw + e * p.sw_stride, n0, T::BN, p.K,
+              p.KB, 0, p.KB, smem, acc);
+  store_tile<T>(p, row0, m_valid, n0, 0, acc);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Host side: planning and launch.
+// ---------------------------------------------------------------------------------------------
+namespace {
+
+constexpr int kCfgLarge = 0, kCfgSmall = 1;
+constexpr int kTargetWorkgroups = 512;  // two per CU on 256 CUs
+constexpr int kMinSlicesPerSplit = 4;
+
+// Kernels that use more than the default 64 KiB of dynamic LDS must opt in, once per kernel and
+// device. `done` holds one bit per device id (ids >= 64 always call the runtime).
+hipError_t ensure_lds(std::atomic<uint64_t>& done, const void* kernel, int bytes) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = dev < 64 ? (uint64_t{1} << dev) : 0;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_release);
+  return e;
+}
+
+}  // namespace
+
+GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
+  GemmPlan pl{};
+  const int64_t KB = K / 128;
+  if (M >= 512) {
+    pl.cfg = kCfgLarge;
+    pl.bm = TileLarge::BM;
+    pl.bn = TileLarge::BN;
+  } else {
+    pl.cfg = kCfgSmall;
+    pl.bm = TileSmall::BM;
+    pl.bn = TileSmall::BN;
+  }
+  const int64_t tiles = ((M + pl.bm - 1) / pl.bm) * (N / pl.bn);
+  int64_t splits = 1;
+  if (tiles > 0 && tiles < kTargetWorkgroups) {
+    splits = (kTargetWorkgroups + tiles - 1) / tiles;
+    const int64_t max_splits = KB / kMinSlicesPerSplit;
+    if (splits > max_splits) splits = max_splits;
+    if (splits < 1) splits = 1;
+  }
+  pl.kb_per_split = (int)((KB + splits - 1) / splits);
+  pl.splits = (int)((KB + pl.kb_per_split - 1) / pl.kb_per_split);
+  if (pl.splits < 1) pl.splits = 1;
+  pl.workspace_bytes = pl.splits > 1 ? (size_t)pl.splits * (size_t)M * (size_t)N * sizeof(float) : 0;
+  return pl;
+}
+
+GemmPlan plan_grouped_gemm(int64_t M_total, int64_t N, int64_t K, int32_t E) {
+  GemmPlan pl{};
+  (void)M_total;
+  (void)E;
+  pl.cfg = kCfgLarge;
+  pl.bm = TileLarge::BM;
+  pl.bn = TileLarge::BN;
+  pl.splits = 1;
+  pl.kb_per_split = (int)(K / 128);
+  pl.workspace_bytes = 0;
+  return pl;
+}
+
+template <class T>
+static hipError_t launch_dense(const GemmArgs& a, const GemmPlan& pl, hipStream_t stream) {
+  static std::atomic<uint64_t> lds_done{0};
+  hipError_t e = ensure_lds(lds_done, (const void*)gemm_kernel<T>, T::LDS_BYTES);
+  if (e != hipSuccess) return e;
+  const int tiles_m = (a.M + T::BM - 1) / T::BM;
+  const int tiles_n = a.N / T::BN;
+  dim3 grid((unsigned)(tiles_m * tiles_n), (unsigned)pl.splits);
+  hipLaunchKernelGGL(gemm_kernel<T>, grid, dim3(T::NT), T::LDS_BYTES, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm(const uint8_t* xq, const float* sa, const uint8_t* wq, const float* sw,
+                       int64_t M, int64_t N, int64_t K, void* y, int out_f32, int64_t ld_y,
+                       void* workspace, const GemmPlan& pl, hipStream_t stream) {
+  GemmArgs a{};
+  a.xq = xq;
+  a.sa = sa;
+  a.wq = wq;
+  a.sw = sw;
+  a.M = (int)M;
+  a.N = (int)N;
+  a.K = (int)K;
+  a.KB = (int)(K / 128);
+  a.y = y;
+  a.ldy = ld_y;
+  a.out_f32 = out_f32;
+  a.ws = pl.splits > 1 ? reinterpret_cast<float*>(workspace) : nullptr;
+  a.splits = pl.splits;
+  a.kb_per_split = pl.kb_per_split;
+  hipError_t e = pl.cfg == kCfgLarge ? launch_dense<TileLarge>(a, pl, stream)
+                                     : launch_dense<TileSmall>(a, pl, stream);
+  if (e != hipSuccess || pl.splits == 1) return e;
+  const int64_t total4 = M * N / 4;
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((total4 + 255) / 256)), dim3(256), 0,
+                     stream, a.ws, pl.splits, M, (int)N, y, ld_y, out_f32);
+  return hipGetLastError();
+}
+
+hipError_t launch_grouped_gemm(const uint8_t* xq, const float* sa, const uint8_t* wq,
+                               const float* sw, const int32_t* offsets, int32_t E,
+                               int64_t M_total, int64_t N, int64_t K, void* y, int out_f32,
+                               void* workspace, const GemmPlan& pl, hipStream_t stream) {
+  (void)workspace;
+  using T = TileLarge;
+  GemmArgs a{};
+  a.xq = xq;
+  a.sa = sa;
+  a.wq = wq;
+  a.sw = sw;
+  a.M = (int)M_total;
+  a.N = (int)N;
+  a.K = (int)K;
+  a.KB = (int)(K / 128);
+  a.y = y;
+  a.ldy = N;
+  a.out_f32 = out_f32;
+  a.ws = nullptr;
+  a.splits = 1;
+  a.kb_per_split = a.KB;
+  a.offsets = offsets;
+  a.E = E;
+  a.wq_stride = N * K;
+  a.sw_stride = (N / 128) * (K / 128);
+  a.tiles_n = (int)(N / T::BN);
+  (void)pl;
+  const int lds = T::LDS_BYTES + T::NT * (int)sizeof(int);
+  static std::atomic<uint64_t> lds_done{0};
+  hipError_t e = ensure_lds(lds_done, (const void*)grouped_gemm_kernel<T>, lds);
+  if (e != hipSuccess) return e;
+  // sum_e ceil(rows_e / BM) <= sum_e (rows_e / BM + 1) <= ceil(M_total / BM) + E
+  const int64_t tiles_m_bound = (M_total + T::BM - 1) / T::BM + E;
+  const int64_t grid = tiles_m_bound * a.tiles_n;
+  hipLaunchKernelGGL(grouped_gemm_kernel<T>, dim3((unsigned)grid), dim3(T::NT), lds, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace fp8rl

@@ -1,0 +1,166 @@
+// Quantizer kernels: 128x128 weight blocks, 1x128 activation groups, element-wise E4M3 encode.
+//
+// Quantization rule (Unified FP8 blog, quick-read section; V_max = 448 and the E4M3 layout from
+// the FP8-RL write-up, section 1; FP32 scales from the NeMo RL blog, Table 1):
+//   S = fp32(amax / 448) (1 when amax == 0),  code = E4M3_RNE_sat(fp32(x) / S).
+// Both quotients are the IEEE float32 ones; see device_common.hpp for how they are formed exactly
+// without a per-element division.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace fp8rl {
+
+// ---------------------------------------------------------------------------------------------
+// Weights: one workgroup (4 waves) per 128x128 block. Thread t owns the 16-byte column chunk
+// (t & 15) of rows (t >> 4) + 16 i, i = 0..7, so each load instruction of a wave reads four
+// 256-byte row segments and the block (32 KiB of bf16) lives in registers between the amax pass
+// and the encode pass: HBM traffic is one read of W and one write of Wq.
+// ---------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void quant_weight_blk128_kernel(
+    const uint16_t* __restrict__ w, int64_t ld_w, uint8_t* __restrict__ wq, int64_t ld_wq,
+    float* __restrict__ sw, int KB) {
+  const int bid = blockIdx.x;
+  const int bi = bid / KB, bj = bid - (bid / KB) * KB;
+  const int t = threadIdx.x;
+  const int c = t & 15;
+  const int r0 = t >> 4;
+
+  const uint16_t* src = w + (int64_t)(bi * kBlock + r0) * ld_w + bj * kBlock + c * 8;
+  u32x4 v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + (int64_t)(16 * i) * ld_w));
+
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m = pk_max_u16(m, amax8_pk(v[i]));
+  m = wave_max_u32(hmax_u16(m));
+
+  __shared__ uint32_t red[4];
+  if ((t & 63) == 0) red[t >> 6] = m;
+  __syncthreads();
+  m = red[0];
+  m = m > red[1] ? m : red[1];
+  m = m > red[2] ? m : red[2];
+  m = m > red[3] ? m : red[3];
+
+  const float S = scale_from_amax_bits(m);
+  const double r = recip_f64(S);
+  if (t == 0) sw[bid] = S;
+
+  uint8_t* dst = wq + (int64_t)(bi * kBlock + r0) * ld_wq + bj * kBlock + c * 8;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    __builtin_nontemporal_store(quant8(v[i], r), reinterpret_cast<u32x2*>(dst + (int64_t)(16 * i) * ld_wq));
+}
+
+// ---------------------------------------------------------------------------------------------
+// Activations: each 16-lane DPP row of a wave owns one 1x128 group (8 bf16 per lane, one 16-byte
+// load), reduces its amax with four DPP steps and writes 128 codes plus one scale. A workgroup
+// covers 16 groups per step and kActSteps steps, with all loads issued before any reduction.
+// Group g is (row g / KB, slice g % KB), so neighbouring rows of a wave read neighbouring slices.
+// ---------------------------------------------------------------------------------------------
+constexpr int kActSteps = 4;
+constexpr int kActGroupsPerWG = 16 * kActSteps;
+
+__global__ __launch_bounds__(256) void quant_act_tok128_kernel(
+    const uint16_t* __restrict__ x, int64_t ld_x, uint8_t* __restrict__ xq, int64_t ld_xq,
+    float* __restrict__ sa, int KB, int64_t total_groups) {
+  const int lane16 = threadIdx.x & 15;
+  const int64_t g0 = (int64_t)blockIdx.x * kActGroupsPerWG + (threadIdx.x >> 4);
+
+  u32x4 v[kActSteps];
+#pragma unroll
+  for (int s = 0; s < kActSteps; ++s) {
+    const int64_t g = g0 + 16 * s;
+    v[s] = u32x4{0u, 0u, 0u, 0u};
+    if (g < total_groups) {
+      const int64_t row = g / KB, slice = g - (g / KB) * KB;
+      v[s] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(x + row * ld_x + slice * kBlock + lane16 * 8));
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < kActSteps; ++s) {
+    const int64_t g = g0 + 16 * s;
+    // every lane of the row takes part in the reduction, whether or not its group exists
+    const uint32_t m = row16_max_u32(hmax_u16(amax8_pk(v[s])));
+    const float S = scale_from_amax_bits(m);
+    const double r = recip_f64(S);
+    if (g < total_groups) {
+      const int64_t row = g / KB, slice = g - (g / KB) * KB;
+      if (lane16 == 0) sa[g] = S;
+      __builtin_nontemporal_store(
+          quant8(v[s], r), reinterpret_cast<u32x2*>(xq + row * ld_xq + slice * kBlock + lane16 * 8));
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Element-wise encoder (4 values per thread). NaN keeps its sign and becomes 0x7F; everything
+// else is clamped to +-448 and converted with round-to-nearest-even.
+// ---------------------------------------------------------------------------------------------
+__device__ __forceinline__ float encode_prep(float f) {
+  return __builtin_isnan(f) ? f : clamp_e4m3(f);
+}
+
+__device__ __forceinline__ uint32_t encode_fix_nan(uint32_t codes, float f, int byte) {
+  if (__builtin_isnan(f)) {
+    const uint32_t c = 0x7Fu | ((__float_as_uint(f) >> 24) & 0x80u);
+    codes = (codes & ~(0xFFu << (8 * byte))) | (c << (8 * byte));
+  }
+  return codes;
+}
+
+__global__ __launch_bounds__(256) void encode_e4m3_kernel(const float* __restrict__ v, int64_t n,
+                                                          uint8_t* __restrict__ out) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= n) return;
+  if (i + 4 <= n) {
+    const float4 f = *reinterpret_cast<const float4*>(v + i);
+    uint32_t c = pack4_e4m3(encode_prep(f.x), encode_prep(f.y), encode_prep(f.z), encode_prep(f.w));
+    c = encode_fix_nan(c, f.x, 0);
+    c = encode_fix_nan(c, f.y, 1);
+    c = encode_fix_nan(c, f.z, 2);
+    c = encode_fix_nan(c, f.w, 3);
+    *reinterpret_cast<uint32_t*>(out + i) = c;
+  } else {
+    for (int64_t j = i; j < n; ++j) {
+      const float f = v[j];
+      uint32_t c = pack4_e4m3(encode_prep(f), 0.f, 0.f, 0.f) & 0xFFu;
+      c = encode_fix_nan(c, f, 0);
+      out[j] = (uint8_t)c;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Launchers (arguments already validated by the C ABI layer).
+// ---------------------------------------------------------------------------------------------
+hipError_t launch_quant_weight(const uint16_t* w, int64_t N, int64_t K, int64_t ld_w, uint8_t* wq,
+                               int64_t ld_wq, float* sw, hipStream_t stream) {
+  const int KB = (int)(K / kBlock);
+  const int64_t blocks = (N / kBlock) * KB;
+  hipLaunchKernelGGL(quant_weight_blk128_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, w,
+                     ld_w, wq, ld_wq, sw, KB);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_act(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x, uint8_t* xq,
+                            int64_t ld_xq, float* sa, hipStream_t stream) {
+  const int KB = (int)(K / kBlock);
+  const int64_t groups = M * KB;
+  const int64_t wgs = (groups + kActGroupsPerWG - 1) / kActGroupsPerWG;
+  hipLaunchKernelGGL(quant_act_tok128_kernel, dim3((unsigned)wgs), dim3(256), 0, stream, x, ld_x,
+                     xq, ld_xq, sa, KB, groups);
+  return hipGetLastError();
+}
+
+hipError_t launch_encode(const float* v, int64_t n, uint8_t* out, hipStream_t stream) {
+  const int64_t threads = (n + 3) / 4;
+  const int64_t wgs = (threads + 255) / 256;
+  hipLaunchKernelGGL(encode_e4m3_kernel, dim3((unsigned)wgs), dim3(256), 0, stream, v, n, out);
+  return hipGetLastError();
+}
+
+}  // namespace fp8rl

@@ -1,0 +1,162 @@
+/*
+ * fp8rl.h -- C ABI of the MI355X (gfx950) FP8 blockwise-quantized W8A8 linear-layer library.
+ *
+ * The library implements the data-parallel hot path of an FP8 W8A8 linear layer as used for RL
+ * rollouts with FP8 weights:
+ *
+ *   1. per-step re-quantization of bf16 weights W[N][K] to OCP E4M3 codes with one float32 scale
+ *      per 128x128 block                      (fp8rl_quant_weight_blk128);
+ *   2. dynamic per-token quantization of bf16 activations X[M][K] to E4M3 with one float32 scale
+ *      per 1x128 group                         (fp8rl_quant_act_tok128);
+ *   3. the blockwise-scaled FP8 GEMM Y = X W^T that consumes both
+ *                                             (fp8rl_gemm_w8a8_blockscaled),
+ *      and its mixture-of-experts grouped form (fp8rl_grouped_gemm_w8a8);
+ *   plus the element-wise E4M3 encoder the quantizers share (fp8rl_encode_e4m3_f32).
+ *
+ * Sources, by page title and section:
+ *   [UFP8]  "Unified FP8: Moving Beyond Mixed Precision for Stable and Accelerated MoE RL"
+ *           (LMSYS blog digest), quick-read section: scale S = max|X| / V_max, Q(x) = round(x/S);
+ *           "FP8 scale choice" section: FP32 scales rather than E8M0.
+ *   [FP8RL] "FP8-RL: A Practical and Stable Low-Precision Stack for LLM Reinforcement Learning"
+ *           (write-up), section 1 "dynamic weight sync": weights re-quantized after every update
+ *           in independent 128x128 blocks, activations quantized dynamically, E4M3 with 4 exponent
+ *           bits, 3 mantissa bits and range [-448, 448]; attention/MLP/MoE-expert linears in FP8.
+ *   [NEMO]  NVIDIA NeMo RL FP8 blog, "FP8 for linear layers in RL", Table 1: weights E4M3 in
+ *           [128,128] blocks, input activations E4M3 in [1,128] groups, FP32 block scales; FP8
+ *           math for the linear layers.
+ *
+ * Conventions for every entry point
+ *   - Every pointer is a DEVICE pointer (memory the caller allocated on the current HIP device),
+ *     except where marked "host". The library never allocates, frees or copies memory and never
+ *     synchronizes: each call validates its arguments on the host, enqueues its kernel(s) on
+ *     `stream` (a hipStream_t; NULL means the default stream) and returns.
+ *   - bf16 tensors are passed as uint16_t bit patterns; E4M3 codes as uint8_t (OCP E4M3: sign,
+ *     4-bit exponent with bias 7, 3-bit mantissa, subnormals, no infinities, NaN = 0x7F/0xFF).
+ *   - Row-major layouts; ld_* is the distance in ELEMENTS between consecutive rows.
+ *   - Alignment: every base pointer must be 16-byte aligned (float scale arrays: 4-byte) and every
+ *     row pitch in bytes (ld_* times the element size) a multiple of 16.
+ *   - Shapes: K % 128 == 0, and N % 128 == 0 for weights and GEMMs; M >= 0 is arbitrary.
+ *     A call with nothing to do (M == 0, or N == 0 / K == 0 for the weight quantizer) returns
+ *     FP8RL_OK without touching memory or the stream. Dimensions must be below 2^31.
+ *   - Errors: all validation happens before any HIP call; a failing check returns its status and
+ *     enqueues nothing. FP8RL_ERR_HIP reports a failed launch. Faults inside a kernel surface at
+ *     the caller's next synchronization. Inputs are read-only, outputs are fully overwritten
+ *     (no bias, no accumulation into Y); outputs must not alias inputs.
+ *   - Calls are re-entrant and may be made concurrently on different streams.
+ */
+#ifndef FP8RL_H
+#define FP8RL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FP8RL_OK = 0,
+  FP8RL_ERR_NULL = 1,      /* a required pointer is NULL */
+  FP8RL_ERR_SHAPE = 2,     /* a dimension is negative, too large or not a multiple of 128 */
+  FP8RL_ERR_ALIGN = 3,     /* a pointer or row pitch breaks the alignment rule */
+  FP8RL_ERR_DTYPE = 4,     /* unknown output type */
+  FP8RL_ERR_WORKSPACE = 5, /* workspace smaller than fp8rl_workspace_bytes() asks for */
+  FP8RL_ERR_HIP = 6,       /* the HIP runtime rejected a launch */
+  FP8RL_ERR_ARG = 7        /* any other invalid argument (e.g. E < 1) */
+} fp8rl_status;
+
+typedef enum { FP8RL_OUT_BF16 = 0, FP8RL_OUT_F32 = 1 } fp8rl_out_dtype;
+
+typedef enum { FP8RL_OP_GEMM = 0, FP8RL_OP_GROUPED_GEMM = 1 } fp8rl_op;
+
+/*
+ * Element-wise E4M3 encoder: out[i] = nearest E4M3 code of v[i], ties to the even mantissa,
+ * magnitudes above 448 saturate to +-448, the sign bit is always kept (so -0.0 and negative values
+ * that round to zero give 0x80), NaN gives 0x7F with its sign.  This is the rounding step of
+ * Q(x) = round(x / S) [UFP8, quick-read section] onto the E4M3 grid [FP8RL, section 1].
+ *   v   : n float32 values (device, 16-byte aligned)
+ *   out : n codes (device, 16-byte aligned)
+ */
+int fp8rl_encode_e4m3_f32(const float* v, int64_t n, uint8_t* out, void* stream);
+
+/*
+ * Weight re-quantization, 128x128 blocks [FP8RL, section 1; NEMO, Table 1; UFP8, quick-read].
+ * For block (i, j) covering rows 128i..128i+127 and columns 128j..128j+127 of W[N][K]:
+ *   amax      = max |W| over the block (exact on bf16),
+ *   sw[i][j]  = fp32(amax / 448) by IEEE float32 division, or 1.0f when amax == 0,
+ *   Wq[n][k]  = E4M3 code of fp32(W[n][k]) / sw[i][j] (IEEE float32 quotient, then the encoder
+ *               above).
+ *   w   : bf16 W, N rows of pitch ld_w (>= K) elements
+ *   wq  : uint8 codes, N rows of pitch ld_wq (>= K)
+ *   sw  : float32 scales, dense row-major [N/128][K/128]
+ * Requires N % 128 == 0 and K % 128 == 0.
+ */
+int fp8rl_quant_weight_blk128(const uint16_t* w, int64_t N, int64_t K, int64_t ld_w, uint8_t* wq,
+                              int64_t ld_wq, float* sw, void* stream);
+
+/*
+ * Dynamic activation quantization, 1x128 groups per token row [NEMO, Table 1; FP8RL, section 1;
+ * UFP8, quick-read].  For row m and group g (columns 128g..128g+127 of X[M][K]):
+ *   sa[m][g]  = fp32(max |X[m, group]| / 448), or 1.0f when that max is 0,
+ *   Xq[m][k]  = E4M3 code of fp32(X[m][k]) / sa[m][k/128].
+ *   x   : bf16 X, M rows of pitch ld_x (>= K)
+ *   xq  : uint8 codes, M rows of pitch ld_xq (>= K)
+ *   sa  : float32 scales, dense row-major [M][K/128]
+ * Requires K % 128 == 0; any M >= 0.
+ */
+int fp8rl_quant_act_tok128(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x, uint8_t* xq,
+                           int64_t ld_xq, float* sa, void* stream);
+
+/*
+ * Blockwise-scaled W8A8 GEMM, Y = X W^T [NEMO, "FP8 for linear layers in RL"; FP8RL, section 1]:
+ *   Y[m][n] = sum_kb sa[m][kb] * sw[n/128][kb] * sum_{k in slice kb} dec(Xq[m][k]) * dec(Wq[n][k])
+ * with kb running over the K/128 slices of 128. Products of E4M3 values are exact; each slice's
+ * sum is formed by the FP8 matrix cores in float32, scaled by its two block scales and added into
+ * a float32 accumulator; the result is rounded once (to nearest even) to bf16 or kept as float32.
+ *   xq, sa : activation codes [M][K] (pitch K) and scales [M][K/128]
+ *   wq, sw : weight codes [N][K] (pitch K) and scales [N/128][K/128]
+ *   y      : output [M][ld_y] (ld_y >= N) of type y_dtype
+ *   workspace, workspace_bytes: scratch of at least fp8rl_workspace_bytes(FP8RL_OP_GEMM, M, N, K, 0)
+ *            bytes (device, 16-byte aligned; may be NULL when that size is 0). Its contents on
+ *            entry are ignored; the result does not depend on them.
+ * Requires N % 128 == 0, K % 128 == 0. The result is deterministic (same bits every run).
+ */
+int fp8rl_gemm_w8a8_blockscaled(const uint8_t* xq, const float* sa, const uint8_t* wq,
+                                const float* sw, int64_t M, int64_t N, int64_t K, void* y,
+                                int y_dtype, int64_t ld_y, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+/*
+ * Grouped (mixture-of-experts) blockwise-scaled W8A8 GEMM [FP8RL, section 1: MoE expert linears
+ * are quantized like the other linears].  Rows off[e] .. off[e+1]-1 of Xq belong to expert e and
+ * are multiplied by that expert's weights:
+ *   Y[m][n] = sum_kb sa[m][kb] * sw[e][n/128][kb] * sum_k dec(Xq[m][k]) * dec(Wq[e][n][k])
+ *   xq, sa           : [M_total][K] codes and [M_total][K/128] scales, rows grouped by expert
+ *   wq, sw           : [E][N][K] codes and [E][N/128][K/128] scales
+ *   expert_offsets   : E+1 int32 on the DEVICE; off[0] = 0, nondecreasing, off[E] = M_total
+ *                      (read by the kernels, so no host synchronization is needed). Empty experts
+ *                      are allowed. Row indices are clamped to [0, M_total], so a malformed array
+ *                      cannot cause out-of-bounds accesses, but its result is then undefined.
+ *   y                : [M_total][N] (pitch N), row order kept
+ *   workspace        : as for the dense GEMM, sized by fp8rl_workspace_bytes(FP8RL_OP_GROUPED_GEMM, ...)
+ * Requires E >= 1, N % 128 == 0, K % 128 == 0.
+ */
+int fp8rl_grouped_gemm_w8a8(const uint8_t* xq, const float* sa, const uint8_t* wq, const float* sw,
+                            const int32_t* expert_offsets, int32_t E, int64_t M_total, int64_t N,
+                            int64_t K, void* y, int y_dtype, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace the GEMM entry points need for this shape (0 when none). Host-only. */
+size_t fp8rl_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int32_t E);
+
+/* Static, NUL-terminated description of a status code. Host-only. */
+const char* fp8rl_status_string(int status);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. Host-only. */
+int fp8rl_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8RL_H */

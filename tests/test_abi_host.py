@@ -1,0 +1,140 @@
+"""Host-side checks of the C ABI (CPU only: no kernel is ever launched here).
+
+The library must load, export every function include/fp8rl.h declares, and reject invalid
+arguments with the documented status before making any HIP call.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from fp8_blockwise_quantization_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8rl.h")
+
+OK, ENULL, ESHAPE, EALIGN, EDTYPE, EWS, EHIP, EARG = range(8)
+A = 1 << 20  # a fake, 16-byte aligned "device address": never dereferenced by these calls
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fp8rl_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return _lib.lib()
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared_functions()
+    assert len(names) == 8
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(_lib.EXPORTED) == names
+
+
+def test_status_strings_and_version(L):
+    for s in range(8):
+        assert L.fp8rl_status_string(s)
+    assert L.fp8rl_status_string(99) == b"unknown status"
+    assert L.fp8rl_version() >= 100
+
+
+def test_quant_weight_validation(L):
+    f = L.fp8rl_quant_weight_blk128
+    assert f(A, 0, 128, 128, A, 128, A, None) == OK  # nothing to do
+    assert f(A, 128, 0, 128, A, 128, A, None) == OK
+    assert f(None, 128, 128, 128, A, 128, A, None) == ENULL
+    assert f(A, 128, 128, 128, A, 128, None, None) == ENULL
+    assert f(A, -1, 128, 128, A, 128, A, None) == ESHAPE
+    assert f(A, 100, 128, 128, A, 128, A, None) == ESHAPE
+    assert f(A, 128, 130, 130, A, 130, A, None) == ESHAPE
+    assert f(A, 128, 128, 64, A, 128, A, None) == ESHAPE  # ld < K
+    assert f(A + 2, 128, 128, 128, A, 128, A, None) == EALIGN
+    assert f(A, 128, 128, 132, A, 128, A, None) == EALIGN  # 264-byte pitch
+    assert f(A, 128, 128, 128, A, 136, A, None) == EALIGN
+    assert f(A, 128, 128, 128, A, 128, A + 2, None) == EALIGN
+
+
+def test_quant_act_validation(L):
+    f = L.fp8rl_quant_act_tok128
+    assert f(None, 0, 128, 128, None, 128, None, None) == OK  # M == 0
+    assert f(None, 4, 128, 128, A, 128, A, None) == ENULL
+    assert f(A, 4, 100, 128, A, 128, A, None) == ESHAPE
+    assert f(A, -4, 128, 128, A, 128, A, None) == ESHAPE
+    assert f(A, 4, 128, 128, A + 8, 128, A, None) == EALIGN
+
+
+def test_encode_validation(L):
+    f = L.fp8rl_encode_e4m3_f32
+    assert f(None, 0, None, None) == OK
+    assert f(None, 4, A, None) == ENULL
+    assert f(A + 4, 4, A, None) == EALIGN
+    assert f(A, -1, A, None) == ESHAPE
+
+
+def test_gemm_validation(L):
+    f = L.fp8rl_gemm_w8a8_blockscaled
+    args = lambda **k: dict(dict(xq=A, sa=A, wq=A, sw=A, M=64, N=256, K=256, y=A, dt=0, ldy=256,
+                                 ws=A, wsb=1 << 30), **k)
+
+    def call(**k):
+        a = args(**k)
+        return f(a["xq"], a["sa"], a["wq"], a["sw"], a["M"], a["N"], a["K"], a["y"], a["dt"],
+                 a["ldy"], a["ws"], a["wsb"], None)
+
+    assert call(M=0, xq=None) == OK
+    assert call(xq=None) == ENULL
+    assert call(y=None) == ENULL
+    assert call(N=200) == ESHAPE
+    assert call(K=192) == ESHAPE
+    assert call(M=-1) == ESHAPE
+    assert call(ldy=128) == ESHAPE
+    assert call(dt=5) == EDTYPE
+    assert call(xq=A + 1) == EALIGN
+    assert call(ldy=260) == EALIGN  # 520-byte bf16 pitch
+    need = L.fp8rl_workspace_bytes(0, 64, 256, 4096, 0)
+    assert need > 0  # a decode-shaped problem uses split-K partials
+    assert call(K=4096, wsb=need - 1) == EWS
+    assert call(K=4096, ws=None) == EWS
+
+
+def test_grouped_gemm_validation(L):
+    f = L.fp8rl_grouped_gemm_w8a8
+    base = [A, A, A, A, A, 4, 1000, 256, 256, A, 0, None, 0, None]
+    assert f(*base[:6], 0, *base[7:]) == OK  # M_total == 0
+    b = list(base)
+    b[5] = 0
+    assert f(*b) == EARG
+    b = list(base)
+    b[4] = None
+    assert f(*b) == ENULL
+    b = list(base)
+    b[7] = 300
+    assert f(*b) == ESHAPE
+    b = list(base)
+    b[4] = A + 2
+    assert f(*b) == EALIGN
+    b = list(base)
+    b[10] = 3
+    assert f(*b) == EDTYPE
+
+
+def test_workspace_query_is_pure_host(L):
+    assert L.fp8rl_workspace_bytes(0, 0, 256, 256, 0) == 0
+    assert L.fp8rl_workspace_bytes(0, 8192, 4096, 4096, 0) == 0  # large M: no split
+    assert L.fp8rl_workspace_bytes(1, 32768, 1536, 2048, 128) == 0
+    assert L.fp8rl_workspace_bytes(7, 64, 256, 256, 0) == 0
+
+
+def test_python_binding_rejects_host_tensors():
+    import torch
+
+    w = torch.zeros((128, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        _lib.fp8rl_quant_weight_blk128(w)

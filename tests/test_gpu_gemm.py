@@ -1,0 +1,192 @@
+"""GPU parity of the blockscaled W8A8 GEMM and its grouped (MoE) form against the fp64 oracle.
+
+Operands (codes and scales) come from the oracle's quantizers applied to the seeded synthetic
+workload tensors, or are drawn directly as random finite codes and scales; the GPU result must
+lie within |gpu - ref| <= 2^-7 |ref| + 1e-3 rms(ref) (bf16 output) or <= 1e-5 rms(ref) (float32
+output) of the oracle's once-rounded result, element by element.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import fp8_blockwise_quantization_amd as fq
+from oracle import gemm as og
+from oracle import quant as oq
+from tests.gpu_util import assert_gemm_close, bits16, gemm_out_to_f64, to_dev_f32, to_dev_u8
+from workloads import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def quantized_operands(M, N, K, seed, w_outliers=0.001):
+    x = synth.act_bf16(M, K, seed=seed)
+    w = synth.weight_bf16(N, K, seed=seed + 1, outlier_frac=w_outliers)
+    xq, sa = oq.quant_act_tok128(bits16(x))
+    wq, sw = oq.quant_weight_blk128(bits16(w))
+    return xq, sa, wq, sw
+
+
+def random_operands(M, N, K, seed):
+    rng = np.random.default_rng(seed)
+    xq = rng.integers(0, 256, size=(M, K)).astype(np.uint8)
+    wq = rng.integers(0, 256, size=(N, K)).astype(np.uint8)
+    xq[(xq & 0x7F) == 0x7F] = 0x7E
+    wq[(wq & 0x7F) == 0x7F] = 0xFE
+    sa = (2.0 ** rng.uniform(-20, 4, size=(M, K // 128))).astype(np.float32)
+    sw = (2.0 ** rng.uniform(-20, 4, size=(N // 128, K // 128))).astype(np.float32)
+    return xq, sa, wq, sw
+
+
+def run_and_check(xq, sa, wq, sw, what, outs=("bf16", "f32")):
+    M, N = xq.shape[0], wq.shape[0]
+    print(f"[gemm] {what} M={M} N={N} K={xq.shape[1]}", flush=True)
+    ref64 = og.gemm_blockscaled(xq, sa, wq, sw, out="f64")
+    d = [to_dev_u8(xq), to_dev_f32(sa), to_dev_u8(wq), to_dev_f32(sw)]
+    worst = {}
+    for out in outs:
+        dt = torch.bfloat16 if out == "bf16" else torch.float32
+        y = fq.gemm(*d, out_dtype=dt)
+        torch.cuda.synchronize()
+        got = gemm_out_to_f64(y)
+        if out == "bf16":
+            ref = og.bf16_bits_to_f64(og.round_f64_to_bf16_bits(ref64))
+        else:
+            ref = ref64.astype(np.float32).astype(np.float64)
+        worst[out] = assert_gemm_close(got, ref, ref64, out, what)
+    print(f"    worst err/bound {worst}", flush=True)
+    return worst
+
+
+def test_tiny_config_both_outputs():
+    run_and_check(*quantized_operands(4, 256, 256, synth.seed_of(1, 5), w_outliers=0.0), "tiny")
+
+
+@pytest.mark.parametrize("M,N,K", [(64, 4096, 4096), (64, 1024, 4096), (64, 4096, 12288),
+                                   (256, 14336, 4096), (1, 128, 128), (3, 384, 640),
+                                   (67, 1024, 4096), (130, 512, 1024)])
+def test_small_m_shapes(M, N, K):
+    run_and_check(*quantized_operands(M, N, K, 1000 + M + N + K), f"small-M {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M,N,K", [(512, 512, 512), (1000, 1024, 2048), (2048 + 37, 768, 1536),
+                                   (4096, 4096, 4096)])
+def test_large_m_shapes(M, N, K):
+    run_and_check(*quantized_operands(M, N, K, 2000 + M + N + K), f"large-M {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M,N,K", [(96, 256, 512), (700, 640, 768)])
+def test_random_codes_and_scales(M, N, K):
+    run_and_check(*random_operands(M, N, K, 3000 + M), f"random {M}x{N}x{K}")
+
+
+def test_prefill_q_proj_full_size():
+    """Qwen3-8B q_proj at prefill M = 8192 (the full GEMM, checked element by element)."""
+    run_and_check(*quantized_operands(8192, 4096, 4096, 4242), "prefill q_proj", outs=("bf16",))
+
+
+def test_output_pitch_canary_and_determinism():
+    xq, sa, wq, sw = quantized_operands(70, 256, 512, 55)
+    d = [to_dev_u8(xq), to_dev_f32(sa), to_dev_u8(wq), to_dev_f32(sw)]
+    for dt, ld in ((torch.bfloat16, 256 + 8), (torch.float32, 256 + 4)):
+        ybuf = torch.full((70, ld), 7.0, dtype=dt, device="cuda")
+        fq.gemm(*d, y=ybuf[:, :256])
+        y2 = fq.gemm(*d, out_dtype=dt)
+        torch.cuda.synchronize()
+        assert torch.all(ybuf[:, 256:] == 7.0)
+        assert torch.equal(ybuf[:, :256], y2)
+    # split-K shape: two runs give identical bits
+    xq, sa, wq, sw = quantized_operands(64, 1024, 4096, 56)
+    d = [to_dev_u8(xq), to_dev_f32(sa), to_dev_u8(wq), to_dev_f32(sw)]
+    a = fq.gemm(*d, out_dtype=torch.float32)
+    b = fq.gemm(*d, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_zero_rows_noop():
+    xq = torch.empty((0, 256), dtype=torch.uint8, device="cuda")
+    sa = torch.empty((0, 2), dtype=torch.float32, device="cuda")
+    wq = torch.zeros((256, 256), dtype=torch.uint8, device="cuda")
+    sw = torch.ones((2, 2), dtype=torch.float32, device="cuda")
+    y = fq.gemm(xq, sa, wq, sw)
+    assert y.shape == (0, 256)
+
+
+# ------------------------------------------------------------------------------- grouped GEMM
+
+
+def grouped_operands(counts, N, K, seed):
+    counts = [int(c) for c in counts]
+    E, M = len(counts), int(sum(counts))
+    x = synth.act_bf16(max(M, 1), K, seed=seed)[:M]
+    w = synth.weight_bf16(N, K, seed=seed + 1, batch=E)
+    xq, sa = oq.quant_act_tok128(bits16(x)) if M else (np.zeros((0, K), np.uint8),
+                                                        np.zeros((0, K // 128), np.float32))
+    wq = np.empty((E, N, K), np.uint8)
+    sw = np.empty((E, N // 128, K // 128), np.float32)
+    wb = bits16(w)
+    for e in range(E):
+        wq[e], sw[e] = oq.quant_weight_blk128(wb[e])
+    off = np.zeros(E + 1, np.int32)
+    off[1:] = np.cumsum(counts)
+    return xq, sa, wq, sw, off
+
+
+def grouped_random_operands(counts, N, K, seed):
+    """Random finite codes and scales for every expert (fast to build at full MoE size)."""
+    counts = [int(c) for c in counts]
+    E, M = len(counts), int(sum(counts))
+    xq, sa, _, _ = random_operands(M, 128, K, seed)
+    rng = np.random.default_rng(seed + 1)
+    wq = rng.integers(0, 256, size=(E, N, K)).astype(np.uint8)
+    wq[(wq & 0x7F) == 0x7F] = 0x7E
+    sw = (2.0 ** rng.uniform(-20, 4, size=(E, N // 128, K // 128))).astype(np.float32)
+    off = np.zeros(E + 1, np.int32)
+    off[1:] = np.cumsum(counts)
+    return xq, sa, wq, sw, off
+
+
+def run_grouped(xq, sa, wq, sw, off, what, outs=("bf16", "f32")):
+    print(f"[grouped] {what} M={xq.shape[0]} E={wq.shape[0]} N={wq.shape[1]} K={xq.shape[1]}",
+          flush=True)
+    ref64 = og.grouped_gemm_blockscaled(xq, sa, wq, sw, off, out="f64")
+    d = [to_dev_u8(xq), to_dev_f32(sa), to_dev_u8(wq), to_dev_f32(sw),
+         torch.from_numpy(off).cuda()]
+    for out in outs:
+        dt = torch.bfloat16 if out == "bf16" else torch.float32
+        y = fq.grouped_gemm(*d, out_dtype=dt)
+        torch.cuda.synchronize()
+        got = gemm_out_to_f64(y)
+        ref = (og.bf16_bits_to_f64(og.round_f64_to_bf16_bits(ref64)) if out == "bf16"
+               else ref64.astype(np.float32).astype(np.float64))
+        w = assert_gemm_close(got, ref, ref64, out, what)
+        print(f"    {out}: worst err/bound {w:.3f}", flush=True)
+
+
+def test_grouped_small_with_empty_and_single_row_experts():
+    run_grouped(*grouped_operands([0, 1, 130, 0, 5, 257, 0], 256, 384, 71), "ragged experts")
+
+
+def test_grouped_single_expert_equals_dense_path():
+    xq, sa, wq, sw, off = grouped_operands([300], 384, 512, 72)
+    run_grouped(xq, sa, wq, sw, off, "one expert")
+
+
+def test_grouped_moe_gate_up_full_size():
+    """Qwen3-30B-A3B MoE layer, expert gate/up (2048 -> 1536) with Zipf(1.1) top-8 routing."""
+    counts = synth.moe_routing_counts(4096, 128, 8, seed=synth.seed_of(5, 0))
+    run_grouped(*grouped_random_operands(counts.tolist(), 1536, 2048, 73), "moe gate_up",
+                outs=("bf16",))
+
+
+def test_grouped_moe_down_full_size():
+    counts = synth.moe_routing_counts(4096, 128, 8, seed=synth.seed_of(5, 0))
+    run_grouped(*grouped_random_operands(counts.tolist(), 2048, 768, 74), "moe down",
+                outs=("bf16",))
+
+
+def test_grouped_quantized_moe_subset():
+    """Sixteen experts of the Zipf-routed layer with quantized synthetic operands (both outputs)."""
+    counts = synth.moe_routing_counts(4096, 128, 8, seed=synth.seed_of(5, 0))[:16]
+    run_grouped(*grouped_operands(counts.tolist(), 1536, 2048, 75), "moe 16-expert subset")

@@ -6,6 +6,7 @@ implementation of the OCP E4M3 format, and (c) exact rational arithmetic.
 """
 
 import json
+import multiprocessing
 import os
 from concurrent.futures import ProcessPoolExecutor
 from fractions import Fraction
@@ -106,7 +107,8 @@ def test_saturation_and_specials():
 def test_encode_exhaustive_nonnegative_vs_torch():
     """Every non-negative float32 up to 464 (1,139,277,825 values) against torch's cast."""
     work = list(_codec_sweep.chunks())
-    with ProcessPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
+    with ProcessPoolExecutor(max_workers=min(8, os.cpu_count() or 1),
+                             mp_context=multiprocessing.get_context("spawn")) as ex:
         bad = sum(ex.map(_codec_sweep.mismatches_vs_torch, work))
     assert bad == 0
 
