@@ -1,0 +1,387 @@
+"""Benchmark of the FP8 W8A8 linear-layer hot path on one MI355X.
+
+Default workload: one Qwen3-8B-shaped decoder block at decode (M = 64 tokens, hidden 4096,
+7 linears: q/o 4096x4096, k/v 1024x4096, gate/up 12288x4096, down 4096x12288). One step is the
+whole hot path over that block:
+
+  1. per-step re-quantization of all 7 bf16 weights to E4M3 with 128x128 FP32 block scales,
+  2. dynamic 1x128 per-token quantization of each linear's bf16 input activation,
+  3. the 7 blockwise-scaled FP8 GEMMs (bf16 output).
+
+Inputs are seeded synthetic tensors resident in HBM (weights N(0, 0.02) with 0.1 % x10 outliers,
+activations N(0, 1) with 1 % x20 outlier channels), rotated over enough copies that every step
+reads more than 1 GiB, so the 256 MiB Infinity Cache cannot hold a step's working set.
+
+Prints one JSON line. `value` is the step's algorithmic HBM traffic (bytes each kernel must move
+at least once) divided by the step time, in GB/s; per-part GB/s and the GEMMs' TFLOP/s are
+reported beside it. `roofline` describes the dominant kernel (the weight re-quantization), timed
+with HIP events around each of its launches inside the timed region. `cpu_baseline` times the
+CPU oracle on a bounded sample of the same step.
+
+Other workloads (`--workload`): qwen3-8b-prefill (M = 8192), llama31-8b-mlp (M in {256, 4096}),
+llama31-8b-weight-sync (32 layers of weights), qwen3-30b-a3b-moe (grouped expert GEMMs).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+FP8_PEAK_TFLOPS = 5000.0
+ROTATE_BYTES = 1 << 30
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="qwen3-8b-decode",
+                    choices=["qwen3-8b-decode", "qwen3-8b-prefill", "llama31-8b-mlp",
+                             "llama31-8b-weight-sync", "qwen3-30b-a3b-moe"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--seed", type=int, default=0)
+    return ap.parse_args()
+
+
+class KernelTimer:
+    """HIP events around launches of one kernel on the current stream, averaged at the end."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = []
+        self.bytes = 0
+
+    def reset(self):
+        self.pairs = []
+        self.bytes = 0
+
+    def launch(self, fn, nbytes):
+        a = self.torch.cuda.Event(enable_timing=True)
+        b = self.torch.cuda.Event(enable_timing=True)
+        a.record()
+        out = fn()
+        b.record()
+        self.pairs.append((a, b))
+        self.bytes += nbytes
+        return out
+
+    def result(self):
+        ms = sum(a.elapsed_time(b) for a, b in self.pairs)
+        n = len(self.pairs)
+        return dict(launches=n, avg_us=1e3 * ms / max(n, 1),
+                    gbs=self.bytes / max(ms, 1e-12) / 1e6)
+
+
+# --------------------------------------------------------------------------------- workloads
+
+
+def w_bytes(N, K):
+    """Algorithmic bytes of re-quantizing a bf16 [N][K] weight: read 2, write 1 per element,
+    plus the float32 scale of each 128x128 block."""
+    return 3 * N * K + 4 * (N // 128) * (K // 128)
+
+
+def a_bytes(M, K):
+    return 3 * M * K + 4 * M * (K // 128)
+
+
+def g_bytes(M, N, K, out_bytes=2):
+    return M * K + N * K + out_bytes * M * N + 4 * M * (K // 128) + 4 * (N // 128) * (K // 128)
+
+
+class DenseBlock:
+    """The 7 linears of one decoder block at a given M: re-quantize, quantize, multiply."""
+
+    def __init__(self, torch, fq, synth, linears, M, seed, requant=True):
+        self.torch, self.fq = torch, fq
+        self.linears, self.M, self.requant = linears, M, requant
+        dev = "cuda"
+        wbytes = sum(2 * N * K for _, N, K in linears)
+        self.copies = max(1, -(-ROTATE_BYTES // wbytes)) if requant else 1
+        self.w = [[synth.weight_bf16(N, K, seed=seed + 100 * c + i, outlier_frac=0.001, device=dev)
+                   for i, (_, N, K) in enumerate(linears)] for c in range(self.copies)]
+        self.x = [synth.act_bf16(M, K, seed=seed + 7 + i, device=dev)
+                  for i, (_, N, K) in enumerate(linears)]
+        self.wq = [[torch.empty((N, K), dtype=torch.uint8, device=dev) for _, N, K in linears]
+                   for _ in range(self.copies)]
+        self.sw = [[torch.empty((N // 128, K // 128), dtype=torch.float32, device=dev)
+                    for _, N, K in linears] for _ in range(self.copies)]
+        self.xq = [torch.empty((M, K), dtype=torch.uint8, device=dev) for _, N, K in linears]
+        self.sa = [torch.empty((M, K // 128), dtype=torch.float32, device=dev) for _, N, K in linears]
+        self.y = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _, N, K in linears]
+        self.ws = []
+        for _, N, K in linears:
+            nb = fq.fp8rl_workspace_bytes(fq.FP8RL_OP_GEMM, M, N, K)
+            self.ws.append(torch.empty(max(nb, 16), dtype=torch.uint8, device=dev))
+        if not requant:  # weights quantized once, outside the timed region
+            for i in range(len(linears)):
+                fq.quant_weight(self.w[0][i], self.wq[0][i], self.sw[0][i])
+        self.it = 0
+        self.bytes_w = sum(w_bytes(N, K) for _, N, K in linears) if requant else 0
+        self.bytes_a = sum(a_bytes(M, K) for _, N, K in linears)
+        self.bytes_g = sum(g_bytes(M, N, K) for _, N, K in linears)
+        self.flops = sum(2 * M * N * K for _, N, K in linears)
+        self.t_w = KernelTimer(torch)
+        self.t_a = KernelTimer(torch)
+        self.t_g = KernelTimer(torch)
+
+    def step(self, timed=False):
+        fq = self.fq
+        c = self.it % self.copies
+        self.it += 1
+        L = len(self.linears)
+        if self.requant:
+            for i, (_, N, K) in enumerate(self.linears):
+                f = lambda i=i: fq.quant_weight(self.w[c][i], self.wq[c][i], self.sw[c][i])
+                self.t_w.launch(f, w_bytes(N, K)) if timed else f()
+        for i, (_, N, K) in enumerate(self.linears):
+            f = lambda i=i: fq.quant_act(self.x[i], self.xq[i], self.sa[i])
+            self.t_a.launch(f, a_bytes(self.M, K)) if timed else f()
+        for i, (_, N, K) in enumerate(self.linears):
+            f = lambda i=i: fq.gemm(self.xq[i], self.sa[i], self.wq[c][i], self.sw[c][i],
+                                    y=self.y[i], workspace=self.ws[i])
+            self.t_g.launch(f, g_bytes(self.M, N, K)) if timed else f()
+        return L
+
+    def report(self, ms):
+        parts = {}
+        if self.requant:
+            r = self.t_w.result()
+            parts["quant_weight"] = dict(r, frac_hbm=r["gbs"] / HBM_PEAK_GBS)
+        r = self.t_a.result()
+        parts["quant_act"] = dict(r, frac_hbm=r["gbs"] / HBM_PEAK_GBS)
+        r = self.t_g.result()
+        g_ms = r["avg_us"] * r["launches"] / 1e3
+        tflops = self.flops * (r["launches"] / len(self.linears)) / max(g_ms, 1e-12) / 1e9
+        parts["gemm"] = dict(r, frac_hbm=r["gbs"] / HBM_PEAK_GBS, tflops=tflops,
+                             frac_mfma=tflops / FP8_PEAK_TFLOPS)
+        return parts
+
+
+# ------------------------------------------------------------------------------ cpu baseline
+
+
+def cpu_baseline_dense(linears, M, seed, budget_linears):
+    """Time the CPU oracle on the first `budget_linears` linears of the step (full per-linear
+    work: weight re-quantization, activation quantization, GEMM)."""
+    import numpy as np
+    import torch
+
+    from oracle import gemm as og
+    from oracle import quant as oq
+    from workloads import synth
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = os.cpu_count() or 1
+    bits = lambda t: t.view(torch.int16).numpy().view(np.uint16)
+    total_bytes = 0
+    elapsed = 0.0
+    for i, (_, N, K) in enumerate(linears[:budget_linears]):
+        w = bits(synth.weight_bf16(N, K, seed=seed + i, outlier_frac=0.001))
+        x = bits(synth.act_bf16(M, K, seed=seed + 7 + i))
+        t0 = time.perf_counter()
+        wq, sw = oq.quant_weight_blk128(w)
+        xq, sa = oq.quant_act_tok128(x)
+        og.gemm_blockscaled(xq, sa, wq, sw, out="bf16")
+        elapsed += time.perf_counter() - t0
+        total_bytes += w_bytes(N, K) + a_bytes(M, K) + g_bytes(M, N, K)
+    names = ",".join(n for n, _, _ in linears[:budget_linears])
+    return dict(value=total_bytes / elapsed / 1e9, unit="GB/s", cores=int(blas_threads),
+                kind="oracle", seconds=elapsed,
+                sample=f"linears {names} of the block at M={M} (weight re-quant + activation "
+                       f"quant + fp64 GEMM each); quantizers single-threaded numpy, GEMM fp64 BLAS")
+
+
+# ------------------------------------------------------------------------------------- main
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+
+    import fp8_blockwise_quantization_amd as fq
+    from workloads import synth
+
+    torch.cuda.set_device(0)
+    fq.lib()
+    dev_name = torch.cuda.get_device_name(0)
+    props = torch.cuda.get_device_properties(0)
+
+    if args.workload == "qwen3-8b-decode":
+        linears, M, requant = synth.DENSE_LINEARS_QWEN3_8B, 64, True
+        cfg = {"workload": "Qwen3-8B decoder block, decode step", "tokens_M": 64, "hidden": 4096,
+               "linears": [list(l) for l in linears], "weight_requant_per_step": True,
+               "gemm_out": "bf16", "config_index": 1}
+    elif args.workload == "qwen3-8b-prefill":
+        linears, M, requant = synth.DENSE_LINEARS_QWEN3_8B, 8192, False
+        cfg = {"workload": "Qwen3-8B decoder block, prefill", "tokens_M": 8192, "hidden": 4096,
+               "linears": [list(l) for l in linears], "weight_requant_per_step": False,
+               "gemm_out": "bf16", "config_index": 2}
+    elif args.workload == "llama31-8b-mlp":
+        return run_mlp(args, torch, fq, synth, dev_name)
+    elif args.workload == "llama31-8b-weight-sync":
+        return run_weight_sync(args, torch, fq, synth, dev_name)
+    else:
+        return run_moe(args, torch, fq, synth, dev_name)
+
+    blk = DenseBlock(torch, fq, synth, linears, M, seed=1000 + args.seed, requant=requant)
+    for _ in range(args.warmup):
+        blk.step()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        blk.step(timed=True)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    step_bytes = blk.bytes_w + blk.bytes_a + blk.bytes_g
+    value = step_bytes / (ms * 1e-3) / 1e9
+    parts = blk.report(ms)
+    dom = "quant_weight" if requant else "gemm"
+    d = parts[dom]
+    if dom == "quant_weight":
+        roof = {"kernel": "quant_weight_blk128_kernel", "bound": "hbm", "achieved": d["gbs"],
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": d["gbs"] / HBM_PEAK_GBS,
+                "traffic": None, "avg_launch_us": d["avg_us"],
+                "per_unit": "3 B per weight element + 4 B per 128x128 block",
+                "units_per_launch": "one bf16 weight matrix (7 per step, sizes differ)"}
+    else:
+        roof = {"kernel": "gemm_kernel", "bound": "mfma", "achieved": d["tflops"],
+                "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": d["tflops"] / FP8_PEAK_TFLOPS,
+                "traffic": None, "avg_launch_us": d["avg_us"], "per_unit": "2*M*N*K flops",
+                "units_per_launch": "one linear"}
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline_dense(linears, M, seed=5000, budget_linears=5 if M <= 256 else 1)
+    line = {
+        "metric": "blockscaled FP8 GEMM TFLOP/s (% MFMA peak); block-quant GB/s (% HBM peak)",
+        "value": value, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8-e4m3 x fp8-e4m3 -> f32 accumulate, bf16 out", "data": "synthetic",
+        "config": cfg,
+        "step_bytes": step_bytes, "step_gemm_flops": blk.flops,
+        "gemm_tflops": parts["gemm"]["tflops"], "gemm_frac_mfma": parts["gemm"]["frac_mfma"],
+        "parts": parts, "roofline": roof, "cpu_baseline": cpu, "gpu": dev_name,
+        "cus": props.multi_processor_count,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def _timed(torch, fn, steps, warmup, timers=()):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    for t in timers:  # only launches inside the timed region count
+        t.reset()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
+def run_mlp(args, torch, fq, synth, dev_name):
+    out = []
+    for M in (256, 4096):
+        blk = DenseBlock(torch, fq, synth, synth.LLAMA31_8B_LAYER_LINEARS[4:], M, seed=2000 + M,
+                         requant=False)
+        ms = _timed(torch, lambda: blk.step(timed=True), args.steps, args.warmup,
+                    (blk.t_w, blk.t_a, blk.t_g))
+        parts = blk.report(ms)
+        out.append({"M": M, "ms_per_step": ms, "gemm_tflops": parts["gemm"]["tflops"],
+                    "gemm_gbs": parts["gemm"]["gbs"], "parts": parts})
+    print(json.dumps({"workload": "Llama-3.1-8B MLP (gate/up/down) GEMMs + act quant",
+                      "results": out, "gpu": dev_name}), flush=True)
+
+
+def run_weight_sync(args, torch, fq, synth, dev_name):
+    """Re-quantize every linear weight of 32 Llama-3.1-8B layers (6.98e9 elements, 14 GB bf16)."""
+    layers = 32
+    shapes = [(N, K) for _ in range(layers) for _, N, K in synth.LLAMA31_8B_LAYER_LINEARS]
+    ws, wqs, sws = [], [], []
+    uniq = {}
+    for li, (N, K) in enumerate(shapes):
+        ws.append(synth.weight_bf16(N, K, seed=3000 + li, outlier_frac=0.001, device="cuda"))
+        wqs.append(torch.empty((N, K), dtype=torch.uint8, device="cuda"))
+        sws.append(torch.empty((N // 128, K // 128), dtype=torch.float32, device="cuda"))
+    tot = sum(w_bytes(N, K) for N, K in shapes)
+    timer = KernelTimer(torch)
+
+    def step():
+        for i, (N, K) in enumerate(shapes):
+            timer.launch(lambda i=i: fq.quant_weight(ws[i], wqs[i], sws[i]), w_bytes(N, K))
+
+    ms = _timed(torch, step, max(1, args.steps // 4), max(1, args.warmup // 2), (timer,))
+    r = timer.result()
+    print(json.dumps({"workload": "Llama-3.1-8B weight sync, 32 layers", "elements":
+                      sum(N * K for N, K in shapes), "bytes": tot, "ms_per_pass": ms,
+                      "GB/s": tot / (ms * 1e-3) / 1e9, "frac_hbm": tot / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                      "kernel_only": r, "launches_per_pass": len(shapes), "gpu": dev_name}),
+          flush=True)
+
+
+def run_moe(args, torch, fq, synth, dev_name):
+    """Qwen3-30B-A3B MoE layer: act quant + grouped gate/up (2048->1536) and down (768->2048)."""
+    T, H, I, E, topk = 4096, 2048, 768, 128, 8
+    counts = synth.moe_routing_counts(T, E, topk, seed=synth.seed_of(5, 0))
+    off = synth.offsets_from_counts(counts).cuda()
+    M = int(counts.sum())
+    x1 = synth.act_bf16(M, H, seed=41, device="cuda")
+    x2 = synth.act_bf16(M, I, seed=42, device="cuda")
+    w1 = synth.weight_bf16(2 * I, H, seed=43, batch=E, device="cuda")
+    w2 = synth.weight_bf16(H, I, seed=44, batch=E, device="cuda")
+    wq1 = torch.empty((E, 2 * I, H), dtype=torch.uint8, device="cuda")
+    sw1 = torch.empty((E, 2 * I // 128, H // 128), dtype=torch.float32, device="cuda")
+    wq2 = torch.empty((E, H, I), dtype=torch.uint8, device="cuda")
+    sw2 = torch.empty((E, H // 128, I // 128), dtype=torch.float32, device="cuda")
+    for e in range(E):
+        fq.quant_weight(w1[e], wq1[e], sw1[e])
+        fq.quant_weight(w2[e], wq2[e], sw2[e])
+    xq1, sa1 = fq.quant_act(x1)
+    xq2, sa2 = fq.quant_act(x2)
+    y1 = torch.empty((M, 2 * I), dtype=torch.bfloat16, device="cuda")
+    y2 = torch.empty((M, H), dtype=torch.bfloat16, device="cuda")
+    tg = KernelTimer(torch)
+    b1 = g_bytes(M, 2 * I, H) + (E - 1) * 2 * I * H + 4 * (E - 1) * (2 * I // 128) * (H // 128)
+    b2 = g_bytes(M, H, I) + (E - 1) * H * I + 4 * (E - 1) * (H // 128) * (I // 128)
+
+    def step():
+        fq.quant_act(x1, xq1, sa1)
+        tg.launch(lambda: fq.grouped_gemm(xq1, sa1, wq1, sw1, off, y=y1), b1)
+        fq.quant_act(x2, xq2, sa2)
+        tg.launch(lambda: fq.grouped_gemm(xq2, sa2, wq2, sw2, off, y=y2), b2)
+
+    ms = _timed(torch, step, args.steps, args.warmup, (tg,))
+    r = tg.result()
+    flops = 2 * M * (2 * I) * H + 2 * M * H * I
+    g_ms = r["avg_us"] * r["launches"] / 1e3 / max(1, args.steps)
+    print(json.dumps({"workload": "Qwen3-30B-A3B MoE layer (T=4096, E=128, top-8, Zipf 1.1)",
+                      "rows": M, "max_expert_rows": int(counts.max()), "ms_per_step": ms,
+                      "grouped_gemm": r, "grouped_tflops": flops / (g_ms * 1e-3) / 1e12,
+                      "gpu": dev_name}), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -7,6 +7,8 @@ the GPU; the functions only marshal arguments into the C ABI (include/fp8rl.h).
 
 from ._lib import (  # noqa: F401
     EXPORTED,
+    FP8RL_ACCUM_F16,
+    FP8RL_ACCUM_FP8,
     FP8RL_OP_GEMM,
     FP8RL_OP_GROUPED_GEMM,
     FP8RL_OUT_BF16,

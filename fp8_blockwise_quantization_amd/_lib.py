@@ -19,6 +19,8 @@ from .build import LIB_PATH
 
 FP8RL_OUT_BF16 = 0
 FP8RL_OUT_F32 = 1
+FP8RL_ACCUM_FP8 = 0
+FP8RL_ACCUM_F16 = 1
 FP8RL_OP_GEMM = 0
 FP8RL_OP_GROUPED_GEMM = 1
 
@@ -52,9 +54,11 @@ def lib() -> ctypes.CDLL:
             "fp8rl_quant_weight_blk128": (ctypes.c_int, [vp, i64, i64, i64, vp, i64, vp, vp]),
             "fp8rl_quant_act_tok128": (ctypes.c_int, [vp, i64, i64, i64, vp, i64, vp, vp]),
             "fp8rl_gemm_w8a8_blockscaled": (
-                ctypes.c_int, [vp, vp, vp, vp, i64, i64, i64, vp, ctypes.c_int, i64, vp, sz, vp]),
+                ctypes.c_int,
+                [vp, vp, vp, vp, i64, i64, i64, vp, ctypes.c_int, i64, ctypes.c_int, vp, sz, vp]),
             "fp8rl_grouped_gemm_w8a8": (
-                ctypes.c_int, [vp, vp, vp, vp, vp, i32, i64, i64, i64, vp, ctypes.c_int, vp, sz, vp]),
+                ctypes.c_int,
+                [vp, vp, vp, vp, vp, i32, i64, i64, i64, vp, ctypes.c_int, ctypes.c_int, vp, sz, vp]),
             "fp8rl_workspace_bytes": (sz, [ctypes.c_int, i64, i64, i64, i32]),
             "fp8rl_status_string": (ctypes.c_char_p, [ctypes.c_int]),
             "fp8rl_version": (ctypes.c_int, []),
@@ -168,6 +172,17 @@ def fp8rl_workspace_bytes(op: int, M: int, N: int, K: int, E: int = 0) -> int:
     return int(lib().fp8rl_workspace_bytes(op, M, N, K, E))
 
 
+def _accum_code(accum, out_dtype) -> int:
+    """None picks FP8 matrix-core sums for bf16 output and f16 (float32-grade) ones for float32."""
+    if accum is None:
+        return FP8RL_ACCUM_FP8 if out_dtype == torch.bfloat16 else FP8RL_ACCUM_F16
+    if accum in ("fp8", FP8RL_ACCUM_FP8):
+        return FP8RL_ACCUM_FP8
+    if accum in ("f16", FP8RL_ACCUM_F16):
+        return FP8RL_ACCUM_F16
+    raise ValueError("accum must be None, 'fp8' or 'f16'")
+
+
 def _out_code(dtype) -> int:
     if dtype == torch.bfloat16:
         return FP8RL_OUT_BF16
@@ -177,7 +192,7 @@ def _out_code(dtype) -> int:
 
 
 def fp8rl_gemm_w8a8_blockscaled(xq, sa, wq, sw, out_dtype=torch.bfloat16, y=None,
-                                workspace=None, stream=None):
+                                workspace=None, stream=None, accum=None):
     """Y[M][N] = blockscaled Xq Wq^T (bf16 or float32)."""
     _dense(xq, "xq", torch.uint8)
     _dense(wq, "wq", torch.uint8)
@@ -195,14 +210,15 @@ def fp8rl_gemm_w8a8_blockscaled(xq, sa, wq, sw, out_dtype=torch.bfloat16, y=None
         workspace = torch.empty(need, dtype=torch.uint8, device=xq.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().fp8rl_gemm_w8a8_blockscaled(_ptr(xq), _ptr(sa), _ptr(wq), _ptr(sw), M, N, K,
-                                             _ptr(y), _out_code(y.dtype), ld_y, _ptr(workspace),
+                                             _ptr(y), _out_code(y.dtype), ld_y,
+                                             _accum_code(accum, y.dtype), _ptr(workspace),
                                              ws_bytes, _stream(stream)),
            "fp8rl_gemm_w8a8_blockscaled")
     return y
 
 
 def fp8rl_grouped_gemm_w8a8(xq, sa, wq, sw, expert_offsets, out_dtype=torch.bfloat16, y=None,
-                            workspace=None, stream=None):
+                            workspace=None, stream=None, accum=None):
     """Per-expert blockscaled GEMM over row segments given by device int32 ``expert_offsets``."""
     _dense(xq, "xq", torch.uint8)
     _dense(wq, "wq", torch.uint8)
@@ -222,6 +238,7 @@ def fp8rl_grouped_gemm_w8a8(xq, sa, wq, sw, expert_offsets, out_dtype=torch.bflo
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().fp8rl_grouped_gemm_w8a8(_ptr(xq), _ptr(sa), _ptr(wq), _ptr(sw),
                                          _ptr(expert_offsets), E, M, N, K, _ptr(y),
-                                         _out_code(y.dtype), _ptr(workspace), ws_bytes,
-                                         _stream(stream)), "fp8rl_grouped_gemm_w8a8")
+                                         _out_code(y.dtype), _accum_code(accum, y.dtype),
+                                         _ptr(workspace), ws_bytes, _stream(stream)),
+           "fp8rl_grouped_gemm_w8a8")
     return y

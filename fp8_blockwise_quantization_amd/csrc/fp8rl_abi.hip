@@ -95,11 +95,12 @@ size_t fp8rl_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int32_t E)
 
 int fp8rl_gemm_w8a8_blockscaled(const uint8_t* xq, const float* sa, const uint8_t* wq,
                                 const float* sw, int64_t M, int64_t N, int64_t K, void* y,
-                                int y_dtype, int64_t ld_y, void* workspace, size_t workspace_bytes,
-                                void* stream) {
+                                int y_dtype, int64_t ld_y, int accum, void* workspace,
+                                size_t workspace_bytes, void* stream) {
   if (int s = check_dims(M, N, K)) return s;
   if (M == 0) return FP8RL_OK;
   if (int s = check_gemm_common(xq, sa, wq, sw, N, K, y, y_dtype, ld_y)) return s;
+  if (accum != FP8RL_ACCUM_FP8 && accum != FP8RL_ACCUM_F16) return FP8RL_ERR_ARG;
   if (((M + 127) / 128) * (N / 64) >= (int64_t{1} << 22)) return FP8RL_ERR_SHAPE;  // grid limit
   const fp8rl::GemmPlan plan = fp8rl::plan_gemm(M, N, K);
   if (plan.workspace_bytes > 0) {
@@ -107,18 +108,20 @@ int fp8rl_gemm_w8a8_blockscaled(const uint8_t* xq, const float* sa, const uint8_
     if (!aligned(workspace, 16)) return FP8RL_ERR_ALIGN;
   }
   return hip_status(fp8rl::launch_gemm(xq, sa, wq, sw, M, N, K, y, y_dtype == FP8RL_OUT_F32, ld_y,
-                                       workspace, plan, as_stream(stream)));
+                                       accum == FP8RL_ACCUM_F16, workspace, plan,
+                                       as_stream(stream)));
 }
 
 int fp8rl_grouped_gemm_w8a8(const uint8_t* xq, const float* sa, const uint8_t* wq, const float* sw,
                             const int32_t* expert_offsets, int32_t E, int64_t M_total, int64_t N,
-                            int64_t K, void* y, int y_dtype, void* workspace,
+                            int64_t K, void* y, int y_dtype, int accum, void* workspace,
                             size_t workspace_bytes, void* stream) {
   if (int s = check_dims(M_total, N, K)) return s;
   if (E < 1 || E > 1024) return FP8RL_ERR_ARG;
   if (M_total == 0) return FP8RL_OK;
   if (!expert_offsets) return FP8RL_ERR_NULL;
   if (int s = check_gemm_common(xq, sa, wq, sw, N, K, y, y_dtype, N)) return s;
+  if (accum != FP8RL_ACCUM_FP8 && accum != FP8RL_ACCUM_F16) return FP8RL_ERR_ARG;
   if (!aligned(expert_offsets, 4)) return FP8RL_ERR_ALIGN;
   if (((M_total + 127) / 128 + E) * (N / 128) >= (int64_t{1} << 22)) return FP8RL_ERR_SHAPE;
   if ((int64_t)E * N * K >= (int64_t{1} << 40)) return FP8RL_ERR_SHAPE;
@@ -128,8 +131,8 @@ int fp8rl_grouped_gemm_w8a8(const uint8_t* xq, const float* sa, const uint8_t* w
     if (!aligned(workspace, 16)) return FP8RL_ERR_ALIGN;
   }
   return hip_status(fp8rl::launch_grouped_gemm(xq, sa, wq, sw, expert_offsets, E, M_total, N, K, y,
-                                               y_dtype == FP8RL_OUT_F32, workspace, plan,
-                                               as_stream(stream)));
+                                               y_dtype == FP8RL_OUT_F32, accum == FP8RL_ACCUM_F16,
+                                               workspace, plan, as_stream(stream)));
 }
 
 }  // extern "C"

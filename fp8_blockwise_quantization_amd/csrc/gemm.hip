@@ -124,7 +124,47 @@ __device__ __forceinline__ v8i load_frag(const uint8_t* s, int row, int kq) {
   return f;
 }
 
-template <class T>
+// Exact widening of the four E4M3 codes in a dword to four f16 values (two per result).
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ v8h widen8_f16(int lo, int hi) {
+  const v2h a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, false);
+  const v2h b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, true);
+  const v2h c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, false);
+  const v2h d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, true);
+  v8h r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+  r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
+  return r;
+}
+
+// Sum over one 128-wide K slice for a 16x16 output tile.
+//
+// Fast form (PRECISE = false): one v_mfma_f32_16x16x128_f8f6f4. Its adder aligns the slice's
+// products to the largest one and keeps about 15 bits below it (measured on gfx950), like the
+// narrow FP8 accumulators the pages describe for other hardware; the per-slice promotion to the
+// float32 accumulator bounds that loss to one slice.
+//
+// Precise form (PRECISE = true): the same codes widened exactly to f16 and summed by four
+// v_mfma_f32_16x16x32_f16 (lane l's bytes 8s .. 8s+7 in step s, the same k for A and B), whose
+// adder keeps float32-level precision.
+template <bool PRECISE>
+__device__ __forceinline__ v4f slice_product(const v8i& a, const v8i& b) {
+  const v4f zero = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (!PRECISE) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 0, 0, 0, 0, 0, 0);
+  } else {
+    v4f p = zero;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      p = __builtin_amdgcn_mfma_f32_16x16x32_f16(widen8_f16(a[2 * s], a[2 * s + 1]),
+                                                  widen8_f16(b[2 * s], b[2 * s + 1]), p, 0, 0, 0);
+    return p;
+  }
+}
+
+template <class T, bool PRECISE>
 __device__ __forceinline__ void mma_slice(const uint8_t* stage, float swv, int wm, int wn, int lane,
                                           v4f (&acc)[T::TM][T::TN]) {
   const uint8_t* sA = stage;
@@ -142,13 +182,11 @@ __device__ __forceinline__ void mma_slice(const uint8_t* stage, float swv, int w
     // output rows of this lane in sub-tile i: 4 * kq + v, v = 0..3
     sc[i] = *reinterpret_cast<const v4f*>(sS + wm * T::WM + i * 16 + 4 * kq) * swv;
   }
-  const v4f zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < T::TM; ++i) {
 #pragma unroll
     for (int j = 0; j < T::TN; ++j) {
-      const v4f p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i], bf[j], zero, 0, 0, 0, 0,
-                                                                      0, 0);
+      const v4f p = slice_product<PRECISE>(af[i], bf[j]);
       acc[i][j] += p * sc[i];
     }
   }
@@ -156,7 +194,7 @@ __device__ __forceinline__ void mma_slice(const uint8_t* stage, float swv, int w
 
 // One output tile over K slices [kb0, kb1). A/SA start at the tile's first row, B at its first
 // column (weight row); SW is the weight-scale matrix [N/128][KB] of the current expert.
-template <class T>
+template <class T, bool PRECISE>
 __device__ __forceinline__ void run_tile(const uint8_t* A, const float* SA, int m_valid,
                                          const uint8_t* B, const float* SW, int n0, int n_valid,
                                          int64_t ld, int KB, int kb0, int kb1, uint8_t* smem,
@@ -182,7 +220,7 @@ __device__ __forceinline__ void run_tile(const uint8_t* A, const float* SA, int 
     const bool more = kb + 1 < kb1;
     if (more) load_slice<T>(st, A, m_valid, B, n_valid, ld, SA, KB, kb + 1, tid);
     const float swv = swrow[kb];
-    mma_slice<T>(smem + cur * T::STAGE_BYTES, swv, wm, wn, lane, acc);
+    mma_slice<T, PRECISE>(smem + cur * T::STAGE_BYTES, swv, wm, wn, lane, acc);
     if (more) store_slice<T>(st, smem + (cur ^ 1) * T::STAGE_BYTES, tid);
     __syncthreads();
   }
@@ -235,7 +273,7 @@ __device__ __forceinline__ void tile_coords(int pid, int total, int tiles_m, int
   tn = in_group / gsize;
 }
 
-template <class T>
+template <class T, bool PRECISE>
 __global__ __launch_bounds__(T::NT) void gemm_kernel(GemmArgs p) {
   extern __shared__ __align__(16) uint8_t smem[];
   const int tiles_m = (p.M + T::BM - 1) / T::BM;
@@ -248,7 +286,7 @@ __global__ __launch_bounds__(T::NT) void gemm_kernel(GemmArgs p) {
   const int m0 = tm * T::BM, n0 = tn * T::BN;
   const int m_valid = min(T::BM, p.M - m0);
   v4f acc[T::TM][T::TN];
-  run_tile<T>(p.xq + (int64_t)m0 * p.K, p.sa + (int64_t)m0 * p.KB, m_valid,
+  run_tile<T, PRECISE>(p.xq + (int64_t)m0 * p.K, p.sa + (int64_t)m0 * p.KB, m_valid,
               p.wq + (int64_t)n0 * p.K, p.sw, n0, T::BN, p.K, p.KB, kb0, kb1, smem, acc);
   store_tile<T>(p, m0, m_valid, n0, split, acc);
 }
@@ -288,7 +326,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 // ---------------------------------------------------------------------------------------------
 constexpr int kMaxExperts = 1024;
 
-template <class T>
+template <class T, bool PRECISE>
 __global__ __launch_bounds__(T::NT) void grouped_gemm_kernel(GemmArgs p) {
   extern __shared__ __align__(16) uint8_t smem[];
   int* s_scan = reinterpret_cast<int*>(smem + T::LDS_BYTES);  // [NT] scan scratch
@@ -332,7 +370,7 @@ __global__ __launch_bounds__(T::NT) void grouped_gemm_kernel(GemmArgs p) {
   const int row0 = s_row0, m_valid = s_rows;
   const int n0 = tn * T::BN;
   v4f acc[T::TM][T::TN];
-  run_tile<T>(p.xq + (int64_t)row0 * p.K, p.sa + (int64_t)row0 * p.KB, m_valid,
+  run_tile<T, PRECISE>(p.xq + (int64_t)row0 * p.K, p.sa + (int64_t)row0 * p.KB, m_valid,
               p.wq + e * p.wq_stride + (int64_t)n0 * p.K, p.sw + e * p.sw_stride, n0, T::BN, p.K,
               p.KB, 0, p.KB, smem, acc);
   store_tile<T>(p, row0, m_valid, n0, 0, acc);
@@ -402,21 +440,21 @@ GemmPlan plan_grouped_gemm(int64_t M_total, int64_t N, int64_t K, int32_t E) {
   return pl;
 }
 
-template <class T>
+template <class T, bool PRECISE>
 static hipError_t launch_dense(const GemmArgs& a, const GemmPlan& pl, hipStream_t stream) {
   static std::atomic<uint64_t> lds_done{0};
-  hipError_t e = ensure_lds(lds_done, (const void*)gemm_kernel<T>, T::LDS_BYTES);
+  hipError_t e = ensure_lds(lds_done, (const void*)gemm_kernel<T, PRECISE>, T::LDS_BYTES);
   if (e != hipSuccess) return e;
   const int tiles_m = (a.M + T::BM - 1) / T::BM;
   const int tiles_n = a.N / T::BN;
   dim3 grid((unsigned)(tiles_m * tiles_n), (unsigned)pl.splits);
-  hipLaunchKernelGGL(gemm_kernel<T>, grid, dim3(T::NT), T::LDS_BYTES, stream, a);
+  hipLaunchKernelGGL((gemm_kernel<T, PRECISE>), grid, dim3(T::NT), T::LDS_BYTES, stream, a);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm(const uint8_t* xq, const float* sa, const uint8_t* wq, const float* sw,
                        int64_t M, int64_t N, int64_t K, void* y, int out_f32, int64_t ld_y,
-                       void* workspace, const GemmPlan& pl, hipStream_t stream) {
+                       bool precise, void* workspace, const GemmPlan& pl, hipStream_t stream) {
   GemmArgs a{};
   a.xq = xq;
   a.sa = sa;
@@ -432,8 +470,13 @@ hipError_t launch_gemm(const uint8_t* xq, const float* sa, const uint8_t* wq, co
   a.ws = pl.splits > 1 ? reinterpret_cast<float*>(workspace) : nullptr;
   a.splits = pl.splits;
   a.kb_per_split = pl.kb_per_split;
-  hipError_t e = pl.cfg == kCfgLarge ? launch_dense<TileLarge>(a, pl, stream)
-                                     : launch_dense<TileSmall>(a, pl, stream);
+  hipError_t e;
+  if (pl.cfg == kCfgLarge)
+    e = precise ? launch_dense<TileLarge, true>(a, pl, stream)
+                : launch_dense<TileLarge, false>(a, pl, stream);
+  else
+    e = precise ? launch_dense<TileSmall, true>(a, pl, stream)
+                : launch_dense<TileSmall, false>(a, pl, stream);
   if (e != hipSuccess || pl.splits == 1) return e;
   const int64_t total4 = M * N / 4;
   hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((total4 + 255) / 256)), dim3(256), 0,
@@ -444,7 +487,8 @@ hipError_t launch_gemm(const uint8_t* xq, const float* sa, const uint8_t* wq, co
 hipError_t launch_grouped_gemm(const uint8_t* xq, const float* sa, const uint8_t* wq,
                                const float* sw, const int32_t* offsets, int32_t E,
                                int64_t M_total, int64_t N, int64_t K, void* y, int out_f32,
-                               void* workspace, const GemmPlan& pl, hipStream_t stream) {
+                               bool precise, void* workspace, const GemmPlan& pl,
+                               hipStream_t stream) {
   (void)workspace;
   using T = TileLarge;
   GemmArgs a{};
@@ -469,13 +513,20 @@ hipError_t launch_grouped_gemm(const uint8_t* xq, const float* sa, const uint8_t
   a.tiles_n = (int)(N / T::BN);
   (void)pl;
   const int lds = T::LDS_BYTES + T::NT * (int)sizeof(int);
-  static std::atomic<uint64_t> lds_done{0};
-  hipError_t e = ensure_lds(lds_done, (const void*)grouped_gemm_kernel<T>, lds);
+  static std::atomic<uint64_t> lds_done_fast{0}, lds_done_precise{0};
+  const void* kern = precise ? (const void*)grouped_gemm_kernel<T, true>
+                             : (const void*)grouped_gemm_kernel<T, false>;
+  hipError_t e = ensure_lds(precise ? lds_done_precise : lds_done_fast, kern, lds);
   if (e != hipSuccess) return e;
   // sum_e ceil(rows_e / BM) <= sum_e (rows_e / BM + 1) <= ceil(M_total / BM) + E
   const int64_t tiles_m_bound = (M_total + T::BM - 1) / T::BM + E;
   const int64_t grid = tiles_m_bound * a.tiles_n;
-  hipLaunchKernelGGL(grouped_gemm_kernel<T>, dim3((unsigned)grid), dim3(T::NT), lds, stream, a);
+  if (precise)
+    hipLaunchKernelGGL((grouped_gemm_kernel<T, true>), dim3((unsigned)grid), dim3(T::NT), lds,
+                       stream, a);
+  else
+    hipLaunchKernelGGL((grouped_gemm_kernel<T, false>), dim3((unsigned)grid), dim3(T::NT), lds,
+                       stream, a);
   return hipGetLastError();
 }
 

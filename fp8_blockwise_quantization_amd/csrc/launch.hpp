@@ -27,10 +27,11 @@ GemmPlan plan_grouped_gemm(int64_t M_total, int64_t N, int64_t K, int32_t E);
 
 hipError_t launch_gemm(const uint8_t* xq, const float* sa, const uint8_t* wq, const float* sw,
                        int64_t M, int64_t N, int64_t K, void* y, int out_f32, int64_t ld_y,
-                       void* workspace, const GemmPlan& plan, hipStream_t stream);
+                       bool precise, void* workspace, const GemmPlan& plan, hipStream_t stream);
 hipError_t launch_grouped_gemm(const uint8_t* xq, const float* sa, const uint8_t* wq,
                                const float* sw, const int32_t* offsets, int32_t E,
                                int64_t M_total, int64_t N, int64_t K, void* y, int out_f32,
-                               void* workspace, const GemmPlan& plan, hipStream_t stream);
+                               bool precise, void* workspace, const GemmPlan& plan,
+                               hipStream_t stream);
 
 }  // namespace fp8rl

@@ -70,6 +70,20 @@ typedef enum { FP8RL_OUT_BF16 = 0, FP8RL_OUT_F32 = 1 } fp8rl_out_dtype;
 typedef enum { FP8RL_OP_GEMM = 0, FP8RL_OP_GROUPED_GEMM = 1 } fp8rl_op;
 
 /*
+ * How the matrix cores form the sum over one 128-wide K slice (the per-slice scaling, the float32
+ * accumulation across slices and the final rounding are the same for both):
+ *   FP8RL_ACCUM_FP8  the FP8 matrix-core instruction (v_mfma_f32_16x16x128_f8f6f4). Its internal
+ *                    adder aligns the slice's products to the largest one and keeps about 15 bits
+ *                    below it (measured on gfx950), comparable to the narrow FP8 accumulators the
+ *                    Unified FP8 blog reports for Hopper tensor cores ("Tensor Core" hardware
+ *                    table); promoting every 128-wide slice to float32 bounds the loss to one
+ *                    slice. Full FP8 rate.
+ *   FP8RL_ACCUM_F16  the same E4M3 codes widened exactly to f16 and summed by f16 matrix-core
+ *                    instructions, whose adder keeps float32-level precision. Half the FP8 rate.
+ */
+typedef enum { FP8RL_ACCUM_FP8 = 0, FP8RL_ACCUM_F16 = 1 } fp8rl_accum;
+
+/*
  * Element-wise E4M3 encoder: out[i] = nearest E4M3 code of v[i], ties to the even mantissa,
  * magnitudes above 448 saturate to +-448, the sign bit is always kept (so -0.0 and negative values
  * that round to zero give 0x80), NaN gives 0x7F with its sign.  This is the rounding step of
@@ -111,11 +125,13 @@ int fp8rl_quant_act_tok128(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x
  * Blockwise-scaled W8A8 GEMM, Y = X W^T [NEMO, "FP8 for linear layers in RL"; FP8RL, section 1]:
  *   Y[m][n] = sum_kb sa[m][kb] * sw[n/128][kb] * sum_{k in slice kb} dec(Xq[m][k]) * dec(Wq[n][k])
  * with kb running over the K/128 slices of 128. Products of E4M3 values are exact; each slice's
- * sum is formed by the FP8 matrix cores in float32, scaled by its two block scales and added into
- * a float32 accumulator; the result is rounded once (to nearest even) to bf16 or kept as float32.
+ * sum is formed by the matrix cores as `accum` selects (fp8rl_accum), scaled in float32 by its
+ * two block scales and added into a float32 accumulator; the result is rounded once (to nearest
+ * even) to bf16 or kept as float32.
  *   xq, sa : activation codes [M][K] (pitch K) and scales [M][K/128]
  *   wq, sw : weight codes [N][K] (pitch K) and scales [N/128][K/128]
  *   y      : output [M][ld_y] (ld_y >= N) of type y_dtype
+ *   accum  : FP8RL_ACCUM_FP8 or FP8RL_ACCUM_F16 (see fp8rl_accum)
  *   workspace, workspace_bytes: scratch of at least fp8rl_workspace_bytes(FP8RL_OP_GEMM, M, N, K, 0)
  *            bytes (device, 16-byte aligned; may be NULL when that size is 0). Its contents on
  *            entry are ignored; the result does not depend on them.
@@ -123,8 +139,8 @@ int fp8rl_quant_act_tok128(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x
  */
 int fp8rl_gemm_w8a8_blockscaled(const uint8_t* xq, const float* sa, const uint8_t* wq,
                                 const float* sw, int64_t M, int64_t N, int64_t K, void* y,
-                                int y_dtype, int64_t ld_y, void* workspace, size_t workspace_bytes,
-                                void* stream);
+                                int y_dtype, int64_t ld_y, int accum, void* workspace,
+                                size_t workspace_bytes, void* stream);
 
 /*
  * Grouped (mixture-of-experts) blockwise-scaled W8A8 GEMM [FP8RL, section 1: MoE expert linears
@@ -138,12 +154,13 @@ int fp8rl_gemm_w8a8_blockscaled(const uint8_t* xq, const float* sa, const uint8_
  *                      are allowed. Row indices are clamped to [0, M_total], so a malformed array
  *                      cannot cause out-of-bounds accesses, but its result is then undefined.
  *   y                : [M_total][N] (pitch N), row order kept
+ *   accum            : as for the dense GEMM (fp8rl_accum)
  *   workspace        : as for the dense GEMM, sized by fp8rl_workspace_bytes(FP8RL_OP_GROUPED_GEMM, ...)
  * Requires E >= 1, N % 128 == 0, K % 128 == 0.
  */
 int fp8rl_grouped_gemm_w8a8(const uint8_t* xq, const float* sa, const uint8_t* wq, const float* sw,
                             const int32_t* expert_offsets, int32_t E, int64_t M_total, int64_t N,
-                            int64_t K, void* y, int y_dtype, void* workspace,
+                            int64_t K, void* y, int y_dtype, int accum, void* workspace,
                             size_t workspace_bytes, void* stream);
 
 /* Bytes of workspace the GEMM entry points need for this shape (0 when none). Host-only. */

@@ -81,12 +81,12 @@ def test_encode_validation(L):
 def test_gemm_validation(L):
     f = L.fp8rl_gemm_w8a8_blockscaled
     args = lambda **k: dict(dict(xq=A, sa=A, wq=A, sw=A, M=64, N=256, K=256, y=A, dt=0, ldy=256,
-                                 ws=A, wsb=1 << 30), **k)
+                                 acc=0, ws=A, wsb=1 << 30), **k)
 
     def call(**k):
         a = args(**k)
         return f(a["xq"], a["sa"], a["wq"], a["sw"], a["M"], a["N"], a["K"], a["y"], a["dt"],
-                 a["ldy"], a["ws"], a["wsb"], None)
+                 a["ldy"], a["acc"], a["ws"], a["wsb"], None)
 
     assert call(M=0, xq=None) == OK
     assert call(xq=None) == ENULL
@@ -96,6 +96,8 @@ def test_gemm_validation(L):
     assert call(M=-1) == ESHAPE
     assert call(ldy=128) == ESHAPE
     assert call(dt=5) == EDTYPE
+    assert call(acc=2) == EARG
+    assert call(acc=-1) == EARG
     assert call(xq=A + 1) == EALIGN
     assert call(ldy=260) == EALIGN  # 520-byte bf16 pitch
     need = L.fp8rl_workspace_bytes(0, 64, 256, 4096, 0)
@@ -106,7 +108,7 @@ def test_gemm_validation(L):
 
 def test_grouped_gemm_validation(L):
     f = L.fp8rl_grouped_gemm_w8a8
-    base = [A, A, A, A, A, 4, 1000, 256, 256, A, 0, None, 0, None]
+    base = [A, A, A, A, A, 4, 1000, 256, 256, A, 0, 0, None, 0, None]
     assert f(*base[:6], 0, *base[7:]) == OK  # M_total == 0
     b = list(base)
     b[5] = 0
@@ -123,6 +125,9 @@ def test_grouped_gemm_validation(L):
     b = list(base)
     b[10] = 3
     assert f(*b) == EDTYPE
+    b = list(base)
+    b[11] = 5
+    assert f(*b) == EARG
 
 
 def test_workspace_query_is_pure_host(L):

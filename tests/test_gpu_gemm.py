@@ -4,6 +4,11 @@ Operands (codes and scales) come from the oracle's quantizers applied to the see
 workload tensors, or are drawn directly as random finite codes and scales; the GPU result must
 lie within |gpu - ref| <= 2^-7 |ref| + 1e-3 rms(ref) (bf16 output) or <= 1e-5 rms(ref) (float32
 output) of the oracle's once-rounded result, element by element.
+
+Default accumulation: FP8 matrix-core slice sums for bf16 output, f16 (float32-grade) slice sums
+for float32 output. Random full-range codes with scales spread over 2^24 stress the FP8 form's
+narrow adder; there the f16 form must meet the same bounds for both outputs, and the FP8 form is
+checked against its own derived bound (tests/gpu_util.fp8_slice_bound).
 """
 
 import numpy as np
@@ -13,7 +18,8 @@ import torch
 import fp8_blockwise_quantization_amd as fq
 from oracle import gemm as og
 from oracle import quant as oq
-from tests.gpu_util import assert_gemm_close, bits16, gemm_out_to_f64, to_dev_f32, to_dev_u8
+from tests.gpu_util import (assert_gemm_close, assert_within, bits16, fp8_slice_bound,
+                            gemm_out_to_f64, to_dev_f32, to_dev_u8)
 from workloads import synth
 
 pytestmark = pytest.mark.gpu
@@ -38,15 +44,15 @@ def random_operands(M, N, K, seed):
     return xq, sa, wq, sw
 
 
-def run_and_check(xq, sa, wq, sw, what, outs=("bf16", "f32")):
+def run_and_check(xq, sa, wq, sw, what, outs=("bf16", "f32"), accum=None):
     M, N = xq.shape[0], wq.shape[0]
-    print(f"[gemm] {what} M={M} N={N} K={xq.shape[1]}", flush=True)
+    print(f"[gemm] {what} M={M} N={N} K={xq.shape[1]} accum={accum}", flush=True)
     ref64 = og.gemm_blockscaled(xq, sa, wq, sw, out="f64")
     d = [to_dev_u8(xq), to_dev_f32(sa), to_dev_u8(wq), to_dev_f32(sw)]
     worst = {}
     for out in outs:
         dt = torch.bfloat16 if out == "bf16" else torch.float32
-        y = fq.gemm(*d, out_dtype=dt)
+        y = fq.gemm(*d, out_dtype=dt, accum=accum)
         torch.cuda.synchronize()
         got = gemm_out_to_f64(y)
         if out == "bf16":
@@ -75,9 +81,36 @@ def test_large_m_shapes(M, N, K):
     run_and_check(*quantized_operands(M, N, K, 2000 + M + N + K), f"large-M {M}x{N}x{K}")
 
 
-@pytest.mark.parametrize("M,N,K", [(96, 256, 512), (700, 640, 768)])
-def test_random_codes_and_scales(M, N, K):
-    run_and_check(*random_operands(M, N, K, 3000 + M), f"random {M}x{N}x{K}")
+@pytest.mark.parametrize("M,N,K", [(96, 256, 512), (700, 640, 768), (64, 1024, 4096)])
+def test_random_codes_and_scales_f16_slices(M, N, K):
+    run_and_check(*random_operands(M, N, K, 3000 + M), f"random {M}x{N}x{K}", accum="f16")
+
+
+@pytest.mark.parametrize("M,N,K", [(96, 256, 512), (700, 640, 768), (64, 1024, 4096)])
+def test_random_codes_and_scales_fp8_slices_derived_bound(M, N, K):
+    xq, sa, wq, sw = random_operands(M, N, K, 3100 + M)
+    print(f"[gemm] random fp8-slice bound {M}x{N}x{K}", flush=True)
+    ref64 = og.gemm_blockscaled(xq, sa, wq, sw, out="f64")
+    bound = fp8_slice_bound(xq, sa, wq, sw)
+    d = [to_dev_u8(xq), to_dev_f32(sa), to_dev_u8(wq), to_dev_f32(sw)]
+    y32 = gemm_out_to_f64(fq.gemm(*d, out_dtype=torch.float32, accum="fp8"))
+    w32 = assert_within(y32, ref64, bound + 1e-6 * np.abs(ref64), "fp8 slices, f32 out")
+    yb = gemm_out_to_f64(fq.gemm(*d, out_dtype=torch.bfloat16, accum="fp8"))
+    wb = assert_within(yb, ref64, bound + 2.0 ** -8 * np.abs(ref64), "fp8 slices, bf16 out")
+    print(f"    worst err/bound f32 {w32:.3f} bf16 {wb:.3f}", flush=True)
+
+
+@pytest.mark.parametrize("M,N,K", [(64, 4096, 4096), (2048, 1024, 2048)])
+def test_fp8_slices_with_float32_output(M, N, K):
+    """The FP8 form with float32 output on workload-distributed operands (bf16 tolerance)."""
+    xq, sa, wq, sw = quantized_operands(M, N, K, 3200 + M)
+    ref64 = og.gemm_blockscaled(xq, sa, wq, sw, out="f64")
+    d = [to_dev_u8(xq), to_dev_f32(sa), to_dev_u8(wq), to_dev_f32(sw)]
+    y = gemm_out_to_f64(fq.gemm(*d, out_dtype=torch.float32, accum="fp8"))
+    w = assert_gemm_close(y, ref64, ref64, "bf16", "fp8 slices f32 out")
+    bound = fp8_slice_bound(xq, sa, wq, sw)
+    w2 = assert_within(y, ref64, bound + 1e-6 * np.abs(ref64), "fp8 slices derived bound")
+    print(f"    worst err/(bf16 tol) {w:.3f}, err/(derived) {w2:.3f}", flush=True)
 
 
 def test_prefill_q_proj_full_size():
@@ -147,15 +180,15 @@ def grouped_random_operands(counts, N, K, seed):
     return xq, sa, wq, sw, off
 
 
-def run_grouped(xq, sa, wq, sw, off, what, outs=("bf16", "f32")):
-    print(f"[grouped] {what} M={xq.shape[0]} E={wq.shape[0]} N={wq.shape[1]} K={xq.shape[1]}",
-          flush=True)
+def run_grouped(xq, sa, wq, sw, off, what, outs=("bf16", "f32"), accum=None):
+    print(f"[grouped] {what} M={xq.shape[0]} E={wq.shape[0]} N={wq.shape[1]} K={xq.shape[1]}"
+          f" accum={accum}", flush=True)
     ref64 = og.grouped_gemm_blockscaled(xq, sa, wq, sw, off, out="f64")
     d = [to_dev_u8(xq), to_dev_f32(sa), to_dev_u8(wq), to_dev_f32(sw),
          torch.from_numpy(off).cuda()]
     for out in outs:
         dt = torch.bfloat16 if out == "bf16" else torch.float32
-        y = fq.grouped_gemm(*d, out_dtype=dt)
+        y = fq.grouped_gemm(*d, out_dtype=dt, accum=accum)
         torch.cuda.synchronize()
         got = gemm_out_to_f64(y)
         ref = (og.bf16_bits_to_f64(og.round_f64_to_bf16_bits(ref64)) if out == "bf16"
@@ -173,17 +206,36 @@ def test_grouped_single_expert_equals_dense_path():
     run_grouped(xq, sa, wq, sw, off, "one expert")
 
 
+def moe_operands(counts, N, K, seed, distinct=16):
+    """Full-size MoE operands: synthetic bf16 activations and `distinct` synthetic experts,
+    quantized by the oracle; expert e uses the quantized weights of expert e % distinct."""
+    xq, sa, wq16, sw16, off = grouped_operands(list(counts[:distinct]), N, K, seed)
+    M = int(sum(int(c) for c in counts))
+    x = synth.act_bf16(M, K, seed=seed + 2)
+    xq, sa = oq.quant_act_tok128(bits16(x))
+    E = len(counts)
+    wq = np.ascontiguousarray(np.tile(wq16, (E // distinct, 1, 1)))
+    sw = np.ascontiguousarray(np.tile(sw16, (E // distinct, 1, 1)))
+    off = np.zeros(E + 1, np.int32)
+    off[1:] = np.cumsum([int(c) for c in counts])
+    return xq, sa, wq, sw, off
+
+
 def test_grouped_moe_gate_up_full_size():
     """Qwen3-30B-A3B MoE layer, expert gate/up (2048 -> 1536) with Zipf(1.1) top-8 routing."""
     counts = synth.moe_routing_counts(4096, 128, 8, seed=synth.seed_of(5, 0))
-    run_grouped(*grouped_random_operands(counts.tolist(), 1536, 2048, 73), "moe gate_up",
-                outs=("bf16",))
+    run_grouped(*moe_operands(counts.tolist(), 1536, 2048, 73), "moe gate_up")
 
 
 def test_grouped_moe_down_full_size():
     counts = synth.moe_routing_counts(4096, 128, 8, seed=synth.seed_of(5, 0))
-    run_grouped(*grouped_random_operands(counts.tolist(), 2048, 768, 74), "moe down",
-                outs=("bf16",))
+    run_grouped(*moe_operands(counts.tolist(), 2048, 768, 74), "moe down")
+
+
+def test_grouped_random_operands_f16_slices():
+    counts = synth.moe_routing_counts(512, 32, 4, seed=99)
+    run_grouped(*grouped_random_operands(counts.tolist(), 512, 1024, 76), "random experts",
+                accum="f16")
 
 
 def test_grouped_quantized_moe_subset():
