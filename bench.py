@@ -99,7 +99,12 @@ def g_bytes(M, N, K, out_bytes=2):
 
 
 class DenseBlock:
-    """The 7 linears of one decoder block at a given M: re-quantize, quantize, multiply."""
+    """The 7 linears of one decoder block at a given M: re-quantize, quantize, multiply.
+
+    The per-step weight re-quantization of all linears is one batched launch (timed on its own
+    with HIP events); the activation quantizations and GEMMs of the 7 linears are captured once
+    per weight copy into a HIP graph and replayed, so host launch overhead does not pace the GPU.
+    """
 
     def __init__(self, torch, fq, synth, linears, M, seed, requant=True):
         self.torch, self.fq = torch, fq
@@ -115,6 +120,7 @@ class DenseBlock:
                    for _ in range(self.copies)]
         self.sw = [[torch.empty((N // 128, K // 128), dtype=torch.float32, device=dev)
                     for _, N, K in linears] for _ in range(self.copies)]
+        self.descs = [fq.weight_descs(self.w[c], self.wq[c], self.sw[c]) for c in range(self.copies)]
         self.xq = [torch.empty((M, K), dtype=torch.uint8, device=dev) for _, N, K in linears]
         self.sa = [torch.empty((M, K // 128), dtype=torch.float32, device=dev) for _, N, K in linears]
         self.y = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _, N, K in linears]
@@ -122,57 +128,69 @@ class DenseBlock:
         for _, N, K in linears:
             nb = fq.fp8rl_workspace_bytes(fq.FP8RL_OP_GEMM, M, N, K)
             self.ws.append(torch.empty(max(nb, 16), dtype=torch.uint8, device=dev))
-        if not requant:  # weights quantized once, outside the timed region
-            for i in range(len(linears)):
-                fq.quant_weight(self.w[0][i], self.wq[0][i], self.sw[0][i])
+        for c in range(self.copies):  # every copy holds valid codes before the first replay
+            self.requant_step(c)
         self.it = 0
         self.bytes_w = sum(w_bytes(N, K) for _, N, K in linears) if requant else 0
         self.bytes_a = sum(a_bytes(M, K) for _, N, K in linears)
         self.bytes_g = sum(g_bytes(M, N, K) for _, N, K in linears)
         self.flops = sum(2 * M * N * K for _, N, K in linears)
         self.t_w = KernelTimer(torch)
-        self.t_a = KernelTimer(torch)
-        self.t_g = KernelTimer(torch)
+        self.graphs = None
+
+    def requant_step(self, c):
+        self.fq.quant_weights(None, None, None, descs=self.descs[c])
+
+    def linears_step(self, c):
+        fq = self.fq
+        for i in range(len(self.linears)):
+            fq.quant_act(self.x[i], self.xq[i], self.sa[i])
+            fq.gemm(self.xq[i], self.sa[i], self.wq[c][i], self.sw[c][i], y=self.y[i],
+                    workspace=self.ws[i])
+
+    def capture(self):
+        torch = self.torch
+        for c in range(self.copies):  # warm the launch paths (LDS attributes) before capture
+            self.linears_step(c)
+        torch.cuda.synchronize()
+        self.graphs = []
+        for c in range(self.copies):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                self.linears_step(c)
+            self.graphs.append(g)
+        torch.cuda.synchronize()
 
     def step(self, timed=False):
-        fq = self.fq
         c = self.it % self.copies
         self.it += 1
-        L = len(self.linears)
         if self.requant:
-            for i, (_, N, K) in enumerate(self.linears):
-                f = lambda i=i: fq.quant_weight(self.w[c][i], self.wq[c][i], self.sw[c][i])
-                self.t_w.launch(f, w_bytes(N, K)) if timed else f()
-        for i, (_, N, K) in enumerate(self.linears):
-            f = lambda i=i: fq.quant_act(self.x[i], self.xq[i], self.sa[i])
-            self.t_a.launch(f, a_bytes(self.M, K)) if timed else f()
-        for i, (_, N, K) in enumerate(self.linears):
-            f = lambda i=i: fq.gemm(self.xq[i], self.sa[i], self.wq[c][i], self.sw[c][i],
-                                    y=self.y[i], workspace=self.ws[i])
-            self.t_g.launch(f, g_bytes(self.M, N, K)) if timed else f()
-        return L
+            if timed:
+                self.t_w.launch(lambda: self.requant_step(c), self.bytes_w)
+            else:
+                self.requant_step(c)
+        self.graphs[c].replay()
 
-    def report(self, ms):
-        parts = {}
-        if self.requant:
-            r = self.t_w.result()
-            parts["quant_weight"] = dict(r, frac_hbm=r["gbs"] / HBM_PEAK_GBS)
-        r = self.t_a.result()
-        parts["quant_act"] = dict(r, frac_hbm=r["gbs"] / HBM_PEAK_GBS)
-        r = self.t_g.result()
-        g_ms = r["avg_us"] * r["launches"] / 1e3
-        tflops = self.flops * (r["launches"] / len(self.linears)) / max(g_ms, 1e-12) / 1e9
-        parts["gemm"] = dict(r, frac_hbm=r["gbs"] / HBM_PEAK_GBS, tflops=tflops,
-                             frac_mfma=tflops / FP8_PEAK_TFLOPS)
-        return parts
+    def time_linears(self, reps):
+        """Kernel time of the captured act-quant + GEMM part alone (graph replays)."""
+        torch = self.torch
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for r in range(reps):
+            self.graphs[r % self.copies].replay()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
 
 
 # ------------------------------------------------------------------------------ cpu baseline
 
 
-def cpu_baseline_dense(linears, M, seed, budget_linears):
-    """Time the CPU oracle on the first `budget_linears` linears of the step (full per-linear
-    work: weight re-quantization, activation quantization, GEMM)."""
+def cpu_baseline_dense(linears, M, seed, budget_linears, min_seconds=10.0):
+    """Time the CPU oracle on the linears of the step, in order and cycling, for at least
+    `budget_linears` linears and `min_seconds` of oracle time (full per-linear work: weight
+    re-quantization, activation quantization, GEMM)."""
     import numpy as np
     import torch
 
@@ -189,7 +207,10 @@ def cpu_baseline_dense(linears, M, seed, budget_linears):
     bits = lambda t: t.view(torch.int16).numpy().view(np.uint16)
     total_bytes = 0
     elapsed = 0.0
-    for i, (_, N, K) in enumerate(linears[:budget_linears]):
+    done = []
+    i = 0
+    while i < budget_linears or elapsed < min_seconds:
+        name, N, K = linears[i % len(linears)]
         w = bits(synth.weight_bf16(N, K, seed=seed + i, outlier_frac=0.001))
         x = bits(synth.act_bf16(M, K, seed=seed + 7 + i))
         t0 = time.perf_counter()
@@ -198,11 +219,13 @@ def cpu_baseline_dense(linears, M, seed, budget_linears):
         og.gemm_blockscaled(xq, sa, wq, sw, out="bf16")
         elapsed += time.perf_counter() - t0
         total_bytes += w_bytes(N, K) + a_bytes(M, K) + g_bytes(M, N, K)
-    names = ",".join(n for n, _, _ in linears[:budget_linears])
+        done.append(name)
+        i += 1
     return dict(value=total_bytes / elapsed / 1e9, unit="GB/s", cores=int(blas_threads),
                 kind="oracle", seconds=elapsed,
-                sample=f"linears {names} of the block at M={M} (weight re-quant + activation "
-                       f"quant + fp64 GEMM each); quantizers single-threaded numpy, GEMM fp64 BLAS")
+                sample=f"{len(done)} linears of the block at M={M} ({','.join(done)}): weight "
+                       f"re-quant + activation quant + fp64 GEMM each; quantizers single-threaded "
+                       f"numpy, GEMM fp64 BLAS; input generation not timed")
 
 
 # ------------------------------------------------------------------------------------- main
@@ -242,6 +265,7 @@ def main():
         return run_moe(args, torch, fq, synth, dev_name)
 
     blk = DenseBlock(torch, fq, synth, linears, M, seed=1000 + args.seed, requant=requant)
+    blk.capture()
     for _ in range(args.warmup):
         blk.step()
     torch.cuda.synchronize()
@@ -255,23 +279,28 @@ def main():
     ms = start.elapsed_time(end) / args.steps
     step_bytes = blk.bytes_w + blk.bytes_a + blk.bytes_g
     value = step_bytes / (ms * 1e-3) / 1e9
-    parts = blk.report(ms)
-    dom = "quant_weight" if requant else "gemm"
-    d = parts[dom]
-    if dom == "quant_weight":
-        roof = {"kernel": "quant_weight_blk128_kernel", "bound": "hbm", "achieved": d["gbs"],
-                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": d["gbs"] / HBM_PEAK_GBS,
-                "traffic": None, "avg_launch_us": d["avg_us"],
+    lin_ms = blk.time_linears(max(args.steps, 10))
+    parts = {"act_quant_and_gemm_graph": {
+        "us_per_step": 1e3 * lin_ms, "bytes": blk.bytes_a + blk.bytes_g, "flops": blk.flops,
+        "gbs": (blk.bytes_a + blk.bytes_g) / (lin_ms * 1e-3) / 1e9,
+        "gemm_tflops": blk.flops / (lin_ms * 1e-3) / 1e12}}
+    if requant:
+        r = blk.t_w.result()
+        parts["quant_weight_batched"] = dict(r, frac_hbm=r["gbs"] / HBM_PEAK_GBS)
+        roof = {"kernel": "quant_weight_blk128_kernel", "bound": "hbm", "achieved": r["gbs"],
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": r["gbs"] / HBM_PEAK_GBS,
+                "traffic": None, "avg_launch_us": r["avg_us"],
                 "per_unit": "3 B per weight element + 4 B per 128x128 block",
-                "units_per_launch": "one bf16 weight matrix (7 per step, sizes differ)"}
+                "units_per_launch": "all 7 weights of the block (192,937,984 elements, 11,776 blocks)"}
     else:
-        roof = {"kernel": "gemm_kernel", "bound": "mfma", "achieved": d["tflops"],
-                "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": d["tflops"] / FP8_PEAK_TFLOPS,
-                "traffic": None, "avg_launch_us": d["avg_us"], "per_unit": "2*M*N*K flops",
-                "units_per_launch": "one linear"}
+        tf = blk.flops / (lin_ms * 1e-3) / 1e12
+        roof = {"kernel": "gemm_kernel", "bound": "mfma", "achieved": tf, "peak": FP8_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": tf / FP8_PEAK_TFLOPS, "traffic": None,
+                "avg_launch_us": None, "per_unit": "2*M*N*K flops per linear",
+                "units_per_launch": "one linear (graph of 7 act quants + 7 GEMMs timed)"}
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline_dense(linears, M, seed=5000, budget_linears=5 if M <= 256 else 1)
+        cpu = cpu_baseline_dense(linears, M, seed=5000, budget_linears=7 if M <= 256 else 1)
     line = {
         "metric": "blockscaled FP8 GEMM TFLOP/s (% MFMA peak); block-quant GB/s (% HBM peak)",
         "value": value, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -279,7 +308,6 @@ def main():
         "dtype": "fp8-e4m3 x fp8-e4m3 -> f32 accumulate, bf16 out", "data": "synthetic",
         "config": cfg,
         "step_bytes": step_bytes, "step_gemm_flops": blk.flops,
-        "gemm_tflops": parts["gemm"]["tflops"], "gemm_frac_mfma": parts["gemm"]["frac_mfma"],
         "parts": parts, "roofline": roof, "cpu_baseline": cpu, "gpu": dev_name,
         "cus": props.multi_processor_count,
     }
@@ -307,11 +335,11 @@ def run_mlp(args, torch, fq, synth, dev_name):
     for M in (256, 4096):
         blk = DenseBlock(torch, fq, synth, synth.LLAMA31_8B_LAYER_LINEARS[4:], M, seed=2000 + M,
                          requant=False)
-        ms = _timed(torch, lambda: blk.step(timed=True), args.steps, args.warmup,
-                    (blk.t_w, blk.t_a, blk.t_g))
-        parts = blk.report(ms)
-        out.append({"M": M, "ms_per_step": ms, "gemm_tflops": parts["gemm"]["tflops"],
-                    "gemm_gbs": parts["gemm"]["gbs"], "parts": parts})
+        blk.capture()
+        ms = blk.time_linears(max(args.steps, 10))
+        out.append({"M": M, "us_per_step": 1e3 * ms, "gemm_tflops_incl_act_quant":
+                    blk.flops / (ms * 1e-3) / 1e12,
+                    "gbs": (blk.bytes_a + blk.bytes_g) / (ms * 1e-3) / 1e9})
     print(json.dumps({"workload": "Llama-3.1-8B MLP (gate/up/down) GEMMs + act quant",
                       "results": out, "gpu": dev_name}), flush=True)
 
@@ -328,17 +356,17 @@ def run_weight_sync(args, torch, fq, synth, dev_name):
         sws.append(torch.empty((N // 128, K // 128), dtype=torch.float32, device="cuda"))
     tot = sum(w_bytes(N, K) for N, K in shapes)
     timer = KernelTimer(torch)
+    descs = fq.weight_descs(ws, wqs, sws)
 
-    def step():
-        for i, (N, K) in enumerate(shapes):
-            timer.launch(lambda i=i: fq.quant_weight(ws[i], wqs[i], sws[i]), w_bytes(N, K))
+    def step():  # 224 matrices -> 7 launches of 32
+        timer.launch(lambda: fq.quant_weights(None, None, None, descs=descs), tot)
 
     ms = _timed(torch, step, max(1, args.steps // 4), max(1, args.warmup // 2), (timer,))
     r = timer.result()
     print(json.dumps({"workload": "Llama-3.1-8B weight sync, 32 layers", "elements":
                       sum(N * K for N, K in shapes), "bytes": tot, "ms_per_pass": ms,
                       "GB/s": tot / (ms * 1e-3) / 1e9, "frac_hbm": tot / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                      "kernel_only": r, "launches_per_pass": len(shapes), "gpu": dev_name}),
+                      "events": r, "launches_per_pass": -(-len(shapes) // 32), "gpu": dev_name}),
           flush=True)
 
 

@@ -19,12 +19,15 @@ from ._lib import (  # noqa: F401
     fp8rl_grouped_gemm_w8a8,
     fp8rl_quant_act_tok128,
     fp8rl_quant_weight_blk128,
+    fp8rl_quant_weight_blk128_batched,
+    weight_descs,
     fp8rl_workspace_bytes,
     lib,
 )
 
 # Short aliases.
 quant_weight = fp8rl_quant_weight_blk128
+quant_weights = fp8rl_quant_weight_blk128_batched
 quant_act = fp8rl_quant_act_tok128
 gemm = fp8rl_gemm_w8a8_blockscaled
 grouped_gemm = fp8rl_grouped_gemm_w8a8

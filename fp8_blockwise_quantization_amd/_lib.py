@@ -24,6 +24,14 @@ FP8RL_ACCUM_F16 = 1
 FP8RL_OP_GEMM = 0
 FP8RL_OP_GROUPED_GEMM = 1
 
+class WeightDesc(ctypes.Structure):
+    """fp8rl_weight_desc (include/fp8rl.h)."""
+
+    _fields_ = [("w", ctypes.c_void_p), ("wq", ctypes.c_void_p), ("sw", ctypes.c_void_p),
+                ("N", ctypes.c_int64), ("K", ctypes.c_int64), ("ld_w", ctypes.c_int64),
+                ("ld_wq", ctypes.c_int64)]
+
+
 _lock = threading.Lock()
 _lib = None
 
@@ -52,6 +60,8 @@ def lib() -> ctypes.CDLL:
         sig = {
             "fp8rl_encode_e4m3_f32": (ctypes.c_int, [vp, i64, vp, vp]),
             "fp8rl_quant_weight_blk128": (ctypes.c_int, [vp, i64, i64, i64, vp, i64, vp, vp]),
+            "fp8rl_quant_weight_blk128_batched": (ctypes.c_int,
+                                                  [ctypes.POINTER(WeightDesc), i32, vp]),
             "fp8rl_quant_act_tok128": (ctypes.c_int, [vp, i64, i64, i64, vp, i64, vp, vp]),
             "fp8rl_gemm_w8a8_blockscaled": (
                 ctypes.c_int,
@@ -74,6 +84,7 @@ def lib() -> ctypes.CDLL:
 EXPORTED = (
     "fp8rl_encode_e4m3_f32",
     "fp8rl_quant_weight_blk128",
+    "fp8rl_quant_weight_blk128_batched",
     "fp8rl_quant_act_tok128",
     "fp8rl_gemm_w8a8_blockscaled",
     "fp8rl_grouped_gemm_w8a8",
@@ -148,6 +159,30 @@ def fp8rl_quant_weight_blk128(w: torch.Tensor, wq: torch.Tensor | None = None,
     _check(lib().fp8rl_quant_weight_blk128(_ptr(w), N, K, ld_w, _ptr(wq), ld_wq, _ptr(sw),
                                            _stream(stream)), "fp8rl_quant_weight_blk128")
     return wq, sw
+
+
+def weight_descs(ws, wqs, sws):
+    """Validate tensors and build the descriptor array for fp8rl_quant_weight_blk128_batched."""
+    arr = (WeightDesc * len(ws))()
+    for i, (w, wq, sw) in enumerate(zip(ws, wqs, sws)):
+        ld_w = _rows(w, "w", torch.bfloat16)
+        ld_wq = _rows(wq, "wq", torch.uint8)
+        _dense(sw, "sw", torch.float32)
+        N, K = w.shape
+        if tuple(wq.shape) != (N, K) or sw.numel() != (N // 128) * (K // 128):
+            raise ValueError(f"descriptor {i}: output shapes do not match the weight")
+        arr[i] = WeightDesc(_ptr(w), _ptr(wq), _ptr(sw), N, K, ld_w, ld_wq)
+    return arr
+
+
+def fp8rl_quant_weight_blk128_batched(ws, wqs, sws, stream=None, descs=None):
+    """Re-quantize several bf16 weights in ceil(len/32) launches; outputs are given by the caller.
+
+    ``descs`` may be a prebuilt array from ``weight_descs`` (saves re-validating every call)."""
+    if descs is None:
+        descs = weight_descs(ws, wqs, sws)
+    _check(lib().fp8rl_quant_weight_blk128_batched(descs, len(descs), _stream(stream)),
+           "fp8rl_quant_weight_blk128_batched")
 
 
 def fp8rl_quant_act_tok128(x: torch.Tensor, xq: torch.Tensor | None = None,

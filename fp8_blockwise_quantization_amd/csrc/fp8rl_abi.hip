@@ -62,16 +62,67 @@ int fp8rl_encode_e4m3_f32(const float* v, int64_t n, uint8_t* out, void* stream)
   return hip_status(fp8rl::launch_encode(v, n, out, as_stream(stream)));
 }
 
+namespace {
+
+int check_weight(const fp8rl_weight_desc& d) {
+  if (int s = check_dims(d.N, d.K, 0)) return s;
+  if (d.N == 0 || d.K == 0) return FP8RL_OK;
+  if (!d.w || !d.wq || !d.sw) return FP8RL_ERR_NULL;
+  if (d.N % 128 || d.K % 128 || d.ld_w < d.K || d.ld_wq < d.K) return FP8RL_ERR_SHAPE;
+  if ((d.N / 128) * (d.K / 128) >= (int64_t{1} << 24)) return FP8RL_ERR_SHAPE;  // grid limit
+  if (!aligned(d.w, 16) || !aligned(d.wq, 16) || !aligned(d.sw, 4) || (d.ld_w * 2) % 16 ||
+      d.ld_wq % 16)
+    return FP8RL_ERR_ALIGN;
+  return FP8RL_OK;
+}
+
+// Launch the (already validated) descriptors in groups that fit one kernel's argument block
+// and keep every grid below 2^24 workgroups.
+int launch_weights(const fp8rl_weight_desc* descs, int32_t count, hipStream_t stream) {
+  fp8rl::WeightBatch b{};
+  int64_t blocks = 0;
+  auto flush = [&]() -> int {
+    if (b.count == 0) return FP8RL_OK;
+    hipError_t e = fp8rl::launch_quant_weight_batch(b, (int)blocks, stream);
+    b = fp8rl::WeightBatch{};
+    blocks = 0;
+    return hip_status(e);
+  };
+  for (int32_t i = 0; i < count; ++i) {
+    const fp8rl_weight_desc& d = descs[i];
+    if (d.N == 0 || d.K == 0) continue;
+    const int64_t nb = (d.N / 128) * (d.K / 128);
+    if (b.count == fp8rl::kWeightBatch || blocks + nb >= (int64_t{1} << 24))
+      if (int s = flush()) return s;
+    b.w[b.count] = d.w;
+    b.wq[b.count] = d.wq;
+    b.sw[b.count] = d.sw;
+    b.ld_w[b.count] = d.ld_w;
+    b.ld_wq[b.count] = d.ld_wq;
+    b.kb[b.count] = (int)(d.K / 128);
+    b.block_begin[b.count] = (int)blocks;
+    ++b.count;
+    blocks += nb;
+  }
+  return flush();
+}
+
+}  // namespace
+
 int fp8rl_quant_weight_blk128(const uint16_t* w, int64_t N, int64_t K, int64_t ld_w, uint8_t* wq,
                               int64_t ld_wq, float* sw, void* stream) {
-  if (int s = check_dims(N, K, 0)) return s;
-  if (N == 0 || K == 0) return FP8RL_OK;
-  if (!w || !wq || !sw) return FP8RL_ERR_NULL;
-  if (N % 128 || K % 128 || ld_w < K || ld_wq < K) return FP8RL_ERR_SHAPE;
-  if ((N / 128) * (K / 128) >= (int64_t{1} << 24)) return FP8RL_ERR_SHAPE;  // grid limit
-  if (!aligned(w, 16) || !aligned(wq, 16) || !aligned(sw, 4) || (ld_w * 2) % 16 || ld_wq % 16)
-    return FP8RL_ERR_ALIGN;
-  return hip_status(fp8rl::launch_quant_weight(w, N, K, ld_w, wq, ld_wq, sw, as_stream(stream)));
+  const fp8rl_weight_desc d{w, wq, sw, N, K, ld_w, ld_wq};
+  if (int s = check_weight(d)) return s;
+  return launch_weights(&d, 1, as_stream(stream));
+}
+
+int fp8rl_quant_weight_blk128_batched(const fp8rl_weight_desc* descs, int32_t count, void* stream) {
+  if (count < 0) return FP8RL_ERR_ARG;
+  if (count == 0) return FP8RL_OK;
+  if (!descs) return FP8RL_ERR_NULL;
+  for (int32_t i = 0; i < count; ++i)
+    if (int s = check_weight(descs[i])) return s;
+  return launch_weights(descs, count, as_stream(stream));
 }
 
 int fp8rl_quant_act_tok128(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x, uint8_t* xq,

@@ -7,8 +7,20 @@
 
 namespace fp8rl {
 
-hipError_t launch_quant_weight(const uint16_t* w, int64_t N, int64_t K, int64_t ld_w, uint8_t* wq,
-                               int64_t ld_wq, float* sw, hipStream_t stream);
+// Up to kWeightBatch weight matrices quantized by one launch (passed by value as kernel
+// arguments: 32 * 48 bytes + 4).
+constexpr int kWeightBatch = 32;
+struct WeightBatch {
+  const uint16_t* w[kWeightBatch];
+  uint8_t* wq[kWeightBatch];
+  float* sw[kWeightBatch];
+  int64_t ld_w[kWeightBatch];
+  int64_t ld_wq[kWeightBatch];
+  int kb[kWeightBatch];
+  int block_begin[kWeightBatch];  // first grid block of matrix i (prefix sum of block counts)
+  int count;
+};
+hipError_t launch_quant_weight_batch(const WeightBatch& b, int total_blocks, hipStream_t stream);
 hipError_t launch_quant_act(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x, uint8_t* xq,
                             int64_t ld_xq, float* sa, hipStream_t stream);
 hipError_t launch_encode(const float* v, int64_t n, uint8_t* out, hipStream_t stream);

@@ -15,12 +15,14 @@ namespace fp8rl {
 // (t & 15) of rows (t >> 4) + 16 i, i = 0..7, so each load instruction of a wave reads four
 // 256-byte row segments and the block (32 KiB of bf16) lives in registers between the amax pass
 // and the encode pass: HBM traffic is one read of W and one write of Wq.
+//
+// One launch covers a batch of up to kWeightBatch matrices (a whole layer or model): the grid
+// is the concatenation of every matrix's blocks, and each workgroup finds its matrix from the
+// block prefix sums passed by value.
 // ---------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void quant_weight_blk128_kernel(
-    const uint16_t* __restrict__ w, int64_t ld_w, uint8_t* __restrict__ wq, int64_t ld_wq,
-    float* __restrict__ sw, int KB) {
-  const int bid = blockIdx.x;
-  const int bi = bid / KB, bj = bid - (bid / KB) * KB;
+__device__ __forceinline__ void quant_weight_block(const uint16_t* __restrict__ w, int64_t ld_w,
+                                                   uint8_t* __restrict__ wq, int64_t ld_wq,
+                                                   float* __restrict__ sw_out, int bi, int bj) {
   const int t = threadIdx.x;
   const int c = t & 15;
   const int r0 = t >> 4;
@@ -46,7 +48,7 @@ __global__ __launch_bounds__(256) void quant_weight_blk128_kernel(
 
   const float S = scale_from_amax_bits(m);
   const double r = recip_f64(S);
-  if (t == 0) sw[bid] = S;
+  if (t == 0) *sw_out = S;
 
   uint8_t* dst = wq + (int64_t)(bi * kBlock + r0) * ld_wq + bj * kBlock + c * 8;
 #pragma unroll
@@ -54,24 +56,34 @@ __global__ __launch_bounds__(256) void quant_weight_blk128_kernel(
     __builtin_nontemporal_store(quant8(v[i], r), reinterpret_cast<u32x2*>(dst + (int64_t)(16 * i) * ld_wq));
 }
 
+__global__ __launch_bounds__(256) void quant_weight_blk128_kernel(WeightBatch b) {
+  const int bid = blockIdx.x;
+  int t = 0;
+#pragma unroll 1
+  while (t + 1 < b.count && bid >= b.block_begin[t + 1]) ++t;  // uniform: bid is uniform
+  const int local = bid - b.block_begin[t];
+  const int KB = b.kb[t];
+  const int bi = local / KB, bj = local - (local / KB) * KB;
+  quant_weight_block(b.w[t], b.ld_w[t], b.wq[t], b.ld_wq[t], b.sw[t] + local, bi, bj);
+}
+
 // ---------------------------------------------------------------------------------------------
 // Activations: each 16-lane DPP row of a wave owns one 1x128 group (8 bf16 per lane, one 16-byte
 // load), reduces its amax with four DPP steps and writes 128 codes plus one scale. A workgroup
-// covers 16 groups per step and kActSteps steps, with all loads issued before any reduction.
+// covers 16 groups per step and STEPS steps, with all loads issued before any reduction (4 steps
+// for large inputs; 1 for small ones, which then spread over 4x more workgroups and CUs).
 // Group g is (row g / KB, slice g % KB), so neighbouring rows of a wave read neighbouring slices.
 // ---------------------------------------------------------------------------------------------
-constexpr int kActSteps = 4;
-constexpr int kActGroupsPerWG = 16 * kActSteps;
-
+template <int STEPS>
 __global__ __launch_bounds__(256) void quant_act_tok128_kernel(
     const uint16_t* __restrict__ x, int64_t ld_x, uint8_t* __restrict__ xq, int64_t ld_xq,
     float* __restrict__ sa, int KB, int64_t total_groups) {
   const int lane16 = threadIdx.x & 15;
-  const int64_t g0 = (int64_t)blockIdx.x * kActGroupsPerWG + (threadIdx.x >> 4);
+  const int64_t g0 = (int64_t)blockIdx.x * (16 * STEPS) + (threadIdx.x >> 4);
 
-  u32x4 v[kActSteps];
+  u32x4 v[STEPS];
 #pragma unroll
-  for (int s = 0; s < kActSteps; ++s) {
+  for (int s = 0; s < STEPS; ++s) {
     const int64_t g = g0 + 16 * s;
     v[s] = u32x4{0u, 0u, 0u, 0u};
     if (g < total_groups) {
@@ -81,7 +93,7 @@ __global__ __launch_bounds__(256) void quant_act_tok128_kernel(
     }
   }
 #pragma unroll
-  for (int s = 0; s < kActSteps; ++s) {
+  for (int s = 0; s < STEPS; ++s) {
     const int64_t g = g0 + 16 * s;
     // every lane of the row takes part in the reduction, whether or not its group exists
     const uint32_t m = row16_max_u32(hmax_u16(amax8_pk(v[s])));
@@ -137,12 +149,9 @@ __global__ __launch_bounds__(256) void encode_e4m3_kernel(const float* __restric
 // ---------------------------------------------------------------------------------------------
 // Launchers (arguments already validated by the C ABI layer).
 // ---------------------------------------------------------------------------------------------
-hipError_t launch_quant_weight(const uint16_t* w, int64_t N, int64_t K, int64_t ld_w, uint8_t* wq,
-                               int64_t ld_wq, float* sw, hipStream_t stream) {
-  const int KB = (int)(K / kBlock);
-  const int64_t blocks = (N / kBlock) * KB;
-  hipLaunchKernelGGL(quant_weight_blk128_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, w,
-                     ld_w, wq, ld_wq, sw, KB);
+hipError_t launch_quant_weight_batch(const WeightBatch& b, int total_blocks, hipStream_t stream) {
+  hipLaunchKernelGGL(quant_weight_blk128_kernel, dim3((unsigned)total_blocks), dim3(256), 0, stream,
+                     b);
   return hipGetLastError();
 }
 
@@ -150,9 +159,15 @@ hipError_t launch_quant_act(const uint16_t* x, int64_t M, int64_t K, int64_t ld_
                             int64_t ld_xq, float* sa, hipStream_t stream) {
   const int KB = (int)(K / kBlock);
   const int64_t groups = M * KB;
-  const int64_t wgs = (groups + kActGroupsPerWG - 1) / kActGroupsPerWG;
-  hipLaunchKernelGGL(quant_act_tok128_kernel, dim3((unsigned)wgs), dim3(256), 0, stream, x, ld_x,
-                     xq, ld_xq, sa, KB, groups);
+  if (groups >= int64_t{64} * 1024) {  // >= 1024 workgroups even at 4 steps each
+    const int64_t wgs = (groups + 63) / 64;
+    hipLaunchKernelGGL(quant_act_tok128_kernel<4>, dim3((unsigned)wgs), dim3(256), 0, stream, x,
+                       ld_x, xq, ld_xq, sa, KB, groups);
+  } else {
+    const int64_t wgs = (groups + 15) / 16;
+    hipLaunchKernelGGL(quant_act_tok128_kernel<1>, dim3((unsigned)wgs), dim3(256), 0, stream, x,
+                       ld_x, xq, ld_xq, sa, KB, groups);
+  }
   return hipGetLastError();
 }
 

@@ -108,6 +108,24 @@ int fp8rl_encode_e4m3_f32(const float* v, int64_t n, uint8_t* out, void* stream)
 int fp8rl_quant_weight_blk128(const uint16_t* w, int64_t N, int64_t K, int64_t ld_w, uint8_t* wq,
                               int64_t ld_wq, float* sw, void* stream);
 
+/* One weight matrix of a batched re-quantization (all pointers device, same rules as above). */
+typedef struct {
+  const uint16_t* w; /* bf16 W[N][ld_w] */
+  uint8_t* wq;       /* uint8 Wq[N][ld_wq] */
+  float* sw;         /* float32 sw[N/128][K/128] */
+  int64_t N, K, ld_w, ld_wq;
+} fp8rl_weight_desc;
+
+/*
+ * Batched weight re-quantization: the same operation as fp8rl_quant_weight_blk128 applied to
+ * each of `count` matrices (e.g. every linear of a layer or a model, the per-step weight sync of
+ * [FP8RL, section 1]), enqueued as ceil(count / 32) kernel launches instead of `count`.
+ *   descs : HOST array of `count` descriptors; read during the call only.
+ * Every descriptor is validated before anything is enqueued; the first failing one decides the
+ * returned status and nothing is launched. Matrices with N == 0 or K == 0 are skipped.
+ */
+int fp8rl_quant_weight_blk128_batched(const fp8rl_weight_desc* descs, int32_t count, void* stream);
+
 /*
  * Dynamic activation quantization, 1x128 groups per token row [NEMO, Table 1; FP8RL, section 1;
  * UFP8, quick-read].  For row m and group g (columns 128g..128g+127 of X[M][K]):

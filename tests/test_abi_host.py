@@ -32,7 +32,7 @@ def L():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 8
+    assert len(names) == 9
     for n in names:
         assert hasattr(L, n), n
     assert sorted(_lib.EXPORTED) == names
@@ -59,6 +59,20 @@ def test_quant_weight_validation(L):
     assert f(A, 128, 128, 132, A, 128, A, None) == EALIGN  # 264-byte pitch
     assert f(A, 128, 128, 128, A, 136, A, None) == EALIGN
     assert f(A, 128, 128, 128, A, 128, A + 2, None) == EALIGN
+
+
+def test_quant_weight_batched_validation(L):
+    f = L.fp8rl_quant_weight_blk128_batched
+    D = _lib.WeightDesc
+    ok = D(A, A, A, 128, 256, 256, 256)
+    arr = (D * 3)(ok, D(A, A, A, 0, 256, 256, 256), D(A, A, A + 2, 128, 256, 256, 256))
+    assert f(arr, 0, None) == OK
+    assert f(None, 2, None) == ENULL
+    assert f(arr, -1, None) == EARG
+    assert f(arr, 3, None) == EALIGN  # the third descriptor fails: nothing is launched
+    bad = (D * 2)(ok, D(A, A, A, 100, 256, 256, 256))
+    assert f(bad, 2, None) == ESHAPE
+    assert f((D * 1)(D(A, None, A, 128, 128, 128, 128)), 1, None) == ENULL
 
 
 def test_quant_act_validation(L):

@@ -119,3 +119,38 @@ def test_zero_rows_is_a_noop_and_deterministic():
     a2, s2 = fq.quant_weight(w)
     torch.cuda.synchronize()
     assert torch.equal(a1, a2) and torch.equal(s1, s2)
+
+
+def test_batched_weights_one_launch_per_32():
+    """40 matrices (more than one launch) plus empty ones through the batched entry point."""
+    shapes = [(128 * (1 + i % 3), 128 * (1 + (i * 7) % 4)) for i in range(40)]
+    ws = [synth.weight_bf16(N, K, seed=500 + i, outlier_frac=0.001).cuda()
+          for i, (N, K) in enumerate(shapes)]
+    wqs = [torch.empty((N, K), dtype=torch.uint8, device="cuda") for N, K in shapes]
+    sws = [torch.empty((N // 128, K // 128), dtype=torch.float32, device="cuda") for N, K in shapes]
+    empty_w = torch.empty((0, 256), dtype=torch.bfloat16, device="cuda")
+    empty_q = torch.empty((0, 256), dtype=torch.uint8, device="cuda")
+    empty_s = torch.empty((0, 2), dtype=torch.float32, device="cuda")
+    fq.quant_weights(ws[:20] + [empty_w] + ws[20:], wqs[:20] + [empty_q] + wqs[20:],
+                     sws[:20] + [empty_s] + sws[20:])
+    torch.cuda.synchronize()
+    for i, w in enumerate(ws):
+        rq, rs = oq.quant_weight_blk128(bits16(w))
+        assert np.array_equal(wqs[i].cpu().numpy(), rq), i
+        assert np.array_equal(sws[i].cpu().numpy().view(np.uint32), rs.view(np.uint32)), i
+
+
+def test_batched_qwen3_block_matches_single_calls():
+    ws = [synth.weight_bf16(N, K, seed=synth.seed_of(2, i), outlier_frac=0.001).cuda()
+          for i, (_, N, K) in enumerate(synth.DENSE_LINEARS_QWEN3_8B)]
+    wqs = [torch.empty(w.shape, dtype=torch.uint8, device="cuda") for w in ws]
+    sws = [torch.empty((w.shape[0] // 128, w.shape[1] // 128), dtype=torch.float32, device="cuda")
+           for w in ws]
+    fq.quant_weights(ws, wqs, sws)
+    for i, w in enumerate(ws):
+        a, b = fq.quant_weight(w)
+        torch.cuda.synchronize()
+        assert torch.equal(a, wqs[i]) and torch.equal(b, sws[i])
+    # and against the oracle for the smallest one
+    rq, rs = oq.quant_weight_blk128(bits16(ws[1]))
+    assert np.array_equal(wqs[1].cpu().numpy(), rq)
