@@ -1,7 +1,7 @@
 // C ABI entry points: argument validation (host only, before any HIP call) and dispatch.
 #include <stdint.h>
 
-#include "../../include/fp8rl.h"
+#include "fp8rl.h"
 #include "launch.hpp"
 
 namespace {

@@ -13,8 +13,11 @@
 // copied global -> registers -> LDS with a double buffer (the next slice's global loads are in
 // flight while the current slice is multiplied), the activation scales of the slice go to LDS
 // beside them, and the weight scale of a wave's 128-column block is a wave-uniform load.
-// LDS rows are 128 bytes; the 16-byte chunk c of row r is stored at chunk c ^ (r & 7), so the
-// fragment reads of 8 consecutive rows at the same k hit 8 different bank groups.
+// LDS rows are 128 bytes; the 16-byte chunk c of row r is stored at chunk c ^ swz(r) with
+// swz(r) = (r & 7) ^ ((r >> 3) & 1). A fragment read has 16 consecutive rows read the same
+// logical chunk: any 8 consecutive rows then hit 8 different 16-byte bank groups of a 128-byte
+// row, and the 8 even (odd) rows of 16 hit 8 different groups too, so the read is free of bank
+// conflicts whether the LDS serves 8 lanes (32 banks) or 16 lanes (64 banks) per cycle.
 #include <atomic>
 
 #include "device_common.hpp"
@@ -70,6 +73,8 @@ struct Prefetch {
   float s;
 };
 
+__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+
 __device__ __forceinline__ uint4 ldg16(const uint8_t* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
@@ -100,12 +105,12 @@ __device__ __forceinline__ void store_slice(const Prefetch<T>& st, uint8_t* stag
 #pragma unroll
   for (int i = 0; i < T::A_LOADS; ++i) {
     const int c = tid + i * T::NT, row = c >> 3, cc = c & 7;
-    *reinterpret_cast<uint4*>(sA + row * 128 + ((cc ^ (row & 7)) << 4)) = st.a[i];
+    *reinterpret_cast<uint4*>(sA + row * 128 + ((cc ^ swz(row)) << 4)) = st.a[i];
   }
 #pragma unroll
   for (int i = 0; i < T::B_LOADS; ++i) {
     const int c = tid + i * T::NT, row = c >> 3, cc = c & 7;
-    *reinterpret_cast<uint4*>(sB + row * 128 + ((cc ^ (row & 7)) << 4)) = st.b[i];
+    *reinterpret_cast<uint4*>(sB + row * 128 + ((cc ^ swz(row)) << 4)) = st.b[i];
   }
   if (tid < T::BM) sS[tid] = st.s;
 }
@@ -115,7 +120,7 @@ __device__ __forceinline__ void store_slice(const Prefetch<T>& st, uint8_t* stag
 // every k of the slice exactly once.
 __device__ __forceinline__ v8i load_frag(const uint8_t* s, int row, int kq) {
   const uint8_t* p = s + row * 128;
-  const int sw = row & 7;
+  const int sw = swz(row);
   const uint4 lo = *reinterpret_cast<const uint4*>(p + (((2 * kq) ^ sw) << 4));
   const uint4 hi = *reinterpret_cast<const uint4*>(p + (((2 * kq + 1) ^ sw) << 4));
   v8i f;
@@ -291,6 +296,231 @@ __global__ __launch_bounds__(T::NT) void gemm_kernel(GemmArgs p) {
   store_tile<T>(p, m0, m_valid, n0, split, acc);
 }
 
+// ---------------------------------------------------------------------------------------------
+// Large-M GEMM. Workgroup tiles of BM x BN (256 x 256 or 256 x 128) split over waves of
+// WM x WN (128 x 64: 8 MFMA row tiles by 4 column tiles), so every LDS byte a wave reads feeds
+// 1.5x (vs 64 x 64) more matrix-core work. K slices reach LDS by direct global->LDS DMA
+// (global_load_lds_dwordx4: each lane's 16 bytes land at the wave's base + 16 * lane), so
+// staging costs no registers; the 16-byte chunk order inside each 128-byte row is the same XOR
+// swizzle as above, applied on the global side. Two LDS stages as two separate arrays, with the
+// K loop unrolled by two so that the stage each instruction touches is known statically (the
+// compiler then does not have to wait for the in-flight DMA into the other stage before reading
+// this one). Per K slice: wait for this wave's DMA, one barrier, start the next slice's DMA into
+// the other stage, then multiply out of this stage.
+// ---------------------------------------------------------------------------------------------
+template <int BM_, int BN_, int WM_, int WN_>
+struct Big {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+  static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
+  static constexpr int WAVES = WAVES_M * WAVES_N;
+  static constexpr int NT = WAVES * 64;
+  static constexpr int TM = WM / 16, TN = WN / 16;
+  static constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128, S_BYTES = BM * 4;
+  static constexpr int STAGE_BYTES = A_BYTES + B_BYTES + S_BYTES;
+  static constexpr int A_PER_WAVE = BM / 8 / WAVES;  // one DMA instruction moves 8 rows (1 KiB)
+  static constexpr int B_PER_WAVE = BN / 8 / WAVES;
+  static constexpr int S_ROWS = BM / WAVES;  // activation scales loaded per wave
+  static_assert(A_PER_WAVE * 8 * WAVES == BM && B_PER_WAVE * 8 * WAVES == BN, "DMA split");
+  static_assert(S_ROWS <= 64 && S_ROWS * WAVES == BM, "scale DMA split");
+  static_assert(128 % WN == 0, "a wave's columns must share one weight-scale block");
+};
+
+constexpr int kMaxSlices = 128;  // K <= 16384 on the large-tile path
+using BigWide = Big<256, 256, 128, 64>;  // 8 waves
+using BigNarrow = Big<256, 128, 128, 64>;  // 4 waves
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Global -> LDS DMA of 16 (or 4) bytes per lane from base + off (off a per-lane 32-bit byte
+// offset, base wave-uniform): lane l's bytes land at lds + 16 * l (4 * l); `lds` must be the same
+// for the whole wave (it goes to M0). Written as inline assembly so that the compiler does not
+// track these loads: it would otherwise wait for every DMA in flight before any later LDS read,
+// even of the other stage. Completion is waited for explicitly (wait_dma_and_barrier) before the
+// stage is read.
+__device__ __forceinline__ uint32_t lds_offset(const uint8_t* p) {
+  return (uint32_t)(uintptr_t)(lds_ptr_t)p;
+}
+__device__ __forceinline__ void dma16(const void* base, uint32_t off, const uint8_t* lds) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_offset(lds));
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :: "s"(m0v), "v"(off), "s"(base) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* base, uint32_t off, const uint8_t* lds) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_offset(lds));
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2"
+               :: "s"(m0v), "v"(off), "s"(base) : "memory", "m0");
+}
+
+// Per-lane byte offsets of this lane's DMA sources within a K slice (computed once per tile).
+// Rows past the end of the matrix are clamped to its last row: they load valid memory whose
+// products only reach output rows / columns that are never stored.
+template <class T>
+struct DmaPlan {
+  uint32_t a[T::A_PER_WAVE];
+  uint32_t b[T::B_PER_WAVE];
+  uint32_t s;
+};
+
+template <class T>
+__device__ __forceinline__ DmaPlan<T> make_dma_plan(int m_valid, int n_valid, int K, int KB,
+                                                    int wave, int lane) {
+  DmaPlan<T> d;
+  const int sub = lane >> 3;
+  // lane l fills LDS slot l & 7 of tile row 8 * ins + (l >> 3): it loads the logical chunk that
+  // the swizzle puts there (the row used for the swizzle is the unclamped tile row)
+#pragma unroll
+  for (int t = 0; t < T::A_PER_WAVE; ++t) {
+    const int trow = (t * T::WAVES + wave) * 8 + sub;
+    const int cc = (lane & 7) ^ swz(trow);
+    d.a[t] = (uint32_t)(min(trow, m_valid - 1) * K + cc * 16);
+  }
+#pragma unroll
+  for (int t = 0; t < T::B_PER_WAVE; ++t) {
+    const int trow = (t * T::WAVES + wave) * 8 + sub;
+    const int cc = (lane & 7) ^ swz(trow);
+    d.b[t] = (uint32_t)(min(trow, n_valid - 1) * K + cc * 16);
+  }
+  d.s = (uint32_t)(min(wave * T::S_ROWS + lane, m_valid - 1) * KB * 4);
+  return d;
+}
+
+template <class T>
+__device__ __forceinline__ void dma_slice(uint8_t* stage, const DmaPlan<T>& d, const uint8_t* A,
+                                          const uint8_t* B, const float* SA, int kb, int wave,
+                                          int lane) {
+  const uint8_t* a = A + (int64_t)kb * 128;
+  const uint8_t* b = B + (int64_t)kb * 128;
+  // the scale DMA goes first: anything the compiler has to wait for before computing its
+  // operands (e.g. a reloaded register) then does not wait on this slice's tile DMA as well
+  if (lane < T::S_ROWS)
+    dma4(SA + kb, d.s, stage + T::A_BYTES + T::B_BYTES + wave * T::S_ROWS * 4);
+#pragma unroll
+  for (int t = 0; t < T::A_PER_WAVE; ++t) dma16(a, d.a[t], stage + (t * T::WAVES + wave) * 1024);
+#pragma unroll
+  for (int t = 0; t < T::B_PER_WAVE; ++t)
+    dma16(b, d.b[t], stage + T::A_BYTES + (t * T::WAVES + wave) * 1024);
+}
+
+// Wait for this wave's outstanding DMA and LDS operations, then a workgroup barrier. The memory
+// clobber keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void wait_dma_and_barrier() {
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// One K slice of a wave's WM x WN tile, software-pipelined by row tile: the matrix-core sums of
+// row tile i are issued interleaved with the scale-and-accumulate FMAs of row tile i - 1 (whose
+// sums finished long before), so the VALU works while the matrix core runs and no FMA waits on
+// the sum it consumes; the next row tile's operands are read from LDS meanwhile. Scheduling
+// fences keep the compiler from regrouping the FMAs next to the sums they depend on.
+template <class T, bool PRECISE>
+__device__ __forceinline__ void mma_slice_big(const uint8_t* stage, float swv, int wm, int wn,
+                                              int lane, v4f (&acc)[T::TM][T::TN]) {
+  const uint8_t* sA = stage;
+  const uint8_t* sB = stage + T::A_BYTES;
+  const float* sS = reinterpret_cast<const float*>(stage + T::A_BYTES + T::B_BYTES);
+  const int r16 = lane & 15, kq = lane >> 4;
+  v8i bf[T::TN];
+#pragma unroll
+  for (int j = 0; j < T::TN; ++j) bf[j] = load_frag(sB, wn * T::WN + j * 16 + r16, kq);
+  v8i af = load_frag(sA, wm * T::WM + r16, kq);
+  v4f sc = *reinterpret_cast<const v4f*>(sS + wm * T::WM + 4 * kq) * swv;
+  v4f p_prev[T::TN];
+  v4f sc_prev = sc;
+#pragma unroll
+  for (int i = 0; i < T::TM; ++i) {
+    v8i af_next = af;
+    v4f sn = sc;
+    if (i + 1 < T::TM) {
+      af_next = load_frag(sA, wm * T::WM + (i + 1) * 16 + r16, kq);
+      sn = *reinterpret_cast<const v4f*>(sS + wm * T::WM + (i + 1) * 16 + 4 * kq);
+    }
+    v4f p_cur[T::TN];
+#pragma unroll
+    for (int j = 0; j < T::TN; ++j) {
+      p_cur[j] = slice_product<PRECISE>(af, bf[j]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (i > 0) acc[i - 1][j] += p_prev[j] * sc_prev;
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int j = 0; j < T::TN; ++j) p_prev[j] = p_cur[j];
+    sc_prev = sc;
+    af = af_next;
+    sc = sn * swv;
+  }
+#pragma unroll
+  for (int j = 0; j < T::TN; ++j) acc[T::TM - 1][j] += p_prev[j] * sc_prev;
+}
+
+template <class T, bool PRECISE>
+__global__ __launch_bounds__(T::NT) void gemm_big_kernel(GemmArgs p) {
+  __shared__ __attribute__((aligned(16))) uint8_t stage0[T::STAGE_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t stage1[T::STAGE_BYTES];
+  // weight scales of the tile's (up to two) 128-column blocks for every K slice, read once
+  __shared__ float sw_s[(T::BN + 127) / 128][kMaxSlices];
+  const int tiles_m = (p.M + T::BM - 1) / T::BM;
+  const int tiles_n = (p.N + T::BN - 1) / T::BN;
+  int tm, tn;
+  tile_coords(blockIdx.x, tiles_m * tiles_n, tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * T::BM, n0 = tn * T::BN;
+  const int m_valid = min(T::BM, p.M - m0);
+  const int n_valid = min(T::BN, p.N - n0);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / T::WAVES_N, wn = wave % T::WAVES_N;
+  const uint8_t* A = p.xq + (int64_t)m0 * p.K;
+  const float* SA = p.sa + (int64_t)m0 * p.KB;
+  const uint8_t* B = p.wq + (int64_t)n0 * p.K;
+  const int KB = p.KB;
+  // a wave whose columns are all past N still runs (it takes part in the DMA and barriers) on a
+  // clamped scale row; its results are not stored
+  constexpr int NBLK = (T::BN + 127) / 128;
+  for (int e = tid; e < NBLK * KB; e += T::NT) {
+    const int b = e / KB, k = e - (e / KB) * KB;
+    const int nb = min((n0 >> 7) + b, p.N / 128 - 1);
+    sw_s[b][k] = p.sw[(int64_t)nb * KB + k];
+  }
+  const float* swrow = sw_s[((n0 + wn * T::WN) >> 7) - (n0 >> 7)];
+
+  v4f acc[T::TM][T::TN];
+#pragma unroll
+  for (int i = 0; i < T::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < T::TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  const DmaPlan<T> dp = make_dma_plan<T>(m_valid, n_valid, p.K, KB, wave, lane);
+  dma_slice<T>(stage0, dp, A, B, SA, 0, wave, lane);
+  for (int kb = 0; kb < KB; kb += 2) {
+    wait_dma_and_barrier();
+    if (kb + 1 < KB) dma_slice<T>(stage1, dp, A, B, SA, kb + 1, wave, lane);
+    mma_slice_big<T, PRECISE>(stage0, swrow[kb], wm, wn, lane, acc);
+    if (kb + 1 >= KB) break;
+    wait_dma_and_barrier();
+    if (kb + 2 < KB) dma_slice<T>(stage0, dp, A, B, SA, kb + 2, wave, lane);
+    mma_slice_big<T, PRECISE>(stage1, swrow[kb + 1], wm, wn, lane, acc);
+  }
+
+  const int r16 = lane & 15, kq = lane >> 4;
+#pragma unroll
+  for (int i = 0; i < T::TM; ++i) {
+#pragma unroll
+    for (int j = 0; j < T::TN; ++j) {
+      const int c = wn * T::WN + j * 16 + r16;
+      if (c >= n_valid) continue;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int r = wm * T::WM + i * 16 + 4 * kq + v;
+        if (r >= m_valid) continue;
+        const int64_t off = (int64_t)(m0 + r) * p.ldy + n0 + c;
+        if (p.out_f32)
+          reinterpret_cast<float*>(p.y)[off] = acc[i][j][v];
+        else
+          reinterpret_cast<uint16_t*>(p.y)[off] = f32_to_bf16_rne(acc[i][j][v]);
+      }
+    }
+  }
+}
+
 // Deterministic split-K reduction: partials are summed in split order.
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ ws,
                                                             int splits, int64_t M, int N, void* y,
@@ -381,7 +611,7 @@ __global__ __launch_bounds__(T::NT) void grouped_gemm_kernel(GemmArgs p) {
 // ---------------------------------------------------------------------------------------------
 namespace {
 
-constexpr int kCfgLarge = 0, kCfgSmall = 1;
+constexpr int kCfgLarge = 0, kCfgSmall = 1, kCfgBigWide = 2, kCfgBigNarrow = 3;
 constexpr int kTargetWorkgroups = 512;  // two per CU on 256 CUs
 constexpr int kMinSlicesPerSplit = 4;
 
@@ -403,6 +633,16 @@ hipError_t ensure_lds(std::atomic<uint64_t>& done, const void* kernel, int bytes
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
   GemmPlan pl{};
   const int64_t KB = K / 128;
+  if (M >= 1024 && KB <= kMaxSlices) {
+    const int64_t wide_tiles = ((M + 255) / 256) * ((N + 255) / 256);
+    pl.cfg = wide_tiles >= 240 ? kCfgBigWide : kCfgBigNarrow;
+    pl.bm = 256;
+    pl.bn = pl.cfg == kCfgBigWide ? 256 : 128;
+    pl.splits = 1;
+    pl.kb_per_split = (int)KB;
+    pl.workspace_bytes = 0;
+    return pl;
+  }
   if (M >= 512) {
     pl.cfg = kCfgLarge;
     pl.bm = TileLarge::BM;
@@ -441,6 +681,15 @@ GemmPlan plan_grouped_gemm(int64_t M_total, int64_t N, int64_t K, int32_t E) {
 }
 
 template <class T, bool PRECISE>
+static hipError_t launch_big(const GemmArgs& a, hipStream_t stream) {
+  const int tiles_m = (a.M + T::BM - 1) / T::BM;
+  const int tiles_n = (a.N + T::BN - 1) / T::BN;
+  hipLaunchKernelGGL((gemm_big_kernel<T, PRECISE>), dim3((unsigned)(tiles_m * tiles_n)), dim3(T::NT),
+                     0, stream, a);
+  return hipGetLastError();
+}
+
+template <class T, bool PRECISE>
 static hipError_t launch_dense(const GemmArgs& a, const GemmPlan& pl, hipStream_t stream) {
   static std::atomic<uint64_t> lds_done{0};
   hipError_t e = ensure_lds(lds_done, (const void*)gemm_kernel<T, PRECISE>, T::LDS_BYTES);
@@ -471,6 +720,11 @@ hipError_t launch_gemm(const uint8_t* xq, const float* sa, const uint8_t* wq, co
   a.splits = pl.splits;
   a.kb_per_split = pl.kb_per_split;
   hipError_t e;
+  // the f16 form needs more registers per wave than the 8-wave tile leaves: 4-wave tiles
+  if (pl.cfg == kCfgBigWide && !precise) return launch_big<BigWide, false>(a, stream);
+  if (pl.cfg == kCfgBigNarrow || pl.cfg == kCfgBigWide)
+    return precise ? launch_big<BigNarrow, true>(a, stream)
+                   : launch_big<BigNarrow, false>(a, stream);
   if (pl.cfg == kCfgLarge)
     e = precise ? launch_dense<TileLarge, true>(a, pl, stream)
                 : launch_dense<TileLarge, false>(a, pl, stream);

@@ -76,7 +76,7 @@ def test_small_m_shapes(M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(512, 512, 512), (1000, 1024, 2048), (2048 + 37, 768, 1536),
-                                   (4096, 4096, 4096)])
+                                   (4096, 4096, 4096), (8192 + 77, 1920, 1024), (1024, 384, 256)])
 def test_large_m_shapes(M, N, K):
     run_and_check(*quantized_operands(M, N, K, 2000 + M + N + K), f"large-M {M}x{N}x{K}")
 
