@@ -37,6 +37,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0
 FP8_PEAK_TFLOPS = 5000.0
 ROTATE_BYTES = 1 << 30
+COPY_BYTES = 1 << 30
 
 
 def parse():
@@ -49,6 +50,9 @@ def parse():
                              "llama31-8b-weight-sync", "qwen3-30b-a3b-moe"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run one plain 1 GiB device copy (a known-size reference for the "
+                         "FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
 
 
@@ -184,6 +188,31 @@ class DenseBlock:
         return a.elapsed_time(b) / reps
 
 
+# ---------------------------------------------------------------------------- measured traffic
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "quant_weight_blk128__qwen3-8b-decode-step.traffic.txt")
+
+
+def measured_traffic():
+    """HBM bytes per launch of the weight re-quantization kernel from the committed FETCH_SIZE /
+    WRITE_SIZE counter runs (scaled by a 1 GiB copy), or None if the kernel's sources have changed
+    since the counters were taken."""
+    import hashlib
+
+    try:
+        with open(TRAFFIC_FILE) as f:
+            d = json.load(f)
+        h = hashlib.sha256()
+        for rel in d["source_files"]:
+            with open(os.path.join(ROOT, rel), "rb") as f:
+                h.update(f.read())
+        if h.hexdigest() != d["source_sha256"]:
+            return None
+        return float(d["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 # ------------------------------------------------------------------------------ cpu baseline
 
 
@@ -244,6 +273,13 @@ def main():
 
     torch.cuda.set_device(0)
     fq.lib()
+    if args.copy_calibration:
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     dev_name = torch.cuda.get_device_name(0)
     props = torch.cuda.get_device_properties(0)
 
@@ -289,7 +325,8 @@ def main():
         parts["quant_weight_batched"] = dict(r, frac_hbm=r["gbs"] / HBM_PEAK_GBS)
         roof = {"kernel": "quant_weight_blk128_kernel", "bound": "hbm", "achieved": r["gbs"],
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": r["gbs"] / HBM_PEAK_GBS,
-                "traffic": None, "avg_launch_us": r["avg_us"],
+                "traffic": measured_traffic(), "avg_launch_us": r["avg_us"],
+                "algorithmic_bytes_per_launch": blk.bytes_w,
                 "per_unit": "3 B per weight element + 4 B per 128x128 block",
                 "units_per_launch": "all 7 weights of the block (192,937,984 elements, 11,776 blocks)"}
     else:
