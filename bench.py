@@ -131,7 +131,7 @@ class DenseBlock:
         self.ws = []
         for _, N, K in linears:
             nb = fq.fp8rl_workspace_bytes(fq.FP8RL_OP_GEMM, M, N, K)
-            self.ws.append(torch.empty(max(nb, 16), dtype=torch.uint8, device=dev))
+            self.ws.append(fq.new_workspace(nb, dev))
         for c in range(self.copies):  # every copy holds valid codes before the first replay
             self.requant_step(c)
         self.it = 0

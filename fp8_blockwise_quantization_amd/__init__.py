@@ -20,9 +20,11 @@ from ._lib import (  # noqa: F401
     fp8rl_quant_act_tok128,
     fp8rl_quant_weight_blk128,
     fp8rl_quant_weight_blk128_batched,
+    WORKSPACE_HEADER_BYTES,
     weight_descs,
     fp8rl_workspace_bytes,
     lib,
+    new_workspace,
 )
 
 # Short aliases.

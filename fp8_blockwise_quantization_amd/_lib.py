@@ -207,6 +207,17 @@ def fp8rl_workspace_bytes(op: int, M: int, N: int, K: int, E: int = 0) -> int:
     return int(lib().fp8rl_workspace_bytes(op, M, N, K, E))
 
 
+WORKSPACE_HEADER_BYTES = 4096  # FP8RL_WORKSPACE_HEADER_BYTES: counters that must start at zero
+
+
+def new_workspace(nbytes: int, device) -> torch.Tensor:
+    """A GEMM workspace of at least ``nbytes`` whose counter header is zero (ready for any call;
+    the library leaves the header zero after each call)."""
+    ws = torch.empty(max(int(nbytes), WORKSPACE_HEADER_BYTES), dtype=torch.uint8, device=device)
+    ws[:WORKSPACE_HEADER_BYTES].zero_()
+    return ws
+
+
 def _accum_code(accum, out_dtype) -> int:
     """None picks FP8 matrix-core sums for bf16 output and f16 (float32-grade) ones for float32."""
     if accum is None:
@@ -242,7 +253,7 @@ def fp8rl_gemm_w8a8_blockscaled(xq, sa, wq, sw, out_dtype=torch.bfloat16, y=None
     ld_y = _rows(y, "y", y.dtype)
     need = fp8rl_workspace_bytes(FP8RL_OP_GEMM, M, N, K)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=xq.device)
+        workspace = new_workspace(need, xq.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().fp8rl_gemm_w8a8_blockscaled(_ptr(xq), _ptr(sa), _ptr(wq), _ptr(sw), M, N, K,
                                              _ptr(y), _out_code(y.dtype), ld_y,
@@ -269,7 +280,7 @@ def fp8rl_grouped_gemm_w8a8(xq, sa, wq, sw, expert_offsets, out_dtype=torch.bflo
     _dense(y, "y", y.dtype)
     need = fp8rl_workspace_bytes(FP8RL_OP_GROUPED_GEMM, M, N, K, E)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=xq.device)
+        workspace = new_workspace(need, xq.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().fp8rl_grouped_gemm_w8a8(_ptr(xq), _ptr(sa), _ptr(wq), _ptr(sw),
                                          _ptr(expert_offsets), E, M, N, K, _ptr(y),

@@ -57,7 +57,8 @@ struct GemmArgs {
   void* y;
   int64_t ldy;
   int out_f32;
-  float* ws;  // split-K partials [splits][M][N], or null
+  float* ws;      // split-K partials (layout per kernel), or null
+  int* counters;  // arrival counters of the decode path's output tiles, zero between calls
   int splits, kb_per_split;
   // grouped form
   const int32_t* offsets;
@@ -521,6 +522,208 @@ __global__ __launch_bounds__(T::NT) void gemm_big_kernel(GemmArgs p) {
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// Decode-sized GEMM (M <= 64): weight streaming. Workgroup (t, s) of 4 waves computes output
+// tile t (64 columns, 16 per wave) over K slices [s L, (s + 1) L) (L divides KB). Each wave
+// keeps the weight fragments of the next D slices in flight in registers (a ring unrolled D
+// times, so every load and wait is visible to the compiler), the activation rows of the same
+// slices are staged through registers into a double-buffered LDS tile shared by the waves, and
+// each slice is multiplied as soon as it has landed. Every weight byte is read from HBM once,
+// and 4 waves x D slices x 2 KiB per CU-resident workgroup keep the weight stream saturated.
+//
+// K splits (s > 0 exist when KB / L > 1): each split stores its float32 partial with
+// agent-scope stores (written through to the level all XCDs share) into slot (t, s) of the
+// workspace and bumps the tile's arrival counter; the split that arrives last reads the
+// partials back with agent-scope loads, sums them in split order -- the same bits whatever the
+// arrival order -- writes Y and re-arms the counter for the next call.
+// ---------------------------------------------------------------------------------------------
+template <int MT_, int R_>
+struct Dec {
+  static constexpr int MT = MT_;  // 16-row MFMA blocks covering M
+  static constexpr int R = R_;    // K slices per round; two rounds are in flight
+  static constexpr int WAVES = 4, NT = 256;
+  static constexpr int BN = 64;
+  static constexpr int MP = 16 * MT;
+  static constexpr int MPA = MP < 32 ? 32 : MP;  // staged rows: at least one 16-byte load per thread
+  static constexpr int A_LD = MPA * 8 / NT;       // 16-byte activation loads per thread and slice
+  static constexpr int A_BYTES = MPA * 128;
+  static constexpr int SA_OFF = A_BYTES;          // activation scales of the slice (x NT / MPA)
+  static constexpr int STAGE = A_BYTES + NT * 4;  // one slice
+  static constexpr int LDS_BYTES = 2 * R * STAGE; // two rounds
+  static constexpr int SLOT_FLOATS = BN * MP;     // one partial tile
+};
+
+// A GEMM workspace starts with a header of arrival counters, one per output tile of the decode
+// path (which therefore splits K only while it has at most kWsCounters tiles); partials follow.
+constexpr size_t kWsHeaderBytes = 4096;
+constexpr int64_t kWsCounters = kWsHeaderBytes / sizeof(int);
+constexpr int64_t kDecWorkgroups = 512;  // split K until about this many workgroups (2 per CU)
+constexpr int64_t kDecMinSlices = 8;     // ... keeping at least this many slices per split
+
+__device__ __forceinline__ v8i load_frag_global(const uint8_t* row_base, int kb, int kq) {
+  const u32x4* p = reinterpret_cast<const u32x4*>(row_base + (int64_t)kb * 128 + kq * 32);
+  const u32x4 lo = __builtin_nontemporal_load(p), hi = __builtin_nontemporal_load(p + 1);
+  v8i f;
+  f[0] = (int)lo.x; f[1] = (int)lo.y; f[2] = (int)lo.z; f[3] = (int)lo.w;
+  f[4] = (int)hi.x; f[5] = (int)hi.y; f[6] = (int)hi.z; f[7] = (int)hi.w;
+  return f;
+}
+
+template <class T>
+struct DecSlot {
+  u32x4 a[T::A_LD];
+  v8i b;
+  float sa;
+  float sw;
+};
+
+template <class T>
+__device__ __forceinline__ void dec_fetch(DecSlot<T>& d, const GemmArgs& p, const uint8_t* wrow,
+                                          const float* swrow, int kb, int tid) {
+  const uint8_t* xs = p.xq + (int64_t)kb * 128;
+#pragma unroll
+  for (int j = 0; j < T::A_LD; ++j) {
+    const int e = j * T::NT + tid;  // 16-byte chunk e: row e / 8, chunk e % 8
+    // activation rows are read by every tile: ordinary (cached) loads
+    d.a[j] = *reinterpret_cast<const u32x4*>(xs + (int64_t)min(e >> 3, p.M - 1) * p.K + (e & 7) * 16);
+  }
+  d.b = load_frag_global(wrow, kb, (tid & 63) >> 4);
+  d.sa = p.sa[(int64_t)min(tid & (T::MPA - 1), p.M - 1) * p.KB + kb];
+  d.sw = swrow[kb];
+}
+
+template <class T>
+__device__ __forceinline__ void dec_stage(uint8_t* st, const DecSlot<T>& d, int tid) {
+#pragma unroll
+  for (int j = 0; j < T::A_LD; ++j) {
+    const int e = j * T::NT + tid;
+    const int row = e >> 3;
+    *reinterpret_cast<u32x4*>(st + row * 128 + (((e & 7) ^ swz(row)) << 4)) = d.a[j];
+  }
+  reinterpret_cast<float*>(st + T::SA_OFF)[tid] = d.sa;  // copies past MPA are not read
+}
+
+template <class T, bool PRECISE>
+__device__ __forceinline__ void dec_mma(const uint8_t* st, const DecSlot<T>& d, int lane,
+                                        v4f (&acc)[T::MT]) {
+  const int r16 = lane & 15, kq = lane >> 4;
+  v4f cur[T::MT];
+#pragma unroll
+  for (int i = 0; i < T::MT; ++i) cur[i] = slice_product<PRECISE>(load_frag(st, i * 16 + r16, kq), d.b);
+  __builtin_amdgcn_sched_barrier(0);  // all MT products in flight before the first is consumed
+  const float* sa = reinterpret_cast<const float*>(st + T::SA_OFF);
+#pragma unroll
+  for (int i = 0; i < T::MT; ++i) {
+    acc[i] += cur[i] * (*reinterpret_cast<const v4f*>(sa + i * 16 + 4 * kq) * d.sw);
+    asm volatile("" : "+v"(acc[i]));  // keep each slice's update in place
+  }
+}
+
+template <class T, bool PRECISE>
+__global__ __launch_bounds__(T::NT) void gemm_decode_kernel(GemmArgs p) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[T::LDS_BYTES];
+  __shared__ int s_flag;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int t = blockIdx.x, split = blockIdx.y, L = p.kb_per_split;
+  const int kb0 = split * L;
+  const int ncol = t * T::BN + wave * 16;  // this wave's 16 weight rows
+  const uint8_t* wrow = p.wq + (int64_t)(ncol + (lane & 15)) * p.K;
+  const float* swrow = p.sw + (int64_t)(ncol >> 7) * p.KB;
+
+  // L is a multiple of 2R. Round r (R slices) lives in register set r & 1 while its loads are
+  // in flight; it is staged into LDS buffer r & 1 with one barrier, multiplied, and its
+  // registers refilled with round r + 2. All loads and waits are visible to the compiler: the
+  // rounds are unrolled, so no branch separates a load from its use.
+  DecSlot<T> ring0[T::R], ring1[T::R];
+#pragma unroll
+  for (int u = 0; u < T::R; ++u) dec_fetch<T>(ring0[u], p, wrow, swrow, kb0 + u, tid);
+#pragma unroll
+  for (int u = 0; u < T::R; ++u) dec_fetch<T>(ring1[u], p, wrow, swrow, kb0 + T::R + u, tid);
+  v4f acc[T::MT];
+#pragma unroll
+  for (int i = 0; i < T::MT; ++i) acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
+  uint8_t* const buf0 = lds;
+  uint8_t* const buf1 = lds + T::R * T::STAGE;
+  auto round = [&](DecSlot<T>(&ring)[T::R], uint8_t* buf, int refill_kb) {
+#pragma unroll
+    for (int u = 0; u < T::R; ++u) dec_stage<T>(buf + u * T::STAGE, ring[u], tid);
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < T::R; ++u) dec_mma<T, PRECISE>(buf + u * T::STAGE, ring[u], lane, acc);
+    // refill only once consumed, so each set keeps its registers across the loop
+    if (refill_kb >= 0) {
+#pragma unroll
+      for (int u = 0; u < T::R; ++u) dec_fetch<T>(ring[u], p, wrow, swrow, refill_kb + u, tid);
+    }
+  };
+  for (int k0 = 0; k0 < L - 2 * T::R; k0 += 2 * T::R) {
+    round(ring0, buf0, kb0 + k0 + 2 * T::R);
+    round(ring1, buf1, kb0 + k0 + 3 * T::R);
+  }
+  round(ring0, buf0, -1);
+  round(ring1, buf1, -1);
+
+  const int kq = lane >> 4, col = ncol + (lane & 15);
+  float vals[T::MT * 4];
+  auto store_y = [&]() {
+#pragma unroll
+    for (int i = 0; i < T::MT; ++i)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int row = i * 16 + 4 * kq + v;
+        if (row >= p.M) continue;
+        if (p.out_f32)
+          reinterpret_cast<float*>(p.y)[row * p.ldy + col] = vals[i * 4 + v];
+        else
+          reinterpret_cast<uint16_t*>(p.y)[row * p.ldy + col] = f32_to_bf16_rne(vals[i * 4 + v]);
+      }
+  };
+#pragma unroll
+  for (int i = 0; i < T::MT; ++i)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) vals[i * 4 + v] = acc[i][v];
+  const int S = gridDim.y;
+  if (S == 1) {
+    store_y();
+    return;
+  }
+  float* base = p.ws + (size_t)wave * T::MT * 256 + lane;
+  float* mine = base + ((size_t)t * S + split) * T::SLOT_FLOATS;
+#pragma unroll
+  for (int j = 0; j < T::MT * 4; ++j)
+    __hip_atomic_store(mine + j * 64, vals[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (tid == 0) {
+    const int prev = __hip_atomic_fetch_add(p.counters + t, 1, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT);
+    s_flag = prev == S - 1;
+  }
+  __syncthreads();
+  if (!s_flag) return;
+  // last arrival: sum the partials in split order, 4 splits' loads in flight at a time
+#pragma unroll
+  for (int j = 0; j < T::MT * 4; ++j) vals[j] = 0.f;
+  for (int s0 = 0; s0 < S; s0 += 4) {
+    float v4[4][T::MT * 4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float* src = base + ((size_t)t * S + min(s0 + u, S - 1)) * T::SLOT_FLOATS;
+#pragma unroll
+      for (int j = 0; j < T::MT * 4; ++j)
+        v4[u][j] = __hip_atomic_load(src + j * 64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int j = 0; j < T::MT * 4; ++j) vals[j] = s0 + u < S ? vals[j] + v4[u][j] : vals[j];
+  }
+  store_y();
+  if (tid == 0)
+    __hip_atomic_store(p.counters + t, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Deterministic split-K reduction: partials are summed in split order.
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ ws,
                                                             int splits, int64_t M, int N, void* y,
@@ -611,7 +814,7 @@ __global__ __launch_bounds__(T::NT) void grouped_gemm_kernel(GemmArgs p) {
 // ---------------------------------------------------------------------------------------------
 namespace {
 
-constexpr int kCfgLarge = 0, kCfgSmall = 1, kCfgBigWide = 2, kCfgBigNarrow = 3;
+constexpr int kCfgLarge = 0, kCfgSmall = 1, kCfgBigWide = 2, kCfgBigNarrow = 3, kCfgDecode = 4;
 constexpr int kTargetWorkgroups = 512;  // two per CU on 256 CUs
 constexpr int kMinSlicesPerSplit = 4;
 
@@ -643,6 +846,31 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
     pl.workspace_bytes = 0;
     return pl;
   }
+  if (M <= 64 && KB % 2 == 0) {
+    // weight streaming: 64-column tiles, D slices in flight per wave (the largest of 8, 4, 2
+    // dividing KB); split K into ranges of L slices (L a multiple of D dividing KB) while there
+    // are fewer than kDecWorkgroups workgroups and ranges keep at least kDecMinSlices slices
+    constexpr int64_t BN = 64;
+    const int64_t D = KB % 8 == 0 ? 8 : KB % 4 == 0 ? 4 : 2;  // two rounds of D / 2 slices
+    const int64_t tiles = N / BN;
+    int64_t S = 1;
+    if (tiles <= kWsCounters)
+      for (int64_t s = 2; s <= KB / D; ++s) {
+        if ((KB / D) % s || KB / s < kDecMinSlices) continue;
+        if (tiles * S >= kDecWorkgroups) break;
+        S = s;
+      }
+    pl.cfg = kCfgDecode;
+    pl.bm = (int)M;
+    pl.bn = (int)BN;
+    pl.depth = (int)D;
+    pl.splits = (int)S;
+    pl.kb_per_split = (int)(KB / S);
+    const int64_t mp = M <= 16 ? 16 : M <= 32 ? 32 : 64;  // rows the kernel pads M to
+    pl.workspace_bytes =
+        S > 1 ? kWsHeaderBytes + (size_t)(tiles * S) * BN * mp * sizeof(float) : 0;
+    return pl;
+  }
   if (M >= 512) {
     pl.cfg = kCfgLarge;
     pl.bm = TileLarge::BM;
@@ -663,7 +891,8 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
   pl.kb_per_split = (int)((KB + splits - 1) / splits);
   pl.splits = (int)((KB + pl.kb_per_split - 1) / pl.kb_per_split);
   if (pl.splits < 1) pl.splits = 1;
-  pl.workspace_bytes = pl.splits > 1 ? (size_t)pl.splits * (size_t)M * (size_t)N * sizeof(float) : 0;
+  pl.workspace_bytes =
+      pl.splits > 1 ? kWsHeaderBytes + (size_t)pl.splits * (size_t)M * (size_t)N * sizeof(float) : 0;
   return pl;
 }
 
@@ -687,6 +916,27 @@ static hipError_t launch_big(const GemmArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((gemm_big_kernel<T, PRECISE>), dim3((unsigned)(tiles_m * tiles_n)), dim3(T::NT),
                      0, stream, a);
   return hipGetLastError();
+}
+
+template <class T, bool PRECISE>
+static hipError_t launch_decode_t(const GemmArgs& a, const GemmPlan& pl, hipStream_t stream) {
+  hipLaunchKernelGGL((gemm_decode_kernel<T, PRECISE>), dim3((unsigned)(a.N / T::BN), (unsigned)pl.splits),
+                     dim3(T::NT), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int R, bool PRECISE>
+static hipError_t launch_decode_d(const GemmArgs& a, const GemmPlan& pl, hipStream_t stream) {
+  if (a.M <= 16) return launch_decode_t<Dec<1, R>, PRECISE>(a, pl, stream);
+  if (a.M <= 32) return launch_decode_t<Dec<2, R>, PRECISE>(a, pl, stream);
+  return launch_decode_t<Dec<4, R>, PRECISE>(a, pl, stream);
+}
+
+template <bool PRECISE>
+static hipError_t launch_decode(const GemmArgs& a, const GemmPlan& pl, hipStream_t stream) {
+  if (pl.depth == 8) return launch_decode_d<4, PRECISE>(a, pl, stream);
+  if (pl.depth == 4) return launch_decode_d<2, PRECISE>(a, pl, stream);
+  return launch_decode_d<1, PRECISE>(a, pl, stream);
 }
 
 template <class T, bool PRECISE>
@@ -716,21 +966,33 @@ hipError_t launch_gemm(const uint8_t* xq, const float* sa, const uint8_t* wq, co
   a.y = y;
   a.ldy = ld_y;
   a.out_f32 = out_f32;
-  a.ws = pl.splits > 1 ? reinterpret_cast<float*>(workspace) : nullptr;
+  // workspace: the counter header, then the partials
+  a.counters = pl.workspace_bytes > 0 ? reinterpret_cast<int*>(workspace) : nullptr;
+  a.ws = pl.workspace_bytes > 0
+             ? reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + kWsHeaderBytes)
+             : nullptr;
   a.splits = pl.splits;
   a.kb_per_split = pl.kb_per_split;
   hipError_t e;
-  // the f16 form needs more registers per wave than the 8-wave tile leaves: 4-wave tiles
-  if (pl.cfg == kCfgBigWide && !precise) return launch_big<BigWide, false>(a, stream);
-  if (pl.cfg == kCfgBigNarrow || pl.cfg == kCfgBigWide)
-    return precise ? launch_big<BigNarrow, true>(a, stream)
-                   : launch_big<BigNarrow, false>(a, stream);
-  if (pl.cfg == kCfgLarge)
-    e = precise ? launch_dense<TileLarge, true>(a, pl, stream)
-                : launch_dense<TileLarge, false>(a, pl, stream);
-  else
-    e = precise ? launch_dense<TileSmall, true>(a, pl, stream)
-                : launch_dense<TileSmall, false>(a, pl, stream);
+  switch (pl.cfg) {
+    case kCfgBigWide:
+      // the f16 form needs more registers per wave than the 8-wave tile leaves: 4-wave tiles
+      return precise ? launch_big<BigNarrow, true>(a, stream)
+                     : launch_big<BigWide, false>(a, stream);
+    case kCfgBigNarrow:
+      return precise ? launch_big<BigNarrow, true>(a, stream)
+                     : launch_big<BigNarrow, false>(a, stream);
+    case kCfgDecode:  // reduces its own split tiles
+      return precise ? launch_decode<true>(a, pl, stream) : launch_decode<false>(a, pl, stream);
+    case kCfgLarge:
+      e = precise ? launch_dense<TileLarge, true>(a, pl, stream)
+                  : launch_dense<TileLarge, false>(a, pl, stream);
+      break;
+    default:
+      e = precise ? launch_dense<TileSmall, true>(a, pl, stream)
+                  : launch_dense<TileSmall, false>(a, pl, stream);
+      break;
+  }
   if (e != hipSuccess || pl.splits == 1) return e;
   const int64_t total4 = M * N / 4;
   hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((total4 + 255) / 256)), dim3(256), 0,

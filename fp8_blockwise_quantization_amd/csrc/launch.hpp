@@ -32,6 +32,7 @@ struct GemmPlan {
   int bm, bn;  // workgroup tile
   int splits;  // K splits (1 = no split, result written directly)
   int kb_per_split;
+  int depth;   // decode path: K slices in flight per wave
   size_t workspace_bytes;
 };
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K);

@@ -151,8 +151,13 @@ int fp8rl_quant_act_tok128(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x
  *   y      : output [M][ld_y] (ld_y >= N) of type y_dtype
  *   accum  : FP8RL_ACCUM_FP8 or FP8RL_ACCUM_F16 (see fp8rl_accum)
  *   workspace, workspace_bytes: scratch of at least fp8rl_workspace_bytes(FP8RL_OP_GEMM, M, N, K, 0)
- *            bytes (device, 16-byte aligned; may be NULL when that size is 0). Its contents on
- *            entry are ignored; the result does not depend on them.
+ *            bytes (device, 16-byte aligned; may be NULL when that size is 0). Its first
+ *            FP8RL_WORKSPACE_HEADER_BYTES bytes hold arrival counters of the K-split reduction:
+ *            they must be zero before the workspace is first used (allocate it zero-filled), and
+ *            every call that returns FP8RL_OK leaves them zero again once its kernels have run,
+ *            so one workspace serves any sequence of calls and shapes. Calls that use the same
+ *            workspace must not run concurrently (different streams without ordering). The rest
+ *            of the workspace is overwritten; the result does not depend on its contents.
  * Requires N % 128 == 0, K % 128 == 0. The result is deterministic (same bits every run).
  */
 int fp8rl_gemm_w8a8_blockscaled(const uint8_t* xq, const float* sa, const uint8_t* wq,
@@ -181,7 +186,12 @@ int fp8rl_grouped_gemm_w8a8(const uint8_t* xq, const float* sa, const uint8_t* w
                             int64_t K, void* y, int y_dtype, int accum, void* workspace,
                             size_t workspace_bytes, void* stream);
 
-/* Bytes of workspace the GEMM entry points need for this shape (0 when none). Host-only. */
+/* Bytes at the start of every GEMM workspace that hold the K-split arrival counters (see
+ * fp8rl_gemm_w8a8_blockscaled). */
+#define FP8RL_WORKSPACE_HEADER_BYTES 4096
+
+/* Bytes of workspace the GEMM entry points need for this shape (0 when none; otherwise it includes
+ * the FP8RL_WORKSPACE_HEADER_BYTES header). Host-only. */
 size_t fp8rl_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int32_t E);
 
 /* Static, NUL-terminated description of a status code. Host-only. */

@@ -145,6 +145,29 @@ def test_grouped_gemm_validation(L):
 
 
 def test_workspace_query_is_pure_host(L):
+    hdr = _lib.WORKSPACE_HEADER_BYTES
+    assert hdr == 4096  # FP8RL_WORKSPACE_HEADER_BYTES
+    # decode shapes (M <= 64, even K/128): 64-column tiles, K split into S ranges of whole
+    # rounds of D slices (D = 8, 4 or 2 dividing K/128) while fewer than 512 workgroups and
+    # ranges of >= 8 slices; workspace = header + [tiles][S] partial tiles of 64 columns x
+    # padded rows (16, 32 or 64) float32
+    def dec(M, N, K):
+        tiles, kb = N // 64, K // 128
+        d = 8 if kb % 8 == 0 else 4 if kb % 4 == 0 else 2
+        S = 1
+        for s_ in range(2, kb // d + 1):
+            if (kb // d) % s_ or kb // s_ < 8:
+                continue
+            if tiles * S >= 512:
+                break
+            S = s_
+        mp = 16 if M <= 16 else 32 if M <= 32 else 64
+        return hdr + tiles * S * 64 * mp * 4 if S > 1 else 0
+    for shape in [(64, 4096, 4096), (20, 1024, 12288), (64, 12288, 4096), (1, 256, 2048)]:
+        assert L.fp8rl_workspace_bytes(0, *shape, 0) == dec(*shape) > 0, shape
+    assert L.fp8rl_workspace_bytes(0, 64, 4096, 4096, 0) == hdr + 64 * 4 * 64 * 64 * 4
+    assert L.fp8rl_workspace_bytes(0, 64, 4096, 1024, 0) == 0  # 8 slices: one range
+    assert L.fp8rl_workspace_bytes(0, 8, 131072, 2048, 0) == 0  # more tiles than counters
     assert L.fp8rl_workspace_bytes(0, 0, 256, 256, 0) == 0
     assert L.fp8rl_workspace_bytes(0, 8192, 4096, 4096, 0) == 0  # large M: no split
     assert L.fp8rl_workspace_bytes(1, 32768, 1536, 2048, 128) == 0

@@ -70,7 +70,9 @@ def test_tiny_config_both_outputs():
 
 @pytest.mark.parametrize("M,N,K", [(64, 4096, 4096), (64, 1024, 4096), (64, 4096, 12288),
                                    (256, 14336, 4096), (1, 128, 128), (3, 384, 640),
-                                   (67, 1024, 4096), (130, 512, 1024)])
+                                   (67, 1024, 4096), (130, 512, 1024), (20, 512, 1024),
+                                   (32, 2048, 2048), (48, 12288, 4096), (17, 256, 16384),
+                                   (33, 1024, 1280), (8, 65664, 256), (8, 65664, 1152)])
 def test_small_m_shapes(M, N, K):
     run_and_check(*quantized_operands(M, N, K, 1000 + M + N + K), f"small-M {M}x{N}x{K}")
 
@@ -135,6 +137,27 @@ def test_output_pitch_canary_and_determinism():
     b = fq.gemm(*d, out_dtype=torch.float32)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+def test_one_workspace_reused_across_shapes():
+    """One zero-headed workspace serves decode GEMMs of several shapes in a row (each split-K
+    reduction re-arms its counters), and its counter header is zero again afterwards."""
+    shapes = [(64, 4096, 4096), (20, 1024, 12288), (64, 4096, 4096), (1, 256, 2048),
+              (48, 2048, 1280)]
+    need = max(fq.fp8rl_workspace_bytes(fq.FP8RL_OP_GEMM, *s) for s in shapes)
+    ws = fq.new_workspace(need, "cuda")
+    ws[fq.WORKSPACE_HEADER_BYTES:].fill_(0xC3)  # garbage partials from an earlier call
+    for i, (M, N, K) in enumerate(shapes):
+        xq, sa, wq, sw = quantized_operands(M, N, K, 3000 + i)
+        ref64 = og.gemm_blockscaled(xq, sa, wq, sw, out="f64")
+        d = [to_dev_u8(xq), to_dev_f32(sa), to_dev_u8(wq), to_dev_f32(sw)]
+        for out, dt in (("bf16", torch.bfloat16), ("f32", torch.float32)):
+            y = fq.gemm(*d, out_dtype=dt, workspace=ws)
+            torch.cuda.synchronize()
+            ref = (og.bf16_bits_to_f64(og.round_f64_to_bf16_bits(ref64)) if out == "bf16"
+                   else ref64.astype(np.float32).astype(np.float64))
+            assert_gemm_close(gemm_out_to_f64(y), ref, ref64, out, f"reuse {M}x{N}x{K} {out}")
+    assert int(ws[:fq.WORKSPACE_HEADER_BYTES].count_nonzero()) == 0
 
 
 def test_zero_rows_noop():

@@ -26,8 +26,8 @@ def test_graph_replays_match_eager_and_oracle():
     xqs = [torch.empty(x.shape, dtype=torch.uint8, device="cuda") for x in xs]
     sas = [torch.empty((M, x.shape[1] // 128), dtype=torch.float32, device="cuda") for x in xs]
     ys = [torch.empty((M, N), dtype=torch.bfloat16, device="cuda") for N, K in shapes]
-    wss = [torch.empty(max(16, fq.fp8rl_workspace_bytes(fq.FP8RL_OP_GEMM, M, N, K)),
-                       dtype=torch.uint8, device="cuda") for N, K in shapes]
+    wss = [fq.new_workspace(fq.fp8rl_workspace_bytes(fq.FP8RL_OP_GEMM, M, N, K), "cuda")
+           for N, K in shapes]
     descs = fq.weight_descs(ws, wqs, sws)
 
     def step():
