@@ -5,8 +5,13 @@ Default workload: one Qwen3-8B-shaped decoder block at decode (M = 64 tokens, hi
 whole hot path over that block:
 
   1. per-step re-quantization of all 7 bf16 weights to E4M3 with 128x128 FP32 block scales,
+     in one batched launch,
   2. dynamic 1x128 per-token quantization of each linear's bf16 input activation,
-  3. the 7 blockwise-scaled FP8 GEMMs (bf16 output).
+  3. the blockwise-scaled FP8 GEMMs (bf16 output).
+
+The weights are laid out as a serving engine keeps them: q/k/v concatenated along N (6144x4096)
+and gate/up concatenated (24576x4096), so the block is 4 GEMMs over 4 activation quantizations
+(one per distinct input), with the same bytes and FLOPs as the 7 separate linears.
 
 Inputs are seeded synthetic tensors resident in HBM (weights N(0, 0.02) with 0.1 % x10 outliers,
 activations N(0, 1) with 1 % x20 outlier channels), rotated over enough copies that every step
@@ -102,11 +107,33 @@ def g_bytes(M, N, K, out_bytes=2):
     return M * K + N * K + out_bytes * M * N + 4 * M * (K // 128) + 4 * (N // 128) * (K // 128)
 
 
+#: Linears that read the same input, stored concatenated along N as a serving engine does
+#: (per-128x128-block quantization of the concatenation equals that of the parts: every N is a
+#: multiple of 128). Each group is one activation quantization and one GEMM.
+FUSED_GROUPS = (("qkv_proj", ("q_proj", "k_proj", "v_proj")), ("gate_up_proj", ("gate_proj", "up_proj")))
+
+
+def serving_layout(linears):
+    """(name, N, K) groups of `linears` with the FUSED_GROUPS merged (consecutive, same K)."""
+    out, i = [], 0
+    while i < len(linears):
+        for fused, parts in FUSED_GROUPS:
+            names = tuple(l[0] for l in linears[i:i + len(parts)])
+            if names == parts and len({l[2] for l in linears[i:i + len(parts)]}) == 1:
+                out.append((fused, sum(l[1] for l in linears[i:i + len(parts)]), linears[i][2]))
+                i += len(parts)
+                break
+        else:
+            out.append(tuple(linears[i]))
+            i += 1
+    return tuple(out)
+
+
 class DenseBlock:
-    """The 7 linears of one decoder block at a given M: re-quantize, quantize, multiply.
+    """The GEMMs of one decoder block at a given M: re-quantize, quantize, multiply.
 
     The per-step weight re-quantization of all linears is one batched launch (timed on its own
-    with HIP events); the activation quantizations and GEMMs of the 7 linears are captured once
+    with HIP events); the activation quantizations and GEMMs of the block are captured once
     per weight copy into a HIP graph and replayed, so host launch overhead does not pace the GPU.
     """
 
@@ -300,7 +327,11 @@ def main():
     else:
         return run_moe(args, torch, fq, synth, dev_name)
 
-    blk = DenseBlock(torch, fq, synth, linears, M, seed=1000 + args.seed, requant=requant)
+    groups = serving_layout(linears)
+    cfg["gemms"] = [list(g) for g in groups]
+    cfg["layout"] = ("q/k/v and gate/up weights concatenated along N (one activation "
+                     "quantization and one GEMM per shared input)")
+    blk = DenseBlock(torch, fq, synth, groups, M, seed=1000 + args.seed, requant=requant)
     blk.capture()
     for _ in range(args.warmup):
         blk.step()
@@ -328,13 +359,14 @@ def main():
                 "traffic": measured_traffic(), "avg_launch_us": r["avg_us"],
                 "algorithmic_bytes_per_launch": blk.bytes_w,
                 "per_unit": "3 B per weight element + 4 B per 128x128 block",
-                "units_per_launch": "all 7 weights of the block (192,937,984 elements, 11,776 blocks)"}
+                "units_per_launch": "all weights of the block (192,937,984 elements, 11,776 "
+                                    "blocks) in one launch"}
     else:
         tf = blk.flops / (lin_ms * 1e-3) / 1e12
         roof = {"kernel": "gemm_kernel", "bound": "mfma", "achieved": tf, "peak": FP8_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": tf / FP8_PEAK_TFLOPS, "traffic": None,
                 "avg_launch_us": None, "per_unit": "2*M*N*K flops per linear",
-                "units_per_launch": "one linear (graph of 7 act quants + 7 GEMMs timed)"}
+                "units_per_launch": "the block's GEMMs (graph of their act quants + GEMMs timed)"}
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline_dense(linears, M, seed=5000, budget_linears=7 if M <= 256 else 1)
@@ -370,8 +402,8 @@ def _timed(torch, fn, steps, warmup, timers=()):
 def run_mlp(args, torch, fq, synth, dev_name):
     out = []
     for M in (256, 4096):
-        blk = DenseBlock(torch, fq, synth, synth.LLAMA31_8B_LAYER_LINEARS[4:], M, seed=2000 + M,
-                         requant=False)
+        blk = DenseBlock(torch, fq, synth, serving_layout(synth.LLAMA31_8B_LAYER_LINEARS[4:]), M,
+                         seed=2000 + M, requant=False)
         blk.capture()
         ms = blk.time_linears(max(args.steps, 10))
         out.append({"M": M, "us_per_step": 1e3 * ms, "gemm_tflops_incl_act_quant":
