@@ -327,8 +327,10 @@ struct Big {
 };
 
 constexpr int kMaxSlices = 128;  // K <= 16384 on the large-tile path
+constexpr int kMaxExperts = 1024;
 using BigWide = Big<256, 256, 128, 64>;  // 8 waves
 using BigNarrow = Big<256, 128, 128, 64>;  // 4 waves
+using BigGroup = Big<128, 256, 64, 64>;    // 8 waves; grouped GEMM (expert segments are short)
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -453,25 +455,19 @@ __device__ __forceinline__ void mma_slice_big(const uint8_t* stage, float swv, i
   for (int j = 0; j < T::TN; ++j) acc[T::TM - 1][j] += p_prev[j] * sc_prev;
 }
 
+// One BM x BN output tile over all K slices: operands DMA'd through two LDS stages (slice kb + 1
+// in flight while slice kb is multiplied), the weight scales of the tile's (up to two)
+// 128-column blocks read into LDS once. A / SA start at the tile's first row, B at its first
+// column (weight row); SW is the weight-scale matrix [N/128][KB] (of the tile's expert); Y rows
+// y_row0 + r, r < m_valid, pitch ldy. The caller's previous use of the LDS arrays must be over.
 template <class T, bool PRECISE>
-__global__ __launch_bounds__(T::NT) void gemm_big_kernel(GemmArgs p) {
-  __shared__ __attribute__((aligned(16))) uint8_t stage0[T::STAGE_BYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t stage1[T::STAGE_BYTES];
-  // weight scales of the tile's (up to two) 128-column blocks for every K slice, read once
-  __shared__ float sw_s[(T::BN + 127) / 128][kMaxSlices];
-  const int tiles_m = (p.M + T::BM - 1) / T::BM;
-  const int tiles_n = (p.N + T::BN - 1) / T::BN;
-  int tm, tn;
-  tile_coords(blockIdx.x, tiles_m * tiles_n, tiles_m, tiles_n, tm, tn);
-  const int m0 = tm * T::BM, n0 = tn * T::BN;
-  const int m_valid = min(T::BM, p.M - m0);
-  const int n_valid = min(T::BN, p.N - n0);
+__device__ __forceinline__ void big_tile(const GemmArgs& p, uint8_t* stage0, uint8_t* stage1,
+                                         float (*sw_s)[kMaxSlices], const uint8_t* A,
+                                         const float* SA, int m_valid, const uint8_t* B,
+                                         const float* SW, int n0, int n_valid, int64_t y_row0) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / T::WAVES_N, wn = wave % T::WAVES_N;
-  const uint8_t* A = p.xq + (int64_t)m0 * p.K;
-  const float* SA = p.sa + (int64_t)m0 * p.KB;
-  const uint8_t* B = p.wq + (int64_t)n0 * p.K;
   const int KB = p.KB;
   // a wave whose columns are all past N still runs (it takes part in the DMA and barriers) on a
   // clamped scale row; its results are not stored
@@ -479,7 +475,7 @@ __global__ __launch_bounds__(T::NT) void gemm_big_kernel(GemmArgs p) {
   for (int e = tid; e < NBLK * KB; e += T::NT) {
     const int b = e / KB, k = e - (e / KB) * KB;
     const int nb = min((n0 >> 7) + b, p.N / 128 - 1);
-    sw_s[b][k] = p.sw[(int64_t)nb * KB + k];
+    sw_s[b][k] = SW[(int64_t)nb * KB + k];
   }
   const float* swrow = sw_s[((n0 + wn * T::WN) >> 7) - (n0 >> 7)];
 
@@ -512,13 +508,94 @@ __global__ __launch_bounds__(T::NT) void gemm_big_kernel(GemmArgs p) {
       for (int v = 0; v < 4; ++v) {
         const int r = wm * T::WM + i * 16 + 4 * kq + v;
         if (r >= m_valid) continue;
-        const int64_t off = (int64_t)(m0 + r) * p.ldy + n0 + c;
+        const int64_t off = (y_row0 + r) * p.ldy + n0 + c;
         if (p.out_f32)
           reinterpret_cast<float*>(p.y)[off] = acc[i][j][v];
         else
           reinterpret_cast<uint16_t*>(p.y)[off] = f32_to_bf16_rne(acc[i][j][v]);
       }
     }
+  }
+}
+
+template <class T, bool PRECISE>
+__global__ __launch_bounds__(T::NT) void gemm_big_kernel(GemmArgs p) {
+  __shared__ __attribute__((aligned(16))) uint8_t stage0[T::STAGE_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t stage1[T::STAGE_BYTES];
+  __shared__ float sw_s[(T::BN + 127) / 128][kMaxSlices];
+  const int tiles_m = (p.M + T::BM - 1) / T::BM;
+  const int tiles_n = (p.N + T::BN - 1) / T::BN;
+  int tm, tn;
+  tile_coords(blockIdx.x, tiles_m * tiles_n, tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * T::BM, n0 = tn * T::BN;
+  big_tile<T, PRECISE>(p, stage0, stage1, sw_s, p.xq + (int64_t)m0 * p.K,
+                       p.sa + (int64_t)m0 * p.KB, min(T::BM, p.M - m0), p.wq + (int64_t)n0 * p.K,
+                       p.sw, n0, min(T::BN, p.N - n0), m0);
+}
+
+// Grouped GEMM on the DMA-fed tiles, persistent: a fixed grid of workgroups walks the list of
+// (expert m-tile, n-tile) pairs. Each workgroup first forms, from the device offsets, the prefix
+// sums of the per-expert m-tile counts in LDS (once), then finds each tile's expert by binary
+// search. The tile list is cut into one contiguous chunk per XCD (workgroup w runs on XCD
+// w % 8), so the m-tiles of one expert -- which read the same weight panels -- and the n-tiles
+// of one m-tile -- which read the same activation rows -- share an L2.
+template <class T, bool PRECISE>
+__global__ __launch_bounds__(T::NT) void grouped_big_kernel(GemmArgs p) {
+  __shared__ __attribute__((aligned(16))) uint8_t stage0[T::STAGE_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t stage1[T::STAGE_BYTES];
+  __shared__ float sw_s[(T::BN + 127) / 128][kMaxSlices];
+  __shared__ int s_first[kMaxExperts + 1];  // m-tiles of experts before e
+  __shared__ int s_part[T::NT];
+  const int tid = threadIdx.x;
+  const int E = p.E;
+  // prefix sums of ceil(rows_e / BM), NT experts per pass (E <= kMaxExperts)
+  int carry = 0;
+  for (int base = 0; base < E; base += T::NT) {
+    const int e = base + tid;
+    int cnt = 0;
+    if (e < E) {
+      const int lo = min(max(p.offsets[e], 0), p.M);
+      const int hi = min(max(p.offsets[e + 1], lo), p.M);
+      cnt = (hi - lo + T::BM - 1) / T::BM;
+    }
+    s_part[tid] = cnt;
+    __syncthreads();
+    for (int d = 1; d < T::NT; d <<= 1) {
+      const int v = tid >= d ? s_part[tid - d] : 0;
+      __syncthreads();
+      s_part[tid] += v;
+      __syncthreads();
+    }
+    if (e < E) s_first[e] = carry + s_part[tid] - cnt;
+    carry += s_part[T::NT - 1];
+    __syncthreads();
+  }
+  if (tid == 0) s_first[E] = carry;
+  __syncthreads();
+  const int tiles_n = p.tiles_n;
+  const int total = s_first[E] * tiles_n;
+  const int G = gridDim.x, per_xcd = G / 8;
+  const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+  const int chunk = (total + 7) / 8;
+  const int t_end = min(total, (xcd + 1) * chunk);
+  for (int t = xcd * chunk + slot; t < t_end; t += per_xcd) {
+    const int tm_lin = t / tiles_n, tn = t - (t / tiles_n) * tiles_n;
+    // expert e: s_first[e] <= tm_lin < s_first[e + 1]
+    int lo = 0, hi = E;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (s_first[mid] <= tm_lin) lo = mid; else hi = mid;
+    }
+    const int e = lo;
+    const int r_lo = min(max(p.offsets[e], 0), p.M);
+    const int r_hi = min(max(p.offsets[e + 1], r_lo), p.M);
+    const int row0 = r_lo + (tm_lin - s_first[e]) * T::BM;
+    const int n0 = tn * T::BN;
+    __syncthreads();  // the previous tile is done with the LDS arrays
+    big_tile<T, PRECISE>(p, stage0, stage1, sw_s, p.xq + (int64_t)row0 * p.K,
+                         p.sa + (int64_t)row0 * p.KB, min(T::BM, r_hi - row0),
+                         p.wq + e * p.wq_stride + (int64_t)n0 * p.K, p.sw + e * p.sw_stride, n0,
+                         min(T::BN, p.N - n0), row0);
   }
 }
 
@@ -757,7 +834,6 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 // per-expert tile counts and their prefix sums in LDS, finds which expert its m-tile belongs to
 // and exits if it is past the last real tile. No host round trip and no workspace are needed.
 // ---------------------------------------------------------------------------------------------
-constexpr int kMaxExperts = 1024;
 
 template <class T, bool PRECISE>
 __global__ __launch_bounds__(T::NT) void grouped_gemm_kernel(GemmArgs p) {
@@ -814,7 +890,9 @@ __global__ __launch_bounds__(T::NT) void grouped_gemm_kernel(GemmArgs p) {
 // ---------------------------------------------------------------------------------------------
 namespace {
 
-constexpr int kCfgLarge = 0, kCfgSmall = 1, kCfgBigWide = 2, kCfgBigNarrow = 3, kCfgDecode = 4;
+constexpr int kCfgLarge = 0, kCfgSmall = 1, kCfgBigWide = 2, kCfgBigNarrow = 3, kCfgDecode = 4,
+              kCfgGroupedBig = 5;
+constexpr int64_t kGroupedWorkgroups = 256;  // persistent grouped GEMM: one per CU (LDS-bound)
 constexpr int kTargetWorkgroups = 512;  // two per CU on 256 CUs
 constexpr int kMinSlicesPerSplit = 4;
 
@@ -900,10 +978,11 @@ GemmPlan plan_grouped_gemm(int64_t M_total, int64_t N, int64_t K, int32_t E) {
   GemmPlan pl{};
   (void)M_total;
   (void)E;
-  pl.cfg = kCfgLarge;
-  pl.bm = TileLarge::BM;
-  pl.bn = TileLarge::BN;
-  pl.splits = 1;
+  const bool big = K / 128 <= kMaxSlices;
+  pl.cfg = big ? kCfgGroupedBig : kCfgLarge;
+  pl.bm = big ? BigGroup::BM : TileLarge::BM;
+  pl.bn = big ? BigGroup::BN : TileLarge::BN;
+  pl.splits = big ? (int)kGroupedWorkgroups : 1;  // persistent workgroups
   pl.kb_per_split = (int)(K / 128);
   pl.workspace_bytes = 0;
   return pl;
@@ -1026,8 +1105,17 @@ hipError_t launch_grouped_gemm(const uint8_t* xq, const float* sa, const uint8_t
   a.E = E;
   a.wq_stride = N * K;
   a.sw_stride = (N / 128) * (K / 128);
+  if (pl.cfg == kCfgGroupedBig) {
+    a.tiles_n = (int)((N + BigGroup::BN - 1) / BigGroup::BN);
+    if (precise)
+      hipLaunchKernelGGL((grouped_big_kernel<BigGroup, true>), dim3((unsigned)pl.splits),
+                         dim3(BigGroup::NT), 0, stream, a);
+    else
+      hipLaunchKernelGGL((grouped_big_kernel<BigGroup, false>), dim3((unsigned)pl.splits),
+                         dim3(BigGroup::NT), 0, stream, a);
+    return hipGetLastError();
+  }
   a.tiles_n = (int)(N / T::BN);
-  (void)pl;
   const int lds = T::LDS_BYTES + T::NT * (int)sizeof(int);
   static std::atomic<uint64_t> lds_done_fast{0}, lds_done_precise{0};
   const void* kern = precise ? (const void*)grouped_gemm_kernel<T, true>
