@@ -309,9 +309,9 @@ __global__ __launch_bounds__(T::NT) void gemm_kernel(GemmArgs p) {
 // this one). Per K slice: wait for this wave's DMA, one barrier, start the next slice's DMA into
 // the other stage, then multiply out of this stage.
 // ---------------------------------------------------------------------------------------------
-template <int BM_, int BN_, int WM_, int WN_>
+template <int BM_, int BN_, int WM_, int WN_, int STAGES_>
 struct Big {
-  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, STAGES = STAGES_;
   static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
   static constexpr int WAVES = WAVES_M * WAVES_N;
   static constexpr int NT = WAVES * 64;
@@ -321,6 +321,8 @@ struct Big {
   static constexpr int A_PER_WAVE = BM / 8 / WAVES;  // one DMA instruction moves 8 rows (1 KiB)
   static constexpr int B_PER_WAVE = BN / 8 / WAVES;
   static constexpr int S_ROWS = BM / WAVES;  // activation scales loaded per wave
+  static constexpr int DMA_OPS = A_PER_WAVE + B_PER_WAVE + 1;  // DMA instructions per wave, slice
+  static_assert(STAGES >= 2 && STAGES <= 3, "waits are written out for up to one slice ahead");
   static_assert(A_PER_WAVE * 8 * WAVES == BM && B_PER_WAVE * 8 * WAVES == BN, "DMA split");
   static_assert(S_ROWS <= 64 && S_ROWS * WAVES == BM, "scale DMA split");
   static_assert(128 % WN == 0, "a wave's columns must share one weight-scale block");
@@ -328,9 +330,9 @@ struct Big {
 
 constexpr int kMaxSlices = 128;  // K <= 16384 on the large-tile path
 constexpr int kMaxExperts = 1024;
-using BigWide = Big<256, 256, 128, 64>;  // 8 waves
-using BigNarrow = Big<256, 128, 128, 64>;  // 4 waves
-using BigGroup = Big<128, 256, 64, 64>;    // 8 waves; grouped GEMM (expert segments are short)
+using BigWide = Big<256, 256, 128, 64, 2>;    // 8 waves
+using BigNarrow = Big<256, 128, 128, 64, 2>;  // 4 waves
+using BigGroup = Big<128, 256, 64, 64, 3>;    // 8 waves; grouped GEMM (expert segments are short)
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -409,6 +411,15 @@ __device__ __forceinline__ void dma_slice(uint8_t* stage, const DmaPlan<T>& d, c
 __device__ __forceinline__ void wait_dma_and_barrier() {
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
+// The same, but leaving the DMAs of the next `ahead` slices (issued after the awaited one) in
+// flight: vector-memory operations complete in order, so at most that many may be outstanding.
+template <class T>
+__device__ __forceinline__ void wait_slice_and_barrier(int ahead) {
+  if (T::STAGES >= 3 && ahead >= 1)
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(T::DMA_OPS) : "memory");
+  else
+    wait_dma_and_barrier();
+}
 
 // One K slice of a wave's WM x WN tile, software-pipelined by row tile: the matrix-core sums of
 // row tile i are issued interleaved with the scale-and-accumulate FMAs of row tile i - 1 (whose
@@ -455,13 +466,13 @@ __device__ __forceinline__ void mma_slice_big(const uint8_t* stage, float swv, i
   for (int j = 0; j < T::TN; ++j) acc[T::TM - 1][j] += p_prev[j] * sc_prev;
 }
 
-// One BM x BN output tile over all K slices: operands DMA'd through two LDS stages (slice kb + 1
-// in flight while slice kb is multiplied), the weight scales of the tile's (up to two)
+// One BM x BN output tile over all K slices: operands DMA'd through STAGES LDS stages (the next
+// STAGES - 1 slices in flight while slice kb is multiplied), the weight scales of the tile's (up to two)
 // 128-column blocks read into LDS once. A / SA start at the tile's first row, B at its first
 // column (weight row); SW is the weight-scale matrix [N/128][KB] (of the tile's expert); Y rows
 // y_row0 + r, r < m_valid, pitch ldy. The caller's previous use of the LDS arrays must be over.
 template <class T, bool PRECISE>
-__device__ __forceinline__ void big_tile(const GemmArgs& p, uint8_t* stage0, uint8_t* stage1,
+__device__ __forceinline__ void big_tile(const GemmArgs& p, uint8_t* stages,
                                          float (*sw_s)[kMaxSlices], const uint8_t* A,
                                          const float* SA, int m_valid, const uint8_t* B,
                                          const float* SW, int n0, int n_valid, int64_t y_row0) {
@@ -486,15 +497,31 @@ __device__ __forceinline__ void big_tile(const GemmArgs& p, uint8_t* stage0, uin
     for (int j = 0; j < T::TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
   const DmaPlan<T> dp = make_dma_plan<T>(m_valid, n_valid, p.K, KB, wave, lane);
-  dma_slice<T>(stage0, dp, A, B, SA, 0, wave, lane);
-  for (int kb = 0; kb < KB; kb += 2) {
-    wait_dma_and_barrier();
-    if (kb + 1 < KB) dma_slice<T>(stage1, dp, A, B, SA, kb + 1, wave, lane);
-    mma_slice_big<T, PRECISE>(stage0, swrow[kb], wm, wn, lane, acc);
-    if (kb + 1 >= KB) break;
-    wait_dma_and_barrier();
-    if (kb + 2 < KB) dma_slice<T>(stage0, dp, A, B, SA, kb + 2, wave, lane);
-    mma_slice_big<T, PRECISE>(stage1, swrow[kb + 1], wm, wn, lane, acc);
+  if constexpr (T::STAGES == 2) {
+    uint8_t* const stage0 = stages;
+    uint8_t* const stage1 = stages + T::STAGE_BYTES;
+    dma_slice<T>(stage0, dp, A, B, SA, 0, wave, lane);
+    for (int kb = 0; kb < KB; kb += 2) {
+      wait_dma_and_barrier();
+      if (kb + 1 < KB) dma_slice<T>(stage1, dp, A, B, SA, kb + 1, wave, lane);
+      mma_slice_big<T, PRECISE>(stage0, swrow[kb], wm, wn, lane, acc);
+      if (kb + 1 >= KB) break;
+      wait_dma_and_barrier();
+      if (kb + 2 < KB) dma_slice<T>(stage0, dp, A, B, SA, kb + 2, wave, lane);
+      mma_slice_big<T, PRECISE>(stage1, swrow[kb + 1], wm, wn, lane, acc);
+    }
+  } else {
+    // slices kb + 1 and kb + 2 in flight while kb is multiplied
+    dma_slice<T>(stages, dp, A, B, SA, 0, wave, lane);
+    if (KB > 1) dma_slice<T>(stages + T::STAGE_BYTES, dp, A, B, SA, 1, wave, lane);
+    int cur = 0;
+    for (int kb = 0; kb < KB; ++kb) {
+      wait_slice_and_barrier<T>(KB - 1 - kb);
+      const int nxt = cur == 0 ? 2 : cur - 1;  // (kb + 2) % 3
+      if (kb + 2 < KB) dma_slice<T>(stages + nxt * T::STAGE_BYTES, dp, A, B, SA, kb + 2, wave, lane);
+      mma_slice_big<T, PRECISE>(stages + cur * T::STAGE_BYTES, swrow[kb], wm, wn, lane, acc);
+      cur = cur == 2 ? 0 : cur + 1;
+    }
   }
 
   const int r16 = lane & 15, kq = lane >> 4;
@@ -520,15 +547,14 @@ __device__ __forceinline__ void big_tile(const GemmArgs& p, uint8_t* stage0, uin
 
 template <class T, bool PRECISE>
 __global__ __launch_bounds__(T::NT) void gemm_big_kernel(GemmArgs p) {
-  __shared__ __attribute__((aligned(16))) uint8_t stage0[T::STAGE_BYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t stage1[T::STAGE_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t stages[T::STAGES * T::STAGE_BYTES];
   __shared__ float sw_s[(T::BN + 127) / 128][kMaxSlices];
   const int tiles_m = (p.M + T::BM - 1) / T::BM;
   const int tiles_n = (p.N + T::BN - 1) / T::BN;
   int tm, tn;
   tile_coords(blockIdx.x, tiles_m * tiles_n, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * T::BM, n0 = tn * T::BN;
-  big_tile<T, PRECISE>(p, stage0, stage1, sw_s, p.xq + (int64_t)m0 * p.K,
+  big_tile<T, PRECISE>(p, stages, sw_s, p.xq + (int64_t)m0 * p.K,
                        p.sa + (int64_t)m0 * p.KB, min(T::BM, p.M - m0), p.wq + (int64_t)n0 * p.K,
                        p.sw, n0, min(T::BN, p.N - n0), m0);
 }
@@ -541,8 +567,7 @@ __global__ __launch_bounds__(T::NT) void gemm_big_kernel(GemmArgs p) {
 // of one m-tile -- which read the same activation rows -- share an L2.
 template <class T, bool PRECISE>
 __global__ __launch_bounds__(T::NT) void grouped_big_kernel(GemmArgs p) {
-  __shared__ __attribute__((aligned(16))) uint8_t stage0[T::STAGE_BYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t stage1[T::STAGE_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t stages[T::STAGES * T::STAGE_BYTES];
   __shared__ float sw_s[(T::BN + 127) / 128][kMaxSlices];
   __shared__ int s_first[kMaxExperts + 1];  // m-tiles of experts before e
   __shared__ int s_part[T::NT];
@@ -592,7 +617,7 @@ __global__ __launch_bounds__(T::NT) void grouped_big_kernel(GemmArgs p) {
     const int row0 = r_lo + (tm_lin - s_first[e]) * T::BM;
     const int n0 = tn * T::BN;
     __syncthreads();  // the previous tile is done with the LDS arrays
-    big_tile<T, PRECISE>(p, stage0, stage1, sw_s, p.xq + (int64_t)row0 * p.K,
+    big_tile<T, PRECISE>(p, stages, sw_s, p.xq + (int64_t)row0 * p.K,
                          p.sa + (int64_t)row0 * p.KB, min(T::BM, r_hi - row0),
                          p.wq + e * p.wq_stride + (int64_t)n0 * p.K, p.sw + e * p.sw_stride, n0,
                          min(T::BN, p.N - n0), row0);
