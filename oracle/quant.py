@@ -21,6 +21,13 @@ Readings where the pages leave a step open (each also listed in the design notes
   scales are sw[ceil(N/128)][ceil(K/128)] row-major; activation groups are 128 consecutive K
   elements of one row of X[M][K], scales sa[M][ceil(K/128)] row-major;
 * Q12: non-finite inputs are outside the contract and raise ValueError.
+
+Power-of-two scales (the NeMo RL blog's advanced FP8 options, which switch the weight and
+activation scaling factors from FP32 to powers of 2; Unified FP8's "FP8 scale choice" section
+contrasts FP32 scales with power-of-two E8M0 ones). Reading Q13: S is the smallest power of two
+not below amax / 448 -- so no element leaves [-448, 448] -- but at least 2^-127, the smallest
+E8M0 value; amax == 0 gives S = 1. The element step is unchanged: fp32(x) / S, which is exact
+unless the quotient is below the float32 normal range.
 """
 
 from __future__ import annotations
@@ -53,18 +60,43 @@ def scale_from_amax(amax) -> np.ndarray:
     return np.where(a == np.float32(0), np.float32(1.0), s).astype(np.float32)
 
 
-def quantize_group(x32: np.ndarray):
+POW2_MIN_EXP = -127  # 2^-127: the smallest E8M0 scale
+
+
+def scale_from_amax_pow2(amax) -> np.ndarray:
+    """Q13: S = 2^e, e the least integer with 448 * 2^e >= amax (exact, from frexp), e >= -127;
+    S = 1 where amax == 0."""
+    a = np.asarray(amax, dtype=np.float64)  # float32 amax widens exactly
+    f, E = np.frexp(a)                       # a = f * 2^E, f in [0.5, 1)
+    # 448 = 0.875 * 2^9:  448 * 2^e >= f * 2^E  <=>  2^(e + 9 - E) >= f / 0.875
+    e = E - 9 + (f > 0.875)
+    e = np.maximum(e, POW2_MIN_EXP)
+    s = np.ldexp(np.float64(1.0), e).astype(np.float32)
+    return np.where(a == 0.0, np.float32(1.0), s).astype(np.float32)
+
+
+SCALES = {"fp32": scale_from_amax, "pow2": scale_from_amax_pow2}
+
+
+def _scale_fn(scale: str):
+    if scale not in SCALES:
+        raise ValueError(f"scale must be one of {sorted(SCALES)}")
+    return SCALES[scale]
+
+
+def quantize_group(x32: np.ndarray, scale: str = "fp32"):
     """Quantize one group (any shape) of float32 values: returns (codes uint8, S float32)."""
     x32 = np.asarray(x32, dtype=np.float32)
     _check_finite(x32)
     amax = np.max(np.abs(x32)) if x32.size else np.float32(0)
-    S = scale_from_amax(amax)
+    S = _scale_fn(scale)(amax)
     q = e4m3.encode((x32 / S).astype(np.float32))
     return q, np.float32(S)
 
 
-def quant_weight_blk128(w_bits):
-    """Weight W[N][K] (bf16 bits) -> (Wq uint8 [N][K], sw float32 [ceil(N/128)][ceil(K/128)])."""
+def quant_weight_blk128(w_bits, scale: str = "fp32"):
+    """Weight W[N][K] (bf16 bits) -> (Wq uint8 [N][K], sw float32 [ceil(N/128)][ceil(K/128)]).
+    `scale`: "fp32" (Q2) or "pow2" (Q13)."""
     x32 = bf16_bits_to_f32(w_bits)
     if x32.ndim != 2:
         raise ValueError("weight must be 2-D [N][K]")
@@ -76,12 +108,15 @@ def quant_weight_blk128(w_bits):
     for i in range(nb):
         for j in range(kb):
             blk = x32[i * BLOCK:(i + 1) * BLOCK, j * BLOCK:(j + 1) * BLOCK]
-            q[i * BLOCK:(i + 1) * BLOCK, j * BLOCK:(j + 1) * BLOCK], sw[i, j] = quantize_group(blk)
+            q[i * BLOCK:(i + 1) * BLOCK, j * BLOCK:(j + 1) * BLOCK], sw[i, j] = quantize_group(
+                blk, scale)
     return q, sw
 
 
-def quant_act_tok128(x_bits):
-    """Activation X[M][K] (bf16 bits) -> (Xq uint8 [M][K], sa float32 [M][ceil(K/128)])."""
+def quant_act_tok128(x_bits, scale: str = "fp32"):
+    """Activation X[M][K] (bf16 bits) -> (Xq uint8 [M][K], sa float32 [M][ceil(K/128)]).
+    `scale`: "fp32" (Q2) or "pow2" (Q13)."""
+    scale_of = _scale_fn(scale)
     x32 = bf16_bits_to_f32(x_bits)
     if x32.ndim != 2:
         raise ValueError("activation must be 2-D [M][K]")
@@ -93,7 +128,7 @@ def quant_act_tok128(x_bits):
     for j in range(kb):
         cols = x32[:, j * BLOCK:(j + 1) * BLOCK]  # every row's j-th group at once
         amax = np.max(np.abs(cols), axis=1) if cols.shape[1] else np.zeros(M, np.float32)
-        S = scale_from_amax(amax)
+        S = scale_of(amax)
         sa[:, j] = S
         q[:, j * BLOCK:(j + 1) * BLOCK] = e4m3.encode((cols / S[:, None]).astype(np.float32))
     return q, sa
