@@ -9,17 +9,23 @@ from ._lib import (  # noqa: F401
     EXPORTED,
     FP8RL_ACCUM_F16,
     FP8RL_ACCUM_FP8,
+    FP8RL_ACCUM_MX,
     FP8RL_OP_GEMM,
     FP8RL_OP_GROUPED_GEMM,
     FP8RL_OUT_BF16,
     FP8RL_OUT_F32,
+    FP8RL_SCALE_FP32,
+    FP8RL_SCALE_POW2,
     Fp8rlError,
     fp8rl_encode_e4m3_f32,
     fp8rl_gemm_w8a8_blockscaled,
     fp8rl_grouped_gemm_w8a8,
     fp8rl_quant_act_tok128,
+    fp8rl_quant_act_tok128_ex,
     fp8rl_quant_weight_blk128,
     fp8rl_quant_weight_blk128_batched,
+    fp8rl_quant_weight_blk128_batched_ex,
+    fp8rl_quant_weight_blk128_ex,
     WORKSPACE_HEADER_BYTES,
     weight_descs,
     fp8rl_workspace_bytes,

@@ -21,6 +21,9 @@ FP8RL_OUT_BF16 = 0
 FP8RL_OUT_F32 = 1
 FP8RL_ACCUM_FP8 = 0
 FP8RL_ACCUM_F16 = 1
+FP8RL_ACCUM_MX = 2
+FP8RL_SCALE_FP32 = 0
+FP8RL_SCALE_POW2 = 1
 FP8RL_OP_GEMM = 0
 FP8RL_OP_GROUPED_GEMM = 1
 
@@ -63,6 +66,12 @@ def lib() -> ctypes.CDLL:
             "fp8rl_quant_weight_blk128_batched": (ctypes.c_int,
                                                   [ctypes.POINTER(WeightDesc), i32, vp]),
             "fp8rl_quant_act_tok128": (ctypes.c_int, [vp, i64, i64, i64, vp, i64, vp, vp]),
+            "fp8rl_quant_weight_blk128_ex": (ctypes.c_int,
+                                             [vp, i64, i64, i64, vp, i64, vp, ctypes.c_int, vp]),
+            "fp8rl_quant_weight_blk128_batched_ex": (
+                ctypes.c_int, [ctypes.POINTER(WeightDesc), i32, ctypes.c_int, vp]),
+            "fp8rl_quant_act_tok128_ex": (ctypes.c_int,
+                                          [vp, i64, i64, i64, vp, i64, vp, ctypes.c_int, vp]),
             "fp8rl_gemm_w8a8_blockscaled": (
                 ctypes.c_int,
                 [vp, vp, vp, vp, i64, i64, i64, vp, ctypes.c_int, i64, ctypes.c_int, vp, sz, vp]),
@@ -86,12 +95,25 @@ EXPORTED = (
     "fp8rl_quant_weight_blk128",
     "fp8rl_quant_weight_blk128_batched",
     "fp8rl_quant_act_tok128",
+    "fp8rl_quant_weight_blk128_ex",
+    "fp8rl_quant_weight_blk128_batched_ex",
+    "fp8rl_quant_act_tok128_ex",
     "fp8rl_gemm_w8a8_blockscaled",
     "fp8rl_grouped_gemm_w8a8",
     "fp8rl_workspace_bytes",
     "fp8rl_status_string",
     "fp8rl_version",
 )
+
+
+def _scale_code(scale) -> int:
+    """'fp32' / 'pow2' (or the fp8rl_scale_fmt value) -> fp8rl_scale_fmt."""
+    codes = {"fp32": FP8RL_SCALE_FP32, "pow2": FP8RL_SCALE_POW2}
+    if isinstance(scale, str):
+        if scale not in codes:
+            raise ValueError(f"scale must be one of {sorted(codes)}")
+        return codes[scale]
+    return int(scale)
 
 
 def _check(status: int, func: str) -> None:
@@ -144,8 +166,8 @@ def fp8rl_encode_e4m3_f32(v: torch.Tensor, out: torch.Tensor | None = None, stre
 
 
 def fp8rl_quant_weight_blk128(w: torch.Tensor, wq: torch.Tensor | None = None,
-                              sw: torch.Tensor | None = None, stream=None):
-    """bf16 W[N][K] -> (Wq uint8 [N][K], sw float32 [N/128][K/128])."""
+                              sw: torch.Tensor | None = None, stream=None, scale="fp32"):
+    """bf16 W[N][K] -> (Wq uint8 [N][K], sw float32 [N/128][K/128]); scale 'fp32' or 'pow2'."""
     ld_w = _rows(w, "w", torch.bfloat16)
     N, K = w.shape
     if wq is None:
@@ -156,9 +178,19 @@ def fp8rl_quant_weight_blk128(w: torch.Tensor, wq: torch.Tensor | None = None,
     _dense(sw, "sw", torch.float32)
     if tuple(wq.shape) != (N, K) or sw.numel() != (N // 128) * (K // 128):
         raise ValueError("output shapes do not match the weight")
-    _check(lib().fp8rl_quant_weight_blk128(_ptr(w), N, K, ld_w, _ptr(wq), ld_wq, _ptr(sw),
-                                           _stream(stream)), "fp8rl_quant_weight_blk128")
+    fmt = _scale_code(scale)
+    if fmt == FP8RL_SCALE_FP32:
+        _check(lib().fp8rl_quant_weight_blk128(_ptr(w), N, K, ld_w, _ptr(wq), ld_wq, _ptr(sw),
+                                               _stream(stream)), "fp8rl_quant_weight_blk128")
+    else:
+        _check(lib().fp8rl_quant_weight_blk128_ex(_ptr(w), N, K, ld_w, _ptr(wq), ld_wq, _ptr(sw),
+                                                  fmt, _stream(stream)),
+               "fp8rl_quant_weight_blk128_ex")
     return wq, sw
+
+
+def fp8rl_quant_weight_blk128_ex(w, wq=None, sw=None, scale_fmt=FP8RL_SCALE_FP32, stream=None):
+    return fp8rl_quant_weight_blk128(w, wq, sw, stream=stream, scale=scale_fmt)
 
 
 def weight_descs(ws, wqs, sws):
@@ -175,19 +207,30 @@ def weight_descs(ws, wqs, sws):
     return arr
 
 
-def fp8rl_quant_weight_blk128_batched(ws, wqs, sws, stream=None, descs=None):
+def fp8rl_quant_weight_blk128_batched(ws, wqs, sws, stream=None, descs=None, scale="fp32"):
     """Re-quantize several bf16 weights in ceil(len/32) launches; outputs are given by the caller.
 
     ``descs`` may be a prebuilt array from ``weight_descs`` (saves re-validating every call)."""
     if descs is None:
         descs = weight_descs(ws, wqs, sws)
-    _check(lib().fp8rl_quant_weight_blk128_batched(descs, len(descs), _stream(stream)),
-           "fp8rl_quant_weight_blk128_batched")
+    fmt = _scale_code(scale)
+    if fmt == FP8RL_SCALE_FP32:
+        _check(lib().fp8rl_quant_weight_blk128_batched(descs, len(descs), _stream(stream)),
+               "fp8rl_quant_weight_blk128_batched")
+    else:
+        _check(lib().fp8rl_quant_weight_blk128_batched_ex(descs, len(descs), fmt, _stream(stream)),
+               "fp8rl_quant_weight_blk128_batched_ex")
+
+
+def fp8rl_quant_weight_blk128_batched_ex(ws, wqs, sws, scale_fmt=FP8RL_SCALE_FP32, stream=None,
+                                         descs=None):
+    return fp8rl_quant_weight_blk128_batched(ws, wqs, sws, stream=stream, descs=descs,
+                                             scale=scale_fmt)
 
 
 def fp8rl_quant_act_tok128(x: torch.Tensor, xq: torch.Tensor | None = None,
-                           sa: torch.Tensor | None = None, stream=None):
-    """bf16 X[M][K] -> (Xq uint8 [M][K], sa float32 [M][K/128])."""
+                           sa: torch.Tensor | None = None, stream=None, scale="fp32"):
+    """bf16 X[M][K] -> (Xq uint8 [M][K], sa float32 [M][K/128]); scale 'fp32' or 'pow2'."""
     ld_x = _rows(x, "x", torch.bfloat16)
     M, K = x.shape
     if xq is None:
@@ -198,9 +241,18 @@ def fp8rl_quant_act_tok128(x: torch.Tensor, xq: torch.Tensor | None = None,
     _dense(sa, "sa", torch.float32)
     if tuple(xq.shape) != (M, K) or sa.numel() != M * (K // 128):
         raise ValueError("output shapes do not match the activation")
-    _check(lib().fp8rl_quant_act_tok128(_ptr(x), M, K, ld_x, _ptr(xq), ld_xq, _ptr(sa),
-                                        _stream(stream)), "fp8rl_quant_act_tok128")
+    fmt = _scale_code(scale)
+    if fmt == FP8RL_SCALE_FP32:
+        _check(lib().fp8rl_quant_act_tok128(_ptr(x), M, K, ld_x, _ptr(xq), ld_xq, _ptr(sa),
+                                            _stream(stream)), "fp8rl_quant_act_tok128")
+    else:
+        _check(lib().fp8rl_quant_act_tok128_ex(_ptr(x), M, K, ld_x, _ptr(xq), ld_xq, _ptr(sa), fmt,
+                                               _stream(stream)), "fp8rl_quant_act_tok128_ex")
     return xq, sa
+
+
+def fp8rl_quant_act_tok128_ex(x, xq=None, sa=None, scale_fmt=FP8RL_SCALE_FP32, stream=None):
+    return fp8rl_quant_act_tok128(x, xq, sa, stream=stream, scale=scale_fmt)
 
 
 def fp8rl_workspace_bytes(op: int, M: int, N: int, K: int, E: int = 0) -> int:
@@ -226,7 +278,9 @@ def _accum_code(accum, out_dtype) -> int:
         return FP8RL_ACCUM_FP8
     if accum in ("f16", FP8RL_ACCUM_F16):
         return FP8RL_ACCUM_F16
-    raise ValueError("accum must be None, 'fp8' or 'f16'")
+    if accum in ("mx", FP8RL_ACCUM_MX):
+        return FP8RL_ACCUM_MX
+    raise ValueError("accum must be None, 'fp8', 'f16' or 'mx'")
 
 
 def _out_code(dtype) -> int:

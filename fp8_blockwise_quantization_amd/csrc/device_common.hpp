@@ -72,6 +72,25 @@ __device__ __forceinline__ float scale_from_amax_bits(uint32_t amax_bits16) {
   return (float)(amax * (1.0 / 448.0));
 }
 
+// Power-of-two scale (the NeMo RL blog's power-of-2 scaling-factor option): the least 2^e with
+// 448 * 2^e >= amax, e >= -127 (the smallest E8M0 value), 1 when amax == 0. With amax = f 2^E,
+// f in [0.5, 1): 448 = 0.875 * 2^9, so e = E - 9 when f <= 0.875 and E - 8 otherwise; for a
+// normal float32 amax with biased exponent ef and fraction bits t, E = ef - 126 and
+// f > 0.875 <=> t > 0x600000. Exact: only exponent arithmetic.
+__device__ __forceinline__ float pow2_scale_from_amax_bits(uint32_t amax_bits16) {
+  if (amax_bits16 == 0) return 1.0f;
+  const uint32_t a = amax_bits16 << 16;
+  const int ef = (int)(a >> 23);
+  int e = ef - 135 + ((a & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+  if (ef == 0 || e < -127) e = -127;
+  return e >= -126 ? __uint_as_float((uint32_t)(e + 127) << 23) : __uint_as_float(0x00400000u);
+}
+
+// E8M0 exponent byte of a power-of-two float32 scale (2^-127 .. 2^127): its biased exponent
+// field (the subnormal 2^-127 has field 0, which is E8M0's 2^-127). The fraction bits of a scale
+// that is not a power of two are ignored.
+__device__ __forceinline__ int e8m0_of(float s) { return (int)((__float_as_uint(s) >> 23) & 0xFFu); }
+
 // Reciprocal of a (positive, finite, possibly subnormal) float32 scale, correctly rounded in
 // float64. Used once per group/block; the element quotients are then formed as float64 products.
 __device__ __forceinline__ double recip_f64(float s) { return 1.0 / (double)s; }

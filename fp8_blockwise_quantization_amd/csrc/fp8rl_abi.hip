@@ -78,13 +78,15 @@ int check_weight(const fp8rl_weight_desc& d) {
 
 // Launch the (already validated) descriptors in groups that fit one kernel's argument block
 // and keep every grid below 2^24 workgroups.
-int launch_weights(const fp8rl_weight_desc* descs, int32_t count, hipStream_t stream) {
+int launch_weights(const fp8rl_weight_desc* descs, int32_t count, int pow2, hipStream_t stream) {
   fp8rl::WeightBatch b{};
+  b.pow2 = pow2;
   int64_t blocks = 0;
   auto flush = [&]() -> int {
     if (b.count == 0) return FP8RL_OK;
     hipError_t e = fp8rl::launch_quant_weight_batch(b, (int)blocks, stream);
     b = fp8rl::WeightBatch{};
+    b.pow2 = pow2;
     blocks = 0;
     return hip_status(e);
   };
@@ -109,24 +111,38 @@ int launch_weights(const fp8rl_weight_desc* descs, int32_t count, hipStream_t st
 
 }  // namespace
 
-int fp8rl_quant_weight_blk128(const uint16_t* w, int64_t N, int64_t K, int64_t ld_w, uint8_t* wq,
-                              int64_t ld_wq, float* sw, void* stream) {
+int fp8rl_quant_weight_blk128_ex(const uint16_t* w, int64_t N, int64_t K, int64_t ld_w,
+                                 uint8_t* wq, int64_t ld_wq, float* sw, int scale_fmt,
+                                 void* stream) {
+  if (scale_fmt != FP8RL_SCALE_FP32 && scale_fmt != FP8RL_SCALE_POW2) return FP8RL_ERR_ARG;
   const fp8rl_weight_desc d{w, wq, sw, N, K, ld_w, ld_wq};
   if (int s = check_weight(d)) return s;
-  return launch_weights(&d, 1, as_stream(stream));
+  return launch_weights(&d, 1, scale_fmt == FP8RL_SCALE_POW2, as_stream(stream));
 }
 
-int fp8rl_quant_weight_blk128_batched(const fp8rl_weight_desc* descs, int32_t count, void* stream) {
+int fp8rl_quant_weight_blk128(const uint16_t* w, int64_t N, int64_t K, int64_t ld_w, uint8_t* wq,
+                              int64_t ld_wq, float* sw, void* stream) {
+  return fp8rl_quant_weight_blk128_ex(w, N, K, ld_w, wq, ld_wq, sw, FP8RL_SCALE_FP32, stream);
+}
+
+int fp8rl_quant_weight_blk128_batched_ex(const fp8rl_weight_desc* descs, int32_t count,
+                                         int scale_fmt, void* stream) {
+  if (scale_fmt != FP8RL_SCALE_FP32 && scale_fmt != FP8RL_SCALE_POW2) return FP8RL_ERR_ARG;
   if (count < 0) return FP8RL_ERR_ARG;
   if (count == 0) return FP8RL_OK;
   if (!descs) return FP8RL_ERR_NULL;
   for (int32_t i = 0; i < count; ++i)
     if (int s = check_weight(descs[i])) return s;
-  return launch_weights(descs, count, as_stream(stream));
+  return launch_weights(descs, count, scale_fmt == FP8RL_SCALE_POW2, as_stream(stream));
 }
 
-int fp8rl_quant_act_tok128(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x, uint8_t* xq,
-                           int64_t ld_xq, float* sa, void* stream) {
+int fp8rl_quant_weight_blk128_batched(const fp8rl_weight_desc* descs, int32_t count, void* stream) {
+  return fp8rl_quant_weight_blk128_batched_ex(descs, count, FP8RL_SCALE_FP32, stream);
+}
+
+int fp8rl_quant_act_tok128_ex(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x, uint8_t* xq,
+                              int64_t ld_xq, float* sa, int scale_fmt, void* stream) {
+  if (scale_fmt != FP8RL_SCALE_FP32 && scale_fmt != FP8RL_SCALE_POW2) return FP8RL_ERR_ARG;
   if (int s = check_dims(M, K, 0)) return s;
   if (M == 0 || K == 0) return FP8RL_OK;
   if (!x || !xq || !sa) return FP8RL_ERR_NULL;
@@ -134,7 +150,13 @@ int fp8rl_quant_act_tok128(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x
   if (M * (K / 128) >= (int64_t{1} << 30)) return FP8RL_ERR_SHAPE;  // grid limit
   if (!aligned(x, 16) || !aligned(xq, 16) || !aligned(sa, 4) || (ld_x * 2) % 16 || ld_xq % 16)
     return FP8RL_ERR_ALIGN;
-  return hip_status(fp8rl::launch_quant_act(x, M, K, ld_x, xq, ld_xq, sa, as_stream(stream)));
+  return hip_status(fp8rl::launch_quant_act(x, M, K, ld_x, xq, ld_xq, sa,
+                                            scale_fmt == FP8RL_SCALE_POW2, as_stream(stream)));
+}
+
+int fp8rl_quant_act_tok128(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x, uint8_t* xq,
+                           int64_t ld_xq, float* sa, void* stream) {
+  return fp8rl_quant_act_tok128_ex(x, M, K, ld_x, xq, ld_xq, sa, FP8RL_SCALE_FP32, stream);
 }
 
 size_t fp8rl_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int32_t E) {
@@ -151,7 +173,8 @@ int fp8rl_gemm_w8a8_blockscaled(const uint8_t* xq, const float* sa, const uint8_
   if (int s = check_dims(M, N, K)) return s;
   if (M == 0) return FP8RL_OK;
   if (int s = check_gemm_common(xq, sa, wq, sw, N, K, y, y_dtype, ld_y)) return s;
-  if (accum != FP8RL_ACCUM_FP8 && accum != FP8RL_ACCUM_F16) return FP8RL_ERR_ARG;
+  if (accum != FP8RL_ACCUM_FP8 && accum != FP8RL_ACCUM_F16 && accum != FP8RL_ACCUM_MX)
+    return FP8RL_ERR_ARG;
   if (((M + 127) / 128) * (N / 64) >= (int64_t{1} << 22)) return FP8RL_ERR_SHAPE;  // grid limit
   const fp8rl::GemmPlan plan = fp8rl::plan_gemm(M, N, K);
   if (plan.workspace_bytes > 0) {
@@ -159,8 +182,7 @@ int fp8rl_gemm_w8a8_blockscaled(const uint8_t* xq, const float* sa, const uint8_
     if (!aligned(workspace, 16)) return FP8RL_ERR_ALIGN;
   }
   return hip_status(fp8rl::launch_gemm(xq, sa, wq, sw, M, N, K, y, y_dtype == FP8RL_OUT_F32, ld_y,
-                                       accum == FP8RL_ACCUM_F16, workspace, plan,
-                                       as_stream(stream)));
+                                       accum, workspace, plan, as_stream(stream)));
 }
 
 int fp8rl_grouped_gemm_w8a8(const uint8_t* xq, const float* sa, const uint8_t* wq, const float* sw,
@@ -172,7 +194,8 @@ int fp8rl_grouped_gemm_w8a8(const uint8_t* xq, const float* sa, const uint8_t* w
   if (M_total == 0) return FP8RL_OK;
   if (!expert_offsets) return FP8RL_ERR_NULL;
   if (int s = check_gemm_common(xq, sa, wq, sw, N, K, y, y_dtype, N)) return s;
-  if (accum != FP8RL_ACCUM_FP8 && accum != FP8RL_ACCUM_F16) return FP8RL_ERR_ARG;
+  if (accum != FP8RL_ACCUM_FP8 && accum != FP8RL_ACCUM_F16 && accum != FP8RL_ACCUM_MX)
+    return FP8RL_ERR_ARG;
   if (!aligned(expert_offsets, 4)) return FP8RL_ERR_ALIGN;
   if (((M_total + 127) / 128 + E) * (N / 128) >= (int64_t{1} << 22)) return FP8RL_ERR_SHAPE;
   if ((int64_t)E * N * K >= (int64_t{1} << 40)) return FP8RL_ERR_SHAPE;
@@ -182,8 +205,8 @@ int fp8rl_grouped_gemm_w8a8(const uint8_t* xq, const float* sa, const uint8_t* w
     if (!aligned(workspace, 16)) return FP8RL_ERR_ALIGN;
   }
   return hip_status(fp8rl::launch_grouped_gemm(xq, sa, wq, sw, expert_offsets, E, M_total, N, K, y,
-                                               y_dtype == FP8RL_OUT_F32, accum == FP8RL_ACCUM_F16,
-                                               workspace, plan, as_stream(stream)));
+                                               y_dtype == FP8RL_OUT_F32, accum, workspace, plan,
+                                               as_stream(stream)));
 }
 
 }  // extern "C"

@@ -426,9 +426,10 @@ __device__ __forceinline__ void wait_slice_and_barrier(int ahead) {
 // sums finished long before), so the VALU works while the matrix core runs and no FMA waits on
 // the sum it consumes; the next row tile's operands are read from LDS meanwhile. Scheduling
 // fences keep the compiler from regrouping the FMAs next to the sums they depend on.
-template <class T, bool PRECISE>
+template <class T, int ACC>
 __device__ __forceinline__ void mma_slice_big(const uint8_t* stage, float swv, int wm, int wn,
                                               int lane, v4f (&acc)[T::TM][T::TN]) {
+  constexpr bool PRECISE = ACC == 1;
   const uint8_t* sA = stage;
   const uint8_t* sB = stage + T::A_BYTES;
   const float* sS = reinterpret_cast<const float*>(stage + T::A_BYTES + T::B_BYTES);
@@ -436,6 +437,21 @@ __device__ __forceinline__ void mma_slice_big(const uint8_t* stage, float swv, i
   v8i bf[T::TN];
 #pragma unroll
   for (int j = 0; j < T::TN; ++j) bf[j] = load_frag(sB, wn * T::WN + j * 16 + r16, kq);
+  if constexpr (ACC == 2) {
+    // power-of-two scales: lane l's E8M0 exponents scale A row l % 16 and B column l % 16 of
+    // every 32-wide K block it holds; the instruction adds the running sum itself
+    const int swe = e8m0_of(swv);
+#pragma unroll
+    for (int i = 0; i < T::TM; ++i) {
+      const v8i af = load_frag(sA, wm * T::WM + i * 16 + r16, kq);
+      const int sae = e8m0_of(sS[wm * T::WM + i * 16 + r16]);
+#pragma unroll
+      for (int j = 0; j < T::TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[j], acc[i][j], 0, 0, 0,
+                                                                     sae, 0, swe);
+    }
+    return;
+  }
   v8i af = load_frag(sA, wm * T::WM + r16, kq);
   v4f sc = *reinterpret_cast<const v4f*>(sS + wm * T::WM + 4 * kq) * swv;
   v4f p_prev[T::TN];
@@ -471,7 +487,7 @@ __device__ __forceinline__ void mma_slice_big(const uint8_t* stage, float swv, i
 // 128-column blocks read into LDS once. A / SA start at the tile's first row, B at its first
 // column (weight row); SW is the weight-scale matrix [N/128][KB] (of the tile's expert); Y rows
 // y_row0 + r, r < m_valid, pitch ldy. The caller's previous use of the LDS arrays must be over.
-template <class T, bool PRECISE>
+template <class T, int ACC>
 __device__ __forceinline__ void big_tile(const GemmArgs& p, uint8_t* stages,
                                          float (*sw_s)[kMaxSlices], const uint8_t* A,
                                          const float* SA, int m_valid, const uint8_t* B,
@@ -504,11 +520,11 @@ __device__ __forceinline__ void big_tile(const GemmArgs& p, uint8_t* stages,
     for (int kb = 0; kb < KB; kb += 2) {
       wait_dma_and_barrier();
       if (kb + 1 < KB) dma_slice<T>(stage1, dp, A, B, SA, kb + 1, wave, lane);
-      mma_slice_big<T, PRECISE>(stage0, swrow[kb], wm, wn, lane, acc);
+      mma_slice_big<T, ACC>(stage0, swrow[kb], wm, wn, lane, acc);
       if (kb + 1 >= KB) break;
       wait_dma_and_barrier();
       if (kb + 2 < KB) dma_slice<T>(stage0, dp, A, B, SA, kb + 2, wave, lane);
-      mma_slice_big<T, PRECISE>(stage1, swrow[kb + 1], wm, wn, lane, acc);
+      mma_slice_big<T, ACC>(stage1, swrow[kb + 1], wm, wn, lane, acc);
     }
   } else {
     // slices kb + 1 and kb + 2 in flight while kb is multiplied
@@ -519,7 +535,7 @@ __device__ __forceinline__ void big_tile(const GemmArgs& p, uint8_t* stages,
       wait_slice_and_barrier<T>(KB - 1 - kb);
       const int nxt = cur == 0 ? 2 : cur - 1;  // (kb + 2) % 3
       if (kb + 2 < KB) dma_slice<T>(stages + nxt * T::STAGE_BYTES, dp, A, B, SA, kb + 2, wave, lane);
-      mma_slice_big<T, PRECISE>(stages + cur * T::STAGE_BYTES, swrow[kb], wm, wn, lane, acc);
+      mma_slice_big<T, ACC>(stages + cur * T::STAGE_BYTES, swrow[kb], wm, wn, lane, acc);
       cur = cur == 2 ? 0 : cur + 1;
     }
   }
@@ -545,7 +561,7 @@ __device__ __forceinline__ void big_tile(const GemmArgs& p, uint8_t* stages,
   }
 }
 
-template <class T, bool PRECISE>
+template <class T, int ACC>
 __global__ __launch_bounds__(T::NT) void gemm_big_kernel(GemmArgs p) {
   __shared__ __attribute__((aligned(16))) uint8_t stages[T::STAGES * T::STAGE_BYTES];
   __shared__ float sw_s[(T::BN + 127) / 128][kMaxSlices];
@@ -554,7 +570,7 @@ __global__ __launch_bounds__(T::NT) void gemm_big_kernel(GemmArgs p) {
   int tm, tn;
   tile_coords(blockIdx.x, tiles_m * tiles_n, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * T::BM, n0 = tn * T::BN;
-  big_tile<T, PRECISE>(p, stages, sw_s, p.xq + (int64_t)m0 * p.K,
+  big_tile<T, ACC>(p, stages, sw_s, p.xq + (int64_t)m0 * p.K,
                        p.sa + (int64_t)m0 * p.KB, min(T::BM, p.M - m0), p.wq + (int64_t)n0 * p.K,
                        p.sw, n0, min(T::BN, p.N - n0), m0);
 }
@@ -565,7 +581,7 @@ __global__ __launch_bounds__(T::NT) void gemm_big_kernel(GemmArgs p) {
 // search. The tile list is cut into one contiguous chunk per XCD (workgroup w runs on XCD
 // w % 8), so the m-tiles of one expert -- which read the same weight panels -- and the n-tiles
 // of one m-tile -- which read the same activation rows -- share an L2.
-template <class T, bool PRECISE>
+template <class T, int ACC>
 __global__ __launch_bounds__(T::NT) void grouped_big_kernel(GemmArgs p) {
   __shared__ __attribute__((aligned(16))) uint8_t stages[T::STAGES * T::STAGE_BYTES];
   __shared__ float sw_s[(T::BN + 127) / 128][kMaxSlices];
@@ -617,7 +633,7 @@ __global__ __launch_bounds__(T::NT) void grouped_big_kernel(GemmArgs p) {
     const int row0 = r_lo + (tm_lin - s_first[e]) * T::BM;
     const int n0 = tn * T::BN;
     __syncthreads();  // the previous tile is done with the LDS arrays
-    big_tile<T, PRECISE>(p, stages, sw_s, p.xq + (int64_t)row0 * p.K,
+    big_tile<T, ACC>(p, stages, sw_s, p.xq + (int64_t)row0 * p.K,
                          p.sa + (int64_t)row0 * p.KB, min(T::BM, r_hi - row0),
                          p.wq + e * p.wq_stride + (int64_t)n0 * p.K, p.sw + e * p.sw_stride, n0,
                          min(T::BN, p.N - n0), row0);
@@ -705,10 +721,23 @@ __device__ __forceinline__ void dec_stage(uint8_t* st, const DecSlot<T>& d, int 
   reinterpret_cast<float*>(st + T::SA_OFF)[tid] = d.sa;  // copies past MPA are not read
 }
 
-template <class T, bool PRECISE>
+template <class T, int ACC>
 __device__ __forceinline__ void dec_mma(const uint8_t* st, const DecSlot<T>& d, int lane,
                                         v4f (&acc)[T::MT]) {
   const int r16 = lane & 15, kq = lane >> 4;
+  if constexpr (ACC == 2) {  // power-of-two scales applied by the matrix cores (see mma_slice_big)
+    const float* sa = reinterpret_cast<const float*>(st + T::SA_OFF);
+    const int swe = e8m0_of(d.sw);
+#pragma unroll
+    for (int i = 0; i < T::MT; ++i) {
+      acc[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+          load_frag(st, i * 16 + r16, kq), d.b, acc[i], 0, 0, 0, e8m0_of(sa[i * 16 + r16]), 0, swe);
+      asm volatile("" : "+v"(acc[i]));  // keep each slice's update in place
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    return;
+  }
+  constexpr bool PRECISE = ACC == 1;
   v4f cur[T::MT];
 #pragma unroll
   for (int i = 0; i < T::MT; ++i) cur[i] = slice_product<PRECISE>(load_frag(st, i * 16 + r16, kq), d.b);
@@ -721,7 +750,7 @@ __device__ __forceinline__ void dec_mma(const uint8_t* st, const DecSlot<T>& d, 
   }
 }
 
-template <class T, bool PRECISE>
+template <class T, int ACC>
 __global__ __launch_bounds__(T::NT) void gemm_decode_kernel(GemmArgs p) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[T::LDS_BYTES];
   __shared__ int s_flag;
@@ -752,7 +781,7 @@ __global__ __launch_bounds__(T::NT) void gemm_decode_kernel(GemmArgs p) {
     for (int u = 0; u < T::R; ++u) dec_stage<T>(buf + u * T::STAGE, ring[u], tid);
     __syncthreads();
 #pragma unroll
-    for (int u = 0; u < T::R; ++u) dec_mma<T, PRECISE>(buf + u * T::STAGE, ring[u], lane, acc);
+    for (int u = 0; u < T::R; ++u) dec_mma<T, ACC>(buf + u * T::STAGE, ring[u], lane, acc);
     // refill only once consumed, so each set keeps its registers across the loop
     if (refill_kb >= 0) {
 #pragma unroll
@@ -1013,34 +1042,34 @@ GemmPlan plan_grouped_gemm(int64_t M_total, int64_t N, int64_t K, int32_t E) {
   return pl;
 }
 
-template <class T, bool PRECISE>
+template <class T, int ACC>
 static hipError_t launch_big(const GemmArgs& a, hipStream_t stream) {
   const int tiles_m = (a.M + T::BM - 1) / T::BM;
   const int tiles_n = (a.N + T::BN - 1) / T::BN;
-  hipLaunchKernelGGL((gemm_big_kernel<T, PRECISE>), dim3((unsigned)(tiles_m * tiles_n)), dim3(T::NT),
+  hipLaunchKernelGGL((gemm_big_kernel<T, ACC>), dim3((unsigned)(tiles_m * tiles_n)), dim3(T::NT),
                      0, stream, a);
   return hipGetLastError();
 }
 
-template <class T, bool PRECISE>
+template <class T, int ACC>
 static hipError_t launch_decode_t(const GemmArgs& a, const GemmPlan& pl, hipStream_t stream) {
-  hipLaunchKernelGGL((gemm_decode_kernel<T, PRECISE>), dim3((unsigned)(a.N / T::BN), (unsigned)pl.splits),
+  hipLaunchKernelGGL((gemm_decode_kernel<T, ACC>), dim3((unsigned)(a.N / T::BN), (unsigned)pl.splits),
                      dim3(T::NT), 0, stream, a);
   return hipGetLastError();
 }
 
-template <int R, bool PRECISE>
+template <int R, int ACC>
 static hipError_t launch_decode_d(const GemmArgs& a, const GemmPlan& pl, hipStream_t stream) {
-  if (a.M <= 16) return launch_decode_t<Dec<1, R>, PRECISE>(a, pl, stream);
-  if (a.M <= 32) return launch_decode_t<Dec<2, R>, PRECISE>(a, pl, stream);
-  return launch_decode_t<Dec<4, R>, PRECISE>(a, pl, stream);
+  if (a.M <= 16) return launch_decode_t<Dec<1, R>, ACC>(a, pl, stream);
+  if (a.M <= 32) return launch_decode_t<Dec<2, R>, ACC>(a, pl, stream);
+  return launch_decode_t<Dec<4, R>, ACC>(a, pl, stream);
 }
 
-template <bool PRECISE>
+template <int ACC>
 static hipError_t launch_decode(const GemmArgs& a, const GemmPlan& pl, hipStream_t stream) {
-  if (pl.depth == 8) return launch_decode_d<4, PRECISE>(a, pl, stream);
-  if (pl.depth == 4) return launch_decode_d<2, PRECISE>(a, pl, stream);
-  return launch_decode_d<1, PRECISE>(a, pl, stream);
+  if (pl.depth == 8) return launch_decode_d<4, ACC>(a, pl, stream);
+  if (pl.depth == 4) return launch_decode_d<2, ACC>(a, pl, stream);
+  return launch_decode_d<1, ACC>(a, pl, stream);
 }
 
 template <class T, bool PRECISE>
@@ -1057,7 +1086,10 @@ static hipError_t launch_dense(const GemmArgs& a, const GemmPlan& pl, hipStream_
 
 hipError_t launch_gemm(const uint8_t* xq, const float* sa, const uint8_t* wq, const float* sw,
                        int64_t M, int64_t N, int64_t K, void* y, int out_f32, int64_t ld_y,
-                       bool precise, void* workspace, const GemmPlan& pl, hipStream_t stream) {
+                       int accum, void* workspace, const GemmPlan& pl, hipStream_t stream) {
+  // accum: 0 FP8 slice sums, 1 f16 slice sums, 2 power-of-two scales in the matrix cores (the
+  // register-staged tiles have no such form: their FP8 form gives the same results then)
+  const bool precise = accum == 1;
   GemmArgs a{};
   a.xq = xq;
   a.sa = sa;
@@ -1081,13 +1113,14 @@ hipError_t launch_gemm(const uint8_t* xq, const float* sa, const uint8_t* wq, co
   switch (pl.cfg) {
     case kCfgBigWide:
       // the f16 form needs more registers per wave than the 8-wave tile leaves: 4-wave tiles
-      return precise ? launch_big<BigNarrow, true>(a, stream)
-                     : launch_big<BigWide, false>(a, stream);
+      if (accum == 1) return launch_big<BigNarrow, 1>(a, stream);
+      return accum == 2 ? launch_big<BigWide, 2>(a, stream) : launch_big<BigWide, 0>(a, stream);
     case kCfgBigNarrow:
-      return precise ? launch_big<BigNarrow, true>(a, stream)
-                     : launch_big<BigNarrow, false>(a, stream);
+      if (accum == 1) return launch_big<BigNarrow, 1>(a, stream);
+      return accum == 2 ? launch_big<BigNarrow, 2>(a, stream) : launch_big<BigNarrow, 0>(a, stream);
     case kCfgDecode:  // reduces its own split tiles
-      return precise ? launch_decode<true>(a, pl, stream) : launch_decode<false>(a, pl, stream);
+      if (accum == 1) return launch_decode<1>(a, pl, stream);
+      return accum == 2 ? launch_decode<2>(a, pl, stream) : launch_decode<0>(a, pl, stream);
     case kCfgLarge:
       e = precise ? launch_dense<TileLarge, true>(a, pl, stream)
                   : launch_dense<TileLarge, false>(a, pl, stream);
@@ -1107,9 +1140,10 @@ hipError_t launch_gemm(const uint8_t* xq, const float* sa, const uint8_t* wq, co
 hipError_t launch_grouped_gemm(const uint8_t* xq, const float* sa, const uint8_t* wq,
                                const float* sw, const int32_t* offsets, int32_t E,
                                int64_t M_total, int64_t N, int64_t K, void* y, int out_f32,
-                               bool precise, void* workspace, const GemmPlan& pl,
+                               int accum, void* workspace, const GemmPlan& pl,
                                hipStream_t stream) {
   (void)workspace;
+  const bool precise = accum == 1;
   using T = TileLarge;
   GemmArgs a{};
   a.xq = xq;
@@ -1132,12 +1166,13 @@ hipError_t launch_grouped_gemm(const uint8_t* xq, const float* sa, const uint8_t
   a.sw_stride = (N / 128) * (K / 128);
   if (pl.cfg == kCfgGroupedBig) {
     a.tiles_n = (int)((N + BigGroup::BN - 1) / BigGroup::BN);
-    if (precise)
-      hipLaunchKernelGGL((grouped_big_kernel<BigGroup, true>), dim3((unsigned)pl.splits),
-                         dim3(BigGroup::NT), 0, stream, a);
+    const dim3 grid((unsigned)pl.splits), block(BigGroup::NT);
+    if (accum == 1)
+      hipLaunchKernelGGL((grouped_big_kernel<BigGroup, 1>), grid, block, 0, stream, a);
+    else if (accum == 2)
+      hipLaunchKernelGGL((grouped_big_kernel<BigGroup, 2>), grid, block, 0, stream, a);
     else
-      hipLaunchKernelGGL((grouped_big_kernel<BigGroup, false>), dim3((unsigned)pl.splits),
-                         dim3(BigGroup::NT), 0, stream, a);
+      hipLaunchKernelGGL((grouped_big_kernel<BigGroup, 0>), grid, block, 0, stream, a);
     return hipGetLastError();
   }
   a.tiles_n = (int)(N / T::BN);

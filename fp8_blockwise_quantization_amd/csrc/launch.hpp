@@ -19,10 +19,11 @@ struct WeightBatch {
   int kb[kWeightBatch];
   int block_begin[kWeightBatch];  // first grid block of matrix i (prefix sum of block counts)
   int count;
+  int pow2;  // power-of-two scales instead of fp32(amax / 448)
 };
 hipError_t launch_quant_weight_batch(const WeightBatch& b, int total_blocks, hipStream_t stream);
 hipError_t launch_quant_act(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x, uint8_t* xq,
-                            int64_t ld_xq, float* sa, hipStream_t stream);
+                            int64_t ld_xq, float* sa, int pow2, hipStream_t stream);
 hipError_t launch_encode(const float* v, int64_t n, uint8_t* out, hipStream_t stream);
 
 // GEMM planning: which tile configuration and how many K splits a shape uses. Pure host logic,
@@ -40,11 +41,11 @@ GemmPlan plan_grouped_gemm(int64_t M_total, int64_t N, int64_t K, int32_t E);
 
 hipError_t launch_gemm(const uint8_t* xq, const float* sa, const uint8_t* wq, const float* sw,
                        int64_t M, int64_t N, int64_t K, void* y, int out_f32, int64_t ld_y,
-                       bool precise, void* workspace, const GemmPlan& plan, hipStream_t stream);
+                       int accum, void* workspace, const GemmPlan& plan, hipStream_t stream);
 hipError_t launch_grouped_gemm(const uint8_t* xq, const float* sa, const uint8_t* wq,
                                const float* sw, const int32_t* offsets, int32_t E,
                                int64_t M_total, int64_t N, int64_t K, void* y, int out_f32,
-                               bool precise, void* workspace, const GemmPlan& plan,
+                               int accum, void* workspace, const GemmPlan& plan,
                                hipStream_t stream);
 
 }  // namespace fp8rl

@@ -3,6 +3,8 @@
 // Quantization rule (Unified FP8 blog, quick-read section; V_max = 448 and the E4M3 layout from
 // the FP8-RL write-up, section 1; FP32 scales from the NeMo RL blog, Table 1):
 //   S = fp32(amax / 448) (1 when amax == 0),  code = E4M3_RNE_sat(fp32(x) / S).
+// With power-of-two scales (the NeMo RL blog's advanced FP8 options) S is instead the least power
+// of two not below amax / 448 (at least 2^-127); the element step is the same.
 // Both quotients are the IEEE float32 ones; see device_common.hpp for how they are formed exactly
 // without a per-element division.
 #include "device_common.hpp"
@@ -22,7 +24,8 @@ namespace fp8rl {
 // ---------------------------------------------------------------------------------------------
 __device__ __forceinline__ void quant_weight_block(const uint16_t* __restrict__ w, int64_t ld_w,
                                                    uint8_t* __restrict__ wq, int64_t ld_wq,
-                                                   float* __restrict__ sw_out, int bi, int bj) {
+                                                   float* __restrict__ sw_out, int bi, int bj,
+                                                   int pow2) {
   const int t = threadIdx.x;
   const int c = t & 15;
   const int r0 = t >> 4;
@@ -46,7 +49,7 @@ __device__ __forceinline__ void quant_weight_block(const uint16_t* __restrict__ 
   m = m > red[2] ? m : red[2];
   m = m > red[3] ? m : red[3];
 
-  const float S = scale_from_amax_bits(m);
+  const float S = pow2 ? pow2_scale_from_amax_bits(m) : scale_from_amax_bits(m);
   const double r = recip_f64(S);
   if (t == 0) *sw_out = S;
 
@@ -64,7 +67,7 @@ __global__ __launch_bounds__(256) void quant_weight_blk128_kernel(WeightBatch b)
   const int local = bid - b.block_begin[t];
   const int KB = b.kb[t];
   const int bi = local / KB, bj = local - (local / KB) * KB;
-  quant_weight_block(b.w[t], b.ld_w[t], b.wq[t], b.ld_wq[t], b.sw[t] + local, bi, bj);
+  quant_weight_block(b.w[t], b.ld_w[t], b.wq[t], b.ld_wq[t], b.sw[t] + local, bi, bj, b.pow2);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -77,7 +80,7 @@ __global__ __launch_bounds__(256) void quant_weight_blk128_kernel(WeightBatch b)
 template <int STEPS>
 __global__ __launch_bounds__(256) void quant_act_tok128_kernel(
     const uint16_t* __restrict__ x, int64_t ld_x, uint8_t* __restrict__ xq, int64_t ld_xq,
-    float* __restrict__ sa, int KB, int64_t total_groups) {
+    float* __restrict__ sa, int KB, int64_t total_groups, int pow2) {
   const int lane16 = threadIdx.x & 15;
   const int64_t g0 = (int64_t)blockIdx.x * (16 * STEPS) + (threadIdx.x >> 4);
 
@@ -97,7 +100,7 @@ __global__ __launch_bounds__(256) void quant_act_tok128_kernel(
     const int64_t g = g0 + 16 * s;
     // every lane of the row takes part in the reduction, whether or not its group exists
     const uint32_t m = row16_max_u32(hmax_u16(amax8_pk(v[s])));
-    const float S = scale_from_amax_bits(m);
+    const float S = pow2 ? pow2_scale_from_amax_bits(m) : scale_from_amax_bits(m);
     const double r = recip_f64(S);
     if (g < total_groups) {
       const int64_t row = g / KB, slice = g - (g / KB) * KB;
@@ -156,17 +159,17 @@ hipError_t launch_quant_weight_batch(const WeightBatch& b, int total_blocks, hip
 }
 
 hipError_t launch_quant_act(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x, uint8_t* xq,
-                            int64_t ld_xq, float* sa, hipStream_t stream) {
+                            int64_t ld_xq, float* sa, int pow2, hipStream_t stream) {
   const int KB = (int)(K / kBlock);
   const int64_t groups = M * KB;
   if (groups >= int64_t{64} * 1024) {  // >= 1024 workgroups even at 4 steps each
     const int64_t wgs = (groups + 63) / 64;
     hipLaunchKernelGGL(quant_act_tok128_kernel<4>, dim3((unsigned)wgs), dim3(256), 0, stream, x,
-                       ld_x, xq, ld_xq, sa, KB, groups);
+                       ld_x, xq, ld_xq, sa, KB, groups, pow2);
   } else {
     const int64_t wgs = (groups + 15) / 16;
     hipLaunchKernelGGL(quant_act_tok128_kernel<1>, dim3((unsigned)wgs), dim3(256), 0, stream, x,
-                       ld_x, xq, ld_xq, sa, KB, groups);
+                       ld_x, xq, ld_xq, sa, KB, groups, pow2);
   }
   return hipGetLastError();
 }

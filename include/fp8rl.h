@@ -81,7 +81,30 @@ typedef enum { FP8RL_OP_GEMM = 0, FP8RL_OP_GROUPED_GEMM = 1 } fp8rl_op;
  *   FP8RL_ACCUM_F16  the same E4M3 codes widened exactly to f16 and summed by f16 matrix-core
  *                    instructions, whose adder keeps float32-level precision. Half the FP8 rate.
  */
-typedef enum { FP8RL_ACCUM_FP8 = 0, FP8RL_ACCUM_F16 = 1 } fp8rl_accum;
+typedef enum { FP8RL_ACCUM_FP8 = 0, FP8RL_ACCUM_F16 = 1, FP8RL_ACCUM_MX = 2 } fp8rl_accum;
+/*
+ *   FP8RL_ACCUM_MX   for power-of-two scales (FP8RL_SCALE_POW2): the block scales are applied by
+ *                    the block-scaled FP8 matrix-core instruction (v_mfma_scale_f32_16x16x128_f8f6f4,
+ *                    one E8M0 exponent per 32 K-values of a row; gfx950 has the E8M0 scaling units
+ *                    the NeMo RL blog and the Unified FP8 blog say Hopper lacks), which also adds the
+ *                    running float32 sum, so no per-slice float32 rescale is needed. Each slice sum
+ *                    has the FP8 form's precision. Every sa and sw must be a power of two in
+ *                    [2^-127, 2^127]; the fraction bits of any other scale are ignored (the scale
+ *                    is taken as 2^floor(log2 s)). Shapes without such a kernel (64 < M < 1024,
+ *                    or an odd K/128 at M <= 64) compute as FP8RL_ACCUM_FP8, which gives the same
+ *                    results for power-of-two scales.
+ */
+
+/*
+ * Scale format of the quantizers (the _ex entry points):
+ *   FP8RL_SCALE_FP32  S = fp32(amax / 448) [UFP8 quick-read; NEMO Table 1] -- the default.
+ *   FP8RL_SCALE_POW2  S = the least power of two with 448 * S >= amax, at least 2^-127, 1 when
+ *                     amax == 0 (the NeMo RL blog's advanced option that makes the weight and
+ *                     activation scaling factors powers of 2 instead of FP32). Codes are then the
+ *                     exact quotients x / S rounded onto the E4M3 grid; the scales are exact E8M0
+ *                     values stored as float32.
+ */
+typedef enum { FP8RL_SCALE_FP32 = 0, FP8RL_SCALE_POW2 = 1 } fp8rl_scale_fmt;
 
 /*
  * Element-wise E4M3 encoder: out[i] = nearest E4M3 code of v[i], ties to the even mantissa,
@@ -108,6 +131,11 @@ int fp8rl_encode_e4m3_f32(const float* v, int64_t n, uint8_t* out, void* stream)
 int fp8rl_quant_weight_blk128(const uint16_t* w, int64_t N, int64_t K, int64_t ld_w, uint8_t* wq,
                               int64_t ld_wq, float* sw, void* stream);
 
+/* The same with an explicit scale format (fp8rl_scale_fmt); FP8RL_ERR_ARG for an unknown one. */
+int fp8rl_quant_weight_blk128_ex(const uint16_t* w, int64_t N, int64_t K, int64_t ld_w,
+                                 uint8_t* wq, int64_t ld_wq, float* sw, int scale_fmt,
+                                 void* stream);
+
 /* One weight matrix of a batched re-quantization (all pointers device, same rules as above). */
 typedef struct {
   const uint16_t* w; /* bf16 W[N][ld_w] */
@@ -126,6 +154,10 @@ typedef struct {
  */
 int fp8rl_quant_weight_blk128_batched(const fp8rl_weight_desc* descs, int32_t count, void* stream);
 
+/* The same with an explicit scale format for every matrix (fp8rl_scale_fmt). */
+int fp8rl_quant_weight_blk128_batched_ex(const fp8rl_weight_desc* descs, int32_t count,
+                                         int scale_fmt, void* stream);
+
 /*
  * Dynamic activation quantization, 1x128 groups per token row [NEMO, Table 1; FP8RL, section 1;
  * UFP8, quick-read].  For row m and group g (columns 128g..128g+127 of X[M][K]):
@@ -139,6 +171,10 @@ int fp8rl_quant_weight_blk128_batched(const fp8rl_weight_desc* descs, int32_t co
 int fp8rl_quant_act_tok128(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x, uint8_t* xq,
                            int64_t ld_xq, float* sa, void* stream);
 
+/* The same with an explicit scale format (fp8rl_scale_fmt). */
+int fp8rl_quant_act_tok128_ex(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x, uint8_t* xq,
+                              int64_t ld_xq, float* sa, int scale_fmt, void* stream);
+
 /*
  * Blockwise-scaled W8A8 GEMM, Y = X W^T [NEMO, "FP8 for linear layers in RL"; FP8RL, section 1]:
  *   Y[m][n] = sum_kb sa[m][kb] * sw[n/128][kb] * sum_{k in slice kb} dec(Xq[m][k]) * dec(Wq[n][k])
@@ -149,7 +185,7 @@ int fp8rl_quant_act_tok128(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x
  *   xq, sa : activation codes [M][K] (pitch K) and scales [M][K/128]
  *   wq, sw : weight codes [N][K] (pitch K) and scales [N/128][K/128]
  *   y      : output [M][ld_y] (ld_y >= N) of type y_dtype
- *   accum  : FP8RL_ACCUM_FP8 or FP8RL_ACCUM_F16 (see fp8rl_accum)
+ *   accum  : FP8RL_ACCUM_FP8, FP8RL_ACCUM_F16 or FP8RL_ACCUM_MX (see fp8rl_accum)
  *   workspace, workspace_bytes: scratch of at least fp8rl_workspace_bytes(FP8RL_OP_GEMM, M, N, K, 0)
  *            bytes (device, 16-byte aligned; may be NULL when that size is 0). Its first
  *            FP8RL_WORKSPACE_HEADER_BYTES bytes hold arrival counters of the K-split reduction:

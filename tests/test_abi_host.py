@@ -32,10 +32,27 @@ def L():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 9
+    assert len(names) == 12
     for n in names:
         assert hasattr(L, n), n
     assert sorted(_lib.EXPORTED) == names
+
+
+def test_scale_format_and_accum_validation(L):
+    # unknown scale format / accumulation mode: rejected before anything else
+    assert L.fp8rl_quant_weight_blk128_ex(A, 128, 128, 128, A, 128, A, 2, None) == EARG
+    assert L.fp8rl_quant_weight_blk128_ex(A, 128, 128, 128, A, 128, A, -1, None) == EARG
+    assert L.fp8rl_quant_weight_blk128_ex(A, 0, 128, 128, A, 128, A, 1, None) == OK
+    assert L.fp8rl_quant_weight_blk128_ex(A + 2, 128, 128, 128, A, 128, A, 1, None) == EALIGN
+    assert L.fp8rl_quant_act_tok128_ex(A, 4, 128, 128, A, 128, A, 7, None) == EARG
+    assert L.fp8rl_quant_act_tok128_ex(A, 0, 128, 128, A, 128, A, 1, None) == OK
+    assert L.fp8rl_quant_act_tok128_ex(None, 4, 128, 128, A, 128, A, 1, None) == ENULL
+    assert L.fp8rl_quant_weight_blk128_batched_ex(None, 0, 1, None) == OK
+    assert L.fp8rl_quant_weight_blk128_batched_ex(None, 1, 1, None) == ENULL
+    assert L.fp8rl_quant_weight_blk128_batched_ex(None, 1, 3, None) == EARG
+    g = L.fp8rl_gemm_w8a8_blockscaled
+    assert g(A, A, A, A, 64, 256, 256, A, 0, 256, 3, None, 0, None) == EARG
+    assert g(A, A, A, A, 0, 256, 256, A, 0, 256, 2, None, 0, None) == OK
 
 
 def test_status_strings_and_version(L):
@@ -110,7 +127,7 @@ def test_gemm_validation(L):
     assert call(M=-1) == ESHAPE
     assert call(ldy=128) == ESHAPE
     assert call(dt=5) == EDTYPE
-    assert call(acc=2) == EARG
+    assert call(acc=3) == EARG  # (2 is FP8RL_ACCUM_MX)
     assert call(acc=-1) == EARG
     assert call(xq=A + 1) == EALIGN
     assert call(ldy=260) == EALIGN  # 520-byte bf16 pitch
