@@ -54,6 +54,9 @@ def parse():
                     choices=["qwen3-8b-decode", "qwen3-8b-prefill", "llama31-8b-mlp",
                              "llama31-8b-weight-sync", "qwen3-30b-a3b-moe"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--scales", default="fp32", choices=["fp32", "pow2"],
+                    help="block-scale format: fp32(amax/448) (default) or powers of two, whose "
+                         "GEMMs apply the scales in the matrix cores (accum 'mx')")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 1 GiB device copy (a known-size reference for the "
@@ -137,8 +140,10 @@ class DenseBlock:
     per weight copy into a HIP graph and replayed, so host launch overhead does not pace the GPU.
     """
 
-    def __init__(self, torch, fq, synth, linears, M, seed, requant=True):
+    def __init__(self, torch, fq, synth, linears, M, seed, requant=True, scales="fp32"):
         self.torch, self.fq = torch, fq
+        self.scales = scales
+        self.accum = "mx" if scales == "pow2" else None
         self.linears, self.M, self.requant = linears, M, requant
         dev = "cuda"
         wbytes = sum(2 * N * K for _, N, K in linears)
@@ -169,14 +174,21 @@ class DenseBlock:
         self.t_w = KernelTimer(torch)
         self.graphs = None
 
+    def roofline_us(self):
+        """Roofline time of the captured part: per GEMM max(flops / FP8 peak, bytes / HBM peak),
+        plus the activation quantizations at HBM peak."""
+        t = sum(max(2 * self.M * N * K / (FP8_PEAK_TFLOPS * 1e12), g_bytes(self.M, N, K) /
+                    (HBM_PEAK_GBS * 1e9)) for _, N, K in self.linears)
+        return 1e6 * (t + self.bytes_a / (HBM_PEAK_GBS * 1e9))
+
     def requant_step(self, c):
-        self.fq.quant_weights(None, None, None, descs=self.descs[c])
+        self.fq.quant_weights(None, None, None, descs=self.descs[c], scale=self.scales)
 
     def linears_step(self, c):
         fq = self.fq
         for i in range(len(self.linears)):
-            fq.quant_act(self.x[i], self.xq[i], self.sa[i])
-            fq.gemm(self.xq[i], self.sa[i], self.wq[c][i], self.sw[c][i], y=self.y[i],
+            fq.quant_act(self.x[i], self.xq[i], self.sa[i], scale=self.scales)
+            fq.gemm(self.xq[i], self.sa[i], self.wq[c][i], self.sw[c][i], y=self.y[i], accum=self.accum,
                     workspace=self.ws[i])
 
     def capture(self):
@@ -243,7 +255,7 @@ def measured_traffic():
 # ------------------------------------------------------------------------------ cpu baseline
 
 
-def cpu_baseline_dense(linears, M, seed, budget_linears, min_seconds=10.0):
+def cpu_baseline_dense(linears, M, seed, budget_linears, min_seconds=10.0, scales="fp32"):
     """Time the CPU oracle on the linears of the step, in order and cycling, for at least
     `budget_linears` linears and `min_seconds` of oracle time (full per-linear work: weight
     re-quantization, activation quantization, GEMM)."""
@@ -270,14 +282,15 @@ def cpu_baseline_dense(linears, M, seed, budget_linears, min_seconds=10.0):
         w = bits(synth.weight_bf16(N, K, seed=seed + i, outlier_frac=0.001))
         x = bits(synth.act_bf16(M, K, seed=seed + 7 + i))
         t0 = time.perf_counter()
-        wq, sw = oq.quant_weight_blk128(w)
-        xq, sa = oq.quant_act_tok128(x)
+        wq, sw = oq.quant_weight_blk128(w, scale=scales)
+        xq, sa = oq.quant_act_tok128(x, scale=scales)
         og.gemm_blockscaled(xq, sa, wq, sw, out="bf16")
         elapsed += time.perf_counter() - t0
         total_bytes += w_bytes(N, K) + a_bytes(M, K) + g_bytes(M, N, K)
         done.append(name)
         i += 1
     return dict(value=total_bytes / elapsed / 1e9, unit="GB/s", cores=int(blas_threads),
+                host_cpus=os.cpu_count(), host_cpus_usable=len(os.sched_getaffinity(0)),
                 kind="oracle", seconds=elapsed,
                 sample=f"{len(done)} linears of the block at M={M} ({','.join(done)}): weight "
                        f"re-quant + activation quant + fp64 GEMM each; quantizers single-threaded "
@@ -331,26 +344,33 @@ def main():
     cfg["gemms"] = [list(g) for g in groups]
     cfg["layout"] = ("q/k/v and gate/up weights concatenated along N (one activation "
                      "quantization and one GEMM per shared input)")
-    blk = DenseBlock(torch, fq, synth, groups, M, seed=1000 + args.seed, requant=requant)
+    cfg["scales"] = args.scales
+    blk = DenseBlock(torch, fq, synth, groups, M, seed=1000 + args.seed, requant=requant,
+                     scales=args.scales)
     blk.capture()
     for _ in range(args.warmup):
         blk.step()
     torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record()
-    for _ in range(args.steps):
+    # one event at every step boundary: the total gives ms_per_step, the differences the spread
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    marks[0].record()
+    for i in range(args.steps):
         blk.step(timed=True)
-    end.record()
+        marks[i + 1].record()
     torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / args.steps
+    ms = marks[0].elapsed_time(marks[-1]) / args.steps
+    per_step = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps))
     step_bytes = blk.bytes_w + blk.bytes_a + blk.bytes_g
     value = step_bytes / (ms * 1e-3) / 1e9
     lin_ms = blk.time_linears(max(args.steps, 10))
+    roof_us = blk.roofline_us()
     parts = {"act_quant_and_gemm_graph": {
         "us_per_step": 1e3 * lin_ms, "bytes": blk.bytes_a + blk.bytes_g, "flops": blk.flops,
         "gbs": (blk.bytes_a + blk.bytes_g) / (lin_ms * 1e-3) / 1e9,
-        "gemm_tflops": blk.flops / (lin_ms * 1e-3) / 1e12}}
+        "gemm_tflops": blk.flops / (lin_ms * 1e-3) / 1e12,
+        "roofline_us": roof_us, "frac_roofline": roof_us / (1e3 * lin_ms),
+        "roofline_rule": "sum over the GEMMs of max(2MNK / 5.0 PFLOP/s, bytes / 8 TB/s) plus "
+                         "activation-quant bytes / 8 TB/s"}}
     if requant:
         r = blk.t_w.result()
         parts["quant_weight_batched"] = dict(r, frac_hbm=r["gbs"] / HBM_PEAK_GBS)
@@ -369,11 +389,14 @@ def main():
                 "units_per_launch": "the block's GEMMs (graph of their act quants + GEMMs timed)"}
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline_dense(linears, M, seed=5000, budget_linears=7 if M <= 256 else 1)
+        cpu = cpu_baseline_dense(linears, M, seed=5000, budget_linears=7 if M <= 256 else 1,
+                                 scales=args.scales)
     line = {
         "metric": "blockscaled FP8 GEMM TFLOP/s (% MFMA peak); block-quant GB/s (% HBM peak)",
         "value": value, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "ms_per_step_p10_p50_p90": [per_step[len(per_step) // 10], per_step[len(per_step) // 2],
+                                    per_step[(9 * len(per_step)) // 10]],
         "dtype": "fp8-e4m3 x fp8-e4m3 -> f32 accumulate, bf16 out", "data": "synthetic",
         "config": cfg,
         "step_bytes": step_bytes, "step_gemm_flops": blk.flops,
@@ -403,14 +426,14 @@ def run_mlp(args, torch, fq, synth, dev_name):
     out = []
     for M in (256, 4096):
         blk = DenseBlock(torch, fq, synth, serving_layout(synth.LLAMA31_8B_LAYER_LINEARS[4:]), M,
-                         seed=2000 + M, requant=False)
+                         seed=2000 + M, requant=False, scales=args.scales)
         blk.capture()
         ms = blk.time_linears(max(args.steps, 10))
         out.append({"M": M, "us_per_step": 1e3 * ms, "gemm_tflops_incl_act_quant":
                     blk.flops / (ms * 1e-3) / 1e12,
                     "gbs": (blk.bytes_a + blk.bytes_g) / (ms * 1e-3) / 1e9})
     print(json.dumps({"workload": "Llama-3.1-8B MLP (gate/up/down) GEMMs + act quant",
-                      "results": out, "gpu": dev_name}), flush=True)
+                      "scales": args.scales, "results": out, "gpu": dev_name}), flush=True)
 
 
 def run_weight_sync(args, torch, fq, synth, dev_name):
@@ -454,10 +477,11 @@ def run_moe(args, torch, fq, synth, dev_name):
     wq2 = torch.empty((E, H, I), dtype=torch.uint8, device="cuda")
     sw2 = torch.empty((E, H // 128, I // 128), dtype=torch.float32, device="cuda")
     for e in range(E):
-        fq.quant_weight(w1[e], wq1[e], sw1[e])
-        fq.quant_weight(w2[e], wq2[e], sw2[e])
-    xq1, sa1 = fq.quant_act(x1)
-    xq2, sa2 = fq.quant_act(x2)
+        fq.quant_weight(w1[e], wq1[e], sw1[e], scale=args.scales)
+        fq.quant_weight(w2[e], wq2[e], sw2[e], scale=args.scales)
+    xq1, sa1 = fq.quant_act(x1, scale=args.scales)
+    xq2, sa2 = fq.quant_act(x2, scale=args.scales)
+    accum = "mx" if args.scales == "pow2" else None
     y1 = torch.empty((M, 2 * I), dtype=torch.bfloat16, device="cuda")
     y2 = torch.empty((M, H), dtype=torch.bfloat16, device="cuda")
     tg = KernelTimer(torch)
@@ -465,18 +489,25 @@ def run_moe(args, torch, fq, synth, dev_name):
     b2 = g_bytes(M, H, I) + (E - 1) * H * I + 4 * (E - 1) * (H // 128) * (I // 128)
 
     def step():
-        fq.quant_act(x1, xq1, sa1)
-        tg.launch(lambda: fq.grouped_gemm(xq1, sa1, wq1, sw1, off, y=y1), b1)
-        fq.quant_act(x2, xq2, sa2)
-        tg.launch(lambda: fq.grouped_gemm(xq2, sa2, wq2, sw2, off, y=y2), b2)
+        fq.quant_act(x1, xq1, sa1, scale=args.scales)
+        tg.launch(lambda: fq.grouped_gemm(xq1, sa1, wq1, sw1, off, y=y1, accum=accum), b1)
+        fq.quant_act(x2, xq2, sa2, scale=args.scales)
+        tg.launch(lambda: fq.grouped_gemm(xq2, sa2, wq2, sw2, off, y=y2, accum=accum), b2)
 
     ms = _timed(torch, step, args.steps, args.warmup, (tg,))
     r = tg.result()
     flops = 2 * M * (2 * I) * H + 2 * M * H * I
     g_ms = r["avg_us"] * r["launches"] / 1e3 / max(1, args.steps)
+    roof_us = 1e6 * (max(2 * M * (2 * I) * H / (FP8_PEAK_TFLOPS * 1e12), b1 / (HBM_PEAK_GBS * 1e9)) +
+                     max(2 * M * H * I / (FP8_PEAK_TFLOPS * 1e12), b2 / (HBM_PEAK_GBS * 1e9)))
     print(json.dumps({"workload": "Qwen3-30B-A3B MoE layer (T=4096, E=128, top-8, Zipf 1.1)",
+                      "scales": args.scales,
                       "rows": M, "max_expert_rows": int(counts.max()), "ms_per_step": ms,
                       "grouped_gemm": r, "grouped_tflops": flops / (g_ms * 1e-3) / 1e12,
+                      "grouped_roofline_us": roof_us,
+                      "grouped_frac_roofline": roof_us / (1e3 * g_ms),
+                      "roofline_rule": "per GEMM max(2MNK / 5.0 PFLOP/s, bytes / 8 TB/s), every "
+                                       "expert's weights read once",
                       "gpu": dev_name}), flush=True)
 
 

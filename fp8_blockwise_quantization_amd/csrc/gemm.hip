@@ -441,14 +441,22 @@ __device__ __forceinline__ void mma_slice_big(const uint8_t* stage, float swv, i
     // power-of-two scales: lane l's E8M0 exponents scale A row l % 16 and B column l % 16 of
     // every 32-wide K block it holds; the instruction adds the running sum itself
     const int swe = e8m0_of(swv);
+    int sae[T::TM];  // every row tile's scale exponent, read with the B fragments
+#pragma unroll
+    for (int i = 0; i < T::TM; ++i) sae[i] = e8m0_of(sS[wm * T::WM + i * 16 + r16]);
+    // row tile i + 1's fragment is read while row tile i's products run (separate registers)
+    v8i af = load_frag(sA, wm * T::WM + r16, kq);
 #pragma unroll
     for (int i = 0; i < T::TM; ++i) {
-      const v8i af = load_frag(sA, wm * T::WM + i * 16 + r16, kq);
-      const int sae = e8m0_of(sS[wm * T::WM + i * 16 + r16]);
+      v8i af_next = af;
+      if (i + 1 < T::TM) af_next = load_frag(sA, wm * T::WM + (i + 1) * 16 + r16, kq);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int j = 0; j < T::TN; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[j], acc[i][j], 0, 0, 0,
-                                                                     sae, 0, swe);
+                                                                     sae[i], 0, swe);
+      __builtin_amdgcn_sched_barrier(0);
+      af = af_next;
     }
     return;
   }
