@@ -24,7 +24,8 @@ with HIP events around each of its launches inside the timed region. `cpu_baseli
 CPU oracle on a bounded sample of the same step.
 
 Other workloads (`--workload`): qwen3-8b-prefill (M = 8192), llama31-8b-mlp (M in {256, 4096}),
-llama31-8b-weight-sync (32 layers of weights), qwen3-30b-a3b-moe (grouped expert GEMMs).
+llama31-8b-weight-sync (32 layers of weights), qwen3-30b-a3b-moe (grouped expert GEMMs),
+qwen3-8b-kv-cache (per-tensor Q/K/V recalibration and FP8 KV-cache store over 36 layers).
 """
 
 from __future__ import annotations
@@ -52,7 +53,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="qwen3-8b-decode",
                     choices=["qwen3-8b-decode", "qwen3-8b-prefill", "llama31-8b-mlp",
-                             "llama31-8b-weight-sync", "qwen3-30b-a3b-moe"])
+                             "llama31-8b-weight-sync", "qwen3-30b-a3b-moe", "qwen3-8b-kv-cache"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--scales", default="fp32", choices=["fp32", "pow2"],
                     help="block-scale format: fp32(amax/448) (default) or powers of two, whose "
@@ -352,6 +353,8 @@ def main():
         return run_mlp(args, torch, fq, synth, dev_name)
     elif args.workload == "llama31-8b-weight-sync":
         return run_weight_sync(args, torch, fq, synth, dev_name)
+    elif args.workload == "qwen3-8b-kv-cache":
+        return run_kv_cache(args, torch, fq, synth, dev_name)
     else:
         return run_moe(args, torch, fq, synth, dev_name)
 
@@ -481,6 +484,71 @@ def run_weight_sync(args, torch, fq, synth, dev_name):
                       "GB/s": tot / (ms * 1e-3) / 1e9, "frac_hbm": tot / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                       "events": r, "launches_per_pass": -(-len(shapes) // 32), "gpu": dev_name}),
           flush=True)
+
+
+def run_kv_cache(args, torch, fq, synth, dev_name):
+    """Per-tensor FP8 of Qwen3-8B's attention inputs over 36 layers: (1) recalibration -- the
+    running amax of Q, K and V (column slices of each layer's fused [T][6144] QKV output) over a
+    4096-token calibration batch in one batched call, then the 108 scales; (2) the KV-cache store
+    of an 8192-token prefill chunk: each layer's K and V quantized with its scale into a
+    65536-row FP8 cache at slot-mapped rows (one launch per layer for its K and V, replayed from a
+    HIP graph)."""
+    layers, hidden, kv, T_cal, T_new, cache_rows = 36, 4096, 1024, 4096, 8192, 65536
+    qkv_cols = hidden + 2 * kv
+    cal = [synth.act_bf16(T_cal, qkv_cols, seed=7000 + l, device="cuda") for l in range(layers)]
+    xs = [c[:, lo:hi] for c in cal for lo, hi in ((0, hidden), (hidden, hidden + kv),
+                                                  (hidden + kv, qkv_cols))]
+    amax = torch.zeros(len(xs), dtype=torch.float32, device="cuda")
+    scale = torch.empty_like(amax)
+    amax_descs = fq.tensor_descs(xs, amax)
+    cal_bytes = sum(2 * x.shape[0] * x.shape[1] for x in xs)
+    t_cal = KernelTimer(torch)
+
+    def recal():
+        amax.zero_()
+        t_cal.launch(lambda: fq.amax_batched(None, amax, descs=amax_descs), cal_bytes)
+        fq.scale_from_amax(amax, scale)
+
+    new = [synth.act_bf16(T_new, 2 * kv, seed=8000 + l, device="cuda") for l in range(layers)]
+    g = torch.Generator(device="cuda").manual_seed(9)
+    slots = torch.randperm(cache_rows, generator=g, device="cuda")[:T_new].contiguous()
+    kc = [torch.empty((cache_rows, kv), dtype=torch.uint8, device="cuda") for _ in range(layers)]
+    vc = [torch.empty((cache_rows, kv), dtype=torch.uint8, device="cuda") for _ in range(layers)]
+    recal()
+    torch.cuda.synchronize()
+
+    # one launch per layer: its K and V rows, each with its own scale and cache
+    kv_descs = [fq.quant_descs([new[l][:, :kv], new[l][:, kv:]],
+                            [scale[3 * l + 1:3 * l + 2], scale[3 * l + 2:3 * l + 3]],
+                            [kc[l], vc[l]], [slots, slots]) for l in range(layers)]
+
+    def store():
+        for l in range(layers):
+            fq.quant_per_tensor_batched(descs=kv_descs[l])
+
+    store()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        store()
+    store_bytes = layers * 2 * (T_new * kv * 3 + T_new * 8)
+    ms_cal = _timed(torch, recal, max(args.steps, 5), max(args.warmup, 2), (t_cal,))
+    r_cal = t_cal.result()
+    ms_store = _timed(torch, graph.replay, max(args.steps, 5), max(args.warmup, 2))
+    amax_gbs = r_cal["gbs"]
+    print(json.dumps({
+        "workload": "Qwen3-8B per-tensor FP8 Q/K/V recalibration and KV-cache store, 36 layers",
+        "metric": "per-tensor quantizer GB/s (% HBM peak)",
+        "recalibration": {"tensors": len(xs), "calibration_tokens": T_cal, "bytes": cal_bytes,
+                          "ms_per_pass_incl_scales": ms_cal, "amax_launch_us": r_cal["avg_us"],
+                          "amax_gbs": amax_gbs, "amax_frac_hbm": amax_gbs / HBM_PEAK_GBS,
+                          "per_unit": "2 B per element read"},
+        "kv_store": {"launches": layers, "new_tokens": T_new, "cache_rows": cache_rows,
+                     "bytes": store_bytes, "ms_per_pass": ms_store,
+                     "gbs": store_bytes / (ms_store * 1e-3) / 1e9,
+                     "frac_hbm": store_bytes / (ms_store * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                     "per_unit": "3 B per element + 8 B slot per row"},
+        "gpu": dev_name}), flush=True)
 
 
 def run_moe(args, torch, fq, synth, dev_name):

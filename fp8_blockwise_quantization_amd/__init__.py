@@ -1,7 +1,8 @@
 """MI355X (gfx950) FP8 blockwise-quantized W8A8 linear layer.
 
 Python face of ``libfp8rl.so``: 128x128 weight re-quantization, 1x128 per-token activation
-quantization, the blockwise-scaled FP8 GEMM and its grouped-expert (MoE) form. Tensors live on
+quantization, the blockwise-scaled FP8 GEMM and its grouped-expert (MoE) form, and per-tensor
+FP8 for attention Q/K/V and the KV cache with recalibrated scales. Tensors live on
 the GPU; the functions only marshal arguments into the C ABI (include/fp8rl.h).
 """
 
@@ -17,16 +18,23 @@ from ._lib import (  # noqa: F401
     FP8RL_SCALE_FP32,
     FP8RL_SCALE_POW2,
     Fp8rlError,
+    fp8rl_amax_bf16,
+    fp8rl_amax_bf16_batched,
     fp8rl_encode_e4m3_f32,
     fp8rl_gemm_w8a8_blockscaled,
     fp8rl_grouped_gemm_w8a8,
     fp8rl_quant_act_tok128,
+    fp8rl_quant_bf16_per_tensor,
+    fp8rl_quant_bf16_per_tensor_batched,
     fp8rl_quant_act_tok128_ex,
     fp8rl_quant_weight_blk128,
     fp8rl_quant_weight_blk128_batched,
     fp8rl_quant_weight_blk128_batched_ex,
     fp8rl_quant_weight_blk128_ex,
+    fp8rl_scale_from_amax,
     WORKSPACE_HEADER_BYTES,
+    quant_descs,
+    tensor_descs,
     weight_descs,
     fp8rl_workspace_bytes,
     lib,
@@ -40,3 +48,8 @@ quant_act = fp8rl_quant_act_tok128
 gemm = fp8rl_gemm_w8a8_blockscaled
 grouped_gemm = fp8rl_grouped_gemm_w8a8
 encode_e4m3 = fp8rl_encode_e4m3_f32
+amax = fp8rl_amax_bf16
+amax_batched = fp8rl_amax_bf16_batched
+scale_from_amax = fp8rl_scale_from_amax
+quant_per_tensor = fp8rl_quant_bf16_per_tensor
+quant_per_tensor_batched = fp8rl_quant_bf16_per_tensor_batched

@@ -35,6 +35,22 @@ class WeightDesc(ctypes.Structure):
                 ("ld_wq", ctypes.c_int64)]
 
 
+class TensorDesc(ctypes.Structure):
+    """fp8rl_tensor_desc (include/fp8rl.h)."""
+
+    _fields_ = [("x", ctypes.c_void_p), ("amax", ctypes.c_void_p), ("rows", ctypes.c_int64),
+                ("cols", ctypes.c_int64), ("ld_x", ctypes.c_int64)]
+
+
+class QuantDesc(ctypes.Structure):
+    """fp8rl_quant_desc (include/fp8rl.h)."""
+
+    _fields_ = [("x", ctypes.c_void_p), ("scale", ctypes.c_void_p), ("out", ctypes.c_void_p),
+                ("slot_mapping", ctypes.c_void_p), ("rows", ctypes.c_int64),
+                ("cols", ctypes.c_int64), ("ld_x", ctypes.c_int64), ("out_rows", ctypes.c_int64),
+                ("ld_out", ctypes.c_int64)]
+
+
 _lock = threading.Lock()
 _lib = None
 
@@ -78,6 +94,13 @@ def lib() -> ctypes.CDLL:
             "fp8rl_grouped_gemm_w8a8": (
                 ctypes.c_int,
                 [vp, vp, vp, vp, vp, i32, i64, i64, i64, vp, ctypes.c_int, ctypes.c_int, vp, sz, vp]),
+            "fp8rl_amax_bf16": (ctypes.c_int, [vp, i64, i64, i64, vp, vp]),
+            "fp8rl_amax_bf16_batched": (ctypes.c_int, [ctypes.POINTER(TensorDesc), i32, vp]),
+            "fp8rl_scale_from_amax": (ctypes.c_int, [vp, i32, vp, vp]),
+            "fp8rl_quant_bf16_per_tensor": (ctypes.c_int,
+                                            [vp, i64, i64, i64, vp, vp, i64, i64, vp, vp]),
+            "fp8rl_quant_bf16_per_tensor_batched": (ctypes.c_int,
+                                                    [ctypes.POINTER(QuantDesc), i32, vp]),
             "fp8rl_workspace_bytes": (sz, [ctypes.c_int, i64, i64, i64, i32]),
             "fp8rl_status_string": (ctypes.c_char_p, [ctypes.c_int]),
             "fp8rl_version": (ctypes.c_int, []),
@@ -100,6 +123,11 @@ EXPORTED = (
     "fp8rl_quant_act_tok128_ex",
     "fp8rl_gemm_w8a8_blockscaled",
     "fp8rl_grouped_gemm_w8a8",
+    "fp8rl_amax_bf16",
+    "fp8rl_amax_bf16_batched",
+    "fp8rl_scale_from_amax",
+    "fp8rl_quant_bf16_per_tensor",
+    "fp8rl_quant_bf16_per_tensor_batched",
     "fp8rl_workspace_bytes",
     "fp8rl_status_string",
     "fp8rl_version",
@@ -342,3 +370,106 @@ def fp8rl_grouped_gemm_w8a8(xq, sa, wq, sw, expert_offsets, out_dtype=torch.bflo
                                          _ptr(workspace), ws_bytes, _stream(stream)),
            "fp8rl_grouped_gemm_w8a8")
     return y
+
+
+# ---------------------------------------------------------------- per-tensor (Q/K/V, KV cache)
+
+
+def _tensor_rows(x: torch.Tensor, name: str = "x") -> int:
+    """Row pitch of a 2-D bf16 tensor with unit column stride (e.g. a column slice of a fused QKV
+    output)."""
+    return _rows(x, name, torch.bfloat16)
+
+
+def fp8rl_amax_bf16(x: torch.Tensor, amax: torch.Tensor, stream=None):
+    """amax (1-element float32) <- max(amax, max|x|) for a 2-D bf16 tensor; set amax to 0 first."""
+    ld = _tensor_rows(x)
+    _dense(amax, "amax", torch.float32)
+    if amax.numel() != 1:
+        raise ValueError("amax must hold one float32")
+    rows, cols = x.shape
+    _check(lib().fp8rl_amax_bf16(_ptr(x), rows, cols, ld, _ptr(amax), _stream(stream)),
+           "fp8rl_amax_bf16")
+    return amax
+
+
+def tensor_descs(xs, amax: torch.Tensor):
+    """Descriptor array for fp8rl_amax_bf16_batched: tensor i accumulates into amax[i]."""
+    _dense(amax, "amax", torch.float32)
+    if amax.numel() < len(xs):
+        raise ValueError("one amax slot per tensor")
+    arr = (TensorDesc * len(xs))()
+    for i, x in enumerate(xs):
+        ld = _tensor_rows(x, f"xs[{i}]")
+        arr[i] = TensorDesc(_ptr(x), amax.data_ptr() + 4 * i, x.shape[0], x.shape[1], ld)
+    return arr
+
+
+def fp8rl_amax_bf16_batched(xs, amax: torch.Tensor, stream=None, descs=None):
+    """amax[i] <- max(amax[i], max|xs[i]|) for every tensor, in ceil(len / 32) launches."""
+    if descs is None:
+        descs = tensor_descs(xs, amax)
+    _check(lib().fp8rl_amax_bf16_batched(descs, len(descs), _stream(stream)),
+           "fp8rl_amax_bf16_batched")
+    return amax
+
+
+def fp8rl_scale_from_amax(amax: torch.Tensor, scale: torch.Tensor | None = None, stream=None):
+    """scale[i] = fp32(amax[i] / 448), 1 where amax[i] == 0."""
+    _dense(amax, "amax", torch.float32)
+    if scale is None:
+        scale = torch.empty_like(amax)
+    _dense(scale, "scale", torch.float32)
+    if scale.numel() != amax.numel():
+        raise ValueError("scale and amax must have the same length")
+    _check(lib().fp8rl_scale_from_amax(_ptr(amax), amax.numel(), _ptr(scale), _stream(stream)),
+           "fp8rl_scale_from_amax")
+    return scale
+
+
+def fp8rl_quant_bf16_per_tensor(x: torch.Tensor, scale: torch.Tensor, out: torch.Tensor | None = None,
+                                slot_mapping: torch.Tensor | None = None, stream=None):
+    """Codes of x / scale (device scalar) into out[slot[r]] (or out[r]); returns out (uint8)."""
+    ld_x = _tensor_rows(x)
+    rows, cols = x.shape
+    if scale.dtype != torch.float32 or not scale.is_cuda or scale.numel() < 1:
+        raise ValueError("scale must be a cuda float32 tensor holding the per-tensor scale")
+    if out is None:
+        out = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    ld_out = _rows(out, "out", torch.uint8)
+    if slot_mapping is not None:
+        _dense(slot_mapping, "slot_mapping", torch.int64)
+        if slot_mapping.numel() != rows:
+            raise ValueError("one slot per row of x")
+    _check(lib().fp8rl_quant_bf16_per_tensor(_ptr(x), rows, cols, ld_x, _ptr(scale), _ptr(out),
+                                             out.shape[0], ld_out, _ptr(slot_mapping),
+                                             _stream(stream)), "fp8rl_quant_bf16_per_tensor")
+    return out
+
+
+def quant_descs(xs, scales, outs, slots=None):
+    """Descriptor array for fp8rl_quant_bf16_per_tensor_batched: xs[i] / scales[i] (a one-element
+    cuda float32 tensor or view) into outs[i] at rows slots[i] (an int64 cuda tensor or None)."""
+    arr = (QuantDesc * len(xs))()
+    for i, (x, sc, out) in enumerate(zip(xs, scales, outs)):
+        ld_x = _tensor_rows(x, f"xs[{i}]")
+        if sc.dtype != torch.float32 or not sc.is_cuda or sc.numel() < 1:
+            raise ValueError(f"scales[{i}] must be a cuda float32 tensor")
+        ld_out = _rows(out, f"outs[{i}]", torch.uint8)
+        sl = None if slots is None else slots[i]
+        if sl is not None:
+            _dense(sl, "slot_mapping", torch.int64)
+            if sl.numel() != x.shape[0]:
+                raise ValueError(f"descriptor {i}: one slot per row")
+        arr[i] = QuantDesc(_ptr(x), _ptr(sc), _ptr(out), _ptr(sl), x.shape[0], x.shape[1], ld_x,
+                           out.shape[0], ld_out)
+    return arr
+
+
+def fp8rl_quant_bf16_per_tensor_batched(xs=None, scales=None, outs=None, slots=None, stream=None,
+                                        descs=None):
+    """Per-tensor quantization of several tensors in ceil(len / 16) launches."""
+    if descs is None:
+        descs = quant_descs(xs, scales, outs, slots)
+    _check(lib().fp8rl_quant_bf16_per_tensor_batched(descs, len(descs), _stream(stream)),
+           "fp8rl_quant_bf16_per_tensor_batched")

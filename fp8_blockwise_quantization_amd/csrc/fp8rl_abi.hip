@@ -159,6 +159,179 @@ int fp8rl_quant_act_tok128(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x
   return fp8rl_quant_act_tok128_ex(x, M, K, ld_x, xq, ld_xq, sa, FP8RL_SCALE_FP32, stream);
 }
 
+namespace {
+
+// Shape / alignment rules of the per-tensor calls; `empty` is set when there is nothing to do.
+int check_tensor(const void* x, int64_t rows, int64_t cols, int64_t ld_x, bool& empty) {
+  if (int s = check_dims(rows, cols, ld_x)) return s;
+  empty = rows == 0 || cols == 0;
+  if (empty) return FP8RL_OK;
+  if (!x) return FP8RL_ERR_NULL;
+  if (cols % 8 || ld_x < cols) return FP8RL_ERR_SHAPE;
+  if (rows * (cols / 8) >= (int64_t{1} << 31)) return FP8RL_ERR_SHAPE;
+  if (!aligned(x, 16) || ld_x % 8) return FP8RL_ERR_ALIGN;
+  return FP8RL_OK;
+}
+
+int check_amax_desc(const fp8rl_tensor_desc& d, bool& empty) {
+  if (int s = check_tensor(d.x, d.rows, d.cols, d.ld_x, empty)) return s;
+  if (empty) return FP8RL_OK;
+  if (!d.amax) return FP8RL_ERR_NULL;
+  if (!aligned(d.amax, 4)) return FP8RL_ERR_ALIGN;
+  return FP8RL_OK;
+}
+
+int launch_amax(const fp8rl_tensor_desc* descs, int32_t count, hipStream_t stream) {
+  int64_t total = 0;
+  for (int32_t i = 0; i < count; ++i) total += descs[i].rows * (descs[i].cols / 8);
+  const int launches = (count + fp8rl::kTensorBatch - 1) / fp8rl::kTensorBatch;
+  const fp8rl::AmaxShape shape = fp8rl::amax_shape(total / launches);  // chunks of one launch
+  const int64_t upw = int64_t{256} * shape.steps * shape.chunks;  // chunks per workgroup
+  fp8rl::AmaxBatch b{};
+  int64_t wgs = 0;
+  auto reset = [&]() {
+    b = fp8rl::AmaxBatch{};
+    b.steps = shape.steps;
+    b.chunks = shape.chunks;
+    wgs = 0;
+  };
+  auto flush = [&]() -> int {
+    if (b.count == 0) return FP8RL_OK;
+    hipError_t e = fp8rl::launch_amax_batch(b, (int)wgs, stream);
+    reset();
+    return hip_status(e);
+  };
+  reset();
+  for (int32_t i = 0; i < count; ++i) {
+    const fp8rl_tensor_desc& d = descs[i];
+    const int64_t units = d.rows * (d.cols / 8);
+    if (units == 0) continue;
+    const int64_t n = (units + upw - 1) / upw;
+    if (b.count == fp8rl::kTensorBatch || wgs + n >= (int64_t{1} << 30))
+      if (int s = flush()) return s;
+    b.x[b.count] = d.x;
+    b.amax[b.count] = d.amax;
+    b.ld_x[b.count] = d.ld_x;
+    b.cols8[b.count] = (int)(d.cols / 8);
+    b.units[b.count] = (int)units;
+    b.wg_begin[b.count] = (int)wgs;
+    ++b.count;
+    wgs += n;
+  }
+  return flush();
+}
+
+}  // namespace
+
+int fp8rl_amax_bf16(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, float* amax,
+                    void* stream) {
+  const fp8rl_tensor_desc d{x, amax, rows, cols, ld_x};
+  bool empty = false;
+  if (int s = check_amax_desc(d, empty)) return s;
+  if (empty) return FP8RL_OK;
+  return launch_amax(&d, 1, as_stream(stream));
+}
+
+int fp8rl_amax_bf16_batched(const fp8rl_tensor_desc* descs, int32_t count, void* stream) {
+  if (count < 0) return FP8RL_ERR_ARG;
+  if (count == 0) return FP8RL_OK;
+  if (!descs) return FP8RL_ERR_NULL;
+  for (int32_t i = 0; i < count; ++i) {
+    bool empty = false;
+    if (int s = check_amax_desc(descs[i], empty)) return s;
+  }
+  return launch_amax(descs, count, as_stream(stream));
+}
+
+int fp8rl_scale_from_amax(const float* amax, int32_t n, float* scale, void* stream) {
+  if (n < 0) return FP8RL_ERR_SHAPE;
+  if (n == 0) return FP8RL_OK;
+  if (!amax || !scale) return FP8RL_ERR_NULL;
+  if (!aligned(amax, 4) || !aligned(scale, 4)) return FP8RL_ERR_ALIGN;
+  return hip_status(fp8rl::launch_scale_from_amax(amax, n, scale, as_stream(stream)));
+}
+
+namespace {
+
+int check_quant_desc(const fp8rl_quant_desc& d, bool& empty) {
+  if (int s = check_tensor(d.x, d.rows, d.cols, d.ld_x, empty)) return s;
+  if (int s = check_dims(d.out_rows, d.ld_out, 0)) return s;
+  if (empty) return FP8RL_OK;
+  if (!d.scale || !d.out) return FP8RL_ERR_NULL;
+  if (d.ld_out < d.cols || (!d.slot_mapping && d.rows > d.out_rows)) return FP8RL_ERR_SHAPE;
+  if (!aligned(d.scale, 4) || !aligned(d.out, 8) || d.ld_out % 8 ||
+      (d.slot_mapping && !aligned(d.slot_mapping, 8)))
+    return FP8RL_ERR_ALIGN;
+  return FP8RL_OK;
+}
+
+int launch_quant(const fp8rl_quant_desc* descs, int32_t count, hipStream_t stream) {
+  int64_t total = 0;
+  for (int32_t i = 0; i < count; ++i) total += descs[i].rows * (descs[i].cols / 8);
+  const int steps = fp8rl::quant_steps(total);
+  const int64_t upw = int64_t{256} * steps;
+  fp8rl::QuantBatch b{};
+  int64_t wgs = 0;
+  auto reset = [&]() {
+    b = fp8rl::QuantBatch{};
+    b.steps = steps;
+    wgs = 0;
+  };
+  auto flush = [&]() -> int {
+    if (b.count == 0) return FP8RL_OK;
+    hipError_t e = fp8rl::launch_quant_batch(b, (int)wgs, stream);
+    reset();
+    return hip_status(e);
+  };
+  reset();
+  for (int32_t i = 0; i < count; ++i) {
+    const fp8rl_quant_desc& d = descs[i];
+    const int64_t units = d.rows * (d.cols / 8);
+    if (units == 0) continue;
+    const int64_t n = (units + upw - 1) / upw;
+    if (b.count == fp8rl::kQuantBatch || wgs + n >= (int64_t{1} << 30))
+      if (int s = flush()) return s;
+    const int c = b.count;
+    b.x[c] = d.x;
+    b.scale[c] = d.scale;
+    b.out[c] = d.out;
+    b.slot[c] = d.slot_mapping;
+    b.ld_x[c] = d.ld_x;
+    b.out_rows[c] = d.out_rows;
+    b.ld_out[c] = d.ld_out;
+    b.cols8[c] = (int)(d.cols / 8);
+    b.units[c] = (int)units;
+    b.wg_begin[c] = (int)wgs;
+    ++b.count;
+    wgs += n;
+  }
+  return flush();
+}
+
+}  // namespace
+
+int fp8rl_quant_bf16_per_tensor(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                                const float* scale, uint8_t* out, int64_t out_rows,
+                                int64_t ld_out, const int64_t* slot_mapping, void* stream) {
+  const fp8rl_quant_desc d{x, scale, out, slot_mapping, rows, cols, ld_x, out_rows, ld_out};
+  bool empty = false;
+  if (int s = check_quant_desc(d, empty)) return s;
+  if (empty) return FP8RL_OK;
+  return launch_quant(&d, 1, as_stream(stream));
+}
+
+int fp8rl_quant_bf16_per_tensor_batched(const fp8rl_quant_desc* descs, int32_t count,
+                                        void* stream) {
+  if (count < 0) return FP8RL_ERR_ARG;
+  if (count == 0) return FP8RL_OK;
+  if (!descs) return FP8RL_ERR_NULL;
+  for (int32_t i = 0; i < count; ++i) {
+    bool empty = false;
+    if (int s = check_quant_desc(descs[i], empty)) return s;
+  }
+  return launch_quant(descs, count, as_stream(stream));
+}
+
 size_t fp8rl_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int32_t E) {
   if (M <= 0 || N <= 0 || K <= 0 || N % 128 || K % 128) return 0;
   if (op == FP8RL_OP_GEMM) return fp8rl::plan_gemm(M, N, K).workspace_bytes;

@@ -26,6 +26,47 @@ hipError_t launch_quant_act(const uint16_t* x, int64_t M, int64_t K, int64_t ld_
                             int64_t ld_xq, float* sa, int pow2, hipStream_t stream);
 hipError_t launch_encode(const float* v, int64_t n, uint8_t* out, hipStream_t stream);
 
+// Per-tensor amax of up to kTensorBatch bf16 tensors in one launch (by value, like WeightBatch).
+// A tensor is `units` 16-byte chunks (8 elements): chunk u is row u / cols8, column chunk
+// u % cols8. Every workgroup reads steps * 256 * chunks consecutive chunks of one tensor.
+constexpr int kTensorBatch = 32;
+struct AmaxShape {
+  int steps;   // chunks per thread per pass (1 or 8)
+  int chunks;  // passes per workgroup
+};
+struct AmaxBatch {
+  const uint16_t* x[kTensorBatch];
+  float* amax[kTensorBatch];
+  int64_t ld_x[kTensorBatch];
+  int cols8[kTensorBatch];
+  int units[kTensorBatch];
+  int wg_begin[kTensorBatch];  // first workgroup of tensor i (prefix sum)
+  int count;
+  int steps, chunks;
+};
+AmaxShape amax_shape(int64_t total_units);
+hipError_t launch_amax_batch(const AmaxBatch& b, int total_wgs, hipStream_t stream);
+hipError_t launch_scale_from_amax(const float* amax, int n, float* scale, hipStream_t stream);
+// Per-tensor quantization of up to kQuantBatch tensors in one launch (same chunk numbering as
+// AmaxBatch; each workgroup covers 256 * steps chunks of one tensor).
+constexpr int kQuantBatch = 16;
+struct QuantBatch {
+  const uint16_t* x[kQuantBatch];
+  const float* scale[kQuantBatch];
+  uint8_t* out[kQuantBatch];
+  const int64_t* slot[kQuantBatch];
+  int64_t ld_x[kQuantBatch];
+  int64_t out_rows[kQuantBatch];
+  int64_t ld_out[kQuantBatch];
+  int cols8[kQuantBatch];
+  int units[kQuantBatch];
+  int wg_begin[kQuantBatch];
+  int count;
+  int steps;
+};
+int quant_steps(int64_t total_units);
+hipError_t launch_quant_batch(const QuantBatch& b, int total_wgs, hipStream_t stream);
+
 // GEMM planning: which tile configuration and how many K splits a shape uses. Pure host logic,
 // shared by the workspace query and the launcher so both always agree.
 struct GemmPlan {

@@ -11,7 +11,10 @@
  *   3. the blockwise-scaled FP8 GEMM Y = X W^T that consumes both
  *                                             (fp8rl_gemm_w8a8_blockscaled),
  *      and its mixture-of-experts grouped form (fp8rl_grouped_gemm_w8a8);
- *   plus the element-wise E4M3 encoder the quantizers share (fp8rl_encode_e4m3_f32).
+ *   plus the element-wise E4M3 encoder the quantizers share (fp8rl_encode_e4m3_f32), and the
+ *   per-tensor FP8 of attention Q/K/V activations and the KV cache with per-step recalibrated
+ *   scales (fp8rl_amax_bf16, fp8rl_scale_from_amax, fp8rl_quant_bf16_per_tensor and their
+ *   batched forms).
  *
  * Sources, by page title and section:
  *   [UFP8]  "Unified FP8: Moving Beyond Mixed Precision for Stable and Accelerated MoE RL"
@@ -23,7 +26,8 @@
  *           bits, 3 mantissa bits and range [-448, 448]; attention/MLP/MoE-expert linears in FP8.
  *   [NEMO]  NVIDIA NeMo RL FP8 blog, "FP8 for linear layers in RL", Table 1: weights E4M3 in
  *           [128,128] blocks, input activations E4M3 in [1,128] groups, FP32 block scales; FP8
- *           math for the linear layers.
+ *           math for the linear layers. Section on FP8 for the KV cache and attention, Table 3:
+ *           per-tensor FP32 scales for Q/K/V and the KV cache, recalibrated every step.
  *
  * Conventions for every entry point
  *   - Every pointer is a DEVICE pointer (memory the caller allocated on the current HIP device),
@@ -221,6 +225,84 @@ int fp8rl_grouped_gemm_w8a8(const uint8_t* xq, const float* sa, const uint8_t* w
                             const int32_t* expert_offsets, int32_t E, int64_t M_total, int64_t N,
                             int64_t K, void* y, int y_dtype, int accum, void* workspace,
                             size_t workspace_bytes, void* stream);
+
+/*
+ * Per-tensor FP8 for attention Q/K/V activations and the stored KV cache [NEMO, section on FP8
+ * for the KV cache and attention, Table 3: E4M3 with one FP32 scale per tensor, the Q/K/V scales
+ * recalibrated at the end of every training step from data run through the updated weights and
+ * then handed to the inference engine; FP8RL, section 4 (KV-cache compression)]. Three calls:
+ * accumulate each tensor's amax over its calibration batches, turn the amax values into scales,
+ * and quantize new rows (into the KV cache) with a scale that stays in device memory.
+ *
+ * Shape rules for these calls (they differ from the 128-granular ones above): cols % 8 == 0,
+ * ld_x >= cols with ld_x % 8 == 0, x 16-byte aligned, rows * cols / 8 < 2^31.
+ */
+
+/*
+ * Running per-tensor amax: *amax = max(*amax, max |x|) over the bf16 tensor x[rows][ld_x]
+ * (first `cols` elements of each row; exact). *amax must hold a non-negative float32 -- set it to
+ * 0 before the first calibration batch -- and is updated with a device atomic, so calls on the
+ * same amax may overlap. Values must be finite.
+ *   x    : bf16 tensor, rows of pitch ld_x elements (e.g. the K columns of a fused QKV output)
+ *   amax : one float32 (4-byte aligned)
+ */
+int fp8rl_amax_bf16(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, float* amax,
+                    void* stream);
+
+/* One tensor of a batched amax (device pointers, rules as for fp8rl_amax_bf16). */
+typedef struct {
+  const uint16_t* x;
+  float* amax;
+  int64_t rows, cols, ld_x;
+} fp8rl_tensor_desc;
+
+/*
+ * fp8rl_amax_bf16 for each of `count` tensors (e.g. Q, K and V of every layer), enqueued as
+ * ceil(count / 32) launches. descs is a HOST array read during the call; every descriptor is
+ * validated first and nothing is enqueued if one fails. Tensors with no elements are skipped.
+ */
+int fp8rl_amax_bf16_batched(const fp8rl_tensor_desc* descs, int32_t count, void* stream);
+
+/*
+ * Per-tensor scales from amax values: scale[i] = fp32(amax[i] / 448) by IEEE float32 division,
+ * or 1.0f when amax[i] == 0 (the block quantizers' rule applied to a whole tensor).
+ *   amax, scale : n float32 each (4-byte aligned; amax[i] non-negative and finite)
+ */
+int fp8rl_scale_from_amax(const float* amax, int32_t n, float* scale, void* stream);
+
+/*
+ * Per-tensor quantization of new rows, e.g. the K or V of new tokens into an FP8 KV cache:
+ *   out[slot[r]][c] = E4M3 code of fp32(x[r][c]) / *scale   for r < rows, c < cols,
+ * with the IEEE float32 quotient and the E4M3 encoder above (magnitudes beyond 448, i.e. values
+ * larger than the calibrated amax, saturate to +-448). A row whose slot is negative or >= out_rows
+ * is skipped (nothing written); with slot_mapping == NULL row r goes to out row r and rows <=
+ * out_rows is required. Bytes of `out` outside the written rows and columns are untouched.
+ *   x            : bf16 [rows][ld_x]
+ *   scale        : one float32 on the device (positive, finite), e.g. from fp8rl_scale_from_amax
+ *   out          : uint8 [out_rows][ld_out] (ld_out >= cols, ld_out % 8 == 0, 8-byte aligned)
+ *   slot_mapping : `rows` int64 on the device (8-byte aligned), or NULL
+ */
+int fp8rl_quant_bf16_per_tensor(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                                const float* scale, uint8_t* out, int64_t out_rows,
+                                int64_t ld_out, const int64_t* slot_mapping, void* stream);
+
+/* One tensor of a batched per-tensor quantization (device pointers, rules as above). */
+typedef struct {
+  const uint16_t* x;
+  const float* scale;
+  uint8_t* out;
+  const int64_t* slot_mapping; /* may be NULL */
+  int64_t rows, cols, ld_x, out_rows, ld_out;
+} fp8rl_quant_desc;
+
+/*
+ * fp8rl_quant_bf16_per_tensor for each of `count` tensors -- e.g. a layer's new K and V rows,
+ * each with its own scale and cache -- enqueued as ceil(count / 16) launches. descs is a HOST
+ * array read during the call; all descriptors are validated before anything is enqueued.
+ * Outputs of different descriptors must not overlap.
+ */
+int fp8rl_quant_bf16_per_tensor_batched(const fp8rl_quant_desc* descs, int32_t count,
+                                        void* stream);
 
 /* Bytes at the start of every GEMM workspace that hold the K-split arrival counters (see
  * fp8rl_gemm_w8a8_blockscaled). */

@@ -32,7 +32,7 @@ def L():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 12
+    assert len(names) == 17
     for n in names:
         assert hasattr(L, n), n
     assert sorted(_lib.EXPORTED) == names
@@ -99,6 +99,53 @@ def test_quant_act_validation(L):
     assert f(A, 4, 100, 128, A, 128, A, None) == ESHAPE
     assert f(A, -4, 128, 128, A, 128, A, None) == ESHAPE
     assert f(A, 4, 128, 128, A + 8, 128, A, None) == EALIGN
+
+
+def test_per_tensor_validation(L):
+    a = L.fp8rl_amax_bf16
+    assert a(None, 0, 16, 16, None, None) == OK  # nothing to do
+    assert a(None, 4, 16, 16, A, None) == ENULL
+    assert a(A, 4, 16, 16, None, None) == ENULL
+    assert a(A, 4, 12, 16, A, None) == ESHAPE  # cols % 8
+    assert a(A, 4, 16, 8, A, None) == ESHAPE   # ld < cols
+    assert a(A, 1 << 28, 128, 128, A, None) == ESHAPE  # 2^32 chunks
+    assert a(A + 8, 4, 16, 16, A, None) == EALIGN
+    assert a(A, 4, 16, 20, A, None) == EALIGN
+    assert a(A, 4, 16, 16, A + 2, None) == EALIGN
+    D = _lib.TensorDesc
+    b = L.fp8rl_amax_bf16_batched
+    arr = (D * 2)(D(A, A, 4, 16, 16), D(A, A + 1, 4, 16, 16))
+    assert b(arr, 0, None) == OK
+    assert b(None, 1, None) == ENULL
+    assert b(arr, -1, None) == EARG
+    assert b(arr, 2, None) == EALIGN  # the second descriptor fails: nothing is launched
+    assert b((D * 1)(D(None, None, 0, 16, 16)), 1, None) == OK
+    sc = L.fp8rl_scale_from_amax
+    assert sc(None, 0, None, None) == OK
+    assert sc(None, 3, A, None) == ENULL
+    assert sc(A, -1, A, None) == ESHAPE
+    assert sc(A, 3, A + 2, None) == EALIGN
+    q = L.fp8rl_quant_bf16_per_tensor
+    assert q(None, 0, 16, 16, None, None, 0, 16, None, None) == OK
+    assert q(A, 4, 16, 16, None, A, 4, 16, None, None) == ENULL
+    assert q(A, 4, 16, 16, A, None, 4, 16, None, None) == ENULL
+    assert q(A, 4, 16, 16, A, A, 3, 16, None, None) == ESHAPE  # rows > out rows without slots
+    assert q(A, 4, 16, 16, A, A, 4, 8, None, None) == ESHAPE   # ld_out < cols
+    assert q(A, 4, 16, 16, A, A, -1, 16, A, None) == ESHAPE
+    assert q(A, 4, 16, 16, A, A + 4, 4, 16, None, None) == EALIGN
+    assert q(A, 4, 16, 16, A, A, 4, 20, None, None) == EALIGN
+    assert q(A, 4, 16, 16, A, A, 4, 16, A + 4, None) == EALIGN
+    assert q(A, 4, 16, 16, A + 2, A, 4, 16, None, None) == EALIGN
+    Q = _lib.QuantDesc
+    qb = L.fp8rl_quant_bf16_per_tensor_batched
+    good = Q(A, A, A, None, 4, 16, 16, 4, 16)
+    assert qb(None, 0, None) == OK
+    assert qb(None, 2, None) == ENULL
+    assert qb((Q * 1)(good), -1, None) == EARG
+    assert qb((Q * 2)(good, Q(A, A, A, None, 5, 16, 16, 4, 16)), 2, None) == ESHAPE
+    assert qb((Q * 2)(good, Q(A, None, A, None, 4, 16, 16, 4, 16)), 2, None) == ENULL
+    assert qb((Q * 2)(good, Q(A, A, A, A + 2, 4, 16, 16, 4, 16)), 2, None) == EALIGN
+    assert qb((Q * 1)(Q(None, None, None, None, 0, 16, 16, 0, 16)), 1, None) == OK
 
 
 def test_encode_validation(L):
