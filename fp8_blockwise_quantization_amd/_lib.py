@@ -26,6 +26,7 @@ FP8RL_SCALE_FP32 = 0
 FP8RL_SCALE_POW2 = 1
 FP8RL_OP_GEMM = 0
 FP8RL_OP_GROUPED_GEMM = 1
+FP8RL_OP_GEMM_ROWSCALED = 2
 
 class WeightDesc(ctypes.Structure):
     """fp8rl_weight_desc (include/fp8rl.h)."""
@@ -101,6 +102,13 @@ def lib() -> ctypes.CDLL:
                                             [vp, i64, i64, i64, vp, vp, i64, i64, vp, vp]),
             "fp8rl_quant_bf16_per_tensor_batched": (ctypes.c_int,
                                                     [ctypes.POINTER(QuantDesc), i32, vp]),
+            "fp8rl_quant_weight_blk128_t": (
+                ctypes.c_int, [vp, i64, i64, i64, vp, i64, vp, vp, i64, vp, ctypes.c_int, vp]),
+            "fp8rl_quant_act_colwise128": (
+                ctypes.c_int, [vp, i64, i64, i64, vp, i64, vp, vp, i64, vp, ctypes.c_int, vp]),
+            "fp8rl_gemm_w8a8_rowscaled": (
+                ctypes.c_int,
+                [vp, vp, vp, vp, i64, i64, i64, vp, ctypes.c_int, i64, ctypes.c_int, vp, sz, vp]),
             "fp8rl_workspace_bytes": (sz, [ctypes.c_int, i64, i64, i64, i32]),
             "fp8rl_status_string": (ctypes.c_char_p, [ctypes.c_int]),
             "fp8rl_version": (ctypes.c_int, []),
@@ -128,6 +136,9 @@ EXPORTED = (
     "fp8rl_scale_from_amax",
     "fp8rl_quant_bf16_per_tensor",
     "fp8rl_quant_bf16_per_tensor_batched",
+    "fp8rl_quant_weight_blk128_t",
+    "fp8rl_quant_act_colwise128",
+    "fp8rl_gemm_w8a8_rowscaled",
     "fp8rl_workspace_bytes",
     "fp8rl_status_string",
     "fp8rl_version",
@@ -345,6 +356,32 @@ def fp8rl_gemm_w8a8_blockscaled(xq, sa, wq, sw, out_dtype=torch.bfloat16, y=None
     return y
 
 
+def fp8rl_gemm_w8a8_rowscaled(aq, sa, bq, sb, out_dtype=torch.bfloat16, y=None, workspace=None,
+                              stream=None, accum=None):
+    """Y[M][N] = sum over 128-wide K slices of sa[m][kb] sb[n][kb] (Aq Bq^T)_kb: both operands
+    scaled per row and slice (the weight-gradient GEMM)."""
+    _dense(aq, "aq", torch.uint8)
+    _dense(bq, "bq", torch.uint8)
+    _dense(sa, "sa", torch.float32)
+    _dense(sb, "sb", torch.float32)
+    M, K = aq.shape
+    N = bq.shape[0]
+    if bq.shape[1] != K or sb.numel() != N * (K // 128) or sa.numel() != M * (K // 128):
+        raise ValueError("shape mismatch between aq, sa, bq and sb")
+    if y is None:
+        y = torch.empty((M, N), dtype=out_dtype, device=aq.device)
+    ld_y = _rows(y, "y", y.dtype)
+    need = fp8rl_workspace_bytes(FP8RL_OP_GEMM_ROWSCALED, M, N, K)
+    if workspace is None and need > 0:
+        workspace = new_workspace(need, aq.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().fp8rl_gemm_w8a8_rowscaled(_ptr(aq), _ptr(sa), _ptr(bq), _ptr(sb), M, N, K,
+                                           _ptr(y), _out_code(y.dtype), ld_y,
+                                           _accum_code(accum, y.dtype), _ptr(workspace), ws_bytes,
+                                           _stream(stream)), "fp8rl_gemm_w8a8_rowscaled")
+    return y
+
+
 def fp8rl_grouped_gemm_w8a8(xq, sa, wq, sw, expert_offsets, out_dtype=torch.bfloat16, y=None,
                             workspace=None, stream=None, accum=None):
     """Per-expert blockscaled GEMM over row segments given by device int32 ``expert_offsets``."""
@@ -473,3 +510,62 @@ def fp8rl_quant_bf16_per_tensor_batched(xs=None, scales=None, outs=None, slots=N
         descs = quant_descs(xs, scales, outs, slots)
     _check(lib().fp8rl_quant_bf16_per_tensor_batched(descs, len(descs), _stream(stream)),
            "fp8rl_quant_bf16_per_tensor_batched")
+
+
+# ------------------------------------------------------------------ backward (transposed outputs)
+
+
+def fp8rl_quant_weight_blk128_t(w: torch.Tensor, wqt=None, swt=None, wq=None, sw=None,
+                                rowmajor: bool = False, scale="fp32", stream=None):
+    """bf16 W[N][K] -> (WqT uint8 [K][N], swT float32 [K/128][N/128]), the block quantization of
+    W^T; with ``rowmajor`` also (Wq [N][K], sw [N/128][K/128]) from the same read. Returns
+    (wqt, swt, wq, sw) with wq, sw None unless asked for."""
+    ld_w = _rows(w, "w", torch.bfloat16)
+    N, K = w.shape
+    dev = w.device
+    if wqt is None:
+        wqt = torch.empty((K, N), dtype=torch.uint8, device=dev)
+    if swt is None:
+        swt = torch.empty((K // 128, N // 128), dtype=torch.float32, device=dev)
+    if rowmajor and wq is None:
+        wq = torch.empty((N, K), dtype=torch.uint8, device=dev)
+    if rowmajor and sw is None:
+        sw = torch.empty((N // 128, K // 128), dtype=torch.float32, device=dev)
+    ld_wqt = _rows(wqt, "wqt", torch.uint8)
+    _dense(swt, "swt", torch.float32)
+    ld_wq = 0
+    if wq is not None:
+        ld_wq = _rows(wq, "wq", torch.uint8)
+        _dense(sw, "sw", torch.float32)
+    _check(lib().fp8rl_quant_weight_blk128_t(_ptr(w), N, K, ld_w, _ptr(wq), ld_wq, _ptr(sw),
+                                             _ptr(wqt), ld_wqt, _ptr(swt), _scale_code(scale),
+                                             _stream(stream)), "fp8rl_quant_weight_blk128_t")
+    return wqt, swt, wq, sw
+
+
+def fp8rl_quant_act_colwise128(x: torch.Tensor, xtq=None, sat=None, xq=None, sa=None,
+                               rowwise: bool = False, scale="fp32", stream=None):
+    """bf16 X[M][K] (M % 128 == 0) -> (XtQ uint8 [K][M], st float32 [K][M/128]): 128x1 token
+    groups stored transposed; with ``rowwise`` also the 1x128 row quantization (Xq, sa) from the
+    same read. Returns (xtq, sat, xq, sa)."""
+    ld_x = _rows(x, "x", torch.bfloat16)
+    M, K = x.shape
+    dev = x.device
+    if xtq is None:
+        xtq = torch.empty((K, M), dtype=torch.uint8, device=dev)
+    if sat is None:
+        sat = torch.empty((K, M // 128), dtype=torch.float32, device=dev)
+    if rowwise and xq is None:
+        xq = torch.empty((M, K), dtype=torch.uint8, device=dev)
+    if rowwise and sa is None:
+        sa = torch.empty((M, K // 128), dtype=torch.float32, device=dev)
+    ld_xtq = _rows(xtq, "xtq", torch.uint8)
+    _dense(sat, "sat", torch.float32)
+    ld_xq = 0
+    if xq is not None:
+        ld_xq = _rows(xq, "xq", torch.uint8)
+        _dense(sa, "sa", torch.float32)
+    _check(lib().fp8rl_quant_act_colwise128(_ptr(x), M, K, ld_x, _ptr(xq), ld_xq, _ptr(sa),
+                                            _ptr(xtq), ld_xtq, _ptr(sat), _scale_code(scale),
+                                            _stream(stream)), "fp8rl_quant_act_colwise128")
+    return xtq, sat, xq, sa

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 LIB_NAME = "libfp8rl.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
-SOURCES = ("quant.hip", "tensor_quant.hip", "gemm.hip", "fp8rl_abi.hip")
+SOURCES = ("quant.hip", "tensor_quant.hip", "transpose_quant.hip", "gemm.hip", "fp8rl_abi.hip")
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep the compiler from forming packed FP32 instructions.

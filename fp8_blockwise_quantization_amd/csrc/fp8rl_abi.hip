@@ -332,30 +332,84 @@ int fp8rl_quant_bf16_per_tensor_batched(const fp8rl_quant_desc* descs, int32_t c
   return launch_quant(descs, count, as_stream(stream));
 }
 
+int fp8rl_quant_weight_blk128_t(const uint16_t* w, int64_t N, int64_t K, int64_t ld_w, uint8_t* wq,
+                                int64_t ld_wq, float* sw, uint8_t* wqt, int64_t ld_wqt, float* swt,
+                                int scale_fmt, void* stream) {
+  if (scale_fmt != FP8RL_SCALE_FP32 && scale_fmt != FP8RL_SCALE_POW2) return FP8RL_ERR_ARG;
+  if (int s = check_dims(N, K, 0)) return s;
+  if (N == 0 || K == 0) return FP8RL_OK;
+  if (!w || !wqt || !swt || (!wq) != (!sw)) return FP8RL_ERR_NULL;
+  if (N % 128 || K % 128 || ld_w < K || ld_wqt < N || (wq && ld_wq < K)) return FP8RL_ERR_SHAPE;
+  if ((N / 128) * (K / 128) >= (int64_t{1} << 24)) return FP8RL_ERR_SHAPE;  // grid limit
+  if (!aligned(w, 16) || !aligned(wqt, 16) || !aligned(swt, 4) || (ld_w * 2) % 16 || ld_wqt % 16 ||
+      (wq && (!aligned(wq, 16) || !aligned(sw, 4) || ld_wq % 16)))
+    return FP8RL_ERR_ALIGN;
+  const fp8rl::TileQuantArgs a{w, ld_w, (int)N, (int)K, wq, ld_wq, sw, wqt, ld_wqt, swt,
+                               scale_fmt == FP8RL_SCALE_POW2};
+  return hip_status(fp8rl::launch_quant_tile_t(a, 0, as_stream(stream)));
+}
+
+int fp8rl_quant_act_colwise128(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x, uint8_t* xq,
+                               int64_t ld_xq, float* sa, uint8_t* xtq, int64_t ld_xtq, float* sat,
+                               int scale_fmt, void* stream) {
+  if (scale_fmt != FP8RL_SCALE_FP32 && scale_fmt != FP8RL_SCALE_POW2) return FP8RL_ERR_ARG;
+  if (int s = check_dims(M, K, 0)) return s;
+  if (M == 0 || K == 0) return FP8RL_OK;
+  if (!x || !xtq || !sat || (!xq) != (!sa)) return FP8RL_ERR_NULL;
+  if (M % 128 || K % 128 || ld_x < K || ld_xtq < M || (xq && ld_xq < K)) return FP8RL_ERR_SHAPE;
+  if ((M / 128) * (K / 128) >= (int64_t{1} << 24)) return FP8RL_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(xtq, 16) || !aligned(sat, 4) || (ld_x * 2) % 16 || ld_xtq % 16 ||
+      (xq && (!aligned(xq, 16) || !aligned(sa, 4) || ld_xq % 16)))
+    return FP8RL_ERR_ALIGN;
+  const fp8rl::TileQuantArgs a{x, ld_x, (int)M, (int)K, xq, ld_xq, sa, xtq, ld_xtq, sat,
+                               scale_fmt == FP8RL_SCALE_POW2};
+  return hip_status(fp8rl::launch_quant_tile_t(a, 1, as_stream(stream)));
+}
+
 size_t fp8rl_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int32_t E) {
   if (M <= 0 || N <= 0 || K <= 0 || N % 128 || K % 128) return 0;
   if (op == FP8RL_OP_GEMM) return fp8rl::plan_gemm(M, N, K).workspace_bytes;
+  if (op == FP8RL_OP_GEMM_ROWSCALED) return fp8rl::plan_gemm(M, N, K, true).workspace_bytes;
   if (op == FP8RL_OP_GROUPED_GEMM) return fp8rl::plan_grouped_gemm(M, N, K, E).workspace_bytes;
   return 0;
 }
 
-int fp8rl_gemm_w8a8_blockscaled(const uint8_t* xq, const float* sa, const uint8_t* wq,
-                                const float* sw, int64_t M, int64_t N, int64_t K, void* y,
-                                int y_dtype, int64_t ld_y, int accum, void* workspace,
-                                size_t workspace_bytes, void* stream) {
+namespace {
+
+int gemm_common(const uint8_t* xq, const float* sa, const uint8_t* wq, const float* sw, int64_t M,
+                int64_t N, int64_t K, void* y, int y_dtype, int64_t ld_y, int accum, bool rowb,
+                void* workspace, size_t workspace_bytes, void* stream) {
   if (int s = check_dims(M, N, K)) return s;
   if (M == 0) return FP8RL_OK;
   if (int s = check_gemm_common(xq, sa, wq, sw, N, K, y, y_dtype, ld_y)) return s;
   if (accum != FP8RL_ACCUM_FP8 && accum != FP8RL_ACCUM_F16 && accum != FP8RL_ACCUM_MX)
     return FP8RL_ERR_ARG;
   if (((M + 127) / 128) * (N / 64) >= (int64_t{1} << 22)) return FP8RL_ERR_SHAPE;  // grid limit
-  const fp8rl::GemmPlan plan = fp8rl::plan_gemm(M, N, K);
+  const fp8rl::GemmPlan plan = fp8rl::plan_gemm(M, N, K, rowb);
   if (plan.workspace_bytes > 0) {
     if (!workspace || workspace_bytes < plan.workspace_bytes) return FP8RL_ERR_WORKSPACE;
     if (!aligned(workspace, 16)) return FP8RL_ERR_ALIGN;
   }
   return hip_status(fp8rl::launch_gemm(xq, sa, wq, sw, M, N, K, y, y_dtype == FP8RL_OUT_F32, ld_y,
-                                       accum, workspace, plan, as_stream(stream)));
+                                       accum, rowb, workspace, plan, as_stream(stream)));
+}
+
+}  // namespace
+
+int fp8rl_gemm_w8a8_blockscaled(const uint8_t* xq, const float* sa, const uint8_t* wq,
+                                const float* sw, int64_t M, int64_t N, int64_t K, void* y,
+                                int y_dtype, int64_t ld_y, int accum, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  return gemm_common(xq, sa, wq, sw, M, N, K, y, y_dtype, ld_y, accum, false, workspace,
+                     workspace_bytes, stream);
+}
+
+int fp8rl_gemm_w8a8_rowscaled(const uint8_t* aq, const float* sa, const uint8_t* bq,
+                              const float* sb, int64_t M, int64_t N, int64_t K, void* y,
+                              int y_dtype, int64_t ld_y, int accum, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  return gemm_common(aq, sa, bq, sb, M, N, K, y, y_dtype, ld_y, accum, true, workspace,
+                     workspace_bytes, stream);
 }
 
 int fp8rl_grouped_gemm_w8a8(const uint8_t* xq, const float* sa, const uint8_t* wq, const float* sw,

@@ -28,25 +28,30 @@ namespace fp8rl {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-template <int BM_, int BN_, int WM_, int WN_>
+// ROWB_: the B operand carries one scale per row and K slice (sb[N][KB]) instead of one per
+// 128x128 block; those scales then travel with each slice like the activation scales.
+template <int BM_, int BN_, int WM_, int WN_, bool ROWB_ = false>
 struct Tile {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+  static constexpr bool ROWB = ROWB_;
   static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
   static constexpr int WAVES = WAVES_M * WAVES_N;
   static constexpr int NT = WAVES * 64;
   static constexpr int TM = WM / 16, TN = WN / 16;
   static constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;
-  static constexpr int STAGE_BYTES = A_BYTES + B_BYTES + BM * 4;
+  static constexpr int STAGE_BYTES = A_BYTES + B_BYTES + BM * 4 + (ROWB ? BN * 4 : 0);
   static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
   static constexpr int A_LOADS = BM * 8 / NT;
   static constexpr int B_LOADS = BN * 8 / NT;
   static_assert((BM * 8) % NT == 0 && (BN * 8) % NT == 0, "tile must split into 16-byte loads");
-  static_assert(BM <= NT, "one scale load per tile row");
+  static_assert(BM <= NT && BN <= NT, "one scale load per tile row");
   static_assert(128 % WN == 0, "a wave's columns must share one weight-scale block");
 };
 
 using TileLarge = Tile<128, 128, 64, 64>;  // prefill-sized M
 using TileSmall = Tile<64, 64, 32, 32>;    // decode-sized M
+using TileLargeRow = Tile<128, 128, 64, 64, true>;
+using TileSmallRow = Tile<64, 64, 32, 32, true>;
 
 struct GemmArgs {
   const uint8_t* xq;
@@ -72,6 +77,7 @@ struct Prefetch {
   uint4 a[T::A_LOADS];
   uint4 b[T::B_LOADS];
   float s;
+  float sb;  // row-scaled B only
 };
 
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
@@ -83,7 +89,7 @@ __device__ __forceinline__ uint4 ldg16(const uint8_t* p) {
 template <class T>
 __device__ __forceinline__ void load_slice(Prefetch<T>& st, const uint8_t* A, int m_valid,
                                            const uint8_t* B, int n_valid, int64_t ld, const float* SA,
-                                           int KB, int kb, int tid) {
+                                           const float* SB, int KB, int kb, int tid) {
   const int64_t koff = (int64_t)kb * 128;
 #pragma unroll
   for (int i = 0; i < T::A_LOADS; ++i) {
@@ -96,6 +102,7 @@ __device__ __forceinline__ void load_slice(Prefetch<T>& st, const uint8_t* A, in
     st.b[i] = row < n_valid ? ldg16(B + row * ld + koff + cc * 16) : make_uint4(0, 0, 0, 0);
   }
   st.s = (tid < T::BM && tid < m_valid) ? SA[(int64_t)tid * KB + kb] : 0.f;
+  if constexpr (T::ROWB) st.sb = (tid < T::BN && tid < n_valid) ? SB[(int64_t)tid * KB + kb] : 0.f;
 }
 
 template <class T>
@@ -114,6 +121,8 @@ __device__ __forceinline__ void store_slice(const Prefetch<T>& st, uint8_t* stag
     *reinterpret_cast<uint4*>(sB + row * 128 + ((cc ^ swz(row)) << 4)) = st.b[i];
   }
   if (tid < T::BM) sS[tid] = st.s;
+  if constexpr (T::ROWB)
+    if (tid < T::BN) sS[T::BM + tid] = st.sb;
 }
 
 // Fragment of a 16x128 operand tile for v_mfma_f32_16x16x128_f8f6f4: lane l holds row l % 16 and
@@ -179,10 +188,14 @@ __device__ __forceinline__ void mma_slice(const uint8_t* stage, float swv, int w
   const int r16 = lane & 15, kq = lane >> 4;
   v8i af[T::TM], bf[T::TN];
   v4f sc[T::TM];
+  float sb[T::TN];  // row-scaled B: the scale of this lane's output column in sub-tile j
 #pragma unroll
   for (int i = 0; i < T::TM; ++i) af[i] = load_frag(sA, wm * T::WM + i * 16 + r16, kq);
 #pragma unroll
-  for (int j = 0; j < T::TN; ++j) bf[j] = load_frag(sB, wn * T::WN + j * 16 + r16, kq);
+  for (int j = 0; j < T::TN; ++j) {
+    bf[j] = load_frag(sB, wn * T::WN + j * 16 + r16, kq);
+    sb[j] = T::ROWB ? sS[T::BM + wn * T::WN + j * 16 + r16] : 1.f;
+  }
 #pragma unroll
   for (int i = 0; i < T::TM; ++i) {
     // output rows of this lane in sub-tile i: 4 * kq + v, v = 0..3
@@ -193,13 +206,17 @@ __device__ __forceinline__ void mma_slice(const uint8_t* stage, float swv, int w
 #pragma unroll
     for (int j = 0; j < T::TN; ++j) {
       const v4f p = slice_product<PRECISE>(af[i], bf[j]);
-      acc[i][j] += p * sc[i];
+      if constexpr (T::ROWB)
+        acc[i][j] += p * (sc[i] * sb[j]);
+      else
+        acc[i][j] += p * sc[i];
     }
   }
 }
 
 // One output tile over K slices [kb0, kb1). A/SA start at the tile's first row, B at its first
-// column (weight row); SW is the weight-scale matrix [N/128][KB] of the current expert.
+// column (weight row); SW is the weight-scale matrix [N/128][KB] of the current expert, or, with
+// row-scaled B, the tile's first row of sb [N][KB].
 template <class T, bool PRECISE>
 __device__ __forceinline__ void run_tile(const uint8_t* A, const float* SA, int m_valid,
                                          const uint8_t* B, const float* SW, int n0, int n_valid,
@@ -209,7 +226,7 @@ __device__ __forceinline__ void run_tile(const uint8_t* A, const float* SA, int 
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / T::WAVES_N, wn = wave % T::WAVES_N;
-  const float* swrow = SW + (int64_t)((n0 + wn * T::WN) >> 7) * KB;
+  const float* swrow = T::ROWB ? nullptr : SW + (int64_t)((n0 + wn * T::WN) >> 7) * KB;
 
 #pragma unroll
   for (int i = 0; i < T::TM; ++i)
@@ -218,14 +235,14 @@ __device__ __forceinline__ void run_tile(const uint8_t* A, const float* SA, int 
   if (kb0 >= kb1) return;
 
   Prefetch<T> st;
-  load_slice<T>(st, A, m_valid, B, n_valid, ld, SA, KB, kb0, tid);
+  load_slice<T>(st, A, m_valid, B, n_valid, ld, SA, SW, KB, kb0, tid);
   store_slice<T>(st, smem, tid);
   __syncthreads();
   for (int kb = kb0; kb < kb1; ++kb) {
     const int cur = (kb - kb0) & 1;
     const bool more = kb + 1 < kb1;
-    if (more) load_slice<T>(st, A, m_valid, B, n_valid, ld, SA, KB, kb + 1, tid);
-    const float swv = swrow[kb];
+    if (more) load_slice<T>(st, A, m_valid, B, n_valid, ld, SA, SW, KB, kb + 1, tid);
+    const float swv = T::ROWB ? 1.f : swrow[kb];
     mma_slice<T, PRECISE>(smem + cur * T::STAGE_BYTES, swv, wm, wn, lane, acc);
     if (more) store_slice<T>(st, smem + (cur ^ 1) * T::STAGE_BYTES, tid);
     __syncthreads();
@@ -293,7 +310,8 @@ __global__ __launch_bounds__(T::NT) void gemm_kernel(GemmArgs p) {
   const int m_valid = min(T::BM, p.M - m0);
   v4f acc[T::TM][T::TN];
   run_tile<T, PRECISE>(p.xq + (int64_t)m0 * p.K, p.sa + (int64_t)m0 * p.KB, m_valid,
-              p.wq + (int64_t)n0 * p.K, p.sw, n0, T::BN, p.K, p.KB, kb0, kb1, smem, acc);
+              p.wq + (int64_t)n0 * p.K, T::ROWB ? p.sw + (int64_t)n0 * p.KB : p.sw, n0, T::BN,
+              p.K, p.KB, kb0, kb1, smem, acc);
   store_tile<T>(p, m0, m_valid, n0, split, acc);
 }
 
@@ -309,22 +327,26 @@ __global__ __launch_bounds__(T::NT) void gemm_kernel(GemmArgs p) {
 // this one). Per K slice: wait for this wave's DMA, one barrier, start the next slice's DMA into
 // the other stage, then multiply out of this stage.
 // ---------------------------------------------------------------------------------------------
-template <int BM_, int BN_, int WM_, int WN_, int STAGES_>
+template <int BM_, int BN_, int WM_, int WN_, int STAGES_, bool ROWB_ = false>
 struct Big {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, STAGES = STAGES_;
+  static constexpr bool ROWB = ROWB_;  // B scales per row and slice (see Tile)
   static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
   static constexpr int WAVES = WAVES_M * WAVES_N;
   static constexpr int NT = WAVES * 64;
   static constexpr int TM = WM / 16, TN = WN / 16;
   static constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128, S_BYTES = BM * 4;
-  static constexpr int STAGE_BYTES = A_BYTES + B_BYTES + S_BYTES;
+  static constexpr int SB_BYTES = ROWB ? BN * 4 : 0;
+  static constexpr int STAGE_BYTES = A_BYTES + B_BYTES + S_BYTES + SB_BYTES;
   static constexpr int A_PER_WAVE = BM / 8 / WAVES;  // one DMA instruction moves 8 rows (1 KiB)
   static constexpr int B_PER_WAVE = BN / 8 / WAVES;
   static constexpr int S_ROWS = BM / WAVES;  // activation scales loaded per wave
-  static constexpr int DMA_OPS = A_PER_WAVE + B_PER_WAVE + 1;  // DMA instructions per wave, slice
+  static constexpr int SB_ROWS = BN / WAVES;  // row-scaled B: B scales loaded per wave
+  static constexpr int DMA_OPS = A_PER_WAVE + B_PER_WAVE + 1 + (ROWB ? 1 : 0);  // per wave, slice
   static_assert(STAGES >= 2 && STAGES <= 3, "waits are written out for up to one slice ahead");
   static_assert(A_PER_WAVE * 8 * WAVES == BM && B_PER_WAVE * 8 * WAVES == BN, "DMA split");
   static_assert(S_ROWS <= 64 && S_ROWS * WAVES == BM, "scale DMA split");
+  static_assert(SB_ROWS <= 64 && SB_ROWS * WAVES == BN, "B-scale DMA split");
   static_assert(128 % WN == 0, "a wave's columns must share one weight-scale block");
 };
 
@@ -333,6 +355,8 @@ constexpr int kMaxExperts = 1024;
 using BigWide = Big<256, 256, 128, 64, 2>;    // 8 waves
 using BigNarrow = Big<256, 128, 128, 64, 2>;  // 4 waves
 using BigGroup = Big<128, 256, 64, 64, 3>;    // 8 waves; grouped GEMM (expert segments are short)
+using BigWideRow = Big<256, 256, 128, 64, 2, true>;
+using BigNarrowRow = Big<256, 128, 128, 64, 2, true>;
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -364,6 +388,7 @@ struct DmaPlan {
   uint32_t a[T::A_PER_WAVE];
   uint32_t b[T::B_PER_WAVE];
   uint32_t s;
+  uint32_t sb;  // row-scaled B
 };
 
 template <class T>
@@ -386,19 +411,23 @@ __device__ __forceinline__ DmaPlan<T> make_dma_plan(int m_valid, int n_valid, in
     d.b[t] = (uint32_t)(min(trow, n_valid - 1) * K + cc * 16);
   }
   d.s = (uint32_t)(min(wave * T::S_ROWS + lane, m_valid - 1) * KB * 4);
+  d.sb = (uint32_t)(min(wave * T::SB_ROWS + lane, n_valid - 1) * KB * 4);
   return d;
 }
 
 template <class T>
 __device__ __forceinline__ void dma_slice(uint8_t* stage, const DmaPlan<T>& d, const uint8_t* A,
-                                          const uint8_t* B, const float* SA, int kb, int wave,
-                                          int lane) {
+                                          const uint8_t* B, const float* SA, const float* SB,
+                                          int kb, int wave, int lane) {
   const uint8_t* a = A + (int64_t)kb * 128;
   const uint8_t* b = B + (int64_t)kb * 128;
   // the scale DMA goes first: anything the compiler has to wait for before computing its
   // operands (e.g. a reloaded register) then does not wait on this slice's tile DMA as well
   if (lane < T::S_ROWS)
     dma4(SA + kb, d.s, stage + T::A_BYTES + T::B_BYTES + wave * T::S_ROWS * 4);
+  if constexpr (T::ROWB)
+    if (lane < T::SB_ROWS)
+      dma4(SB + kb, d.sb, stage + T::A_BYTES + T::B_BYTES + T::S_BYTES + wave * T::SB_ROWS * 4);
 #pragma unroll
   for (int t = 0; t < T::A_PER_WAVE; ++t) dma16(a, d.a[t], stage + (t * T::WAVES + wave) * 1024);
 #pragma unroll
@@ -433,14 +462,21 @@ __device__ __forceinline__ void mma_slice_big(const uint8_t* stage, float swv, i
   const uint8_t* sA = stage;
   const uint8_t* sB = stage + T::A_BYTES;
   const float* sS = reinterpret_cast<const float*>(stage + T::A_BYTES + T::B_BYTES);
+  const float* sSB = sS + T::BM;  // row-scaled B: this slice's scales of the tile's B rows
   const int r16 = lane & 15, kq = lane >> 4;
   v8i bf[T::TN];
+  float sb[T::TN];  // row-scaled B: the scale of this lane's output column in sub-tile j
 #pragma unroll
-  for (int j = 0; j < T::TN; ++j) bf[j] = load_frag(sB, wn * T::WN + j * 16 + r16, kq);
+  for (int j = 0; j < T::TN; ++j) {
+    bf[j] = load_frag(sB, wn * T::WN + j * 16 + r16, kq);
+    sb[j] = T::ROWB ? sSB[wn * T::WN + j * 16 + r16] : 1.f;
+  }
   if constexpr (ACC == 2) {
     // power-of-two scales: lane l's E8M0 exponents scale A row l % 16 and B column l % 16 of
     // every 32-wide K block it holds; the instruction adds the running sum itself
-    const int swe = e8m0_of(swv);
+    int sbe[T::TN];  // B exponent of this lane's column: one per block, or one per row
+#pragma unroll
+    for (int j = 0; j < T::TN; ++j) sbe[j] = e8m0_of(T::ROWB ? sb[j] : swv);
     int sae[T::TM];  // every row tile's scale exponent, read with the B fragments
 #pragma unroll
     for (int i = 0; i < T::TM; ++i) sae[i] = e8m0_of(sS[wm * T::WM + i * 16 + r16]);
@@ -454,7 +490,7 @@ __device__ __forceinline__ void mma_slice_big(const uint8_t* stage, float swv, i
 #pragma unroll
       for (int j = 0; j < T::TN; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[j], acc[i][j], 0, 0, 0,
-                                                                     sae[i], 0, swe);
+                                                                     sae[i], 0, sbe[j]);
       __builtin_amdgcn_sched_barrier(0);
       af = af_next;
     }
@@ -477,7 +513,12 @@ __device__ __forceinline__ void mma_slice_big(const uint8_t* stage, float swv, i
     for (int j = 0; j < T::TN; ++j) {
       p_cur[j] = slice_product<PRECISE>(af, bf[j]);
       __builtin_amdgcn_sched_barrier(0);
-      if (i > 0) acc[i - 1][j] += p_prev[j] * sc_prev;
+      if (i > 0) {
+        if constexpr (T::ROWB)
+          acc[i - 1][j] += p_prev[j] * (sc_prev * sb[j]);
+        else
+          acc[i - 1][j] += p_prev[j] * sc_prev;
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
@@ -487,7 +528,12 @@ __device__ __forceinline__ void mma_slice_big(const uint8_t* stage, float swv, i
     sc = sn * swv;
   }
 #pragma unroll
-  for (int j = 0; j < T::TN; ++j) acc[T::TM - 1][j] += p_prev[j] * sc_prev;
+  for (int j = 0; j < T::TN; ++j) {
+    if constexpr (T::ROWB)
+      acc[T::TM - 1][j] += p_prev[j] * (sc_prev * sb[j]);
+    else
+      acc[T::TM - 1][j] += p_prev[j] * sc_prev;
+  }
 }
 
 // One BM x BN output tile over all K slices: operands DMA'd through STAGES LDS stages (the next
@@ -507,12 +553,16 @@ __device__ __forceinline__ void big_tile(const GemmArgs& p, uint8_t* stages,
   // a wave whose columns are all past N still runs (it takes part in the DMA and barriers) on a
   // clamped scale row; its results are not stored
   constexpr int NBLK = (T::BN + 127) / 128;
-  for (int e = tid; e < NBLK * KB; e += T::NT) {
-    const int b = e / KB, k = e - (e / KB) * KB;
-    const int nb = min((n0 >> 7) + b, p.N / 128 - 1);
-    sw_s[b][k] = SW[(int64_t)nb * KB + k];
+  if constexpr (!T::ROWB) {
+    for (int e = tid; e < NBLK * KB; e += T::NT) {
+      const int b = e / KB, k = e - (e / KB) * KB;
+      const int nb = min((n0 >> 7) + b, p.N / 128 - 1);
+      sw_s[b][k] = SW[(int64_t)nb * KB + k];
+    }
   }
   const float* swrow = sw_s[((n0 + wn * T::WN) >> 7) - (n0 >> 7)];
+  // row-scaled B: the tile's rows of sb [N][KB] travel with each slice instead
+  const float* SB = T::ROWB ? SW + (int64_t)n0 * KB : nullptr;
 
   v4f acc[T::TM][T::TN];
 #pragma unroll
@@ -524,26 +574,26 @@ __device__ __forceinline__ void big_tile(const GemmArgs& p, uint8_t* stages,
   if constexpr (T::STAGES == 2) {
     uint8_t* const stage0 = stages;
     uint8_t* const stage1 = stages + T::STAGE_BYTES;
-    dma_slice<T>(stage0, dp, A, B, SA, 0, wave, lane);
+    dma_slice<T>(stage0, dp, A, B, SA, SB, 0, wave, lane);
     for (int kb = 0; kb < KB; kb += 2) {
       wait_dma_and_barrier();
-      if (kb + 1 < KB) dma_slice<T>(stage1, dp, A, B, SA, kb + 1, wave, lane);
-      mma_slice_big<T, ACC>(stage0, swrow[kb], wm, wn, lane, acc);
+      if (kb + 1 < KB) dma_slice<T>(stage1, dp, A, B, SA, SB, kb + 1, wave, lane);
+      mma_slice_big<T, ACC>(stage0, T::ROWB ? 1.f : swrow[kb], wm, wn, lane, acc);
       if (kb + 1 >= KB) break;
       wait_dma_and_barrier();
-      if (kb + 2 < KB) dma_slice<T>(stage0, dp, A, B, SA, kb + 2, wave, lane);
-      mma_slice_big<T, ACC>(stage1, swrow[kb + 1], wm, wn, lane, acc);
+      if (kb + 2 < KB) dma_slice<T>(stage0, dp, A, B, SA, SB, kb + 2, wave, lane);
+      mma_slice_big<T, ACC>(stage1, T::ROWB ? 1.f : swrow[kb + 1], wm, wn, lane, acc);
     }
   } else {
     // slices kb + 1 and kb + 2 in flight while kb is multiplied
-    dma_slice<T>(stages, dp, A, B, SA, 0, wave, lane);
-    if (KB > 1) dma_slice<T>(stages + T::STAGE_BYTES, dp, A, B, SA, 1, wave, lane);
+    dma_slice<T>(stages, dp, A, B, SA, SB, 0, wave, lane);
+    if (KB > 1) dma_slice<T>(stages + T::STAGE_BYTES, dp, A, B, SA, SB, 1, wave, lane);
     int cur = 0;
     for (int kb = 0; kb < KB; ++kb) {
       wait_slice_and_barrier<T>(KB - 1 - kb);
       const int nxt = cur == 0 ? 2 : cur - 1;  // (kb + 2) % 3
-      if (kb + 2 < KB) dma_slice<T>(stages + nxt * T::STAGE_BYTES, dp, A, B, SA, kb + 2, wave, lane);
-      mma_slice_big<T, ACC>(stages + cur * T::STAGE_BYTES, swrow[kb], wm, wn, lane, acc);
+      if (kb + 2 < KB) dma_slice<T>(stages + nxt * T::STAGE_BYTES, dp, A, B, SA, SB, kb + 2, wave, lane);
+      mma_slice_big<T, ACC>(stages + cur * T::STAGE_BYTES, T::ROWB ? 1.f : swrow[kb], wm, wn, lane, acc);
       cur = cur == 2 ? 0 : cur + 1;
     }
   }
@@ -973,7 +1023,7 @@ hipError_t ensure_lds(std::atomic<uint64_t>& done, const void* kernel, int bytes
 
 }  // namespace
 
-GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
+GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool rowb) {
   GemmPlan pl{};
   const int64_t KB = K / 128;
   if (M >= 1024 && KB <= kMaxSlices) {
@@ -986,7 +1036,7 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
     pl.workspace_bytes = 0;
     return pl;
   }
-  if (M <= 64 && KB % 2 == 0) {
+  if (M <= 64 && KB % 2 == 0 && !rowb) {
     // weight streaming: 64-column tiles, D slices in flight per wave (the largest of 8, 4, 2
     // dividing KB); split K into ranges of L slices (L a multiple of D dividing KB) while there
     // are fewer than kDecWorkgroups workgroups and ranges keep at least kDecMinSlices slices
@@ -1094,7 +1144,8 @@ static hipError_t launch_dense(const GemmArgs& a, const GemmPlan& pl, hipStream_
 
 hipError_t launch_gemm(const uint8_t* xq, const float* sa, const uint8_t* wq, const float* sw,
                        int64_t M, int64_t N, int64_t K, void* y, int out_f32, int64_t ld_y,
-                       int accum, void* workspace, const GemmPlan& pl, hipStream_t stream) {
+                       int accum, int rowb, void* workspace, const GemmPlan& pl,
+                       hipStream_t stream) {
   // accum: 0 FP8 slice sums, 1 f16 slice sums, 2 power-of-two scales in the matrix cores (the
   // register-staged tiles have no such form: their FP8 form gives the same results then)
   const bool precise = accum == 1;
@@ -1118,6 +1169,25 @@ hipError_t launch_gemm(const uint8_t* xq, const float* sa, const uint8_t* wq, co
   a.splits = pl.splits;
   a.kb_per_split = pl.kb_per_split;
   hipError_t e;
+  if (rowb) {  // sw is sb [N][KB]: one scale per B row and slice
+    switch (pl.cfg) {
+      case kCfgBigWide:
+        if (accum == 1) return launch_big<BigNarrowRow, 1>(a, stream);
+        return accum == 2 ? launch_big<BigWideRow, 2>(a, stream) : launch_big<BigWideRow, 0>(a, stream);
+      case kCfgBigNarrow:
+        if (accum == 1) return launch_big<BigNarrowRow, 1>(a, stream);
+        return accum == 2 ? launch_big<BigNarrowRow, 2>(a, stream)
+                          : launch_big<BigNarrowRow, 0>(a, stream);
+      case kCfgLarge:
+        e = precise ? launch_dense<TileLargeRow, true>(a, pl, stream)
+                    : launch_dense<TileLargeRow, false>(a, pl, stream);
+        break;
+      default:  // the planner never picks the decode path for row-scaled B
+        e = precise ? launch_dense<TileSmallRow, true>(a, pl, stream)
+                    : launch_dense<TileSmallRow, false>(a, pl, stream);
+        break;
+    }
+  } else {
   switch (pl.cfg) {
     case kCfgBigWide:
       // the f16 form needs more registers per wave than the 8-wave tile leaves: 4-wave tiles
@@ -1137,6 +1207,7 @@ hipError_t launch_gemm(const uint8_t* xq, const float* sa, const uint8_t* wq, co
       e = precise ? launch_dense<TileSmall, true>(a, pl, stream)
                   : launch_dense<TileSmall, false>(a, pl, stream);
       break;
+  }
   }
   if (e != hipSuccess || pl.splits == 1) return e;
   const int64_t total4 = M * N / 4;

@@ -67,6 +67,24 @@ struct QuantBatch {
 int quant_steps(int64_t total_units);
 hipError_t launch_quant_batch(const QuantBatch& b, int total_wgs, hipStream_t stream);
 
+// Quantization of 128x128 tiles of a bf16 matrix X[R][C] with a transposed code output:
+// qt [C][ld_qt] (and st) always, row-major q [R][ld_q] (and s) when q is not null.
+// Weight mode: one scale per tile, s [R/128][C/128], st [C/128][R/128].
+// Activation mode: st [C][R/128] per 128x1 column group; s [R][C/128] per 1x128 row group.
+struct TileQuantArgs {
+  const uint16_t* x;
+  int64_t ld_x;
+  int R, C;
+  uint8_t* q;
+  int64_t ld_q;
+  float* s;
+  uint8_t* qt;
+  int64_t ld_qt;
+  float* st;
+  int pow2;
+};
+hipError_t launch_quant_tile_t(const TileQuantArgs& a, int act, hipStream_t stream);
+
 // GEMM planning: which tile configuration and how many K splits a shape uses. Pure host logic,
 // shared by the workspace query and the launcher so both always agree.
 struct GemmPlan {
@@ -77,12 +95,14 @@ struct GemmPlan {
   int depth;   // decode path: K slices in flight per wave
   size_t workspace_bytes;
 };
-GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K);
+GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool rowb = false);
 GemmPlan plan_grouped_gemm(int64_t M_total, int64_t N, int64_t K, int32_t E);
 
+// rowb: sw is sb [N][K/128], one scale per row of B and K slice, instead of [N/128][K/128]
 hipError_t launch_gemm(const uint8_t* xq, const float* sa, const uint8_t* wq, const float* sw,
                        int64_t M, int64_t N, int64_t K, void* y, int out_f32, int64_t ld_y,
-                       int accum, void* workspace, const GemmPlan& plan, hipStream_t stream);
+                       int accum, int rowb, void* workspace, const GemmPlan& plan,
+                       hipStream_t stream);
 hipError_t launch_grouped_gemm(const uint8_t* xq, const float* sa, const uint8_t* wq,
                                const float* sw, const int32_t* offsets, int32_t E,
                                int64_t M_total, int64_t N, int64_t K, void* y, int out_f32,

@@ -71,7 +71,7 @@ typedef enum {
 
 typedef enum { FP8RL_OUT_BF16 = 0, FP8RL_OUT_F32 = 1 } fp8rl_out_dtype;
 
-typedef enum { FP8RL_OP_GEMM = 0, FP8RL_OP_GROUPED_GEMM = 1 } fp8rl_op;
+typedef enum { FP8RL_OP_GEMM = 0, FP8RL_OP_GROUPED_GEMM = 1, FP8RL_OP_GEMM_ROWSCALED = 2 } fp8rl_op;
 
 /*
  * How the matrix cores form the sum over one 128-wide K slice (the per-slice scaling, the float32
@@ -180,6 +180,51 @@ int fp8rl_quant_act_tok128_ex(const uint16_t* x, int64_t M, int64_t K, int64_t l
                               int64_t ld_xq, float* sa, int scale_fmt, void* stream);
 
 /*
+ * Backward pass of the linear layer in FP8 [NEMO, Table 1: output gradients in [1,128] groups,
+ * weights in [128,128] blocks, FP32 scales; UFP8, quick-read section and the Megatron
+ * mixed-granularity figure: FProp, Dgrad and Wgrad in FP8 with per-token activations and
+ * gradients and per-block weights; its limitations paragraph: a transposed copy of each quantized
+ * weight is kept for the backward pass]. For Y = X W^T and the output gradient dY [M][N]:
+ *   Dgrad  dX = dY W:     dYq, s_dy = fp8rl_quant_act_tok128(dY) (1x128 along N), then
+ *                         fp8rl_gemm_w8a8_blockscaled(dYq, s_dy, WqT, swT) with M, N := K, K := N,
+ *                         WqT / swT from fp8rl_quant_weight_blk128_t;
+ *   Wgrad  dW = dY^T X:   dYtq, s_dyt = fp8rl_quant_act_colwise128(dY), Xtq, s_xt =
+ *                         fp8rl_quant_act_colwise128(X) (128x1 groups along the tokens, stored
+ *                         transposed), then fp8rl_gemm_w8a8_rowscaled(dYtq, s_dyt, Xtq, s_xt)
+ *                         with M := N, N := K, K := tokens.
+ * A per-token scale varies along Wgrad's summation axis, so Wgrad's operands are re-quantized in
+ * groups along that axis; the token count must then be a multiple of 128 (pad with zero rows,
+ * which change neither an amax nor a sum).
+ */
+
+/*
+ * Weight quantization with a transposed copy: the 128x128 block quantization of W (as
+ * fp8rl_quant_weight_blk128) and of W^T, which is its transpose (a block's amax does not depend
+ * on orientation):  WqT[k][n] = Wq[n][k],  swT[k/128][n/128] = sw[n/128][k/128].
+ *   wq, sw   : row-major codes [N][ld_wq] and scales [N/128][K/128], or both NULL (not written)
+ *   wqt, swt : transposed codes [K][ld_wqt] (ld_wqt >= N) and scales [K/128][N/128]
+ * Requires N % 128 == 0, K % 128 == 0; scale_fmt as for the _ex quantizers.
+ */
+int fp8rl_quant_weight_blk128_t(const uint16_t* w, int64_t N, int64_t K, int64_t ld_w, uint8_t* wq,
+                                int64_t ld_wq, float* sw, uint8_t* wqt, int64_t ld_wqt, float* swt,
+                                int scale_fmt, void* stream);
+
+/*
+ * Column-group quantization with a transposed output (Wgrad operands): for column k of X[M][K]
+ * and token group g (rows 128g .. 128g+127):
+ *   sat[k][g]       = fp32(max |X[group, k]| / 448), or 1.0f when that max is 0,
+ *   xtq[k][m]       = E4M3 code of fp32(X[m][k]) / sat[k][m/128]
+ * i.e. fp8rl_quant_act_tok128 applied to X^T. Optionally (xq, sa not NULL) also the row-wise
+ * 1x128 quantization of fp8rl_quant_act_tok128 from the same read of X (e.g. dY for Dgrad).
+ *   xtq, sat : [K][ld_xtq] (ld_xtq >= M) codes and [K][M/128] scales
+ *   xq, sa   : [M][ld_xq] codes and [M][K/128] scales, or both NULL
+ * Requires M % 128 == 0 and K % 128 == 0; scale_fmt as for the _ex quantizers.
+ */
+int fp8rl_quant_act_colwise128(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x, uint8_t* xq,
+                               int64_t ld_xq, float* sa, uint8_t* xtq, int64_t ld_xtq, float* sat,
+                               int scale_fmt, void* stream);
+
+/*
  * Blockwise-scaled W8A8 GEMM, Y = X W^T [NEMO, "FP8 for linear layers in RL"; FP8RL, section 1]:
  *   Y[m][n] = sum_kb sa[m][kb] * sw[n/128][kb] * sum_{k in slice kb} dec(Xq[m][k]) * dec(Wq[n][k])
  * with kb running over the K/128 slices of 128. Products of E4M3 values are exact; each slice's
@@ -204,6 +249,20 @@ int fp8rl_gemm_w8a8_blockscaled(const uint8_t* xq, const float* sa, const uint8_
                                 const float* sw, int64_t M, int64_t N, int64_t K, void* y,
                                 int y_dtype, int64_t ld_y, int accum, void* workspace,
                                 size_t workspace_bytes, void* stream);
+
+/*
+ * Row-scaled FP8 GEMM (the weight-gradient product of the backward pass: both operands quantized
+ * in 1x128 groups along the summed axis):
+ *   Y[m][n] = sum_kb sa[m][kb] * sb[n][kb] * sum_{k in slice kb} dec(Aq[m][k]) * dec(Bq[n][k])
+ * i.e. fp8rl_gemm_w8a8_blockscaled with one B scale per row and slice, sb [N][K/128], instead of
+ * one per 128x128 block. Same arguments, rules, accumulation modes (with FP8RL_ACCUM_MX every sb
+ * must be a power of two) and determinism; the workspace is sized by
+ * fp8rl_workspace_bytes(FP8RL_OP_GEMM_ROWSCALED, M, N, K, 0).
+ */
+int fp8rl_gemm_w8a8_rowscaled(const uint8_t* aq, const float* sa, const uint8_t* bq,
+                              const float* sb, int64_t M, int64_t N, int64_t K, void* y,
+                              int y_dtype, int64_t ld_y, int accum, void* workspace,
+                              size_t workspace_bytes, void* stream);
 
 /*
  * Grouped (mixture-of-experts) blockwise-scaled W8A8 GEMM [FP8RL, section 1: MoE expert linears

@@ -32,7 +32,7 @@ def L():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 17
+    assert len(names) == 20
     for n in names:
         assert hasattr(L, n), n
     assert sorted(_lib.EXPORTED) == names
@@ -146,6 +146,34 @@ def test_per_tensor_validation(L):
     assert qb((Q * 2)(good, Q(A, None, A, None, 4, 16, 16, 4, 16)), 2, None) == ENULL
     assert qb((Q * 2)(good, Q(A, A, A, A + 2, 4, 16, 16, 4, 16)), 2, None) == EALIGN
     assert qb((Q * 1)(Q(None, None, None, None, 0, 16, 16, 0, 16)), 1, None) == OK
+
+
+def test_backward_validation(L):
+    w = L.fp8rl_quant_weight_blk128_t
+    assert w(A, 0, 128, 128, None, 0, None, A, 0, A, 0, None) == OK
+    assert w(A, 128, 256, 256, A, 256, None, A, 128, A, 0, None) == ENULL  # wq without sw
+    assert w(A, 128, 256, 256, None, 0, None, None, 128, A, 0, None) == ENULL
+    assert w(A, 128, 256, 256, None, 0, None, A, 64, A, 0, None) == ESHAPE  # ld_wqt < N
+    assert w(A, 100, 256, 256, None, 0, None, A, 128, A, 0, None) == ESHAPE
+    assert w(A, 128, 256, 256, None, 0, None, A + 8, 128, A, 0, None) == EALIGN
+    assert w(A, 128, 256, 256, None, 0, None, A, 128, A, 5, None) == EARG
+    c = L.fp8rl_quant_act_colwise128
+    assert c(A, 0, 128, 128, None, 0, None, A, 0, A, 0, None) == OK
+    assert c(A, 100, 128, 128, None, 0, None, A, 128, A, 0, None) == ESHAPE  # M % 128
+    assert c(A, 128, 128, 128, A, 128, None, A, 128, A, 0, None) == ENULL
+    assert c(A, 128, 128, 128, None, 0, None, A, 64, A, 0, None) == ESHAPE
+    assert c(A, 128, 128, 128, None, 0, None, A, 128, A + 2, 0, None) == EALIGN
+    assert c(A, 128, 128, 128, None, 0, None, A, 128, A, 9, None) == EARG
+    g = L.fp8rl_gemm_w8a8_rowscaled
+    assert g(A, A, A, A, 0, 256, 256, A, 0, 256, 0, None, 0, None) == OK
+    assert g(A, A, A, A, 64, 256, 200, A, 0, 256, 0, None, 0, None) == ESHAPE
+    assert g(A, A, A, None, 64, 256, 256, A, 0, 256, 0, None, 0, None) == ENULL
+    assert g(A, A, A, A, 64, 256, 256, A, 0, 256, 3, None, 0, None) == EARG
+    # row-scaled B never takes the decode path: its small-M plan has its own workspace rule
+    ws_row = L.fp8rl_workspace_bytes(2, 64, 4096, 4096, 0)
+    ws_blk = L.fp8rl_workspace_bytes(0, 64, 4096, 4096, 0)
+    assert ws_row != ws_blk
+    assert g(A, A, A, A, 64, 4096, 4096, A, 0, 4096, 0, A, ws_row - 1, None) == EWS
 
 
 def test_encode_validation(L):
