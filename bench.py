@@ -25,7 +25,8 @@ CPU oracle on a bounded sample of the same step.
 
 Other workloads (`--workload`): qwen3-8b-prefill (M = 8192), llama31-8b-mlp (M in {256, 4096}),
 llama31-8b-weight-sync (32 layers of weights), qwen3-30b-a3b-moe (grouped expert GEMMs),
-qwen3-8b-kv-cache (per-tensor Q/K/V recalibration and FP8 KV-cache store over 36 layers).
+qwen3-8b-kv-cache (per-tensor Q/K/V recalibration and FP8 KV-cache store over 36 layers),
+qwen3-8b-backward (FP8 Dgrad and Wgrad of the decoder block's linears over 8192 tokens).
 """
 
 from __future__ import annotations
@@ -53,7 +54,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="qwen3-8b-decode",
                     choices=["qwen3-8b-decode", "qwen3-8b-prefill", "llama31-8b-mlp",
-                             "llama31-8b-weight-sync", "qwen3-30b-a3b-moe", "qwen3-8b-kv-cache"])
+                             "llama31-8b-weight-sync", "qwen3-30b-a3b-moe", "qwen3-8b-kv-cache",
+                             "qwen3-8b-backward"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--scales", default="fp32", choices=["fp32", "pow2"],
                     help="block-scale format: fp32(amax/448) (default) or powers of two, whose "
@@ -355,6 +357,8 @@ def main():
         return run_weight_sync(args, torch, fq, synth, dev_name)
     elif args.workload == "qwen3-8b-kv-cache":
         return run_kv_cache(args, torch, fq, synth, dev_name)
+    elif args.workload == "qwen3-8b-backward":
+        return run_backward(args, torch, fq, synth, dev_name)
     else:
         return run_moe(args, torch, fq, synth, dev_name)
 
@@ -548,6 +552,82 @@ def run_kv_cache(args, torch, fq, synth, dev_name):
                      "gbs": store_bytes / (ms_store * 1e-3) / 1e9,
                      "frac_hbm": store_bytes / (ms_store * 1e-3) / 1e9 / HBM_PEAK_GBS,
                      "per_unit": "3 B per element + 8 B slot per row"},
+        "gpu": dev_name}), flush=True)
+
+
+def run_backward(args, torch, fq, synth, dev_name):
+    """FP8 backward of the Qwen3-8B decoder block's linears (serving layout: q/k/v and gate/up
+    fused) over T = 8192 tokens. Per linear: the output gradient dY quantized both ways from one
+    read (1x128 rows for Dgrad, 128x1 token groups stored transposed for Wgrad), the input X in
+    128x1 token groups, the weight's transposed block-quantized copy, then Dgrad = dYq WqT^T
+    (blockwise-scaled GEMM) and Wgrad = dYqT XqT^T (row-scaled GEMM). Each part is captured in
+    its own HIP graph and timed over replays; bf16 outputs, FP8 slice sums (the FP32-scale
+    default) or, with --scales pow2, matrix-core scales."""
+    T = 8192
+    groups = serving_layout(synth.DENSE_LINEARS_QWEN3_8B)
+    acc = "mx" if args.scales == "pow2" else None
+    L = []
+    for i, (name, N, K) in enumerate(groups):
+        L.append(dict(name=name, N=N, K=K,
+                      dy=synth.act_bf16(T, N, seed=9000 + i, device="cuda") * 0.01,
+                      x=synth.act_bf16(T, K, seed=9100 + i, device="cuda"),
+                      w=synth.weight_bf16(N, K, seed=9200 + i, outlier_frac=0.001, device="cuda")))
+
+    def quant_part():
+        for l in L:
+            l["q_dy"] = fq.quant_colwise(l["dy"], rowwise=True, scale=args.scales, **l.get("o_dy", {}))
+            l["q_x"] = fq.quant_colwise(l["x"], scale=args.scales, **l.get("o_x", {}))
+            l["q_w"] = fq.quant_weight_t(l["w"], scale=args.scales, **l.get("o_w", {}))
+
+    quant_part()  # allocate the outputs once, then reuse them in place
+    for l in L:
+        dyt, s_dyt, dyq, s_dy = l["q_dy"]
+        l["o_dy"] = dict(xtq=dyt, sat=s_dyt, xq=dyq, sa=s_dy)
+        xt, s_xt, _, _ = l["q_x"]
+        l["o_x"] = dict(xtq=xt, sat=s_xt)
+        wqt, swt, _, _ = l["q_w"]
+        l["o_w"] = dict(wqt=wqt, swt=swt)
+        l["dx"] = torch.empty((T, l["K"]), dtype=torch.bfloat16, device="cuda")
+        l["dw"] = torch.empty((l["N"], l["K"]), dtype=torch.bfloat16, device="cuda")
+        l["ws_dx"] = fq.new_workspace(fq.fp8rl_workspace_bytes(fq.FP8RL_OP_GEMM, T, l["K"], l["N"]), "cuda")
+        l["ws_dw"] = fq.new_workspace(fq.fp8rl_workspace_bytes(fq.FP8RL_OP_GEMM_ROWSCALED, l["N"], l["K"], T), "cuda")
+
+    def dgrad_part():
+        for l in L:
+            _, _, dyq, s_dy = l["q_dy"]
+            wqt, swt, _, _ = l["q_w"]
+            fq.gemm(dyq, s_dy, wqt, swt, y=l["dx"], workspace=l["ws_dx"], accum=acc)
+
+    def wgrad_part():
+        for l in L:
+            dyt, s_dyt, _, _ = l["q_dy"]
+            xt, s_xt, _, _ = l["q_x"]
+            fq.gemm_rowscaled(dyt, s_dyt, xt, s_xt, y=l["dw"], workspace=l["ws_dw"], accum=acc)
+
+    res = {}
+    flops = sum(2 * T * l["N"] * l["K"] for l in L)
+    qbytes = sum(T * l["N"] * (2 + 2) + T * l["N"] // 128 * 8 + T * l["K"] * 3 + T * l["K"] // 128 * 4
+                 + l["N"] * l["K"] * 3 for l in L)
+    for name, fn in (("quantizers", quant_part), ("dgrad", dgrad_part), ("wgrad", wgrad_part)):
+        fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        res[name] = _timed(torch, g.replay, max(args.steps, 5), max(args.warmup, 2))
+    print(json.dumps({
+        "workload": "Qwen3-8B decoder block linears, FP8 backward (Dgrad + Wgrad), 8192 tokens",
+        "metric": "blockscaled FP8 GEMM TFLOP/s (% MFMA peak); quantizer GB/s (% HBM peak)",
+        "gemms": [[l["name"], l["N"], l["K"]] for l in L], "tokens": T, "scales": args.scales,
+        "quantizers": {"ms": res["quantizers"], "bytes": qbytes,
+                       "gbs": qbytes / (res["quantizers"] * 1e-3) / 1e9,
+                       "frac_hbm": qbytes / (res["quantizers"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                       "per_unit": "dY: 2 B read + 2 B of codes (both layouts) per element + both "
+                                   "scale sets; X: 3 B per element + scales; W: 3 B per element"},
+        "dgrad": {"ms": res["dgrad"], "tflops": flops / (res["dgrad"] * 1e-3) / 1e12,
+                  "frac_mfma": flops / (res["dgrad"] * 1e-3) / 1e12 / FP8_PEAK_TFLOPS},
+        "wgrad": {"ms": res["wgrad"], "tflops": flops / (res["wgrad"] * 1e-3) / 1e12,
+                  "frac_mfma": flops / (res["wgrad"] * 1e-3) / 1e12 / FP8_PEAK_TFLOPS},
         "gpu": dev_name}), flush=True)
 
 

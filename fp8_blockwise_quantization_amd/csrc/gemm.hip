@@ -350,7 +350,7 @@ struct Big {
   static_assert(128 % WN == 0, "a wave's columns must share one weight-scale block");
 };
 
-constexpr int kMaxSlices = 128;  // K <= 16384 on the large-tile path
+constexpr int kMaxSlices = 256;  // K <= 32768 on the large-tile path
 constexpr int kMaxExperts = 1024;
 using BigWide = Big<256, 256, 128, 64, 2>;    // 8 waves
 using BigNarrow = Big<256, 128, 128, 64, 2>;  // 4 waves

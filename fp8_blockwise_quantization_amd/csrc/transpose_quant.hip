@@ -9,10 +9,12 @@
 // gradients and per-block weights, and a transposed copy of each quantized weight kept for the
 // backward pass.) The element rule is the forward one: code = E4M3_RNE_sat(fp32(x) / S).
 //
-// One workgroup (256 threads) per 128x128 tile of the bf16 input, loaded exactly as the forward
-// weight quantizer does (thread t: 16-byte column chunk t & 15 of rows (t >> 4) + 16 i), so the
-// tile sits in registers. Row-major codes, if asked for, are stored straight from registers; the
-// transposed codes go through a 128 x 128-byte LDS tile and leave as 16-byte row segments.
+// One workgroup (256 threads) per 128x128 tile of the bf16 input; thread t holds the 16-byte
+// column chunk c = t & 15 of the 8 consecutive rows 8g .. 8g+7, g = t >> 4, so the tile sits in
+// registers. Row-major codes, if asked for, are stored straight from registers. For the
+// transposed codes a thread's 8 x 8 block of codes is transposed in registers (byte permutes),
+// written to a 128 x 128-byte LDS tile as eight 8-byte pieces, and leaves as 16-byte row
+// segments.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -21,8 +23,8 @@ namespace fp8rl {
 constexpr int kTPitch = 144;  // bytes per LDS row of the transposed tile (128 codes + padding)
 
 // Per-column amax of the tile (columns 8c .. 8c+7 of thread t's chunk c), as four packed pairs
-// of 16-bit magnitudes, combined over the tile's 128 rows: in-thread over i, across the four rows
-// r0 of a wave that share c (lanes c + 16q), then across the four waves through LDS.
+// of 16-bit magnitudes, combined over the tile's 128 rows: in-thread over its 8 rows, across the
+// four row groups of a wave that share c (lanes c + 16q), then across the four waves via LDS.
 __device__ __forceinline__ void column_amax(const u32x4 (&v)[8], uint32_t (&red)[4][16][4],
                                             uint32_t (&cm)[4]) {
   const int t = threadIdx.x, c = t & 15, wave = t >> 6;
@@ -66,13 +68,25 @@ __device__ __forceinline__ u32x2 quant8_cols(u32x4 w, const double (&r)[8]) {
   return u32x2{pack4_e4m3(f0, f1, f2, f3), pack4_e4m3(f4, f5, f6, f7)};
 }
 
-// Put the 8 codes of source row `row`, columns 8c .. 8c+7, into column `row` of the transposed
-// tile rows 8c .. 8c+7.
-__device__ __forceinline__ void scatter_t(uint8_t* tq, u32x2 codes, int c, int row) {
+// Byte e of each of 4 words, packed into one word (the word of `a0` in the low byte).
+__device__ __forceinline__ uint32_t gather_byte(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3,
+                                                int e) {
+  // v_perm_b32: selector byte k picks byte k' of {hi: first, lo: second}; 0x0c gives 0
+  const uint32_t sel = 0x0c0c0000u | ((uint32_t)(4 + e) << 8) | (uint32_t)e;
+  const uint32_t u = __builtin_amdgcn_perm(a1, a0, sel);  // [a0_e, a1_e, 0, 0]
+  const uint32_t v = __builtin_amdgcn_perm(a3, a2, sel);  // [a2_e, a3_e, 0, 0]
+  return __builtin_amdgcn_perm(v, u, 0x05040100u);          // [a0_e, a1_e, a2_e, a3_e]
+}
+
+// Transpose a thread's 8 x 8 codes (q[i]: row i, columns 0..7) and store column e's 8 codes (rows
+// 0..7 in order) at transposed-tile row 8c + e, bytes row0 .. row0 + 7.
+__device__ __forceinline__ void store_t(uint8_t* tq, const u32x2 (&q)[8], int c, int row0) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const uint32_t w = e < 4 ? codes.x : codes.y;
-    tq[(8 * c + e) * kTPitch + row] = (uint8_t)(w >> (8 * (e & 3)));
+    const int w = e >> 2, b = e & 3;
+    const uint32_t lo = gather_byte(q[0][w], q[1][w], q[2][w], q[3][w], b);
+    const uint32_t hi = gather_byte(q[4][w], q[5][w], q[6][w], q[7][w], b);
+    *reinterpret_cast<u32x2*>(tq + (8 * c + e) * kTPitch + row0) = u32x2{lo, hi};
   }
 }
 
@@ -85,13 +99,14 @@ __global__ __launch_bounds__(256) void quant_tile_t_kernel(TileQuantArgs a) {
   __shared__ uint32_t red[4][16][4];
   const int tiles_c = a.C / kBlock, tiles_r = a.R / kBlock;
   const int bi = blockIdx.x / tiles_c, bj = blockIdx.x - (blockIdx.x / tiles_c) * tiles_c;
-  const int t = threadIdx.x, c = t & 15, r0 = t >> 4;
+  const int t = threadIdx.x, c = t & 15, r0 = 8 * (t >> 4);  // rows r0 .. r0 + 7
 
   const uint16_t* src = a.x + (int64_t)(bi * kBlock + r0) * a.ld_x + bj * kBlock + c * 8;
   u32x4 v[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i)
-    v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + (int64_t)(16 * i) * a.ld_x));
+    v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + (int64_t)i * a.ld_x));
+  u32x2 q[8];
 
   if constexpr (ACT == 0) {
     uint32_t m = 0;
@@ -112,12 +127,11 @@ __global__ __launch_bounds__(256) void quant_tile_t_kernel(TileQuantArgs a) {
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const u32x2 q = quant8(v[i], r);
+      q[i] = quant8(v[i], r);
       if (a.q)
         __builtin_nontemporal_store(
-            q, reinterpret_cast<u32x2*>(a.q + (int64_t)(bi * kBlock + r0 + 16 * i) * a.ld_q +
-                                        bj * kBlock + c * 8));
-      scatter_t(tq, q, c, r0 + 16 * i);
+            q[i], reinterpret_cast<u32x2*>(a.q + (int64_t)(bi * kBlock + r0 + i) * a.ld_q +
+                                           bj * kBlock + c * 8));
     }
   } else {
     if (a.q) {  // row-major codes with 1x128 row groups
@@ -125,7 +139,7 @@ __global__ __launch_bounds__(256) void quant_tile_t_kernel(TileQuantArgs a) {
       for (int i = 0; i < 8; ++i) {
         const uint32_t m = row16_max_u32(hmax_u16(amax8_pk(v[i])));
         const float S = scale_of(m, a.pow2);
-        const int64_t row = (int64_t)bi * kBlock + r0 + 16 * i;
+        const int64_t row = (int64_t)bi * kBlock + r0 + i;
         if (c == 0) a.s[row * tiles_c + bj] = S;
         __builtin_nontemporal_store(
             quant8(v[i], recip_f64(S)),
@@ -141,15 +155,16 @@ __global__ __launch_bounds__(256) void quant_tile_t_kernel(TileQuantArgs a) {
       const float s_hi = scale_of(cm[p] >> 16, a.pow2);
       r[2 * p] = recip_f64(s_lo);
       r[2 * p + 1] = recip_f64(s_hi);
-      if (r0 == 0) {
+      if (t < 16) {
         const int64_t col = (int64_t)bj * kBlock + 8 * c + 2 * p;
         a.st[col * tiles_r + bi] = s_lo;
         a.st[(col + 1) * tiles_r + bi] = s_hi;
       }
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) scatter_t(tq, quant8_cols(v[i], r), c, r0 + 16 * i);
+    for (int i = 0; i < 8; ++i) q[i] = quant8_cols(v[i], r);
   }
+  store_t(tq, q, c, r0);
   __syncthreads();
   // transposed tile row j (source column bj*128 + j) holds the codes of source rows bi*128 ..
 #pragma unroll
