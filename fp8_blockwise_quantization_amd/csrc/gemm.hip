@@ -749,7 +749,6 @@ template <class T>
 struct DecSlot {
   u32x4 a[T::A_LD];
   v8i b;
-  float sa;
   float sw;
 };
 
@@ -764,8 +763,16 @@ __device__ __forceinline__ void dec_fetch(DecSlot<T>& d, const GemmArgs& p, cons
     d.a[j] = *reinterpret_cast<const u32x4*>(xs + (int64_t)min(e >> 3, p.M - 1) * p.K + (e & 7) * 16);
   }
   d.b = load_frag_global(wrow, kb, (tid & 63) >> 4);
-  d.sa = p.sa[(int64_t)min(tid & (T::MPA - 1), p.M - 1) * p.KB + kb];
   d.sw = swrow[kb];
+}
+
+// Activation scales of a round (R slices from kb): thread tid loads the one of row tid % MPA and
+// slice kb + tid / MPA (every value once per workgroup, instead of once per wave and slice).
+template <class T>
+__device__ __forceinline__ float dec_fetch_sa(const GemmArgs& p, int kb, int tid) {
+  static_assert(T::MPA * T::R <= T::NT, "one activation scale per thread and round");
+  const int u = tid / T::MPA;
+  return u < T::R ? p.sa[(int64_t)min(tid % T::MPA, p.M - 1) * p.KB + kb + u] : 0.f;
 }
 
 template <class T>
@@ -776,7 +783,6 @@ __device__ __forceinline__ void dec_stage(uint8_t* st, const DecSlot<T>& d, int 
     const int row = e >> 3;
     *reinterpret_cast<u32x4*>(st + row * 128 + (((e & 7) ^ swz(row)) << 4)) = d.a[j];
   }
-  reinterpret_cast<float*>(st + T::SA_OFF)[tid] = d.sa;  // copies past MPA are not read
 }
 
 template <class T, int ACC>
@@ -825,6 +831,7 @@ __global__ __launch_bounds__(T::NT) void gemm_decode_kernel(GemmArgs p) {
   // registers refilled with round r + 2. All loads and waits are visible to the compiler: the
   // rounds are unrolled, so no branch separates a load from its use.
   DecSlot<T> ring0[T::R], ring1[T::R];
+  float sa0 = dec_fetch_sa<T>(p, kb0, tid), sa1 = dec_fetch_sa<T>(p, kb0 + T::R, tid);
 #pragma unroll
   for (int u = 0; u < T::R; ++u) dec_fetch<T>(ring0[u], p, wrow, swrow, kb0 + u, tid);
 #pragma unroll
@@ -834,24 +841,27 @@ __global__ __launch_bounds__(T::NT) void gemm_decode_kernel(GemmArgs p) {
   for (int i = 0; i < T::MT; ++i) acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
   uint8_t* const buf0 = lds;
   uint8_t* const buf1 = lds + T::R * T::STAGE;
-  auto round = [&](DecSlot<T>(&ring)[T::R], uint8_t* buf, int refill_kb) {
+  auto round = [&](DecSlot<T>(&ring)[T::R], float& sa, uint8_t* buf, int refill_kb) {
 #pragma unroll
     for (int u = 0; u < T::R; ++u) dec_stage<T>(buf + u * T::STAGE, ring[u], tid);
+    if (tid / T::MPA < T::R)
+      reinterpret_cast<float*>(buf + (tid / T::MPA) * T::STAGE + T::SA_OFF)[tid % T::MPA] = sa;
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < T::R; ++u) dec_mma<T, ACC>(buf + u * T::STAGE, ring[u], lane, acc);
     // refill only once consumed, so each set keeps its registers across the loop
     if (refill_kb >= 0) {
+      sa = dec_fetch_sa<T>(p, refill_kb, tid);
 #pragma unroll
       for (int u = 0; u < T::R; ++u) dec_fetch<T>(ring[u], p, wrow, swrow, refill_kb + u, tid);
     }
   };
   for (int k0 = 0; k0 < L - 2 * T::R; k0 += 2 * T::R) {
-    round(ring0, buf0, kb0 + k0 + 2 * T::R);
-    round(ring1, buf1, kb0 + k0 + 3 * T::R);
+    round(ring0, sa0, buf0, kb0 + k0 + 2 * T::R);
+    round(ring1, sa1, buf1, kb0 + k0 + 3 * T::R);
   }
-  round(ring0, buf0, -1);
-  round(ring1, buf1, -1);
+  round(ring0, sa0, buf0, -1);
+  round(ring1, sa1, buf1, -1);
 
   const int kq = lane >> 4, col = ncol + (lane & 15);
   float vals[T::MT * 4];
