@@ -536,6 +536,11 @@ __device__ __forceinline__ void mma_slice_big(const uint8_t* stage, float swv, i
   }
 }
 
+// Row pitch (bf16 elements) of the output tile staged in LDS by the bf16 epilogue: 8 bytes of
+// padding per row spread the column-wise writes over the banks and keep rows 8-byte aligned.
+template <class T>
+constexpr int kEpiPitch = T::BN + 4;
+
 // One BM x BN output tile over all K slices: operands DMA'd through STAGES LDS stages (the next
 // STAGES - 1 slices in flight while slice kb is multiplied), the weight scales of the tile's (up to two)
 // 128-column blocks read into LDS once. A / SA start at the tile's first row, B at its first
@@ -599,6 +604,33 @@ __device__ __forceinline__ void big_tile(const GemmArgs& p, uint8_t* stages,
   }
 
   const int r16 = lane & 15, kq = lane >> 4;
+  if (!p.out_f32) {
+    // bf16 output: the tile is rounded into LDS (the stages are free once every wave is past its
+    // last slice), then leaves as whole 16-byte pieces of rows instead of 2-byte stores
+    static_assert(T::BM * kEpiPitch<T> * 2 <= T::STAGES * T::STAGE_BYTES, "epilogue tile fits");
+    uint16_t* t16 = reinterpret_cast<uint16_t*>(stages);
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < T::TM; ++i)
+#pragma unroll
+      for (int j = 0; j < T::TN; ++j)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          t16[(wm * T::WM + i * 16 + 4 * kq + v) * kEpiPitch<T> + wn * T::WN + j * 16 + r16] =
+              f32_to_bf16_rne(acc[i][j][v]);
+    __syncthreads();
+    constexpr int CH = T::BN / 8;  // 16-byte pieces per row
+    for (int q = tid; q < T::BM * CH; q += T::NT) {
+      const int r = q / CH, c8 = (q - (q / CH) * CH) * 8;
+      if (r >= m_valid || c8 >= n_valid) continue;
+      const uint16_t* src = t16 + r * kEpiPitch<T> + c8;  // 8-byte aligned
+      const u32x2 lo = *reinterpret_cast<const u32x2*>(src);
+      const u32x2 hi = *reinterpret_cast<const u32x2*>(src + 4);
+      *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(p.y) + (y_row0 + r) * p.ldy + n0 + c8) =
+          u32x4{lo.x, lo.y, hi.x, hi.y};
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < T::TM; ++i) {
 #pragma unroll
@@ -609,11 +641,7 @@ __device__ __forceinline__ void big_tile(const GemmArgs& p, uint8_t* stages,
       for (int v = 0; v < 4; ++v) {
         const int r = wm * T::WM + i * 16 + 4 * kq + v;
         if (r >= m_valid) continue;
-        const int64_t off = (y_row0 + r) * p.ldy + n0 + c;
-        if (p.out_f32)
-          reinterpret_cast<float*>(p.y)[off] = acc[i][j][v];
-        else
-          reinterpret_cast<uint16_t*>(p.y)[off] = f32_to_bf16_rne(acc[i][j][v]);
+        reinterpret_cast<float*>(p.y)[(y_row0 + r) * p.ldy + n0 + c] = acc[i][j][v];
       }
     }
   }
