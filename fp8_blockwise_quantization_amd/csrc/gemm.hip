@@ -369,15 +369,23 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 __device__ __forceinline__ uint32_t lds_offset(const uint8_t* p) {
   return (uint32_t)(uintptr_t)(lds_ptr_t)p;
 }
+// The base address is wave-uniform; readfirstlane states that to the compiler, which must hold
+// it in scalar registers for the instruction's saddr operand.
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
 __device__ __forceinline__ void dma16(const void* base, uint32_t off, const uint8_t* lds) {
   const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_offset(lds));
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
-               :: "s"(m0v), "v"(off), "s"(base) : "memory", "m0");
+               :: "s"(m0v), "v"(off), "s"(uniform_ptr(base)) : "memory", "m0");
 }
 __device__ __forceinline__ void dma4(const void* base, uint32_t off, const uint8_t* lds) {
   const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_offset(lds));
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2"
-               :: "s"(m0v), "v"(off), "s"(base) : "memory", "m0");
+               :: "s"(m0v), "v"(off), "s"(uniform_ptr(base)) : "memory", "m0");
 }
 
 // Per-lane byte offsets of this lane's DMA sources within a K slice (computed once per tile).
@@ -546,14 +554,13 @@ constexpr int kEpiPitch = T::BN + 4;
 // 128-column blocks read into LDS once. A / SA start at the tile's first row, B at its first
 // column (weight row); SW is the weight-scale matrix [N/128][KB] (of the tile's expert); Y rows
 // y_row0 + r, r < m_valid, pitch ldy. The caller's previous use of the LDS arrays must be over.
-template <class T, int ACC>
-__device__ __forceinline__ void big_tile(const GemmArgs& p, uint8_t* stages,
-                                         float (*sw_s)[kMaxSlices], const uint8_t* A,
-                                         const float* SA, int m_valid, const uint8_t* B,
-                                         const float* SW, int n0, int n_valid, int64_t y_row0) {
+// Weight scales of the tile's (up to two) 128-column blocks into LDS, and the tile's DMA plan.
+template <class T>
+__device__ __forceinline__ DmaPlan<T> big_tile_prepare(const GemmArgs& p,
+                                                       float (*sw_s)[kMaxSlices], const float* SW,
+                                                       int n0, int m_valid, int n_valid) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave / T::WAVES_N, wn = wave % T::WAVES_N;
   const int KB = p.KB;
   // a wave whose columns are all past N still runs (it takes part in the DMA and barriers) on a
   // clamped scale row; its results are not stored
@@ -565,6 +572,24 @@ __device__ __forceinline__ void big_tile(const GemmArgs& p, uint8_t* stages,
       sw_s[b][k] = SW[(int64_t)nb * KB + k];
     }
   }
+  return make_dma_plan<T>(m_valid, n_valid, p.K, KB, wave, lane);
+}
+
+// The tile's multiply-accumulate and store. dma0_done: slice 0 is already on its way into stage
+// 0 (issued by the caller). on_loop_end runs once every wave is past the last slice -- the
+// stages are free then -- and before the epilogue, which stages the bf16 tile in LDS from byte
+// epi_off (so a caller may start the next tile's slice 0 into stage 0 meanwhile).
+template <class T, int ACC, class OnLoopEnd>
+__device__ __forceinline__ void big_tile_core(const GemmArgs& p, uint8_t* stages,
+                                              float (*sw_s)[kMaxSlices], const DmaPlan<T>& dp,
+                                              const uint8_t* A, const float* SA, int m_valid,
+                                              const uint8_t* B, const float* SW, int n0,
+                                              int n_valid, int64_t y_row0, bool dma0_done,
+                                              int epi_off, OnLoopEnd on_loop_end) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / T::WAVES_N, wn = wave % T::WAVES_N;
+  const int KB = p.KB;
   const float* swrow = sw_s[((n0 + wn * T::WN) >> 7) - (n0 >> 7)];
   // row-scaled B: the tile's rows of sb [N][KB] travel with each slice instead
   const float* SB = T::ROWB ? SW + (int64_t)n0 * KB : nullptr;
@@ -575,11 +600,10 @@ __device__ __forceinline__ void big_tile(const GemmArgs& p, uint8_t* stages,
 #pragma unroll
     for (int j = 0; j < T::TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  const DmaPlan<T> dp = make_dma_plan<T>(m_valid, n_valid, p.K, KB, wave, lane);
   if constexpr (T::STAGES == 2) {
     uint8_t* const stage0 = stages;
     uint8_t* const stage1 = stages + T::STAGE_BYTES;
-    dma_slice<T>(stage0, dp, A, B, SA, SB, 0, wave, lane);
+    if (!dma0_done) dma_slice<T>(stage0, dp, A, B, SA, SB, 0, wave, lane);
     for (int kb = 0; kb < KB; kb += 2) {
       wait_dma_and_barrier();
       if (kb + 1 < KB) dma_slice<T>(stage1, dp, A, B, SA, SB, kb + 1, wave, lane);
@@ -591,7 +615,7 @@ __device__ __forceinline__ void big_tile(const GemmArgs& p, uint8_t* stages,
     }
   } else {
     // slices kb + 1 and kb + 2 in flight while kb is multiplied
-    dma_slice<T>(stages, dp, A, B, SA, SB, 0, wave, lane);
+    if (!dma0_done) dma_slice<T>(stages, dp, A, B, SA, SB, 0, wave, lane);
     if (KB > 1) dma_slice<T>(stages + T::STAGE_BYTES, dp, A, B, SA, SB, 1, wave, lane);
     int cur = 0;
     for (int kb = 0; kb < KB; ++kb) {
@@ -607,9 +631,9 @@ __device__ __forceinline__ void big_tile(const GemmArgs& p, uint8_t* stages,
   if (!p.out_f32) {
     // bf16 output: the tile is rounded into LDS (the stages are free once every wave is past its
     // last slice), then leaves as whole 16-byte pieces of rows instead of 2-byte stores
-    static_assert(T::BM * kEpiPitch<T> * 2 <= T::STAGES * T::STAGE_BYTES, "epilogue tile fits");
-    uint16_t* t16 = reinterpret_cast<uint16_t*>(stages);
+    uint16_t* t16 = reinterpret_cast<uint16_t*>(stages + epi_off);
     __syncthreads();
+    on_loop_end();
 #pragma unroll
     for (int i = 0; i < T::TM; ++i)
 #pragma unroll
@@ -631,6 +655,8 @@ __device__ __forceinline__ void big_tile(const GemmArgs& p, uint8_t* stages,
     }
     return;
   }
+  __syncthreads();
+  on_loop_end();
 #pragma unroll
   for (int i = 0; i < T::TM; ++i) {
 #pragma unroll
@@ -656,9 +682,12 @@ __global__ __launch_bounds__(T::NT) void gemm_big_kernel(GemmArgs p) {
   int tm, tn;
   tile_coords(blockIdx.x, tiles_m * tiles_n, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * T::BM, n0 = tn * T::BN;
-  big_tile<T, ACC>(p, stages, sw_s, p.xq + (int64_t)m0 * p.K,
-                       p.sa + (int64_t)m0 * p.KB, min(T::BM, p.M - m0), p.wq + (int64_t)n0 * p.K,
-                       p.sw, n0, min(T::BN, p.N - n0), m0);
+  const int m_valid = min(T::BM, p.M - m0), n_valid = min(T::BN, p.N - n0);
+  static_assert(T::BM * kEpiPitch<T> * 2 <= T::STAGES * T::STAGE_BYTES, "epilogue tile fits");
+  const DmaPlan<T> dp = big_tile_prepare<T>(p, sw_s, p.sw, n0, m_valid, n_valid);
+  big_tile_core<T, ACC>(p, stages, sw_s, dp, p.xq + (int64_t)m0 * p.K, p.sa + (int64_t)m0 * p.KB,
+                        m_valid, p.wq + (int64_t)n0 * p.K, p.sw, n0, n_valid, m0, false, 0,
+                        [] {});
 }
 
 // Grouped GEMM on the DMA-fed tiles, persistent: a fixed grid of workgroups walks the list of
@@ -705,7 +734,11 @@ __global__ __launch_bounds__(T::NT) void grouped_big_kernel(GemmArgs p) {
   const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
   const int chunk = (total + 7) / 8;
   const int t_end = min(total, (xcd + 1) * chunk);
-  for (int t = xcd * chunk + slot; t < t_end; t += per_xcd) {
+  // tile t -> (expert e, first row, valid rows, first column)
+  struct Coords {
+    int e, row0, m_valid, n0, n_valid;
+  };
+  auto coords = [&](int t) {
     const int tm_lin = t / tiles_n, tn = t - (t / tiles_n) * tiles_n;
     // expert e: s_first[e] <= tm_lin < s_first[e + 1]
     int lo = 0, hi = E;
@@ -713,16 +746,53 @@ __global__ __launch_bounds__(T::NT) void grouped_big_kernel(GemmArgs p) {
       const int mid = (lo + hi) >> 1;
       if (s_first[mid] <= tm_lin) lo = mid; else hi = mid;
     }
-    const int e = lo;
-    const int r_lo = min(max(p.offsets[e], 0), p.M);
-    const int r_hi = min(max(p.offsets[e + 1], r_lo), p.M);
-    const int row0 = r_lo + (tm_lin - s_first[e]) * T::BM;
-    const int n0 = tn * T::BN;
-    __syncthreads();  // the previous tile is done with the LDS arrays
-    big_tile<T, ACC>(p, stages, sw_s, p.xq + (int64_t)row0 * p.K,
-                         p.sa + (int64_t)row0 * p.KB, min(T::BM, r_hi - row0),
-                         p.wq + e * p.wq_stride + (int64_t)n0 * p.K, p.sw + e * p.sw_stride, n0,
-                         min(T::BN, p.N - n0), row0);
+    // every lane computes the same values; readfirstlane tells the compiler so (the DMA bases
+    // must be scalar registers)
+    Coords c;
+    c.e = __builtin_amdgcn_readfirstlane(lo);
+    const int r_lo = min(max(p.offsets[c.e], 0), p.M);
+    const int r_hi = min(max(p.offsets[c.e + 1], r_lo), p.M);
+    c.row0 = __builtin_amdgcn_readfirstlane(r_lo + (tm_lin - s_first[c.e]) * T::BM);
+    c.m_valid = __builtin_amdgcn_readfirstlane(min(T::BM, r_hi - c.row0));
+    c.n0 = __builtin_amdgcn_readfirstlane(tn * T::BN);
+    c.n_valid = __builtin_amdgcn_readfirstlane(min(T::BN, p.N - c.n0));
+    return c;
+  };
+  const uint8_t* const wq0 = p.wq;
+  auto a_of = [&](const Coords& c) { return p.xq + (int64_t)c.row0 * p.K; };
+  auto sa_of = [&](const Coords& c) { return p.sa + (int64_t)c.row0 * p.KB; };
+  auto b_of = [&](const Coords& c) { return wq0 + c.e * p.wq_stride + (int64_t)c.n0 * p.K; };
+  auto sw_of = [&](const Coords& c) { return p.sw + c.e * p.sw_stride; };
+  // The next tile's slice 0 goes out into stage 0 while this tile's epilogue works in the
+  // stages behind it: each tile's DMA start-up hides behind the previous tile's store phase.
+  static_assert(T::STAGE_BYTES + T::BM * kEpiPitch<T> * 2 <= T::STAGES * T::STAGE_BYTES,
+                "epilogue tile fits behind stage 0");
+  int t = xcd * chunk + slot;
+  if (t >= t_end) return;
+  const int tid2 = threadIdx.x, lane = tid2 & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid2 >> 6);
+  Coords c = coords(t);
+  DmaPlan<T> dp = big_tile_prepare<T>(p, sw_s, sw_of(c), c.n0, c.m_valid, c.n_valid);
+  dma_slice<T>(stages, dp, a_of(c), b_of(c), sa_of(c), nullptr, 0, wave, lane);
+  for (;;) {
+    const int t_next = t + per_xcd;
+    const bool more = t_next < t_end;
+    Coords cn = c;
+    DmaPlan<T> dpn = dp;
+    big_tile_core<T, ACC>(p, stages, sw_s, dp, a_of(c), sa_of(c), c.m_valid, b_of(c), sw_of(c),
+                          c.n0, c.n_valid, c.row0, true, T::STAGE_BYTES, [&] {
+                            if (!more) return;
+                            cn = coords(t_next);
+                            dpn = big_tile_prepare<T>(p, sw_s, sw_of(cn), cn.n0, cn.m_valid,
+                                                      cn.n_valid);
+                            dma_slice<T>(stages, dpn, a_of(cn), b_of(cn), sa_of(cn), nullptr, 0,
+                                         wave, lane);
+                          });
+    if (!more) break;
+    __syncthreads();  // the epilogue's LDS reads are done before the next tile's DMA lands there
+    t = t_next;
+    c = cn;
+    dp = dpn;
   }
 }
 
