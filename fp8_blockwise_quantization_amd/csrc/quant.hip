@@ -80,33 +80,33 @@ __global__ __launch_bounds__(256) void quant_weight_blk128_kernel(WeightBatch b)
 template <int STEPS>
 __global__ __launch_bounds__(256) void quant_act_tok128_kernel(
     const uint16_t* __restrict__ x, int64_t ld_x, uint8_t* __restrict__ xq, int64_t ld_xq,
-    float* __restrict__ sa, int KB, int64_t total_groups, int pow2) {
+    float* __restrict__ sa, int KB, int total_groups, int pow2) {
+  // group indices fit 32 bits (the C ABI keeps M * K/128 below 2^30): 32-bit division only
   const int lane16 = threadIdx.x & 15;
-  const int64_t g0 = (int64_t)blockIdx.x * (16 * STEPS) + (threadIdx.x >> 4);
+  const unsigned g0 = blockIdx.x * (16u * STEPS) + (threadIdx.x >> 4);
+  const unsigned kb = (unsigned)KB, total = (unsigned)total_groups;
 
   u32x4 v[STEPS];
+  int64_t xoff[STEPS], qoff[STEPS];  // element offsets of the group's 16-byte chunk in X and Xq
 #pragma unroll
   for (int s = 0; s < STEPS; ++s) {
-    const int64_t g = g0 + 16 * s;
+    const unsigned g = g0 + 16u * s;
+    const unsigned row = g / kb, slice = g - row * kb;
+    xoff[s] = (int64_t)row * ld_x + slice * kBlock + lane16 * 8;
+    qoff[s] = (int64_t)row * ld_xq + slice * kBlock + lane16 * 8;
     v[s] = u32x4{0u, 0u, 0u, 0u};
-    if (g < total_groups) {
-      const int64_t row = g / KB, slice = g - (g / KB) * KB;
-      v[s] = __builtin_nontemporal_load(
-          reinterpret_cast<const u32x4*>(x + row * ld_x + slice * kBlock + lane16 * 8));
-    }
+    if (g < total) v[s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x + xoff[s]));
   }
 #pragma unroll
   for (int s = 0; s < STEPS; ++s) {
-    const int64_t g = g0 + 16 * s;
+    const unsigned g = g0 + 16u * s;
     // every lane of the row takes part in the reduction, whether or not its group exists
     const uint32_t m = row16_max_u32(hmax_u16(amax8_pk(v[s])));
     const float S = pow2 ? pow2_scale_from_amax_bits(m) : scale_from_amax_bits(m);
     const double r = recip_f64(S);
-    if (g < total_groups) {
-      const int64_t row = g / KB, slice = g - (g / KB) * KB;
+    if (g < total) {
       if (lane16 == 0) sa[g] = S;
-      __builtin_nontemporal_store(
-          quant8(v[s], r), reinterpret_cast<u32x2*>(xq + row * ld_xq + slice * kBlock + lane16 * 8));
+      __builtin_nontemporal_store(quant8(v[s], r), reinterpret_cast<u32x2*>(xq + qoff[s]));
     }
   }
 }
@@ -161,15 +161,15 @@ hipError_t launch_quant_weight_batch(const WeightBatch& b, int total_blocks, hip
 hipError_t launch_quant_act(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x, uint8_t* xq,
                             int64_t ld_xq, float* sa, int pow2, hipStream_t stream) {
   const int KB = (int)(K / kBlock);
-  const int64_t groups = M * KB;
+  const int64_t groups = M * KB;  // < 2^30 (checked by the C ABI)
   if (groups >= int64_t{64} * 1024) {  // >= 1024 workgroups even at 4 steps each
     const int64_t wgs = (groups + 63) / 64;
     hipLaunchKernelGGL(quant_act_tok128_kernel<4>, dim3((unsigned)wgs), dim3(256), 0, stream, x,
-                       ld_x, xq, ld_xq, sa, KB, groups, pow2);
+                       ld_x, xq, ld_xq, sa, KB, (int)groups, pow2);
   } else {
     const int64_t wgs = (groups + 15) / 16;
     hipLaunchKernelGGL(quant_act_tok128_kernel<1>, dim3((unsigned)wgs), dim3(256), 0, stream, x,
-                       ld_x, xq, ld_xq, sa, KB, groups, pow2);
+                       ld_x, xq, ld_xq, sa, KB, (int)groups, pow2);
   }
   return hipGetLastError();
 }
