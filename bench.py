@@ -321,7 +321,7 @@ def cpu_baseline_dense(linears, M, seed, budget_linears, min_seconds=10.0, scale
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "this benchmark runs on one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
     import torch
