@@ -764,24 +764,25 @@ __global__ __launch_bounds__(T::NT) void grouped_big_kernel(GemmArgs p) {
   auto b_of = [&](const Coords& c) { return wq0 + c.e * p.wq_stride + (int64_t)c.n0 * p.K; };
   auto sw_of = [&](const Coords& c) { return p.sw + c.e * p.sw_stride; };
   // The next tile's slice 0 goes out into stage 0 while this tile's epilogue works in the
-  // stages behind it: each tile's DMA start-up hides behind the previous tile's store phase.
-  static_assert(T::STAGE_BYTES + T::BM * kEpiPitch<T> * 2 <= T::STAGES * T::STAGE_BYTES,
-                "epilogue tile fits behind stage 0");
+  // stages behind it (when the staged tile fits there): each tile's DMA start-up hides behind
+  // the previous tile's store phase.
+  constexpr bool kAhead = T::STAGE_BYTES + T::BM * kEpiPitch<T> * 2 <= T::STAGES * T::STAGE_BYTES;
+  static_assert(T::BM * kEpiPitch<T> * 2 <= T::STAGES * T::STAGE_BYTES, "epilogue tile fits");
   int t = xcd * chunk + slot;
   if (t >= t_end) return;
   const int tid2 = threadIdx.x, lane = tid2 & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid2 >> 6);
   Coords c = coords(t);
   DmaPlan<T> dp = big_tile_prepare<T>(p, sw_s, sw_of(c), c.n0, c.m_valid, c.n_valid);
-  dma_slice<T>(stages, dp, a_of(c), b_of(c), sa_of(c), nullptr, 0, wave, lane);
+  if (kAhead) dma_slice<T>(stages, dp, a_of(c), b_of(c), sa_of(c), nullptr, 0, wave, lane);
   for (;;) {
     const int t_next = t + per_xcd;
     const bool more = t_next < t_end;
     Coords cn = c;
     DmaPlan<T> dpn = dp;
     big_tile_core<T, ACC>(p, stages, sw_s, dp, a_of(c), sa_of(c), c.m_valid, b_of(c), sw_of(c),
-                          c.n0, c.n_valid, c.row0, true, T::STAGE_BYTES, [&] {
-                            if (!more) return;
+                          c.n0, c.n_valid, c.row0, kAhead, kAhead ? T::STAGE_BYTES : 0, [&] {
+                            if (!kAhead || !more) return;
                             cn = coords(t_next);
                             dpn = big_tile_prepare<T>(p, sw_s, sw_of(cn), cn.n0, cn.m_valid,
                                                       cn.n_valid);
@@ -791,8 +792,13 @@ __global__ __launch_bounds__(T::NT) void grouped_big_kernel(GemmArgs p) {
     if (!more) break;
     __syncthreads();  // the epilogue's LDS reads are done before the next tile's DMA lands there
     t = t_next;
-    c = cn;
-    dp = dpn;
+    if (kAhead) {
+      c = cn;
+      dp = dpn;
+    } else {
+      c = coords(t);
+      dp = big_tile_prepare<T>(p, sw_s, sw_of(c), c.n0, c.m_valid, c.n_valid);
+    }
   }
 }
 
