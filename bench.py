@@ -55,7 +55,7 @@ def parse():
     ap.add_argument("--workload", default="qwen3-8b-decode",
                     choices=["qwen3-8b-decode", "qwen3-8b-prefill", "llama31-8b-mlp",
                              "llama31-8b-weight-sync", "qwen3-30b-a3b-moe", "qwen3-8b-kv-cache",
-                             "qwen3-8b-backward"])
+                             "qwen3-8b-backward", "qwen3-8b-decode-fused-act"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--scales", default="fp32", choices=["fp32", "pow2"],
                     help="block-scale format: fp32(amax/448) (default) or powers of two, whose "
@@ -359,6 +359,8 @@ def main():
         return run_kv_cache(args, torch, fq, synth, dev_name)
     elif args.workload == "qwen3-8b-backward":
         return run_backward(args, torch, fq, synth, dev_name)
+    elif args.workload == "qwen3-8b-decode-fused-act":
+        return run_fused_act(args, torch, fq, synth, dev_name)
     else:
         return run_moe(args, torch, fq, synth, dev_name)
 
@@ -448,6 +450,59 @@ def _timed(torch, fn, steps, warmup, timers=()):
     b.record()
     torch.cuda.synchronize()
     return a.elapsed_time(b) / steps
+
+
+def run_fused_act(args, torch, fq, synth, dev_name):
+    """The decode GEMMs of one Qwen3-8B block (serving layout: q/k/v, o, gate/up, down) at small
+    token counts, two ways: activation quantization and GEMM as two launches per GEMM, or the
+    GEMM with the quantization fused in (one launch). Both are timed as the host launches them
+    (where small batches are launch-bound) and replayed from a HIP graph (GPU time only)."""
+    groups = serving_layout(synth.DENSE_LINEARS_QWEN3_8B)
+    pow2 = args.scales == "pow2"
+    accum = "mx" if pow2 else "fp8"
+    g = torch.Generator(device="cuda").manual_seed(11 + args.seed)
+    weights = []
+    for i, (name, N, K) in enumerate(groups):
+        w = synth.weight_bf16(N, K, seed=9100 + i, device="cuda")
+        weights.append(fq.quant_weight(w, scale=args.scales))
+        del w
+    results = []
+    for M in (1, 16, 64):
+        xs = [synth.act_bf16(M, K, seed=9200 + M + i, device="cuda")
+              for i, (_, _, K) in enumerate(groups)]
+        ys = [torch.empty((M, N), dtype=torch.bfloat16, device="cuda") for _, N, _ in groups]
+        qs = [(torch.empty((M, K), dtype=torch.uint8, device="cuda"),
+               torch.empty((M, K // 128), dtype=torch.float32, device="cuda")) for _, _, K in groups]
+        ws = fq.new_workspace(max(fq.fp8rl_workspace_bytes(fq.FP8RL_OP_GEMM, M, N, K)
+                                  for _, N, K in groups), "cuda")
+
+        def unfused():
+            for x, (wq, sw), y, (xq, sa) in zip(xs, weights, ys, qs):
+                fq.quant_act(x, xq, sa, scale=args.scales)
+                fq.gemm(xq, sa, wq, sw, y=y, workspace=ws, accum=accum)
+
+        def fused():
+            for x, (wq, sw), y in zip(xs, weights, ys):
+                fq.gemm_fused_act(x, wq, sw, y=y, workspace=ws, accum=accum, scale=args.scales)
+
+        row = {"M": M}
+        for label, fn in (("unfused", unfused), ("fused", fused)):
+            row[f"eager_{label}_us"] = 1e3 * _timed(torch, fn, max(args.steps, 20), max(args.warmup, 3))
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                fn()
+            row[f"graph_{label}_us"] = 1e3 * _timed(torch, graph.replay, max(args.steps, 20),
+                                                    max(args.warmup, 3))
+        row["graph_fused_over_unfused"] = row["graph_fused_us"] / row["graph_unfused_us"]
+        row["eager_fused_over_unfused"] = row["eager_fused_us"] / row["eager_unfused_us"]
+        results.append(row)
+    print(json.dumps({
+        "workload": "Qwen3-8B decode GEMMs (q/k/v, o, gate/up, down), activation quantization "
+                    "fused into the GEMM vs a separate launch",
+        "metric": "microseconds per block (4 GEMMs with their activation quantization)",
+        "scales": args.scales, "launches_per_block": {"unfused": 2 * len(groups),
+                                                      "fused": len(groups)},
+        "gemms": [list(gr) for gr in groups], "results": results, "gpu": dev_name}), flush=True)
 
 
 def run_mlp(args, torch, fq, synth, dev_name):

@@ -27,6 +27,7 @@ FP8RL_SCALE_POW2 = 1
 FP8RL_OP_GEMM = 0
 FP8RL_OP_GROUPED_GEMM = 1
 FP8RL_OP_GEMM_ROWSCALED = 2
+FP8RL_OP_GEMM_FUSED_ACT = 3
 
 class WeightDesc(ctypes.Structure):
     """fp8rl_weight_desc (include/fp8rl.h)."""
@@ -109,6 +110,10 @@ def lib() -> ctypes.CDLL:
             "fp8rl_gemm_w8a8_rowscaled": (
                 ctypes.c_int,
                 [vp, vp, vp, vp, i64, i64, i64, vp, ctypes.c_int, i64, ctypes.c_int, vp, sz, vp]),
+            "fp8rl_gemm_w8a8_fused_act_quant": (
+                ctypes.c_int,
+                [vp, i64, vp, vp, i64, i64, i64, vp, ctypes.c_int, i64, ctypes.c_int,
+                 ctypes.c_int, vp, sz, vp]),
             "fp8rl_workspace_bytes": (sz, [ctypes.c_int, i64, i64, i64, i32]),
             "fp8rl_status_string": (ctypes.c_char_p, [ctypes.c_int]),
             "fp8rl_version": (ctypes.c_int, []),
@@ -139,6 +144,7 @@ EXPORTED = (
     "fp8rl_quant_weight_blk128_t",
     "fp8rl_quant_act_colwise128",
     "fp8rl_gemm_w8a8_rowscaled",
+    "fp8rl_gemm_w8a8_fused_act_quant",
     "fp8rl_workspace_bytes",
     "fp8rl_status_string",
     "fp8rl_version",
@@ -379,6 +385,32 @@ def fp8rl_gemm_w8a8_rowscaled(aq, sa, bq, sb, out_dtype=torch.bfloat16, y=None, 
                                            _ptr(y), _out_code(y.dtype), ld_y,
                                            _accum_code(accum, y.dtype), _ptr(workspace), ws_bytes,
                                            _stream(stream)), "fp8rl_gemm_w8a8_rowscaled")
+    return y
+
+
+def fp8rl_gemm_w8a8_fused_act_quant(x, wq, sw, out_dtype=torch.bfloat16, y=None, workspace=None,
+                                    stream=None, accum=None, scale="fp32"):
+    """Y[M][N] for bf16 X (M <= 64): the activation quantization (1x128 groups, `scale` format)
+    fused into the blockscaled GEMM; the same bits as quantizing X first."""
+    ld_x = _rows(x, "x", torch.bfloat16)
+    _dense(wq, "wq", torch.uint8)
+    _dense(sw, "sw", torch.float32)
+    M, K = x.shape
+    N = wq.shape[0]
+    if wq.shape[1] != K:
+        raise ValueError("K mismatch between x and wq")
+    if y is None:
+        y = torch.empty((M, N), dtype=out_dtype, device=x.device)
+    ld_y = _rows(y, "y", y.dtype)
+    need = fp8rl_workspace_bytes(FP8RL_OP_GEMM_FUSED_ACT, M, N, K)
+    if workspace is None and need > 0:
+        workspace = new_workspace(need, x.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().fp8rl_gemm_w8a8_fused_act_quant(_ptr(x), ld_x, _ptr(wq), _ptr(sw), M, N, K,
+                                                 _ptr(y), _out_code(y.dtype), ld_y,
+                                                 _accum_code(accum, y.dtype), _scale_code(scale),
+                                                 _ptr(workspace), ws_bytes, _stream(stream)),
+           "fp8rl_gemm_w8a8_fused_act_quant")
     return y
 
 

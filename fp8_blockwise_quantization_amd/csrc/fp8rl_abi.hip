@@ -371,6 +371,10 @@ size_t fp8rl_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int32_t E)
   if (op == FP8RL_OP_GEMM) return fp8rl::plan_gemm(M, N, K).workspace_bytes;
   if (op == FP8RL_OP_GEMM_ROWSCALED) return fp8rl::plan_gemm(M, N, K, true).workspace_bytes;
   if (op == FP8RL_OP_GROUPED_GEMM) return fp8rl::plan_grouped_gemm(M, N, K, E).workspace_bytes;
+  if (op == FP8RL_OP_GEMM_FUSED_ACT) {
+    const fp8rl::GemmPlan plan = fp8rl::plan_gemm(M, N, K);
+    return fp8rl::plan_fuses_act(plan) ? plan.workspace_bytes : 0;
+  }
   return 0;
 }
 
@@ -402,6 +406,36 @@ int fp8rl_gemm_w8a8_blockscaled(const uint8_t* xq, const float* sa, const uint8_
                                 size_t workspace_bytes, void* stream) {
   return gemm_common(xq, sa, wq, sw, M, N, K, y, y_dtype, ld_y, accum, false, workspace,
                      workspace_bytes, stream);
+}
+
+int fp8rl_gemm_w8a8_fused_act_quant(const uint16_t* x, int64_t ld_x, const uint8_t* wq,
+                                    const float* sw, int64_t M, int64_t N, int64_t K, void* y,
+                                    int y_dtype, int64_t ld_y, int accum, int scale_fmt,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  if (int s = check_dims(M, N, K)) return s;
+  if (M == 0) return FP8RL_OK;
+  if (!x || !wq || !sw || !y) return FP8RL_ERR_NULL;
+  if (N == 0 || K == 0 || N % 128 || K % 128) return FP8RL_ERR_SHAPE;
+  if (ld_x < K || ld_x > kMaxDim) return FP8RL_ERR_SHAPE;
+  if (y_dtype != FP8RL_OUT_BF16 && y_dtype != FP8RL_OUT_F32) return FP8RL_ERR_DTYPE;
+  if (ld_y < N) return FP8RL_ERR_SHAPE;
+  if (accum != FP8RL_ACCUM_FP8 && accum != FP8RL_ACCUM_F16 && accum != FP8RL_ACCUM_MX)
+    return FP8RL_ERR_ARG;
+  if (scale_fmt != FP8RL_SCALE_FP32 && scale_fmt != FP8RL_SCALE_POW2) return FP8RL_ERR_ARG;
+  if (accum == FP8RL_ACCUM_MX && scale_fmt != FP8RL_SCALE_POW2) return FP8RL_ERR_ARG;
+  const int64_t ybytes = y_dtype == FP8RL_OUT_F32 ? 4 : 2;
+  if (!aligned(x, 16) || (ld_x * 2) % 16 || !aligned(wq, 16) || !aligned(sw, 4) ||
+      !aligned(y, 16) || (ld_y * ybytes) % 16)
+    return FP8RL_ERR_ALIGN;
+  const fp8rl::GemmPlan plan = fp8rl::plan_gemm(M, N, K);
+  if (!fp8rl::plan_fuses_act(plan)) return FP8RL_ERR_SHAPE;  // M > 64 or K/128 odd
+  if (plan.workspace_bytes > 0) {
+    if (!workspace || workspace_bytes < plan.workspace_bytes) return FP8RL_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return FP8RL_ERR_ALIGN;
+  }
+  return hip_status(fp8rl::launch_gemm_fused_act(
+      x, ld_x, scale_fmt == FP8RL_SCALE_POW2, wq, sw, M, N, K, y, y_dtype == FP8RL_OUT_F32, ld_y,
+      accum, workspace, plan, as_stream(stream)));
 }
 
 int fp8rl_gemm_w8a8_rowscaled(const uint8_t* aq, const float* sa, const uint8_t* bq,

@@ -70,6 +70,11 @@ struct GemmArgs {
   int E;
   int64_t wq_stride, sw_stride;  // per expert
   int tiles_n;
+  // decode GEMM with the activation quantization fused in: bf16 X rows (pitch ld_x) replace
+  // xq / sa, and pow2 selects the scale format of its 1x128 groups
+  const uint16_t* x;
+  int64_t ld_x;
+  int pow2;
 };
 
 template <class T>
@@ -826,6 +831,7 @@ struct Dec {
   static constexpr int MP = 16 * MT;
   static constexpr int MPA = MP < 32 ? 32 : MP;  // staged rows: at least one 16-byte load per thread
   static constexpr int A_LD = MPA * 8 / NT;       // 16-byte activation loads per thread and slice
+  static constexpr int X_LD = MPA * 16 / NT;      // the same for bf16 activations (fused form)
   static constexpr int A_BYTES = MPA * 128;
   static constexpr int SA_OFF = A_BYTES;          // activation scales of the slice (x NT / MPA)
   static constexpr int STAGE = A_BYTES + NT * 4;  // one slice
@@ -849,22 +855,45 @@ __device__ __forceinline__ v8i load_frag_global(const uint8_t* row_base, int kb,
   return f;
 }
 
-template <class T>
+// One slice in registers: the activation rows' 16-byte pieces (E4M3 codes, or bf16 values in the
+// fused form), this lane's weight fragment and the weight block scale.
+template <class T, bool F>
 struct DecSlot {
-  u32x4 a[T::A_LD];
+  u32x4 a[F ? T::X_LD : T::A_LD];
   v8i b;
   float sw;
 };
 
+// Fused form: bf16 piece j of thread tid for the slice at ring position u: the 16 lanes of a
+// DPP row hold one activation row (a 1x128 group), so its amax is one row reduction. The map is
+// rotated by one wave per ring position, so that with few live rows the R slices of a round
+// fall on different waves: row r < 4 of slice u sits on wave (4 - u) % 4.
 template <class T>
-__device__ __forceinline__ void dec_fetch(DecSlot<T>& d, const GemmArgs& p, const uint8_t* wrow,
-                                          const float* swrow, int kb, int tid) {
-  const uint8_t* xs = p.xq + (int64_t)kb * 128;
+__device__ __forceinline__ int dec_x_piece(int j, int tid, int u) {
+  return j * T::NT + ((tid + 64 * u) & (T::NT - 1));  // row e / 16, values 8 (e % 16) ..
+}
+
+template <class T, bool F>
+__device__ __forceinline__ void dec_fetch(DecSlot<T, F>& d, const GemmArgs& p, const uint8_t* wrow,
+                                          const float* swrow, int kb, int tid, int u) {
+  // activation rows are read by every tile: ordinary (cached) loads; rows past M repeat row
+  // M - 1 (codes) or are not loaded (bf16), as their products reach no stored output
+  if constexpr (F) {
+    const uint16_t* xs = p.x + (int64_t)kb * 128;
 #pragma unroll
-  for (int j = 0; j < T::A_LD; ++j) {
-    const int e = j * T::NT + tid;  // 16-byte chunk e: row e / 8, chunk e % 8
-    // activation rows are read by every tile: ordinary (cached) loads
-    d.a[j] = *reinterpret_cast<const u32x4*>(xs + (int64_t)min(e >> 3, p.M - 1) * p.K + (e & 7) * 16);
+    for (int j = 0; j < T::X_LD; ++j) {
+      const int e = dec_x_piece<T>(j, tid, u);
+      d.a[j] = u32x4{0u, 0u, 0u, 0u};
+      if ((e >> 4) < p.M)
+        d.a[j] = *reinterpret_cast<const u32x4*>(xs + (int64_t)(e >> 4) * p.ld_x + (e & 15) * 8);
+    }
+  } else {
+    const uint8_t* xs = p.xq + (int64_t)kb * 128;
+#pragma unroll
+    for (int j = 0; j < T::A_LD; ++j) {
+      const int e = j * T::NT + tid;  // 16-byte chunk e: row e / 8, chunk e % 8
+      d.a[j] = *reinterpret_cast<const u32x4*>(xs + (int64_t)min(e >> 3, p.M - 1) * p.K + (e & 7) * 16);
+    }
   }
   d.b = load_frag_global(wrow, kb, (tid & 63) >> 4);
   d.sw = swrow[kb];
@@ -880,7 +909,7 @@ __device__ __forceinline__ float dec_fetch_sa(const GemmArgs& p, int kb, int tid
 }
 
 template <class T>
-__device__ __forceinline__ void dec_stage(uint8_t* st, const DecSlot<T>& d, int tid) {
+__device__ __forceinline__ void dec_stage(uint8_t* st, const DecSlot<T, false>& d, int tid) {
 #pragma unroll
   for (int j = 0; j < T::A_LD; ++j) {
     const int e = j * T::NT + tid;
@@ -889,8 +918,32 @@ __device__ __forceinline__ void dec_stage(uint8_t* st, const DecSlot<T>& d, int 
   }
 }
 
-template <class T, int ACC>
-__device__ __forceinline__ void dec_mma(const uint8_t* st, const DecSlot<T>& d, int lane,
+// Fused form: quantize the slice's bf16 activation rows into the staged layout, exactly as the
+// 1x128 activation quantizer does: each lane writes its 8 codes and lane 0 of the row the group's
+// scale. Padding rows (M <= row < MPA) get zero codes and a zero scale without the arithmetic:
+// whole rows, so the reduction's lanes are all active or all idle.
+template <class T>
+__device__ __forceinline__ void dec_stage(uint8_t* st, const DecSlot<T, true>& d, int tid, int u,
+                                          int M, int pow2) {
+  float* sa = reinterpret_cast<float*>(st + T::SA_OFF);
+#pragma unroll
+  for (int j = 0; j < T::X_LD; ++j) {
+    const int e = dec_x_piece<T>(j, tid, u), row = e >> 4, c = e & 15;
+    u32x2 q = u32x2{0u, 0u};
+    float S = 0.f;
+    if (row < M) {
+      const uint32_t m = row16_max_u32(hmax_u16(amax8_pk(d.a[j])));
+      S = pow2 ? pow2_scale_from_amax_bits(m) : scale_from_amax_bits(m);
+      q = quant8(d.a[j], recip_f64(S));
+    }
+    // codes 8c .. 8c + 7 of the row: half c & 1 of its (swizzled) 16-byte chunk c / 2
+    *reinterpret_cast<u32x2*>(st + row * 128 + ((((c >> 1) ^ swz(row)) << 4) | ((c & 1) << 3))) = q;
+    if (c == 0) sa[row] = S;
+  }
+}
+
+template <class T, int ACC, bool F>
+__device__ __forceinline__ void dec_mma(const uint8_t* st, const DecSlot<T, F>& d, int lane,
                                         v4f (&acc)[T::MT]) {
   const int r16 = lane & 15, kq = lane >> 4;
   if constexpr (ACC == 2) {  // power-of-two scales applied by the matrix cores (see mma_slice_big)
@@ -918,7 +971,8 @@ __device__ __forceinline__ void dec_mma(const uint8_t* st, const DecSlot<T>& d, 
   }
 }
 
-template <class T, int ACC>
+// F: the activation quantization is fused in (bf16 rows p.x instead of p.xq / p.sa).
+template <class T, int ACC, bool F>
 __global__ __launch_bounds__(T::NT) void gemm_decode_kernel(GemmArgs p) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[T::LDS_BYTES];
   __shared__ int s_flag;
@@ -934,30 +988,36 @@ __global__ __launch_bounds__(T::NT) void gemm_decode_kernel(GemmArgs p) {
   // in flight; it is staged into LDS buffer r & 1 with one barrier, multiplied, and its
   // registers refilled with round r + 2. All loads and waits are visible to the compiler: the
   // rounds are unrolled, so no branch separates a load from its use.
-  DecSlot<T> ring0[T::R], ring1[T::R];
-  float sa0 = dec_fetch_sa<T>(p, kb0, tid), sa1 = dec_fetch_sa<T>(p, kb0 + T::R, tid);
+  DecSlot<T, F> ring0[T::R], ring1[T::R];
+  float sa0 = F ? 0.f : dec_fetch_sa<T>(p, kb0, tid);
+  float sa1 = F ? 0.f : dec_fetch_sa<T>(p, kb0 + T::R, tid);
 #pragma unroll
-  for (int u = 0; u < T::R; ++u) dec_fetch<T>(ring0[u], p, wrow, swrow, kb0 + u, tid);
+  for (int u = 0; u < T::R; ++u) dec_fetch<T>(ring0[u], p, wrow, swrow, kb0 + u, tid, u);
 #pragma unroll
-  for (int u = 0; u < T::R; ++u) dec_fetch<T>(ring1[u], p, wrow, swrow, kb0 + T::R + u, tid);
+  for (int u = 0; u < T::R; ++u) dec_fetch<T>(ring1[u], p, wrow, swrow, kb0 + T::R + u, tid, u);
   v4f acc[T::MT];
 #pragma unroll
   for (int i = 0; i < T::MT; ++i) acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
   uint8_t* const buf0 = lds;
   uint8_t* const buf1 = lds + T::R * T::STAGE;
-  auto round = [&](DecSlot<T>(&ring)[T::R], float& sa, uint8_t* buf, int refill_kb) {
+  auto round = [&](DecSlot<T, F>(&ring)[T::R], float& sa, uint8_t* buf, int refill_kb) {
+    if constexpr (F) {
 #pragma unroll
-    for (int u = 0; u < T::R; ++u) dec_stage<T>(buf + u * T::STAGE, ring[u], tid);
-    if (tid / T::MPA < T::R)
-      reinterpret_cast<float*>(buf + (tid / T::MPA) * T::STAGE + T::SA_OFF)[tid % T::MPA] = sa;
+      for (int u = 0; u < T::R; ++u) dec_stage<T>(buf + u * T::STAGE, ring[u], tid, u, p.M, p.pow2);
+    } else {
+#pragma unroll
+      for (int u = 0; u < T::R; ++u) dec_stage<T>(buf + u * T::STAGE, ring[u], tid);
+      if (tid / T::MPA < T::R)
+        reinterpret_cast<float*>(buf + (tid / T::MPA) * T::STAGE + T::SA_OFF)[tid % T::MPA] = sa;
+    }
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < T::R; ++u) dec_mma<T, ACC>(buf + u * T::STAGE, ring[u], lane, acc);
     // refill only once consumed, so each set keeps its registers across the loop
     if (refill_kb >= 0) {
-      sa = dec_fetch_sa<T>(p, refill_kb, tid);
+      if constexpr (!F) sa = dec_fetch_sa<T>(p, refill_kb, tid);
 #pragma unroll
-      for (int u = 0; u < T::R; ++u) dec_fetch<T>(ring[u], p, wrow, swrow, refill_kb + u, tid);
+      for (int u = 0; u < T::R; ++u) dec_fetch<T>(ring[u], p, wrow, swrow, refill_kb + u, tid, u);
     }
   };
   for (int k0 = 0; k0 < L - 2 * T::R; k0 += 2 * T::R) {
@@ -1223,25 +1283,29 @@ static hipError_t launch_big(const GemmArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <class T, int ACC>
+template <class T, int ACC, bool F>
 static hipError_t launch_decode_t(const GemmArgs& a, const GemmPlan& pl, hipStream_t stream) {
-  hipLaunchKernelGGL((gemm_decode_kernel<T, ACC>), dim3((unsigned)(a.N / T::BN), (unsigned)pl.splits),
-                     dim3(T::NT), 0, stream, a);
+  hipLaunchKernelGGL((gemm_decode_kernel<T, ACC, F>),
+                     dim3((unsigned)(a.N / T::BN), (unsigned)pl.splits), dim3(T::NT), 0, stream, a);
   return hipGetLastError();
 }
 
-template <int R, int ACC>
+template <int R, int ACC, bool F>
 static hipError_t launch_decode_d(const GemmArgs& a, const GemmPlan& pl, hipStream_t stream) {
-  if (a.M <= 16) return launch_decode_t<Dec<1, R>, ACC>(a, pl, stream);
-  if (a.M <= 32) return launch_decode_t<Dec<2, R>, ACC>(a, pl, stream);
-  return launch_decode_t<Dec<4, R>, ACC>(a, pl, stream);
+  if (a.M <= 16) return launch_decode_t<Dec<1, R>, ACC, F>(a, pl, stream);
+  if (a.M <= 32) return launch_decode_t<Dec<2, R>, ACC, F>(a, pl, stream);
+  return launch_decode_t<Dec<4, R>, ACC, F>(a, pl, stream);
 }
 
-template <int ACC>
+template <int ACC, bool F = false>
 static hipError_t launch_decode(const GemmArgs& a, const GemmPlan& pl, hipStream_t stream) {
-  if (pl.depth == 8) return launch_decode_d<4, ACC>(a, pl, stream);
-  if (pl.depth == 4) return launch_decode_d<2, ACC>(a, pl, stream);
-  return launch_decode_d<1, ACC>(a, pl, stream);
+  // the fused form's register ring holds bf16 activations, twice the bytes of codes: above 32
+  // rows it keeps at most 4 slices in flight, so that two waves per SIMD still fit (the split
+  // lengths stay multiples of the smaller depth, as depths are powers of two)
+  const int depth = F && a.M > 32 && pl.depth > 4 ? 4 : pl.depth;
+  if (depth == 8) return launch_decode_d<4, ACC, F>(a, pl, stream);
+  if (depth == 4) return launch_decode_d<2, ACC, F>(a, pl, stream);
+  return launch_decode_d<1, ACC, F>(a, pl, stream);
 }
 
 template <class T, bool PRECISE>
@@ -1328,6 +1392,36 @@ hipError_t launch_gemm(const uint8_t* xq, const float* sa, const uint8_t* wq, co
   hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((total4 + 255) / 256)), dim3(256), 0,
                      stream, a.ws, pl.splits, M, (int)N, y, ld_y, out_f32);
   return hipGetLastError();
+}
+
+bool plan_fuses_act(const GemmPlan& pl) { return pl.cfg == kCfgDecode; }
+
+hipError_t launch_gemm_fused_act(const uint16_t* x, int64_t ld_x, int pow2, const uint8_t* wq,
+                                 const float* sw, int64_t M, int64_t N, int64_t K, void* y,
+                                 int out_f32, int64_t ld_y, int accum, void* workspace,
+                                 const GemmPlan& pl, hipStream_t stream) {
+  if (!plan_fuses_act(pl)) return hipErrorInvalidValue;
+  GemmArgs a{};
+  a.x = x;
+  a.ld_x = ld_x;
+  a.pow2 = pow2;
+  a.wq = wq;
+  a.sw = sw;
+  a.M = (int)M;
+  a.N = (int)N;
+  a.K = (int)K;
+  a.KB = (int)(K / 128);
+  a.y = y;
+  a.ldy = ld_y;
+  a.out_f32 = out_f32;
+  a.counters = pl.workspace_bytes > 0 ? reinterpret_cast<int*>(workspace) : nullptr;
+  a.ws = pl.workspace_bytes > 0
+             ? reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + kWsHeaderBytes)
+             : nullptr;
+  a.splits = pl.splits;
+  a.kb_per_split = pl.kb_per_split;
+  if (accum == 1) return launch_decode<1, true>(a, pl, stream);
+  return accum == 2 ? launch_decode<2, true>(a, pl, stream) : launch_decode<0, true>(a, pl, stream);
 }
 
 hipError_t launch_grouped_gemm(const uint8_t* xq, const float* sa, const uint8_t* wq,

@@ -103,6 +103,14 @@ hipError_t launch_gemm(const uint8_t* xq, const float* sa, const uint8_t* wq, co
                        int64_t M, int64_t N, int64_t K, void* y, int out_f32, int64_t ld_y,
                        int accum, int rowb, void* workspace, const GemmPlan& plan,
                        hipStream_t stream);
+// The decode GEMM (M <= 64) with the 1x128 activation quantization fused into its staging: bf16
+// X [M][ld_x] in place of xq / sa (pow2: scale format of the groups). Only for plans with
+// plan_fuses_act(plan); the workspace is the dense GEMM's for the same shape.
+bool plan_fuses_act(const GemmPlan& plan);
+hipError_t launch_gemm_fused_act(const uint16_t* x, int64_t ld_x, int pow2, const uint8_t* wq,
+                                 const float* sw, int64_t M, int64_t N, int64_t K, void* y,
+                                 int out_f32, int64_t ld_y, int accum, void* workspace,
+                                 const GemmPlan& plan, hipStream_t stream);
 hipError_t launch_grouped_gemm(const uint8_t* xq, const float* sa, const uint8_t* wq,
                                const float* sw, const int32_t* offsets, int32_t E,
                                int64_t M_total, int64_t N, int64_t K, void* y, int out_f32,

@@ -71,7 +71,12 @@ typedef enum {
 
 typedef enum { FP8RL_OUT_BF16 = 0, FP8RL_OUT_F32 = 1 } fp8rl_out_dtype;
 
-typedef enum { FP8RL_OP_GEMM = 0, FP8RL_OP_GROUPED_GEMM = 1, FP8RL_OP_GEMM_ROWSCALED = 2 } fp8rl_op;
+typedef enum {
+  FP8RL_OP_GEMM = 0,
+  FP8RL_OP_GROUPED_GEMM = 1,
+  FP8RL_OP_GEMM_ROWSCALED = 2,
+  FP8RL_OP_GEMM_FUSED_ACT = 3
+} fp8rl_op;
 
 /*
  * How the matrix cores form the sum over one 128-wide K slice (the per-slice scaling, the float32
@@ -249,6 +254,29 @@ int fp8rl_gemm_w8a8_blockscaled(const uint8_t* xq, const float* sa, const uint8_
                                 const float* sw, int64_t M, int64_t N, int64_t K, void* y,
                                 int y_dtype, int64_t ld_y, int accum, void* workspace,
                                 size_t workspace_bytes, void* stream);
+
+/*
+ * The blockwise-scaled GEMM with the activation quantization fused in, for small token counts
+ * (decode: M <= 64). [NEMO, speed-up discussion of the Llama 3 8B results: the quantization
+ * kernels placed before each linear are overhead, and fusing them is expected to raise the gain
+ * further; UFP8, limitations paragraph: at the small batches of RL the extra quantize steps
+ * leave the GPU under-fed.] The result is bit for bit that of fp8rl_quant_act_tok128_ex(x,
+ * scale_fmt) followed by fp8rl_gemm_w8a8_blockscaled on its codes and scales: each workgroup
+ * quantizes the 1x128 groups of the K range it multiplies as it stages them, so the FP8
+ * activations never go to memory and one launch replaces two.
+ *   x      : bf16 activations X, M rows of pitch ld_x (>= K; ld_x * 2 a multiple of 16)
+ *   wq, sw, y, ld_y, accum : as for fp8rl_gemm_w8a8_blockscaled
+ *   scale_fmt : FP8RL_SCALE_FP32 or FP8RL_SCALE_POW2, the activation groups' scale format;
+ *            FP8RL_ACCUM_MX requires FP8RL_SCALE_POW2 (and power-of-two weight scales)
+ *   workspace, workspace_bytes: at least fp8rl_workspace_bytes(FP8RL_OP_GEMM_FUSED_ACT, M, N, K,
+ *            0) bytes, same rules as the dense GEMM's workspace
+ * Requires N % 128 == 0, K % 128 == 0, 1 <= M <= 64 and K/128 even (the decode tiling);
+ * FP8RL_ERR_SHAPE otherwise (M == 0 returns FP8RL_OK). Deterministic.
+ */
+int fp8rl_gemm_w8a8_fused_act_quant(const uint16_t* x, int64_t ld_x, const uint8_t* wq,
+                                    const float* sw, int64_t M, int64_t N, int64_t K, void* y,
+                                    int y_dtype, int64_t ld_y, int accum, int scale_fmt,
+                                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Row-scaled FP8 GEMM (the weight-gradient product of the backward pass: both operands quantized

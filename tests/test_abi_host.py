@@ -32,7 +32,7 @@ def L():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 20
+    assert len(names) == 21
     for n in names:
         assert hasattr(L, n), n
     assert sorted(_lib.EXPORTED) == names
@@ -210,6 +210,36 @@ def test_gemm_validation(L):
     assert need > 0  # a decode-shaped problem uses split-K partials
     assert call(K=4096, wsb=need - 1) == EWS
     assert call(K=4096, ws=None) == EWS
+
+
+def test_fused_act_gemm_validation(L):
+    f = L.fp8rl_gemm_w8a8_fused_act_quant
+    args = lambda **k: dict(dict(x=A, ldx=4096, wq=A, sw=A, M=64, N=256, K=4096, y=A, dt=0,
+                                 ldy=256, acc=0, sf=0, ws=A, wsb=1 << 30), **k)
+
+    def call(**k):
+        a = args(**k)
+        return f(a["x"], a["ldx"], a["wq"], a["sw"], a["M"], a["N"], a["K"], a["y"], a["dt"],
+                 a["ldy"], a["acc"], a["sf"], a["ws"], a["wsb"], None)
+
+    assert call(M=0, x=None) == OK
+    assert call(x=None) == ENULL
+    assert call(sw=None) == ENULL
+    assert call(N=200) == ESHAPE
+    assert call(ldx=4000) == ESHAPE  # pitch below K
+    assert call(M=65) == ESHAPE  # decode shapes only
+    assert call(K=384, ldx=384) == ESHAPE  # odd number of K slices
+    assert call(dt=2) == EDTYPE
+    assert call(acc=3) == EARG
+    assert call(sf=2) == EARG
+    assert call(acc=2, sf=0) == EARG  # matrix-core scaling needs power-of-two scales
+    assert call(x=A + 2) == EALIGN
+    assert call(ldx=4100) == EALIGN  # 8200-byte bf16 pitch
+    need = L.fp8rl_workspace_bytes(3, 64, 256, 4096, 0)
+    assert need == L.fp8rl_workspace_bytes(0, 64, 256, 4096, 0) > 0
+    assert call(wsb=need - 1) == EWS
+    assert call(ws=None) == EWS
+    assert L.fp8rl_workspace_bytes(3, 65, 256, 4096, 0) == 0  # not a fused shape
 
 
 def test_grouped_gemm_validation(L):
