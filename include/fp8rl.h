@@ -10,7 +10,9 @@
  *      per 1x128 group                         (fp8rl_quant_act_tok128);
  *   3. the blockwise-scaled FP8 GEMM Y = X W^T that consumes both
  *                                             (fp8rl_gemm_w8a8_blockscaled),
- *      and its mixture-of-experts grouped form (fp8rl_grouped_gemm_w8a8);
+ *      and its mixture-of-experts grouped form (fp8rl_grouped_gemm_w8a8), and for decode
+ *      shapes a form that takes bf16 activations and quantizes them inside the GEMM
+ *      (fp8rl_gemm_w8a8_fused_act_quant);
  *   plus the element-wise E4M3 encoder the quantizers share (fp8rl_encode_e4m3_f32), and the
  *   per-tensor FP8 of attention Q/K/V activations and the KV cache with per-step recalibrated
  *   scales (fp8rl_amax_bf16, fp8rl_scale_from_amax, fp8rl_quant_bf16_per_tensor and their
