@@ -81,20 +81,20 @@ int check_weight(const fp8rl_weight_desc& d) {
 int launch_weights(const fp8rl_weight_desc* descs, int32_t count, int pow2, hipStream_t stream) {
   fp8rl::WeightBatch b{};
   b.pow2 = pow2;
-  int64_t blocks = 0;
+  int64_t strips = 0;
   auto flush = [&]() -> int {
     if (b.count == 0) return FP8RL_OK;
-    hipError_t e = fp8rl::launch_quant_weight_batch(b, (int)blocks, stream);
+    hipError_t e = fp8rl::launch_quant_weight_batch(b, (int)strips, stream);
     b = fp8rl::WeightBatch{};
     b.pow2 = pow2;
-    blocks = 0;
+    strips = 0;
     return hip_status(e);
   };
   for (int32_t i = 0; i < count; ++i) {
     const fp8rl_weight_desc& d = descs[i];
     if (d.N == 0 || d.K == 0) continue;
-    const int64_t nb = (d.N / 128) * (d.K / 128);
-    if (b.count == fp8rl::kWeightBatch || blocks + nb >= (int64_t{1} << 24))
+    const int64_t nb = (d.N / 128) * ((d.K / 128 + 1) / 2);  // workgroups: 128x256 strips
+    if (b.count == fp8rl::kWeightBatch || strips + nb >= (int64_t{1} << 24))
       if (int s = flush()) return s;
     b.w[b.count] = d.w;
     b.wq[b.count] = d.wq;
@@ -102,9 +102,9 @@ int launch_weights(const fp8rl_weight_desc* descs, int32_t count, int pow2, hipS
     b.ld_w[b.count] = d.ld_w;
     b.ld_wq[b.count] = d.ld_wq;
     b.kb[b.count] = (int)(d.K / 128);
-    b.block_begin[b.count] = (int)blocks;
+    b.block_begin[b.count] = (int)strips;
     ++b.count;
-    blocks += nb;
+    strips += nb;
   }
   return flush();
 }

@@ -17,11 +17,11 @@ struct WeightBatch {
   int64_t ld_w[kWeightBatch];
   int64_t ld_wq[kWeightBatch];
   int kb[kWeightBatch];
-  int block_begin[kWeightBatch];  // first grid block of matrix i (prefix sum of block counts)
+  int block_begin[kWeightBatch];  // first workgroup of matrix i (prefix sum of its 128x256 strips)
   int count;
   int pow2;  // power-of-two scales instead of fp32(amax / 448)
 };
-hipError_t launch_quant_weight_batch(const WeightBatch& b, int total_blocks, hipStream_t stream);
+hipError_t launch_quant_weight_batch(const WeightBatch& b, int total_strips, hipStream_t stream);
 hipError_t launch_quant_act(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x, uint8_t* xq,
                             int64_t ld_xq, float* sa, int pow2, hipStream_t stream);
 hipError_t launch_encode(const float* v, int64_t n, uint8_t* out, hipStream_t stream);

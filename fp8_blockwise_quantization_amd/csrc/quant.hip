@@ -13,50 +13,65 @@
 namespace fp8rl {
 
 // ---------------------------------------------------------------------------------------------
-// Weights: one workgroup (4 waves) per 128x128 block. Thread t owns the 16-byte column chunk
-// (t & 15) of rows (t >> 4) + 16 i, i = 0..7, so each load instruction of a wave reads four
-// 256-byte row segments and the block (32 KiB of bf16) lives in registers between the amax pass
-// and the encode pass: HBM traffic is one read of W and one write of Wq.
+// Weights: one workgroup (4 waves) per pair of horizontally adjacent 128x128 blocks, a 128x256
+// strip of W (the last strip of a block row is a single block when K/128 is odd). Thread t owns
+// the 16-byte column chunk c = t & 31 of rows (t >> 5) + 8 i, i = 0..15, so each load
+// instruction of a wave reads two 512-byte row segments; chunks c < 16 lie in the left block,
+// the others in the right one. Both blocks (64 KiB of bf16) stay in registers between the amax
+// pass and the encode pass: HBM traffic is one read of W and one write of Wq. Whole 512-byte
+// row segments stream about 5 % faster than the 256-byte segments of one block.
 //
 // One launch covers a batch of up to kWeightBatch matrices (a whole layer or model): the grid
-// is the concatenation of every matrix's blocks, and each workgroup finds its matrix from the
-// block prefix sums passed by value.
+// is the concatenation of every matrix's strips, and each workgroup finds its matrix from the
+// strip prefix sums passed by value.
 // ---------------------------------------------------------------------------------------------
-__device__ __forceinline__ void quant_weight_block(const uint16_t* __restrict__ w, int64_t ld_w,
-                                                   uint8_t* __restrict__ wq, int64_t ld_wq,
-                                                   float* __restrict__ sw_out, int bi, int bj,
-                                                   int pow2) {
+__device__ __forceinline__ void quant_weight_pair(const uint16_t* __restrict__ w, int64_t ld_w,
+                                                  uint8_t* __restrict__ wq, int64_t ld_wq,
+                                                  float* __restrict__ sw_row, int bi, int bp,
+                                                  int KB, int pow2) {
   const int t = threadIdx.x;
-  const int c = t & 15;
-  const int r0 = t >> 4;
+  const int c = t & 31, r0 = t >> 5;
+  const int hb = c >> 4;               // 0: left block, 1: right block
+  const int bj = 2 * bp + hb;          // this lane's block column
+  const bool live = bj < KB;           // false only in the missing right block of an odd row
 
-  const uint16_t* src = w + (int64_t)(bi * kBlock + r0) * ld_w + bj * kBlock + c * 8;
-  u32x4 v[8];
+  const uint16_t* src = w + (int64_t)(bi * kBlock + r0) * ld_w + bp * (2 * kBlock) + c * 8;
+  u32x4 v[16];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-    v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + (int64_t)(16 * i) * ld_w));
+  for (int i = 0; i < 16; ++i) {
+    v[i] = u32x4{0u, 0u, 0u, 0u};
+    if (live)
+      v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + (int64_t)(8 * i) * ld_w));
+  }
 
+  // lane l of wave q holds row 2q + (l >> 5) of block (l >> 4) & 1: a DPP row (16 lanes) is one
+  // block's 256-byte segment of one row, and lanes l and l ^ 32 belong to the same block
   uint32_t m = 0;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) m = pk_max_u16(m, amax8_pk(v[i]));
-  m = wave_max_u32(hmax_u16(m));
+  for (int i = 0; i < 16; ++i) m = pk_max_u16(m, amax8_pk(v[i]));
+  m = row16_max_u32(hmax_u16(m));
+  const uint32_t o = (uint32_t)__shfl_xor((int)m, 32, 64);
+  m = m > o ? m : o;
 
-  __shared__ uint32_t red[4];
-  if ((t & 63) == 0) red[t >> 6] = m;
+  __shared__ uint32_t red[2][4];
+  const int lane = t & 63, wv = t >> 6;
+  if (lane == 0) red[0][wv] = m;
+  if (lane == 16) red[1][wv] = m;
   __syncthreads();
-  m = red[0];
-  m = m > red[1] ? m : red[1];
-  m = m > red[2] ? m : red[2];
-  m = m > red[3] ? m : red[3];
+  m = red[hb][0];
+  m = m > red[hb][1] ? m : red[hb][1];
+  m = m > red[hb][2] ? m : red[hb][2];
+  m = m > red[hb][3] ? m : red[hb][3];
+  if (!live) return;
 
   const float S = pow2 ? pow2_scale_from_amax_bits(m) : scale_from_amax_bits(m);
   const double r = recip_f64(S);
-  if (t == 0) *sw_out = S;
+  if (t == 0 || t == 16) sw_row[bj] = S;
 
-  uint8_t* dst = wq + (int64_t)(bi * kBlock + r0) * ld_wq + bj * kBlock + c * 8;
+  uint8_t* dst = wq + (int64_t)(bi * kBlock + r0) * ld_wq + bp * (2 * kBlock) + c * 8;
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-    __builtin_nontemporal_store(quant8(v[i], r), reinterpret_cast<u32x2*>(dst + (int64_t)(16 * i) * ld_wq));
+  for (int i = 0; i < 16; ++i)
+    __builtin_nontemporal_store(quant8(v[i], r), reinterpret_cast<u32x2*>(dst + (int64_t)(8 * i) * ld_wq));
 }
 
 __global__ __launch_bounds__(256) void quant_weight_blk128_kernel(WeightBatch b) {
@@ -66,8 +81,10 @@ __global__ __launch_bounds__(256) void quant_weight_blk128_kernel(WeightBatch b)
   while (t + 1 < b.count && bid >= b.block_begin[t + 1]) ++t;  // uniform: bid is uniform
   const int local = bid - b.block_begin[t];
   const int KB = b.kb[t];
-  const int bi = local / KB, bj = local - (local / KB) * KB;
-  quant_weight_block(b.w[t], b.ld_w[t], b.wq[t], b.ld_wq[t], b.sw[t] + local, bi, bj, b.pow2);
+  const int KP = (KB + 1) >> 1;  // strips per block row
+  const int bi = local / KP, bp = local - (local / KP) * KP;
+  quant_weight_pair(b.w[t], b.ld_w[t], b.wq[t], b.ld_wq[t], b.sw[t] + (int64_t)bi * KB, bi, bp,
+                    KB, b.pow2);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -152,8 +169,8 @@ __global__ __launch_bounds__(256) void encode_e4m3_kernel(const float* __restric
 // ---------------------------------------------------------------------------------------------
 // Launchers (arguments already validated by the C ABI layer).
 // ---------------------------------------------------------------------------------------------
-hipError_t launch_quant_weight_batch(const WeightBatch& b, int total_blocks, hipStream_t stream) {
-  hipLaunchKernelGGL(quant_weight_blk128_kernel, dim3((unsigned)total_blocks), dim3(256), 0, stream,
+hipError_t launch_quant_weight_batch(const WeightBatch& b, int total_strips, hipStream_t stream) {
+  hipLaunchKernelGGL(quant_weight_blk128_kernel, dim3((unsigned)total_strips), dim3(256), 0, stream,
                      b);
   return hipGetLastError();
 }
