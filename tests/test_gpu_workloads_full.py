@@ -4,6 +4,10 @@
   the batched entry point in 7 launches of 32 matrices, exactly as the benchmark runs it. Layers
   0, 15 and 31 are checked whole against the oracle; every other matrix on three sampled 128x128
   blocks (first, last and a seeded one). Codes and scales bit-exact.
+* Qwen3-30B-A3B expert weights (128 experts, gate/up [1536][2048] and down [2048][768]) re-quantized
+  as the benchmark does it: each [E][N][K] tensor as one [E*N][K] matrix (its 128x128 blocks never
+  straddle experts), both in one batched launch; six experts of each checked whole against the
+  oracle run on that expert alone.
 * The decoder-block GEMMs in the serving layout (q/k/v and gate/up weights concatenated along N):
   Qwen3-8B decode (M = 64) checked whole, Qwen3-8B prefill (M = 8192) and the Llama-3.1-8B MLP
   (M = 256 whole, M = 4096 on sampled rows). Operands are quantized by the oracle from the seeded
@@ -58,6 +62,26 @@ def test_llama31_8b_weight_sync_32_layers():
             assert np.array_equal(got_s.view(np.uint32), rs.view(np.uint32)), (i, bi, bj)
             assert np.array_equal(wqs[i][rows, cols].cpu().numpy(), rq), (i, bi, bj)
     print("    layers 0, 15, 31 whole; 3 blocks of every other matrix", flush=True)
+
+
+def test_qwen3_30b_a3b_expert_requant_one_launch():
+    E, H, I = 128, 2048, 768
+    print(f"[expert requant] E={E} gate/up [{2 * I}][{H}], down [{H}][{I}]", flush=True)
+    w1 = synth.weight_bf16(2 * I, H, seed=43, batch=E, device="cuda")
+    w2 = synth.weight_bf16(H, I, seed=44, batch=E, device="cuda")
+    wq1 = torch.empty((E, 2 * I, H), dtype=torch.uint8, device="cuda")
+    sw1 = torch.empty((E, 2 * I // 128, H // 128), dtype=torch.float32, device="cuda")
+    wq2 = torch.empty((E, H, I), dtype=torch.uint8, device="cuda")
+    sw2 = torch.empty((E, H // 128, I // 128), dtype=torch.float32, device="cuda")
+    fq.quant_weights([w1.view(E * 2 * I, H), w2.view(E * H, I)],
+                     [wq1.view(E * 2 * I, H), wq2.view(E * H, I)],
+                     [sw1.view(E * 2 * I // 128, H // 128), sw2.view(E * H // 128, I // 128)])
+    torch.cuda.synchronize()
+    for w, wq, sw in ((w1, wq1, sw1), (w2, wq2, sw2)):
+        for e in (0, 1, 63, 64, 100, 127):
+            rq, rs = oq.quant_weight_blk128(bits16(w[e]))
+            assert np.array_equal(sw[e].cpu().numpy().view(np.uint32), rs.view(np.uint32)), e
+            assert np.array_equal(wq[e].cpu().numpy(), rq), e
 
 
 def _operands(M, N, K, seed):
