@@ -13,13 +13,15 @@
 namespace fp8rl {
 
 // ---------------------------------------------------------------------------------------------
-// Weights: one workgroup (4 waves) per pair of horizontally adjacent 128x128 blocks, a 128x256
+// Weights: one workgroup (8 waves) per pair of horizontally adjacent 128x128 blocks, a 128x256
 // strip of W (the last strip of a block row is a single block when K/128 is odd). Thread t owns
-// the 16-byte column chunk c = t & 31 of rows (t >> 5) + 8 i, i = 0..15, so each load
+// the 16-byte column chunk c = t & 31 of rows (t >> 5) + 16 i, i = 0..7, so each load
 // instruction of a wave reads two 512-byte row segments; chunks c < 16 lie in the left block,
-// the others in the right one. Both blocks (64 KiB of bf16) stay in registers between the amax
-// pass and the encode pass: HBM traffic is one read of W and one write of Wq. Whole 512-byte
-// row segments stream about 5 % faster than the 256-byte segments of one block.
+// the others in the right one. The strip (64 KiB of bf16) stays in registers between the amax
+// pass and the encode pass: HBM traffic is one read of W and one write of Wq. Measured on the
+// Qwen3-8B block's 7 weights: whole 512-byte row segments stream faster than one block's 256-byte
+// ones, and 8 waves per strip (8 loads per thread) beat 4 (16 loads, fewer resident waves) and
+// 16 (4 loads, more barrier and reduction work per byte).
 //
 // One launch covers a batch of up to kWeightBatch matrices (a whole layer or model): the grid
 // is the concatenation of every matrix's strips, and each workgroup finds its matrix from the
@@ -30,38 +32,37 @@ __device__ __forceinline__ void quant_weight_pair(const uint16_t* __restrict__ w
                                                   float* __restrict__ sw_row, int bi, int bp,
                                                   int KB, int pow2) {
   const int t = threadIdx.x;
-  const int c = t & 31, r0 = t >> 5;
+  const int c = t & 31, r0 = t >> 5;  // r0 < 16
   const int hb = c >> 4;               // 0: left block, 1: right block
   const int bj = 2 * bp + hb;          // this lane's block column
   const bool live = bj < KB;           // false only in the missing right block of an odd row
 
   const uint16_t* src = w + (int64_t)(bi * kBlock + r0) * ld_w + bp * (2 * kBlock) + c * 8;
-  u32x4 v[16];
+  u32x4 v[8];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
+  for (int i = 0; i < 8; ++i) {
     v[i] = u32x4{0u, 0u, 0u, 0u};
     if (live)
-      v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + (int64_t)(8 * i) * ld_w));
+      v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + (int64_t)(16 * i) * ld_w));
   }
 
   // lane l of wave q holds row 2q + (l >> 5) of block (l >> 4) & 1: a DPP row (16 lanes) is one
   // block's 256-byte segment of one row, and lanes l and l ^ 32 belong to the same block
   uint32_t m = 0;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) m = pk_max_u16(m, amax8_pk(v[i]));
+  for (int i = 0; i < 8; ++i) m = pk_max_u16(m, amax8_pk(v[i]));
   m = row16_max_u32(hmax_u16(m));
   const uint32_t o = (uint32_t)__shfl_xor((int)m, 32, 64);
   m = m > o ? m : o;
 
-  __shared__ uint32_t red[2][4];
+  __shared__ uint32_t red[2][8];
   const int lane = t & 63, wv = t >> 6;
   if (lane == 0) red[0][wv] = m;
   if (lane == 16) red[1][wv] = m;
   __syncthreads();
   m = red[hb][0];
-  m = m > red[hb][1] ? m : red[hb][1];
-  m = m > red[hb][2] ? m : red[hb][2];
-  m = m > red[hb][3] ? m : red[hb][3];
+#pragma unroll
+  for (int k = 1; k < 8; ++k) m = m > red[hb][k] ? m : red[hb][k];
   if (!live) return;
 
   const float S = pow2 ? pow2_scale_from_amax_bits(m) : scale_from_amax_bits(m);
@@ -70,11 +71,11 @@ __device__ __forceinline__ void quant_weight_pair(const uint16_t* __restrict__ w
 
   uint8_t* dst = wq + (int64_t)(bi * kBlock + r0) * ld_wq + bp * (2 * kBlock) + c * 8;
 #pragma unroll
-  for (int i = 0; i < 16; ++i)
-    __builtin_nontemporal_store(quant8(v[i], r), reinterpret_cast<u32x2*>(dst + (int64_t)(8 * i) * ld_wq));
+  for (int i = 0; i < 8; ++i)
+    __builtin_nontemporal_store(quant8(v[i], r), reinterpret_cast<u32x2*>(dst + (int64_t)(16 * i) * ld_wq));
 }
 
-__global__ __launch_bounds__(256) void quant_weight_blk128_kernel(WeightBatch b) {
+__global__ __launch_bounds__(512) void quant_weight_blk128_kernel(WeightBatch b) {
   const int bid = blockIdx.x;
   int t = 0;
 #pragma unroll 1
@@ -170,7 +171,7 @@ __global__ __launch_bounds__(256) void encode_e4m3_kernel(const float* __restric
 // Launchers (arguments already validated by the C ABI layer).
 // ---------------------------------------------------------------------------------------------
 hipError_t launch_quant_weight_batch(const WeightBatch& b, int total_strips, hipStream_t stream) {
-  hipLaunchKernelGGL(quant_weight_blk128_kernel, dim3((unsigned)total_strips), dim3(256), 0, stream,
+  hipLaunchKernelGGL(quant_weight_blk128_kernel, dim3((unsigned)total_strips), dim3(512), 0, stream,
                      b);
   return hipGetLastError();
 }
