@@ -92,12 +92,18 @@ def test_strided_rows_and_canaries():
     w_full = synth.weight_bf16(N, K + pad, seed=91)
     w = w_full[:, :K].cuda()  # pitch K + pad
     wq_full = torch.full((N, K + 32), 0xA5, dtype=torch.uint8, device="cuda")
-    sw = torch.empty((N // 128, K // 128), dtype=torch.float32, device="cuda")
+    # K / 128 = 3 is odd: the last 128x256 strip of each block row holds one block; the scales
+    # are followed by canaries that no missing right block may touch
+    nsw = (N // 128) * (K // 128)
+    sw_full = torch.full((nsw + 8,), -7.0, dtype=torch.float32, device="cuda")
+    sw = sw_full[:nsw].view(N // 128, K // 128)
     fq.quant_weight(w, wq_full[:, :K], sw)
     torch.cuda.synchronize()
     assert torch.all(wq_full[:, K:] == 0xA5)
+    assert torch.all(sw_full[nsw:] == -7.0)
     rq, rs = oq.quant_weight_blk128(bits16(w_full[:, :K]))
     assert np.array_equal(wq_full[:, :K].cpu().numpy(), rq)
+    assert np.array_equal(sw.cpu().numpy().view(np.uint32), rs.view(np.uint32))
     x_full = synth.act_bf16(37, K + pad, seed=92)
     x = x_full[:, :K].cuda()
     xq_full = torch.full((37, K + 16), 0x5A, dtype=torch.uint8, device="cuda")
