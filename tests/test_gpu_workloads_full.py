@@ -14,6 +14,9 @@
   synthetic tensors; the GEMM runs through the same entry point and planner as the benchmark.
   Sampled rows: GEMM rows are independent, so the oracle computes just those rows of the product;
   rms(ref) in the bf16 tolerance is taken over the sampled rows.
+* The FP8 backward of the Qwen3-8B gate/up linear over 8192 tokens as the benchmark runs it: the
+  three quantizers bit-exact at full size, Dgrad (K = 24576) and Wgrad (contraction over the 8192
+  tokens, FP8 slice sums against their derived bound) on sampled output rows.
 """
 
 import numpy as np
@@ -21,9 +24,11 @@ import pytest
 import torch
 
 import fp8_blockwise_quantization_amd as fq
+from oracle import backward as ob
 from oracle import gemm as og
 from oracle import quant as oq
-from tests.gpu_util import assert_gemm_close, bits16, gemm_out_to_f64, to_dev_f32, to_dev_u8
+from tests.gpu_util import (assert_gemm_close, assert_within, bits16, fp8_slice_bound,
+                            gemm_out_to_f64, to_dev_f32, to_dev_u8)
 from workloads import synth
 
 pytestmark = pytest.mark.gpu
@@ -146,3 +151,51 @@ def test_llama31_8b_mlp_m4096_sampled_rows(idx):
     name, N, K = LLAMA_MLP_GEMMS[idx]
     _check_gemm(4096, N, K, 5400 + idx, rows=_sample_rows(4096, 48, 5450 + idx),
                 what=f"llama-3.1-8b mlp M=4096 {name}")
+
+
+def test_qwen3_8b_gate_up_backward_8192_tokens():
+    T, N, K = 8192, 24576, 4096
+    print(f"[backward full size] gate/up {N}x{K} over {T} tokens", flush=True)
+    dy = synth.act_bf16(T, N, seed=synth.seed_of(46, 0)) * 0.01
+    x = synth.act_bf16(T, K, seed=synth.seed_of(46, 1))
+    w = synth.weight_bf16(N, K, seed=synth.seed_of(46, 2), outlier_frac=0.001)
+    dyt, s_dyt, dyq, s_dy = fq.quant_colwise(dy.cuda(), rowwise=True)
+    xt, s_xt, _, _ = fq.quant_colwise(x.cuda())
+    wqt, swt, _, _ = fq.quant_weight_t(w.cuda())
+    dx = fq.gemm(dyq, s_dy, wqt, swt)  # Dgrad: [T][K], contraction over N
+    dw = fq.gemm_rowscaled(dyt, s_dyt, xt, s_xt)  # Wgrad: [N][K], contraction over T
+    torch.cuda.synchronize()
+
+    def same(got, ref, what):
+        got = got.cpu().numpy()
+        if got.dtype == np.float32:
+            assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), what
+        else:
+            assert int(np.count_nonzero(got != ref)) == 0, what
+
+    r_dyq, r_sdy = oq.quant_act_tok128(bits16(dy))
+    same(dyq, r_dyq, "dY codes (1x128)")
+    same(s_dy, r_sdy, "dY scales (1x128)")
+    r_dyt, r_sdyt = ob.quant_colwise128(bits16(dy))
+    same(dyt, r_dyt, "dY codes (128x1, transposed)")
+    same(s_dyt, r_sdyt, "dY scales (128x1)")
+    r_xt, r_sxt = ob.quant_colwise128(bits16(x))
+    same(xt, r_xt, "X codes (128x1, transposed)")
+    same(s_xt, r_sxt, "X scales (128x1)")
+    r_wqt, r_swt = ob.quant_weight_blk128_t(bits16(w))
+    same(wqt, r_wqt, "W^T codes")
+    same(swt, r_swt, "W^T scales")
+
+    rows = _sample_rows(T, 48, 5500)
+    ref64 = og.gemm_blockscaled(r_dyq[rows], r_sdy[rows], r_wqt, r_swt, out="f64")
+    ref = og.bf16_bits_to_f64(og.round_f64_to_bf16_bits(ref64))
+    got = gemm_out_to_f64(dx[torch.from_numpy(rows).cuda()])
+    print(f"    dX worst err/bound {assert_gemm_close(got, ref, ref64, 'bf16', 'dX'):.3f}", flush=True)
+
+    rows_w = _sample_rows(N, 48, 5501)
+    ref64w = ob.gemm_rowscaled(r_dyt[rows_w], r_sdyt[rows_w], r_xt, r_sxt, out="f64")
+    bound = (fp8_slice_bound(r_dyt[rows_w], r_sdyt[rows_w], r_xt, r_sxt, b_rows=True) +
+             2.0 ** -8 * np.abs(ref64w))
+    got_w = gemm_out_to_f64(dw[torch.from_numpy(rows_w).cuda()])
+    print(f"    dW worst err/bound {assert_within(got_w, ref64w, bound, 'dW fp8 slices'):.3f}",
+          flush=True)
