@@ -270,6 +270,65 @@ def measured_traffic():
         return None
 
 
+# --------------------------------------------------------------------------------- gpu clocks
+
+def gpu_clocks():
+    """Engine and memory clock tables of the visible GPUs from the driver's sysfs files (MHz; the
+    entry the driver marks current is reported as `*_now_mhz`), or None where they are not
+    readable. Sampled while timed work is still executing, the engine clock is the one it ran at."""
+    import glob
+
+    def table(path):
+        try:
+            with open(path) as f:
+                rows = [l.split() for l in f.read().strip().splitlines()]
+        except OSError:
+            return None, None
+        mhz, now = [], None
+        for r in rows:
+            if len(r) >= 2 and r[1].lower().endswith("mhz"):
+                v = int(r[1][:-3])
+                mhz.append(v)
+                if "*" in r[2:]:
+                    now = v
+        return mhz, now
+
+    out = []
+    for dev in sorted(glob.glob("/sys/class/drm/card*/device")):
+        sclk, sclk_now = table(dev + "/pp_dpm_sclk")
+        mclk, mclk_now = table(dev + "/pp_dpm_mclk")
+        if sclk is None and mclk is None:
+            continue
+        out.append({"card": dev.split("/")[-2], "sclk_levels_mhz": sclk, "sclk_now_mhz": sclk_now,
+                    "mclk_levels_mhz": mclk, "mclk_now_mhz": mclk_now})
+    return out or None
+
+
+def sample_clocks(done_event, period_s=0.002, max_samples=200):
+    """Engine clock of the first GPU sampled every `period_s` until `done_event` has completed:
+    min / median / max of the current level (MHz) and the number of samples, plus the tables."""
+    import time
+
+    first, now = None, []
+    while len(now) < max_samples:
+        c = gpu_clocks()
+        if not c:
+            return None
+        first = first or c
+        if c[0]["sclk_now_mhz"] is not None:
+            now.append(c[0]["sclk_now_mhz"])
+        if done_event.query():
+            break
+        time.sleep(period_s)
+    now.sort()
+    out = dict(first[0])
+    out.pop("sclk_now_mhz", None)
+    if now:
+        out.update(sclk_samples=len(now), sclk_min_mhz=now[0], sclk_median_mhz=now[len(now) // 2],
+                   sclk_max_mhz=now[-1])
+    return out
+
+
 # ------------------------------------------------------------------------------ cpu baseline
 
 
@@ -381,6 +440,7 @@ def main():
     for i in range(args.steps):
         blk.step(timed=True)
         marks[i + 1].record()
+    clocks = sample_clocks(marks[-1])  # the host is ahead of the GPU: the timed steps run
     torch.cuda.synchronize()
     ms = marks[0].elapsed_time(marks[-1]) / args.steps
     per_step = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps))
@@ -417,6 +477,13 @@ def main():
                 "algorithmic_flops_per_launch": 2 * M * gN * gK,
                 "per_unit": "2 flops per multiply-add: 2*M*N*K per GEMM",
                 "units_per_launch": f"{gname}: M={M}, N={gN}, K={gK}"}
+        # context, not the reported peak: the matrix cores' peak scales with the engine clock,
+        # which drops well below its top level under sustained FP8 matrix-core load
+        if clocks and clocks.get("sclk_median_mhz") and clocks.get("sclk_levels_mhz"):
+            top = max(clocks["sclk_levels_mhz"])
+            p_clk = FP8_PEAK_TFLOPS * clocks["sclk_median_mhz"] / top
+            roof.update(peak_at_median_sampled_sclk=p_clk, frac_at_median_sampled_sclk=tf / p_clk,
+                        sclk_rule=f"peak x median sampled engine clock / {top} MHz")
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline_dense(linears, M, seed=5000, budget_linears=7 if M <= 256 else 1,
@@ -431,7 +498,7 @@ def main():
         "config": cfg,
         "step_bytes": step_bytes, "step_gemm_flops": blk.flops,
         "parts": parts, "roofline": roof, "cpu_baseline": cpu, "gpu": dev_name,
-        "cus": props.multi_processor_count,
+        "cus": props.multi_processor_count, "clocks_during_timed_steps": clocks,
     }
     print(json.dumps(line), flush=True)
 
