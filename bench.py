@@ -275,7 +275,9 @@ def measured_traffic():
 def gpu_clocks():
     """Engine and memory clock tables of the visible GPUs from the driver's sysfs files (MHz; the
     entry the driver marks current is reported as `*_now_mhz`), or None where they are not
-    readable. Sampled while timed work is still executing, the engine clock is the one it ran at."""
+    readable. The current entry is the driver's report, not a cycle count: under a vendor FP8
+    GEMM it read a level at which that GEMM's throughput would exceed the matrix cores' peak, so
+    it is printed as context and used for nothing else."""
     import glob
 
     def table(path):
@@ -477,13 +479,7 @@ def main():
                 "algorithmic_flops_per_launch": 2 * M * gN * gK,
                 "per_unit": "2 flops per multiply-add: 2*M*N*K per GEMM",
                 "units_per_launch": f"{gname}: M={M}, N={gN}, K={gK}"}
-        # context, not the reported peak: the matrix cores' peak scales with the engine clock,
-        # which drops well below its top level under sustained FP8 matrix-core load
-        if clocks and clocks.get("sclk_median_mhz") and clocks.get("sclk_levels_mhz"):
-            top = max(clocks["sclk_levels_mhz"])
-            p_clk = FP8_PEAK_TFLOPS * clocks["sclk_median_mhz"] / top
-            roof.update(peak_at_median_sampled_sclk=p_clk, frac_at_median_sampled_sclk=tf / p_clk,
-                        sclk_rule=f"peak x median sampled engine clock / {top} MHz")
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline_dense(linears, M, seed=5000, budget_linears=7 if M <= 256 else 1,
