@@ -369,6 +369,7 @@ def cpu_baseline_dense(linears, M, seed, budget_linears, min_seconds=10.0, scale
         done.append(name)
         i += 1
     return dict(value=total_bytes / elapsed / 1e9, unit="GB/s", cores=int(blas_threads),
+                quantizer_threads=1, gemm_blas_threads=int(blas_threads),
                 host_cpus=os.cpu_count(), host_cpus_usable=len(os.sched_getaffinity(0)),
                 kind="oracle", seconds=elapsed,
                 sample=f"{len(done)} linears of the block at M={M} ({','.join(done)}): weight "
