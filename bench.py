@@ -248,16 +248,17 @@ class DenseBlock:
 # ---------------------------------------------------------------------------- measured traffic
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "quant_weight_blk128__qwen3-8b-decode-step.traffic.txt")
+PREFILL_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_big_kernel__qwen3-8b-prefill.traffic.txt")
 
 
-def measured_traffic():
-    """HBM bytes per launch of the weight re-quantization kernel from the committed FETCH_SIZE /
-    WRITE_SIZE counter runs (scaled by a 1 GiB copy), or None if the kernel's sources have changed
-    since the counters were taken."""
+def measured_traffic(path=TRAFFIC_FILE):
+    """HBM bytes per launch of a kernel from committed FETCH_SIZE / WRITE_SIZE counter runs
+    (scaled by a 1 GiB copy), or None if the kernel's sources have changed since the counters
+    were taken."""
     import hashlib
 
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             d = json.load(f)
         h = hashlib.sha256()
         for rel in d["source_files"]:
@@ -476,7 +477,9 @@ def main():
         tf = 2 * M * gN * gK / (g_us * 1e-6) / 1e12
         roof = {"kernel": "gemm_big_kernel", "bound": "mfma", "achieved": tf,
                 "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": tf / FP8_PEAK_TFLOPS,
-                "traffic": None, "avg_launch_us": g_us,
+                "traffic": measured_traffic(PREFILL_TRAFFIC_FILE)
+                if (M, gN, gK) == (8192, 24576, 4096) and args.scales == "fp32" else None,
+                "avg_launch_us": g_us,
                 "algorithmic_flops_per_launch": 2 * M * gN * gK,
                 "per_unit": "2 flops per multiply-add: 2*M*N*K per GEMM",
                 "units_per_launch": f"{gname}: M={M}, N={gN}, K={gK}"}
