@@ -19,8 +19,10 @@ Sources (the pages this follows, cited by title and section):
   blocks, input activations E4M3 with [1, 128] groups, FP32 block scales.
 
 Modules: ``e4m3`` (codec), ``quant`` (the two quantizers), ``gemm`` (dequantized fp64 GEMM and its
-grouped-expert form). Every function with no independent pin would say "parity unpinned"; none
-does at present (see the tests under ``tests/test_oracle_*.py``).
+grouped-expert form), ``backward`` (the FP8 input- and weight-gradient GEMMs and the quantizations
+they need) and ``kvcache`` (per-tensor Q/K/V scale recalibration and the FP8 KV-cache store).
+Every function with no independent pin would say "parity unpinned"; none does at present (see the
+tests under ``tests/test_oracle_*.py``).
 """
 
-from . import e4m3, gemm, quant  # noqa: F401
+from . import backward, e4m3, gemm, kvcache, quant  # noqa: F401
