@@ -34,6 +34,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import queue
 import sys
 import time
 
@@ -378,6 +379,100 @@ def cpu_baseline_dense(linears, M, seed, budget_linears, min_seconds=10.0, scale
                        f"numpy, GEMM fp64 BLAS; input generation not timed")
 
 
+def _quant_inputs(tensors):
+    """bf16 bit patterns (uint16 numpy) of the step's tensors, each ("w", name, N, K, seed, nbytes)
+    or ("x", name, M, K, seed, nbytes)."""
+    import numpy as np
+    import torch
+
+    from workloads import synth
+
+    out = []
+    for kind, _, R, K, seed, _ in tensors:
+        t = (synth.weight_bf16(R, K, seed=seed, outlier_frac=0.001) if kind == "w"
+             else synth.act_bf16(R, K, seed=seed))
+        out.append(t.view(torch.int16).numpy().view(np.uint16))
+    return out
+
+
+def _quantize(tensors, inputs, scales):
+    from oracle import quant as oq
+
+    for (kind, *_), t in zip(tensors, inputs):
+        if kind == "w":
+            oq.quant_weight_blk128(t, scale=scales)
+        else:
+            oq.quant_act_tok128(t, scale=scales)
+
+
+def _quant_worker(tensors, scales, barrier, results):
+    """One process of the all-cores run: make its share of the inputs, wait for every process,
+    quantize, report (start, end) on the system-wide monotonic clock."""
+    inputs = _quant_inputs(tensors)
+    barrier.wait(timeout=300)
+    t0 = time.monotonic()
+    _quantize(tensors, inputs, scales)
+    results.put((t0, time.monotonic()))
+
+
+def cpu_quantizers_all_cores(linears, M, seed, scales="fp32"):
+    """The oracle's two quantizers over one step's tensors (each linear's bf16 weight and its
+    [M][K] activations): first one tensor after another in this process, then the same tensors
+    partitioned over one process per usable core (at most one process per tensor, larger
+    tensors dealt out first to the least-loaded process). The processes are fresh interpreters
+    (spawn), so this must run before this process touches the GPU. Input generation is not
+    timed; the all-cores time runs from the first process's start to the last one's end."""
+    import multiprocessing as mp
+
+    tensors = []
+    for i, (name, N, K) in enumerate(linears):
+        tensors.append(("w", name, N, K, seed + i, w_bytes(N, K)))
+        tensors.append(("x", name, M, K, seed + 7 + i, a_bytes(M, K)))
+    total_bytes = sum(t[5] for t in tensors)
+
+    inputs = _quant_inputs(tensors)
+    t0 = time.perf_counter()
+    _quantize(tensors, inputs, scales)
+    t_one = time.perf_counter() - t0
+    del inputs
+
+    procs = max(1, min(len(os.sched_getaffinity(0)), len(tensors)))
+    shares, load = [[] for _ in range(procs)], [0] * procs
+    for t in sorted(tensors, key=lambda t: -t[5]):
+        j = load.index(min(load))
+        shares[j].append(t)
+        load[j] += t[5]
+    ctx = mp.get_context("spawn")
+    barrier, results = ctx.Barrier(procs), ctx.Queue()
+    ps = [ctx.Process(target=_quant_worker, args=(sh, scales, barrier, results)) for sh in shares]
+    for p in ps:
+        p.start()
+    spans, deadline = [], time.monotonic() + 600
+    try:
+        while len(spans) < procs:
+            try:
+                spans.append(results.get(timeout=1.0))
+            except queue.Empty:
+                # a process that ended without a result (an error) fails the run at once
+                if any(p.exitcode not in (None, 0) for p in ps) or time.monotonic() > deadline:
+                    raise RuntimeError("a process of the all-cores oracle run failed")
+    finally:
+        for p in ps:
+            if p.is_alive() and len(spans) < procs:
+                p.terminate()
+            p.join()
+    t_all = max(e for _, e in spans) - min(s for s, _ in spans)
+    return dict(one_thread={"value": total_bytes / t_one / 1e9, "unit": "GB/s", "cores": 1,
+                            "seconds": t_one},
+                all_cores={"value": total_bytes / t_all / 1e9, "unit": "GB/s", "cores": procs,
+                           "seconds": t_all, "largest_share_bytes": max(load)},
+                kind="oracle",
+                sample=f"weight re-quantization and 1x128 activation quantization of the "
+                       f"{len(linears)} linears of the block at M={M} ({len(tensors)} tensors, "
+                       f"{total_bytes / 1e6:.0f} MB of algorithmic bytes), partitioned by tensor "
+                       f"over {procs} processes")
+
+
 # ------------------------------------------------------------------------------------- main
 
 
@@ -389,8 +484,19 @@ def main():
         sys.exit(2)
     import torch
 
-    import fp8_blockwise_quantization_amd as fq
     from workloads import synth
+
+    # the oracle's quantizers on every host core: worker processes are started here, before
+    # anything in this process touches the GPU
+    quant_cpu = None
+    if args.workload == "qwen3-8b-decode" and not args.no_cpu_baseline:
+        try:
+            quant_cpu = cpu_quantizers_all_cores(synth.DENSE_LINEARS_QWEN3_8B, 64, seed=6000,
+                                                 scales=args.scales)
+        except Exception as e:  # reported in the line; the GPU measurement goes on
+            quant_cpu = {"error": f"{type(e).__name__}: {e}"}
+
+    import fp8_blockwise_quantization_amd as fq
 
     torch.cuda.set_device(0)
     fq.lib()
@@ -488,6 +594,8 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline_dense(linears, M, seed=5000, budget_linears=7 if M <= 256 else 1,
                                  scales=args.scales)
+        if quant_cpu is not None:
+            cpu["quantizers"] = quant_cpu
     line = {
         "metric": "blockscaled FP8 GEMM TFLOP/s (% MFMA peak); block-quant GB/s (% HBM peak)",
         "value": value, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
