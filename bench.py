@@ -489,7 +489,12 @@ def main():
     # the oracle's quantizers on every host core: worker processes are started here, before
     # anything in this process touches the GPU
     quant_cpu = None
-    if args.workload == "qwen3-8b-decode" and not args.no_cpu_baseline:
+    profiled = ("rocprof" in os.environ.get("LD_PRELOAD", "")
+                or any(k.startswith("ROCPROF") for k in os.environ))
+    if args.workload == "qwen3-8b-decode" and not args.no_cpu_baseline and profiled:
+        # a profiler's preloaded library may already hold the GPU: start no processes
+        quant_cpu = {"skipped": "running under a profiler"}
+    elif args.workload == "qwen3-8b-decode" and not args.no_cpu_baseline:
         try:
             quant_cpu = cpu_quantizers_all_cores(synth.DENSE_LINEARS_QWEN3_8B, 64, seed=6000,
                                                  scales=args.scales)
