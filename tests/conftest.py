@@ -1,3 +1,4 @@
+import json
 import os
 import sys
 
@@ -27,3 +28,20 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+def pytest_terminal_summary(terminalreporter):
+    """The GEMM tolerance slack of every GPU parity check that ran (worst |gpu - ref| / bound per
+    check; <= 1 passes), and, if FP8RL_SLACK_REPORT names a file, the same list as JSON."""
+    mod = sys.modules.get("tests.gpu_util")
+    rows = getattr(mod, "SLACK", None) if mod else None
+    if not rows:
+        return
+    terminalreporter.write_sep("-", "GEMM parity slack: worst |gpu - ref| / bound per check")
+    for r in rows:
+        terminalreporter.write_line(f"{r['slack']:7.4f}  {r['kind']:<9} {r['out']:<4} "
+                                    f"{'x'.join(map(str, r['shape'])):<13} {r['test']} [{r['check']}]")
+    path = os.environ.get("FP8RL_SLACK_REPORT")
+    if path:
+        with open(path, "w") as f:
+            json.dump(rows, f, indent=1)

@@ -2,8 +2,20 @@
 
 from __future__ import annotations
 
+import os
+
 import numpy as np
 import torch
+
+#: Every tolerance check of this session: the worst |gpu - ref| / bound (the slack; <= 1 passes)
+#: with the check's label and the test it ran in. conftest.py prints them at the end of the run.
+SLACK: list = []
+
+
+def _record(kind: str, what: str, out: str, shape, worst: float) -> None:
+    test = os.environ.get("PYTEST_CURRENT_TEST", "").split(" ")[0]
+    SLACK.append({"test": test, "check": what, "kind": kind, "out": out,
+                  "shape": [int(d) for d in shape], "slack": worst})
 
 
 def bits16(t: torch.Tensor) -> np.ndarray:
@@ -42,6 +54,7 @@ def assert_gemm_close(got: np.ndarray, ref_rounded: np.ndarray, ref_f64: np.ndar
     bound = np.maximum(bound, np.finfo(np.float64).tiny)
     ratio = err / bound
     worst = float(ratio.max()) if ratio.size else 0.0
+    _record("tolerance", what, out, got.shape, worst)
     if worst > 1.0:
         idx = np.unravel_index(int(np.argmax(ratio)), ratio.shape)
         raise AssertionError(
@@ -78,6 +91,7 @@ def assert_within(got: np.ndarray, ref: np.ndarray, bound: np.ndarray, what: str
     err = np.abs(got - ref)
     ratio = err / np.maximum(bound, np.finfo(np.float64).tiny)
     worst = float(ratio.max()) if ratio.size else 0.0
+    _record("bound", what, "", got.shape, worst)
     if worst > 1.0:
         idx = np.unravel_index(int(np.argmax(ratio)), ratio.shape)
         raise AssertionError(f"{what}: outside bound at {idx}: gpu={got[idx]!r} ref={ref[idx]!r} "
