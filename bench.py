@@ -599,8 +599,13 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline_dense(linears, M, seed=5000, budget_linears=7 if M <= 256 else 1,
                                  scales=args.scales)
+        cpu["gpu_over_oracle"] = value / cpu["value"]  # whole step, same algorithmic bytes
         if quant_cpu is not None:
             cpu["quantizers"] = quant_cpu
+            if requant and "all_cores" in quant_cpu:
+                # the GPU's weight re-quantization against the oracle's quantizers on every core
+                quant_cpu["gpu_weight_requant_over_oracle_all_cores"] = (
+                    parts["quant_weight_batched"]["gbs"] / quant_cpu["all_cores"]["value"])
     line = {
         "metric": "blockscaled FP8 GEMM TFLOP/s (% MFMA peak); block-quant GB/s (% HBM peak)",
         "value": value, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
