@@ -415,6 +415,18 @@ def _quant_worker(tensors, scales, barrier, results):
     results.put((t0, time.monotonic()))
 
 
+def partition_by_bytes(tensors, procs):
+    """Deal the tensors (tuples whose last field is their byte count) out to `procs` shares,
+    largest first, each to the share with the fewest bytes so far. Returns (shares, bytes per
+    share)."""
+    shares, load = [[] for _ in range(procs)], [0] * procs
+    for t in sorted(tensors, key=lambda t: -t[-1]):
+        j = load.index(min(load))
+        shares[j].append(t)
+        load[j] += t[-1]
+    return shares, load
+
+
 def cpu_quantizers_all_cores(linears, M, seed, scales="fp32"):
     """The oracle's two quantizers over one step's tensors (each linear's bf16 weight and its
     [M][K] activations): first one tensor after another in this process, then the same tensors
@@ -437,11 +449,7 @@ def cpu_quantizers_all_cores(linears, M, seed, scales="fp32"):
     del inputs
 
     procs = max(1, min(len(os.sched_getaffinity(0)), len(tensors)))
-    shares, load = [[] for _ in range(procs)], [0] * procs
-    for t in sorted(tensors, key=lambda t: -t[5]):
-        j = load.index(min(load))
-        shares[j].append(t)
-        load[j] += t[5]
+    shares, load = partition_by_bytes(tensors, procs)
     ctx = mp.get_context("spawn")
     barrier, results = ctx.Barrier(procs), ctx.Queue()
     ps = [ctx.Process(target=_quant_worker, args=(sh, scales, barrier, results)) for sh in shares]
