@@ -1,32 +1,34 @@
 """Benchmark of the FP8 W8A8 linear-layer hot path on one MI355X.
 
-Default workload: one Qwen3-8B-shaped decoder block at decode (M = 64 tokens, hidden 4096,
-7 linears: q/o 4096x4096, k/v 1024x4096, gate/up 12288x4096, down 4096x12288). One step is the
-whole hot path over that block:
+Default workload (`qwen3-8b-prefill`): one Qwen3-8B-shaped decoder block at prefill (M = 8192
+tokens, hidden 4096, 7 linears: q/o 4096x4096, k/v 1024x4096, gate/up 12288x4096, down
+4096x12288). One step is the dynamic 1x128 quantization of each distinct bf16 input activation
+and the blockwise-scaled FP8 GEMMs (bf16 output), replayed from a HIP graph. `value` is the GEMM
+TFLOP/s of the step (2MNK over the 7 linears / step time); `roofline` is the largest GEMM's kernel
+(gate/up, 8192 x 24576 x 4096), timed per launch with HIP events on the stream it runs on. Parts
+of the same line: every GEMM's launch time, the 32-layer Llama-3.1-8B weight sync (20.94 GB of
+algorithmic traffic per pass) and the decode step below.
 
-  1. per-step re-quantization of all 7 bf16 weights to E4M3 with 128x128 FP32 block scales,
-     in one batched launch,
-  2. dynamic 1x128 per-token quantization of each linear's bf16 input activation,
-  3. the blockwise-scaled FP8 GEMMs (bf16 output).
+Decode workload (`qwen3-8b-decode`, M = 64): per-step re-quantization of all 7 bf16 weights to
+E4M3 with 128x128 FP32 block scales in one batched launch, then the activation quantizations and
+GEMMs; `value` is the step's algorithmic HBM traffic / step time (GB/s), `roofline` the weight
+re-quantization kernel. Its weights rotate over enough copies that every step reads more than
+1 GiB, so the 256 MiB Infinity Cache cannot hold a step's working set.
 
 The weights are laid out as a serving engine keeps them: q/k/v concatenated along N (6144x4096)
 and gate/up concatenated (24576x4096), so the block is 4 GEMMs over 4 activation quantizations
 (one per distinct input), with the same bytes and FLOPs as the 7 separate linears.
 
 Inputs are seeded synthetic tensors resident in HBM (weights N(0, 0.02) with 0.1 % x10 outliers,
-activations N(0, 1) with 1 % x20 outlier channels), rotated over enough copies that every step
-reads more than 1 GiB, so the 256 MiB Infinity Cache cannot hold a step's working set.
+activations N(0, 1) with 1 % x20 outlier channels). Every workload prints one JSON line of the
+same schema (`roofline` of its dominant kernel, `cpu_baseline` = the CPU oracle timed on a bounded
+sample of the same workload on this host's cores).
 
-Prints one JSON line. `value` is the step's algorithmic HBM traffic (bytes each kernel must move
-at least once) divided by the step time, in GB/s; per-part GB/s and the GEMMs' TFLOP/s are
-reported beside it. `roofline` describes the dominant kernel (the weight re-quantization), timed
-with HIP events around each of its launches inside the timed region. `cpu_baseline` times the
-CPU oracle on a bounded sample of the same step.
-
-Other workloads (`--workload`): qwen3-8b-prefill (M = 8192), llama31-8b-mlp (M in {256, 4096}),
-llama31-8b-weight-sync (32 layers of weights), qwen3-30b-a3b-moe (grouped expert GEMMs),
-qwen3-8b-kv-cache (per-tensor Q/K/V recalibration and FP8 KV-cache store over 36 layers),
-qwen3-8b-backward (FP8 Dgrad and Wgrad of the decoder block's linears over 8192 tokens).
+Other workloads (`--workload`): llama31-8b-mlp (M in {256, 4096}), llama31-8b-weight-sync (32
+layers of weights), qwen3-30b-a3b-moe (grouped expert GEMMs), qwen3-8b-kv-cache (per-tensor Q/K/V
+recalibration and FP8 KV-cache store over 36 layers), qwen3-8b-backward (FP8 Dgrad and Wgrad of
+the decoder block's linears over 8192 tokens), qwen3-8b-decode-fused-act (decode GEMMs with the
+activation quantization fused in, against two launches).
 """
 
 from __future__ import annotations
@@ -53,7 +55,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="qwen3-8b-decode",
+    ap.add_argument("--workload", default="qwen3-8b-prefill",
                     choices=["qwen3-8b-decode", "qwen3-8b-prefill", "llama31-8b-mlp",
                              "llama31-8b-weight-sync", "qwen3-30b-a3b-moe", "qwen3-8b-kv-cache",
                              "qwen3-8b-backward", "qwen3-8b-decode-fused-act"])
@@ -336,10 +338,12 @@ def sample_clocks(done_event, period_s=0.002, max_samples=200):
 # ------------------------------------------------------------------------------ cpu baseline
 
 
-def cpu_baseline_dense(linears, M, seed, budget_linears, min_seconds=10.0, scales="fp32"):
+def cpu_baseline_dense(linears, M, seed, budget_linears, min_seconds=10.0, scales="fp32",
+                       unit="GB/s"):
     """Time the CPU oracle on the linears of the step, in order and cycling, for at least
     `budget_linears` linears and `min_seconds` of oracle time (full per-linear work: weight
-    re-quantization, activation quantization, GEMM)."""
+    re-quantization, activation quantization, GEMM). `unit`: GB/s of algorithmic bytes or
+    TFLOP/s of GEMM flops over the oracle's time."""
     import numpy as np
     import torch
 
@@ -355,6 +359,7 @@ def cpu_baseline_dense(linears, M, seed, budget_linears, min_seconds=10.0, scale
         blas_threads = os.cpu_count() or 1
     bits = lambda t: t.view(torch.int16).numpy().view(np.uint16)
     total_bytes = 0
+    total_flops = 0
     elapsed = 0.0
     done = []
     i = 0
@@ -368,9 +373,14 @@ def cpu_baseline_dense(linears, M, seed, budget_linears, min_seconds=10.0, scale
         og.gemm_blockscaled(xq, sa, wq, sw, out="bf16")
         elapsed += time.perf_counter() - t0
         total_bytes += w_bytes(N, K) + a_bytes(M, K) + g_bytes(M, N, K)
+        total_flops += 2 * M * N * K
         done.append(name)
         i += 1
-    return dict(value=total_bytes / elapsed / 1e9, unit="GB/s", cores=int(blas_threads),
+    if unit == "TFLOP/s":
+        value = total_flops / elapsed / 1e12
+    else:
+        value = total_bytes / elapsed / 1e9
+    return dict(value=value, unit=unit, cores=int(blas_threads),
                 quantizer_threads=1, gemm_blas_threads=int(blas_threads),
                 host_cpus=os.cpu_count(), host_cpus_usable=len(os.sched_getaffinity(0)),
                 kind="oracle", seconds=elapsed,
@@ -439,7 +449,8 @@ def cpu_quantizers_all_cores(linears, M, seed, scales="fp32"):
     tensors = []
     for i, (name, N, K) in enumerate(linears):
         tensors.append(("w", name, N, K, seed + i, w_bytes(N, K)))
-        tensors.append(("x", name, M, K, seed + 7 + i, a_bytes(M, K)))
+        if M > 0:  # M == 0: the weights alone (a weight-sync sample)
+            tensors.append(("x", name, M, K, seed + 7 + i, a_bytes(M, K)))
     total_bytes = sum(t[5] for t in tensors)
 
     inputs = _quant_inputs(tensors)
@@ -475,13 +486,173 @@ def cpu_quantizers_all_cores(linears, M, seed, scales="fp32"):
                 all_cores={"value": total_bytes / t_all / 1e9, "unit": "GB/s", "cores": procs,
                            "seconds": t_all, "largest_share_bytes": max(load)},
                 kind="oracle",
-                sample=f"weight re-quantization and 1x128 activation quantization of the "
-                       f"{len(linears)} linears of the block at M={M} ({len(tensors)} tensors, "
-                       f"{total_bytes / 1e6:.0f} MB of algorithmic bytes), partitioned by tensor "
-                       f"over {procs} processes")
+                sample=(f"weight re-quantization and 1x128 activation quantization of the "
+                        f"{len(linears)} linears of the block at M={M}" if M > 0 else
+                        f"weight re-quantization of {len(linears)} weight matrices") +
+                       f" ({len(tensors)} tensors, {total_bytes / 1e6:.0f} MB of algorithmic "
+                       f"bytes), partitioned by tensor over {procs} processes")
 
 
 # ------------------------------------------------------------------------------------- main
+
+
+METRIC = "blockscaled FP8 GEMM TFLOP/s (% MFMA peak); block-quant GB/s (% HBM peak)"
+DTYPE = "fp8-e4m3 x fp8-e4m3 -> f32 accumulate, bf16 out"
+GEMM_KERNEL = "gemm_big_kernel"  # the large-M blockscaled GEMM kernel (what rocprofv3 lists)
+WQ_KERNEL = "quant_weight_blk128_kernel"
+
+
+def roof_mfma(kernel, flops, us, units, traffic=None):
+    """`roofline` of a matrix-core-bound kernel: algorithmic flops per launch over its average
+    launch duration, against the FP8 dense peak."""
+    tf = flops / (us * 1e-6) / 1e12
+    return {"kernel": kernel, "bound": "mfma", "achieved": tf, "peak": FP8_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": tf / FP8_PEAK_TFLOPS, "traffic": traffic,
+            "avg_launch_us": us, "algorithmic_flops_per_launch": flops,
+            "per_unit": "2 flops per multiply-add: 2*M*N*K per GEMM", "units_per_launch": units}
+
+
+def roof_hbm(kernel, nbytes, us, per_unit, units, traffic=None):
+    """`roofline` of an HBM-bound kernel: algorithmic bytes per launch over its average launch
+    duration, against the HBM peak."""
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"kernel": kernel, "bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": gbs / HBM_PEAK_GBS, "traffic": traffic, "avg_launch_us": us,
+            "algorithmic_bytes_per_launch": nbytes, "per_unit": per_unit,
+            "units_per_launch": units}
+
+
+def emit(args, value, unit, ms, cfg, roofline, cpu, **extra):
+    """Print the one JSON line of a workload (the same schema for every workload)."""
+    line = {"metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": DTYPE, "data": "synthetic",
+            "config": cfg}
+    line.update(extra)
+    line["roofline"] = roofline
+    line["cpu_baseline"] = cpu
+    print(json.dumps(line), flush=True)
+
+
+def timed_steps(torch, step, steps, warmup):
+    """`warmup` untimed steps, then `steps` steps with an event at every step boundary: returns
+    (ms per step, sorted per-step ms, the last event)."""
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    marks[0].record()
+    for i in range(steps):
+        step()
+        marks[i + 1].record()
+    return marks
+
+
+def finish_marks(torch, marks):
+    torch.cuda.synchronize()
+    n = len(marks) - 1
+    ms = marks[0].elapsed_time(marks[-1]) / n
+    per = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(n))
+    return ms, [per[n // 10], per[n // 2], per[(9 * n) // 10]]
+
+
+def dense_parts(blk, args, M):
+    """Per-GEMM launch timings and the captured act-quant + GEMM part of a dense block."""
+    lin_ms = blk.time_linears(max(args.steps, 10))
+    roof_us = blk.roofline_us()
+    gemms = []
+    for i, (name, N, K) in enumerate(blk.linears):
+        us = blk.time_gemm(i, max(args.steps, 10))
+        fl = 2 * M * N * K
+        gemms.append({"gemm": name, "M": M, "N": N, "K": K, "avg_launch_us": us,
+                      "tflops": fl / (us * 1e-6) / 1e12,
+                      "frac_fp8_peak": fl / (us * 1e-6) / 1e12 / FP8_PEAK_TFLOPS,
+                      "gbs": g_bytes(M, N, K) / (us * 1e-6) / 1e9,
+                      "frac_roofline": 1e6 * max(fl / (FP8_PEAK_TFLOPS * 1e12),
+                                                 g_bytes(M, N, K) / (HBM_PEAK_GBS * 1e9)) / us})
+    graph = {"us_per_step": 1e3 * lin_ms, "bytes": blk.bytes_a + blk.bytes_g, "flops": blk.flops,
+             "gbs": (blk.bytes_a + blk.bytes_g) / (lin_ms * 1e-3) / 1e9,
+             "gemm_tflops": blk.flops / (lin_ms * 1e-3) / 1e12,
+             "roofline_us": roof_us, "frac_roofline": roof_us / (1e3 * lin_ms),
+             "roofline_rule": "sum over the GEMMs of max(2MNK / 5.0 PFLOP/s, bytes / 8 TB/s) "
+                              "plus activation-quant bytes / 8 TB/s"}
+    return graph, gemms
+
+
+class WeightSync:
+    """Every linear weight of 32 Llama-3.1-8B layers (224 matrices, 6.98e9 elements, 20.94 GB of
+    algorithmic traffic) re-quantized per pass in ceil(224 / 32) = 7 batched launches."""
+
+    LAYERS = 32
+
+    def __init__(self, torch, fq, synth, scales="fp32"):
+        self.torch, self.fq, self.scales = torch, fq, scales
+        self.shapes = [(N, K) for _ in range(self.LAYERS) for _, N, K in
+                       synth.LLAMA31_8B_LAYER_LINEARS]
+        ws, wqs, sws = [], [], []
+        for li, (N, K) in enumerate(self.shapes):
+            ws.append(synth.weight_bf16(N, K, seed=3000 + li, outlier_frac=0.001, device="cuda"))
+            wqs.append(torch.empty((N, K), dtype=torch.uint8, device="cuda"))
+            sws.append(torch.empty((N // 128, K // 128), dtype=torch.float32, device="cuda"))
+        self.tensors = (ws, wqs, sws)
+        self.descs = [fq.weight_descs(ws[i:i + 32], wqs[i:i + 32], sws[i:i + 32])
+                      for i in range(0, len(ws), 32)]
+        self.sizes = [sum(w_bytes(N, K) for N, K in self.shapes[i:i + 32])
+                      for i in range(0, len(ws), 32)]
+        self.bytes = sum(self.sizes)
+        self.elements = sum(N * K for N, K in self.shapes)
+        self.timer = KernelTimer(torch)
+
+    def step(self):  # one launch per group of 32 matrices, each timed
+        for d, nb in zip(self.descs, self.sizes):
+            self.timer.launch(lambda: self.fq.quant_weights(None, None, None, descs=d,
+                                                            scale=self.scales), nb)
+
+    def measure(self, steps, warmup):
+        ms = _timed(self.torch, self.step, steps, warmup, (self.timer,))
+        r = self.timer.result()
+        return ms, r
+
+    def free(self):
+        self.tensors = None
+        self.descs = None
+
+
+def weight_sync_part(torch, fq, synth, args):
+    sync = WeightSync(torch, fq, synth, scales=args.scales)
+    ms, r = sync.measure(max(3, args.steps // 4), 1)
+    part = {"matrices": len(sync.shapes), "elements": sync.elements, "bytes": sync.bytes,
+            "launches_per_pass": len(sync.descs), "ms_per_pass": ms,
+            "gbs": sync.bytes / (ms * 1e-3) / 1e9,
+            "frac_hbm": sync.bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "kernel_avg_launch_us": r["avg_us"], "kernel_gbs": r["gbs"],
+            "kernel_frac_hbm": r["gbs"] / HBM_PEAK_GBS,
+            "per_unit": "3 B per weight element + 4 B per 128x128 block"}
+    sync.free()
+    del sync
+    torch.cuda.empty_cache()
+    return part
+
+
+def decode_part(torch, fq, synth, args):
+    """The Qwen3-8B decode step (M = 64) with its per-step weight re-quantization: step time and
+    its parts, for the line of another workload."""
+    blk = DenseBlock(torch, fq, synth, serving_layout(synth.DENSE_LINEARS_QWEN3_8B), 64,
+                     seed=1000 + args.seed, requant=True, scales=args.scales)
+    blk.capture()
+    marks = timed_steps(torch, lambda: blk.step(timed=True), max(args.steps, 10), args.warmup)
+    ms, spread = finish_marks(torch, marks)
+    step_bytes = blk.bytes_w + blk.bytes_a + blk.bytes_g
+    graph, gemms = dense_parts(blk, args, 64)
+    r = blk.t_w.result()
+    out = {"tokens_M": 64, "ms_per_step": ms, "ms_per_step_p10_p50_p90": spread,
+           "step_bytes": step_bytes, "gbs": step_bytes / (ms * 1e-3) / 1e9,
+           "act_quant_and_gemm_graph": graph, "gemms": gemms,
+           "quant_weight_batched": dict(r, frac_hbm=r["gbs"] / HBM_PEAK_GBS,
+                                        bytes=blk.bytes_w)}
+    del blk
+    torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -499,15 +670,17 @@ def main():
     quant_cpu = None
     profiled = ("rocprof" in os.environ.get("LD_PRELOAD", "")
                 or any(k.startswith("ROCPROF") for k in os.environ))
-    if args.workload == "qwen3-8b-decode" and not args.no_cpu_baseline and profiled:
-        # a profiler's preloaded library may already hold the GPU: start no processes
-        quant_cpu = {"skipped": "running under a profiler"}
-    elif args.workload == "qwen3-8b-decode" and not args.no_cpu_baseline:
-        try:
-            quant_cpu = cpu_quantizers_all_cores(synth.DENSE_LINEARS_QWEN3_8B, 64, seed=6000,
-                                                 scales=args.scales)
-        except Exception as e:  # reported in the line; the GPU measurement goes on
-            quant_cpu = {"error": f"{type(e).__name__}: {e}"}
+    quant_sample = {"qwen3-8b-decode": (synth.DENSE_LINEARS_QWEN3_8B, 64),
+                    "llama31-8b-weight-sync": (synth.LLAMA31_8B_LAYER_LINEARS, 0)}
+    if args.workload in quant_sample and not args.no_cpu_baseline:
+        if profiled:  # a profiler's preloaded library may already hold the GPU: no processes
+            quant_cpu = {"skipped": "running under a profiler"}
+        else:
+            try:
+                lin, m = quant_sample[args.workload]
+                quant_cpu = cpu_quantizers_all_cores(lin, m, seed=6000, scales=args.scales)
+            except Exception as e:  # reported in the line; the GPU measurement goes on
+                quant_cpu = {"error": f"{type(e).__name__}: {e}"}
 
     import fp8_blockwise_quantization_amd as fq
 
@@ -522,111 +695,99 @@ def main():
         del src, dst
     dev_name = torch.cuda.get_device_name(0)
     props = torch.cuda.get_device_properties(0)
+    gpu = {"gpu": dev_name, "cus": props.multi_processor_count}
+    runners = {"qwen3-8b-prefill": run_prefill, "qwen3-8b-decode": run_decode,
+               "llama31-8b-mlp": run_mlp, "llama31-8b-weight-sync": run_weight_sync,
+               "qwen3-30b-a3b-moe": run_moe, "qwen3-8b-kv-cache": run_kv_cache,
+               "qwen3-8b-backward": run_backward, "qwen3-8b-decode-fused-act": run_fused_act}
+    return runners[args.workload](args, torch, fq, synth, gpu, quant_cpu)
 
-    if args.workload == "qwen3-8b-decode":
-        linears, M, requant = synth.DENSE_LINEARS_QWEN3_8B, 64, True
-        cfg = {"workload": "Qwen3-8B decoder block, decode step", "tokens_M": 64, "hidden": 4096,
-               "linears": [list(l) for l in linears], "weight_requant_per_step": True,
-               "gemm_out": "bf16", "config_index": 1}
-    elif args.workload == "qwen3-8b-prefill":
-        linears, M, requant = synth.DENSE_LINEARS_QWEN3_8B, 8192, False
-        cfg = {"workload": "Qwen3-8B decoder block, prefill", "tokens_M": 8192, "hidden": 4096,
-               "linears": [list(l) for l in linears], "weight_requant_per_step": False,
-               "gemm_out": "bf16", "config_index": 2}
-    elif args.workload == "llama31-8b-mlp":
-        return run_mlp(args, torch, fq, synth, dev_name)
-    elif args.workload == "llama31-8b-weight-sync":
-        return run_weight_sync(args, torch, fq, synth, dev_name)
-    elif args.workload == "qwen3-8b-kv-cache":
-        return run_kv_cache(args, torch, fq, synth, dev_name)
-    elif args.workload == "qwen3-8b-backward":
-        return run_backward(args, torch, fq, synth, dev_name)
-    elif args.workload == "qwen3-8b-decode-fused-act":
-        return run_fused_act(args, torch, fq, synth, dev_name)
-    else:
-        return run_moe(args, torch, fq, synth, dev_name)
 
+def run_prefill(args, torch, fq, synth, gpu, quant_cpu):
+    """Default line: the Qwen3-8B decoder block at prefill (M = 8192; config "same linears at
+    prefill shape"), one step = the 4 activation quantizations and 4 GEMMs of the serving layout
+    replayed from a HIP graph. value = the step's GEMM TFLOP/s (2MNK over the 7 linears / step
+    time). Parts: every GEMM's launch time, the 32-layer weight sync and the decode step."""
+    M = 8192
+    linears = synth.DENSE_LINEARS_QWEN3_8B
     groups = serving_layout(linears)
-    cfg["gemms"] = [list(g) for g in groups]
-    cfg["layout"] = ("q/k/v and gate/up weights concatenated along N (one activation "
-                     "quantization and one GEMM per shared input)")
-    cfg["scales"] = args.scales
-    blk = DenseBlock(torch, fq, synth, groups, M, seed=1000 + args.seed, requant=requant,
+    cfg = {"workload": "Qwen3-8B decoder block, prefill (M = 8192 tokens)", "tokens_M": M,
+           "hidden": 4096, "linears": [list(l) for l in linears], "gemms": [list(g) for g in groups],
+           "layout": "q/k/v and gate/up weights concatenated along N (one activation "
+                     "quantization and one GEMM per shared input)",
+           "gemm_out": "bf16", "scales": args.scales}
+    blk = DenseBlock(torch, fq, synth, groups, M, seed=1000 + args.seed, requant=False,
                      scales=args.scales)
     blk.capture()
-    for _ in range(args.warmup):
-        blk.step()
-    torch.cuda.synchronize()
-    # one event at every step boundary: the total gives ms_per_step, the differences the spread
-    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    marks[0].record()
-    for i in range(args.steps):
-        blk.step(timed=True)
-        marks[i + 1].record()
-    clocks = sample_clocks(marks[-1])  # the host is ahead of the GPU: the timed steps run
-    torch.cuda.synchronize()
-    ms = marks[0].elapsed_time(marks[-1]) / args.steps
-    per_step = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps))
-    step_bytes = blk.bytes_w + blk.bytes_a + blk.bytes_g
-    value = step_bytes / (ms * 1e-3) / 1e9
-    lin_ms = blk.time_linears(max(args.steps, 10))
-    roof_us = blk.roofline_us()
-    parts = {"act_quant_and_gemm_graph": {
-        "us_per_step": 1e3 * lin_ms, "bytes": blk.bytes_a + blk.bytes_g, "flops": blk.flops,
-        "gbs": (blk.bytes_a + blk.bytes_g) / (lin_ms * 1e-3) / 1e9,
-        "gemm_tflops": blk.flops / (lin_ms * 1e-3) / 1e12,
-        "roofline_us": roof_us, "frac_roofline": roof_us / (1e3 * lin_ms),
-        "roofline_rule": "sum over the GEMMs of max(2MNK / 5.0 PFLOP/s, bytes / 8 TB/s) plus "
-                         "activation-quant bytes / 8 TB/s"}}
-    if requant:
-        r = blk.t_w.result()
-        parts["quant_weight_batched"] = dict(r, frac_hbm=r["gbs"] / HBM_PEAK_GBS)
-        roof = {"kernel": "quant_weight_blk128_kernel", "bound": "hbm", "achieved": r["gbs"],
-                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": r["gbs"] / HBM_PEAK_GBS,
-                "traffic": measured_traffic(), "avg_launch_us": r["avg_us"],
-                "algorithmic_bytes_per_launch": blk.bytes_w,
-                "per_unit": "3 B per weight element + 4 B per 128x128 block",
-                "units_per_launch": "all weights of the block (192,937,984 elements, 11,776 "
-                                    "blocks) in one launch"}
-    else:
-        # dominant kernel: the largest GEMM of the block, timed per launch
-        gi = max(range(len(blk.linears)), key=lambda j: blk.linears[j][1] * blk.linears[j][2])
-        gname, gN, gK = blk.linears[gi]
-        g_us = blk.time_gemm(gi, max(args.steps, 10))
-        tf = 2 * M * gN * gK / (g_us * 1e-6) / 1e12
-        roof = {"kernel": "gemm_big_kernel", "bound": "mfma", "achieved": tf,
-                "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": tf / FP8_PEAK_TFLOPS,
-                "traffic": measured_traffic(PREFILL_TRAFFIC_FILE)
-                if (M, gN, gK) == (8192, 24576, 4096) and args.scales == "fp32" else None,
-                "avg_launch_us": g_us,
-                "algorithmic_flops_per_launch": 2 * M * gN * gK,
-                "per_unit": "2 flops per multiply-add: 2*M*N*K per GEMM",
-                "units_per_launch": f"{gname}: M={M}, N={gN}, K={gK}"}
-
+    marks = timed_steps(torch, blk.step, args.steps, args.warmup)
+    clocks = sample_clocks(marks[-1])
+    ms, spread = finish_marks(torch, marks)
+    value = blk.flops / (ms * 1e-3) / 1e12
+    graph, gemms = dense_parts(blk, args, M)
+    big = max(gemms, key=lambda g: g["N"] * g["K"])
+    roof = roof_mfma(GEMM_KERNEL, 2 * M * big["N"] * big["K"], big["avg_launch_us"],
+                     f"{big['gemm']}: M={M}, N={big['N']}, K={big['K']} (one launch)",
+                     traffic=measured_traffic(PREFILL_TRAFFIC_FILE) if args.scales == "fp32"
+                     else None)
+    del blk
+    torch.cuda.empty_cache()
+    parts = {"act_quant_and_gemm_graph": graph, "gemms": gemms,
+             "weight_sync_32_layers": weight_sync_part(torch, fq, synth, args),
+             "decode_step": decode_part(torch, fq, synth, args)}
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline_dense(linears, M, seed=5000, budget_linears=7 if M <= 256 else 1,
-                                 scales=args.scales)
-        cpu["gpu_over_oracle"] = value / cpu["value"]  # whole step, same algorithmic bytes
+        cpu = cpu_baseline_dense(linears, M, seed=5000, budget_linears=1, scales=args.scales,
+                                 unit="TFLOP/s")
+        cpu["gpu_over_oracle"] = value / cpu["value"]
+    emit(args, value, "TFLOP/s", ms, cfg, roof, cpu, ms_per_step_p10_p50_p90=spread,
+         step_gemm_flops=blk_flops(groups, M), parts=parts, clocks_during_timed_steps=clocks,
+         **gpu)
+
+
+def blk_flops(groups, M):
+    return sum(2 * M * N * K for _, N, K in groups)
+
+
+def run_decode(args, torch, fq, synth, gpu, quant_cpu):
+    """The Qwen3-8B decode step (config "dense decode step", M = 64): per-step re-quantization of
+    all 7 weights in one batched launch, then the 4 activation quantizations and 4 GEMMs from a
+    HIP graph. value = the step's algorithmic bytes / step time (GB/s); roofline = the weight
+    re-quantization kernel."""
+    M = 64
+    linears = synth.DENSE_LINEARS_QWEN3_8B
+    groups = serving_layout(linears)
+    cfg = {"workload": "Qwen3-8B decoder block, decode step (M = 64 tokens)", "tokens_M": M,
+           "hidden": 4096, "linears": [list(l) for l in linears], "gemms": [list(g) for g in groups],
+           "weight_requant_per_step": True, "gemm_out": "bf16", "scales": args.scales,
+           "layout": "q/k/v and gate/up weights concatenated along N"}
+    blk = DenseBlock(torch, fq, synth, groups, M, seed=1000 + args.seed, requant=True,
+                     scales=args.scales)
+    blk.capture()
+    marks = timed_steps(torch, lambda: blk.step(timed=True), args.steps, args.warmup)
+    clocks = sample_clocks(marks[-1])
+    ms, spread = finish_marks(torch, marks)
+    step_bytes = blk.bytes_w + blk.bytes_a + blk.bytes_g
+    value = step_bytes / (ms * 1e-3) / 1e9
+    graph, gemms = dense_parts(blk, args, M)
+    r = blk.t_w.result()
+    roof = roof_hbm(WQ_KERNEL, blk.bytes_w, r["avg_us"],
+                    "3 B per weight element + 4 B per 128x128 block",
+                    "all weights of the block (192,937,984 elements, 11,776 blocks) in one launch",
+                    traffic=measured_traffic())
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline_dense(linears, M, seed=5000, budget_linears=7, scales=args.scales)
+        cpu["gpu_over_oracle"] = value / cpu["value"]
         if quant_cpu is not None:
             cpu["quantizers"] = quant_cpu
-            if requant and "all_cores" in quant_cpu:
-                # the GPU's weight re-quantization against the oracle's quantizers on every core
+            if "all_cores" in quant_cpu:
                 quant_cpu["gpu_weight_requant_over_oracle_all_cores"] = (
-                    parts["quant_weight_batched"]["gbs"] / quant_cpu["all_cores"]["value"])
-    line = {
-        "metric": "blockscaled FP8 GEMM TFLOP/s (% MFMA peak); block-quant GB/s (% HBM peak)",
-        "value": value, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "ms_per_step_p10_p50_p90": [per_step[len(per_step) // 10], per_step[len(per_step) // 2],
-                                    per_step[(9 * len(per_step)) // 10]],
-        "dtype": "fp8-e4m3 x fp8-e4m3 -> f32 accumulate, bf16 out", "data": "synthetic",
-        "config": cfg,
-        "step_bytes": step_bytes, "step_gemm_flops": blk.flops,
-        "parts": parts, "roofline": roof, "cpu_baseline": cpu, "gpu": dev_name,
-        "cus": props.multi_processor_count, "clocks_during_timed_steps": clocks,
-    }
-    print(json.dumps(line), flush=True)
+                    r["gbs"] / quant_cpu["all_cores"]["value"])
+    parts = {"act_quant_and_gemm_graph": graph, "gemms": gemms,
+             "quant_weight_batched": dict(r, frac_hbm=r["gbs"] / HBM_PEAK_GBS)}
+    emit(args, value, "GB/s", ms, cfg, roof, cpu, ms_per_step_p10_p50_p90=spread,
+         step_bytes=step_bytes, step_gemm_flops=blk.flops, parts=parts,
+         clocks_during_timed_steps=clocks, **gpu)
 
 
 def _timed(torch, fn, steps, warmup, timers=()):
@@ -645,21 +806,24 @@ def _timed(torch, fn, steps, warmup, timers=()):
     return a.elapsed_time(b) / steps
 
 
-def run_fused_act(args, torch, fq, synth, dev_name):
+def run_fused_act(args, torch, fq, synth, gpu, quant_cpu):
     """The decode GEMMs of one Qwen3-8B block (serving layout: q/k/v, o, gate/up, down) at small
     token counts, two ways: activation quantization and GEMM as two launches per GEMM, or the
     GEMM with the quantization fused in (one launch). Both are timed as the host launches them
-    (where small batches are launch-bound) and replayed from a HIP graph (GPU time only)."""
+    (where small batches are launch-bound) and replayed from a HIP graph (GPU time only).
+    value = algorithmic GB/s of the fused block at M = 64 (graph replay); roofline = the fused
+    gate/up GEMM."""
     groups = serving_layout(synth.DENSE_LINEARS_QWEN3_8B)
     pow2 = args.scales == "pow2"
     accum = "mx" if pow2 else "fp8"
-    g = torch.Generator(device="cuda").manual_seed(11 + args.seed)
     weights = []
     for i, (name, N, K) in enumerate(groups):
         w = synth.weight_bf16(N, K, seed=9100 + i, device="cuda")
         weights.append(fq.quant_weight(w, scale=args.scales))
         del w
     results = []
+    roof = None
+    value = ms64 = None
     for M in (1, 16, 64):
         xs = [synth.act_bf16(M, K, seed=9200 + M + i, device="cuda")
               for i, (_, _, K) in enumerate(groups)]
@@ -689,62 +853,113 @@ def run_fused_act(args, torch, fq, synth, dev_name):
         row["graph_fused_over_unfused"] = row["graph_fused_us"] / row["graph_unfused_us"]
         row["eager_fused_over_unfused"] = row["eager_fused_us"] / row["eager_unfused_us"]
         results.append(row)
-    print(json.dumps({
-        "workload": "Qwen3-8B decode GEMMs (q/k/v, o, gate/up, down), activation quantization "
-                    "fused into the GEMM vs a separate launch",
-        "metric": "microseconds per block (4 GEMMs with their activation quantization)",
-        "scales": args.scales, "launches_per_block": {"unfused": 2 * len(groups),
-                                                      "fused": len(groups)},
-        "gemms": [list(gr) for gr in groups], "results": results, "gpu": dev_name}), flush=True)
+        if M == 64:
+            nbytes = sum(N * K + 4 * (N // 128) * (K // 128) + 2 * M * K + 2 * M * N
+                         for _, N, K in groups)
+            ms64 = row["graph_fused_us"] / 1e3
+            value = nbytes / (ms64 * 1e-3) / 1e9
+            gi = max(range(len(groups)), key=lambda j: groups[j][1] * groups[j][2])
+            _, gN, gK = groups[gi]
+            t = KernelTimer(torch)
+            x, (wq, sw), y = xs[gi], weights[gi], ys[gi]
+            for _ in range(3):
+                fq.gemm_fused_act(x, wq, sw, y=y, workspace=ws, accum=accum, scale=args.scales)
+            for _ in range(max(args.steps, 10)):
+                t.launch(lambda: fq.gemm_fused_act(x, wq, sw, y=y, workspace=ws, accum=accum,
+                                                   scale=args.scales), 0)
+            torch.cuda.synchronize()
+            gb = gN * gK + 4 * (gN // 128) * (gK // 128) + 2 * M * gK + 2 * M * gN
+            roof = roof_hbm("gemm_decode_kernel (fused activation quantization)", gb,
+                            t.result()["avg_us"],
+                            "weight codes + block scales + bf16 activations + bf16 output",
+                            f"gate_up_proj: M={M}, N={gN}, K={gK} (one launch)")
+    cfg = {"workload": "Qwen3-8B decode GEMMs (q/k/v, o, gate/up, down) with the activation "
+                       "quantization fused into the GEMM", "tokens_M": [1, 16, 64],
+           "gemms": [list(gr) for gr in groups], "scales": args.scales,
+           "launches_per_block": {"unfused": 2 * len(groups), "fused": len(groups)}}
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline_dense(synth.DENSE_LINEARS_QWEN3_8B, 64, seed=5000, budget_linears=7,
+                                 scales=args.scales)
+        cpu["gpu_over_oracle"] = value / cpu["value"]
+    emit(args, value, "GB/s", ms64, cfg, roof, cpu, results=results, **gpu)
 
 
-def run_mlp(args, torch, fq, synth, dev_name):
-    out = []
+def run_mlp(args, torch, fq, synth, gpu, quant_cpu):
+    """Llama-3.1-8B MLP (config "Llama-3.1-8B-shaped MLP"): gate/up (fused, 28672 x 4096) and
+    down (4096 x 14336) with their activation quantizations, at M = 4096 (the line's value, GEMM
+    TFLOP/s over the step) and M = 256 (a part, against its HBM roofline)."""
+    mlp = synth.LLAMA31_8B_LAYER_LINEARS[4:]
+    out = {}
     for M in (256, 4096):
-        blk = DenseBlock(torch, fq, synth, serving_layout(synth.LLAMA31_8B_LAYER_LINEARS[4:]), M,
-                         seed=2000 + M, requant=False, scales=args.scales)
+        blk = DenseBlock(torch, fq, synth, serving_layout(mlp), M, seed=2000 + M, requant=False,
+                         scales=args.scales)
         blk.capture()
-        ms = blk.time_linears(max(args.steps, 10))
-        out.append({"M": M, "us_per_step": 1e3 * ms, "gemm_tflops_incl_act_quant":
-                    blk.flops / (ms * 1e-3) / 1e12,
-                    "gbs": (blk.bytes_a + blk.bytes_g) / (ms * 1e-3) / 1e9})
-    print(json.dumps({"workload": "Llama-3.1-8B MLP (gate/up/down) GEMMs + act quant",
-                      "scales": args.scales, "results": out, "gpu": dev_name}), flush=True)
+        marks = timed_steps(torch, blk.step, args.steps, args.warmup)
+        ms, spread = finish_marks(torch, marks)
+        graph, gemms = dense_parts(blk, args, M)
+        out[M] = {"tokens_M": M, "ms_per_step": ms, "ms_per_step_p10_p50_p90": spread,
+                  "gemm_tflops_incl_act_quant": blk.flops / (ms * 1e-3) / 1e12,
+                  "act_quant_and_gemm_graph": graph, "gemms": gemms}
+        del blk
+        torch.cuda.empty_cache()
+    big = max(out[4096]["gemms"], key=lambda g: g["N"] * g["K"])
+    roof = roof_mfma(GEMM_KERNEL, 2 * 4096 * big["N"] * big["K"], big["avg_launch_us"],
+                     f"{big['gemm']}: M=4096, N={big['N']}, K={big['K']} (one launch)")
+    cfg = {"workload": "Llama-3.1-8B MLP (gate/up + down GEMMs with activation quantization), "
+                       "M = 4096 (M = 256 in parts)", "tokens_M": [256, 4096],
+           "gemms": [list(g) for g in serving_layout(mlp)], "gemm_out": "bf16",
+           "scales": args.scales}
+    value = out[4096]["gemm_tflops_incl_act_quant"]
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline_dense(mlp, 4096, seed=5100, budget_linears=1, scales=args.scales,
+                                 unit="TFLOP/s")
+        cpu["gpu_over_oracle"] = value / cpu["value"]
+    emit(args, value, "TFLOP/s", out[4096]["ms_per_step"], cfg, roof, cpu,
+         parts={"m4096": out[4096], "m256": out[256]}, **gpu)
 
 
-def run_weight_sync(args, torch, fq, synth, dev_name):
-    """Re-quantize every linear weight of 32 Llama-3.1-8B layers (6.98e9 elements, 14 GB bf16)."""
-    layers = 32
-    shapes = [(N, K) for _ in range(layers) for _, N, K in synth.LLAMA31_8B_LAYER_LINEARS]
-    ws, wqs, sws = [], [], []
-    uniq = {}
-    for li, (N, K) in enumerate(shapes):
-        ws.append(synth.weight_bf16(N, K, seed=3000 + li, outlier_frac=0.001, device="cuda"))
-        wqs.append(torch.empty((N, K), dtype=torch.uint8, device="cuda"))
-        sws.append(torch.empty((N // 128, K // 128), dtype=torch.float32, device="cuda"))
-    tot = sum(w_bytes(N, K) for N, K in shapes)
-    timer = KernelTimer(torch)
-    descs = fq.weight_descs(ws, wqs, sws)
+def run_weight_sync(args, torch, fq, synth, gpu, quant_cpu):
+    """Config "weight-sync pass": every linear weight of 32 Llama-3.1-8B layers (6.98e9
+    elements, 14 GB bf16) re-quantized per step in 7 batched launches. value = algorithmic GB/s
+    of the pass; roofline = the weight quantizer kernel over all its launches."""
+    sync = WeightSync(torch, fq, synth, scales=args.scales)
+    for _ in range(args.warmup):
+        sync.step()
+    torch.cuda.synchronize()
+    sync.timer.reset()
+    marks = timed_steps(torch, sync.step, args.steps, 0)
+    ms, spread = finish_marks(torch, marks)
+    r = sync.timer.result()
+    value = sync.bytes / (ms * 1e-3) / 1e9
+    roof = roof_hbm(WQ_KERNEL, sync.bytes / len(sync.descs), r["avg_us"],
+                    "3 B per weight element + 4 B per 128x128 block",
+                    "32 weight matrices (about 3 GB of algorithmic traffic) per launch, 7 launches "
+                    "per pass; achieved = all bytes over all launch time")
+    roof["achieved"] = r["gbs"]
+    roof["frac"] = r["gbs"] / HBM_PEAK_GBS
+    cfg = {"workload": "Llama-3.1-8B weight sync: all linear weights of 32 layers re-quantized "
+                       "to E4M3 with 128x128 block scales", "layers": WeightSync.LAYERS,
+           "matrices": len(sync.shapes), "elements": sync.elements, "bytes": sync.bytes,
+           "launches_per_pass": len(sync.descs), "scales": args.scales}
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = dict(quant_cpu or {}, kind="oracle")
+        best = cpu.get("all_cores") or cpu.get("one_thread")
+        if best:
+            cpu.update(value=best["value"], unit="GB/s", cores=best["cores"])
+            cpu["gpu_over_oracle"] = value / best["value"]
+    emit(args, value, "GB/s", ms, cfg, roof, cpu, ms_per_step_p10_p50_p90=spread, **gpu)
 
-    def step():  # 224 matrices -> 7 launches of 32
-        timer.launch(lambda: fq.quant_weights(None, None, None, descs=descs), tot)
 
-    ms = _timed(torch, step, max(1, args.steps // 4), max(1, args.warmup // 2), (timer,))
-    r = timer.result()
-    print(json.dumps({"workload": "Llama-3.1-8B weight sync, 32 layers", "elements":
-                      sum(N * K for N, K in shapes), "bytes": tot, "ms_per_pass": ms,
-                      "GB/s": tot / (ms * 1e-3) / 1e9, "frac_hbm": tot / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                      "events": r, "launches_per_pass": -(-len(shapes) // 32), "gpu": dev_name}),
-          flush=True)
-
-
-def run_kv_cache(args, torch, fq, synth, dev_name):
+def run_kv_cache(args, torch, fq, synth, gpu, quant_cpu):
     """Per-tensor FP8 of Qwen3-8B's attention inputs over 36 layers: (1) recalibration -- the
     running amax of Q, K and V (column slices of each layer's fused [T][6144] QKV output) over a
     4096-token calibration batch in one batched call, then the 108 scales; (2) the KV-cache store
     of an 8192-token prefill chunk: each layer's K and V quantized with its scale into a
     65536-row FP8 cache at slot-mapped rows (one launch per layer for its K and V, replayed from a
-    HIP graph)."""
+    HIP graph). value = algorithmic GB/s of recalibration + store; roofline = the amax kernel."""
     layers, hidden, kv, T_cal, T_new, cache_rows = 36, 4096, 1024, 4096, 8192, 65536
     qkv_cols = hidden + 2 * kv
     cal = [synth.act_bf16(T_cal, qkv_cols, seed=7000 + l, device="cuda") for l in range(layers)]
@@ -787,30 +1002,69 @@ def run_kv_cache(args, torch, fq, synth, dev_name):
     ms_cal = _timed(torch, recal, max(args.steps, 5), max(args.warmup, 2), (t_cal,))
     r_cal = t_cal.result()
     ms_store = _timed(torch, graph.replay, max(args.steps, 5), max(args.warmup, 2))
-    amax_gbs = r_cal["gbs"]
-    print(json.dumps({
-        "workload": "Qwen3-8B per-tensor FP8 Q/K/V recalibration and KV-cache store, 36 layers",
-        "metric": "per-tensor quantizer GB/s (% HBM peak)",
-        "recalibration": {"tensors": len(xs), "calibration_tokens": T_cal, "bytes": cal_bytes,
-                          "ms_per_pass_incl_scales": ms_cal, "amax_launch_us": r_cal["avg_us"],
-                          "amax_gbs": amax_gbs, "amax_frac_hbm": amax_gbs / HBM_PEAK_GBS,
-                          "per_unit": "2 B per element read"},
-        "kv_store": {"launches": layers, "new_tokens": T_new, "cache_rows": cache_rows,
-                     "bytes": store_bytes, "ms_per_pass": ms_store,
-                     "gbs": store_bytes / (ms_store * 1e-3) / 1e9,
-                     "frac_hbm": store_bytes / (ms_store * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                     "per_unit": "3 B per element + 8 B slot per row"},
-        "gpu": dev_name}), flush=True)
+    ms = ms_cal + ms_store
+    value = (cal_bytes + store_bytes) / (ms * 1e-3) / 1e9
+    roof = roof_hbm("amax_bf16_kernel", cal_bytes, r_cal["avg_us"], "2 B per element read",
+                    f"the running amax of {len(xs)} Q/K/V tensors ({T_cal} calibration tokens, "
+                    f"36 layers) in one launch")
+    cfg = {"workload": "Qwen3-8B per-tensor FP8 Q/K/V recalibration and KV-cache store, 36 "
+                       "layers", "layers": layers, "calibration_tokens": T_cal,
+           "new_tokens": T_new, "cache_rows": cache_rows, "kv_width": kv}
+    parts = {"recalibration": {"tensors": len(xs), "bytes": cal_bytes,
+                               "ms_per_pass_incl_scales": ms_cal, "amax_launch_us": r_cal["avg_us"],
+                               "amax_gbs": r_cal["gbs"], "amax_frac_hbm": r_cal["gbs"] / HBM_PEAK_GBS},
+             "kv_store": {"launches": layers, "bytes": store_bytes, "ms_per_pass": ms_store,
+                          "gbs": store_bytes / (ms_store * 1e-3) / 1e9,
+                          "frac_hbm": store_bytes / (ms_store * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                          "per_unit": "3 B per element + 8 B slot per row"}}
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline_kv(synth, min_seconds=10.0)
+        cpu["gpu_over_oracle"] = value / cpu["value"]
+    emit(args, value, "GB/s", ms, cfg, roof, cpu, parts=parts, **gpu)
 
 
-def run_backward(args, torch, fq, synth, dev_name):
+def cpu_baseline_kv(synth, min_seconds=10.0):
+    """The oracle's per-tensor path on layers of the KV-cache workload, cycling until
+    `min_seconds`: running amax of a layer's Q, K and V over its calibration batch, the three
+    scales, and the per-tensor codes of its new K and V rows."""
+    import numpy as np
+    import torch
+
+    from oracle import kvcache as ok
+
+    bits = lambda t: t.contiguous().view(torch.int16).numpy().view(np.uint16)
+    hidden, kv, T_cal, T_new = 4096, 1024, 4096, 8192
+    elapsed, nbytes, layers = 0.0, 0, 0
+    while elapsed < min_seconds:
+        cal = bits(synth.act_bf16(T_cal, hidden + 2 * kv, seed=7500 + layers))
+        new = bits(synth.act_bf16(T_new, 2 * kv, seed=8500 + layers))
+        t0 = time.perf_counter()
+        scales = []
+        for lo, hi in ((0, hidden), (hidden, hidden + kv), (hidden + kv, hidden + 2 * kv)):
+            scales.append(ok.scale_per_tensor(ok.amax(cal[:, lo:hi])))
+        ok.quant_per_tensor(new[:, :kv], scales[1])
+        ok.quant_per_tensor(new[:, kv:], scales[2])
+        elapsed += time.perf_counter() - t0
+        nbytes += 2 * cal.size + 2 * (T_new * kv * 3 + T_new * 8)
+        layers += 1
+    return dict(value=nbytes / elapsed / 1e9, unit="GB/s", cores=1, kind="oracle",
+                seconds=elapsed, sample=f"{layers} layers: amax + scale of Q, K, V over "
+                                        f"{T_cal} calibration tokens, per-tensor codes of "
+                                        f"{T_new} new K and V rows; numpy, one thread")
+
+
+def run_backward(args, torch, fq, synth, gpu, quant_cpu):
     """FP8 backward of the Qwen3-8B decoder block's linears (serving layout: q/k/v and gate/up
     fused) over T = 8192 tokens. Per linear: the output gradient dY quantized both ways from one
     read (1x128 rows for Dgrad, 128x1 token groups stored transposed for Wgrad), the input X in
     128x1 token groups, the weight's transposed block-quantized copy, then Dgrad = dYq WqT^T
     (blockwise-scaled GEMM) and Wgrad = dYqT XqT^T (row-scaled GEMM). Each part is captured in
-    its own HIP graph and timed over replays; bf16 outputs, FP8 slice sums (the FP32-scale
-    default) or, with --scales pow2, matrix-core scales."""
+    its own HIP graph and timed over replays; bf16 outputs with the library's default
+    accumulation (FP8 slice sums for Dgrad, f16 ones for Wgrad) or, with --scales pow2,
+    matrix-core scales for Dgrad. value = GEMM TFLOP/s of Dgrad + Wgrad over quantizers + both
+    GEMMs; the opt-in FP8-slice Wgrad (outside the bf16 tolerance in rare cancelling elements)
+    is timed as a part of its own."""
     T = 8192
     groups = serving_layout(synth.DENSE_LINEARS_QWEN3_8B)
     acc = "mx" if args.scales == "pow2" else None
@@ -846,41 +1100,104 @@ def run_backward(args, torch, fq, synth, dev_name):
             wqt, swt, _, _ = l["q_w"]
             fq.gemm(dyq, s_dy, wqt, swt, y=l["dx"], workspace=l["ws_dx"], accum=acc)
 
-    def wgrad_part():
+    def wgrad_part(wacc=None):
         for l in L:
             dyt, s_dyt, _, _ = l["q_dy"]
             xt, s_xt, _, _ = l["q_x"]
-            fq.gemm_rowscaled(dyt, s_dyt, xt, s_xt, y=l["dw"], workspace=l["ws_dw"], accum=acc)
+            fq.gemm_rowscaled(dyt, s_dyt, xt, s_xt, y=l["dw"], workspace=l["ws_dw"], accum=wacc)
 
     res = {}
     flops = sum(2 * T * l["N"] * l["K"] for l in L)
     qbytes = sum(T * l["N"] * (2 + 2) + T * l["N"] // 128 * 8 + T * l["K"] * 3 + T * l["K"] // 128 * 4
                  + l["N"] * l["K"] * 3 for l in L)
-    for name, fn in (("quantizers", quant_part), ("dgrad", dgrad_part), ("wgrad", wgrad_part)):
+    parts_fn = (("quantizers", quant_part), ("dgrad", dgrad_part), ("wgrad", wgrad_part),
+                ("wgrad_fp8_slices_opt_in", lambda: wgrad_part("fp8")))
+    for name, fn in parts_fn:
         fn()
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             fn()
         res[name] = _timed(torch, g.replay, max(args.steps, 5), max(args.warmup, 2))
-    print(json.dumps({
-        "workload": "Qwen3-8B decoder block linears, FP8 backward (Dgrad + Wgrad), 8192 tokens",
-        "metric": "blockscaled FP8 GEMM TFLOP/s (% MFMA peak); quantizer GB/s (% HBM peak)",
-        "gemms": [[l["name"], l["N"], l["K"]] for l in L], "tokens": T, "scales": args.scales,
-        "quantizers": {"ms": res["quantizers"], "bytes": qbytes,
-                       "gbs": qbytes / (res["quantizers"] * 1e-3) / 1e9,
-                       "frac_hbm": qbytes / (res["quantizers"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                       "per_unit": "dY: 2 B read + 2 B of codes (both layouts) per element + both "
-                                   "scale sets; X: 3 B per element + scales; W: 3 B per element"},
-        "dgrad": {"ms": res["dgrad"], "tflops": flops / (res["dgrad"] * 1e-3) / 1e12,
-                  "frac_mfma": flops / (res["dgrad"] * 1e-3) / 1e12 / FP8_PEAK_TFLOPS},
-        "wgrad": {"ms": res["wgrad"], "tflops": flops / (res["wgrad"] * 1e-3) / 1e12,
-                  "frac_mfma": flops / (res["wgrad"] * 1e-3) / 1e12 / FP8_PEAK_TFLOPS},
-        "gpu": dev_name}), flush=True)
+    # the dominant kernel: the largest Dgrad GEMM (gate/up: M = T, N = K = 4096, K = 24576),
+    # timed per launch
+    big = max(L, key=lambda l: l["N"] * l["K"])
+    _, _, dyq, s_dy = big["q_dy"]
+    wqt, swt, _, _ = big["q_w"]
+    t = KernelTimer(torch)
+    for _ in range(3):
+        fq.gemm(dyq, s_dy, wqt, swt, y=big["dx"], workspace=big["ws_dx"], accum=acc)
+    for _ in range(max(args.steps, 10)):
+        t.launch(lambda: fq.gemm(dyq, s_dy, wqt, swt, y=big["dx"], workspace=big["ws_dx"],
+                                 accum=acc), 0)
+    torch.cuda.synchronize()
+    roof = roof_mfma(GEMM_KERNEL, 2 * T * big["N"] * big["K"], t.result()["avg_us"],
+                     f"Dgrad of {big['name']}: M={T}, N={big['K']}, K={big['N']} (one launch)")
+    ms = res["quantizers"] + res["dgrad"] + res["wgrad"]
+    value = 2 * flops / (ms * 1e-3) / 1e12
+    gem = lambda k: {"ms": res[k], "tflops": flops / (res[k] * 1e-3) / 1e12,
+                     "frac_mfma": flops / (res[k] * 1e-3) / 1e12 / FP8_PEAK_TFLOPS}
+    parts = {"quantizers": {"ms": res["quantizers"], "bytes": qbytes,
+                            "gbs": qbytes / (res["quantizers"] * 1e-3) / 1e9,
+                            "frac_hbm": qbytes / (res["quantizers"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                            "per_unit": "dY: 2 B read + 2 B of codes (both layouts) per element "
+                                        "+ both scale sets; X: 3 B per element + scales; W: 3 B "
+                                        "per element"},
+             "dgrad": gem("dgrad"), "wgrad": dict(gem("wgrad"), accum="default (f16 slices)"),
+             "wgrad_fp8_slices_opt_in": dict(gem("wgrad_fp8_slices_opt_in"),
+                                             note="FP8 slice sums: outside the bf16 tolerance in "
+                                                  "rare cancelling elements; not the default")}
+    cfg = {"workload": "Qwen3-8B decoder block linears, FP8 backward (Dgrad + Wgrad), 8192 "
+                       "tokens", "tokens": T, "gemms": [[l["name"], l["N"], l["K"]] for l in L],
+           "scales": args.scales}
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline_backward(synth, T, min_seconds=10.0)
+        cpu["gpu_over_oracle"] = value / cpu["value"]
+    emit(args, value, "TFLOP/s", ms, cfg, roof, cpu, parts=parts, **gpu)
 
 
-def run_moe(args, torch, fq, synth, dev_name):
-    """Qwen3-30B-A3B MoE layer: act quant + grouped gate/up (2048->1536) and down (768->2048)."""
+def cpu_baseline_backward(synth, T, min_seconds=10.0):
+    """The oracle's FP8 backward (quantizers, Dgrad, Wgrad) of the o_proj-shaped linear
+    (4096 x 4096) over T tokens, repeated until `min_seconds`."""
+    import numpy as np
+    import torch
+
+    from oracle import backward as ob
+
+    bits = lambda t: t.contiguous().view(torch.int16).numpy().view(np.uint16)
+    N = K = 4096
+    elapsed, flops, reps = 0.0, 0, 0
+    while elapsed < min_seconds or reps == 0:
+        dy = bits(synth.act_bf16(T, N, seed=9600 + reps) * 0.01)
+        x = bits(synth.act_bf16(T, K, seed=9700 + reps))
+        w = bits(synth.weight_bf16(N, K, seed=9800 + reps, outlier_frac=0.001))
+        t0 = time.perf_counter()
+        ob.linear_backward_fp8(dy, x, w, out="bf16")
+        elapsed += time.perf_counter() - t0
+        flops += 2 * (2 * T * N * K)
+        reps += 1
+    return dict(value=flops / elapsed / 1e12, unit="TFLOP/s", cores=blas_threads(),
+                kind="oracle", seconds=elapsed,
+                sample=f"{reps} FP8 backward pass(es) of a 4096x4096 linear over {T} tokens "
+                       f"(quantizers, Dgrad and Wgrad, fp64 BLAS)")
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+
+        return int(max([p.get("num_threads", 1) for p in threadpool_info()] or [1]))
+    except Exception:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def run_moe(args, torch, fq, synth, gpu, quant_cpu):
+    """Qwen3-30B-A3B MoE layer (T = 4096 tokens, E = 128, top-8, Zipf(1.1)-routed): per step the
+    activation quantization and grouped GEMM of the expert gate/up (2048 -> 1536) and of the
+    expert down (768 -> 2048); the per-step re-quantization of all 256 expert weights is timed
+    as a part (one batched launch). value = GEMM TFLOP/s over the step; roofline = the grouped
+    GEMM kernel, every expert's weights read once (HBM-bound by max(flops / P, bytes / B))."""
     T, H, I, E, topk = 4096, 2048, 768, 128, 8
     counts = synth.moe_routing_counts(T, E, topk, seed=synth.seed_of(5, 0))
     off = synth.offsets_from_counts(counts).cuda()
@@ -915,7 +1232,12 @@ def run_moe(args, torch, fq, synth, dev_name):
         fq.quant_act(x2, xq2, sa2, scale=args.scales)
         tg.launch(lambda: fq.grouped_gemm(xq2, sa2, wq2, sw2, off, y=y2, accum=accum), b2)
 
-    ms = _timed(torch, step, args.steps, args.warmup, (tg,))
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    tg.reset()
+    marks = timed_steps(torch, step, args.steps, 0)
+    ms, spread = finish_marks(torch, marks)
     r = tg.result()
     tq = KernelTimer(torch)
     _timed(torch, lambda: tq.launch(lambda: fq.quant_weights(None, None, None, descs=wdescs,
@@ -926,17 +1248,70 @@ def run_moe(args, torch, fq, synth, dev_name):
     g_ms = r["avg_us"] * r["launches"] / 1e3 / max(1, args.steps)
     roof_us = 1e6 * (max(2 * M * (2 * I) * H / (FP8_PEAK_TFLOPS * 1e12), b1 / (HBM_PEAK_GBS * 1e9)) +
                      max(2 * M * H * I / (FP8_PEAK_TFLOPS * 1e12), b2 / (HBM_PEAK_GBS * 1e9)))
-    print(json.dumps({"workload": "Qwen3-30B-A3B MoE layer (T=4096, E=128, top-8, Zipf 1.1)",
-                      "scales": args.scales,
-                      "rows": M, "max_expert_rows": int(counts.max()), "ms_per_step": ms,
-                      "grouped_gemm": r, "grouped_tflops": flops / (g_ms * 1e-3) / 1e12,
-                      "grouped_roofline_us": roof_us,
-                      "grouped_frac_roofline": roof_us / (1e3 * g_ms),
-                      "expert_requant": dict(rq, bytes=wq_bytes, frac_hbm=rq["gbs"] / HBM_PEAK_GBS,
-                                             what="all 2 x 128 expert weights, one batched launch"),
-                      "roofline_rule": "per GEMM max(2MNK / 5.0 PFLOP/s, bytes / 8 TB/s), every "
-                                       "expert's weights read once",
-                      "gpu": dev_name}), flush=True)
+    value = flops / (ms * 1e-3) / 1e12
+    roof = roof_hbm("grouped_big_kernel", (b1 + b2) / 2, r["avg_us"],
+                    "activation codes + scales + every expert's weight codes and block scales "
+                    "once + bf16 output",
+                    "one grouped GEMM (gate/up or down; average of the two)")
+    roof["frac_roofline"] = roof_us / (1e3 * g_ms)
+    roof["roofline_rule"] = ("per GEMM max(2MNK / 5.0 PFLOP/s, bytes / 8 TB/s), every expert's "
+                             "weights read once")
+    cfg = {"workload": "Qwen3-30B-A3B MoE layer (T=4096, E=128, top-8, Zipf 1.1 routing)",
+           "tokens": T, "experts": E, "top_k": topk, "routed_rows": M,
+           "max_expert_rows": int(counts.max()), "gemms": [["gate_up", 2 * I, H], ["down", H, I]],
+           "scales": args.scales}
+    parts = {"grouped_gemm": dict(r, tflops=flops / (g_ms * 1e-3) / 1e12, roofline_us=roof_us,
+                                  frac_roofline=roof_us / (1e3 * g_ms)),
+             "expert_requant": dict(rq, bytes=wq_bytes, frac_hbm=rq["gbs"] / HBM_PEAK_GBS,
+                                    what="all 2 x 128 expert weights, one batched launch")}
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline_moe(synth, counts, min_seconds=10.0)
+        cpu["gpu_over_oracle"] = value / cpu["value"]
+    emit(args, value, "TFLOP/s", ms, cfg, roof, cpu, ms_per_step_p10_p50_p90=spread,
+         parts=parts, **gpu)
+
+
+def cpu_baseline_moe(synth, counts, min_seconds=10.0):
+    """The oracle on a sample of the MoE layer: 16 experts at a time (their Zipf-routed row
+    counts), activation quantization and grouped gate/up and down GEMMs, cycling through the
+    experts until `min_seconds` (expert weights quantized beforehand, not timed)."""
+    import numpy as np
+    import torch
+
+    from oracle import gemm as og
+    from oracle import quant as oq
+
+    bits = lambda t: t.contiguous().view(torch.int16).numpy().view(np.uint16)
+    H, I, G = 2048, 768, 16
+    elapsed, flops, groups = 0.0, 0, 0
+    while elapsed < min_seconds or groups == 0:
+        e0 = (groups * G) % len(counts)
+        c = [int(v) for v in counts[e0:e0 + G]]
+        m = sum(c)
+        off = np.zeros(len(c) + 1, np.int32)
+        off[1:] = np.cumsum(c)
+        w1 = bits(synth.weight_bf16(2 * I, H, seed=4300 + groups, batch=len(c)))
+        w2 = bits(synth.weight_bf16(H, I, seed=4400 + groups, batch=len(c)))
+        q1 = [oq.quant_weight_blk128(w1[e]) for e in range(len(c))]
+        q2 = [oq.quant_weight_blk128(w2[e]) for e in range(len(c))]
+        x1 = bits(synth.act_bf16(m, H, seed=4500 + groups))
+        x2 = bits(synth.act_bf16(m, I, seed=4600 + groups))
+        t0 = time.perf_counter()
+        xq1, sa1 = oq.quant_act_tok128(x1)
+        og.grouped_gemm_blockscaled(xq1, sa1, np.stack([a for a, _ in q1]),
+                                    np.stack([b for _, b in q1]), off, out="bf16")
+        xq2, sa2 = oq.quant_act_tok128(x2)
+        og.grouped_gemm_blockscaled(xq2, sa2, np.stack([a for a, _ in q2]),
+                                    np.stack([b for _, b in q2]), off, out="bf16")
+        elapsed += time.perf_counter() - t0
+        flops += 2 * m * (2 * I) * H + 2 * m * H * I
+        groups += 1
+    return dict(value=flops / elapsed / 1e12, unit="TFLOP/s", cores=blas_threads(),
+                kind="oracle", seconds=elapsed,
+                sample=f"{groups} groups of {G} experts with their routed rows: activation "
+                       f"quantization + grouped gate/up and down GEMMs (fp64 BLAS); expert "
+                       f"weight quantization not timed")
 
 
 if __name__ == "__main__":

@@ -9,6 +9,7 @@ decode GEMM with the activation quantization fused in. Tensors live on the GPU; 
 
 from ._lib import (  # noqa: F401
     EXPORTED,
+    FP8RL_ACCUM_AUTO,
     FP8RL_ACCUM_F16,
     FP8RL_ACCUM_FP8,
     FP8RL_ACCUM_MX,

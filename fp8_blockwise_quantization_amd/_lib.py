@@ -9,7 +9,10 @@ cannot be loaded, every call raises.
 
 from __future__ import annotations
 
+import contextlib
 import ctypes
+import functools
+import inspect
 import os
 import threading
 
@@ -22,6 +25,7 @@ FP8RL_OUT_F32 = 1
 FP8RL_ACCUM_FP8 = 0
 FP8RL_ACCUM_F16 = 1
 FP8RL_ACCUM_MX = 2
+FP8RL_ACCUM_AUTO = 3
 FP8RL_SCALE_FP32 = 0
 FP8RL_SCALE_POW2 = 1
 FP8RL_OP_GEMM = 0
@@ -174,6 +178,33 @@ def _stream(stream) -> int:
     return int(stream)
 
 
+@contextlib.contextmanager
+def _on_stream(stream):
+    """Make `stream` torch's current stream while a binding runs, so that the tensors it
+    allocates (outputs, temporary workspaces) and the workspace header's zero fill are ordered on
+    the stream the kernels run on, and the caching allocator hands a freed temporary to another
+    allocation only behind that stream's work."""
+    if stream is None:
+        yield
+        return
+    s = stream if isinstance(stream, torch.cuda.Stream) else torch.cuda.ExternalStream(int(stream))
+    with torch.cuda.stream(s):
+        yield
+
+
+def _allocs_on_stream(fn):
+    """Run `fn` under _on_stream of its `stream` argument (keyword or positional)."""
+    idx = list(inspect.signature(fn).parameters).index("stream")
+
+    @functools.wraps(fn)
+    def wrapper(*args, **kwargs):
+        stream = kwargs["stream"] if "stream" in kwargs else (args[idx] if len(args) > idx else None)
+        with _on_stream(stream):
+            return fn(*args, **kwargs)
+
+    return wrapper
+
+
 def _ptr(t: torch.Tensor | None) -> int | None:
     return None if t is None else t.data_ptr()
 
@@ -200,6 +231,7 @@ def _dense(t: torch.Tensor, name: str, dtype: torch.dtype):
 # ---------------------------------------------------------------------------------------------
 
 
+@_allocs_on_stream
 def fp8rl_encode_e4m3_f32(v: torch.Tensor, out: torch.Tensor | None = None, stream=None):
     _dense(v, "v", torch.float32)
     if out is None:
@@ -210,6 +242,7 @@ def fp8rl_encode_e4m3_f32(v: torch.Tensor, out: torch.Tensor | None = None, stre
     return out
 
 
+@_allocs_on_stream
 def fp8rl_quant_weight_blk128(w: torch.Tensor, wq: torch.Tensor | None = None,
                               sw: torch.Tensor | None = None, stream=None, scale="fp32"):
     """bf16 W[N][K] -> (Wq uint8 [N][K], sw float32 [N/128][K/128]); scale 'fp32' or 'pow2'."""
@@ -273,6 +306,7 @@ def fp8rl_quant_weight_blk128_batched_ex(ws, wqs, sws, scale_fmt=FP8RL_SCALE_FP3
                                              scale=scale_fmt)
 
 
+@_allocs_on_stream
 def fp8rl_quant_act_tok128(x: torch.Tensor, xq: torch.Tensor | None = None,
                            sa: torch.Tensor | None = None, stream=None, scale="fp32"):
     """bf16 X[M][K] -> (Xq uint8 [M][K], sa float32 [M][K/128]); scale 'fp32' or 'pow2'."""
@@ -315,17 +349,18 @@ def new_workspace(nbytes: int, device) -> torch.Tensor:
     return ws
 
 
-def _accum_code(accum, out_dtype) -> int:
-    """None picks FP8 matrix-core sums for bf16 output and f16 (float32-grade) ones for float32."""
-    if accum is None:
-        return FP8RL_ACCUM_FP8 if out_dtype == torch.bfloat16 else FP8RL_ACCUM_F16
+def _accum_code(accum, out_dtype=None) -> int:
+    """None leaves the choice to the library (FP8RL_ACCUM_AUTO: the form that meets the accuracy
+    contract for the call's output type and GEMM)."""
+    if accum is None or accum in ("auto", FP8RL_ACCUM_AUTO):
+        return FP8RL_ACCUM_AUTO
     if accum in ("fp8", FP8RL_ACCUM_FP8):
         return FP8RL_ACCUM_FP8
     if accum in ("f16", FP8RL_ACCUM_F16):
         return FP8RL_ACCUM_F16
     if accum in ("mx", FP8RL_ACCUM_MX):
         return FP8RL_ACCUM_MX
-    raise ValueError("accum must be None, 'fp8', 'f16' or 'mx'")
+    raise ValueError("accum must be None, 'auto', 'fp8', 'f16' or 'mx'")
 
 
 def _out_code(dtype) -> int:
@@ -336,6 +371,7 @@ def _out_code(dtype) -> int:
     raise TypeError("output dtype must be torch.bfloat16 or torch.float32")
 
 
+@_allocs_on_stream
 def fp8rl_gemm_w8a8_blockscaled(xq, sa, wq, sw, out_dtype=torch.bfloat16, y=None,
                                 workspace=None, stream=None, accum=None):
     """Y[M][N] = blockscaled Xq Wq^T (bf16 or float32)."""
@@ -362,6 +398,7 @@ def fp8rl_gemm_w8a8_blockscaled(xq, sa, wq, sw, out_dtype=torch.bfloat16, y=None
     return y
 
 
+@_allocs_on_stream
 def fp8rl_gemm_w8a8_rowscaled(aq, sa, bq, sb, out_dtype=torch.bfloat16, y=None, workspace=None,
                               stream=None, accum=None):
     """Y[M][N] = sum over 128-wide K slices of sa[m][kb] sb[n][kb] (Aq Bq^T)_kb: both operands
@@ -388,6 +425,7 @@ def fp8rl_gemm_w8a8_rowscaled(aq, sa, bq, sb, out_dtype=torch.bfloat16, y=None, 
     return y
 
 
+@_allocs_on_stream
 def fp8rl_gemm_w8a8_fused_act_quant(x, wq, sw, out_dtype=torch.bfloat16, y=None, workspace=None,
                                     stream=None, accum=None, scale="fp32"):
     """Y[M][N] for bf16 X (M <= 64): the activation quantization (1x128 groups, `scale` format)
@@ -414,6 +452,7 @@ def fp8rl_gemm_w8a8_fused_act_quant(x, wq, sw, out_dtype=torch.bfloat16, y=None,
     return y
 
 
+@_allocs_on_stream
 def fp8rl_grouped_gemm_w8a8(xq, sa, wq, sw, expert_offsets, out_dtype=torch.bfloat16, y=None,
                             workspace=None, stream=None, accum=None):
     """Per-expert blockscaled GEMM over row segments given by device int32 ``expert_offsets``."""
@@ -483,6 +522,7 @@ def fp8rl_amax_bf16_batched(xs, amax: torch.Tensor, stream=None, descs=None):
     return amax
 
 
+@_allocs_on_stream
 def fp8rl_scale_from_amax(amax: torch.Tensor, scale: torch.Tensor | None = None, stream=None):
     """scale[i] = fp32(amax[i] / 448), 1 where amax[i] == 0."""
     _dense(amax, "amax", torch.float32)
@@ -496,6 +536,7 @@ def fp8rl_scale_from_amax(amax: torch.Tensor, scale: torch.Tensor | None = None,
     return scale
 
 
+@_allocs_on_stream
 def fp8rl_quant_bf16_per_tensor(x: torch.Tensor, scale: torch.Tensor, out: torch.Tensor | None = None,
                                 slot_mapping: torch.Tensor | None = None, stream=None):
     """Codes of x / scale (device scalar) into out[slot[r]] (or out[r]); returns out (uint8)."""
@@ -547,6 +588,7 @@ def fp8rl_quant_bf16_per_tensor_batched(xs=None, scales=None, outs=None, slots=N
 # ------------------------------------------------------------------ backward (transposed outputs)
 
 
+@_allocs_on_stream
 def fp8rl_quant_weight_blk128_t(w: torch.Tensor, wqt=None, swt=None, wq=None, sw=None,
                                 rowmajor: bool = False, scale="fp32", stream=None):
     """bf16 W[N][K] -> (WqT uint8 [K][N], swT float32 [K/128][N/128]), the block quantization of
@@ -575,6 +617,7 @@ def fp8rl_quant_weight_blk128_t(w: torch.Tensor, wqt=None, swt=None, wq=None, sw
     return wqt, swt, wq, sw
 
 
+@_allocs_on_stream
 def fp8rl_quant_act_colwise128(x: torch.Tensor, xtq=None, sat=None, xq=None, sa=None,
                                rowwise: bool = False, scale="fp32", stream=None):
     """bf16 X[M][K] (M % 128 == 0) -> (XtQ uint8 [K][M], st float32 [K][M/128]): 128x1 token

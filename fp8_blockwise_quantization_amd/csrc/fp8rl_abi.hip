@@ -34,11 +34,23 @@ int check_gemm_common(const uint8_t* xq, const float* sa, const uint8_t* wq, con
   return FP8RL_OK;
 }
 
+// The accumulation form a GEMM call runs with, or -1 for an invalid request. FP8RL_ACCUM_AUTO
+// resolves to the form that meets the accuracy contract (FP8 slice sums for bf16 output, f16 ones
+// for float32 output and for every row-scaled call); the FP8 and MX forms are refused with float32
+// output, whose tolerance their in-slice truncation does not meet.
+int resolve_accum(int accum, int y_dtype, bool rowscaled) {
+  if (accum == FP8RL_ACCUM_AUTO)
+    return (y_dtype == FP8RL_OUT_F32 || rowscaled) ? FP8RL_ACCUM_F16 : FP8RL_ACCUM_FP8;
+  if (accum != FP8RL_ACCUM_FP8 && accum != FP8RL_ACCUM_F16 && accum != FP8RL_ACCUM_MX) return -1;
+  if (y_dtype == FP8RL_OUT_F32 && accum != FP8RL_ACCUM_F16) return -1;
+  return accum;
+}
+
 }  // namespace
 
 extern "C" {
 
-int fp8rl_version(void) { return 100; }  // 0.1.0
+int fp8rl_version(void) { return 200; }  // 0.2.0
 
 const char* fp8rl_status_string(int s) {
   switch (s) {
@@ -386,8 +398,8 @@ int gemm_common(const uint8_t* xq, const float* sa, const uint8_t* wq, const flo
   if (int s = check_dims(M, N, K)) return s;
   if (M == 0) return FP8RL_OK;
   if (int s = check_gemm_common(xq, sa, wq, sw, N, K, y, y_dtype, ld_y)) return s;
-  if (accum != FP8RL_ACCUM_FP8 && accum != FP8RL_ACCUM_F16 && accum != FP8RL_ACCUM_MX)
-    return FP8RL_ERR_ARG;
+  accum = resolve_accum(accum, y_dtype, rowb);
+  if (accum < 0) return FP8RL_ERR_ARG;
   if (((M + 127) / 128) * (N / 64) >= (int64_t{1} << 22)) return FP8RL_ERR_SHAPE;  // grid limit
   const fp8rl::GemmPlan plan = fp8rl::plan_gemm(M, N, K, rowb);
   if (plan.workspace_bytes > 0) {
@@ -419,8 +431,8 @@ int fp8rl_gemm_w8a8_fused_act_quant(const uint16_t* x, int64_t ld_x, const uint8
   if (ld_x < K || ld_x > kMaxDim) return FP8RL_ERR_SHAPE;
   if (y_dtype != FP8RL_OUT_BF16 && y_dtype != FP8RL_OUT_F32) return FP8RL_ERR_DTYPE;
   if (ld_y < N) return FP8RL_ERR_SHAPE;
-  if (accum != FP8RL_ACCUM_FP8 && accum != FP8RL_ACCUM_F16 && accum != FP8RL_ACCUM_MX)
-    return FP8RL_ERR_ARG;
+  accum = resolve_accum(accum, y_dtype, false);
+  if (accum < 0) return FP8RL_ERR_ARG;
   if (scale_fmt != FP8RL_SCALE_FP32 && scale_fmt != FP8RL_SCALE_POW2) return FP8RL_ERR_ARG;
   if (accum == FP8RL_ACCUM_MX && scale_fmt != FP8RL_SCALE_POW2) return FP8RL_ERR_ARG;
   const int64_t ybytes = y_dtype == FP8RL_OUT_F32 ? 4 : 2;
@@ -455,8 +467,8 @@ int fp8rl_grouped_gemm_w8a8(const uint8_t* xq, const float* sa, const uint8_t* w
   if (M_total == 0) return FP8RL_OK;
   if (!expert_offsets) return FP8RL_ERR_NULL;
   if (int s = check_gemm_common(xq, sa, wq, sw, N, K, y, y_dtype, N)) return s;
-  if (accum != FP8RL_ACCUM_FP8 && accum != FP8RL_ACCUM_F16 && accum != FP8RL_ACCUM_MX)
-    return FP8RL_ERR_ARG;
+  accum = resolve_accum(accum, y_dtype, false);
+  if (accum < 0) return FP8RL_ERR_ARG;
   if (!aligned(expert_offsets, 4)) return FP8RL_ERR_ALIGN;
   if (((M_total + 127) / 128 + E) * (N / 128) >= (int64_t{1} << 22)) return FP8RL_ERR_SHAPE;
   if ((int64_t)E * N * K >= (int64_t{1} << 40)) return FP8RL_ERR_SHAPE;

@@ -382,15 +382,21 @@ __device__ __forceinline__ const void* uniform_ptr(const void* p) {
   const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
   return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
 }
+// The LDS address goes to M0 through an explicit register constraint, so the compiler sets M0
+// itself and knows it is read here. The compiler cannot see the instruction inside the asm, so it
+// inserts none of the wait states the hardware needs before it: the base address SGPRs are often
+// written by v_readfirstlane right before (a VALU write of an SGPR that a vector-memory
+// instruction reads needs 5 wait states; without them the DMA can take a stale base address and
+// fault), and M0 by an SALU instruction (1 wait state). s_nop 4 provides the 5 in every case.
 __device__ __forceinline__ void dma16(const void* base, uint32_t off, const uint8_t* lds) {
   const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_offset(lds));
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
-               :: "s"(m0v), "v"(off), "s"(uniform_ptr(base)) : "memory", "m0");
+  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(off), "s"(uniform_ptr(base)), "{m0}"(m0v) : "memory");
 }
 __device__ __forceinline__ void dma4(const void* base, uint32_t off, const uint8_t* lds) {
   const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_offset(lds));
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2"
-               :: "s"(m0v), "v"(off), "s"(uniform_ptr(base)) : "memory", "m0");
+  asm volatile("s_nop 4\n\tglobal_load_lds_dword %0, %1"
+               :: "v"(off), "s"(uniform_ptr(base)), "{m0}"(m0v) : "memory");
 }
 
 // Per-lane byte offsets of this lane's DMA sources within a K slice (computed once per tile).
@@ -1056,6 +1062,16 @@ __global__ __launch_bounds__(T::NT) void gemm_decode_kernel(GemmArgs p) {
 #pragma unroll
   for (int j = 0; j < T::MT * 4; ++j)
     __hip_atomic_store(mine + j * 64, vals[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // Ordering of the hand-off. Every access to the partials and the counter is an agent-scope
+  // atomic: the partial stores are write-through stores (sc1) that complete only once they have
+  // reached the level all XCDs share, and the read-back loads (sc1) are served from that level,
+  // never from a stale L2 line. The s_waitcnt below completes this thread's partial stores
+  // before the barrier, so every partial of this split is visible agent-wide before thread 0
+  // issues the arrival RMW; the last arrival issues its loads only after that RMW has returned
+  // (its result reaches the other threads through LDS and a barrier). The RMW is therefore
+  // relaxed: release / acquire ordering at agent scope would add a writeback of the whole L2 and
+  // invalidations of it to every arrival, which doubled the decode GEMMs' time (measured) and
+  // orders nothing the write-through atomics do not already order.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (tid == 0) {
@@ -1083,6 +1099,7 @@ __global__ __launch_bounds__(T::NT) void gemm_decode_kernel(GemmArgs p) {
       for (int j = 0; j < T::MT * 4; ++j) vals[j] = s0 + u < S ? vals[j] + v4[u][j] : vals[j];
   }
   store_y();
+  // re-arm for the next call (ordered before it by the kernel boundary)
   if (tid == 0)
     __hip_atomic_store(p.counters + t, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

@@ -82,29 +82,42 @@ typedef enum {
 
 /*
  * How the matrix cores form the sum over one 128-wide K slice (the per-slice scaling, the float32
- * accumulation across slices and the final rounding are the same for both):
+ * accumulation across slices and the final rounding are the same for all of them):
  *   FP8RL_ACCUM_FP8  the FP8 matrix-core instruction (v_mfma_f32_16x16x128_f8f6f4). Its internal
  *                    adder aligns the slice's products to the largest one and keeps about 15 bits
  *                    below it (measured on gfx950), comparable to the narrow FP8 accumulators the
  *                    Unified FP8 blog reports for Hopper tensor cores ("Tensor Core" hardware
  *                    table); promoting every 128-wide slice to float32 bounds the loss to one
- *                    slice. Full FP8 rate.
+ *                    slice. Full FP8 rate. Accepted with bf16 output only (FP8RL_ERR_ARG with
+ *                    float32 output: its error is far above float32 rounding).
  *   FP8RL_ACCUM_F16  the same E4M3 codes widened exactly to f16 and summed by f16 matrix-core
  *                    instructions, whose adder keeps float32-level precision. Half the FP8 rate.
- */
-typedef enum { FP8RL_ACCUM_FP8 = 0, FP8RL_ACCUM_F16 = 1, FP8RL_ACCUM_MX = 2 } fp8rl_accum;
-/*
  *   FP8RL_ACCUM_MX   for power-of-two scales (FP8RL_SCALE_POW2): the block scales are applied by
  *                    the block-scaled FP8 matrix-core instruction (v_mfma_scale_f32_16x16x128_f8f6f4,
  *                    one E8M0 exponent per 32 K-values of a row; gfx950 has the E8M0 scaling units
  *                    the NeMo RL blog and the Unified FP8 blog say Hopper lacks), which also adds the
  *                    running float32 sum, so no per-slice float32 rescale is needed. Each slice sum
- *                    has the FP8 form's precision. Every sa and sw must be a power of two in
- *                    [2^-127, 2^127]; the fraction bits of any other scale are ignored (the scale
- *                    is taken as 2^floor(log2 s)). Shapes without such a kernel (64 < M < 1024,
+ *                    has the FP8 form's precision, so like FP8RL_ACCUM_FP8 it is accepted with
+ *                    bf16 output only. Every sa and sw must be a power of two in [2^-127, 2^127]
+ *                    (what the FP8RL_SCALE_POW2 quantizers produce); for any other scale value
+ *                    the result is undefined (the scales are not inspected on the host, which
+ *                    would need a synchronization). Shapes without such a kernel (64 < M < 1024,
  *                    or an odd K/128 at M <= 64) compute as FP8RL_ACCUM_FP8, which gives the same
  *                    results for power-of-two scales.
+ *   FP8RL_ACCUM_AUTO the form that keeps the result within the library's accuracy contract
+ *                    (elementwise |y - exact| <= 2^-7 |exact| + 1e-3 rms(exact) for bf16 output,
+ *                    <= 1e-5 rms(exact) for float32 output, exact = the float64 sum over the
+ *                    dequantized operands): FP8RL_ACCUM_FP8 for the blockscaled, fused and grouped
+ *                    GEMMs with bf16 output; FP8RL_ACCUM_F16 for float32 output, and for the
+ *                    row-scaled (weight-gradient) GEMM, whose long token sums can cancel far below
+ *                    their slices' largest products. Never FP8RL_ACCUM_MX (ask for it).
  */
+typedef enum {
+  FP8RL_ACCUM_FP8 = 0,
+  FP8RL_ACCUM_F16 = 1,
+  FP8RL_ACCUM_MX = 2,
+  FP8RL_ACCUM_AUTO = 3
+} fp8rl_accum;
 
 /*
  * Scale format of the quantizers (the _ex entry points):
@@ -241,7 +254,9 @@ int fp8rl_quant_act_colwise128(const uint16_t* x, int64_t M, int64_t K, int64_t 
  *   xq, sa : activation codes [M][K] (pitch K) and scales [M][K/128]
  *   wq, sw : weight codes [N][K] (pitch K) and scales [N/128][K/128]
  *   y      : output [M][ld_y] (ld_y >= N) of type y_dtype
- *   accum  : FP8RL_ACCUM_FP8, FP8RL_ACCUM_F16 or FP8RL_ACCUM_MX (see fp8rl_accum)
+ *   accum  : FP8RL_ACCUM_AUTO (the form that meets the accuracy contract), FP8RL_ACCUM_FP8,
+ *            FP8RL_ACCUM_F16 or FP8RL_ACCUM_MX (see fp8rl_accum); FP8 and MX with float32 output
+ *            return FP8RL_ERR_ARG
  *   workspace, workspace_bytes: scratch of at least fp8rl_workspace_bytes(FP8RL_OP_GEMM, M, N, K, 0)
  *            bytes (device, 16-byte aligned; may be NULL when that size is 0). Its first
  *            FP8RL_WORKSPACE_HEADER_BYTES bytes hold arrival counters of the K-split reduction:
@@ -286,7 +301,11 @@ int fp8rl_gemm_w8a8_fused_act_quant(const uint16_t* x, int64_t ld_x, const uint8
  *   Y[m][n] = sum_kb sa[m][kb] * sb[n][kb] * sum_{k in slice kb} dec(Aq[m][k]) * dec(Bq[n][k])
  * i.e. fp8rl_gemm_w8a8_blockscaled with one B scale per row and slice, sb [N][K/128], instead of
  * one per 128x128 block. Same arguments, rules, accumulation modes (with FP8RL_ACCUM_MX every sb
- * must be a power of two) and determinism; the workspace is sized by
+ * must be a power of two) and determinism. FP8RL_ACCUM_AUTO picks the f16 slice sums for both
+ * output types here: a weight gradient sums thousands of tokens whose slices can cancel far below
+ * their largest products, and the FP8 and MX forms' in-slice truncation (relative to that largest
+ * product) can then exceed the bf16 tolerance; they stay available on request for bf16 output.
+ * The workspace is sized by
  * fp8rl_workspace_bytes(FP8RL_OP_GEMM_ROWSCALED, M, N, K, 0).
  */
 int fp8rl_gemm_w8a8_rowscaled(const uint8_t* aq, const float* sa, const uint8_t* bq,

@@ -51,8 +51,25 @@ def test_scale_format_and_accum_validation(L):
     assert L.fp8rl_quant_weight_blk128_batched_ex(None, 1, 1, None) == ENULL
     assert L.fp8rl_quant_weight_blk128_batched_ex(None, 1, 3, None) == EARG
     g = L.fp8rl_gemm_w8a8_blockscaled
-    assert g(A, A, A, A, 64, 256, 256, A, 0, 256, 3, None, 0, None) == EARG
+    assert g(A, A, A, A, 64, 256, 256, A, 0, 256, 4, None, 0, None) == EARG
+    assert g(A, A, A, A, 64, 256, 256, A, 0, 256, -1, None, 0, None) == EARG
     assert g(A, A, A, A, 0, 256, 256, A, 0, 256, 2, None, 0, None) == OK
+    # FP8 and MX slice sums are refused with float32 output (y_dtype 1), on every GEMM entry
+    # point, before any HIP call; F16 and AUTO are not refused by that check
+    for acc in (0, 2):
+        assert g(A, A, A, A, 64, 256, 256, A, 1, 256, acc, None, 0, None) == EARG
+        assert L.fp8rl_gemm_w8a8_rowscaled(A, A, A, A, 64, 256, 256, A, 1, 256, acc, None, 0,
+                                           None) == EARG
+        assert L.fp8rl_grouped_gemm_w8a8(A, A, A, A, A, 2, 64, 256, 256, A, 1, acc, None, 0,
+                                         None) == EARG
+        assert L.fp8rl_gemm_w8a8_fused_act_quant(A, 256, A, A, 64, 256, 256, A, 1, 256, acc, 1,
+                                                 None, 0, None) == EARG
+    # accepted combinations reach the later checks (here: the missing workspace of a split-K
+    # decode shape)
+    need = L.fp8rl_workspace_bytes(0, 64, 1024, 4096, 0)
+    assert need > 0
+    for acc, out in ((3, 0), (3, 1), (1, 1), (0, 0), (2, 0)):
+        assert g(A, A, A, A, 64, 1024, 4096, A, out, 1024, acc, None, 0, None) == EWS
 
 
 def test_status_strings_and_version(L):
@@ -168,7 +185,7 @@ def test_backward_validation(L):
     assert g(A, A, A, A, 0, 256, 256, A, 0, 256, 0, None, 0, None) == OK
     assert g(A, A, A, A, 64, 256, 200, A, 0, 256, 0, None, 0, None) == ESHAPE
     assert g(A, A, A, None, 64, 256, 256, A, 0, 256, 0, None, 0, None) == ENULL
-    assert g(A, A, A, A, 64, 256, 256, A, 0, 256, 3, None, 0, None) == EARG
+    assert g(A, A, A, A, 64, 256, 256, A, 0, 256, 4, None, 0, None) == EARG
     # row-scaled B never takes the decode path: its small-M plan has its own workspace rule
     ws_row = L.fp8rl_workspace_bytes(2, 64, 4096, 4096, 0)
     ws_blk = L.fp8rl_workspace_bytes(0, 64, 4096, 4096, 0)
@@ -202,7 +219,7 @@ def test_gemm_validation(L):
     assert call(M=-1) == ESHAPE
     assert call(ldy=128) == ESHAPE
     assert call(dt=5) == EDTYPE
-    assert call(acc=3) == EARG  # (2 is FP8RL_ACCUM_MX)
+    assert call(acc=4) == EARG  # (2 is FP8RL_ACCUM_MX, 3 FP8RL_ACCUM_AUTO)
     assert call(acc=-1) == EARG
     assert call(xq=A + 1) == EALIGN
     assert call(ldy=260) == EALIGN  # 520-byte bf16 pitch
@@ -230,7 +247,7 @@ def test_fused_act_gemm_validation(L):
     assert call(M=65) == ESHAPE  # decode shapes only
     assert call(K=384, ldx=384) == ESHAPE  # odd number of K slices
     assert call(dt=2) == EDTYPE
-    assert call(acc=3) == EARG
+    assert call(acc=4) == EARG
     assert call(sf=2) == EARG
     assert call(acc=2, sf=0) == EARG  # matrix-core scaling needs power-of-two scales
     assert call(x=A + 2) == EALIGN

@@ -108,11 +108,8 @@ def _check_rowscaled(M, N, K, out, accum, seed=0, pow2=False):
     if out == "bf16":
         ref = oq_bf16(ob.gemm_rowscaled(aq, sa, bq, sb, out="bf16"))
         return assert_gemm_close(got, ref, ref64, "bf16", f"{M}x{N}x{K}")
-    if accum == "f16":
-        return assert_gemm_close(got, ref64.astype(np.float32).astype(np.float64), ref64, "f32",
-                                 f"{M}x{N}x{K}")
-    bound = fp8_slice_bound(aq, sa, bq, sb, b_rows=True) + 2.0 ** -22 * np.abs(ref64)
-    return assert_within(got, ref64, bound, f"{M}x{N}x{K} fp8 slices")
+    return assert_gemm_close(got, ref64.astype(np.float32).astype(np.float64), ref64, "f32",
+                             f"{M}x{N}x{K}")
 
 
 def oq_bf16(bits):
@@ -122,15 +119,44 @@ def oq_bf16(bits):
 
 @pytest.mark.parametrize("M,N,K", [(1, 256, 256), (64, 1024, 1024), (200, 384, 512), (640, 512, 1024),
                                    (1024, 1024, 2048), (4096, 4096, 1024), (1100, 640, 640)])
-@pytest.mark.parametrize("accum", ["fp8", "mx"])
+@pytest.mark.parametrize("accum", [None, "fp8", "mx"])
 def test_rowscaled_gemm_bf16(M, N, K, accum):
     _check_rowscaled(M, N, K, "bf16", accum, pow2=accum == "mx")
 
 
-@pytest.mark.parametrize("M,N,K", [(64, 256, 512), (512, 512, 512), (1024, 512, 1024)])
-@pytest.mark.parametrize("accum", ["fp8", "f16", "mx"])
+@pytest.mark.parametrize("M,N,K", [(64, 256, 512), (512, 512, 512), (1024, 512, 1024),
+                                   (4096, 1024, 2048)])
+@pytest.mark.parametrize("accum", [None, "f16"])
 def test_rowscaled_gemm_f32(M, N, K, accum):
-    _check_rowscaled(M, N, K, "f32", accum, seed=1, pow2=accum == "mx")
+    _check_rowscaled(M, N, K, "f32", accum, seed=1)
+
+
+@pytest.mark.parametrize("accum", ["fp8", "mx"])
+def test_rowscaled_fp8_and_mx_refused_with_float32_output(accum):
+    aq, sa, bq, sb = _rowscaled_operands(64, 256, 512, 2, accum == "mx")
+    t = lambda v: torch.from_numpy(np.ascontiguousarray(v)).cuda()
+    with pytest.raises(fq.Fp8rlError) as e:
+        fq.gemm_rowscaled(t(aq), t(sa), t(bq), t(sb), out_dtype=torch.float32, accum=accum)
+    assert e.value.status == 7  # FP8RL_ERR_ARG
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 512, 1024), (1024, 384, 2048)])
+def test_rowscaled_fp8_slices_random_operands_derived_bound(M, N, K):
+    """Stress test of the opt-in FP8 slice sums of the row-scaled GEMM (bf16 output): random
+    full-range codes with scales spread over 2^24, against the FP8 form's derived bound."""
+    rng = np.random.default_rng(4400 + M)
+    aq = rng.integers(0, 256, size=(M, K)).astype(np.uint8)
+    bq = rng.integers(0, 256, size=(N, K)).astype(np.uint8)
+    aq[(aq & 0x7F) == 0x7F] = 0x7E
+    bq[(bq & 0x7F) == 0x7F] = 0xFE
+    sa = (2.0 ** rng.uniform(-20, 4, size=(M, K // 128))).astype(np.float32)
+    sb = (2.0 ** rng.uniform(-20, 4, size=(N, K // 128))).astype(np.float32)
+    t = lambda v: torch.from_numpy(np.ascontiguousarray(v)).cuda()
+    y = fq.gemm_rowscaled(t(aq), t(sa), t(bq), t(sb), out_dtype=torch.bfloat16, accum="fp8")
+    torch.cuda.synchronize()
+    ref64 = ob.gemm_rowscaled(aq, sa, bq, sb, out="f64")
+    bound = fp8_slice_bound(aq, sa, bq, sb, b_rows=True) + 2.0 ** -8 * np.abs(ref64)
+    assert_within(gemm_out_to_f64(y), ref64, bound, f"rowscaled fp8 slices {M}x{N}x{K}")
 
 
 def test_linear_backward_end_to_end():
@@ -145,19 +171,13 @@ def test_linear_backward_end_to_end():
     xt, s_xt, _, _ = fq.quant_colwise(x.cuda())
     wqt, swt, _, _ = fq.quant_weight_t(w.cuda())
     dx = fq.gemm(dyq, s_dy, wqt, swt)
-    dw16 = fq.gemm_rowscaled(dyt, s_dyt, xt, s_xt, accum="f16")
-    dw8 = fq.gemm_rowscaled(dyt, s_dyt, xt, s_xt, accum="fp8")
+    dw = fq.gemm_rowscaled(dyt, s_dyt, xt, s_xt)  # the library's default form (f16 slice sums)
     torch.cuda.synchronize()
     rdx, rdw = ob.linear_backward_fp8(bits16(dy), bits16(x), bits16(w), out="f64")
     rdx_b, rdw_b = ob.linear_backward_fp8(bits16(dy), bits16(x), bits16(w), out="bf16")
     assert_gemm_close(gemm_out_to_f64(dx), oq_bf16(rdx_b), rdx, "bf16", "dX")
     # Wgrad sums over the tokens, where activation outlier channels make single slices large
-    # against the result: with float32-grade slice sums the GEMM contract holds; the FP8 slice
-    # sums are held to their derived bound (plus the bf16 rounding of the output)
-    assert_gemm_close(gemm_out_to_f64(dw16), oq_bf16(rdw_b), rdw, "bf16", "dW f16 slices")
-    # the bound from the oracle's own 128x1-group operands (the GPU's are checked equal to them
-    # elsewhere; no expected value is taken from the GPU path)
-    r_dyt, r_sdyt = ob.quant_colwise128(bits16(dy))
-    r_xt, r_sxt = ob.quant_colwise128(bits16(x))
-    bound = fp8_slice_bound(r_dyt, r_sdyt, r_xt, r_sxt, b_rows=True) + 2.0 ** -8 * np.abs(rdw)
-    assert_within(gemm_out_to_f64(dw8), rdw, bound, "dW fp8 slices")
+    # against the result; the default form's float32-grade slice sums keep the bf16 contract.
+    # (A float32 dW is not held to 1e-5 rms here: where outlier rows of dY meet outlier columns
+    # of X an element is ~256x the rms, and one float32 ulp there already exceeds that bound.)
+    assert_gemm_close(gemm_out_to_f64(dw), oq_bf16(rdw_b), rdw, "bf16", "dW")

@@ -47,12 +47,7 @@ def _check(x: torch.Tensor, wq, sw, what, scale="fp32", outs=("bf16", "f32"), ac
             ref = og.bf16_bits_to_f64(og.round_f64_to_bf16_bits(ref64))
         else:
             ref = ref64.astype(np.float32).astype(np.float64)
-        if out == "f32" and accum in ("fp8", "mx"):
-            # FP8 slice sums with float32 output: the FP8 form's derived bound
-            bound = fp8_slice_bound(xq, sa, wq, sw)
-            worst[out] = assert_within(got, ref64, bound + 1e-6 * np.abs(ref64), what)
-        else:
-            worst[out] = assert_gemm_close(got, ref, ref64, out, what)
+        worst[out] = assert_gemm_close(got, ref, ref64, out, what)
         assert torch.equal(y, y_unfused), f"{what} {out}: fused and unfused results differ"
     print(f"    worst err/bound {worst}", flush=True)
 
@@ -99,11 +94,22 @@ def test_edge_rows():
 def test_power_of_two_scales_both_accumulations():
     x = synth.act_bf16(64, 4096, seed=synth.seed_of(65, 0)).cuda()
     wq, sw = _weights(2048, 4096, synth.seed_of(65, 1), scale="pow2")
-    _check(x, wq, sw, "pow2, fp8 slices", scale="pow2", accum="fp8")
-    _check(x, wq, sw, "pow2, matrix-core scales", scale="pow2", accum="mx")
+    _check(x, wq, sw, "pow2, fp8 slices", scale="pow2", accum="fp8", outs=("bf16",))
+    _check(x, wq, sw, "pow2, matrix-core scales", scale="pow2", accum="mx", outs=("bf16",))
+    _check(x, wq, sw, "pow2, default accumulation", scale="pow2")
     x = synth.act_bf16(5, 1024, seed=synth.seed_of(65, 2)).cuda()
     wq, sw = _weights(384, 1024, synth.seed_of(65, 3), scale="pow2")
-    _check(x, wq, sw, "pow2, matrix-core scales, M=5", scale="pow2", accum="mx")
+    _check(x, wq, sw, "pow2, matrix-core scales, M=5", scale="pow2", accum="mx", outs=("bf16",))
+
+
+@pytest.mark.parametrize("accum", ["fp8", "mx"])
+def test_fp8_and_mx_refused_with_float32_output(accum):
+    x = torch.zeros((4, 256), dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros((256, 256), dtype=torch.uint8, device="cuda")
+    sw = torch.ones((2, 2), dtype=torch.float32, device="cuda")
+    with pytest.raises(fq.Fp8rlError) as e:
+        fq.gemm_fused_act(x, w, sw, out_dtype=torch.float32, accum=accum, scale="pow2")
+    assert e.value.status == 7
 
 
 def test_f16_slices_float32_output():
