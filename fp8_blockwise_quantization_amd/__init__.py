@@ -26,6 +26,7 @@ from ._lib import (  # noqa: F401
     fp8rl_amax_bf16_batched,
     fp8rl_encode_e4m3_f32,
     fp8rl_gemm_w8a8_blockscaled,
+    fp8rl_gemm_w8a8_blockscaled_noalloc,
     fp8rl_gemm_w8a8_fused_act_quant,
     fp8rl_gemm_w8a8_rowscaled,
     fp8rl_grouped_gemm_w8a8,
@@ -41,6 +42,7 @@ from ._lib import (  # noqa: F401
     fp8rl_quant_weight_blk128_ex,
     fp8rl_scale_from_amax,
     WORKSPACE_HEADER_BYTES,
+    SCRATCH_BYTES,
     quant_descs,
     tensor_descs,
     weight_descs,
@@ -54,6 +56,7 @@ quant_weight = fp8rl_quant_weight_blk128
 quant_weights = fp8rl_quant_weight_blk128_batched
 quant_act = fp8rl_quant_act_tok128
 gemm = fp8rl_gemm_w8a8_blockscaled
+gemm_noalloc = fp8rl_gemm_w8a8_blockscaled_noalloc
 gemm_fused_act = fp8rl_gemm_w8a8_fused_act_quant
 grouped_gemm = fp8rl_grouped_gemm_w8a8
 encode_e4m3 = fp8rl_encode_e4m3_f32

@@ -114,6 +114,9 @@ def lib() -> ctypes.CDLL:
             "fp8rl_gemm_w8a8_rowscaled": (
                 ctypes.c_int,
                 [vp, vp, vp, vp, i64, i64, i64, vp, ctypes.c_int, i64, ctypes.c_int, vp, sz, vp]),
+            "fp8rl_gemm_w8a8_blockscaled_noalloc": (
+                ctypes.c_int,
+                [vp, vp, vp, vp, i64, i64, i64, vp, ctypes.c_int, i64, ctypes.c_int, vp]),
             "fp8rl_gemm_w8a8_fused_act_quant": (
                 ctypes.c_int,
                 [vp, i64, vp, vp, i64, i64, i64, vp, ctypes.c_int, i64, ctypes.c_int,
@@ -149,6 +152,7 @@ EXPORTED = (
     "fp8rl_quant_act_colwise128",
     "fp8rl_gemm_w8a8_rowscaled",
     "fp8rl_gemm_w8a8_fused_act_quant",
+    "fp8rl_gemm_w8a8_blockscaled_noalloc",
     "fp8rl_workspace_bytes",
     "fp8rl_status_string",
     "fp8rl_version",
@@ -395,6 +399,31 @@ def fp8rl_gemm_w8a8_blockscaled(xq, sa, wq, sw, out_dtype=torch.bfloat16, y=None
                                              _accum_code(accum, y.dtype), _ptr(workspace),
                                              ws_bytes, _stream(stream)),
            "fp8rl_gemm_w8a8_blockscaled")
+    return y
+
+
+SCRATCH_BYTES = 32 << 20  # FP8RL_SCRATCH_BYTES: the no-allocation GEMM's static scratch per device
+
+
+@_allocs_on_stream
+def fp8rl_gemm_w8a8_blockscaled_noalloc(xq, sa, wq, sw, y, stream=None, accum=None):
+    """Y = blockscaled Xq Wq^T into the caller's ``y`` (bf16 or float32), with the library's
+    static scratch instead of a workspace: the C call allocates nothing (neither does this
+    binding: ``y`` is required)."""
+    _dense(xq, "xq", torch.uint8)
+    _dense(wq, "wq", torch.uint8)
+    _dense(sa, "sa", torch.float32)
+    _dense(sw, "sw", torch.float32)
+    M, K = xq.shape
+    N = wq.shape[0]
+    if wq.shape[1] != K:
+        raise ValueError("K mismatch between xq and wq")
+    ld_y = _rows(y, "y", y.dtype)
+    _check(lib().fp8rl_gemm_w8a8_blockscaled_noalloc(_ptr(xq), _ptr(sa), _ptr(wq), _ptr(sw), M, N,
+                                                     K, _ptr(y), _out_code(y.dtype), ld_y,
+                                                     _accum_code(accum, y.dtype),
+                                                     _stream(stream)),
+           "fp8rl_gemm_w8a8_blockscaled_noalloc")
     return y
 
 

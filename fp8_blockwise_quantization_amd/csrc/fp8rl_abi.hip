@@ -62,6 +62,8 @@ const char* fp8rl_status_string(int s) {
     case FP8RL_ERR_WORKSPACE: return "workspace too small";
     case FP8RL_ERR_HIP: return "HIP kernel launch failed";
     case FP8RL_ERR_ARG: return "invalid argument";
+    case FP8RL_ERR_SCRATCH:
+      return "shape needs more GEMM scratch than the library's static buffer holds";
     default: return "unknown status";
   }
 }
@@ -418,6 +420,26 @@ int fp8rl_gemm_w8a8_blockscaled(const uint8_t* xq, const float* sa, const uint8_
                                 size_t workspace_bytes, void* stream) {
   return gemm_common(xq, sa, wq, sw, M, N, K, y, y_dtype, ld_y, accum, false, workspace,
                      workspace_bytes, stream);
+}
+
+int fp8rl_gemm_w8a8_blockscaled_noalloc(const uint8_t* xq, const float* sa, const uint8_t* wq,
+                                        const float* sw, int64_t M, int64_t N, int64_t K, void* y,
+                                        int y_dtype, int64_t ld_y, int accum, void* stream) {
+  if (int s = check_dims(M, N, K)) return s;
+  if (M == 0) return FP8RL_OK;
+  if (int s = check_gemm_common(xq, sa, wq, sw, N, K, y, y_dtype, ld_y)) return s;
+  accum = resolve_accum(accum, y_dtype, false);
+  if (accum < 0) return FP8RL_ERR_ARG;
+  if (((M + 127) / 128) * (N / 64) >= (int64_t{1} << 22)) return FP8RL_ERR_SHAPE;
+  const fp8rl::GemmPlan plan = fp8rl::plan_gemm(M, N, K, false);
+  static_assert(fp8rl::kScratchBytes == FP8RL_SCRATCH_BYTES, "scratch size in the header");
+  if (plan.workspace_bytes > fp8rl::kScratchBytes) return FP8RL_ERR_SCRATCH;
+  void* ws = nullptr;
+  if (plan.workspace_bytes > 0) {
+    if (fp8rl::gemm_scratch(as_stream(stream), &ws) != hipSuccess) return FP8RL_ERR_HIP;
+  }
+  return hip_status(fp8rl::launch_gemm(xq, sa, wq, sw, M, N, K, y, y_dtype == FP8RL_OUT_F32, ld_y,
+                                       accum, false, ws, plan, as_stream(stream)));
 }
 
 int fp8rl_gemm_w8a8_fused_act_quant(const uint16_t* x, int64_t ld_x, const uint8_t* wq,

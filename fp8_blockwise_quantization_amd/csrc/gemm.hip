@@ -19,6 +19,7 @@
 // row, and the 8 even (odd) rows of 16 hit 8 different groups too, so the read is free of bank
 // conflicts whether the LDS serves 8 lanes (32 banks) or 16 lanes (64 banks) per cycle.
 #include <atomic>
+#include <mutex>
 
 #include "device_common.hpp"
 #include "launch.hpp"
@@ -1412,6 +1413,51 @@ hipError_t launch_gemm(const uint8_t* xq, const float* sa, const uint8_t* wq, co
 }
 
 bool plan_fuses_act(const GemmPlan& pl) { return pl.cfg == kCfgDecode; }
+
+// ---------------------------------------------------------------------------------------------
+// Scratch for the no-allocation entry point: one static device array per device (the code
+// object's copy on each device it is loaded on), used exactly like a caller's workspace --
+// arrival counters in the first kWsHeaderBytes, split partials after them. In host code the
+// array's name is only a stand-in; its device address comes from hipGetSymbolAddress, once per
+// device with that device current, and only that address is ever passed to kernels.
+// ---------------------------------------------------------------------------------------------
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchDevices] = {};
+
+__global__ __launch_bounds__(256) void zero_words_kernel(uint32_t* p, int n) {
+  for (int i = threadIdx.x; i < n; i += 256) p[i] = 0u;
+}
+
+}  // namespace
+
+hipError_t gemm_scratch(hipStream_t stream, void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    // the counters must start at zero (the loader zero-fills the array too); every GEMM that
+    // uses them leaves them zero again. A fill kernel, not a memset, so that a caller may
+    // capture this first call into a graph.
+    hipLaunchKernelGGL(zero_words_kernel, dim3(1), dim3(256), 0, stream,
+                       reinterpret_cast<uint32_t*>(p), (int)(kWsHeaderBytes / 4));
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_gemm_fused_act(const uint16_t* x, int64_t ld_x, int pow2, const uint8_t* wq,
                                  const float* sw, int64_t M, int64_t N, int64_t K, void* y,

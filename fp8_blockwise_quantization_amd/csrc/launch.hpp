@@ -103,6 +103,11 @@ hipError_t launch_gemm(const uint8_t* xq, const float* sa, const uint8_t* wq, co
                        int64_t M, int64_t N, int64_t K, void* y, int out_f32, int64_t ld_y,
                        int accum, int rowb, void* workspace, const GemmPlan& plan,
                        hipStream_t stream);
+// The library's own GEMM scratch for callers that cannot allocate: a static device array of
+// kScratchBytes per device (see gemm.hip). Returns its address on the current device, clearing
+// its counter header on the first use there (a fill kernel enqueued on `stream`).
+constexpr size_t kScratchBytes = size_t{32} << 20;
+hipError_t gemm_scratch(hipStream_t stream, void** ptr);
 // The decode GEMM (M <= 64) with the 1x128 activation quantization fused into its staging: bf16
 // X [M][ld_x] in place of xq / sa (pow2: scale format of the groups). Only for plans with
 // plan_fuses_act(plan); the workspace is the dense GEMM's for the same shape.

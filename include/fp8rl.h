@@ -68,7 +68,8 @@ typedef enum {
   FP8RL_ERR_DTYPE = 4,     /* unknown output type */
   FP8RL_ERR_WORKSPACE = 5, /* workspace smaller than fp8rl_workspace_bytes() asks for */
   FP8RL_ERR_HIP = 6,       /* the HIP runtime rejected a launch */
-  FP8RL_ERR_ARG = 7        /* any other invalid argument (e.g. E < 1) */
+  FP8RL_ERR_ARG = 7,       /* any other invalid argument (e.g. E < 1) */
+  FP8RL_ERR_SCRATCH = 8    /* the shape needs more than FP8RL_SCRATCH_BYTES of GEMM scratch */
 } fp8rl_status;
 
 typedef enum { FP8RL_OUT_BF16 = 0, FP8RL_OUT_F32 = 1 } fp8rl_out_dtype;
@@ -271,6 +272,24 @@ int fp8rl_gemm_w8a8_blockscaled(const uint8_t* xq, const float* sa, const uint8_
                                 const float* sw, int64_t M, int64_t N, int64_t K, void* y,
                                 int y_dtype, int64_t ld_y, int accum, void* workspace,
                                 size_t workspace_bytes, void* stream);
+
+/*
+ * fp8rl_gemm_w8a8_blockscaled for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the same operation,
+ * kernels, results (the same bits) and argument rules, without the workspace arguments. The
+ * scratch the call needs (K-split arrival counters and partials) is a static device array of
+ * FP8RL_SCRATCH_BYTES that the library holds on every device it runs on until the process ends;
+ * its first use on a device clears its counters (a small kernel on `stream`), and every call
+ * leaves them zero again. A shape whose scratch need (fp8rl_workspace_bytes(FP8RL_OP_GEMM, M, N,
+ * K, 0)) exceeds FP8RL_SCRATCH_BYTES returns FP8RL_ERR_SCRATCH without enqueuing anything.
+ * The call never allocates or frees memory. All calls on one device share that device's array,
+ * so calls that overlap on one GPU (different streams without ordering between them, or threads
+ * enqueueing concurrently) race and give undefined results; order them on one stream.
+ */
+#define FP8RL_SCRATCH_BYTES (32u << 20)
+int fp8rl_gemm_w8a8_blockscaled_noalloc(const uint8_t* xq, const float* sa, const uint8_t* wq,
+                                        const float* sw, int64_t M, int64_t N, int64_t K, void* y,
+                                        int y_dtype, int64_t ld_y, int accum, void* stream);
 
 /*
  * The blockwise-scaled GEMM with the activation quantization fused in, for small token counts

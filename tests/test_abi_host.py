@@ -15,7 +15,7 @@ from fp8_blockwise_quantization_amd import _lib
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fp8rl.h")
 
-OK, ENULL, ESHAPE, EALIGN, EDTYPE, EWS, EHIP, EARG = range(8)
+OK, ENULL, ESHAPE, EALIGN, EDTYPE, EWS, EHIP, EARG, ESCRATCH = range(9)
 A = 1 << 20  # a fake, 16-byte aligned "device address": never dereferenced by these calls
 
 
@@ -32,7 +32,7 @@ def L():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 21
+    assert len(names) == 22
     for n in names:
         assert hasattr(L, n), n
     assert sorted(_lib.EXPORTED) == names
@@ -73,7 +73,7 @@ def test_scale_format_and_accum_validation(L):
 
 
 def test_status_strings_and_version(L):
-    for s in range(8):
+    for s in range(9):
         assert L.fp8rl_status_string(s)
     assert L.fp8rl_status_string(99) == b"unknown status"
     assert L.fp8rl_version() >= 100
@@ -319,3 +319,24 @@ def test_python_binding_rejects_host_tensors():
     w = torch.zeros((128, 128), dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         _lib.fp8rl_quant_weight_blk128(w)
+
+
+def test_noalloc_gemm_validation(L):
+    """The no-allocation GEMM validates like the workspace form and refuses, before any HIP call,
+    a shape whose scratch need exceeds the static buffer."""
+    g = L.fp8rl_gemm_w8a8_blockscaled_noalloc
+    scratch = 32 << 20
+    assert g(A, A, A, A, 0, 256, 256, A, 0, 256, 3, None) == OK
+    assert g(None, A, A, A, 64, 256, 256, A, 0, 256, 3, None) == ENULL
+    assert g(A, A, A, A, 64, 256, 200, A, 0, 256, 3, None) == ESHAPE
+    assert g(A, A, A, A, 64, 256, 256, A, 5, 256, 3, None) == EDTYPE
+    assert g(A, A, A, A, 64, 256, 256, A, 1, 256, 0, None) == EARG  # FP8 slices, float32 out
+    assert g(A, A, A, A, 64, 256, 256, A + 2, 0, 256, 3, None) == EALIGN
+    # a mid-M split-K shape whose partials need more than the scratch holds
+    M, N, K = 1000, 6144, 8192
+    need = L.fp8rl_workspace_bytes(0, M, N, K, 0)
+    assert need > scratch, need
+    assert g(A, A, A, A, M, N, K, A, 0, N, 3, None) == ESCRATCH
+    # the decode shapes of the workloads fit
+    for m, n, k in ((64, 24576, 4096), (64, 6144, 4096), (64, 4096, 12288), (64, 28672, 4096)):
+        assert L.fp8rl_workspace_bytes(0, m, n, k, 0) <= scratch
