@@ -1105,6 +1105,151 @@ __global__ __launch_bounds__(T::NT) void gemm_decode_kernel(GemmArgs p) {
     __hip_atomic_store(p.counters + t, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// ---------------------------------------------------------------------------------------------
+// Decode-sized GEMM (M <= 16), weight streaming without any hand-off between workgroups.
+// Workgroup t of 8 waves computes output columns [BN t, BN t + BN) (BN = 16 NB) for all M rows
+// over the whole K range, which its waves split among themselves: wave w takes the K slices
+// w, w + 8, w + 16, ... Each wave streams its slices' weight fragments (NB blocks of 16 rows x 128
+// bytes), activation fragments (MT blocks of 16 rows) and scales straight from memory into a
+// register ring D slices deep -- no LDS and no barrier inside the K loop, every load and wait
+// visible to the compiler -- and multiplies each slice with the weight fragment as the matrix
+// core's A operand (result rows = output columns) and the activation fragment as its B operand
+// (result columns = output rows), so a lane's rescale needs one activation scale per row block.
+// The eight partial tiles are then summed through LDS in wave order (the same bits every run)
+// and stored.
+// ---------------------------------------------------------------------------------------------
+template <int MT_, int NB_, int D_>
+struct Str {
+  static constexpr int MT = MT_, NB = NB_, D = D_;
+  static constexpr int WAVES = 8, NT = 512;
+  static constexpr int BN = 16 * NB;
+  static constexpr int PARTS = MT * NB;  // 16x16 blocks per wave
+};
+
+template <class T>
+struct StrSlot {
+  v8i w[T::NB];
+  v8i x[T::MT];
+  float sa[T::MT];
+  float sw;
+};
+
+template <class T>
+__device__ __forceinline__ void str_load(StrSlot<T>& s, const GemmArgs& p, int n0, int kb,
+                                         int r16, int kq) {
+#pragma unroll
+  for (int j = 0; j < T::NB; ++j)
+    s.w[j] = load_frag_global(p.wq + (int64_t)(n0 + 16 * j + r16) * p.K, kb, kq);
+#pragma unroll
+  for (int i = 0; i < T::MT; ++i) {
+    const int m = min(16 * i + r16, p.M - 1);
+    const u32x4* src = reinterpret_cast<const u32x4*>(p.xq + (int64_t)m * p.K + (int64_t)kb * 128 +
+                                                      kq * 32);
+    const u32x4 lo = src[0], hi = src[1];
+    s.x[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z,
+                 (int)hi.w};
+    s.sa[i] = p.sa[(int64_t)m * p.KB + kb];
+  }
+  s.sw = p.sw[(int64_t)(n0 >> 7) * p.KB + kb];
+}
+
+template <class T, int ACC>
+__device__ __forceinline__ void str_mma(const StrSlot<T>& s, v4f (&acc)[T::MT][T::NB]) {
+  if constexpr (ACC == 2) {
+    const int swe = e8m0_of(s.sw);
+#pragma unroll
+    for (int i = 0; i < T::MT; ++i) {
+      const int se = e8m0_of(s.sa[i]);
+#pragma unroll
+      for (int j = 0; j < T::NB; ++j) {
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(s.w[j], s.x[i], acc[i][j], 0,
+                                                                     0, 0, swe, 0, se);
+        asm volatile("" : "+v"(acc[i][j]));  // keep each slice's update in place
+      }
+    }
+    return;
+  }
+  v4f pr[T::MT][T::NB];
+#pragma unroll
+  for (int i = 0; i < T::MT; ++i)
+#pragma unroll
+    for (int j = 0; j < T::NB; ++j) pr[i][j] = slice_product<ACC == 1>(s.w[j], s.x[i]);
+  __builtin_amdgcn_sched_barrier(0);  // every product in flight before the first is consumed
+#pragma unroll
+  for (int i = 0; i < T::MT; ++i) {
+    const float sc = s.sa[i] * s.sw;
+#pragma unroll
+    for (int j = 0; j < T::NB; ++j) {
+      acc[i][j] += pr[i][j] * sc;
+      asm volatile("" : "+v"(acc[i][j]));
+    }
+  }
+}
+
+template <class T, int ACC>
+__global__ __launch_bounds__(T::NT) void gemm_stream_kernel(GemmArgs p) {
+  __shared__ __attribute__((aligned(16))) v4f red[T::WAVES][T::PARTS][64];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r16 = lane & 15, kq = lane >> 4;
+  const int n0 = blockIdx.x * T::BN;
+  const int KB = p.KB;
+  // slices of this wave: wave + 8 t, t < cnt (cnt a multiple of D, the same for every wave)
+  const int cnt = ((KB + T::WAVES - 1) / T::WAVES + T::D - 1) / T::D * T::D;
+  v4f acc[T::MT][T::NB];
+#pragma unroll
+  for (int i = 0; i < T::MT; ++i)
+#pragma unroll
+    for (int j = 0; j < T::NB; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+  // The loop is free of branches, so that the compiler's wait counts stay exact (a slice's
+  // operands are waited for with the D - 1 later slices still in flight): a slice past K is
+  // loaded from the last slice and multiplied with zeroed activation codes, and the last round
+  // (no refills) is peeled off.
+  StrSlot<T> ring[T::D];
+  auto mma = [&](StrSlot<T>& s, int kb) {
+    if (kb >= KB) {  // uniform: past K, zero products
+#pragma unroll
+      for (int i = 0; i < T::MT; ++i) s.x[i] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+    str_mma<T, ACC>(s, acc);
+  };
+#pragma unroll
+  for (int u = 0; u < T::D; ++u) str_load<T>(ring[u], p, n0, min(wave + T::WAVES * u, KB - 1), r16, kq);
+  for (int t = 0; t < cnt - T::D; t += T::D) {
+#pragma unroll
+    for (int u = 0; u < T::D; ++u) {
+      mma(ring[u], wave + T::WAVES * (t + u));
+      str_load<T>(ring[u], p, n0, min(wave + T::WAVES * (t + u + T::D), KB - 1), r16, kq);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < T::D; ++u) mma(ring[u], wave + T::WAVES * (cnt - T::D + u));
+  // sum the eight waves' partial tiles in wave order
+#pragma unroll
+  for (int i = 0; i < T::MT; ++i)
+#pragma unroll
+    for (int j = 0; j < T::NB; ++j) red[wave][i * T::NB + j][lane] = acc[i][j];
+  __syncthreads();
+  for (int q = tid; q < T::PARTS * 64; q += T::NT) {
+    const int part = q >> 6, l = q & 63;
+    v4f s = red[0][part][l];
+#pragma unroll
+    for (int w = 1; w < T::WAVES; ++w) s += red[w][part][l];
+    // block (i, j) = (part / NB, part % NB); lane l holds output row 16 i + l % 16 and the four
+    // columns n0 + 16 j + 4 (l / 16) .. + 3
+    const int m = 16 * (part / T::NB) + (l & 15);
+    if (m >= p.M) continue;
+    const int64_t off = (int64_t)m * p.ldy + n0 + 16 * (part % T::NB) + 4 * (l >> 4);
+    if (p.out_f32) {
+      *reinterpret_cast<v4f*>(reinterpret_cast<float*>(p.y) + off) = s;
+    } else {
+      const uint32_t lo = f32_to_bf16_rne(s[0]) | ((uint32_t)f32_to_bf16_rne(s[1]) << 16);
+      const uint32_t hi = f32_to_bf16_rne(s[2]) | ((uint32_t)f32_to_bf16_rne(s[3]) << 16);
+      *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(p.y) + off) = u32x2{lo, hi};
+    }
+  }
+}
+
 // Deterministic split-K reduction: partials are summed in split order.
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ ws,
                                                             int splits, int64_t M, int N, void* y,
@@ -1195,7 +1340,7 @@ __global__ __launch_bounds__(T::NT) void grouped_gemm_kernel(GemmArgs p) {
 namespace {
 
 constexpr int kCfgLarge = 0, kCfgSmall = 1, kCfgBigWide = 2, kCfgBigNarrow = 3, kCfgDecode = 4,
-              kCfgGroupedBig = 5;
+              kCfgGroupedBig = 5, kCfgStream = 6;
 constexpr int64_t kGroupedWorkgroups = 256;  // persistent grouped GEMM: one per CU (LDS-bound)
 constexpr int kTargetWorkgroups = 512;  // two per CU on 256 CUs
 constexpr int kMinSlicesPerSplit = 4;
@@ -1228,31 +1373,21 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool rowb) {
     pl.workspace_bytes = 0;
     return pl;
   }
-  if (M <= 64 && KB % 2 == 0 && !rowb) {
-    // weight streaming: 64-column tiles, D slices in flight per wave (the largest of 8, 4, 2
-    // dividing KB); split K into ranges of L slices (L a multiple of D dividing KB) while there
-    // are fewer than kDecWorkgroups workgroups and ranges keep at least kDecMinSlices slices
-    constexpr int64_t BN = 64;
-    const int64_t D = KB % 8 == 0 ? 8 : KB % 4 == 0 ? 4 : 2;  // two rounds of D / 2 slices
-    const int64_t tiles = N / BN;
-    int64_t S = 1;
-    if (tiles <= kWsCounters)
-      for (int64_t s = 2; s <= KB / D; ++s) {
-        if ((KB / D) % s || KB / s < kDecMinSlices) continue;
-        if (tiles * S >= kDecWorkgroups) break;
-        S = s;
-      }
-    pl.cfg = kCfgDecode;
-    pl.bm = (int)M;
-    pl.bn = (int)BN;
-    pl.depth = (int)D;
-    pl.splits = (int)S;
-    pl.kb_per_split = (int)(KB / S);
-    const int64_t mp = M <= 16 ? 16 : M <= 32 ? 32 : 64;  // rows the kernel pads M to
-    pl.workspace_bytes =
-        S > 1 ? kWsHeaderBytes + (size_t)(tiles * S) * BN * mp * sizeof(float) : 0;
+  if (M <= 16 && !rowb) {
+    // weight streaming, K split over the waves of each workgroup (no workspace). Each
+    // workgroup reads all M activation rows for its 16 or 32 columns, so above 16 rows the
+    // activation traffic outgrows the weights' and the split-K kernel below is faster.
+    pl.cfg = kCfgStream;
+    pl.bm = 16;
+    pl.bn = N % 32 == 0 && N / 16 > 1024 ? 32 : 16;
+    const int64_t per_wave = (KB + 7) / 8;  // slices per wave
+    pl.depth = per_wave >= 4 ? 4 : 2;
+    pl.splits = 1;
+    pl.kb_per_split = (int)KB;
+    pl.workspace_bytes = 0;
     return pl;
   }
+  if (M <= 64 && KB % 2 == 0 && !rowb) return plan_fused_act(M, N, K);  // the split-K decode GEMM
   if (M >= 512) {
     pl.cfg = kCfgLarge;
     pl.bm = TileLarge::BM;
@@ -1278,6 +1413,37 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool rowb) {
   return pl;
 }
 
+GemmPlan plan_fused_act(int64_t M, int64_t N, int64_t K) {
+  GemmPlan pl{};
+  pl.cfg = -1;
+  const int64_t KB = K / 128;
+  if (M < 1 || M > 64 || KB % 2 != 0) return pl;
+  // the decode GEMM with the activation quantization fused in: 64-column tiles, D slices in
+  // flight per wave (the largest of 8, 4, 2
+  // dividing KB); split K into ranges of L slices (L a multiple of D dividing KB) while there
+  // are fewer than kDecWorkgroups workgroups and ranges keep at least kDecMinSlices slices
+  constexpr int64_t BN = 64;
+  const int64_t D = KB % 8 == 0 ? 8 : KB % 4 == 0 ? 4 : 2;  // two rounds of D / 2 slices
+  const int64_t tiles = N / BN;
+  int64_t S = 1;
+  if (tiles <= kWsCounters)
+    for (int64_t s = 2; s <= KB / D; ++s) {
+      if ((KB / D) % s || KB / s < kDecMinSlices) continue;
+      if (tiles * S >= kDecWorkgroups) break;
+      S = s;
+    }
+  pl.cfg = kCfgDecode;
+  pl.bm = (int)M;
+  pl.bn = (int)BN;
+  pl.depth = (int)D;
+  pl.splits = (int)S;
+  pl.kb_per_split = (int)(KB / S);
+  const int64_t mp = M <= 16 ? 16 : M <= 32 ? 32 : 64;  // rows the kernel pads M to
+  pl.workspace_bytes =
+      S > 1 ? kWsHeaderBytes + (size_t)(tiles * S) * BN * mp * sizeof(float) : 0;
+  return pl;
+}
+
 GemmPlan plan_grouped_gemm(int64_t M_total, int64_t N, int64_t K, int32_t E) {
   GemmPlan pl{};
   (void)M_total;
@@ -1299,6 +1465,25 @@ static hipError_t launch_big(const GemmArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((gemm_big_kernel<T, ACC>), dim3((unsigned)(tiles_m * tiles_n)), dim3(T::NT),
                      0, stream, a);
   return hipGetLastError();
+}
+
+template <class T, int ACC>
+static hipError_t launch_stream_t(const GemmArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL((gemm_stream_kernel<T, ACC>), dim3((unsigned)(a.N / T::BN)), dim3(T::NT), 0,
+                     stream, a);
+  return hipGetLastError();
+}
+
+template <int MT, int NB, int ACC>
+static hipError_t launch_stream_d(const GemmArgs& a, const GemmPlan& pl, hipStream_t stream) {
+  if (pl.depth == 4) return launch_stream_t<Str<MT, NB, 4>, ACC>(a, stream);
+  return launch_stream_t<Str<MT, NB, 2>, ACC>(a, stream);
+}
+
+template <int ACC>
+static hipError_t launch_stream(const GemmArgs& a, const GemmPlan& pl, hipStream_t stream) {
+  if (pl.bn == 32) return launch_stream_d<1, 2, ACC>(a, pl, stream);
+  return launch_stream_d<1, 1, ACC>(a, pl, stream);
 }
 
 template <class T, int ACC, bool F>
@@ -1392,6 +1577,9 @@ hipError_t launch_gemm(const uint8_t* xq, const float* sa, const uint8_t* wq, co
     case kCfgBigNarrow:
       if (accum == 1) return launch_big<BigNarrow, 1>(a, stream);
       return accum == 2 ? launch_big<BigNarrow, 2>(a, stream) : launch_big<BigNarrow, 0>(a, stream);
+    case kCfgStream:
+      if (accum == 1) return launch_stream<1>(a, pl, stream);
+      return accum == 2 ? launch_stream<2>(a, pl, stream) : launch_stream<0>(a, pl, stream);
     case kCfgDecode:  // reduces its own split tiles
       if (accum == 1) return launch_decode<1>(a, pl, stream);
       return accum == 2 ? launch_decode<2>(a, pl, stream) : launch_decode<0>(a, pl, stream);

@@ -110,7 +110,8 @@ constexpr size_t kScratchBytes = size_t{32} << 20;
 hipError_t gemm_scratch(hipStream_t stream, void** ptr);
 // The decode GEMM (M <= 64) with the 1x128 activation quantization fused into its staging: bf16
 // X [M][ld_x] in place of xq / sa (pow2: scale format of the groups). Only for plans with
-// plan_fuses_act(plan); the workspace is the dense GEMM's for the same shape.
+// plan_fuses_act(plan), plans from plan_fused_act (its own workspace rule).
+GemmPlan plan_fused_act(int64_t M, int64_t N, int64_t K);
 bool plan_fuses_act(const GemmPlan& plan);
 hipError_t launch_gemm_fused_act(const uint16_t* x, int64_t ld_x, int pow2, const uint8_t* wq,
                                  const float* sw, int64_t M, int64_t N, int64_t K, void* y,

@@ -296,10 +296,12 @@ int fp8rl_gemm_w8a8_blockscaled_noalloc(const uint8_t* xq, const float* sa, cons
  * (decode: M <= 64). [NEMO, speed-up discussion of the Llama 3 8B results: the quantization
  * kernels placed before each linear are overhead, and fusing them is expected to raise the gain
  * further; UFP8, limitations paragraph: at the small batches of RL the extra quantize steps
- * leave the GPU under-fed.] The result is bit for bit that of fp8rl_quant_act_tok128_ex(x,
- * scale_fmt) followed by fp8rl_gemm_w8a8_blockscaled on its codes and scales: each workgroup
- * quantizes the 1x128 groups of the K range it multiplies as it stages them, so the FP8
- * activations never go to memory and one launch replaces two.
+ * leave the GPU under-fed.] It multiplies exactly the codes and scales that
+ * fp8rl_quant_act_tok128_ex(x, scale_fmt) produces: each workgroup quantizes the 1x128 groups of
+ * the K range it multiplies as it stages them, so the FP8 activations never go to memory and one
+ * launch replaces two. Its result meets the same accuracy contract as quantizing first and calling
+ * fp8rl_gemm_w8a8_blockscaled (the two kernels sum the K slices in different fixed orders, so the
+ * last bits of the two results can differ).
  *   x      : bf16 activations X, M rows of pitch ld_x (>= K; ld_x * 2 a multiple of 16)
  *   wq, sw, y, ld_y, accum : as for fp8rl_gemm_w8a8_blockscaled
  *   scale_fmt : FP8RL_SCALE_FP32 or FP8RL_SCALE_POW2, the activation groups' scale format;

@@ -66,10 +66,10 @@ def test_scale_format_and_accum_validation(L):
                                                  None, 0, None) == EARG
     # accepted combinations reach the later checks (here: the missing workspace of a split-K
     # decode shape)
-    need = L.fp8rl_workspace_bytes(0, 64, 1024, 4096, 0)
+    need = L.fp8rl_workspace_bytes(0, 200, 1024, 4096, 0)
     assert need > 0
     for acc, out in ((3, 0), (3, 1), (1, 1), (0, 0), (2, 0)):
-        assert g(A, A, A, A, 64, 1024, 4096, A, out, 1024, acc, None, 0, None) == EWS
+        assert g(A, A, A, A, 200, 1024, 4096, A, out, 1024, acc, None, 0, None) == EWS
 
 
 def test_status_strings_and_version(L):
@@ -223,10 +223,11 @@ def test_gemm_validation(L):
     assert call(acc=-1) == EARG
     assert call(xq=A + 1) == EALIGN
     assert call(ldy=260) == EALIGN  # 520-byte bf16 pitch
-    need = L.fp8rl_workspace_bytes(0, 64, 256, 4096, 0)
-    assert need > 0  # a decode-shaped problem uses split-K partials
-    assert call(K=4096, wsb=need - 1) == EWS
-    assert call(K=4096, ws=None) == EWS
+    assert L.fp8rl_workspace_bytes(0, 16, 256, 4096, 0) == 0  # up to 16 rows: none
+    need = L.fp8rl_workspace_bytes(0, 200, 256, 4096, 0)
+    assert need > 0  # a mid-M problem uses split-K partials
+    assert call(M=200, K=4096, wsb=need - 1) == EWS
+    assert call(M=200, K=4096, ws=None) == EWS
 
 
 def test_fused_act_gemm_validation(L):
@@ -253,7 +254,7 @@ def test_fused_act_gemm_validation(L):
     assert call(x=A + 2) == EALIGN
     assert call(ldx=4100) == EALIGN  # 8200-byte bf16 pitch
     need = L.fp8rl_workspace_bytes(3, 64, 256, 4096, 0)
-    assert need == L.fp8rl_workspace_bytes(0, 64, 256, 4096, 0) > 0
+    assert need > 0  # the fused decode kernel splits K over workgroups
     assert call(wsb=need - 1) == EWS
     assert call(ws=None) == EWS
     assert L.fp8rl_workspace_bytes(3, 65, 256, 4096, 0) == 0  # not a fused shape
@@ -286,10 +287,12 @@ def test_grouped_gemm_validation(L):
 def test_workspace_query_is_pure_host(L):
     hdr = _lib.WORKSPACE_HEADER_BYTES
     assert hdr == 4096  # FP8RL_WORKSPACE_HEADER_BYTES
-    # decode shapes (M <= 64, even K/128): 64-column tiles, K split into S ranges of whole
-    # rounds of D slices (D = 8, 4 or 2 dividing K/128) while fewer than 512 workgroups and
-    # ranges of >= 8 slices; workspace = header + [tiles][S] partial tiles of 64 columns x
-    # padded rows (16, 32 or 64) float32
+    # the blockscaled GEMM up to 16 rows splits K only inside each workgroup (no workspace); the
+    # decode GEMM above that and the fused-activation decode GEMM (op 3) split K over workgroups:
+    # 64-column
+    # tiles, K split into S ranges of whole rounds of D slices (D = 8, 4 or 2 dividing K/128)
+    # while fewer than 512 workgroups and ranges of >= 8 slices; workspace = header + [tiles][S]
+    # partial tiles of 64 columns x padded rows (16, 32 or 64) float32
     def dec(M, N, K):
         tiles, kb = N // 64, K // 128
         d = 8 if kb % 8 == 0 else 4 if kb % 4 == 0 else 2
@@ -303,10 +306,13 @@ def test_workspace_query_is_pure_host(L):
         mp = 16 if M <= 16 else 32 if M <= 32 else 64
         return hdr + tiles * S * 64 * mp * 4 if S > 1 else 0
     for shape in [(64, 4096, 4096), (20, 1024, 12288), (64, 12288, 4096), (1, 256, 2048)]:
-        assert L.fp8rl_workspace_bytes(0, *shape, 0) == dec(*shape) > 0, shape
-    assert L.fp8rl_workspace_bytes(0, 64, 4096, 4096, 0) == hdr + 64 * 4 * 64 * 64 * 4
-    assert L.fp8rl_workspace_bytes(0, 64, 4096, 1024, 0) == 0  # 8 slices: one range
-    assert L.fp8rl_workspace_bytes(0, 8, 131072, 2048, 0) == 0  # more tiles than counters
+        assert L.fp8rl_workspace_bytes(3, *shape, 0) == dec(*shape) > 0, shape
+        blk = L.fp8rl_workspace_bytes(0, *shape, 0)
+        assert blk == (0 if shape[0] <= 16 else dec(*shape)), shape
+    assert L.fp8rl_workspace_bytes(3, 64, 4096, 4096, 0) == hdr + 64 * 4 * 64 * 64 * 4
+    assert L.fp8rl_workspace_bytes(3, 64, 4096, 1024, 0) == 0  # 8 slices: one range
+    assert L.fp8rl_workspace_bytes(3, 8, 131072, 2048, 0) == 0  # more tiles than counters
+    assert L.fp8rl_workspace_bytes(3, 64, 4096, 384, 0) == 0  # odd K/128: no fused form
     assert L.fp8rl_workspace_bytes(0, 0, 256, 256, 0) == 0
     assert L.fp8rl_workspace_bytes(0, 8192, 4096, 4096, 0) == 0  # large M: no split
     assert L.fp8rl_workspace_bytes(1, 32768, 1536, 2048, 128) == 0

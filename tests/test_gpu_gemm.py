@@ -152,10 +152,10 @@ def test_output_pitch_canary_and_determinism():
 
 
 def test_one_workspace_reused_across_shapes():
-    """One zero-headed workspace serves decode GEMMs of several shapes in a row (each split-K
-    reduction re-arms its counters), and its counter header is zero again afterwards."""
-    shapes = [(64, 4096, 4096), (20, 1024, 12288), (64, 4096, 4096), (1, 256, 2048),
-              (48, 2048, 1280)]
+    """One zero-headed workspace serves GEMMs of several shapes in a row (mid-M shapes with K
+    split over workgroups, decode shapes that need none), and its header is zero afterwards."""
+    shapes = [(300, 768, 2048), (64, 4096, 4096), (200, 1024, 4096), (20, 1024, 12288),
+              (130, 512, 1024), (1, 256, 2048), (48, 2048, 1280)]
     need = max(fq.fp8rl_workspace_bytes(fq.FP8RL_OP_GEMM, *s) for s in shapes)
     ws = fq.new_workspace(need, "cuda")
     ws[fq.WORKSPACE_HEADER_BYTES:].fill_(0xC3)  # garbage partials from an earlier call

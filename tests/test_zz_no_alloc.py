@@ -2,10 +2,11 @@
 entry point (fp8rl_gemm_w8a8_blockscaled), both called through the C ABI with raw device pointers,
 and against the oracle.
 
-Three calls in a row share the library's static scratch: the Qwen3-8B gate/up decode GEMM (K split
-over workgroups: arrival counters and partials in the scratch), a mid-M split-K shape (partials
-reduced by a second kernel), then a smaller decode GEMM; each result must equal the workspace
-form's bit for bit and meet the GEMM tolerance against the oracle.
+Four calls in a row share the library's static scratch: mid-M shapes whose K is split over
+workgroups (partials in the scratch, summed by a second kernel), the later ones smaller than the
+first, then a decode shape (K split over workgroups too: arrival counters and partials in the
+scratch); each result must equal the workspace form's bit for bit and meet the GEMM tolerance
+against the oracle.
 """
 
 import ctypes
@@ -22,7 +23,7 @@ from workloads import synth
 
 pytestmark = pytest.mark.gpu
 
-SHAPES = [(64, 24576, 4096), (200, 1024, 4096), (16, 4096, 4096)]
+SHAPES = [(300, 768, 2048), (200, 1024, 4096), (130, 512, 1024), (64, 4096, 4096)]
 
 
 def _operands(M, N, K, seed):
@@ -47,7 +48,7 @@ def test_noalloc_equals_workspace_entry_point(out):
         ptrs = [ctypes.c_void_p(t.data_ptr()) for t in d]
         y_ref = torch.full((M, N), 5.0, dtype=dt, device="cuda")
         need = L.fp8rl_workspace_bytes(0, M, N, K, 0)
-        ws = fq.new_workspace(need, "cuda")
+        ws = fq.new_workspace(need, "cuda")  # (a zeroed header even when need is 0)
         st = L.fp8rl_gemm_w8a8_blockscaled(*ptrs, M, N, K, ctypes.c_void_p(y_ref.data_ptr()), code,
                                            N, 3, ctypes.c_void_p(ws.data_ptr()), ws.numel(), stream)
         assert st == 0
