@@ -68,6 +68,60 @@ class Fp8rlError(RuntimeError):
         super().__init__(f"{func} failed with status {status}: {msg}")
 
 
+def declare(L: ctypes.CDLL) -> ctypes.CDLL:
+    """Set the argument and result types of every C ABI function on a loaded copy of the
+    library (the in-tree build, or another build of the same sources); returns it."""
+    i64, vp, i32, sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    sig = {
+        "fp8rl_encode_e4m3_f32": (ctypes.c_int, [vp, i64, vp, vp]),
+        "fp8rl_quant_weight_blk128": (ctypes.c_int, [vp, i64, i64, i64, vp, i64, vp, vp]),
+        "fp8rl_quant_weight_blk128_batched": (ctypes.c_int,
+                                              [ctypes.POINTER(WeightDesc), i32, vp]),
+        "fp8rl_quant_act_tok128": (ctypes.c_int, [vp, i64, i64, i64, vp, i64, vp, vp]),
+        "fp8rl_quant_weight_blk128_ex": (ctypes.c_int,
+                                         [vp, i64, i64, i64, vp, i64, vp, ctypes.c_int, vp]),
+        "fp8rl_quant_weight_blk128_batched_ex": (
+            ctypes.c_int, [ctypes.POINTER(WeightDesc), i32, ctypes.c_int, vp]),
+        "fp8rl_quant_act_tok128_ex": (ctypes.c_int,
+                                      [vp, i64, i64, i64, vp, i64, vp, ctypes.c_int, vp]),
+        "fp8rl_gemm_w8a8_blockscaled": (
+            ctypes.c_int,
+            [vp, vp, vp, vp, i64, i64, i64, vp, ctypes.c_int, i64, ctypes.c_int, vp, sz, vp]),
+        "fp8rl_grouped_gemm_w8a8": (
+            ctypes.c_int,
+            [vp, vp, vp, vp, vp, i32, i64, i64, i64, vp, ctypes.c_int, ctypes.c_int, vp, sz, vp]),
+        "fp8rl_amax_bf16": (ctypes.c_int, [vp, i64, i64, i64, vp, vp]),
+        "fp8rl_amax_bf16_batched": (ctypes.c_int, [ctypes.POINTER(TensorDesc), i32, vp]),
+        "fp8rl_scale_from_amax": (ctypes.c_int, [vp, i32, vp, vp]),
+        "fp8rl_quant_bf16_per_tensor": (ctypes.c_int,
+                                        [vp, i64, i64, i64, vp, vp, i64, i64, vp, vp]),
+        "fp8rl_quant_bf16_per_tensor_batched": (ctypes.c_int,
+                                                [ctypes.POINTER(QuantDesc), i32, vp]),
+        "fp8rl_quant_weight_blk128_t": (
+            ctypes.c_int, [vp, i64, i64, i64, vp, i64, vp, vp, i64, vp, ctypes.c_int, vp]),
+        "fp8rl_quant_act_colwise128": (
+            ctypes.c_int, [vp, i64, i64, i64, vp, i64, vp, vp, i64, vp, ctypes.c_int, vp]),
+        "fp8rl_gemm_w8a8_rowscaled": (
+            ctypes.c_int,
+            [vp, vp, vp, vp, i64, i64, i64, vp, ctypes.c_int, i64, ctypes.c_int, vp, sz, vp]),
+        "fp8rl_gemm_w8a8_blockscaled_noalloc": (
+            ctypes.c_int,
+            [vp, vp, vp, vp, i64, i64, i64, vp, ctypes.c_int, i64, ctypes.c_int, vp]),
+        "fp8rl_gemm_w8a8_fused_act_quant": (
+            ctypes.c_int,
+            [vp, i64, vp, vp, i64, i64, i64, vp, ctypes.c_int, i64, ctypes.c_int,
+             ctypes.c_int, vp, sz, vp]),
+        "fp8rl_workspace_bytes": (sz, [ctypes.c_int, i64, i64, i64, i32]),
+        "fp8rl_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "fp8rl_version": (ctypes.c_int, []),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+    return L
+
+
 def lib() -> ctypes.CDLL:
     """Load the HIP library (once). Raises if it has not been built."""
     global _lib
@@ -80,55 +134,7 @@ def lib() -> ctypes.CDLL:
             raise RuntimeError(
                 f"{LIB_PATH} is missing: build it with `python -m fp8_blockwise_quantization_amd.build`"
             )
-        L = ctypes.CDLL(LIB_PATH)
-        i64, vp, i32, sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
-        sig = {
-            "fp8rl_encode_e4m3_f32": (ctypes.c_int, [vp, i64, vp, vp]),
-            "fp8rl_quant_weight_blk128": (ctypes.c_int, [vp, i64, i64, i64, vp, i64, vp, vp]),
-            "fp8rl_quant_weight_blk128_batched": (ctypes.c_int,
-                                                  [ctypes.POINTER(WeightDesc), i32, vp]),
-            "fp8rl_quant_act_tok128": (ctypes.c_int, [vp, i64, i64, i64, vp, i64, vp, vp]),
-            "fp8rl_quant_weight_blk128_ex": (ctypes.c_int,
-                                             [vp, i64, i64, i64, vp, i64, vp, ctypes.c_int, vp]),
-            "fp8rl_quant_weight_blk128_batched_ex": (
-                ctypes.c_int, [ctypes.POINTER(WeightDesc), i32, ctypes.c_int, vp]),
-            "fp8rl_quant_act_tok128_ex": (ctypes.c_int,
-                                          [vp, i64, i64, i64, vp, i64, vp, ctypes.c_int, vp]),
-            "fp8rl_gemm_w8a8_blockscaled": (
-                ctypes.c_int,
-                [vp, vp, vp, vp, i64, i64, i64, vp, ctypes.c_int, i64, ctypes.c_int, vp, sz, vp]),
-            "fp8rl_grouped_gemm_w8a8": (
-                ctypes.c_int,
-                [vp, vp, vp, vp, vp, i32, i64, i64, i64, vp, ctypes.c_int, ctypes.c_int, vp, sz, vp]),
-            "fp8rl_amax_bf16": (ctypes.c_int, [vp, i64, i64, i64, vp, vp]),
-            "fp8rl_amax_bf16_batched": (ctypes.c_int, [ctypes.POINTER(TensorDesc), i32, vp]),
-            "fp8rl_scale_from_amax": (ctypes.c_int, [vp, i32, vp, vp]),
-            "fp8rl_quant_bf16_per_tensor": (ctypes.c_int,
-                                            [vp, i64, i64, i64, vp, vp, i64, i64, vp, vp]),
-            "fp8rl_quant_bf16_per_tensor_batched": (ctypes.c_int,
-                                                    [ctypes.POINTER(QuantDesc), i32, vp]),
-            "fp8rl_quant_weight_blk128_t": (
-                ctypes.c_int, [vp, i64, i64, i64, vp, i64, vp, vp, i64, vp, ctypes.c_int, vp]),
-            "fp8rl_quant_act_colwise128": (
-                ctypes.c_int, [vp, i64, i64, i64, vp, i64, vp, vp, i64, vp, ctypes.c_int, vp]),
-            "fp8rl_gemm_w8a8_rowscaled": (
-                ctypes.c_int,
-                [vp, vp, vp, vp, i64, i64, i64, vp, ctypes.c_int, i64, ctypes.c_int, vp, sz, vp]),
-            "fp8rl_gemm_w8a8_blockscaled_noalloc": (
-                ctypes.c_int,
-                [vp, vp, vp, vp, i64, i64, i64, vp, ctypes.c_int, i64, ctypes.c_int, vp]),
-            "fp8rl_gemm_w8a8_fused_act_quant": (
-                ctypes.c_int,
-                [vp, i64, vp, vp, i64, i64, i64, vp, ctypes.c_int, i64, ctypes.c_int,
-                 ctypes.c_int, vp, sz, vp]),
-            "fp8rl_workspace_bytes": (sz, [ctypes.c_int, i64, i64, i64, i32]),
-            "fp8rl_status_string": (ctypes.c_char_p, [ctypes.c_int]),
-            "fp8rl_version": (ctypes.c_int, []),
-        }
-        for name, (res, args) in sig.items():
-            f = getattr(L, name)
-            f.restype = res
-            f.argtypes = args
+        L = declare(ctypes.CDLL(LIB_PATH))
         _lib = L
         return L
 

@@ -37,10 +37,12 @@ def hipcc_path() -> str:
     raise RuntimeError("hipcc not found: the HIP toolchain (ROCm) is required to build libfp8rl")
 
 
-def build(verbose: bool = False, extra_flags=()) -> str:
-    """Compile every HIP source into ``libfp8rl.so`` next to this file; returns its path."""
+def build(verbose: bool = False, extra_flags=(), out_path: str | None = None) -> str:
+    """Compile every HIP source into ``libfp8rl.so`` next to this file (or into ``out_path``);
+    returns its path."""
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB_PATH + ".tmp"
+    out = out_path or LIB_PATH
+    tmp = out + ".tmp"
     cmd = [hipcc_path(), *HIPCC_FLAGS, *extra_flags, "-I", os.path.join(ROOT, "include"),
            "-o", tmp, *srcs]
     if verbose:
@@ -49,8 +51,8 @@ def build(verbose: bool = False, extra_flags=()) -> str:
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
         raise RuntimeError(f"hipcc failed with status {res.returncode}")
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -27,6 +27,11 @@ def declared_functions():
 
 @pytest.fixture(scope="module")
 def L():
+    # FP8RL_TEST_LIBRARY: run these checks against another build of the same sources (the
+    # address-sanitized host build of tests/test_abi_asan.py)
+    other = os.environ.get("FP8RL_TEST_LIBRARY")
+    if other:
+        return _lib.declare(ctypes.CDLL(other))
     return _lib.lib()
 
 

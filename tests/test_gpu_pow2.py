@@ -152,3 +152,25 @@ def test_mx_and_fp8_accum_on_random_pow2_operands_derived_bound():
     bound = fp8_slice_bound(xq, sa, wq, sw) + 2.0 ** -8 * np.abs(ref64)
     assert_within(a, ref64, bound, "fp8 accum")
     assert_within(b, ref64, bound, "mx accum")
+
+
+@pytest.mark.parametrize("M,N,K", [(64, 4096, 4096), (1024, 6144, 4096)])
+def test_gpu_scale_formats_against_unquantized_product(M, N, K):
+    """The GPU's two scale formats end to end (quantizers and GEMM on the GPU: FP32 scales with
+    FP8 slice sums, power-of-two scales with the matrix-core-scaled GEMM, bf16 output) against
+    the exact product of the unquantized bf16 operands: both within the E4M3 bound, and the
+    power-of-two form's relative error 1-2x the FP32 form's, as the oracle's comparison finds."""
+    x = synth.act_bf16(M, K, seed=synth.seed_of(71, M, K))
+    w = synth.weight_bf16(N, K, seed=synth.seed_of(71, N, K), outlier_frac=0.001)
+    ref = x.double() @ w.double().t()
+    rel = {}
+    for scale, accum in (("fp32", None), ("pow2", "mx")):
+        xq, sa = fq.quant_act(x.cuda(), scale=scale)
+        wq, sw = fq.quant_weight(w.cuda(), scale=scale)
+        y = fq.gemm(xq, sa, wq, sw, accum=accum)
+        torch.cuda.synchronize()
+        rel[scale] = float(torch.linalg.norm(y.double().cpu() - ref) / torch.linalg.norm(ref))
+    print(f"[scale formats] {M}x{N}x{K}: relative error fp32 {rel['fp32']:.3e}, "
+          f"pow2 {rel['pow2']:.3e}, ratio {rel['pow2'] / rel['fp32']:.3f}", flush=True)
+    assert rel["fp32"] < 2.0 ** -4 and rel["pow2"] < 2.0 ** -4
+    assert 0.95 < rel["pow2"] / rel["fp32"] < 2.0
