@@ -343,8 +343,8 @@ def test_noalloc_gemm_validation(L):
     assert g(A, A, A, A, 64, 256, 256, A, 5, 256, 3, None) == EDTYPE
     assert g(A, A, A, A, 64, 256, 256, A, 1, 256, 0, None) == EARG  # FP8 slices, float32 out
     assert g(A, A, A, A, 64, 256, 256, A + 2, 0, 256, 3, None) == EALIGN
-    # a mid-M split-K shape whose partials need more than the scratch holds
-    M, N, K = 1000, 6144, 8192
+    # a split-K shape (K beyond the DMA-fed tiles) whose partials need more than the scratch holds
+    M, N, K = 1024, 1152, 65536
     need = L.fp8rl_workspace_bytes(0, M, N, K, 0)
     assert need > scratch, need
     assert g(A, A, A, A, M, N, K, A, 0, N, 3, None) == ESCRATCH

@@ -75,7 +75,7 @@ def test_noalloc_binding_and_scratch_limit():
     torch.cuda.synchronize()
     assert torch.equal(y, ref)
     # a shape whose split partials exceed the static scratch is refused with FP8RL_ERR_SCRATCH
-    M, N, K = 1000, 6144, 8192
+    M, N, K = 1024, 1152, 65536
     big = [torch.zeros((M, K), dtype=torch.uint8, device="cuda"),
            torch.ones((M, K // 128), dtype=torch.float32, device="cuda"),
            torch.zeros((N, K), dtype=torch.uint8, device="cuda"),
