@@ -99,6 +99,30 @@ class KernelTimer:
                     gbs=self.bytes / max(ms, 1e-12) / 1e6)
 
 
+def graph_launch_us(torch, fn, reps, replays=3):
+    """Average duration of one call of `fn` (a single kernel launch, or a fixed sequence): `reps`
+    calls captured in a HIP graph, HIP events around `replays` replays on the current stream.
+    Unlike events around eager launches this leaves out the host's launch cost, which is longer
+    than a decode-sized GEMM."""
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(reps):
+            fn()
+    graph.replay()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(replays):
+        graph.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return 1e3 * a.elapsed_time(b) / (replays * reps)
+
+
 # --------------------------------------------------------------------------------- workloads
 
 
@@ -221,19 +245,14 @@ class DenseBlock:
         self.graphs[c].replay()
 
     def time_gemm(self, i, reps):
-        """HIP events around `reps` eager launches of GEMM i alone (its activation already
-        quantized), on the current stream: the per-launch duration of that kernel."""
-        fq, t = self.fq, KernelTimer(self.torch)
+        """Per-launch duration of GEMM i alone (its activation already quantized): `reps`
+        launches replayed from a HIP graph, timed with HIP events on the current stream."""
+        fq = self.fq
         c = 0
         g = lambda: fq.gemm(self.xq[i], self.sa[i], self.wq[c][i], self.sw[c][i], y=self.y[i],
                             accum=self.accum, workspace=self.ws[i])
         fq.quant_act(self.x[i], self.xq[i], self.sa[i], scale=self.scales)
-        for _ in range(3):
-            g()
-        for _ in range(reps):
-            t.launch(g, 0)
-        self.torch.cuda.synchronize()
-        return t.result()["avg_us"]
+        return graph_launch_us(self.torch, g, reps)
 
     def time_linears(self, reps):
         """Kernel time of the captured act-quant + GEMM part alone (graph replays)."""
@@ -808,11 +827,11 @@ def _timed(torch, fn, steps, warmup, timers=()):
 
 def run_fused_act(args, torch, fq, synth, gpu, quant_cpu):
     """The decode GEMMs of one Qwen3-8B block (serving layout: q/k/v, o, gate/up, down) at small
-    token counts, two ways: activation quantization and GEMM as two launches per GEMM, or the
-    GEMM with the quantization fused in (one launch). Both are timed as the host launches them
-    (where small batches are launch-bound) and replayed from a HIP graph (GPU time only).
-    value = algorithmic GB/s of the fused block at M = 64 (graph replay); roofline = the fused
-    gate/up GEMM."""
+    token counts, two ways: activation quantization and GEMM as two calls per GEMM, or one call
+    of the GEMM on bf16 activations (one kernel up to 4 rows; above, the call runs the same two
+    kernels itself). Both are timed as the host launches them (where small batches are
+    launch-bound) and replayed from a HIP graph (GPU time only). value = algorithmic GB/s of the
+    fused block at M = 1 (graph replay); roofline = the fused gate/up kernel at M = 1."""
     groups = serving_layout(synth.DENSE_LINEARS_QWEN3_8B)
     pow2 = args.scales == "pow2"
     accum = "mx" if pow2 else "fp8"
@@ -823,15 +842,16 @@ def run_fused_act(args, torch, fq, synth, gpu, quant_cpu):
         del w
     results = []
     roof = None
-    value = ms64 = None
-    for M in (1, 16, 64):
+    value = ms1 = None
+    for M in (1, 4, 16, 64):
         xs = [synth.act_bf16(M, K, seed=9200 + M + i, device="cuda")
               for i, (_, _, K) in enumerate(groups)]
         ys = [torch.empty((M, N), dtype=torch.bfloat16, device="cuda") for _, N, _ in groups]
         qs = [(torch.empty((M, K), dtype=torch.uint8, device="cuda"),
                torch.empty((M, K // 128), dtype=torch.float32, device="cuda")) for _, _, K in groups]
-        ws = fq.new_workspace(max(fq.fp8rl_workspace_bytes(fq.FP8RL_OP_GEMM, M, N, K)
-                                  for _, N, K in groups), "cuda")
+        ws = fq.new_workspace(max(fq.fp8rl_workspace_bytes(op, M, N, K) for _, N, K in groups
+                                  for op in (fq.FP8RL_OP_GEMM, fq.FP8RL_OP_GEMM_FUSED_ACT)),
+                              "cuda")
 
         def unfused():
             for x, (wq, sw), y, (xq, sa) in zip(xs, weights, ys, qs):
@@ -853,36 +873,32 @@ def run_fused_act(args, torch, fq, synth, gpu, quant_cpu):
         row["graph_fused_over_unfused"] = row["graph_fused_us"] / row["graph_unfused_us"]
         row["eager_fused_over_unfused"] = row["eager_fused_us"] / row["eager_unfused_us"]
         results.append(row)
-        if M == 64:
+        if M == 1:
             nbytes = sum(N * K + 4 * (N // 128) * (K // 128) + 2 * M * K + 2 * M * N
                          for _, N, K in groups)
-            ms64 = row["graph_fused_us"] / 1e3
-            value = nbytes / (ms64 * 1e-3) / 1e9
+            ms1 = row["graph_fused_us"] / 1e3
+            value = nbytes / (ms1 * 1e-3) / 1e9
             gi = max(range(len(groups)), key=lambda j: groups[j][1] * groups[j][2])
             _, gN, gK = groups[gi]
-            t = KernelTimer(torch)
             x, (wq, sw), y = xs[gi], weights[gi], ys[gi]
-            for _ in range(3):
-                fq.gemm_fused_act(x, wq, sw, y=y, workspace=ws, accum=accum, scale=args.scales)
-            for _ in range(max(args.steps, 10)):
-                t.launch(lambda: fq.gemm_fused_act(x, wq, sw, y=y, workspace=ws, accum=accum,
-                                                   scale=args.scales), 0)
-            torch.cuda.synchronize()
+            us = graph_launch_us(torch, lambda: fq.gemm_fused_act(
+                x, wq, sw, y=y, workspace=ws, accum=accum, scale=args.scales),
+                max(args.steps, 20))
             gb = gN * gK + 4 * (gN // 128) * (gK // 128) + 2 * M * gK + 2 * M * gN
-            roof = roof_hbm("gemm_decode_kernel (fused activation quantization)", gb,
-                            t.result()["avg_us"],
+            roof = roof_hbm("gemm_stream_kernel (fused activation quantization)", gb, us,
                             "weight codes + block scales + bf16 activations + bf16 output",
                             f"gate_up_proj: M={M}, N={gN}, K={gK} (one launch)")
-    cfg = {"workload": "Qwen3-8B decode GEMMs (q/k/v, o, gate/up, down) with the activation "
-                       "quantization fused into the GEMM", "tokens_M": [1, 16, 64],
+    cfg = {"workload": "Qwen3-8B decode GEMMs (q/k/v, o, gate/up, down) on bf16 activations, "
+                       "activation quantization fused into the GEMM", "tokens_M": [1, 4, 16, 64],
            "gemms": [list(gr) for gr in groups], "scales": args.scales,
-           "launches_per_block": {"unfused": 2 * len(groups), "fused": len(groups)}}
+           "launches_per_block": {"unfused": 2 * len(groups),
+                                  "fused": {"M <= 4": len(groups), "M > 4": 2 * len(groups)}}}
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline_dense(synth.DENSE_LINEARS_QWEN3_8B, 64, seed=5000, budget_linears=7,
+        cpu = cpu_baseline_dense(synth.DENSE_LINEARS_QWEN3_8B, 1, seed=5000, budget_linears=7,
                                  scales=args.scales)
         cpu["gpu_over_oracle"] = value / cpu["value"]
-    emit(args, value, "GB/s", ms64, cfg, roof, cpu, results=results, **gpu)
+    emit(args, value, "GB/s", ms1, cfg, roof, cpu, results=results, **gpu)
 
 
 def run_mlp(args, torch, fq, synth, gpu, quant_cpu):

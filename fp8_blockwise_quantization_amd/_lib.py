@@ -463,8 +463,8 @@ def fp8rl_gemm_w8a8_rowscaled(aq, sa, bq, sb, out_dtype=torch.bfloat16, y=None, 
 @_allocs_on_stream
 def fp8rl_gemm_w8a8_fused_act_quant(x, wq, sw, out_dtype=torch.bfloat16, y=None, workspace=None,
                                     stream=None, accum=None, scale="fp32"):
-    """Y[M][N] for bf16 X (M <= 64): the activation quantization (1x128 groups, `scale` format)
-    fused into the blockscaled GEMM (the same codes and scales as quantizing X first)."""
+    """Y[M][N] for bf16 X: quantize X in 1x128 groups (`scale` format) and multiply, in one call
+    (one kernel up to 4 rows); the same bits as quant_act followed by the blockscaled GEMM."""
     ld_x = _rows(x, "x", torch.bfloat16)
     _dense(wq, "wq", torch.uint8)
     _dense(sw, "sw", torch.float32)

@@ -385,10 +385,7 @@ size_t fp8rl_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int32_t E)
   if (op == FP8RL_OP_GEMM) return fp8rl::plan_gemm(M, N, K).workspace_bytes;
   if (op == FP8RL_OP_GEMM_ROWSCALED) return fp8rl::plan_gemm(M, N, K, true).workspace_bytes;
   if (op == FP8RL_OP_GROUPED_GEMM) return fp8rl::plan_grouped_gemm(M, N, K, E).workspace_bytes;
-  if (op == FP8RL_OP_GEMM_FUSED_ACT) {
-    const fp8rl::GemmPlan plan = fp8rl::plan_fused_act(M, N, K);
-    return fp8rl::plan_fuses_act(plan) ? plan.workspace_bytes : 0;
-  }
+  if (op == FP8RL_OP_GEMM_FUSED_ACT) return fp8rl::plan_fused_act(M, N, K).workspace_bytes;
   return 0;
 }
 
@@ -462,7 +459,6 @@ int fp8rl_gemm_w8a8_fused_act_quant(const uint16_t* x, int64_t ld_x, const uint8
       !aligned(y, 16) || (ld_y * ybytes) % 16)
     return FP8RL_ERR_ALIGN;
   const fp8rl::GemmPlan plan = fp8rl::plan_fused_act(M, N, K);
-  if (!fp8rl::plan_fuses_act(plan)) return FP8RL_ERR_SHAPE;  // M > 64 or K/128 odd
   if (plan.workspace_bytes > 0) {
     if (!workspace || workspace_bytes < plan.workspace_bytes) return FP8RL_ERR_WORKSPACE;
     if (!aligned(workspace, 16)) return FP8RL_ERR_ALIGN;

@@ -18,6 +18,7 @@
 // logical chunk: any 8 consecutive rows then hit 8 different 16-byte bank groups of a 128-byte
 // row, and the 8 even (odd) rows of 16 hit 8 different groups too, so the read is free of bank
 // conflicts whether the LDS serves 8 lanes (32 banks) or 16 lanes (64 banks) per cycle.
+#include <algorithm>
 #include <atomic>
 #include <mutex>
 
@@ -838,7 +839,6 @@ struct Dec {
   static constexpr int MP = 16 * MT;
   static constexpr int MPA = MP < 32 ? 32 : MP;  // staged rows: at least one 16-byte load per thread
   static constexpr int A_LD = MPA * 8 / NT;       // 16-byte activation loads per thread and slice
-  static constexpr int X_LD = MPA * 16 / NT;      // the same for bf16 activations (fused form)
   static constexpr int A_BYTES = MPA * 128;
   static constexpr int SA_OFF = A_BYTES;          // activation scales of the slice (x NT / MPA)
   static constexpr int STAGE = A_BYTES + NT * 4;  // one slice
@@ -862,45 +862,25 @@ __device__ __forceinline__ v8i load_frag_global(const uint8_t* row_base, int kb,
   return f;
 }
 
-// One slice in registers: the activation rows' 16-byte pieces (E4M3 codes, or bf16 values in the
-// fused form), this lane's weight fragment and the weight block scale.
-template <class T, bool F>
+// One slice in registers: the activation rows' 16-byte pieces of E4M3 codes, this lane's weight
+// fragment and the weight block scale.
+template <class T>
 struct DecSlot {
-  u32x4 a[F ? T::X_LD : T::A_LD];
+  u32x4 a[T::A_LD];
   v8i b;
   float sw;
 };
 
-// Fused form: bf16 piece j of thread tid for the slice at ring position u: the 16 lanes of a
-// DPP row hold one activation row (a 1x128 group), so its amax is one row reduction. The map is
-// rotated by one wave per ring position, so that with few live rows the R slices of a round
-// fall on different waves: row r < 4 of slice u sits on wave (4 - u) % 4.
 template <class T>
-__device__ __forceinline__ int dec_x_piece(int j, int tid, int u) {
-  return j * T::NT + ((tid + 64 * u) & (T::NT - 1));  // row e / 16, values 8 (e % 16) ..
-}
-
-template <class T, bool F>
-__device__ __forceinline__ void dec_fetch(DecSlot<T, F>& d, const GemmArgs& p, const uint8_t* wrow,
-                                          const float* swrow, int kb, int tid, int u) {
+__device__ __forceinline__ void dec_fetch(DecSlot<T>& d, const GemmArgs& p, const uint8_t* wrow,
+                                          const float* swrow, int kb, int tid) {
   // activation rows are read by every tile: ordinary (cached) loads; rows past M repeat row
-  // M - 1 (codes) or are not loaded (bf16), as their products reach no stored output
-  if constexpr (F) {
-    const uint16_t* xs = p.x + (int64_t)kb * 128;
+  // M - 1, as their products reach no stored output
+  const uint8_t* xs = p.xq + (int64_t)kb * 128;
 #pragma unroll
-    for (int j = 0; j < T::X_LD; ++j) {
-      const int e = dec_x_piece<T>(j, tid, u);
-      d.a[j] = u32x4{0u, 0u, 0u, 0u};
-      if ((e >> 4) < p.M)
-        d.a[j] = *reinterpret_cast<const u32x4*>(xs + (int64_t)(e >> 4) * p.ld_x + (e & 15) * 8);
-    }
-  } else {
-    const uint8_t* xs = p.xq + (int64_t)kb * 128;
-#pragma unroll
-    for (int j = 0; j < T::A_LD; ++j) {
-      const int e = j * T::NT + tid;  // 16-byte chunk e: row e / 8, chunk e % 8
-      d.a[j] = *reinterpret_cast<const u32x4*>(xs + (int64_t)min(e >> 3, p.M - 1) * p.K + (e & 7) * 16);
-    }
+  for (int j = 0; j < T::A_LD; ++j) {
+    const int e = j * T::NT + tid;  // 16-byte chunk e: row e / 8, chunk e % 8
+    d.a[j] = *reinterpret_cast<const u32x4*>(xs + (int64_t)min(e >> 3, p.M - 1) * p.K + (e & 7) * 16);
   }
   d.b = load_frag_global(wrow, kb, (tid & 63) >> 4);
   d.sw = swrow[kb];
@@ -916,7 +896,7 @@ __device__ __forceinline__ float dec_fetch_sa(const GemmArgs& p, int kb, int tid
 }
 
 template <class T>
-__device__ __forceinline__ void dec_stage(uint8_t* st, const DecSlot<T, false>& d, int tid) {
+__device__ __forceinline__ void dec_stage(uint8_t* st, const DecSlot<T>& d, int tid) {
 #pragma unroll
   for (int j = 0; j < T::A_LD; ++j) {
     const int e = j * T::NT + tid;
@@ -925,32 +905,8 @@ __device__ __forceinline__ void dec_stage(uint8_t* st, const DecSlot<T, false>& 
   }
 }
 
-// Fused form: quantize the slice's bf16 activation rows into the staged layout, exactly as the
-// 1x128 activation quantizer does: each lane writes its 8 codes and lane 0 of the row the group's
-// scale. Padding rows (M <= row < MPA) get zero codes and a zero scale without the arithmetic:
-// whole rows, so the reduction's lanes are all active or all idle.
-template <class T>
-__device__ __forceinline__ void dec_stage(uint8_t* st, const DecSlot<T, true>& d, int tid, int u,
-                                          int M, int pow2) {
-  float* sa = reinterpret_cast<float*>(st + T::SA_OFF);
-#pragma unroll
-  for (int j = 0; j < T::X_LD; ++j) {
-    const int e = dec_x_piece<T>(j, tid, u), row = e >> 4, c = e & 15;
-    u32x2 q = u32x2{0u, 0u};
-    float S = 0.f;
-    if (row < M) {
-      const uint32_t m = row16_max_u32(hmax_u16(amax8_pk(d.a[j])));
-      S = pow2 ? pow2_scale_from_amax_bits(m) : scale_from_amax_bits(m);
-      q = quant8(d.a[j], recip_f64(S));
-    }
-    // codes 8c .. 8c + 7 of the row: half c & 1 of its (swizzled) 16-byte chunk c / 2
-    *reinterpret_cast<u32x2*>(st + row * 128 + ((((c >> 1) ^ swz(row)) << 4) | ((c & 1) << 3))) = q;
-    if (c == 0) sa[row] = S;
-  }
-}
-
-template <class T, int ACC, bool F>
-__device__ __forceinline__ void dec_mma(const uint8_t* st, const DecSlot<T, F>& d, int lane,
+template <class T, int ACC>
+__device__ __forceinline__ void dec_mma(const uint8_t* st, const DecSlot<T>& d, int lane,
                                         v4f (&acc)[T::MT]) {
   const int r16 = lane & 15, kq = lane >> 4;
   if constexpr (ACC == 2) {  // power-of-two scales applied by the matrix cores (see mma_slice_big)
@@ -978,8 +934,7 @@ __device__ __forceinline__ void dec_mma(const uint8_t* st, const DecSlot<T, F>& 
   }
 }
 
-// F: the activation quantization is fused in (bf16 rows p.x instead of p.xq / p.sa).
-template <class T, int ACC, bool F>
+template <class T, int ACC>
 __global__ __launch_bounds__(T::NT) void gemm_decode_kernel(GemmArgs p) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[T::LDS_BYTES];
   __shared__ int s_flag;
@@ -995,36 +950,31 @@ __global__ __launch_bounds__(T::NT) void gemm_decode_kernel(GemmArgs p) {
   // in flight; it is staged into LDS buffer r & 1 with one barrier, multiplied, and its
   // registers refilled with round r + 2. All loads and waits are visible to the compiler: the
   // rounds are unrolled, so no branch separates a load from its use.
-  DecSlot<T, F> ring0[T::R], ring1[T::R];
-  float sa0 = F ? 0.f : dec_fetch_sa<T>(p, kb0, tid);
-  float sa1 = F ? 0.f : dec_fetch_sa<T>(p, kb0 + T::R, tid);
+  DecSlot<T> ring0[T::R], ring1[T::R];
+  float sa0 = dec_fetch_sa<T>(p, kb0, tid);
+  float sa1 = dec_fetch_sa<T>(p, kb0 + T::R, tid);
 #pragma unroll
-  for (int u = 0; u < T::R; ++u) dec_fetch<T>(ring0[u], p, wrow, swrow, kb0 + u, tid, u);
+  for (int u = 0; u < T::R; ++u) dec_fetch<T>(ring0[u], p, wrow, swrow, kb0 + u, tid);
 #pragma unroll
-  for (int u = 0; u < T::R; ++u) dec_fetch<T>(ring1[u], p, wrow, swrow, kb0 + T::R + u, tid, u);
+  for (int u = 0; u < T::R; ++u) dec_fetch<T>(ring1[u], p, wrow, swrow, kb0 + T::R + u, tid);
   v4f acc[T::MT];
 #pragma unroll
   for (int i = 0; i < T::MT; ++i) acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
   uint8_t* const buf0 = lds;
   uint8_t* const buf1 = lds + T::R * T::STAGE;
-  auto round = [&](DecSlot<T, F>(&ring)[T::R], float& sa, uint8_t* buf, int refill_kb) {
-    if constexpr (F) {
+  auto round = [&](DecSlot<T>(&ring)[T::R], float& sa, uint8_t* buf, int refill_kb) {
 #pragma unroll
-      for (int u = 0; u < T::R; ++u) dec_stage<T>(buf + u * T::STAGE, ring[u], tid, u, p.M, p.pow2);
-    } else {
-#pragma unroll
-      for (int u = 0; u < T::R; ++u) dec_stage<T>(buf + u * T::STAGE, ring[u], tid);
-      if (tid / T::MPA < T::R)
-        reinterpret_cast<float*>(buf + (tid / T::MPA) * T::STAGE + T::SA_OFF)[tid % T::MPA] = sa;
-    }
+    for (int u = 0; u < T::R; ++u) dec_stage<T>(buf + u * T::STAGE, ring[u], tid);
+    if (tid / T::MPA < T::R)
+      reinterpret_cast<float*>(buf + (tid / T::MPA) * T::STAGE + T::SA_OFF)[tid % T::MPA] = sa;
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < T::R; ++u) dec_mma<T, ACC>(buf + u * T::STAGE, ring[u], lane, acc);
     // refill only once consumed, so each set keeps its registers across the loop
     if (refill_kb >= 0) {
-      if constexpr (!F) sa = dec_fetch_sa<T>(p, refill_kb, tid);
+      sa = dec_fetch_sa<T>(p, refill_kb, tid);
 #pragma unroll
-      for (int u = 0; u < T::R; ++u) dec_fetch<T>(ring[u], p, wrow, swrow, refill_kb + u, tid, u);
+      for (int u = 0; u < T::R; ++u) dec_fetch<T>(ring[u], p, wrow, swrow, refill_kb + u, tid);
     }
   };
   for (int k0 = 0; k0 < L - 2 * T::R; k0 += 2 * T::R) {
@@ -1126,8 +1076,17 @@ struct Str {
   static constexpr int PARTS = MT * NB;  // 16x16 blocks per wave
 };
 
+// One slice of a wave in registers. Unfused form: the activation codes and scales as stored by
+// the 1x128 quantizer. Fused form (F, M <= kStrFusedRows): the slice's bf16 activation values
+// instead, 8 per lane -- the 16 lanes of DPP row r hold row r's 1x128 group, so its amax is one
+// row reduction -- quantized when the slice is multiplied.
+constexpr int kStrFusedRows = 4;
+
+template <class T, bool F>
+struct StrSlot;
+
 template <class T>
-struct StrSlot {
+struct StrSlot<T, false> {
   v8i w[T::NB];
   v8i x[T::MT];
   float sa[T::MT];
@@ -1135,34 +1094,80 @@ struct StrSlot {
 };
 
 template <class T>
-__device__ __forceinline__ void str_load(StrSlot<T>& s, const GemmArgs& p, int n0, int kb,
+struct StrSlot<T, true> {
+  static_assert(T::MT == 1, "fused form: one 16-row block");
+  v8i w[T::NB];
+  u32x4 xb;
+  float sw;
+};
+
+template <class T, bool F>
+__device__ __forceinline__ void str_load(StrSlot<T, F>& s, const GemmArgs& p, int n0, int kb,
                                          int r16, int kq) {
 #pragma unroll
   for (int j = 0; j < T::NB; ++j)
     s.w[j] = load_frag_global(p.wq + (int64_t)(n0 + 16 * j + r16) * p.K, kb, kq);
+  if constexpr (F) {
+    // lane l: values 8 (l % 16) .. + 7 of row l / 16 (rows past M repeat row M - 1)
+    const int lane = 16 * kq + r16;
+    const int m = min(lane >> 4, p.M - 1);
+    s.xb = *reinterpret_cast<const u32x4*>(p.x + (int64_t)m * p.ld_x + (int64_t)kb * 128 +
+                                           (lane & 15) * 8);
+  } else {
 #pragma unroll
-  for (int i = 0; i < T::MT; ++i) {
-    const int m = min(16 * i + r16, p.M - 1);
-    const u32x4* src = reinterpret_cast<const u32x4*>(p.xq + (int64_t)m * p.K + (int64_t)kb * 128 +
-                                                      kq * 32);
-    const u32x4 lo = src[0], hi = src[1];
-    s.x[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z,
-                 (int)hi.w};
-    s.sa[i] = p.sa[(int64_t)m * p.KB + kb];
+    for (int i = 0; i < T::MT; ++i) {
+      // rows past M repeat row M - 1: their products reach no stored output
+      const int m = min(16 * i + r16, p.M - 1);
+      const u32x4* src = reinterpret_cast<const u32x4*>(p.xq + (int64_t)m * p.K +
+                                                        (int64_t)kb * 128 + kq * 32);
+      const u32x4 lo = src[0], hi = src[1];
+      s.x[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z,
+                   (int)hi.w};
+      s.sa[i] = p.sa[(int64_t)m * p.KB + kb];
+    }
   }
   s.sw = p.sw[(int64_t)(n0 >> 7) * p.KB + kb];
 }
 
+// Fused form: the 1x128 activation quantizer's arithmetic on one slice (the same amax, scale and
+// element quotients, hence the same codes and scales), each of the M <= 4 live rows by one DPP
+// row of 16 lanes -- so the work does not grow with the 16-row padding of the matrix-core
+// operand. The codes and scales pass through this wave's own LDS area into the fragment layout
+// (lane l: row l % 16, K quarter l / 16; rows past M read row M - 1). LDS accesses of one wave
+// complete in order, so no barrier and no wait beyond the compiler's are needed.
+template <class T>
+__device__ __forceinline__ void str_quant(const StrSlot<T, true>& s, int M, int pow2,
+                                          uint8_t* codes, float* scales, int r16, int kq,
+                                          v8i (&xq)[1], float (&sa)[1]) {
+  const int lane = 16 * kq + r16, row = lane >> 4, c = lane & 15;
+  const uint32_t m = row16_max_u32(hmax_u16(amax8_pk(s.xb)));
+  const float fs = scale_from_amax_bits(m), ps = pow2_scale_from_amax_bits(m);
+  const float S = pow2 ? ps : fs;
+  const u32x2 q = quant8(s.xb, recip_f64(S));
+  if (row < M) {
+    *reinterpret_cast<u32x2*>(codes + row * 128 + c * 8) = q;
+    if (c == 0) scales[row] = S;
+  }
+  const int rr = min(r16, M - 1);
+  const u32x4* src = reinterpret_cast<const u32x4*>(codes + rr * 128 + kq * 32);
+  const u32x4 lo = src[0], hi = src[1];
+  xq[0] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z,
+              (int)hi.w};
+  sa[0] = scales[rr];
+}
+
 template <class T, int ACC>
-__device__ __forceinline__ void str_mma(const StrSlot<T>& s, v4f (&acc)[T::MT][T::NB]) {
+__device__ __forceinline__ void str_mma(const v8i (&w)[T::NB], const v8i (&x)[T::MT],
+                                        const float (&sa)[T::MT], float sw,
+                                        v4f (&acc)[T::MT][T::NB]) {
   if constexpr (ACC == 2) {
-    const int swe = e8m0_of(s.sw);
+    const int swe = e8m0_of(sw);
 #pragma unroll
     for (int i = 0; i < T::MT; ++i) {
-      const int se = e8m0_of(s.sa[i]);
+      const int se = e8m0_of(sa[i]);
 #pragma unroll
       for (int j = 0; j < T::NB; ++j) {
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(s.w[j], s.x[i], acc[i][j], 0,
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w[j], x[i], acc[i][j], 0,
                                                                      0, 0, swe, 0, se);
         asm volatile("" : "+v"(acc[i][j]));  // keep each slice's update in place
       }
@@ -1173,11 +1178,11 @@ __device__ __forceinline__ void str_mma(const StrSlot<T>& s, v4f (&acc)[T::MT][T
 #pragma unroll
   for (int i = 0; i < T::MT; ++i)
 #pragma unroll
-    for (int j = 0; j < T::NB; ++j) pr[i][j] = slice_product<ACC == 1>(s.w[j], s.x[i]);
+    for (int j = 0; j < T::NB; ++j) pr[i][j] = slice_product<ACC == 1>(w[j], x[i]);
   __builtin_amdgcn_sched_barrier(0);  // every product in flight before the first is consumed
 #pragma unroll
   for (int i = 0; i < T::MT; ++i) {
-    const float sc = s.sa[i] * s.sw;
+    const float sc = sa[i] * sw;
 #pragma unroll
     for (int j = 0; j < T::NB; ++j) {
       acc[i][j] += pr[i][j] * sc;
@@ -1186,9 +1191,14 @@ __device__ __forceinline__ void str_mma(const StrSlot<T>& s, v4f (&acc)[T::MT][T
   }
 }
 
-template <class T, int ACC>
+// F: bf16 activations p.x (pitch p.ld_x, scale format p.pow2; M <= kStrFusedRows) quantized in
+// the kernel instead of the codes p.xq and scales p.sa.
+template <class T, int ACC, bool F>
 __global__ __launch_bounds__(T::NT) void gemm_stream_kernel(GemmArgs p) {
   __shared__ __attribute__((aligned(16))) v4f red[T::WAVES][T::PARTS][64];
+  // fused form: each wave's staged codes (kStrFusedRows rows of one slice) and their scales
+  __shared__ __attribute__((aligned(16))) uint8_t xcodes[F ? T::WAVES : 1][kStrFusedRows * 128];
+  __shared__ float xscales[F ? T::WAVES : 1][kStrFusedRows];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, kq = lane >> 4;
@@ -1205,21 +1215,30 @@ __global__ __launch_bounds__(T::NT) void gemm_stream_kernel(GemmArgs p) {
   // operands are waited for with the D - 1 later slices still in flight): a slice past K is
   // loaded from the last slice and multiplied with zeroed activation codes, and the last round
   // (no refills) is peeled off.
-  StrSlot<T> ring[T::D];
-  auto mma = [&](StrSlot<T>& s, int kb) {
-    if (kb >= KB) {  // uniform: past K, zero products
+  StrSlot<T, F> ring[T::D];
+  auto mma = [&](StrSlot<T, F>& s, int kb) {
+    if constexpr (F) {
+      if (kb >= KB) s.xb = u32x4{0u, 0u, 0u, 0u};  // uniform: past K, zero codes and products
+      v8i xq[1];
+      float sa[1];
+      str_quant<T>(s, p.M, p.pow2, xcodes[F ? wave : 0], xscales[F ? wave : 0], r16, kq, xq, sa);
+      str_mma<T, ACC>(s.w, xq, sa, s.sw, acc);
+    } else {
+      if (kb >= KB) {  // uniform: past K, zero products
 #pragma unroll
-      for (int i = 0; i < T::MT; ++i) s.x[i] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+        for (int i = 0; i < T::MT; ++i) s.x[i] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+      }
+      str_mma<T, ACC>(s.w, s.x, s.sa, s.sw, acc);
     }
-    str_mma<T, ACC>(s, acc);
   };
 #pragma unroll
-  for (int u = 0; u < T::D; ++u) str_load<T>(ring[u], p, n0, min(wave + T::WAVES * u, KB - 1), r16, kq);
+  for (int u = 0; u < T::D; ++u)
+    str_load<T, F>(ring[u], p, n0, min(wave + T::WAVES * u, KB - 1), r16, kq);
   for (int t = 0; t < cnt - T::D; t += T::D) {
 #pragma unroll
     for (int u = 0; u < T::D; ++u) {
       mma(ring[u], wave + T::WAVES * (t + u));
-      str_load<T>(ring[u], p, n0, min(wave + T::WAVES * (t + u + T::D), KB - 1), r16, kq);
+      str_load<T, F>(ring[u], p, n0, min(wave + T::WAVES * (t + u + T::D), KB - 1), r16, kq);
     }
   }
 #pragma unroll
@@ -1391,7 +1410,7 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool rowb) {
     pl.workspace_bytes = 0;
     return pl;
   }
-  if (M <= 64 && KB % 2 == 0 && !rowb) return plan_fused_act(M, N, K);  // the split-K decode GEMM
+  if (M <= 64 && KB % 2 == 0 && !rowb) return plan_decode(M, N, K);  // the split-K decode GEMM
   // 64 x 64 tiles below 1024 rows: against 128 x 128 tiles split four ways over K they measured
   // 1.3-2x faster at 512-1000 rows (the split partials' round trip through memory outweighs the
   // larger tile's operand reuse); the 128 x 128 tiles stay for K beyond the DMA-fed tiles' reach
@@ -1420,13 +1439,10 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool rowb) {
   return pl;
 }
 
-GemmPlan plan_fused_act(int64_t M, int64_t N, int64_t K) {
+GemmPlan plan_decode(int64_t M, int64_t N, int64_t K) {
   GemmPlan pl{};
-  pl.cfg = -1;
   const int64_t KB = K / 128;
-  if (M < 1 || M > 64 || KB % 2 != 0) return pl;
-  // the decode GEMM with the activation quantization fused in: 64-column tiles, D slices in
-  // flight per wave (the largest of 8, 4, 2
+  // 1 <= M <= 64, KB even: 64-column tiles, D slices in flight per wave (the largest of 8, 4, 2
   // dividing KB); split K into ranges of L slices (L a multiple of D dividing KB) while there
   // are fewer than kDecWorkgroups workgroups and ranges keep at least kDecMinSlices slices
   constexpr int64_t BN = 64;
@@ -1448,6 +1464,23 @@ GemmPlan plan_fused_act(int64_t M, int64_t N, int64_t K) {
   const int64_t mp = M <= 16 ? 16 : M <= 32 ? 32 : 64;  // rows the kernel pads M to
   pl.workspace_bytes =
       S > 1 ? kWsHeaderBytes + (size_t)(tiles * S) * BN * mp * sizeof(float) : 0;
+  return pl;
+}
+
+GemmPlan plan_fused_act(int64_t M, int64_t N, int64_t K) {
+  GemmPlan pl = plan_gemm(M, N, K);
+  // up to kStrFusedRows rows the streaming kernel quantizes the activations itself (one launch,
+  // no workspace). Every workgroup quantizes all of X again, which pays only while that work is
+  // small against the weight stream: with 16 rows (and with 64 rows in the 64-column decode
+  // tiles) the fused kernel took 1.2x (1.4x) as long as two launches. Above, the codes and
+  // scales are staged in the workspace by the 1x128 quantizer and the GEMM of the same plan
+  // reads them: [GEMM workspace | codes | scales], each part 256-byte aligned. The counter header
+  // stays reserved even where this GEMM splits nothing, so that the workspace keeps it zero.
+  if (pl.cfg == kCfgStream && M <= kStrFusedRows) return pl;
+  const size_t a256 = 255;
+  pl.stage_off = std::max((pl.workspace_bytes + a256) & ~a256, kWsHeaderBytes);
+  const size_t codes = ((size_t)M * (size_t)K + a256) & ~a256;
+  pl.workspace_bytes = pl.stage_off + codes + (size_t)M * (size_t)(K / 128) * sizeof(float);
   return pl;
 }
 
@@ -1474,48 +1507,44 @@ static hipError_t launch_big(const GemmArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <class T, int ACC>
+template <class T, int ACC, bool F>
 static hipError_t launch_stream_t(const GemmArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((gemm_stream_kernel<T, ACC>), dim3((unsigned)(a.N / T::BN)), dim3(T::NT), 0,
-                     stream, a);
+  hipLaunchKernelGGL((gemm_stream_kernel<T, ACC, F>), dim3((unsigned)(a.N / T::BN)), dim3(T::NT),
+                     0, stream, a);
   return hipGetLastError();
 }
 
-template <int MT, int NB, int ACC>
+template <int MT, int NB, int ACC, bool F>
 static hipError_t launch_stream_d(const GemmArgs& a, const GemmPlan& pl, hipStream_t stream) {
-  if (pl.depth == 4) return launch_stream_t<Str<MT, NB, 4>, ACC>(a, stream);
-  return launch_stream_t<Str<MT, NB, 2>, ACC>(a, stream);
+  if (pl.depth == 4) return launch_stream_t<Str<MT, NB, 4>, ACC, F>(a, stream);
+  return launch_stream_t<Str<MT, NB, 2>, ACC, F>(a, stream);
 }
 
-template <int ACC>
+template <int ACC, bool F = false>
 static hipError_t launch_stream(const GemmArgs& a, const GemmPlan& pl, hipStream_t stream) {
-  if (pl.bn == 32) return launch_stream_d<1, 2, ACC>(a, pl, stream);
-  return launch_stream_d<1, 1, ACC>(a, pl, stream);
+  if (pl.bn == 32) return launch_stream_d<1, 2, ACC, F>(a, pl, stream);
+  return launch_stream_d<1, 1, ACC, F>(a, pl, stream);
 }
 
-template <class T, int ACC, bool F>
+template <class T, int ACC>
 static hipError_t launch_decode_t(const GemmArgs& a, const GemmPlan& pl, hipStream_t stream) {
-  hipLaunchKernelGGL((gemm_decode_kernel<T, ACC, F>),
+  hipLaunchKernelGGL((gemm_decode_kernel<T, ACC>),
                      dim3((unsigned)(a.N / T::BN), (unsigned)pl.splits), dim3(T::NT), 0, stream, a);
   return hipGetLastError();
 }
 
-template <int R, int ACC, bool F>
+template <int R, int ACC>
 static hipError_t launch_decode_d(const GemmArgs& a, const GemmPlan& pl, hipStream_t stream) {
-  if (a.M <= 16) return launch_decode_t<Dec<1, R>, ACC, F>(a, pl, stream);
-  if (a.M <= 32) return launch_decode_t<Dec<2, R>, ACC, F>(a, pl, stream);
-  return launch_decode_t<Dec<4, R>, ACC, F>(a, pl, stream);
+  if (a.M <= 16) return launch_decode_t<Dec<1, R>, ACC>(a, pl, stream);
+  if (a.M <= 32) return launch_decode_t<Dec<2, R>, ACC>(a, pl, stream);
+  return launch_decode_t<Dec<4, R>, ACC>(a, pl, stream);
 }
 
-template <int ACC, bool F = false>
+template <int ACC>
 static hipError_t launch_decode(const GemmArgs& a, const GemmPlan& pl, hipStream_t stream) {
-  // the fused form's register ring holds bf16 activations, twice the bytes of codes: above 32
-  // rows it keeps at most 4 slices in flight, so that two waves per SIMD still fit (the split
-  // lengths stay multiples of the smaller depth, as depths are powers of two)
-  const int depth = F && a.M > 32 && pl.depth > 4 ? 4 : pl.depth;
-  if (depth == 8) return launch_decode_d<4, ACC, F>(a, pl, stream);
-  if (depth == 4) return launch_decode_d<2, ACC, F>(a, pl, stream);
-  return launch_decode_d<1, ACC, F>(a, pl, stream);
+  if (pl.depth == 8) return launch_decode_d<4, ACC>(a, pl, stream);
+  if (pl.depth == 4) return launch_decode_d<2, ACC>(a, pl, stream);
+  return launch_decode_d<1, ACC>(a, pl, stream);
 }
 
 template <class T, bool PRECISE>
@@ -1607,8 +1636,6 @@ hipError_t launch_gemm(const uint8_t* xq, const float* sa, const uint8_t* wq, co
   return hipGetLastError();
 }
 
-bool plan_fuses_act(const GemmPlan& pl) { return pl.cfg == kCfgDecode; }
-
 // ---------------------------------------------------------------------------------------------
 // Scratch for the no-allocation entry point: one static device array per device (the code
 // object's copy on each device it is loaded on), used exactly like a caller's workspace --
@@ -1658,28 +1685,33 @@ hipError_t launch_gemm_fused_act(const uint16_t* x, int64_t ld_x, int pow2, cons
                                  const float* sw, int64_t M, int64_t N, int64_t K, void* y,
                                  int out_f32, int64_t ld_y, int accum, void* workspace,
                                  const GemmPlan& pl, hipStream_t stream) {
-  if (!plan_fuses_act(pl)) return hipErrorInvalidValue;
-  GemmArgs a{};
-  a.x = x;
-  a.ld_x = ld_x;
-  a.pow2 = pow2;
-  a.wq = wq;
-  a.sw = sw;
-  a.M = (int)M;
-  a.N = (int)N;
-  a.K = (int)K;
-  a.KB = (int)(K / 128);
-  a.y = y;
-  a.ldy = ld_y;
-  a.out_f32 = out_f32;
-  a.counters = pl.workspace_bytes > 0 ? reinterpret_cast<int*>(workspace) : nullptr;
-  a.ws = pl.workspace_bytes > 0
-             ? reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + kWsHeaderBytes)
-             : nullptr;
-  a.splits = pl.splits;
-  a.kb_per_split = pl.kb_per_split;
-  if (accum == 1) return launch_decode<1, true>(a, pl, stream);
-  return accum == 2 ? launch_decode<2, true>(a, pl, stream) : launch_decode<0, true>(a, pl, stream);
+  if (pl.cfg == kCfgStream && M <= kStrFusedRows) {
+    GemmArgs a{};
+    a.x = x;
+    a.ld_x = ld_x;
+    a.pow2 = pow2;
+    a.wq = wq;
+    a.sw = sw;
+    a.M = (int)M;
+    a.N = (int)N;
+    a.K = (int)K;
+    a.KB = (int)(K / 128);
+    a.y = y;
+    a.ldy = ld_y;
+    a.out_f32 = out_f32;
+    a.splits = 1;
+    a.kb_per_split = a.KB;
+    if (accum == 1) return launch_stream<1, true>(a, pl, stream);
+    return accum == 2 ? launch_stream<2, true>(a, pl, stream) : launch_stream<0, true>(a, pl, stream);
+  }
+  // staged: quantize into the workspace behind the GEMM's own part, then the GEMM on the codes
+  uint8_t* xq = reinterpret_cast<uint8_t*>(workspace) + pl.stage_off;
+  float* sa = reinterpret_cast<float*>(xq + ((((size_t)M * (size_t)K) + 255) & ~size_t{255}));
+  hipError_t e = launch_quant_act(x, M, K, ld_x, xq, K, sa, pow2, stream);
+  if (e != hipSuccess) return e;
+  // the GEMM's own plan: its workspace size alone decides whether it splits K
+  return launch_gemm(xq, sa, wq, sw, M, N, K, y, out_f32, ld_y, accum, 0, workspace,
+                     plan_gemm(M, N, K), stream);
 }
 
 hipError_t launch_grouped_gemm(const uint8_t* xq, const float* sa, const uint8_t* wq,

@@ -94,6 +94,7 @@ struct GemmPlan {
   int kb_per_split;
   int depth;   // decode path: K slices in flight per wave
   size_t workspace_bytes;
+  size_t stage_off;  // fused activation quantization: workspace offset of the staged codes
 };
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool rowb = false);
 GemmPlan plan_grouped_gemm(int64_t M_total, int64_t N, int64_t K, int32_t E);
@@ -108,11 +109,13 @@ hipError_t launch_gemm(const uint8_t* xq, const float* sa, const uint8_t* wq, co
 // its counter header on the first use there (a fill kernel enqueued on `stream`).
 constexpr size_t kScratchBytes = size_t{32} << 20;
 hipError_t gemm_scratch(hipStream_t stream, void** ptr);
-// The decode GEMM (M <= 64) with the 1x128 activation quantization fused into its staging: bf16
-// X [M][ld_x] in place of xq / sa (pow2: scale format of the groups). Only for plans with
-// plan_fuses_act(plan), plans from plan_fused_act (its own workspace rule).
+// The split-K decode GEMM's plan (1 <= M <= 64, K/128 even).
+GemmPlan plan_decode(int64_t M, int64_t N, int64_t K);
+// The GEMM with the 1x128 activation quantization fused in: bf16 X [M][ld_x] in place of xq / sa
+// (pow2: scale format of the groups). Up to 16 rows one kernel quantizes in registers; above,
+// the codes are staged in the workspace (from plan.stage_off) and the plan's GEMM reads them.
+// Plans from plan_fused_act (its own workspace size).
 GemmPlan plan_fused_act(int64_t M, int64_t N, int64_t K);
-bool plan_fuses_act(const GemmPlan& plan);
 hipError_t launch_gemm_fused_act(const uint16_t* x, int64_t ld_x, int pow2, const uint8_t* wq,
                                  const float* sw, int64_t M, int64_t N, int64_t K, void* y,
                                  int out_f32, int64_t ld_y, int accum, void* workspace,

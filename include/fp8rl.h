@@ -10,9 +10,9 @@
  *      per 1x128 group                         (fp8rl_quant_act_tok128);
  *   3. the blockwise-scaled FP8 GEMM Y = X W^T that consumes both
  *                                             (fp8rl_gemm_w8a8_blockscaled),
- *      and its mixture-of-experts grouped form (fp8rl_grouped_gemm_w8a8), and for decode
- *      shapes a form that takes bf16 activations and quantizes them inside the GEMM
- *      (fp8rl_gemm_w8a8_fused_act_quant);
+ *      and its mixture-of-experts grouped form (fp8rl_grouped_gemm_w8a8), and a form that
+ *      takes bf16 activations and quantizes them itself, inside the GEMM kernel for decode
+ *      shapes (fp8rl_gemm_w8a8_fused_act_quant);
  *   plus the element-wise E4M3 encoder the quantizers share (fp8rl_encode_e4m3_f32), and the
  *   per-tensor FP8 of attention Q/K/V activations and the KV cache with per-step recalibrated
  *   scales (fp8rl_amax_bf16, fp8rl_scale_from_amax, fp8rl_quant_bf16_per_tensor and their
@@ -292,24 +292,26 @@ int fp8rl_gemm_w8a8_blockscaled_noalloc(const uint8_t* xq, const float* sa, cons
                                         int y_dtype, int64_t ld_y, int accum, void* stream);
 
 /*
- * The blockwise-scaled GEMM with the activation quantization fused in, for small token counts
- * (decode: M <= 64). [NEMO, speed-up discussion of the Llama 3 8B results: the quantization
- * kernels placed before each linear are overhead, and fusing them is expected to raise the gain
- * further; UFP8, limitations paragraph: at the small batches of RL the extra quantize steps
- * leave the GPU under-fed.] It multiplies exactly the codes and scales that
- * fp8rl_quant_act_tok128_ex(x, scale_fmt) produces: each workgroup quantizes the 1x128 groups of
- * the K range it multiplies as it stages them, so the FP8 activations never go to memory and one
- * launch replaces two. Its result meets the same accuracy contract as quantizing first and calling
- * fp8rl_gemm_w8a8_blockscaled (the two kernels sum the K slices in different fixed orders, so the
- * last bits of the two results can differ).
+ * The blockwise-scaled GEMM on bf16 activations: quantize X in 1x128 groups and multiply, in one
+ * call. [NEMO, speed-up discussion of the Llama 3 8B results: the quantization kernels placed
+ * before each linear are overhead, and fusing them is expected to raise the gain further; UFP8,
+ * limitations paragraph: at the small batches of RL the extra quantize steps leave the GPU
+ * under-fed.] The result is bit-identical to fp8rl_quant_act_tok128_ex(x, scale_fmt) followed by
+ * fp8rl_gemm_w8a8_blockscaled with the same accum. For M <= 4 it is one kernel: every workgroup
+ * quantizes the activation slices it multiplies, so the FP8 activations never go to memory.
+ * Above 4 rows that repeated quantization (every value once per 16- or 32-column tile) costs
+ * more than the launch it saves, so the call stages the codes and scales in the workspace with
+ * the 1x128 quantizer and runs the GEMM on them: two kernels, one call.
  *   x      : bf16 activations X, M rows of pitch ld_x (>= K; ld_x * 2 a multiple of 16)
  *   wq, sw, y, ld_y, accum : as for fp8rl_gemm_w8a8_blockscaled
  *   scale_fmt : FP8RL_SCALE_FP32 or FP8RL_SCALE_POW2, the activation groups' scale format;
  *            FP8RL_ACCUM_MX requires FP8RL_SCALE_POW2 (and power-of-two weight scales)
  *   workspace, workspace_bytes: at least fp8rl_workspace_bytes(FP8RL_OP_GEMM_FUSED_ACT, M, N, K,
- *            0) bytes, same rules as the dense GEMM's workspace
- * Requires N % 128 == 0, K % 128 == 0, 1 <= M <= 64 and K/128 even (the decode tiling);
- * FP8RL_ERR_SHAPE otherwise (M == 0 returns FP8RL_OK). Deterministic.
+ *            0) bytes (0 for M <= 4; above, the GEMM's own workspace followed by the staged
+ *            codes and scales), 16-byte aligned, its first FP8RL_WORKSPACE_HEADER_BYTES zero
+ *            before the first use (calls leave them zero)
+ * Requires N % 128 == 0 and K % 128 == 0 (FP8RL_ERR_SHAPE otherwise; M == 0 returns FP8RL_OK).
+ * Deterministic.
  */
 int fp8rl_gemm_w8a8_fused_act_quant(const uint16_t* x, int64_t ld_x, const uint8_t* wq,
                                     const float* sw, int64_t M, int64_t N, int64_t K, void* y,

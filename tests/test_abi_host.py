@@ -250,8 +250,6 @@ def test_fused_act_gemm_validation(L):
     assert call(sw=None) == ENULL
     assert call(N=200) == ESHAPE
     assert call(ldx=4000) == ESHAPE  # pitch below K
-    assert call(M=65) == ESHAPE  # decode shapes only
-    assert call(K=384, ldx=384) == ESHAPE  # odd number of K slices
     assert call(dt=2) == EDTYPE
     assert call(acc=4) == EARG
     assert call(sf=2) == EARG
@@ -259,10 +257,11 @@ def test_fused_act_gemm_validation(L):
     assert call(x=A + 2) == EALIGN
     assert call(ldx=4100) == EALIGN  # 8200-byte bf16 pitch
     need = L.fp8rl_workspace_bytes(3, 64, 256, 4096, 0)
-    assert need > 0  # the fused decode kernel splits K over workgroups
+    assert need > 0  # above 16 rows the codes and scales are staged in the workspace
     assert call(wsb=need - 1) == EWS
     assert call(ws=None) == EWS
-    assert L.fp8rl_workspace_bytes(3, 65, 256, 4096, 0) == 0  # not a fused shape
+    assert call(M=65, wsb=L.fp8rl_workspace_bytes(3, 65, 256, 4096, 0) - 1) == EWS
+    assert call(K=384, ldx=384, wsb=L.fp8rl_workspace_bytes(3, 64, 256, 384, 0) - 1) == EWS
 
 
 def test_grouped_gemm_validation(L):
@@ -293,8 +292,7 @@ def test_workspace_query_is_pure_host(L):
     hdr = _lib.WORKSPACE_HEADER_BYTES
     assert hdr == 4096  # FP8RL_WORKSPACE_HEADER_BYTES
     # the blockscaled GEMM up to 16 rows splits K only inside each workgroup (no workspace); the
-    # decode GEMM above that and the fused-activation decode GEMM (op 3) split K over workgroups:
-    # 64-column
+    # decode GEMM above that (up to 64 rows, K/128 even) splits K over workgroups: 64-column
     # tiles, K split into S ranges of whole rounds of D slices (D = 8, 4 or 2 dividing K/128)
     # while fewer than 512 workgroups and ranges of >= 8 slices; workspace = header + [tiles][S]
     # partial tiles of 64 columns x padded rows (16, 32 or 64) float32
@@ -310,14 +308,31 @@ def test_workspace_query_is_pure_host(L):
             S = s_
         mp = 16 if M <= 16 else 32 if M <= 32 else 64
         return hdr + tiles * S * 64 * mp * 4 if S > 1 else 0
-    for shape in [(64, 4096, 4096), (20, 1024, 12288), (64, 12288, 4096), (1, 256, 2048)]:
-        assert L.fp8rl_workspace_bytes(3, *shape, 0) == dec(*shape) > 0, shape
-        blk = L.fp8rl_workspace_bytes(0, *shape, 0)
-        assert blk == (0 if shape[0] <= 16 else dec(*shape)), shape
-    assert L.fp8rl_workspace_bytes(3, 64, 4096, 4096, 0) == hdr + 64 * 4 * 64 * 64 * 4
-    assert L.fp8rl_workspace_bytes(3, 64, 4096, 1024, 0) == 0  # 8 slices: one range
-    assert L.fp8rl_workspace_bytes(3, 8, 131072, 2048, 0) == 0  # more tiles than counters
-    assert L.fp8rl_workspace_bytes(3, 64, 4096, 384, 0) == 0  # odd K/128: no fused form
+    def a256(n):
+        return (n + 255) // 256 * 256
+
+    # the GEMM on bf16 activations (op 3): one kernel and no workspace up to 4 rows; above, the
+    # blockscaled GEMM's workspace (its counter header reserved even when it splits nothing),
+    # then the staged codes and their scales, each part 256-byte aligned
+    def fused(M, N, K):
+        if M <= 4:
+            return 0
+        return (max(a256(L.fp8rl_workspace_bytes(0, M, N, K, 0)), hdr) + a256(M * K)
+                + M * (K // 128) * 4)
+    for shape in [(64, 4096, 4096), (20, 1024, 12288), (64, 12288, 4096)]:
+        assert L.fp8rl_workspace_bytes(0, *shape, 0) == dec(*shape) > 0, shape
+    for shape in [(64, 4096, 4096), (20, 1024, 12288), (64, 12288, 4096), (1, 256, 2048),
+                  (4, 4096, 4096), (5, 4096, 4096), (16, 4096, 4096), (17, 4096, 4096),
+                  (65, 256, 4096), (64, 4096, 384),
+                  (300, 768, 2048), (8192, 4096, 4096)]:
+        assert L.fp8rl_workspace_bytes(3, *shape, 0) == fused(*shape), shape
+    assert L.fp8rl_workspace_bytes(3, 64, 4096, 4096, 0) == (hdr + 64 * 4 * 64 * 64 * 4
+                                                             + 64 * 4096 + 64 * 32 * 4)
+    assert L.fp8rl_workspace_bytes(3, 8192, 4096, 4096, 0) == hdr + 8192 * 4096 + 8192 * 32 * 4
+    assert L.fp8rl_workspace_bytes(3, 1, 256, 2048, 0) == 0
+    assert L.fp8rl_workspace_bytes(0, 64, 4096, 1024, 0) == 0  # 8 slices: one range
+    assert L.fp8rl_workspace_bytes(0, 32, 131072, 2048, 0) == 0  # more tiles than counters
+    assert L.fp8rl_workspace_bytes(0, 64, 4096, 384, 0) == 0  # odd K/128: 64x64 tiles, K unsplit
     assert L.fp8rl_workspace_bytes(0, 0, 256, 256, 0) == 0
     assert L.fp8rl_workspace_bytes(0, 8192, 4096, 4096, 0) == 0  # large M: no split
     assert L.fp8rl_workspace_bytes(1, 32768, 1536, 2048, 128) == 0

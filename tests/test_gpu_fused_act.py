@@ -1,11 +1,13 @@
-"""GPU parity of the decode GEMM with the activation quantization fused in.
+"""GPU parity of the GEMM on bf16 activations (activation quantization fused in).
 
 fp8rl_gemm_w8a8_fused_act_quant takes bf16 activations; its result must equal, within the GEMM
 contract (|gpu - ref| <= 2^-7 |ref| + 1e-3 rms(ref) for bf16 output, <= 1e-5 rms(ref) for float32
 output with f16 slice sums), the oracle's GEMM of the oracle's 1x128 quantization of the same
-activations; the library's unfused path (quantize, then GEMM) must meet the same contract. Inputs:
-seeded synthetic activations (N(0, 1) with outlier channels) and weights of the decode shapes,
-plus edge rows.
+activations, and be bit-identical to the library's two-launch path (quantize, then GEMM): up to
+4 rows one kernel quantizes exactly as the quantizer does and multiplies in the blockscaled
+GEMM's order, above that the call runs those two kernels itself. Inputs: seeded
+synthetic activations (N(0, 1) with outlier channels) and weights of the decode shapes, larger
+token counts on every GEMM path, plus edge rows.
 """
 
 import numpy as np
@@ -48,16 +50,20 @@ def _check(x: torch.Tensor, wq, sw, what, scale="fp32", outs=("bf16", "f32"), ac
         else:
             ref = ref64.astype(np.float32).astype(np.float64)
         worst[out] = assert_gemm_close(got, ref, ref64, out, what)
-        # the two-launch path (activation codes and scales bit-exact against the oracle, checked
-        # elsewhere) meets the same contract; its kernel sums the slices in another order
-        assert_gemm_close(gemm_out_to_f64(y_unfused), ref, ref64, out, what + " (two launches)")
+        # the two-launch path: activation codes and scales bit-exact against the oracle (checked
+        # elsewhere), the same GEMM kernel and slice order, hence the same bits
+        assert torch.equal(y, y_unfused), what + " (two launches)"
     print(f"    worst err/bound {worst}", flush=True)
 
 
 @pytest.mark.parametrize("M,N,K", [(64, 4096, 4096), (64, 6144, 4096), (64, 4096, 12288),
                                    (1, 128, 256), (3, 384, 768), (17, 256, 16384),
                                    (20, 512, 1024), (32, 2048, 2048), (33, 1024, 1280),
-                                   (48, 12288, 4096), (8, 65664, 256), (64, 1024, 512)])
+                                   (48, 12288, 4096), (8, 65664, 256), (64, 1024, 512),
+                                   (16, 4096, 4096), (16, 2048, 384), (5, 8192, 1152),
+                                   (2, 1024, 384), (4, 4096, 4096), (4, 6144, 12288),
+                                   (65, 256, 384), (100, 1024, 4096), (300, 768, 2048),
+                                   (256, 16384, 1024)])
 def test_decode_shapes(M, N, K):
     x = synth.act_bf16(M, K, seed=synth.seed_of(60, M * 7919 + N, K)).cuda()
     _check(x, *_weights(N, K, synth.seed_of(61, N, K)), f"decode {M}x{N}x{K}")
@@ -93,6 +99,25 @@ def test_edge_rows():
     _check(x.cuda(), wq, sw, "edge rows")
 
 
+def test_edge_rows_single_kernel():
+    """The one-kernel form (M <= 4): a zero row, a row of huge values, a bf16-subnormal row and
+    groups 2^4 apart in scale with one dominant outlier."""
+    M, K = 4, 2048
+    x = synth.act_bf16(M, K, seed=synth.seed_of(68, 0))
+    x[0] = 0.0
+    x[1] = 1.0e30
+    x[1, ::3] = -1.0e30
+    x[2] = torch.tensor(1e-40, dtype=torch.bfloat16)
+    x[3, 7] = 1e4
+    for g in range(K // 128):
+        x[3, 128 * g:128 * (g + 1)] *= 2.0 ** (-30 + 4 * g)
+    wq, sw = _weights(1024, K, synth.seed_of(68, 1))
+    _check(x.cuda(), wq, sw, "edge rows, one kernel")
+    wq, sw = _weights(1024, K, synth.seed_of(68, 2), scale="pow2")
+    _check(x.cuda(), wq, sw, "edge rows, one kernel, pow2", scale="pow2", accum="mx",
+           outs=("bf16",))
+
+
 def test_power_of_two_scales_both_accumulations():
     x = synth.act_bf16(64, 4096, seed=synth.seed_of(65, 0)).cuda()
     wq, sw = _weights(2048, 4096, synth.seed_of(65, 1), scale="pow2")
@@ -121,7 +146,8 @@ def test_f16_slices_float32_output():
 
 
 def test_workspace_reuse_determinism_and_canary():
-    shapes = [(64, 4096, 4096), (20, 1024, 12288), (64, 4096, 4096), (1, 256, 2048)]
+    shapes = [(64, 4096, 4096), (20, 1024, 12288), (300, 768, 2048), (64, 4096, 4096),
+              (1, 256, 2048), (65, 512, 1024)]
     need = max(fq.fp8rl_workspace_bytes(fq.FP8RL_OP_GEMM_FUSED_ACT, *s) for s in shapes)
     ws = fq.new_workspace(need, "cuda")
     ws[fq.WORKSPACE_HEADER_BYTES:].fill_(0xC3)
@@ -147,5 +173,6 @@ def test_zero_rows_and_rejected_shapes():
     sw = torch.ones((2, 2), dtype=torch.float32, device="cuda")
     y = fq.gemm_fused_act(torch.empty((0, 256), dtype=torch.bfloat16, device="cuda"), w, sw)
     assert y.shape == (0, 256)
-    with pytest.raises(fq.Fp8rlError):  # prefill-sized M: not a fused shape (host check)
-        fq.gemm_fused_act(torch.zeros((65, 256), dtype=torch.bfloat16, device="cuda"), w, sw)
+    with pytest.raises(fq.Fp8rlError):  # N not a multiple of 128 (host check)
+        fq.gemm_fused_act(torch.zeros((4, 256), dtype=torch.bfloat16, device="cuda"),
+                          torch.zeros((200, 256), dtype=torch.uint8, device="cuda"), sw)
