@@ -5,7 +5,8 @@ tokens, hidden 4096, 7 linears: q/o 4096x4096, k/v 1024x4096, gate/up 12288x4096
 4096x12288). One step is the dynamic 1x128 quantization of each distinct bf16 input activation
 and the blockwise-scaled FP8 GEMMs (bf16 output), replayed from a HIP graph. `value` is the GEMM
 TFLOP/s of the step (2MNK over the 7 linears / step time); `roofline` is the largest GEMM's kernel
-(gate/up, 8192 x 24576 x 4096), timed per launch with HIP events on the stream it runs on. Parts
+(gate/up, 8192 x 24576 x 4096), its launches replayed from a HIP graph and timed with HIP events
+on the stream they run on. Parts
 of the same line: every GEMM's launch time, the 32-layer Llama-3.1-8B weight sync (20.94 GB of
 algorithmic traffic per pass) and the decode step below.
 
@@ -27,8 +28,8 @@ sample of the same workload on this host's cores).
 Other workloads (`--workload`): llama31-8b-mlp (M in {256, 4096}), llama31-8b-weight-sync (32
 layers of weights), qwen3-30b-a3b-moe (grouped expert GEMMs), qwen3-8b-kv-cache (per-tensor Q/K/V
 recalibration and FP8 KV-cache store over 36 layers), qwen3-8b-backward (FP8 Dgrad and Wgrad of
-the decoder block's linears over 8192 tokens), qwen3-8b-decode-fused-act (decode GEMMs with the
-activation quantization fused in, against two launches).
+the decoder block's linears over 8192 tokens), qwen3-8b-decode-fused-act (decode GEMMs on bf16
+activations, the activation quantization fused in, against two calls per GEMM).
 """
 
 from __future__ import annotations
