@@ -181,6 +181,73 @@ def test_zero_rows_noop():
     assert y.shape == (0, 256)
 
 
+@pytest.mark.parametrize("M", [16, 64, 256, 1024])
+def test_fp8_slice_truncation_model(M):
+    """The behaviour behind fp8_slice_bound, pinned on every dense kernel path (streaming, split-K
+    decode, 64x64 tiles, DMA-fed 256-row tiles): in one 32-wide K block of a slice, products
+    +448^2, -448^2 and a small p = v * w. The FP8 matrix cores align the products to the largest
+    (2^17.6, so E = 17) and drop the bits below 2^(E - 14) = 8, so the slice sums to p truncated
+    to a multiple of 8; the f16 slice sums keep p exactly. Scales 1, bf16 output (every value
+    here is exact in bf16)."""
+    from oracle import e4m3
+
+    vs = np.array([0.5, 1.5, 3.0, 3.5, 5.0, 6.5, 7.0, 13.0, 15.0, 11.0, 9.0, 2.75, 4.5, 10.0,
+                   0.75, 12.0], np.float32)
+    ws = np.array([1.0, 1.25, 2.0, 2.5, 4.0, 8.0, 3.0, 0.5], np.float32)
+    N, K = 128, 256
+    xq = np.zeros((M, K), np.uint8)
+    wq = np.zeros((N, K), np.uint8)
+    v = vs[np.arange(M) % len(vs)]
+    w = ws[np.arange(N) % len(ws)]
+    for kb in range(K // 128):  # the same pattern in each slice, the first 3 K of the slice
+        xq[:, 128 * kb + 0] = e4m3.encode(np.float32(448.0))
+        xq[:, 128 * kb + 1] = e4m3.encode(np.float32(448.0))
+        xq[:, 128 * kb + 2] = e4m3.encode(v)
+        wq[:, 128 * kb + 0] = e4m3.encode(np.float32(448.0))
+        wq[:, 128 * kb + 1] = e4m3.encode(np.float32(-448.0))
+        wq[:, 128 * kb + 2] = e4m3.encode(w)
+    sa = np.ones((M, K // 128), np.float32)
+    sw = np.ones((N // 128, K // 128), np.float32)
+    d = [to_dev_u8(xq), to_dev_f32(sa), to_dev_u8(wq), to_dev_f32(sw)]
+    p = np.outer(v.astype(np.float64), w.astype(np.float64))
+    exact = (K // 128) * p
+    truncated = (K // 128) * np.floor(p / 8.0) * 8.0
+    y8 = gemm_out_to_f64(fq.gemm(*d, accum="fp8"))
+    y16 = gemm_out_to_f64(fq.gemm(*d, accum="f16"))
+    torch.cuda.synchronize()
+    print(f"[fp8 truncation] M={M}: {int((p % 8 != 0).sum())} of {p.size} products lose bits",
+          flush=True)
+    np.testing.assert_array_equal(y16, exact)
+    np.testing.assert_array_equal(y8, truncated)
+
+
+def test_side_stream_without_workspace():
+    """Calls on a stream other than torch's current one, with no workspace: the bindings
+    allocate the split-K workspace and the output on that stream and zero the counter header
+    there, so the zero fill is ordered before the kernels and a freed temporary goes to another
+    allocation only behind that stream's work. Split-K decode GEMM and the staged GEMM on bf16
+    activations, three calls each, against the oracle."""
+    M, N, K = 64, 4096, 4096
+    assert fq.fp8rl_workspace_bytes(fq.FP8RL_OP_GEMM, M, N, K) > 0
+    x = synth.act_bf16(M, K, seed=synth.seed_of(80, 0))
+    w = synth.weight_bf16(N, K, seed=synth.seed_of(80, 1), outlier_frac=0.001)
+    xq, sa = oq.quant_act_tok128(bits16(x))
+    wq, sw = oq.quant_weight_blk128(bits16(w))
+    d = [to_dev_u8(xq), to_dev_f32(sa), to_dev_u8(wq), to_dev_f32(sw)]
+    xd = x.cuda()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    ys = [fq.gemm(*d, stream=s) for _ in range(3)]
+    ys += [fq.gemm_fused_act(xd, d[2], d[3], stream=s) for _ in range(3)]
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    ref64 = og.gemm_blockscaled(xq, sa, wq, sw, out="f64")
+    ref = og.bf16_bits_to_f64(og.round_f64_to_bf16_bits(ref64))
+    for i, y in enumerate(ys):
+        assert_gemm_close(gemm_out_to_f64(y), ref, ref64, "bf16", f"side stream call {i}")
+        assert torch.equal(y, ys[0]), i
+
+
 # ------------------------------------------------------------------------------- grouped GEMM
 
 
