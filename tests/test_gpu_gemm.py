@@ -303,6 +303,24 @@ def test_grouped_small_with_empty_and_single_row_experts():
     run_grouped(*grouped_operands([0, 1, 130, 0, 5, 257, 0], 256, 384, 71), "ragged experts")
 
 
+@pytest.mark.parametrize("accum", [None, "mx"])
+def test_grouped_tile_boundaries(accum):
+    """Experts with row counts on both sides of every multiple of 128 up to 1024 (partial, full
+    and multiple m-tiles per expert, empty experts between them), FP32 and power-of-two scales."""
+    counts = [0, 1, 255, 256, 257, 300, 383, 384, 385, 511, 512, 513, 700, 0, 1024, 129]
+    scale = "pow2" if accum == "mx" else "fp32"
+    xq, sa, wq, sw, off = grouped_operands(counts, 512, 1024, 70)
+    if scale == "pow2":
+        x = synth.act_bf16(int(sum(counts)), 1024, seed=70)
+        w = synth.weight_bf16(512, 1024, seed=71, batch=len(counts))
+        xq, sa = oq.quant_act_tok128(bits16(x), scale="pow2")
+        wb = bits16(w)
+        for e in range(len(counts)):
+            wq[e], sw[e] = oq.quant_weight_blk128(wb[e], scale="pow2")
+    run_grouped(xq, sa, wq, sw, off, f"tile boundaries ({scale})",
+                outs=("bf16",) if accum == "mx" else ("bf16", "f32"), accum=accum)
+
+
 def test_grouped_single_expert_equals_dense_path():
     xq, sa, wq, sw, off = grouped_operands([300], 384, 512, 72)
     run_grouped(xq, sa, wq, sw, off, "one expert")
