@@ -272,6 +272,9 @@ class DenseBlock:
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "quant_weight_blk128__qwen3-8b-decode-step.traffic.txt")
 PREFILL_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_big_kernel__qwen3-8b-prefill.traffic.txt")
+WSYNC_TRAFFIC_FILE = os.path.join(ROOT, "profiles",
+                                  "quant_weight_blk128__llama31-8b-weight-sync.traffic.txt")
+MOE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "grouped_big_kernel__qwen3-30b-a3b-moe.traffic.txt")
 
 
 def measured_traffic(path=TRAFFIC_FILE):
@@ -953,7 +956,8 @@ def run_weight_sync(args, torch, fq, synth, gpu, quant_cpu):
     roof = roof_hbm(WQ_KERNEL, sync.bytes / len(sync.descs), r["avg_us"],
                     "3 B per weight element + 4 B per 128x128 block",
                     "32 weight matrices (about 3 GB of algorithmic traffic) per launch, 7 launches "
-                    "per pass; achieved = all bytes over all launch time")
+                    "per pass; achieved = all bytes over all launch time",
+                    traffic=measured_traffic(WSYNC_TRAFFIC_FILE) if args.scales == "fp32" else None)
     roof["achieved"] = r["gbs"]
     roof["frac"] = r["gbs"] / HBM_PEAK_GBS
     cfg = {"workload": "Llama-3.1-8B weight sync: all linear weights of 32 layers re-quantized "
@@ -1269,7 +1273,8 @@ def run_moe(args, torch, fq, synth, gpu, quant_cpu):
     roof = roof_hbm("grouped_big_kernel", (b1 + b2) / 2, r["avg_us"],
                     "activation codes + scales + every expert's weight codes and block scales "
                     "once + bf16 output",
-                    "one grouped GEMM (gate/up or down; average of the two)")
+                    "one grouped GEMM (gate/up or down; average of the two)",
+                    traffic=measured_traffic(MOE_TRAFFIC_FILE) if args.scales == "fp32" else None)
     roof["frac_roofline"] = roof_us / (1e3 * g_ms)
     roof["roofline_rule"] = ("per GEMM max(2MNK / 5.0 PFLOP/s, bytes / 8 TB/s), every expert's "
                              "weights read once")
