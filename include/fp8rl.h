@@ -102,9 +102,10 @@ typedef enum {
  *                    bf16 output only. Every sa and sw must be a power of two in [2^-127, 2^127]
  *                    (what the FP8RL_SCALE_POW2 quantizers produce); for any other scale value
  *                    the result is undefined (the scales are not inspected on the host, which
- *                    would need a synchronization). Shapes without such a kernel (64 < M < 1024,
- *                    or an odd K/128 at M <= 64) compute as FP8RL_ACCUM_FP8, which gives the same
- *                    results for power-of-two scales.
+ *                    would need a synchronization). Shapes that run on the register-staged
+ *                    64x64 tiles (17-1023 rows where the large DMA-fed tiles do not apply, an odd
+ *                    K/128 at 17-64 rows, K > 32768) compute as FP8RL_ACCUM_FP8, which gives the
+ *                    same results for power-of-two scales.
  *   FP8RL_ACCUM_AUTO the form that keeps the result within the library's accuracy contract
  *                    (elementwise |y - exact| <= 2^-7 |exact| + 1e-3 rms(exact) for bf16 output,
  *                    <= 1e-5 rms(exact) for float32 output, exact = the float64 sum over the
