@@ -118,14 +118,15 @@ def oq_bf16(bits):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 256, 256), (64, 1024, 1024), (200, 384, 512), (640, 512, 1024),
-                                   (1024, 1024, 2048), (4096, 4096, 1024), (1100, 640, 640)])
+                                   (1024, 1024, 2048), (4096, 4096, 1024), (1100, 640, 640),
+                                   (300, 16384, 512)])
 @pytest.mark.parametrize("accum", [None, "fp8", "mx"])
 def test_rowscaled_gemm_bf16(M, N, K, accum):
     _check_rowscaled(M, N, K, "bf16", accum, pow2=accum == "mx")
 
 
 @pytest.mark.parametrize("M,N,K", [(64, 256, 512), (512, 512, 512), (1024, 512, 1024),
-                                   (4096, 1024, 2048)])
+                                   (4096, 1024, 2048), (300, 16384, 512)])
 @pytest.mark.parametrize("accum", [None, "f16"])
 def test_rowscaled_gemm_f32(M, N, K, accum):
     _check_rowscaled(M, N, K, "f32", accum, seed=1)

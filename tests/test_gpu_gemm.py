@@ -83,6 +83,18 @@ def test_large_m_shapes(M, N, K):
     run_and_check(*quantized_operands(M, N, K, 2000 + M + N + K), f"large-M {M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("M,N,K", [(200, 16384, 1024), (777, 6144, 2048), (192, 24576, 512),
+                                   (300, 32768, 384)])
+def test_mid_m_on_dma_fed_tiles(M, N, K):
+    """192-1023 rows with at least 128 tiles of 256x128: the DMA-fed 256-row tiles, the last (or
+    only) m-tile part-filled (200 and 192 rows: one tile; 777 rows: 9 rows in the last; 300 rows,
+    K = 384: three slices), both outputs (float32 through the f16 tiles)."""
+    from fp8_blockwise_quantization_amd import _lib
+
+    assert _lib.lib().fp8rl_workspace_bytes(0, M, N, K, 0) == 0  # no split: the large tiles
+    run_and_check(*quantized_operands(M, N, K, 2100 + M + N + K), f"mid-M {M}x{N}x{K}")
+
+
 @pytest.mark.parametrize("M,N,K", [(96, 256, 512), (700, 640, 768), (64, 1024, 4096)])
 def test_random_codes_and_scales_f16_slices(M, N, K):
     run_and_check(*random_operands(M, N, K, 3000 + M), f"random {M}x{N}x{K}", accum="f16")
