@@ -1285,13 +1285,52 @@ def run_moe(args, torch, fq, synth, gpu, quant_cpu):
     parts = {"grouped_gemm": dict(r, tflops=flops / (g_ms * 1e-3) / 1e12, roofline_us=roof_us,
                                   frac_roofline=roof_us / (1e3 * g_ms)),
              "expert_requant": dict(rq, bytes=wq_bytes, frac_hbm=rq["gbs"] / HBM_PEAK_GBS,
-                                    what="all 2 x 128 expert weights, one batched launch")}
+                                    what="all 2 x 128 expert weights, one batched launch"),
+             "fused_act": moe_fused_act_part(args, torch, fq, synth, T, E, topk, off, x1, x2,
+                                             xq1, sa1, xq2, sa2, wq1, sw1, wq2, sw2, y1, y2,
+                                             accum)}
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline_moe(synth, counts, min_seconds=10.0)
         cpu["gpu_over_oracle"] = value / cpu["value"]
     emit(args, value, "TFLOP/s", ms, cfg, roof, cpu, ms_per_step_p10_p50_p90=spread,
          parts=parts, **gpu)
+
+
+def moe_fused_act_part(args, torch, fq, synth, T, E, topk, off, x1, x2, xq1, sa1, xq2, sa2, wq1,
+                       sw1, wq2, sw2, y1, y2, accum):
+    """The grouped GEMMs on bf16 activations against quantize-then-GEMM (graph-replayed, us per
+    layer): gate/up from the T token rows through the router's token indices (each token
+    quantized once, against quantizing its top-k grouped copies), down on the grouped rows."""
+    _, ids = synth.moe_routing(T, E, topk, seed=synth.seed_of(5, 0))
+    ids = ids.cuda()
+    xt = synth.act_bf16(T, x1.shape[1], seed=45, device="cuda")
+    M, H, I = x1.shape[0], x1.shape[1], x2.shape[1]
+    need = max(fq.fp8rl_workspace_bytes(fq.FP8RL_OP_GROUPED_GEMM_FUSED_ACT, M, 2 * I, H, E),
+               fq.fp8rl_workspace_bytes(fq.FP8RL_OP_GROUPED_GEMM_FUSED_ACT, M, H, I, E))
+    ws = fq.new_workspace(need, "cuda")
+    reps = max(5, args.steps)
+    res = {}
+    for name, fused, unfused in (
+            ("gate_up", lambda: fq.grouped_gemm_fused_act(xt, wq1, sw1, off, row_ids=ids, y=y1,
+                                                          workspace=ws, accum=accum,
+                                                          scale=args.scales),
+             lambda: (fq.quant_act(x1, xq1, sa1, scale=args.scales),
+                      fq.grouped_gemm(xq1, sa1, wq1, sw1, off, y=y1, accum=accum))),
+            ("down", lambda: fq.grouped_gemm_fused_act(x2, wq2, sw2, off, y=y2, workspace=ws,
+                                                       accum=accum, scale=args.scales),
+             lambda: (fq.quant_act(x2, xq2, sa2, scale=args.scales),
+                      fq.grouped_gemm(xq2, sa2, wq2, sw2, off, y=y2, accum=accum)))):
+        # alternating rounds, the faster of each: the engine clock settles over the first ones
+        us_f = us_u = float("inf")
+        for _ in range(3):
+            us_f = min(us_f, graph_launch_us(torch, fused, reps))
+            us_u = min(us_u, graph_launch_us(torch, unfused, reps))
+        res[name] = {"one_call_us": us_f, "quant_then_gemm_us": us_u, "ratio": us_f / us_u}
+    res["what"] = ("gate/up: one call on the 4096 token rows with the router's token indices "
+                   "(tokens quantized once) against the 1x128 quantizer on the 32768 grouped "
+                   "rows then the grouped GEMM; down: one call against two on the grouped rows")
+    return res
 
 
 def cpu_baseline_moe(synth, counts, min_seconds=10.0):

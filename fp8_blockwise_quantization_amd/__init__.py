@@ -4,7 +4,9 @@ Python face of ``libfp8rl.so``: 128x128 weight re-quantization, 1x128 per-token 
 quantization, the blockwise-scaled FP8 GEMM and its grouped-expert (MoE) form, and per-tensor
 FP8 for attention Q/K/V and the KV cache with recalibrated scales, and the quantizers and GEMM
 of the FP8 backward pass (transposed weight copy, 128x1 token groups, row-scaled GEMM), and the
-decode GEMM with the activation quantization fused in. Tensors live on the GPU; the functions only marshal arguments into the C ABI (include/fp8rl.h).
+GEMMs with the activation quantization fused in (dense, and grouped with the codes read through
+the router's token indices). Tensors live on the GPU; the functions only marshal arguments into
+the C ABI (include/fp8rl.h).
 """
 
 from ._lib import (  # noqa: F401
@@ -17,6 +19,7 @@ from ._lib import (  # noqa: F401
     FP8RL_OP_GEMM_FUSED_ACT,
     FP8RL_OP_GEMM_ROWSCALED,
     FP8RL_OP_GROUPED_GEMM,
+    FP8RL_OP_GROUPED_GEMM_FUSED_ACT,
     FP8RL_OUT_BF16,
     FP8RL_OUT_F32,
     FP8RL_SCALE_FP32,
@@ -30,6 +33,7 @@ from ._lib import (  # noqa: F401
     fp8rl_gemm_w8a8_fused_act_quant,
     fp8rl_gemm_w8a8_rowscaled,
     fp8rl_grouped_gemm_w8a8,
+    fp8rl_grouped_gemm_w8a8_fused_act_quant,
     fp8rl_quant_act_colwise128,
     fp8rl_quant_act_tok128,
     fp8rl_quant_bf16_per_tensor,
@@ -59,6 +63,7 @@ gemm = fp8rl_gemm_w8a8_blockscaled
 gemm_noalloc = fp8rl_gemm_w8a8_blockscaled_noalloc
 gemm_fused_act = fp8rl_gemm_w8a8_fused_act_quant
 grouped_gemm = fp8rl_grouped_gemm_w8a8
+grouped_gemm_fused_act = fp8rl_grouped_gemm_w8a8_fused_act_quant
 encode_e4m3 = fp8rl_encode_e4m3_f32
 amax = fp8rl_amax_bf16
 amax_batched = fp8rl_amax_bf16_batched

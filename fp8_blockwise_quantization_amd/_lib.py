@@ -32,6 +32,7 @@ FP8RL_OP_GEMM = 0
 FP8RL_OP_GROUPED_GEMM = 1
 FP8RL_OP_GEMM_ROWSCALED = 2
 FP8RL_OP_GEMM_FUSED_ACT = 3
+FP8RL_OP_GROUPED_GEMM_FUSED_ACT = 4
 
 class WeightDesc(ctypes.Structure):
     """fp8rl_weight_desc (include/fp8rl.h)."""
@@ -111,6 +112,10 @@ def declare(L: ctypes.CDLL) -> ctypes.CDLL:
             ctypes.c_int,
             [vp, i64, vp, vp, i64, i64, i64, vp, ctypes.c_int, i64, ctypes.c_int,
              ctypes.c_int, vp, sz, vp]),
+        "fp8rl_grouped_gemm_w8a8_fused_act_quant": (
+            ctypes.c_int,
+            [vp, i64, i64, vp, vp, vp, vp, i32, i64, i64, i64, vp, ctypes.c_int, ctypes.c_int,
+             ctypes.c_int, vp, sz, vp]),
         "fp8rl_workspace_bytes": (sz, [ctypes.c_int, i64, i64, i64, i32]),
         "fp8rl_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "fp8rl_version": (ctypes.c_int, []),
@@ -159,6 +164,7 @@ EXPORTED = (
     "fp8rl_gemm_w8a8_rowscaled",
     "fp8rl_gemm_w8a8_fused_act_quant",
     "fp8rl_gemm_w8a8_blockscaled_noalloc",
+    "fp8rl_grouped_gemm_w8a8_fused_act_quant",
     "fp8rl_workspace_bytes",
     "fp8rl_status_string",
     "fp8rl_version",
@@ -512,6 +518,43 @@ def fp8rl_grouped_gemm_w8a8(xq, sa, wq, sw, expert_offsets, out_dtype=torch.bflo
                                          _out_code(y.dtype), _accum_code(accum, y.dtype),
                                          _ptr(workspace), ws_bytes, _stream(stream)),
            "fp8rl_grouped_gemm_w8a8")
+    return y
+
+
+@_allocs_on_stream
+def fp8rl_grouped_gemm_w8a8_fused_act_quant(x, wq, sw, expert_offsets, row_ids=None,
+                                            out_dtype=torch.bfloat16, y=None, workspace=None,
+                                            stream=None, accum=None, scale="fp32"):
+    """Grouped GEMM on bf16 activations: grouped row r multiplies row ``row_ids[r]`` of ``x``
+    (device int32; None: row r) quantized in 1x128 groups (`scale` format) with its expert's
+    weights. Each row of ``x`` is quantized once; the same bits as quant_act on the gathered rows
+    followed by the grouped GEMM."""
+    ld_x = _rows(x, "x", torch.bfloat16)
+    _dense(wq, "wq", torch.uint8)
+    _dense(sw, "sw", torch.float32)
+    _dense(expert_offsets, "expert_offsets", torch.int32)
+    src_rows, K = x.shape
+    E, N, K2 = wq.shape
+    if K2 != K or expert_offsets.numel() != E + 1:
+        raise ValueError("shape mismatch between x, wq and expert_offsets")
+    if row_ids is not None:
+        _dense(row_ids, "row_ids", torch.int32)
+        M = row_ids.numel()
+    else:
+        M = src_rows
+    if y is None:
+        y = torch.empty((M, N), dtype=out_dtype, device=x.device)
+    _dense(y, "y", y.dtype)
+    if y.shape[0] != M:
+        raise ValueError("y must have one row per grouped row")
+    need = fp8rl_workspace_bytes(FP8RL_OP_GROUPED_GEMM_FUSED_ACT, max(src_rows, M), N, K, E)
+    if workspace is None and need > 0:
+        workspace = new_workspace(need, x.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().fp8rl_grouped_gemm_w8a8_fused_act_quant(
+        _ptr(x), ld_x, src_rows, _ptr(row_ids), _ptr(wq), _ptr(sw), _ptr(expert_offsets), E, M, N,
+        K, _ptr(y), _out_code(y.dtype), _accum_code(accum, y.dtype), _scale_code(scale),
+        _ptr(workspace), ws_bytes, _stream(stream)), "fp8rl_grouped_gemm_w8a8_fused_act_quant")
     return y
 
 

@@ -1,6 +1,8 @@
 // C ABI entry points: argument validation (host only, before any HIP call) and dispatch.
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "fp8rl.h"
 #include "launch.hpp"
 
@@ -386,6 +388,8 @@ size_t fp8rl_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int32_t E)
   if (op == FP8RL_OP_GEMM_ROWSCALED) return fp8rl::plan_gemm(M, N, K, true).workspace_bytes;
   if (op == FP8RL_OP_GROUPED_GEMM) return fp8rl::plan_grouped_gemm(M, N, K, E).workspace_bytes;
   if (op == FP8RL_OP_GEMM_FUSED_ACT) return fp8rl::plan_fused_act(M, N, K).workspace_bytes;
+  if (op == FP8RL_OP_GROUPED_GEMM_FUSED_ACT)
+    return fp8rl::plan_grouped_fused_act(M, N, K, E).workspace_bytes;
   return 0;
 }
 
@@ -448,6 +452,8 @@ int fp8rl_gemm_w8a8_fused_act_quant(const uint16_t* x, int64_t ld_x, const uint8
   if (!x || !wq || !sw || !y) return FP8RL_ERR_NULL;
   if (N == 0 || K == 0 || N % 128 || K % 128) return FP8RL_ERR_SHAPE;
   if (ld_x < K || ld_x > kMaxDim) return FP8RL_ERR_SHAPE;
+  if (M * (K / 128) >= (int64_t{1} << 30)) return FP8RL_ERR_SHAPE;                // quantizer grid
+  if (((M + 127) / 128) * (N / 64) >= (int64_t{1} << 22)) return FP8RL_ERR_SHAPE;  // GEMM grid
   if (y_dtype != FP8RL_OUT_BF16 && y_dtype != FP8RL_OUT_F32) return FP8RL_ERR_DTYPE;
   if (ld_y < N) return FP8RL_ERR_SHAPE;
   accum = resolve_accum(accum, y_dtype, false);
@@ -498,6 +504,41 @@ int fp8rl_grouped_gemm_w8a8(const uint8_t* xq, const float* sa, const uint8_t* w
   return hip_status(fp8rl::launch_grouped_gemm(xq, sa, wq, sw, expert_offsets, E, M_total, N, K, y,
                                                y_dtype == FP8RL_OUT_F32, accum, workspace, plan,
                                                as_stream(stream)));
+}
+
+int fp8rl_grouped_gemm_w8a8_fused_act_quant(const uint16_t* x, int64_t ld_x, int64_t src_rows,
+                                            const int32_t* row_ids, const uint8_t* wq,
+                                            const float* sw, const int32_t* expert_offsets,
+                                            int32_t E, int64_t M_total, int64_t N, int64_t K,
+                                            void* y, int y_dtype, int accum, int scale_fmt,
+                                            void* workspace, size_t workspace_bytes,
+                                            void* stream) {
+  if (int s = check_dims(M_total, N, K)) return s;
+  if (int s = check_dims(src_rows, ld_x, 0)) return s;
+  if (E < 1 || E > 1024) return FP8RL_ERR_ARG;
+  if (M_total == 0) return FP8RL_OK;
+  if (!x || !wq || !sw || !y || !expert_offsets) return FP8RL_ERR_NULL;
+  if (N == 0 || K == 0 || N % 128 || K % 128 || ld_x < K) return FP8RL_ERR_SHAPE;
+  if (row_ids ? src_rows < 1 : src_rows != M_total) return FP8RL_ERR_SHAPE;
+  if (row_ids && src_rows * K >= (int64_t{1} << 32)) return FP8RL_ERR_SHAPE;  // 32-bit DMA offsets
+  if (src_rows * (K / 128) >= (int64_t{1} << 30)) return FP8RL_ERR_SHAPE;      // quantizer grid
+  if (((M_total + 127) / 128 + E) * (N / 128) >= (int64_t{1} << 22)) return FP8RL_ERR_SHAPE;
+  if ((int64_t)E * N * K >= (int64_t{1} << 40)) return FP8RL_ERR_SHAPE;
+  if (y_dtype != FP8RL_OUT_BF16 && y_dtype != FP8RL_OUT_F32) return FP8RL_ERR_DTYPE;
+  accum = resolve_accum(accum, y_dtype, false);
+  if (accum < 0) return FP8RL_ERR_ARG;
+  if (scale_fmt != FP8RL_SCALE_FP32 && scale_fmt != FP8RL_SCALE_POW2) return FP8RL_ERR_ARG;
+  if (accum == FP8RL_ACCUM_MX && scale_fmt != FP8RL_SCALE_POW2) return FP8RL_ERR_ARG;
+  if (!aligned(x, 16) || (ld_x * 2) % 16 || !aligned(wq, 16) || !aligned(sw, 4) ||
+      !aligned(y, 16) || !aligned(expert_offsets, 4) || (row_ids && !aligned(row_ids, 4)))
+    return FP8RL_ERR_ALIGN;
+  const fp8rl::GemmPlan plan =
+      fp8rl::plan_grouped_fused_act(std::max(src_rows, M_total), N, K, E);
+  if (!workspace || workspace_bytes < plan.workspace_bytes) return FP8RL_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return FP8RL_ERR_ALIGN;
+  return hip_status(fp8rl::launch_grouped_gemm_fused_act(
+      x, ld_x, src_rows, row_ids, scale_fmt == FP8RL_SCALE_POW2, wq, sw, expert_offsets, E,
+      M_total, N, K, y, y_dtype == FP8RL_OUT_F32, accum, workspace, as_stream(stream)));
 }
 
 }  // extern "C"

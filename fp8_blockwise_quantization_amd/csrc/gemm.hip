@@ -72,6 +72,10 @@ struct GemmArgs {
   int E;
   int64_t wq_stride, sw_stride;  // per expert
   int tiles_n;
+  // grouped form with a row gather (or null): grouped row r reads the activation codes and
+  // scales of source row rows[r], clamped to [0, src_rows - 1]
+  const int32_t* rows;
+  int src_rows;
   // decode GEMM with the activation quantization fused in: bf16 X rows (pitch ld_x) replace
   // xq / sa, and pow2 selects the scale format of its 1x128 groups
   const uint16_t* x;
@@ -407,7 +411,15 @@ __device__ __forceinline__ void dma4(const void* base, uint32_t off, const uint8
 
 // Per-lane byte offsets of this lane's DMA sources within a K slice (computed once per tile).
 // Rows past the end of the matrix are clamped to its last row: they load valid memory whose
-// products only reach output rows / columns that are never stored.
+// products only reach output rows / columns that are never stored. With a row gather (g
+// non-null: the source rows of this lane's A and scale DMA, as loaded from the gather list) the
+// A and scale offsets are those of the source rows, relative to the start of the source matrix.
+template <class T>
+struct GatherRows {
+  int a[T::A_PER_WAVE];
+  int s;
+};
+
 template <class T>
 struct DmaPlan {
   uint32_t a[T::A_PER_WAVE];
@@ -416,18 +428,38 @@ struct DmaPlan {
   uint32_t sb;  // row-scaled B
 };
 
+// The entries of a tile's gather list (rows: the tile's first entry) that this lane's A and
+// scale DMA read, as loaded (clamped when the plan is made).
+template <class T>
+__device__ __forceinline__ GatherRows<T> load_gather_rows(const int32_t* rows, int m_valid,
+                                                          int wave, int lane) {
+  GatherRows<T> g;
+#pragma unroll
+  for (int t = 0; t < T::A_PER_WAVE; ++t)
+    g.a[t] = rows[min((t * T::WAVES + wave) * 8 + (lane >> 3), m_valid - 1)];
+  g.s = rows[min(wave * T::S_ROWS + lane, m_valid - 1)];
+  return g;
+}
+
 template <class T>
 __device__ __forceinline__ DmaPlan<T> make_dma_plan(int m_valid, int n_valid, int K, int KB,
-                                                    int wave, int lane) {
+                                                    int wave, int lane,
+                                                    const GatherRows<T>* g = nullptr,
+                                                    int src_rows = 0) {
   DmaPlan<T> d;
   const int sub = lane >> 3;
+  // source row of tile row trow (gather entry v), clamped to the matrix (the caller bounds
+  // src_rows * K and src_rows * KB * 4 below 2^32)
+  auto src = [&](int trow, int v) -> uint32_t {
+    return g ? (uint32_t)min(max(v, 0), src_rows - 1) : (uint32_t)min(trow, m_valid - 1);
+  };
   // lane l fills LDS slot l & 7 of tile row 8 * ins + (l >> 3): it loads the logical chunk that
   // the swizzle puts there (the row used for the swizzle is the unclamped tile row)
 #pragma unroll
   for (int t = 0; t < T::A_PER_WAVE; ++t) {
     const int trow = (t * T::WAVES + wave) * 8 + sub;
     const int cc = (lane & 7) ^ swz(trow);
-    d.a[t] = (uint32_t)(min(trow, m_valid - 1) * K + cc * 16);
+    d.a[t] = src(trow, g ? g->a[t] : 0) * (uint32_t)K + (uint32_t)(cc * 16);
   }
 #pragma unroll
   for (int t = 0; t < T::B_PER_WAVE; ++t) {
@@ -435,7 +467,7 @@ __device__ __forceinline__ DmaPlan<T> make_dma_plan(int m_valid, int n_valid, in
     const int cc = (lane & 7) ^ swz(trow);
     d.b[t] = (uint32_t)(min(trow, n_valid - 1) * K + cc * 16);
   }
-  d.s = (uint32_t)(min(wave * T::S_ROWS + lane, m_valid - 1) * KB * 4);
+  d.s = src(wave * T::S_ROWS + lane, g ? g->s : 0) * (uint32_t)(KB * 4);
   d.sb = (uint32_t)(min(wave * T::SB_ROWS + lane, n_valid - 1) * KB * 4);
   return d;
 }
@@ -708,20 +740,26 @@ __global__ __launch_bounds__(T::NT) void gemm_big_kernel(GemmArgs p) {
 }
 
 // Grouped GEMM on the DMA-fed tiles, persistent: a fixed grid of workgroups walks the list of
-// (expert m-tile, n-tile) pairs. Each workgroup first forms, from the device offsets, the prefix
-// sums of the per-expert m-tile counts in LDS (once), then finds each tile's expert by binary
-// search. The tile list is cut into one contiguous chunk per XCD (workgroup w runs on XCD
-// w % 8), so the m-tiles of one expert -- which read the same weight panels -- and the n-tiles
-// of one m-tile -- which read the same activation rows -- share an L2.
+// (expert m-tile, n-tile) pairs. Each workgroup first forms, from the device offsets, the
+// clamped offsets and the prefix sums of the per-expert m-tile counts in LDS (once), then finds
+// each tile's expert by binary search there. The tile list is cut into one contiguous chunk per
+// XCD (workgroup w runs on XCD w % 8), so the m-tiles of one expert -- which read the same weight
+// panels -- and the n-tiles of one m-tile -- which read the same activation rows -- share an L2.
+// The global values a tile's set-up needs (its weight-block scales and, with a row gather, its
+// source rows) are loaded when the tile before it starts, so that the next tile's first slice
+// DMA goes out at the end of the current tile's K loop without a memory round trip.
 template <class T, int ACC>
 __global__ __launch_bounds__(T::NT) void grouped_big_kernel(GemmArgs p) {
   __shared__ __attribute__((aligned(16))) uint8_t stages[T::STAGES * T::STAGE_BYTES];
   __shared__ float sw_s[(T::BN + 127) / 128][kMaxSlices];
   __shared__ int s_first[kMaxExperts + 1];  // m-tiles of experts before e
-  __shared__ int s_part[T::NT];
+  __shared__ int s_lo[kMaxExperts + 1];     // first row of expert e (offsets clamped to [0, M])
+  int* const s_part = reinterpret_cast<int*>(stages);  // scan scratch (before any DMA)
+  static_assert(T::NT * sizeof(int) <= T::STAGES * T::STAGE_BYTES, "scan scratch fits");
   const int tid = threadIdx.x;
   const int E = p.E;
-  // prefix sums of ceil(rows_e / BM), NT experts per pass (E <= kMaxExperts)
+  // prefix sums of ceil(rows_e / BM), NT experts per pass (E <= kMaxExperts); expert e's rows
+  // are [s_lo[e], max(s_lo[e + 1], s_lo[e]))
   int carry = 0;
   for (int base = 0; base < E; base += T::NT) {
     const int e = base + tid;
@@ -730,6 +768,7 @@ __global__ __launch_bounds__(T::NT) void grouped_big_kernel(GemmArgs p) {
       const int lo = min(max(p.offsets[e], 0), p.M);
       const int hi = min(max(p.offsets[e + 1], lo), p.M);
       cnt = (hi - lo + T::BM - 1) / T::BM;
+      s_lo[e] = lo;
     }
     s_part[tid] = cnt;
     __syncthreads();
@@ -743,7 +782,10 @@ __global__ __launch_bounds__(T::NT) void grouped_big_kernel(GemmArgs p) {
     carry += s_part[T::NT - 1];
     __syncthreads();
   }
-  if (tid == 0) s_first[E] = carry;
+  if (tid == 0) {
+    s_first[E] = carry;
+    s_lo[E] = min(max(p.offsets[E], 0), p.M);
+  }
   __syncthreads();
   const int tiles_n = p.tiles_n;
   const int total = s_first[E] * tiles_n;
@@ -751,7 +793,7 @@ __global__ __launch_bounds__(T::NT) void grouped_big_kernel(GemmArgs p) {
   const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
   const int chunk = (total + 7) / 8;
   const int t_end = min(total, (xcd + 1) * chunk);
-  // tile t -> (expert e, first row, valid rows, first column)
+  // tile t -> (expert e, first row, valid rows, first column), from LDS only
   struct Coords {
     int e, row0, m_valid, n0, n_valid;
   };
@@ -767,8 +809,8 @@ __global__ __launch_bounds__(T::NT) void grouped_big_kernel(GemmArgs p) {
     // must be scalar registers)
     Coords c;
     c.e = __builtin_amdgcn_readfirstlane(lo);
-    const int r_lo = min(max(p.offsets[c.e], 0), p.M);
-    const int r_hi = min(max(p.offsets[c.e + 1], r_lo), p.M);
+    const int r_lo = s_lo[c.e];
+    const int r_hi = max(s_lo[c.e + 1], r_lo);
     c.row0 = __builtin_amdgcn_readfirstlane(r_lo + (tm_lin - s_first[c.e]) * T::BM);
     c.m_valid = __builtin_amdgcn_readfirstlane(min(T::BM, r_hi - c.row0));
     c.n0 = __builtin_amdgcn_readfirstlane(tn * T::BN);
@@ -776,10 +818,50 @@ __global__ __launch_bounds__(T::NT) void grouped_big_kernel(GemmArgs p) {
     return c;
   };
   const uint8_t* const wq0 = p.wq;
-  auto a_of = [&](const Coords& c) { return p.xq + (int64_t)c.row0 * p.K; };
-  auto sa_of = [&](const Coords& c) { return p.sa + (int64_t)c.row0 * p.KB; };
+  // with a row gather the DMA offsets address the source rows from the start of xq / sa
+  const bool gather = p.rows != nullptr;
+  auto a_of = [&](const Coords& c) { return gather ? p.xq : p.xq + (int64_t)c.row0 * p.K; };
+  auto sa_of = [&](const Coords& c) { return gather ? p.sa : p.sa + (int64_t)c.row0 * p.KB; };
   auto b_of = [&](const Coords& c) { return wq0 + c.e * p.wq_stride + (int64_t)c.n0 * p.K; };
   auto sw_of = [&](const Coords& c) { return p.sw + c.e * p.sw_stride; };
+  // A tile's set-up in two halves. fetch: the global loads (thread tid < NBLK KB takes weight-
+  // block scale tid: NBLK <= 2 column blocks x KB <= 256 slices <= NT values). commit: the
+  // scales into LDS (the previous tile's K loop is done with them) and the DMA plan.
+  constexpr int NBLK = (T::BN + 127) / 128;
+  static_assert(NBLK * kMaxSlices <= T::NT, "one weight-block scale per thread");
+  static_assert(!T::ROWB, "grouped GEMM: block-scaled weights");
+  const int KB = p.KB;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  struct Fetch {
+    float sw;
+    GatherRows<T> g;
+  };
+  auto fetch = [&](const Coords& c) {
+    Fetch f;
+    {  // every thread loads (threads past NBLK KB a repeat): no register write precedes the load
+      const int e = min(tid, NBLK * KB - 1);
+      const int b = e / KB, k = e - (e / KB) * KB;
+      const int nb = min((c.n0 >> 7) + b, p.N / 128 - 1);
+      f.sw = sw_of(c)[(int64_t)nb * KB + k];
+    }
+    if (gather) f.g = load_gather_rows<T>(p.rows + c.row0, c.m_valid, wave, lane);
+    return f;
+  };
+  auto commit = [&](const Coords& c, Fetch f) {
+    // the fetched values are taken here, on every path: the empty asm statements keep the
+    // compiler from moving any use of them -- and with it the wait for their loads, which would
+    // also wait for the slice DMA in flight -- to the top of the tile
+    asm volatile("" : "+v"(f.sw));
+    if (gather) {
+#pragma unroll
+      for (int i = 0; i < T::A_PER_WAVE; ++i) asm volatile("" : "+v"(f.g.a[i]));
+      asm volatile("" : "+v"(f.g.s));
+    }
+    if (tid < NBLK * KB) sw_s[tid / KB][tid - (tid / KB) * KB] = f.sw;
+    return make_dma_plan<T>(c.m_valid, c.n_valid, p.K, KB, wave, lane, gather ? &f.g : nullptr,
+                            p.src_rows);
+  };
   // The next tile's slice 0 goes out into stage 0 while this tile's epilogue works in the
   // stages behind it (when the staged tile fits there): each tile's DMA start-up hides behind
   // the previous tile's store phase.
@@ -787,35 +869,31 @@ __global__ __launch_bounds__(T::NT) void grouped_big_kernel(GemmArgs p) {
   static_assert(T::BM * kEpiPitch<T> * 2 <= T::STAGES * T::STAGE_BYTES, "epilogue tile fits");
   int t = xcd * chunk + slot;
   if (t >= t_end) return;
-  const int tid2 = threadIdx.x, lane = tid2 & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid2 >> 6);
   Coords c = coords(t);
-  DmaPlan<T> dp = big_tile_prepare<T>(p, sw_s, sw_of(c), c.n0, c.m_valid, c.n_valid);
+  DmaPlan<T> dp = commit(c, fetch(c));
   if (kAhead) dma_slice<T>(stages, dp, a_of(c), b_of(c), sa_of(c), nullptr, 0, wave, lane);
   for (;;) {
     const int t_next = t + per_xcd;
     const bool more = t_next < t_end;
-    Coords cn = c;
+    // fetched and committed on every path (the last tile re-fetches its own values), so that
+    // no load is left pending across the loop's back edge: the compiler would otherwise wait
+    // for all memory operations, the slice DMA in flight included, at the top of each tile
+    const Coords cn = coords(more ? t_next : t);
+    const Fetch fn = fetch(cn);
     DmaPlan<T> dpn = dp;
     big_tile_core<T, ACC>(p, stages, sw_s, dp, a_of(c), sa_of(c), c.m_valid, b_of(c), sw_of(c),
                           c.n0, c.n_valid, c.row0, kAhead, kAhead ? T::STAGE_BYTES : 0, [&] {
-                            if (!kAhead || !more) return;
-                            cn = coords(t_next);
-                            dpn = big_tile_prepare<T>(p, sw_s, sw_of(cn), cn.n0, cn.m_valid,
-                                                      cn.n_valid);
-                            dma_slice<T>(stages, dpn, a_of(cn), b_of(cn), sa_of(cn), nullptr, 0,
-                                         wave, lane);
+                            if (!kAhead) return;
+                            dpn = commit(cn, fn);
+                            if (more)
+                              dma_slice<T>(stages, dpn, a_of(cn), b_of(cn), sa_of(cn), nullptr,
+                                           0, wave, lane);
                           });
     if (!more) break;
     __syncthreads();  // the epilogue's LDS reads are done before the next tile's DMA lands there
     t = t_next;
-    if (kAhead) {
-      c = cn;
-      dp = dpn;
-    } else {
-      c = coords(t);
-      dp = big_tile_prepare<T>(p, sw_s, sw_of(c), c.n0, c.m_valid, c.n_valid);
-    }
+    c = cn;
+    dp = kAhead ? dpn : commit(c, fn);
   }
 }
 
@@ -1488,6 +1566,19 @@ GemmPlan plan_fused_act(int64_t M, int64_t N, int64_t K) {
   return pl;
 }
 
+GemmPlan plan_grouped_fused_act(int64_t M, int64_t N, int64_t K, int32_t E) {
+  // [counter header, kept zero | codes of M rows | their scales] and, where the grouped GEMM
+  // runs on the register-staged tiles (no row gather there), a second such area for the
+  // gathered rows; each part 256-byte aligned
+  GemmPlan pl = plan_grouped_gemm(M, N, K, E);
+  const size_t a256 = 255;
+  const size_t area = (((size_t)M * (size_t)K + a256) & ~a256) +
+                      (((size_t)M * (size_t)(K / 128) * sizeof(float) + a256) & ~a256);
+  pl.stage_off = kWsHeaderBytes;
+  pl.workspace_bytes = kWsHeaderBytes + (pl.cfg == kCfgGroupedBig ? 1 : 2) * area;
+  return pl;
+}
+
 GemmPlan plan_grouped_gemm(int64_t M_total, int64_t N, int64_t K, int32_t E) {
   GemmPlan pl{};
   (void)M_total;
@@ -1722,8 +1813,9 @@ hipError_t launch_grouped_gemm(const uint8_t* xq, const float* sa, const uint8_t
                                const float* sw, const int32_t* offsets, int32_t E,
                                int64_t M_total, int64_t N, int64_t K, void* y, int out_f32,
                                int accum, void* workspace, const GemmPlan& pl,
-                               hipStream_t stream) {
+                               hipStream_t stream, const int32_t* rows, int64_t src_rows) {
   (void)workspace;
+  if (rows && pl.cfg != kCfgGroupedBig) return hipErrorInvalidValue;  // gather: DMA-fed tiles only
   const bool precise = accum == 1;
   using T = TileLarge;
   GemmArgs a{};
@@ -1745,6 +1837,8 @@ hipError_t launch_grouped_gemm(const uint8_t* xq, const float* sa, const uint8_t
   a.E = E;
   a.wq_stride = N * K;
   a.sw_stride = (N / 128) * (K / 128);
+  a.rows = rows;
+  a.src_rows = (int)src_rows;
   if (pl.cfg == kCfgGroupedBig) {
     a.tiles_n = (int)((N + BigGroup::BN - 1) / BigGroup::BN);
     const dim3 grid((unsigned)pl.splits), block(BigGroup::NT);
@@ -1773,6 +1867,60 @@ hipError_t launch_grouped_gemm(const uint8_t* xq, const float* sa, const uint8_t
     hipLaunchKernelGGL((grouped_gemm_kernel<T, false>), dim3((unsigned)grid), dim3(T::NT), lds,
                        stream, a);
   return hipGetLastError();
+}
+
+// Copy the codes and scales of source rows rows[r] (clamped to [0, src_rows - 1]) to row r,
+// r < M: a workgroup per row (grid-stride), 16-byte pieces.
+__global__ __launch_bounds__(256) void gather_rows_kernel(const uint8_t* __restrict__ xq,
+                                                          const float* __restrict__ sa,
+                                                          const int32_t* __restrict__ rows,
+                                                          int src_rows, int64_t M, int K,
+                                                          uint8_t* out_q, float* out_s) {
+  const int KB = K / 128;
+  for (int64_t r = blockIdx.x; r < M; r += gridDim.x) {
+    const int64_t src = min(max(rows[r], 0), src_rows - 1);
+    for (int c = threadIdx.x; c < K / 16; c += 256)
+      reinterpret_cast<uint4*>(out_q + r * K)[c] = reinterpret_cast<const uint4*>(xq + src * K)[c];
+    for (int c = threadIdx.x; c < KB; c += 256) out_s[r * KB + c] = sa[src * KB + c];
+  }
+}
+
+hipError_t launch_grouped_gemm_fused_act(const uint16_t* x, int64_t ld_x, int64_t src_rows,
+                                         const int32_t* rows, int pow2, const uint8_t* wq,
+                                         const float* sw, const int32_t* offsets, int32_t E,
+                                         int64_t M_total, int64_t N, int64_t K, void* y,
+                                         int out_f32, int accum, void* workspace,
+                                         hipStream_t stream) {
+  const int64_t M = rows ? src_rows : M_total;
+  const GemmPlan pl = plan_grouped_fused_act(std::max(src_rows, M_total), N, K, E);
+  const size_t a256 = 255;
+  const int64_t KB = K / 128;
+  auto codes_of = [&](size_t off) { return reinterpret_cast<uint8_t*>(workspace) + off; };
+  auto scales_of = [&](size_t off, int64_t m) {
+    return reinterpret_cast<float*>(codes_of(off) + (((size_t)m * (size_t)K + a256) & ~a256));
+  };
+  // each source row once, into the first area
+  uint8_t* xq = codes_of(pl.stage_off);
+  float* sa = scales_of(pl.stage_off, M);
+  hipError_t e = launch_quant_act(x, M, K, ld_x, xq, K, sa, pow2, stream);
+  if (e != hipSuccess) return e;
+  const GemmPlan gp = plan_grouped_gemm(M_total, N, K, E);
+  if (rows && gp.cfg != kCfgGroupedBig) {
+    // the register-staged tiles read contiguous rows: gather them into the second area
+    const size_t off2 = pl.stage_off + (((size_t)M * (size_t)K + a256) & ~a256) +
+                        (((size_t)M * (size_t)KB * sizeof(float) + a256) & ~a256);
+    uint8_t* xg = codes_of(off2);
+    float* sg = scales_of(off2, M_total);
+    const int64_t wgs = std::min<int64_t>(M_total, 16384);
+    hipLaunchKernelGGL(gather_rows_kernel, dim3((unsigned)wgs), dim3(256), 0, stream, xq, sa, rows,
+                       (int)src_rows, M_total, (int)K, xg, sg);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_grouped_gemm(xg, sg, wq, sw, offsets, E, M_total, N, K, y, out_f32, accum,
+                               nullptr, gp, stream, nullptr, 0);
+  }
+  return launch_grouped_gemm(xq, sa, wq, sw, offsets, E, M_total, N, K, y, out_f32, accum, nullptr,
+                             gp, stream, rows, src_rows);
 }
 
 }  // namespace fp8rl

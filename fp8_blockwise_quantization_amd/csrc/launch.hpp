@@ -112,7 +112,7 @@ hipError_t gemm_scratch(hipStream_t stream, void** ptr);
 // The split-K decode GEMM's plan (1 <= M <= 64, K/128 even).
 GemmPlan plan_decode(int64_t M, int64_t N, int64_t K);
 // The GEMM with the 1x128 activation quantization fused in: bf16 X [M][ld_x] in place of xq / sa
-// (pow2: scale format of the groups). Up to 16 rows one kernel quantizes in registers; above,
+// (pow2: scale format of the groups). Up to 4 rows one kernel quantizes in registers; above,
 // the codes are staged in the workspace (from plan.stage_off) and the plan's GEMM reads them.
 // Plans from plan_fused_act (its own workspace size).
 GemmPlan plan_fused_act(int64_t M, int64_t N, int64_t K);
@@ -120,10 +120,25 @@ hipError_t launch_gemm_fused_act(const uint16_t* x, int64_t ld_x, int pow2, cons
                                  const float* sw, int64_t M, int64_t N, int64_t K, void* y,
                                  int out_f32, int64_t ld_y, int accum, void* workspace,
                                  const GemmPlan& plan, hipStream_t stream);
+// rows (device, M_total entries, or null): grouped row r reads the codes and scales of row
+// rows[r] of xq / sa (clamped to [0, src_rows - 1]); DMA-fed tiles only (plan.cfg grouped-big),
+// with src_rows * K < 2^32
 hipError_t launch_grouped_gemm(const uint8_t* xq, const float* sa, const uint8_t* wq,
                                const float* sw, const int32_t* offsets, int32_t E,
                                int64_t M_total, int64_t N, int64_t K, void* y, int out_f32,
                                int accum, void* workspace, const GemmPlan& plan,
-                               hipStream_t stream);
+                               hipStream_t stream, const int32_t* rows = nullptr,
+                               int64_t src_rows = 0);
+// The grouped GEMM on bf16 activations: x holds src_rows rows of pitch ld_x; grouped row r is
+// row rows[r] (clamped), or row r when rows is null (then src_rows == M_total). Each source row
+// is quantized once into the workspace (pow2: scale format), then the grouped GEMM gathers the
+// codes through rows. The workspace is plan_grouped_fused_act(max(src_rows, M_total), N, K, E)'s.
+GemmPlan plan_grouped_fused_act(int64_t M, int64_t N, int64_t K, int32_t E);
+hipError_t launch_grouped_gemm_fused_act(const uint16_t* x, int64_t ld_x, int64_t src_rows,
+                                         const int32_t* rows, int pow2, const uint8_t* wq,
+                                         const float* sw, const int32_t* offsets, int32_t E,
+                                         int64_t M_total, int64_t N, int64_t K, void* y,
+                                         int out_f32, int accum, void* workspace,
+                                         hipStream_t stream);
 
 }  // namespace fp8rl

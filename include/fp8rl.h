@@ -10,9 +10,10 @@
  *      per 1x128 group                         (fp8rl_quant_act_tok128);
  *   3. the blockwise-scaled FP8 GEMM Y = X W^T that consumes both
  *                                             (fp8rl_gemm_w8a8_blockscaled),
- *      and its mixture-of-experts grouped form (fp8rl_grouped_gemm_w8a8), and a form that
- *      takes bf16 activations and quantizes them itself, inside the GEMM kernel for decode
- *      shapes (fp8rl_gemm_w8a8_fused_act_quant);
+ *      and its mixture-of-experts grouped form (fp8rl_grouped_gemm_w8a8), and forms that
+ *      take bf16 activations and quantize them themselves: inside the GEMM kernel for decode
+ *      shapes (fp8rl_gemm_w8a8_fused_act_quant), once per token with the grouped GEMM reading
+ *      the codes through the router's token indices (fp8rl_grouped_gemm_w8a8_fused_act_quant);
  *   plus the element-wise E4M3 encoder the quantizers share (fp8rl_encode_e4m3_f32), and the
  *   per-tensor FP8 of attention Q/K/V activations and the KV cache with per-step recalibrated
  *   scales (fp8rl_amax_bf16, fp8rl_scale_from_amax, fp8rl_quant_bf16_per_tensor and their
@@ -78,7 +79,8 @@ typedef enum {
   FP8RL_OP_GEMM = 0,
   FP8RL_OP_GROUPED_GEMM = 1,
   FP8RL_OP_GEMM_ROWSCALED = 2,
-  FP8RL_OP_GEMM_FUSED_ACT = 3
+  FP8RL_OP_GEMM_FUSED_ACT = 3,
+  FP8RL_OP_GROUPED_GEMM_FUSED_ACT = 4
 } fp8rl_op;
 
 /*
@@ -357,6 +359,48 @@ int fp8rl_grouped_gemm_w8a8(const uint8_t* xq, const float* sa, const uint8_t* w
                             const int32_t* expert_offsets, int32_t E, int64_t M_total, int64_t N,
                             int64_t K, void* y, int y_dtype, int accum, void* workspace,
                             size_t workspace_bytes, void* stream);
+
+/*
+ * The grouped GEMM on bf16 activations: the activation quantization of
+ * fp8rl_gemm_w8a8_fused_act_quant brought to the expert linears of a mixture-of-experts layer
+ * [FP8RL, section 1: the MoE expert linears are quantized like the other linears; NEMO, speed-up
+ * discussion of the Llama 3 8B results: the quantization kernels placed before the linears are
+ * overhead]. Grouped row r (expert e owns rows expert_offsets[e] .. expert_offsets[e+1]-1, as in
+ * fp8rl_grouped_gemm_w8a8) takes its activations from row row_ids[r] of x, the token the router
+ * sent to that expert, so the caller passes the token activations as they are and the router's
+ * token indices in expert order:
+ *   Y[r][n] = sum_kb sa'[r][kb] * sw[e][n/128][kb] * sum_k dec(Q(x[row_ids[r]])[k]) * dec(Wq[e][n][k])
+ * with Q the 1x128 activation quantizer (scale format scale_fmt) and sa' its scales. The result
+ * is bit-identical to fp8rl_quant_act_tok128_ex on the gathered rows x[row_ids[0 .. M_total-1]]
+ * followed by fp8rl_grouped_gemm_w8a8 with the same accum: a 1x128 group lies within one row,
+ * so a token quantized once has the same codes and scales for each expert it is sent to. Each
+ * row of x is quantized once into the workspace (src_rows rows, against M_total = top-k x tokens
+ * for the gathered form) and the grouped GEMM's tile DMA reads the codes and scales of the
+ * listed rows, so no permuted copy of the activations is ever written. Two kernels in one call
+ * (three where K > 32768: the grouped GEMM's register-staged tiles read contiguous rows, so a
+ * copy kernel gathers the codes first).
+ *   x          : bf16 activations, src_rows rows of pitch ld_x (>= K; ld_x * 2 a multiple of 16)
+ *   src_rows   : rows of x; >= 1 when row_ids is given, and src_rows * K < 2^32
+ *   row_ids    : M_total int32 on the DEVICE, or NULL. Each id is clamped to [0, src_rows - 1], so
+ *                an out-of-range id reads the nearest valid row (never out of bounds). NULL: row r
+ *                of x is grouped row r (src_rows must equal M_total), as for the down projection,
+ *                whose input is already in expert order.
+ *   wq, sw, expert_offsets, E, M_total, N, K, y, y_dtype, accum : as for fp8rl_grouped_gemm_w8a8
+ *   scale_fmt  : FP8RL_SCALE_FP32 or FP8RL_SCALE_POW2 (FP8RL_ACCUM_MX requires FP8RL_SCALE_POW2)
+ *   workspace, workspace_bytes : at least fp8rl_workspace_bytes(FP8RL_OP_GROUPED_GEMM_FUSED_ACT,
+ *                max(src_rows, M_total), N, K, E) bytes, 16-byte aligned. The call does not touch
+ *                its first FP8RL_WORKSPACE_HEADER_BYTES, so one workspace can serve this call and
+ *                the dense GEMMs; the rest is overwritten.
+ * Requires E >= 1, N % 128 == 0, K % 128 == 0 (FP8RL_ERR_SHAPE otherwise; M_total == 0 returns
+ * FP8RL_OK). Deterministic.
+ */
+int fp8rl_grouped_gemm_w8a8_fused_act_quant(const uint16_t* x, int64_t ld_x, int64_t src_rows,
+                                            const int32_t* row_ids, const uint8_t* wq,
+                                            const float* sw, const int32_t* expert_offsets,
+                                            int32_t E, int64_t M_total, int64_t N, int64_t K,
+                                            void* y, int y_dtype, int accum, int scale_fmt,
+                                            void* workspace, size_t workspace_bytes,
+                                            void* stream);
 
 /*
  * Per-tensor FP8 for attention Q/K/V activations and the stored KV cache [NEMO, section on FP8

@@ -37,7 +37,7 @@ def L():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 22
+    assert len(names) == 23
     for n in names:
         assert hasattr(L, n), n
     assert sorted(_lib.EXPORTED) == names
@@ -288,6 +288,49 @@ def test_grouped_gemm_validation(L):
     assert f(*b) == EARG
 
 
+def test_grouped_fused_act_validation(L):
+    f = L.fp8rl_grouped_gemm_w8a8_fused_act_quant
+    # the Qwen3-30B-A3B gate/up shape: 4096 tokens, top-8 (32768 grouped rows), 128 experts
+    args = lambda **k: dict(dict(x=A, ldx=2048, src=4096, ids=A, wq=A, sw=A, off=A, E=128,
+                                 M=32768, N=1536, K=2048, y=A, dt=0, acc=3, sf=0, ws=A,
+                                 wsb=1 << 30), **k)
+
+    def call(**k):
+        a = args(**k)
+        return f(a["x"], a["ldx"], a["src"], a["ids"], a["wq"], a["sw"], a["off"], a["E"],
+                 a["M"], a["N"], a["K"], a["y"], a["dt"], a["acc"], a["sf"], a["ws"], a["wsb"],
+                 None)
+
+    assert call(M=0, x=None, ids=None) == OK  # nothing to do
+    assert call(E=0) == EARG
+    assert call(E=1025) == EARG
+    for k in ("x", "wq", "sw", "off", "y"):
+        assert call(**{k: None}) == ENULL, k
+    assert call(N=200) == ESHAPE
+    assert call(K=2000, ldx=2048) == ESHAPE
+    assert call(ldx=1920) == ESHAPE  # pitch below K
+    assert call(src=0) == ESHAPE  # a gather needs at least one source row
+    assert call(ids=None) == ESHAPE  # no gather: x must hold the M_total grouped rows
+    assert call(src=(1 << 32) // 2048, M=32768) == ESHAPE  # source offsets beyond 32 bits
+    assert call(src=(1 << 30) // 16, ids=A, wsb=1 << 62) == ESHAPE  # quantizer grid limit
+    assert call(dt=2) == EDTYPE
+    assert call(acc=4) == EARG
+    assert call(dt=1, acc=0) == EARG  # FP8 slice sums with float32 output
+    assert call(sf=2) == EARG
+    assert call(acc=2, sf=0) == EARG  # matrix-core scaling needs power-of-two scales
+    assert call(x=A + 2) == EALIGN
+    assert call(ldx=2052) == EALIGN  # 4104-byte bf16 pitch
+    assert call(ids=A + 2) == EALIGN
+    assert call(off=A + 2) == EALIGN
+    need = L.fp8rl_workspace_bytes(4, 32768, 1536, 2048, 128)
+    assert call(wsb=need - 1) == EWS
+    assert call(ws=None) == EWS
+    assert call(ws=A + 8, wsb=need) == EALIGN
+    # the workspace is sized for max(src_rows, M_total) rows
+    assert call(src=40000, ids=A, wsb=need) == EWS
+    assert call(src=32768, ids=None, M=32768, wsb=need - 1) == EWS
+
+
 def test_workspace_query_is_pure_host(L):
     hdr = _lib.WORKSPACE_HEADER_BYTES
     assert hdr == 4096  # FP8RL_WORKSPACE_HEADER_BYTES
@@ -337,6 +380,17 @@ def test_workspace_query_is_pure_host(L):
     assert L.fp8rl_workspace_bytes(0, 8192, 4096, 4096, 0) == 0  # large M: no split
     assert L.fp8rl_workspace_bytes(1, 32768, 1536, 2048, 128) == 0
     assert L.fp8rl_workspace_bytes(7, 64, 256, 256, 0) == 0
+    # the grouped GEMM on bf16 activations (op 4), for M rows: the counter header (left alone),
+    # then the codes and scales of M rows, each 256-byte aligned; twice that area past
+    # K = 32768, where the gathered codes are copied out for the register-staged tiles
+    def grouped_fused(M, N, K):
+        area = a256(M * K) + a256(M * (K // 128) * 4)
+        return hdr + (1 if K <= 32768 else 2) * area
+    for shape in [(32768, 1536, 2048), (32768, 2048, 768), (1, 256, 128), (1000, 256, 32768),
+                  (1000, 256, 32896), (77, 384, 640)]:
+        assert L.fp8rl_workspace_bytes(4, *shape, 128) == grouped_fused(*shape), shape
+    assert L.fp8rl_workspace_bytes(4, 32768, 1536, 2048, 128) == 4096 + 32768 * 2048 + 32768 * 64
+    assert L.fp8rl_workspace_bytes(4, 0, 1536, 2048, 128) == 0
 
 
 def test_python_binding_rejects_host_tensors():

@@ -122,12 +122,8 @@ def act_bf16(M: int, K: int, seed: int, *, outlier_frac: float = 0.01, outlier_m
     return x.to(torch.bfloat16)
 
 
-def moe_routing_counts(tokens: int, experts: int, top_k: int, seed: int, *,
-                       zipf_s: float = 1.1) -> torch.Tensor:
-    """Per-expert row counts (int64, length ``experts``) of a Zipf-skewed top-k router.
-
-    Computed on the CPU; the counts sum to ``tokens * top_k``.
-    """
+def _moe_picks(tokens: int, experts: int, top_k: int, seed: int, zipf_s: float) -> torch.Tensor:
+    """The experts each token picks, [tokens][top_k] int64 (CPU)."""
     g = _gen(seed, "cpu")
     perm = torch.randperm(experts, generator=g)  # expert id of rank 1, 2, ...
     rank = torch.empty(experts, dtype=torch.float64)
@@ -136,8 +132,31 @@ def moe_routing_counts(tokens: int, experts: int, top_k: int, seed: int, *,
     u = torch.rand((tokens, experts), generator=g, dtype=torch.float64)
     u = u.clamp_min(1e-300)
     gumbel = -torch.log(-torch.log(u))
-    picks = torch.topk(logits[None, :] + gumbel, top_k, dim=1).indices  # [T][top_k]
+    return torch.topk(logits[None, :] + gumbel, top_k, dim=1).indices  # [T][top_k]
+
+
+def moe_routing_counts(tokens: int, experts: int, top_k: int, seed: int, *,
+                       zipf_s: float = 1.1) -> torch.Tensor:
+    """Per-expert row counts (int64, length ``experts``) of a Zipf-skewed top-k router.
+
+    Computed on the CPU; the counts sum to ``tokens * top_k``.
+    """
+    picks = _moe_picks(tokens, experts, top_k, seed, zipf_s)
     return torch.bincount(picks.reshape(-1), minlength=experts)
+
+
+def moe_routing(tokens: int, experts: int, top_k: int, seed: int, *,
+                zipf_s: float = 1.1) -> tuple[torch.Tensor, torch.Tensor]:
+    """The same router as ``moe_routing_counts`` (same seed, same picks) with the token of every
+    grouped row: returns ``(counts, row_ids)``, ``row_ids`` int32 of length ``tokens * top_k``
+    listing, expert by expert, the tokens that picked that expert in increasing order (so grouped
+    row r of an expert-sorted layout holds token ``row_ids[r]``). CPU tensors."""
+    picks = _moe_picks(tokens, experts, top_k, seed, zipf_s)
+    flat = picks.reshape(-1)
+    token = torch.arange(tokens, dtype=torch.int64).repeat_interleave(top_k)
+    order = torch.argsort(flat * tokens + token)  # distinct keys: a token picks distinct experts
+    counts = torch.bincount(flat, minlength=experts)
+    return counts, token[order].to(torch.int32)
 
 
 def offsets_from_counts(counts) -> torch.Tensor:
