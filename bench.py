@@ -59,7 +59,8 @@ def parse():
     ap.add_argument("--workload", default="qwen3-8b-prefill",
                     choices=["qwen3-8b-decode", "qwen3-8b-prefill", "llama31-8b-mlp",
                              "llama31-8b-weight-sync", "qwen3-30b-a3b-moe", "qwen3-8b-kv-cache",
-                             "qwen3-8b-backward", "qwen3-8b-decode-fused-act"])
+                             "qwen3-8b-backward", "qwen3-8b-decode-fused-act",
+                             "qwen3-30b-a3b-moe-fused-act"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--scales", default="fp32", choices=["fp32", "pow2"],
                     help="block-scale format: fp32(amax/448) (default) or powers of two, whose "
@@ -722,7 +723,8 @@ def main():
     runners = {"qwen3-8b-prefill": run_prefill, "qwen3-8b-decode": run_decode,
                "llama31-8b-mlp": run_mlp, "llama31-8b-weight-sync": run_weight_sync,
                "qwen3-30b-a3b-moe": run_moe, "qwen3-8b-kv-cache": run_kv_cache,
-               "qwen3-8b-backward": run_backward, "qwen3-8b-decode-fused-act": run_fused_act}
+               "qwen3-8b-backward": run_backward, "qwen3-8b-decode-fused-act": run_fused_act,
+               "qwen3-30b-a3b-moe-fused-act": run_moe_fused_act}
     return runners[args.workload](args, torch, fq, synth, gpu, quant_cpu)
 
 
@@ -1285,10 +1287,7 @@ def run_moe(args, torch, fq, synth, gpu, quant_cpu):
     parts = {"grouped_gemm": dict(r, tflops=flops / (g_ms * 1e-3) / 1e12, roofline_us=roof_us,
                                   frac_roofline=roof_us / (1e3 * g_ms)),
              "expert_requant": dict(rq, bytes=wq_bytes, frac_hbm=rq["gbs"] / HBM_PEAK_GBS,
-                                    what="all 2 x 128 expert weights, one batched launch"),
-             "fused_act": moe_fused_act_part(args, torch, fq, synth, T, E, topk, off, x1, x2,
-                                             xq1, sa1, xq2, sa2, wq1, sw1, wq2, sw2, y1, y2,
-                                             accum)}
+                                    what="all 2 x 128 expert weights, one batched launch")}
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline_moe(synth, counts, min_seconds=10.0)
@@ -1297,40 +1296,81 @@ def run_moe(args, torch, fq, synth, gpu, quant_cpu):
          parts=parts, **gpu)
 
 
-def moe_fused_act_part(args, torch, fq, synth, T, E, topk, off, x1, x2, xq1, sa1, xq2, sa2, wq1,
-                       sw1, wq2, sw2, y1, y2, accum):
-    """The grouped GEMMs on bf16 activations against quantize-then-GEMM (graph-replayed, us per
-    layer): gate/up from the T token rows through the router's token indices (each token
-    quantized once, against quantizing its top-k grouped copies), down on the grouped rows."""
-    _, ids = synth.moe_routing(T, E, topk, seed=synth.seed_of(5, 0))
+def run_moe_fused_act(args, torch, fq, synth, gpu, quant_cpu):
+    """The Qwen3-30B-A3B MoE layer's expert GEMMs on bf16 activations, two ways per step:
+    one call per GEMM -- gate/up on the T token rows read through the router's token indices
+    (each token quantized once), down on its input in expert order -- against the 1x128
+    quantizer on the routed rows followed by the grouped GEMM (the routed gate/up input gathered
+    beforehand, not timed). Both replayed from HIP graphs. value = GEMM TFLOP/s of the one-call
+    step; roofline = the one-call gate/up (its quantizer and grouped GEMM launches together)
+    against max(2MNK / FP8 peak, bytes / HBM peak), bytes = bf16 tokens once + every expert's
+    weight codes and scales once + bf16 output."""
+    T, H, I, E, topk = 4096, 2048, 768, 128, 8
+    counts, ids = synth.moe_routing(T, E, topk, seed=synth.seed_of(5, 0))
+    off = synth.offsets_from_counts(counts).cuda()
     ids = ids.cuda()
-    xt = synth.act_bf16(T, x1.shape[1], seed=45, device="cuda")
-    M, H, I = x1.shape[0], x1.shape[1], x2.shape[1]
-    need = max(fq.fp8rl_workspace_bytes(fq.FP8RL_OP_GROUPED_GEMM_FUSED_ACT, M, 2 * I, H, E),
-               fq.fp8rl_workspace_bytes(fq.FP8RL_OP_GROUPED_GEMM_FUSED_ACT, M, H, I, E))
-    ws = fq.new_workspace(need, "cuda")
-    reps = max(5, args.steps)
-    res = {}
-    for name, fused, unfused in (
-            ("gate_up", lambda: fq.grouped_gemm_fused_act(xt, wq1, sw1, off, row_ids=ids, y=y1,
-                                                          workspace=ws, accum=accum,
-                                                          scale=args.scales),
-             lambda: (fq.quant_act(x1, xq1, sa1, scale=args.scales),
-                      fq.grouped_gemm(xq1, sa1, wq1, sw1, off, y=y1, accum=accum))),
-            ("down", lambda: fq.grouped_gemm_fused_act(x2, wq2, sw2, off, y=y2, workspace=ws,
-                                                       accum=accum, scale=args.scales),
-             lambda: (fq.quant_act(x2, xq2, sa2, scale=args.scales),
-                      fq.grouped_gemm(xq2, sa2, wq2, sw2, off, y=y2, accum=accum)))):
-        # alternating rounds, the faster of each: the engine clock settles over the first ones
-        us_f = us_u = float("inf")
-        for _ in range(3):
-            us_f = min(us_f, graph_launch_us(torch, fused, reps))
-            us_u = min(us_u, graph_launch_us(torch, unfused, reps))
-        res[name] = {"one_call_us": us_f, "quant_then_gemm_us": us_u, "ratio": us_f / us_u}
-    res["what"] = ("gate/up: one call on the 4096 token rows with the router's token indices "
-                   "(tokens quantized once) against the 1x128 quantizer on the 32768 grouped "
-                   "rows then the grouped GEMM; down: one call against two on the grouped rows")
-    return res
+    M = int(counts.sum())
+    xt = synth.act_bf16(T, H, seed=45, device="cuda")
+    x1 = xt[ids.long()].contiguous()  # the routed gate/up input of the two-call flow
+    x2 = synth.act_bf16(M, I, seed=42, device="cuda")
+    wq1, sw1 = fq.quant_weight(synth.weight_bf16(2 * I, H, seed=43, batch=E, device="cuda")
+                               .view(E * 2 * I, H), scale=args.scales)
+    wq2, sw2 = fq.quant_weight(synth.weight_bf16(H, I, seed=44, batch=E, device="cuda")
+                               .view(E * H, I), scale=args.scales)
+    wq1, sw1 = wq1.view(E, 2 * I, H), sw1.view(E, 2 * I // 128, H // 128)
+    wq2, sw2 = wq2.view(E, H, I), sw2.view(E, H // 128, I // 128)
+    accum = "mx" if args.scales == "pow2" else None
+    xq1 = torch.empty((M, H), dtype=torch.uint8, device="cuda")
+    sa1 = torch.empty((M, H // 128), dtype=torch.float32, device="cuda")
+    xq2 = torch.empty((M, I), dtype=torch.uint8, device="cuda")
+    sa2 = torch.empty((M, I // 128), dtype=torch.float32, device="cuda")
+    y1 = torch.empty((M, 2 * I), dtype=torch.bfloat16, device="cuda")
+    y2 = torch.empty((M, H), dtype=torch.bfloat16, device="cuda")
+    ws = fq.new_workspace(max(fq.fp8rl_workspace_bytes(fq.FP8RL_OP_GROUPED_GEMM_FUSED_ACT, M, N, K, E)
+                              for N, K in ((2 * I, H), (H, I))), "cuda")
+    fused_up = lambda: fq.grouped_gemm_fused_act(xt, wq1, sw1, off, row_ids=ids, y=y1,
+                                                 workspace=ws, accum=accum, scale=args.scales)
+    fused_down = lambda: fq.grouped_gemm_fused_act(x2, wq2, sw2, off, y=y2, workspace=ws,
+                                                   accum=accum, scale=args.scales)
+    two_up = lambda: (fq.quant_act(x1, xq1, sa1, scale=args.scales),
+                      fq.grouped_gemm(xq1, sa1, wq1, sw1, off, y=y1, accum=accum))
+    two_down = lambda: (fq.quant_act(x2, xq2, sa2, scale=args.scales),
+                        fq.grouped_gemm(xq2, sa2, wq2, sw2, off, y=y2, accum=accum))
+    reps = max(10, args.steps)
+    # alternating rounds, the faster of each: the engine clock settles over the first ones
+    t = {k: float("inf") for k in ("fused_up", "fused_down", "two_up", "two_down")}
+    for _ in range(3):
+        for k, fn in (("fused_up", fused_up), ("two_up", two_up), ("fused_down", fused_down),
+                      ("two_down", two_down)):
+            t[k] = min(t[k], graph_launch_us(torch, fn, reps))
+    flops_up, flops_down = 2 * M * (2 * I) * H, 2 * M * H * I
+    ms = (t["fused_up"] + t["fused_down"]) / 1e3
+    value = (flops_up + flops_down) / (ms * 1e-3) / 1e12
+    b_up = 2 * T * H + E * (2 * I * H + 4 * (2 * I // 128) * (H // 128)) + 2 * M * 2 * I
+    roof_us = 1e6 * max(flops_up / (FP8_PEAK_TFLOPS * 1e12), b_up / (HBM_PEAK_GBS * 1e9))
+    roof = roof_hbm("quant_act_tok128_kernel + grouped_big_kernel (one call, token gather)",
+                    b_up, t["fused_up"],
+                    "bf16 token activations once + every expert's weight codes and block scales "
+                    "once + bf16 output", "the gate/up call (two launches)")
+    roof["frac_roofline"] = roof_us / t["fused_up"]
+    roof["roofline_rule"] = "max(2MNK / 5.0 PFLOP/s, bytes / 8 TB/s)"
+    cfg = {"workload": "Qwen3-30B-A3B MoE expert GEMMs on bf16 activations (T=4096, E=128, top-8, "
+                       "Zipf 1.1 routing), activation quantization inside the GEMM call",
+           "tokens": T, "experts": E, "top_k": topk, "routed_rows": M,
+           "gemms": [["gate_up", 2 * I, H], ["down", H, I]], "scales": args.scales}
+    parts = {"gate_up": {"one_call_us": t["fused_up"], "two_calls_us": t["two_up"],
+                         "ratio": t["fused_up"] / t["two_up"],
+                         "what": "one call on the token rows with the router's indices against "
+                                 "the quantizer on the routed rows, then the grouped GEMM"},
+             "down": {"one_call_us": t["fused_down"], "two_calls_us": t["two_down"],
+                      "ratio": t["fused_down"] / t["two_down"]},
+             "two_call_step_tflops": (flops_up + flops_down)
+             / ((t["two_up"] + t["two_down"]) * 1e-6) / 1e12}
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline_moe(synth, counts, min_seconds=10.0)
+        cpu["gpu_over_oracle"] = value / cpu["value"]
+    emit(args, value, "TFLOP/s", ms, cfg, roof, cpu, parts=parts, **gpu)
 
 
 def cpu_baseline_moe(synth, counts, min_seconds=10.0):
