@@ -242,6 +242,18 @@ def _dense(t: torch.Tensor, name: str, dtype: torch.dtype):
         raise ValueError(f"{name} must be a contiguous cuda {dtype} tensor")
 
 
+def _sizes(**want):
+    """Raise unless each tensor has the stated element count (int) or shape (tuple): the C calls
+    take only pointers and pitches, so a smaller tensor would be read or written past its end."""
+    for name, (t, w) in want.items():
+        if t is None:
+            continue
+        ok = t.numel() == w if isinstance(w, int) else tuple(t.shape) == tuple(w)
+        if not ok:
+            got = t.numel() if isinstance(w, int) else tuple(t.shape)
+            raise ValueError(f"{name} has {got}, expected {w}")
+
+
 # ---------------------------------------------------------------------------------------------
 # One Python function per C entry point, same name, tensors in place of pointers.
 # ---------------------------------------------------------------------------------------------
@@ -402,6 +414,7 @@ def fp8rl_gemm_w8a8_blockscaled(xq, sa, wq, sw, out_dtype=torch.bfloat16, y=None
     if y is None:
         y = torch.empty((M, N), dtype=out_dtype, device=xq.device)
     ld_y = _rows(y, "y", y.dtype)
+    _sizes(sa=(sa, M * (K // 128)), sw=(sw, (N // 128) * (K // 128)), y=(y, (M, N)))
     need = fp8rl_workspace_bytes(FP8RL_OP_GEMM, M, N, K)
     if workspace is None and need > 0:
         workspace = new_workspace(need, xq.device)
@@ -431,6 +444,7 @@ def fp8rl_gemm_w8a8_blockscaled_noalloc(xq, sa, wq, sw, y, stream=None, accum=No
     if wq.shape[1] != K:
         raise ValueError("K mismatch between xq and wq")
     ld_y = _rows(y, "y", y.dtype)
+    _sizes(sa=(sa, M * (K // 128)), sw=(sw, (N // 128) * (K // 128)), y=(y, (M, N)))
     _check(lib().fp8rl_gemm_w8a8_blockscaled_noalloc(_ptr(xq), _ptr(sa), _ptr(wq), _ptr(sw), M, N,
                                                      K, _ptr(y), _out_code(y.dtype), ld_y,
                                                      _accum_code(accum, y.dtype),
@@ -455,6 +469,7 @@ def fp8rl_gemm_w8a8_rowscaled(aq, sa, bq, sb, out_dtype=torch.bfloat16, y=None, 
     if y is None:
         y = torch.empty((M, N), dtype=out_dtype, device=aq.device)
     ld_y = _rows(y, "y", y.dtype)
+    _sizes(y=(y, (M, N)))
     need = fp8rl_workspace_bytes(FP8RL_OP_GEMM_ROWSCALED, M, N, K)
     if workspace is None and need > 0:
         workspace = new_workspace(need, aq.device)
@@ -481,6 +496,7 @@ def fp8rl_gemm_w8a8_fused_act_quant(x, wq, sw, out_dtype=torch.bfloat16, y=None,
     if y is None:
         y = torch.empty((M, N), dtype=out_dtype, device=x.device)
     ld_y = _rows(y, "y", y.dtype)
+    _sizes(sw=(sw, (N // 128) * (K // 128)), y=(y, (M, N)))
     need = fp8rl_workspace_bytes(FP8RL_OP_GEMM_FUSED_ACT, M, N, K)
     if workspace is None and need > 0:
         workspace = new_workspace(need, x.device)
@@ -509,6 +525,7 @@ def fp8rl_grouped_gemm_w8a8(xq, sa, wq, sw, expert_offsets, out_dtype=torch.bflo
     if y is None:
         y = torch.empty((M, N), dtype=out_dtype, device=xq.device)
     _dense(y, "y", y.dtype)
+    _sizes(sa=(sa, M * (K // 128)), sw=(sw, E * (N // 128) * (K // 128)), y=(y, (M, N)))
     need = fp8rl_workspace_bytes(FP8RL_OP_GROUPED_GEMM, M, N, K, E)
     if workspace is None and need > 0:
         workspace = new_workspace(need, xq.device)
@@ -545,8 +562,7 @@ def fp8rl_grouped_gemm_w8a8_fused_act_quant(x, wq, sw, expert_offsets, row_ids=N
     if y is None:
         y = torch.empty((M, N), dtype=out_dtype, device=x.device)
     _dense(y, "y", y.dtype)
-    if y.shape[0] != M:
-        raise ValueError("y must have one row per grouped row")
+    _sizes(sw=(sw, E * (N // 128) * (K // 128)), y=(y, (M, N)))
     need = fp8rl_workspace_bytes(FP8RL_OP_GROUPED_GEMM_FUSED_ACT, max(src_rows, M), N, K, E)
     if workspace is None and need > 0:
         workspace = new_workspace(need, x.device)

@@ -401,6 +401,21 @@ def test_python_binding_rejects_host_tensors():
         _lib.fp8rl_quant_weight_blk128(w)
 
 
+def test_binding_size_checks():
+    """The bindings compare every tensor the C call reads or writes by pointer alone with the size
+    the call will assume (a smaller tensor would be accessed past its end)."""
+    import torch
+
+    t = torch.zeros((4, 256))
+    _lib._sizes(y=(t, (4, 256)), s=(t, 1024), none=(None, 7))
+    with pytest.raises(ValueError):
+        _lib._sizes(y=(t, (3, 256)))
+    with pytest.raises(ValueError):
+        _lib._sizes(y=(t, (4, 384)))
+    with pytest.raises(ValueError):
+        _lib._sizes(s=(t, 1023))
+
+
 def test_noalloc_gemm_validation(L):
     """The no-allocation GEMM validates like the workspace form and refuses, before any HIP call,
     a shape whose scratch need exceeds the static buffer."""

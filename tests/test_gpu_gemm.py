@@ -184,6 +184,34 @@ def test_one_workspace_reused_across_shapes():
     assert int(ws[:fq.WORKSPACE_HEADER_BYTES].count_nonzero()) == 0
 
 
+def test_bindings_reject_mis_sized_tensors():
+    """Outputs and scales of the wrong size are refused by the bindings before any launch."""
+    xq, sa, wq, sw = quantized_operands(64, 256, 256, 90)
+    d = [to_dev_u8(xq), to_dev_f32(sa), to_dev_u8(wq), to_dev_f32(sw)]
+    with pytest.raises(ValueError):
+        fq.gemm(*d, y=torch.empty((63, 256), dtype=torch.bfloat16, device="cuda"))
+    with pytest.raises(ValueError):
+        fq.gemm(d[0], d[1][:32], d[2], d[3])
+    with pytest.raises(ValueError):
+        fq.gemm_noalloc(*d, torch.empty((64, 128), dtype=torch.bfloat16, device="cuda"))
+    off = torch.tensor([0, 30, 64], dtype=torch.int32, device="cuda")
+    wq2 = torch.stack([d[2], d[2]])
+    sw2 = torch.stack([d[3], d[3]])
+    with pytest.raises(ValueError):
+        fq.grouped_gemm(d[0], d[1], wq2, sw2, off, y=torch.empty((64, 128), dtype=torch.bfloat16,
+                                                                 device="cuda"))
+    with pytest.raises(ValueError):
+        fq.grouped_gemm(d[0], d[1], wq2, d[3], off)  # one expert's scales for two experts
+    x = torch.zeros((64, 256), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError):
+        fq.grouped_gemm_fused_act(x, wq2, sw2, off, y=torch.empty((64, 128), dtype=torch.bfloat16,
+                                                                  device="cuda"))
+    with pytest.raises(ValueError):
+        fq.gemm_fused_act(x, d[2], d[3], y=torch.empty((32, 256), dtype=torch.bfloat16,
+                                                        device="cuda"))
+    torch.cuda.synchronize()
+
+
 def test_zero_rows_noop():
     xq = torch.empty((0, 256), dtype=torch.uint8, device="cuda")
     sa = torch.empty((0, 2), dtype=torch.float32, device="cuda")
