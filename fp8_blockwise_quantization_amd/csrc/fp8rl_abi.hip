@@ -12,19 +12,20 @@ constexpr int64_t kMaxDim = (int64_t{1} << 31) - 1;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
-int hip_status(hipError_t e) { return e == hipSuccess ? FP8RL_OK : FP8RL_ERR_HIP; }
+fp8rl_status hip_status(hipError_t e) { return e == hipSuccess ? FP8RL_OK : FP8RL_ERR_HIP; }
 
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
-int check_dims(int64_t a, int64_t b, int64_t c) {
+fp8rl_status check_dims(int64_t a, int64_t b, int64_t c) {
   if (a < 0 || b < 0 || c < 0) return FP8RL_ERR_SHAPE;
   if (a > kMaxDim || b > kMaxDim || c > kMaxDim) return FP8RL_ERR_SHAPE;
   return FP8RL_OK;
 }
 
 // Shared checks of the dense and grouped GEMMs' operands.
-int check_gemm_common(const uint8_t* xq, const float* sa, const uint8_t* wq, const float* sw,
-                      int64_t N, int64_t K, const void* y, int y_dtype, int64_t ld_y) {
+fp8rl_status check_gemm_common(const uint8_t* xq, const float* sa, const uint8_t* wq,
+                               const float* sw, int64_t N, int64_t K, const void* y, int y_dtype,
+                               int64_t ld_y) {
   if (!xq || !sa || !wq || !sw || !y) return FP8RL_ERR_NULL;
   if (N == 0 || K == 0 || N % 128 || K % 128) return FP8RL_ERR_SHAPE;
   if (y_dtype != FP8RL_OUT_BF16 && y_dtype != FP8RL_OUT_F32) return FP8RL_ERR_DTYPE;
@@ -70,7 +71,7 @@ const char* fp8rl_status_string(int s) {
   }
 }
 
-int fp8rl_encode_e4m3_f32(const float* v, int64_t n, uint8_t* out, void* stream) {
+fp8rl_status fp8rl_encode_e4m3_f32(const float* v, int64_t n, uint8_t* out, void* stream) {
   if (n < 0 || n > (int64_t{1} << 33)) return FP8RL_ERR_SHAPE;
   if (n == 0) return FP8RL_OK;
   if (!v || !out) return FP8RL_ERR_NULL;
@@ -80,8 +81,8 @@ int fp8rl_encode_e4m3_f32(const float* v, int64_t n, uint8_t* out, void* stream)
 
 namespace {
 
-int check_weight(const fp8rl_weight_desc& d) {
-  if (int s = check_dims(d.N, d.K, 0)) return s;
+fp8rl_status check_weight(const fp8rl_weight_desc& d) {
+  if (fp8rl_status s = check_dims(d.N, d.K, 0)) return s;
   if (d.N == 0 || d.K == 0) return FP8RL_OK;
   if (!d.w || !d.wq || !d.sw) return FP8RL_ERR_NULL;
   if (d.N % 128 || d.K % 128 || d.ld_w < d.K || d.ld_wq < d.K) return FP8RL_ERR_SHAPE;
@@ -94,11 +95,12 @@ int check_weight(const fp8rl_weight_desc& d) {
 
 // Launch the (already validated) descriptors in groups that fit one kernel's argument block
 // and keep every grid below 2^24 workgroups.
-int launch_weights(const fp8rl_weight_desc* descs, int32_t count, int pow2, hipStream_t stream) {
+fp8rl_status launch_weights(const fp8rl_weight_desc* descs, int32_t count, int pow2,
+                            hipStream_t stream) {
   fp8rl::WeightBatch b{};
   b.pow2 = pow2;
   int64_t strips = 0;
-  auto flush = [&]() -> int {
+  auto flush = [&]() -> fp8rl_status {
     if (b.count == 0) return FP8RL_OK;
     hipError_t e = fp8rl::launch_quant_weight_batch(b, (int)strips, stream);
     b = fp8rl::WeightBatch{};
@@ -111,7 +113,7 @@ int launch_weights(const fp8rl_weight_desc* descs, int32_t count, int pow2, hipS
     if (d.N == 0 || d.K == 0) continue;
     const int64_t nb = (d.N / 128) * ((d.K / 128 + 1) / 2);  // workgroups: 128x256 strips
     if (b.count == fp8rl::kWeightBatch || strips + nb >= (int64_t{1} << 24))
-      if (int s = flush()) return s;
+      if (fp8rl_status s = flush()) return s;
     b.w[b.count] = d.w;
     b.wq[b.count] = d.wq;
     b.sw[b.count] = d.sw;
@@ -127,39 +129,41 @@ int launch_weights(const fp8rl_weight_desc* descs, int32_t count, int pow2, hipS
 
 }  // namespace
 
-int fp8rl_quant_weight_blk128_ex(const uint16_t* w, int64_t N, int64_t K, int64_t ld_w,
-                                 uint8_t* wq, int64_t ld_wq, float* sw, int scale_fmt,
-                                 void* stream) {
+fp8rl_status fp8rl_quant_weight_blk128_ex(const uint16_t* w, int64_t N, int64_t K, int64_t ld_w,
+                                          uint8_t* wq, int64_t ld_wq, float* sw, int scale_fmt,
+                                          void* stream) {
   if (scale_fmt != FP8RL_SCALE_FP32 && scale_fmt != FP8RL_SCALE_POW2) return FP8RL_ERR_ARG;
   const fp8rl_weight_desc d{w, wq, sw, N, K, ld_w, ld_wq};
-  if (int s = check_weight(d)) return s;
+  if (fp8rl_status s = check_weight(d)) return s;
   return launch_weights(&d, 1, scale_fmt == FP8RL_SCALE_POW2, as_stream(stream));
 }
 
-int fp8rl_quant_weight_blk128(const uint16_t* w, int64_t N, int64_t K, int64_t ld_w, uint8_t* wq,
-                              int64_t ld_wq, float* sw, void* stream) {
+fp8rl_status fp8rl_quant_weight_blk128(const uint16_t* w, int64_t N, int64_t K, int64_t ld_w,
+                                       uint8_t* wq, int64_t ld_wq, float* sw, void* stream) {
   return fp8rl_quant_weight_blk128_ex(w, N, K, ld_w, wq, ld_wq, sw, FP8RL_SCALE_FP32, stream);
 }
 
-int fp8rl_quant_weight_blk128_batched_ex(const fp8rl_weight_desc* descs, int32_t count,
-                                         int scale_fmt, void* stream) {
+fp8rl_status fp8rl_quant_weight_blk128_batched_ex(const fp8rl_weight_desc* descs, int32_t count,
+                                                  int scale_fmt, void* stream) {
   if (scale_fmt != FP8RL_SCALE_FP32 && scale_fmt != FP8RL_SCALE_POW2) return FP8RL_ERR_ARG;
   if (count < 0) return FP8RL_ERR_ARG;
   if (count == 0) return FP8RL_OK;
   if (!descs) return FP8RL_ERR_NULL;
   for (int32_t i = 0; i < count; ++i)
-    if (int s = check_weight(descs[i])) return s;
+    if (fp8rl_status s = check_weight(descs[i])) return s;
   return launch_weights(descs, count, scale_fmt == FP8RL_SCALE_POW2, as_stream(stream));
 }
 
-int fp8rl_quant_weight_blk128_batched(const fp8rl_weight_desc* descs, int32_t count, void* stream) {
+fp8rl_status fp8rl_quant_weight_blk128_batched(const fp8rl_weight_desc* descs, int32_t count,
+                                               void* stream) {
   return fp8rl_quant_weight_blk128_batched_ex(descs, count, FP8RL_SCALE_FP32, stream);
 }
 
-int fp8rl_quant_act_tok128_ex(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x, uint8_t* xq,
-                              int64_t ld_xq, float* sa, int scale_fmt, void* stream) {
+fp8rl_status fp8rl_quant_act_tok128_ex(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x,
+                                       uint8_t* xq, int64_t ld_xq, float* sa, int scale_fmt,
+                                       void* stream) {
   if (scale_fmt != FP8RL_SCALE_FP32 && scale_fmt != FP8RL_SCALE_POW2) return FP8RL_ERR_ARG;
-  if (int s = check_dims(M, K, 0)) return s;
+  if (fp8rl_status s = check_dims(M, K, 0)) return s;
   if (M == 0 || K == 0) return FP8RL_OK;
   if (!x || !xq || !sa) return FP8RL_ERR_NULL;
   if (K % 128 || ld_x < K || ld_xq < K) return FP8RL_ERR_SHAPE;
@@ -170,16 +174,16 @@ int fp8rl_quant_act_tok128_ex(const uint16_t* x, int64_t M, int64_t K, int64_t l
                                             scale_fmt == FP8RL_SCALE_POW2, as_stream(stream)));
 }
 
-int fp8rl_quant_act_tok128(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x, uint8_t* xq,
-                           int64_t ld_xq, float* sa, void* stream) {
+fp8rl_status fp8rl_quant_act_tok128(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x,
+                                    uint8_t* xq, int64_t ld_xq, float* sa, void* stream) {
   return fp8rl_quant_act_tok128_ex(x, M, K, ld_x, xq, ld_xq, sa, FP8RL_SCALE_FP32, stream);
 }
 
 namespace {
 
 // Shape / alignment rules of the per-tensor calls; `empty` is set when there is nothing to do.
-int check_tensor(const void* x, int64_t rows, int64_t cols, int64_t ld_x, bool& empty) {
-  if (int s = check_dims(rows, cols, ld_x)) return s;
+fp8rl_status check_tensor(const void* x, int64_t rows, int64_t cols, int64_t ld_x, bool& empty) {
+  if (fp8rl_status s = check_dims(rows, cols, ld_x)) return s;
   empty = rows == 0 || cols == 0;
   if (empty) return FP8RL_OK;
   if (!x) return FP8RL_ERR_NULL;
@@ -189,15 +193,15 @@ int check_tensor(const void* x, int64_t rows, int64_t cols, int64_t ld_x, bool& 
   return FP8RL_OK;
 }
 
-int check_amax_desc(const fp8rl_tensor_desc& d, bool& empty) {
-  if (int s = check_tensor(d.x, d.rows, d.cols, d.ld_x, empty)) return s;
+fp8rl_status check_amax_desc(const fp8rl_tensor_desc& d, bool& empty) {
+  if (fp8rl_status s = check_tensor(d.x, d.rows, d.cols, d.ld_x, empty)) return s;
   if (empty) return FP8RL_OK;
   if (!d.amax) return FP8RL_ERR_NULL;
   if (!aligned(d.amax, 4)) return FP8RL_ERR_ALIGN;
   return FP8RL_OK;
 }
 
-int launch_amax(const fp8rl_tensor_desc* descs, int32_t count, hipStream_t stream) {
+fp8rl_status launch_amax(const fp8rl_tensor_desc* descs, int32_t count, hipStream_t stream) {
   int64_t total = 0;
   for (int32_t i = 0; i < count; ++i) total += descs[i].rows * (descs[i].cols / 8);
   const int launches = (count + fp8rl::kTensorBatch - 1) / fp8rl::kTensorBatch;
@@ -211,7 +215,7 @@ int launch_amax(const fp8rl_tensor_desc* descs, int32_t count, hipStream_t strea
     b.chunks = shape.chunks;
     wgs = 0;
   };
-  auto flush = [&]() -> int {
+  auto flush = [&]() -> fp8rl_status {
     if (b.count == 0) return FP8RL_OK;
     hipError_t e = fp8rl::launch_amax_batch(b, (int)wgs, stream);
     reset();
@@ -224,7 +228,7 @@ int launch_amax(const fp8rl_tensor_desc* descs, int32_t count, hipStream_t strea
     if (units == 0) continue;
     const int64_t n = (units + upw - 1) / upw;
     if (b.count == fp8rl::kTensorBatch || wgs + n >= (int64_t{1} << 30))
-      if (int s = flush()) return s;
+      if (fp8rl_status s = flush()) return s;
     b.x[b.count] = d.x;
     b.amax[b.count] = d.amax;
     b.ld_x[b.count] = d.ld_x;
@@ -239,27 +243,27 @@ int launch_amax(const fp8rl_tensor_desc* descs, int32_t count, hipStream_t strea
 
 }  // namespace
 
-int fp8rl_amax_bf16(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, float* amax,
-                    void* stream) {
+fp8rl_status fp8rl_amax_bf16(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                             float* amax, void* stream) {
   const fp8rl_tensor_desc d{x, amax, rows, cols, ld_x};
   bool empty = false;
-  if (int s = check_amax_desc(d, empty)) return s;
+  if (fp8rl_status s = check_amax_desc(d, empty)) return s;
   if (empty) return FP8RL_OK;
   return launch_amax(&d, 1, as_stream(stream));
 }
 
-int fp8rl_amax_bf16_batched(const fp8rl_tensor_desc* descs, int32_t count, void* stream) {
+fp8rl_status fp8rl_amax_bf16_batched(const fp8rl_tensor_desc* descs, int32_t count, void* stream) {
   if (count < 0) return FP8RL_ERR_ARG;
   if (count == 0) return FP8RL_OK;
   if (!descs) return FP8RL_ERR_NULL;
   for (int32_t i = 0; i < count; ++i) {
     bool empty = false;
-    if (int s = check_amax_desc(descs[i], empty)) return s;
+    if (fp8rl_status s = check_amax_desc(descs[i], empty)) return s;
   }
   return launch_amax(descs, count, as_stream(stream));
 }
 
-int fp8rl_scale_from_amax(const float* amax, int32_t n, float* scale, void* stream) {
+fp8rl_status fp8rl_scale_from_amax(const float* amax, int32_t n, float* scale, void* stream) {
   if (n < 0) return FP8RL_ERR_SHAPE;
   if (n == 0) return FP8RL_OK;
   if (!amax || !scale) return FP8RL_ERR_NULL;
@@ -269,9 +273,9 @@ int fp8rl_scale_from_amax(const float* amax, int32_t n, float* scale, void* stre
 
 namespace {
 
-int check_quant_desc(const fp8rl_quant_desc& d, bool& empty) {
-  if (int s = check_tensor(d.x, d.rows, d.cols, d.ld_x, empty)) return s;
-  if (int s = check_dims(d.out_rows, d.ld_out, 0)) return s;
+fp8rl_status check_quant_desc(const fp8rl_quant_desc& d, bool& empty) {
+  if (fp8rl_status s = check_tensor(d.x, d.rows, d.cols, d.ld_x, empty)) return s;
+  if (fp8rl_status s = check_dims(d.out_rows, d.ld_out, 0)) return s;
   if (empty) return FP8RL_OK;
   if (!d.scale || !d.out) return FP8RL_ERR_NULL;
   if (d.ld_out < d.cols || (!d.slot_mapping && d.rows > d.out_rows)) return FP8RL_ERR_SHAPE;
@@ -281,7 +285,7 @@ int check_quant_desc(const fp8rl_quant_desc& d, bool& empty) {
   return FP8RL_OK;
 }
 
-int launch_quant(const fp8rl_quant_desc* descs, int32_t count, hipStream_t stream) {
+fp8rl_status launch_quant(const fp8rl_quant_desc* descs, int32_t count, hipStream_t stream) {
   int64_t total = 0;
   for (int32_t i = 0; i < count; ++i) total += descs[i].rows * (descs[i].cols / 8);
   const int steps = fp8rl::quant_steps(total);
@@ -293,7 +297,7 @@ int launch_quant(const fp8rl_quant_desc* descs, int32_t count, hipStream_t strea
     b.steps = steps;
     wgs = 0;
   };
-  auto flush = [&]() -> int {
+  auto flush = [&]() -> fp8rl_status {
     if (b.count == 0) return FP8RL_OK;
     hipError_t e = fp8rl::launch_quant_batch(b, (int)wgs, stream);
     reset();
@@ -306,7 +310,7 @@ int launch_quant(const fp8rl_quant_desc* descs, int32_t count, hipStream_t strea
     if (units == 0) continue;
     const int64_t n = (units + upw - 1) / upw;
     if (b.count == fp8rl::kQuantBatch || wgs + n >= (int64_t{1} << 30))
-      if (int s = flush()) return s;
+      if (fp8rl_status s = flush()) return s;
     const int c = b.count;
     b.x[c] = d.x;
     b.scale[c] = d.scale;
@@ -326,33 +330,34 @@ int launch_quant(const fp8rl_quant_desc* descs, int32_t count, hipStream_t strea
 
 }  // namespace
 
-int fp8rl_quant_bf16_per_tensor(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
-                                const float* scale, uint8_t* out, int64_t out_rows,
-                                int64_t ld_out, const int64_t* slot_mapping, void* stream) {
+fp8rl_status fp8rl_quant_bf16_per_tensor(const uint16_t* x, int64_t rows, int64_t cols,
+                                         int64_t ld_x, const float* scale, uint8_t* out,
+                                         int64_t out_rows, int64_t ld_out,
+                                         const int64_t* slot_mapping, void* stream) {
   const fp8rl_quant_desc d{x, scale, out, slot_mapping, rows, cols, ld_x, out_rows, ld_out};
   bool empty = false;
-  if (int s = check_quant_desc(d, empty)) return s;
+  if (fp8rl_status s = check_quant_desc(d, empty)) return s;
   if (empty) return FP8RL_OK;
   return launch_quant(&d, 1, as_stream(stream));
 }
 
-int fp8rl_quant_bf16_per_tensor_batched(const fp8rl_quant_desc* descs, int32_t count,
-                                        void* stream) {
+fp8rl_status fp8rl_quant_bf16_per_tensor_batched(const fp8rl_quant_desc* descs, int32_t count,
+                                                 void* stream) {
   if (count < 0) return FP8RL_ERR_ARG;
   if (count == 0) return FP8RL_OK;
   if (!descs) return FP8RL_ERR_NULL;
   for (int32_t i = 0; i < count; ++i) {
     bool empty = false;
-    if (int s = check_quant_desc(descs[i], empty)) return s;
+    if (fp8rl_status s = check_quant_desc(descs[i], empty)) return s;
   }
   return launch_quant(descs, count, as_stream(stream));
 }
 
-int fp8rl_quant_weight_blk128_t(const uint16_t* w, int64_t N, int64_t K, int64_t ld_w, uint8_t* wq,
-                                int64_t ld_wq, float* sw, uint8_t* wqt, int64_t ld_wqt, float* swt,
-                                int scale_fmt, void* stream) {
+fp8rl_status fp8rl_quant_weight_blk128_t(const uint16_t* w, int64_t N, int64_t K, int64_t ld_w,
+                                         uint8_t* wq, int64_t ld_wq, float* sw, uint8_t* wqt,
+                                         int64_t ld_wqt, float* swt, int scale_fmt, void* stream) {
   if (scale_fmt != FP8RL_SCALE_FP32 && scale_fmt != FP8RL_SCALE_POW2) return FP8RL_ERR_ARG;
-  if (int s = check_dims(N, K, 0)) return s;
+  if (fp8rl_status s = check_dims(N, K, 0)) return s;
   if (N == 0 || K == 0) return FP8RL_OK;
   if (!w || !wqt || !swt || (!wq) != (!sw)) return FP8RL_ERR_NULL;
   if (N % 128 || K % 128 || ld_w < K || ld_wqt < N || (wq && ld_wq < K)) return FP8RL_ERR_SHAPE;
@@ -365,11 +370,11 @@ int fp8rl_quant_weight_blk128_t(const uint16_t* w, int64_t N, int64_t K, int64_t
   return hip_status(fp8rl::launch_quant_tile_t(a, 0, as_stream(stream)));
 }
 
-int fp8rl_quant_act_colwise128(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x, uint8_t* xq,
-                               int64_t ld_xq, float* sa, uint8_t* xtq, int64_t ld_xtq, float* sat,
-                               int scale_fmt, void* stream) {
+fp8rl_status fp8rl_quant_act_colwise128(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x,
+                                        uint8_t* xq, int64_t ld_xq, float* sa, uint8_t* xtq,
+                                        int64_t ld_xtq, float* sat, int scale_fmt, void* stream) {
   if (scale_fmt != FP8RL_SCALE_FP32 && scale_fmt != FP8RL_SCALE_POW2) return FP8RL_ERR_ARG;
-  if (int s = check_dims(M, K, 0)) return s;
+  if (fp8rl_status s = check_dims(M, K, 0)) return s;
   if (M == 0 || K == 0) return FP8RL_OK;
   if (!x || !xtq || !sat || (!xq) != (!sa)) return FP8RL_ERR_NULL;
   if (M % 128 || K % 128 || ld_x < K || ld_xtq < M || (xq && ld_xq < K)) return FP8RL_ERR_SHAPE;
@@ -395,12 +400,13 @@ size_t fp8rl_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int32_t E)
 
 namespace {
 
-int gemm_common(const uint8_t* xq, const float* sa, const uint8_t* wq, const float* sw, int64_t M,
-                int64_t N, int64_t K, void* y, int y_dtype, int64_t ld_y, int accum, bool rowb,
-                void* workspace, size_t workspace_bytes, void* stream) {
-  if (int s = check_dims(M, N, K)) return s;
+fp8rl_status gemm_common(const uint8_t* xq, const float* sa, const uint8_t* wq, const float* sw,
+                         int64_t M, int64_t N, int64_t K, void* y, int y_dtype, int64_t ld_y,
+                         int accum, bool rowb, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  if (fp8rl_status s = check_dims(M, N, K)) return s;
   if (M == 0) return FP8RL_OK;
-  if (int s = check_gemm_common(xq, sa, wq, sw, N, K, y, y_dtype, ld_y)) return s;
+  if (fp8rl_status s = check_gemm_common(xq, sa, wq, sw, N, K, y, y_dtype, ld_y)) return s;
   accum = resolve_accum(accum, y_dtype, rowb);
   if (accum < 0) return FP8RL_ERR_ARG;
   if (((M + 127) / 128) * (N / 64) >= (int64_t{1} << 22)) return FP8RL_ERR_SHAPE;  // grid limit
@@ -415,20 +421,21 @@ int gemm_common(const uint8_t* xq, const float* sa, const uint8_t* wq, const flo
 
 }  // namespace
 
-int fp8rl_gemm_w8a8_blockscaled(const uint8_t* xq, const float* sa, const uint8_t* wq,
-                                const float* sw, int64_t M, int64_t N, int64_t K, void* y,
-                                int y_dtype, int64_t ld_y, int accum, void* workspace,
-                                size_t workspace_bytes, void* stream) {
+fp8rl_status fp8rl_gemm_w8a8_blockscaled(const uint8_t* xq, const float* sa, const uint8_t* wq,
+                                         const float* sw, int64_t M, int64_t N, int64_t K, void* y,
+                                         int y_dtype, int64_t ld_y, int accum, void* workspace,
+                                         size_t workspace_bytes, void* stream) {
   return gemm_common(xq, sa, wq, sw, M, N, K, y, y_dtype, ld_y, accum, false, workspace,
                      workspace_bytes, stream);
 }
 
-int fp8rl_gemm_w8a8_blockscaled_noalloc(const uint8_t* xq, const float* sa, const uint8_t* wq,
-                                        const float* sw, int64_t M, int64_t N, int64_t K, void* y,
-                                        int y_dtype, int64_t ld_y, int accum, void* stream) {
-  if (int s = check_dims(M, N, K)) return s;
+fp8rl_status fp8rl_gemm_w8a8_blockscaled_noalloc(const uint8_t* xq, const float* sa,
+                                                 const uint8_t* wq, const float* sw, int64_t M,
+                                                 int64_t N, int64_t K, void* y, int y_dtype,
+                                                 int64_t ld_y, int accum, void* stream) {
+  if (fp8rl_status s = check_dims(M, N, K)) return s;
   if (M == 0) return FP8RL_OK;
-  if (int s = check_gemm_common(xq, sa, wq, sw, N, K, y, y_dtype, ld_y)) return s;
+  if (fp8rl_status s = check_gemm_common(xq, sa, wq, sw, N, K, y, y_dtype, ld_y)) return s;
   accum = resolve_accum(accum, y_dtype, false);
   if (accum < 0) return FP8RL_ERR_ARG;
   if (((M + 127) / 128) * (N / 64) >= (int64_t{1} << 22)) return FP8RL_ERR_SHAPE;
@@ -443,11 +450,12 @@ int fp8rl_gemm_w8a8_blockscaled_noalloc(const uint8_t* xq, const float* sa, cons
                                        accum, false, ws, plan, as_stream(stream)));
 }
 
-int fp8rl_gemm_w8a8_fused_act_quant(const uint16_t* x, int64_t ld_x, const uint8_t* wq,
-                                    const float* sw, int64_t M, int64_t N, int64_t K, void* y,
-                                    int y_dtype, int64_t ld_y, int accum, int scale_fmt,
-                                    void* workspace, size_t workspace_bytes, void* stream) {
-  if (int s = check_dims(M, N, K)) return s;
+fp8rl_status fp8rl_gemm_w8a8_fused_act_quant(const uint16_t* x, int64_t ld_x, const uint8_t* wq,
+                                             const float* sw, int64_t M, int64_t N, int64_t K,
+                                             void* y, int y_dtype, int64_t ld_y, int accum,
+                                             int scale_fmt, void* workspace, size_t workspace_bytes,
+                                             void* stream) {
+  if (fp8rl_status s = check_dims(M, N, K)) return s;
   if (M == 0) return FP8RL_OK;
   if (!x || !wq || !sw || !y) return FP8RL_ERR_NULL;
   if (N == 0 || K == 0 || N % 128 || K % 128) return FP8RL_ERR_SHAPE;
@@ -474,23 +482,24 @@ int fp8rl_gemm_w8a8_fused_act_quant(const uint16_t* x, int64_t ld_x, const uint8
       accum, workspace, plan, as_stream(stream)));
 }
 
-int fp8rl_gemm_w8a8_rowscaled(const uint8_t* aq, const float* sa, const uint8_t* bq,
-                              const float* sb, int64_t M, int64_t N, int64_t K, void* y,
-                              int y_dtype, int64_t ld_y, int accum, void* workspace,
-                              size_t workspace_bytes, void* stream) {
+fp8rl_status fp8rl_gemm_w8a8_rowscaled(const uint8_t* aq, const float* sa, const uint8_t* bq,
+                                       const float* sb, int64_t M, int64_t N, int64_t K, void* y,
+                                       int y_dtype, int64_t ld_y, int accum, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
   return gemm_common(aq, sa, bq, sb, M, N, K, y, y_dtype, ld_y, accum, true, workspace,
                      workspace_bytes, stream);
 }
 
-int fp8rl_grouped_gemm_w8a8(const uint8_t* xq, const float* sa, const uint8_t* wq, const float* sw,
-                            const int32_t* expert_offsets, int32_t E, int64_t M_total, int64_t N,
-                            int64_t K, void* y, int y_dtype, int accum, void* workspace,
-                            size_t workspace_bytes, void* stream) {
-  if (int s = check_dims(M_total, N, K)) return s;
+fp8rl_status fp8rl_grouped_gemm_w8a8(const uint8_t* xq, const float* sa, const uint8_t* wq,
+                                     const float* sw, const int32_t* expert_offsets, int32_t E,
+                                     int64_t M_total, int64_t N, int64_t K, void* y, int y_dtype,
+                                     int accum, void* workspace, size_t workspace_bytes,
+                                     void* stream) {
+  if (fp8rl_status s = check_dims(M_total, N, K)) return s;
   if (E < 1 || E > 1024) return FP8RL_ERR_ARG;
   if (M_total == 0) return FP8RL_OK;
   if (!expert_offsets) return FP8RL_ERR_NULL;
-  if (int s = check_gemm_common(xq, sa, wq, sw, N, K, y, y_dtype, N)) return s;
+  if (fp8rl_status s = check_gemm_common(xq, sa, wq, sw, N, K, y, y_dtype, N)) return s;
   accum = resolve_accum(accum, y_dtype, false);
   if (accum < 0) return FP8RL_ERR_ARG;
   if (!aligned(expert_offsets, 4)) return FP8RL_ERR_ALIGN;
@@ -506,15 +515,16 @@ int fp8rl_grouped_gemm_w8a8(const uint8_t* xq, const float* sa, const uint8_t* w
                                                as_stream(stream)));
 }
 
-int fp8rl_grouped_gemm_w8a8_fused_act_quant(const uint16_t* x, int64_t ld_x, int64_t src_rows,
-                                            const int32_t* row_ids, const uint8_t* wq,
-                                            const float* sw, const int32_t* expert_offsets,
-                                            int32_t E, int64_t M_total, int64_t N, int64_t K,
-                                            void* y, int y_dtype, int accum, int scale_fmt,
-                                            void* workspace, size_t workspace_bytes,
-                                            void* stream) {
-  if (int s = check_dims(M_total, N, K)) return s;
-  if (int s = check_dims(src_rows, ld_x, 0)) return s;
+fp8rl_status fp8rl_grouped_gemm_w8a8_fused_act_quant(const uint16_t* x, int64_t ld_x,
+                                                     int64_t src_rows, const int32_t* row_ids,
+                                                     const uint8_t* wq, const float* sw,
+                                                     const int32_t* expert_offsets, int32_t E,
+                                                     int64_t M_total, int64_t N, int64_t K, void* y,
+                                                     int y_dtype, int accum, int scale_fmt,
+                                                     void* workspace, size_t workspace_bytes,
+                                                     void* stream) {
+  if (fp8rl_status s = check_dims(M_total, N, K)) return s;
+  if (fp8rl_status s = check_dims(src_rows, ld_x, 0)) return s;
   if (E < 1 || E > 1024) return FP8RL_ERR_ARG;
   if (M_total == 0) return FP8RL_OK;
   if (!x || !wq || !sw || !y || !expert_offsets) return FP8RL_ERR_NULL;

@@ -36,7 +36,10 @@
  *   - Every pointer is a DEVICE pointer (memory the caller allocated on the current HIP device),
  *     except where marked "host". The library never allocates, frees or copies memory and never
  *     synchronizes: each call validates its arguments on the host, enqueues its kernel(s) on
- *     `stream` (a hipStream_t; NULL means the default stream) and returns.
+ *     `stream` (a hipStream_t, passed as void* so that this header needs no HIP include; NULL
+ *     means the default stream) and returns an fp8rl_status. Arguments that select an option
+ *     (y_dtype, accum, scale_fmt, op) take the values of fp8rl_out_dtype, fp8rl_accum,
+ *     fp8rl_scale_fmt and fp8rl_op as int; an unknown value is an error status, never a crash.
  *   - bf16 tensors are passed as uint16_t bit patterns; E4M3 codes as uint8_t (OCP E4M3: sign,
  *     4-bit exponent with bias 7, 3-bit mantissa, subnormals, no infinities, NaN = 0x7F/0xFF).
  *   - Row-major layouts; ld_* is the distance in ELEMENTS between consecutive rows.
@@ -142,7 +145,7 @@ typedef enum { FP8RL_SCALE_FP32 = 0, FP8RL_SCALE_POW2 = 1 } fp8rl_scale_fmt;
  *   v   : n float32 values (device, 16-byte aligned)
  *   out : n codes (device, 16-byte aligned)
  */
-int fp8rl_encode_e4m3_f32(const float* v, int64_t n, uint8_t* out, void* stream);
+fp8rl_status fp8rl_encode_e4m3_f32(const float* v, int64_t n, uint8_t* out, void* stream);
 
 /*
  * Weight re-quantization, 128x128 blocks [FP8RL, section 1; NEMO, Table 1; UFP8, quick-read].
@@ -156,13 +159,13 @@ int fp8rl_encode_e4m3_f32(const float* v, int64_t n, uint8_t* out, void* stream)
  *   sw  : float32 scales, dense row-major [N/128][K/128]
  * Requires N % 128 == 0 and K % 128 == 0.
  */
-int fp8rl_quant_weight_blk128(const uint16_t* w, int64_t N, int64_t K, int64_t ld_w, uint8_t* wq,
-                              int64_t ld_wq, float* sw, void* stream);
+fp8rl_status fp8rl_quant_weight_blk128(const uint16_t* w, int64_t N, int64_t K, int64_t ld_w,
+                                       uint8_t* wq, int64_t ld_wq, float* sw, void* stream);
 
 /* The same with an explicit scale format (fp8rl_scale_fmt); FP8RL_ERR_ARG for an unknown one. */
-int fp8rl_quant_weight_blk128_ex(const uint16_t* w, int64_t N, int64_t K, int64_t ld_w,
-                                 uint8_t* wq, int64_t ld_wq, float* sw, int scale_fmt,
-                                 void* stream);
+fp8rl_status fp8rl_quant_weight_blk128_ex(const uint16_t* w, int64_t N, int64_t K, int64_t ld_w,
+                                          uint8_t* wq, int64_t ld_wq, float* sw, int scale_fmt,
+                                          void* stream);
 
 /* One weight matrix of a batched re-quantization (all pointers device, same rules as above). */
 typedef struct {
@@ -180,11 +183,12 @@ typedef struct {
  * Every descriptor is validated before anything is enqueued; the first failing one decides the
  * returned status and nothing is launched. Matrices with N == 0 or K == 0 are skipped.
  */
-int fp8rl_quant_weight_blk128_batched(const fp8rl_weight_desc* descs, int32_t count, void* stream);
+fp8rl_status fp8rl_quant_weight_blk128_batched(const fp8rl_weight_desc* descs, int32_t count,
+                                               void* stream);
 
 /* The same with an explicit scale format for every matrix (fp8rl_scale_fmt). */
-int fp8rl_quant_weight_blk128_batched_ex(const fp8rl_weight_desc* descs, int32_t count,
-                                         int scale_fmt, void* stream);
+fp8rl_status fp8rl_quant_weight_blk128_batched_ex(const fp8rl_weight_desc* descs, int32_t count,
+                                                  int scale_fmt, void* stream);
 
 /*
  * Dynamic activation quantization, 1x128 groups per token row [NEMO, Table 1; FP8RL, section 1;
@@ -196,12 +200,13 @@ int fp8rl_quant_weight_blk128_batched_ex(const fp8rl_weight_desc* descs, int32_t
  *   sa  : float32 scales, dense row-major [M][K/128]
  * Requires K % 128 == 0; any M >= 0.
  */
-int fp8rl_quant_act_tok128(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x, uint8_t* xq,
-                           int64_t ld_xq, float* sa, void* stream);
+fp8rl_status fp8rl_quant_act_tok128(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x,
+                                    uint8_t* xq, int64_t ld_xq, float* sa, void* stream);
 
 /* The same with an explicit scale format (fp8rl_scale_fmt). */
-int fp8rl_quant_act_tok128_ex(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x, uint8_t* xq,
-                              int64_t ld_xq, float* sa, int scale_fmt, void* stream);
+fp8rl_status fp8rl_quant_act_tok128_ex(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x,
+                                       uint8_t* xq, int64_t ld_xq, float* sa, int scale_fmt,
+                                       void* stream);
 
 /*
  * Backward pass of the linear layer in FP8 [NEMO, Table 1: output gradients in [1,128] groups,
@@ -229,9 +234,9 @@ int fp8rl_quant_act_tok128_ex(const uint16_t* x, int64_t M, int64_t K, int64_t l
  *   wqt, swt : transposed codes [K][ld_wqt] (ld_wqt >= N) and scales [K/128][N/128]
  * Requires N % 128 == 0, K % 128 == 0; scale_fmt as for the _ex quantizers.
  */
-int fp8rl_quant_weight_blk128_t(const uint16_t* w, int64_t N, int64_t K, int64_t ld_w, uint8_t* wq,
-                                int64_t ld_wq, float* sw, uint8_t* wqt, int64_t ld_wqt, float* swt,
-                                int scale_fmt, void* stream);
+fp8rl_status fp8rl_quant_weight_blk128_t(const uint16_t* w, int64_t N, int64_t K, int64_t ld_w,
+                                         uint8_t* wq, int64_t ld_wq, float* sw, uint8_t* wqt,
+                                         int64_t ld_wqt, float* swt, int scale_fmt, void* stream);
 
 /*
  * Column-group quantization with a transposed output (Wgrad operands): for column k of X[M][K]
@@ -244,9 +249,9 @@ int fp8rl_quant_weight_blk128_t(const uint16_t* w, int64_t N, int64_t K, int64_t
  *   xq, sa   : [M][ld_xq] codes and [M][K/128] scales, or both NULL
  * Requires M % 128 == 0 and K % 128 == 0; scale_fmt as for the _ex quantizers.
  */
-int fp8rl_quant_act_colwise128(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x, uint8_t* xq,
-                               int64_t ld_xq, float* sa, uint8_t* xtq, int64_t ld_xtq, float* sat,
-                               int scale_fmt, void* stream);
+fp8rl_status fp8rl_quant_act_colwise128(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x,
+                                        uint8_t* xq, int64_t ld_xq, float* sa, uint8_t* xtq,
+                                        int64_t ld_xtq, float* sat, int scale_fmt, void* stream);
 
 /*
  * Blockwise-scaled W8A8 GEMM, Y = X W^T [NEMO, "FP8 for linear layers in RL"; FP8RL, section 1]:
@@ -271,10 +276,10 @@ int fp8rl_quant_act_colwise128(const uint16_t* x, int64_t M, int64_t K, int64_t 
  *            of the workspace is overwritten; the result does not depend on its contents.
  * Requires N % 128 == 0, K % 128 == 0. The result is deterministic (same bits every run).
  */
-int fp8rl_gemm_w8a8_blockscaled(const uint8_t* xq, const float* sa, const uint8_t* wq,
-                                const float* sw, int64_t M, int64_t N, int64_t K, void* y,
-                                int y_dtype, int64_t ld_y, int accum, void* workspace,
-                                size_t workspace_bytes, void* stream);
+fp8rl_status fp8rl_gemm_w8a8_blockscaled(const uint8_t* xq, const float* sa, const uint8_t* wq,
+                                         const float* sw, int64_t M, int64_t N, int64_t K, void* y,
+                                         int y_dtype, int64_t ld_y, int accum, void* workspace,
+                                         size_t workspace_bytes, void* stream);
 
 /*
  * fp8rl_gemm_w8a8_blockscaled for callers that cannot allocate device memory (code under HIP
@@ -290,9 +295,10 @@ int fp8rl_gemm_w8a8_blockscaled(const uint8_t* xq, const float* sa, const uint8_
  * enqueueing concurrently) race and give undefined results; order them on one stream.
  */
 #define FP8RL_SCRATCH_BYTES (32u << 20)
-int fp8rl_gemm_w8a8_blockscaled_noalloc(const uint8_t* xq, const float* sa, const uint8_t* wq,
-                                        const float* sw, int64_t M, int64_t N, int64_t K, void* y,
-                                        int y_dtype, int64_t ld_y, int accum, void* stream);
+fp8rl_status fp8rl_gemm_w8a8_blockscaled_noalloc(const uint8_t* xq, const float* sa,
+                                                 const uint8_t* wq, const float* sw, int64_t M,
+                                                 int64_t N, int64_t K, void* y, int y_dtype,
+                                                 int64_t ld_y, int accum, void* stream);
 
 /*
  * The blockwise-scaled GEMM on bf16 activations: quantize X in 1x128 groups and multiply, in one
@@ -316,10 +322,11 @@ int fp8rl_gemm_w8a8_blockscaled_noalloc(const uint8_t* xq, const float* sa, cons
  * Requires N % 128 == 0 and K % 128 == 0 (FP8RL_ERR_SHAPE otherwise; M == 0 returns FP8RL_OK).
  * Deterministic.
  */
-int fp8rl_gemm_w8a8_fused_act_quant(const uint16_t* x, int64_t ld_x, const uint8_t* wq,
-                                    const float* sw, int64_t M, int64_t N, int64_t K, void* y,
-                                    int y_dtype, int64_t ld_y, int accum, int scale_fmt,
-                                    void* workspace, size_t workspace_bytes, void* stream);
+fp8rl_status fp8rl_gemm_w8a8_fused_act_quant(const uint16_t* x, int64_t ld_x, const uint8_t* wq,
+                                             const float* sw, int64_t M, int64_t N, int64_t K,
+                                             void* y, int y_dtype, int64_t ld_y, int accum,
+                                             int scale_fmt, void* workspace, size_t workspace_bytes,
+                                             void* stream);
 
 /*
  * Row-scaled FP8 GEMM (the weight-gradient product of the backward pass: both operands quantized
@@ -334,10 +341,10 @@ int fp8rl_gemm_w8a8_fused_act_quant(const uint16_t* x, int64_t ld_x, const uint8
  * The workspace is sized by
  * fp8rl_workspace_bytes(FP8RL_OP_GEMM_ROWSCALED, M, N, K, 0).
  */
-int fp8rl_gemm_w8a8_rowscaled(const uint8_t* aq, const float* sa, const uint8_t* bq,
-                              const float* sb, int64_t M, int64_t N, int64_t K, void* y,
-                              int y_dtype, int64_t ld_y, int accum, void* workspace,
-                              size_t workspace_bytes, void* stream);
+fp8rl_status fp8rl_gemm_w8a8_rowscaled(const uint8_t* aq, const float* sa, const uint8_t* bq,
+                                       const float* sb, int64_t M, int64_t N, int64_t K, void* y,
+                                       int y_dtype, int64_t ld_y, int accum, void* workspace,
+                                       size_t workspace_bytes, void* stream);
 
 /*
  * Grouped (mixture-of-experts) blockwise-scaled W8A8 GEMM [FP8RL, section 1: MoE expert linears
@@ -355,10 +362,11 @@ int fp8rl_gemm_w8a8_rowscaled(const uint8_t* aq, const float* sa, const uint8_t*
  *   workspace        : as for the dense GEMM, sized by fp8rl_workspace_bytes(FP8RL_OP_GROUPED_GEMM, ...)
  * Requires E >= 1, N % 128 == 0, K % 128 == 0.
  */
-int fp8rl_grouped_gemm_w8a8(const uint8_t* xq, const float* sa, const uint8_t* wq, const float* sw,
-                            const int32_t* expert_offsets, int32_t E, int64_t M_total, int64_t N,
-                            int64_t K, void* y, int y_dtype, int accum, void* workspace,
-                            size_t workspace_bytes, void* stream);
+fp8rl_status fp8rl_grouped_gemm_w8a8(const uint8_t* xq, const float* sa, const uint8_t* wq,
+                                     const float* sw, const int32_t* expert_offsets, int32_t E,
+                                     int64_t M_total, int64_t N, int64_t K, void* y, int y_dtype,
+                                     int accum, void* workspace, size_t workspace_bytes,
+                                     void* stream);
 
 /*
  * The grouped GEMM on bf16 activations: the activation quantization of
@@ -369,7 +377,8 @@ int fp8rl_grouped_gemm_w8a8(const uint8_t* xq, const float* sa, const uint8_t* w
  * fp8rl_grouped_gemm_w8a8) takes its activations from row row_ids[r] of x, the token the router
  * sent to that expert, so the caller passes the token activations as they are and the router's
  * token indices in expert order:
- *   Y[r][n] = sum_kb sa'[r][kb] * sw[e][n/128][kb] * sum_k dec(Q(x[row_ids[r]])[k]) * dec(Wq[e][n][k])
+ *   Y[r][n] = sum_kb sa'[r][kb] * sw[e][n/128][kb]
+ *             * sum_{k in slice kb} dec(Q(x[row_ids[r]])[k]) * dec(Wq[e][n][k])
  * with Q the 1x128 activation quantizer (scale format scale_fmt) and sa' its scales. The result
  * is bit-identical to fp8rl_quant_act_tok128_ex on the gathered rows x[row_ids[0 .. M_total-1]]
  * followed by fp8rl_grouped_gemm_w8a8 with the same accum: a 1x128 group lies within one row,
@@ -394,13 +403,14 @@ int fp8rl_grouped_gemm_w8a8(const uint8_t* xq, const float* sa, const uint8_t* w
  * Requires E >= 1, N % 128 == 0, K % 128 == 0 (FP8RL_ERR_SHAPE otherwise; M_total == 0 returns
  * FP8RL_OK). Deterministic.
  */
-int fp8rl_grouped_gemm_w8a8_fused_act_quant(const uint16_t* x, int64_t ld_x, int64_t src_rows,
-                                            const int32_t* row_ids, const uint8_t* wq,
-                                            const float* sw, const int32_t* expert_offsets,
-                                            int32_t E, int64_t M_total, int64_t N, int64_t K,
-                                            void* y, int y_dtype, int accum, int scale_fmt,
-                                            void* workspace, size_t workspace_bytes,
-                                            void* stream);
+fp8rl_status fp8rl_grouped_gemm_w8a8_fused_act_quant(const uint16_t* x, int64_t ld_x,
+                                                     int64_t src_rows, const int32_t* row_ids,
+                                                     const uint8_t* wq, const float* sw,
+                                                     const int32_t* expert_offsets, int32_t E,
+                                                     int64_t M_total, int64_t N, int64_t K, void* y,
+                                                     int y_dtype, int accum, int scale_fmt,
+                                                     void* workspace, size_t workspace_bytes,
+                                                     void* stream);
 
 /*
  * Per-tensor FP8 for attention Q/K/V activations and the stored KV cache [NEMO, section on FP8
@@ -422,8 +432,8 @@ int fp8rl_grouped_gemm_w8a8_fused_act_quant(const uint16_t* x, int64_t ld_x, int
  *   x    : bf16 tensor, rows of pitch ld_x elements (e.g. the K columns of a fused QKV output)
  *   amax : one float32 (4-byte aligned)
  */
-int fp8rl_amax_bf16(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, float* amax,
-                    void* stream);
+fp8rl_status fp8rl_amax_bf16(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                             float* amax, void* stream);
 
 /* One tensor of a batched amax (device pointers, rules as for fp8rl_amax_bf16). */
 typedef struct {
@@ -437,14 +447,14 @@ typedef struct {
  * ceil(count / 32) launches. descs is a HOST array read during the call; every descriptor is
  * validated first and nothing is enqueued if one fails. Tensors with no elements are skipped.
  */
-int fp8rl_amax_bf16_batched(const fp8rl_tensor_desc* descs, int32_t count, void* stream);
+fp8rl_status fp8rl_amax_bf16_batched(const fp8rl_tensor_desc* descs, int32_t count, void* stream);
 
 /*
  * Per-tensor scales from amax values: scale[i] = fp32(amax[i] / 448) by IEEE float32 division,
  * or 1.0f when amax[i] == 0 (the block quantizers' rule applied to a whole tensor).
  *   amax, scale : n float32 each (4-byte aligned; amax[i] non-negative and finite)
  */
-int fp8rl_scale_from_amax(const float* amax, int32_t n, float* scale, void* stream);
+fp8rl_status fp8rl_scale_from_amax(const float* amax, int32_t n, float* scale, void* stream);
 
 /*
  * Per-tensor quantization of new rows, e.g. the K or V of new tokens into an FP8 KV cache:
@@ -458,9 +468,10 @@ int fp8rl_scale_from_amax(const float* amax, int32_t n, float* scale, void* stre
  *   out          : uint8 [out_rows][ld_out] (ld_out >= cols, ld_out % 8 == 0, 8-byte aligned)
  *   slot_mapping : `rows` int64 on the device (8-byte aligned), or NULL
  */
-int fp8rl_quant_bf16_per_tensor(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
-                                const float* scale, uint8_t* out, int64_t out_rows,
-                                int64_t ld_out, const int64_t* slot_mapping, void* stream);
+fp8rl_status fp8rl_quant_bf16_per_tensor(const uint16_t* x, int64_t rows, int64_t cols,
+                                         int64_t ld_x, const float* scale, uint8_t* out,
+                                         int64_t out_rows, int64_t ld_out,
+                                         const int64_t* slot_mapping, void* stream);
 
 /* One tensor of a batched per-tensor quantization (device pointers, rules as above). */
 typedef struct {
@@ -477,8 +488,8 @@ typedef struct {
  * array read during the call; all descriptors are validated before anything is enqueued.
  * Outputs of different descriptors must not overlap.
  */
-int fp8rl_quant_bf16_per_tensor_batched(const fp8rl_quant_desc* descs, int32_t count,
-                                        void* stream);
+fp8rl_status fp8rl_quant_bf16_per_tensor_batched(const fp8rl_quant_desc* descs, int32_t count,
+                                                 void* stream);
 
 /* Bytes at the start of every GEMM workspace that hold the K-split arrival counters (see
  * fp8rl_gemm_w8a8_blockscaled). */
