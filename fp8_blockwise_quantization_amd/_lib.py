@@ -242,6 +242,12 @@ def _dense(t: torch.Tensor, name: str, dtype: torch.dtype):
         raise ValueError(f"{name} must be a contiguous cuda {dtype} tensor")
 
 
+def _blocks(n: int) -> int:
+    """128-wide blocks covering n (a dimension that is not a multiple of 128 is left to the C
+    call, which rejects it with its own status)."""
+    return -(-n // 128)
+
+
 def _sizes(**want):
     """Raise unless each tensor has the stated element count (int) or shape (tuple): the C calls
     take only pointers and pitches, so a smaller tensor would be read or written past its end."""
@@ -414,7 +420,7 @@ def fp8rl_gemm_w8a8_blockscaled(xq, sa, wq, sw, out_dtype=torch.bfloat16, y=None
     if y is None:
         y = torch.empty((M, N), dtype=out_dtype, device=xq.device)
     ld_y = _rows(y, "y", y.dtype)
-    _sizes(sa=(sa, M * (K // 128)), sw=(sw, (N // 128) * (K // 128)), y=(y, (M, N)))
+    _sizes(sa=(sa, M * _blocks(K)), sw=(sw, _blocks(N) * _blocks(K)), y=(y, (M, N)))
     need = fp8rl_workspace_bytes(FP8RL_OP_GEMM, M, N, K)
     if workspace is None and need > 0:
         workspace = new_workspace(need, xq.device)
@@ -444,7 +450,7 @@ def fp8rl_gemm_w8a8_blockscaled_noalloc(xq, sa, wq, sw, y, stream=None, accum=No
     if wq.shape[1] != K:
         raise ValueError("K mismatch between xq and wq")
     ld_y = _rows(y, "y", y.dtype)
-    _sizes(sa=(sa, M * (K // 128)), sw=(sw, (N // 128) * (K // 128)), y=(y, (M, N)))
+    _sizes(sa=(sa, M * _blocks(K)), sw=(sw, _blocks(N) * _blocks(K)), y=(y, (M, N)))
     _check(lib().fp8rl_gemm_w8a8_blockscaled_noalloc(_ptr(xq), _ptr(sa), _ptr(wq), _ptr(sw), M, N,
                                                      K, _ptr(y), _out_code(y.dtype), ld_y,
                                                      _accum_code(accum, y.dtype),
@@ -496,7 +502,7 @@ def fp8rl_gemm_w8a8_fused_act_quant(x, wq, sw, out_dtype=torch.bfloat16, y=None,
     if y is None:
         y = torch.empty((M, N), dtype=out_dtype, device=x.device)
     ld_y = _rows(y, "y", y.dtype)
-    _sizes(sw=(sw, (N // 128) * (K // 128)), y=(y, (M, N)))
+    _sizes(sw=(sw, _blocks(N) * _blocks(K)), y=(y, (M, N)))
     need = fp8rl_workspace_bytes(FP8RL_OP_GEMM_FUSED_ACT, M, N, K)
     if workspace is None and need > 0:
         workspace = new_workspace(need, x.device)
@@ -525,7 +531,7 @@ def fp8rl_grouped_gemm_w8a8(xq, sa, wq, sw, expert_offsets, out_dtype=torch.bflo
     if y is None:
         y = torch.empty((M, N), dtype=out_dtype, device=xq.device)
     _dense(y, "y", y.dtype)
-    _sizes(sa=(sa, M * (K // 128)), sw=(sw, E * (N // 128) * (K // 128)), y=(y, (M, N)))
+    _sizes(sa=(sa, M * _blocks(K)), sw=(sw, E * _blocks(N) * _blocks(K)), y=(y, (M, N)))
     need = fp8rl_workspace_bytes(FP8RL_OP_GROUPED_GEMM, M, N, K, E)
     if workspace is None and need > 0:
         workspace = new_workspace(need, xq.device)
@@ -562,7 +568,7 @@ def fp8rl_grouped_gemm_w8a8_fused_act_quant(x, wq, sw, expert_offsets, row_ids=N
     if y is None:
         y = torch.empty((M, N), dtype=out_dtype, device=x.device)
     _dense(y, "y", y.dtype)
-    _sizes(sw=(sw, E * (N // 128) * (K // 128)), y=(y, (M, N)))
+    _sizes(sw=(sw, E * _blocks(N) * _blocks(K)), y=(y, (M, N)))
     need = fp8rl_workspace_bytes(FP8RL_OP_GROUPED_GEMM_FUSED_ACT, max(src_rows, M), N, K, E)
     if workspace is None and need > 0:
         workspace = new_workspace(need, x.device)
