@@ -59,3 +59,47 @@ def test_graph_replays_match_eager_and_oracle():
         ref = og.bf16_bits_to_f64(og.round_f64_to_bf16_bits(ref64))
         got = ys[i].float().cpu().numpy().astype(np.float64)
         assert_gemm_close(got, ref, ref64, "bf16", f"graph linear {i}")
+
+
+def test_graph_replays_grouped_and_fused_calls():
+    """The persistent grouped GEMM, its gathered bf16 form and the one-kernel GEMM on bf16
+    activations (M <= 4), captured together (as the benchmark captures them): every replay equals
+    the eager result."""
+    counts, ids = synth.moe_routing(256, 8, 2, seed=620)
+    off = synth.offsets_from_counts(counts).cuda()
+    ids = ids.cuda()
+    M = int(counts.sum())
+    xt = synth.act_bf16(256, 1024, seed=621).cuda()
+    x_rows = xt[ids.long()].contiguous()
+    wq, sw = fq.quant_weight(synth.weight_bf16(8 * 512, 1024, seed=622).cuda())
+    wq, sw = wq.view(8, 512, 1024), sw.view(8, 4, 8)
+    xq, sa = fq.quant_act(x_rows)
+    x_small = synth.act_bf16(3, 4096, seed=623).cuda()
+    wd, swd = fq.quant_weight(synth.weight_bf16(4096, 4096, seed=624).cuda())
+    y_g = torch.empty((M, 512), dtype=torch.bfloat16, device="cuda")
+    y_f = torch.empty((M, 512), dtype=torch.bfloat16, device="cuda")
+    y_s = torch.empty((3, 4096), dtype=torch.bfloat16, device="cuda")
+    ws = fq.new_workspace(fq.fp8rl_workspace_bytes(fq.FP8RL_OP_GROUPED_GEMM_FUSED_ACT, M, 512,
+                                                   1024, 8), "cuda")
+
+    def step():
+        fq.grouped_gemm(xq, sa, wq, sw, off, y=y_g)
+        fq.grouped_gemm_fused_act(xt, wq, sw, off, row_ids=ids, y=y_f, workspace=ws)
+        fq.gemm_fused_act(x_small, wd, swd, y=y_s)
+
+    step()
+    torch.cuda.synchronize()
+    eager = [y.clone() for y in (y_g, y_f, y_s)]
+    assert torch.equal(eager[0], eager[1])  # the gathered form gives the same bits
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for y in (y_g, y_f, y_s):
+            y.fill_(-1.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, y in enumerate((y_g, y_f, y_s)):
+            assert torch.equal(y, eager[i]), (rep, i)
