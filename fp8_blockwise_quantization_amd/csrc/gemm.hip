@@ -824,9 +824,10 @@ __global__ __launch_bounds__(T::NT) void grouped_big_kernel(GemmArgs p) {
   auto sa_of = [&](const Coords& c) { return gather ? p.sa : p.sa + (int64_t)c.row0 * p.KB; };
   auto b_of = [&](const Coords& c) { return wq0 + c.e * p.wq_stride + (int64_t)c.n0 * p.K; };
   auto sw_of = [&](const Coords& c) { return p.sw + c.e * p.sw_stride; };
-  // A tile's set-up in two halves. fetch: the global loads (thread tid < NBLK KB takes weight-
-  // block scale tid: NBLK <= 2 column blocks x KB <= 256 slices <= NT values). commit: the
-  // scales into LDS (the previous tile's K loop is done with them) and the DMA plan.
+  // A tile's set-up in two halves. fetch: the global loads (thread tid < NBLK KB loads weight-
+  // block scale tid -- NBLK <= 2 column blocks x KB <= 256 slices <= NT values -- and the other
+  // threads a copy of the last one; with a row gather, every lane its rows' gather entries).
+  // commit: the scales into LDS (the previous tile's K loop is done with them) and the DMA plan.
   constexpr int NBLK = (T::BN + 127) / 128;
   static_assert(NBLK * kMaxSlices <= T::NT, "one weight-block scale per thread");
   static_assert(!T::ROWB, "grouped GEMM: block-scaled weights");

@@ -32,3 +32,20 @@ def test_moe_counts_sum_and_skew():
     off = synth.offsets_from_counts(counts)
     assert off[0].item() == 0 and off[-1].item() == 4096 * 8
     assert torch.all(off[1:] >= off[:-1])
+
+
+def test_moe_routing_token_indices():
+    """The router's token indices in expert order: the same picks as the counts, each expert's
+    segment lists the distinct tokens that chose it in increasing order, and every token appears
+    once per pick (top_k times)."""
+    import torch
+
+    T, E, k = 512, 16, 4
+    counts, ids = synth.moe_routing(T, E, k, seed=12)
+    assert torch.equal(counts, synth.moe_routing_counts(T, E, k, seed=12))
+    assert ids.dtype == torch.int32 and ids.numel() == T * k
+    off = synth.offsets_from_counts(counts)
+    for e in range(E):
+        seg = ids[int(off[e]):int(off[e + 1])]
+        assert bool((seg[1:] > seg[:-1]).all())
+    assert torch.equal(torch.bincount(ids.long(), minlength=T), torch.full((T,), k))
