@@ -898,43 +898,11 @@ __global__ __launch_bounds__(T::NT) void grouped_big_kernel(GemmArgs p) {
   }
 }
 
-// ---------------------------------------------------------------------------------------------
-// Decode-sized GEMM (M <= 64): weight streaming. Workgroup (t, s) of 4 waves computes output
-// tile t (64 columns, 16 per wave) over K slices [s L, (s + 1) L) (L divides KB). Each wave
-// keeps the weight fragments of the next D slices in flight in registers (a ring unrolled D
-// times, so every load and wait is visible to the compiler), the activation rows of the same
-// slices are staged through registers into a double-buffered LDS tile shared by the waves, and
-// each slice is multiplied as soon as it has landed. Every weight byte is read from HBM once,
-// and 4 waves x D slices x 2 KiB per CU-resident workgroup keep the weight stream saturated.
-//
-// K splits (s > 0 exist when KB / L > 1): each split stores its float32 partial with
-// agent-scope stores (written through to the level all XCDs share) into slot (t, s) of the
-// workspace and bumps the tile's arrival counter; the split that arrives last reads the
-// partials back with agent-scope loads, sums them in split order -- the same bits whatever the
-// arrival order -- writes Y and re-arms the counter for the next call.
-// ---------------------------------------------------------------------------------------------
-template <int MT_, int R_>
-struct Dec {
-  static constexpr int MT = MT_;  // 16-row MFMA blocks covering M
-  static constexpr int R = R_;    // K slices per round; two rounds are in flight
-  static constexpr int WAVES = 4, NT = 256;
-  static constexpr int BN = 64;
-  static constexpr int MP = 16 * MT;
-  static constexpr int MPA = MP < 32 ? 32 : MP;  // staged rows: at least one 16-byte load per thread
-  static constexpr int A_LD = MPA * 8 / NT;       // 16-byte activation loads per thread and slice
-  static constexpr int A_BYTES = MPA * 128;
-  static constexpr int SA_OFF = A_BYTES;          // activation scales of the slice (x NT / MPA)
-  static constexpr int STAGE = A_BYTES + NT * 4;  // one slice
-  static constexpr int LDS_BYTES = 2 * R * STAGE; // two rounds
-  static constexpr int SLOT_FLOATS = BN * MP;     // one partial tile
-};
-
-// A GEMM workspace starts with a header of arrival counters, one per output tile of the decode
-// path (which therefore splits K only while it has at most kWsCounters tiles); partials follow.
+// A GEMM workspace starts with a header of arrival counters, one per output tile of the split-K
+// decode GEMM (which therefore splits K only while it has at most kWsCounters tiles); partials
+// follow.
 constexpr size_t kWsHeaderBytes = 4096;
 constexpr int64_t kWsCounters = kWsHeaderBytes / sizeof(int);
-constexpr int64_t kDecWorkgroups = 512;  // split K until about this many workgroups (2 per CU)
-constexpr int64_t kDecMinSlices = 8;     // ... keeping at least this many slices per split
 
 __device__ __forceinline__ v8i load_frag_global(const uint8_t* row_base, int kb, int kq) {
   const u32x4* p = reinterpret_cast<const u32x4*>(row_base + (int64_t)kb * 128 + kq * 32);
@@ -945,157 +913,135 @@ __device__ __forceinline__ v8i load_frag_global(const uint8_t* row_base, int kb,
   return f;
 }
 
-// One slice in registers: the activation rows' 16-byte pieces of E4M3 codes, this lane's weight
-// fragment and the weight block scale.
-template <class T>
-struct DecSlot {
-  u32x4 a[T::A_LD];
-  v8i b;
-  float sw;
+// ---------------------------------------------------------------------------------------------
+// Decode-sized GEMM (17 <= M <= 64): weight streaming on DMA-fed tiles. Workgroup (t, s) of 4
+// waves computes the BM x BN output tile t (BM = M padded to 32 or 64 rows, BN = 64 or 128
+// columns, BN / 4 per wave) over K slices [s L, s L + L). Both operands of a slice reach LDS as
+// in the large-M GEMM (global_load_lds_dwordx4, so each load instruction reads whole 128-byte
+// rows; fragment loads straight into registers, where a quarter-wave touches 16 rows, stream
+// the weights more slowly), through three stages: two slices in flight while one is multiplied.
+// Each wave's weight-block scale travels with the slice (one 4-byte DMA per wave), so the K
+// loop issues no other memory access. Every weight byte is read from HBM once.
+//
+// K splits (S > 1): each split stores its float32 partial tile with agent-scope stores into
+// slot (t, s) of the workspace and bumps the tile's arrival counter; the split that arrives
+// last reads the partials back, sums them in split order -- the same bits whatever the arrival
+// order -- writes Y and re-arms the counter for the next call.
+// ---------------------------------------------------------------------------------------------
+template <int BM_, int BN_, int WN_>
+struct Dec : Big<BM_, BN_, BM_, WN_, 3> {
+  using Base = Big<BM_, BN_, BM_, WN_, 3>;
+  static constexpr int SW_OFF = Base::STAGE_BYTES;  // one weight-block scale per wave
+  static constexpr int STAGE_BYTES = SW_OFF + 16 * ((Base::WAVES * 4 + 15) / 16);
+  static constexpr int DMA_OPS = Base::DMA_OPS + 1;  // per wave and slice
+  static constexpr int SLOT_FLOATS = BM_ * BN_;      // one partial tile
+  static constexpr int NV = Base::TM * Base::TN * 4;  // accumulator values per lane
+  static_assert(Base::WAVES_M == 1 && NV <= 32, "waves side by side along N");
 };
-
-template <class T>
-__device__ __forceinline__ void dec_fetch(DecSlot<T>& d, const GemmArgs& p, const uint8_t* wrow,
-                                          const float* swrow, int kb, int tid) {
-  // activation rows are read by every tile: ordinary (cached) loads; rows past M repeat row
-  // M - 1, as their products reach no stored output
-  const uint8_t* xs = p.xq + (int64_t)kb * 128;
-#pragma unroll
-  for (int j = 0; j < T::A_LD; ++j) {
-    const int e = j * T::NT + tid;  // 16-byte chunk e: row e / 8, chunk e % 8
-    d.a[j] = *reinterpret_cast<const u32x4*>(xs + (int64_t)min(e >> 3, p.M - 1) * p.K + (e & 7) * 16);
-  }
-  d.b = load_frag_global(wrow, kb, (tid & 63) >> 4);
-  d.sw = swrow[kb];
-}
-
-// Activation scales of a round (R slices from kb): thread tid loads the one of row tid % MPA and
-// slice kb + tid / MPA (every value once per workgroup, instead of once per wave and slice).
-template <class T>
-__device__ __forceinline__ float dec_fetch_sa(const GemmArgs& p, int kb, int tid) {
-  static_assert(T::MPA * T::R <= T::NT, "one activation scale per thread and round");
-  const int u = tid / T::MPA;
-  return u < T::R ? p.sa[(int64_t)min(tid % T::MPA, p.M - 1) * p.KB + kb + u] : 0.f;
-}
-
-template <class T>
-__device__ __forceinline__ void dec_stage(uint8_t* st, const DecSlot<T>& d, int tid) {
-#pragma unroll
-  for (int j = 0; j < T::A_LD; ++j) {
-    const int e = j * T::NT + tid;
-    const int row = e >> 3;
-    *reinterpret_cast<u32x4*>(st + row * 128 + (((e & 7) ^ swz(row)) << 4)) = d.a[j];
-  }
-}
-
-template <class T, int ACC>
-__device__ __forceinline__ void dec_mma(const uint8_t* st, const DecSlot<T>& d, int lane,
-                                        v4f (&acc)[T::MT]) {
-  const int r16 = lane & 15, kq = lane >> 4;
-  if constexpr (ACC == 2) {  // power-of-two scales applied by the matrix cores (see mma_slice_big)
-    const float* sa = reinterpret_cast<const float*>(st + T::SA_OFF);
-    const int swe = e8m0_of(d.sw);
-#pragma unroll
-    for (int i = 0; i < T::MT; ++i) {
-      acc[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-          load_frag(st, i * 16 + r16, kq), d.b, acc[i], 0, 0, 0, e8m0_of(sa[i * 16 + r16]), 0, swe);
-      asm volatile("" : "+v"(acc[i]));  // keep each slice's update in place
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    return;
-  }
-  constexpr bool PRECISE = ACC == 1;
-  v4f cur[T::MT];
-#pragma unroll
-  for (int i = 0; i < T::MT; ++i) cur[i] = slice_product<PRECISE>(load_frag(st, i * 16 + r16, kq), d.b);
-  __builtin_amdgcn_sched_barrier(0);  // all MT products in flight before the first is consumed
-  const float* sa = reinterpret_cast<const float*>(st + T::SA_OFF);
-#pragma unroll
-  for (int i = 0; i < T::MT; ++i) {
-    acc[i] += cur[i] * (*reinterpret_cast<const v4f*>(sa + i * 16 + 4 * kq) * d.sw);
-    asm volatile("" : "+v"(acc[i]));  // keep each slice's update in place
-  }
-}
 
 template <class T, int ACC>
 __global__ __launch_bounds__(T::NT) void gemm_decode_kernel(GemmArgs p) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[T::LDS_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t stages[T::STAGES * T::STAGE_BYTES];
   __shared__ int s_flag;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int t = blockIdx.x, split = blockIdx.y, L = p.kb_per_split;
-  const int kb0 = split * L;
-  const int ncol = t * T::BN + wave * 16;  // this wave's 16 weight rows
-  const uint8_t* wrow = p.wq + (int64_t)(ncol + (lane & 15)) * p.K;
-  const float* swrow = p.sw + (int64_t)(ncol >> 7) * p.KB;
+  const int t = blockIdx.x, split = blockIdx.y;
+  const int kb0 = split * p.kb_per_split;
+  const int nk = min(p.kb_per_split, p.KB - kb0);  // >= 1: the plan leaves no empty range
+  const int n0 = t * T::BN;
+  const DmaPlan<T> dp = make_dma_plan<T>(p.M, T::BN, p.K, p.KB, wave, lane);
+  const uint8_t* B = p.wq + (int64_t)n0 * p.K;
+  // byte offset of this wave's weight-block scale row in sw (its lane 0 loads the slice's scale)
+  const uint32_t sw_off = (uint32_t)((n0 + wave * T::WN) >> 7) * (uint32_t)(p.KB * 4);
+  auto dma = [&](uint8_t* stage, int kb) {
+    dma_slice<T>(stage, dp, p.xq, B, p.sa, nullptr, kb, wave, lane);
+    if (lane == 0) dma4(p.sw + kb, sw_off, stage + T::SW_OFF + wave * 4);
+  };
 
-  // L is a multiple of 2R. Round r (R slices) lives in register set r & 1 while its loads are
-  // in flight; it is staged into LDS buffer r & 1 with one barrier, multiplied, and its
-  // registers refilled with round r + 2. All loads and waits are visible to the compiler: the
-  // rounds are unrolled, so no branch separates a load from its use.
-  DecSlot<T> ring0[T::R], ring1[T::R];
-  float sa0 = dec_fetch_sa<T>(p, kb0, tid);
-  float sa1 = dec_fetch_sa<T>(p, kb0 + T::R, tid);
+  v4f acc[T::TM][T::TN];
 #pragma unroll
-  for (int u = 0; u < T::R; ++u) dec_fetch<T>(ring0[u], p, wrow, swrow, kb0 + u, tid);
+  for (int i = 0; i < T::TM; ++i)
 #pragma unroll
-  for (int u = 0; u < T::R; ++u) dec_fetch<T>(ring1[u], p, wrow, swrow, kb0 + T::R + u, tid);
-  v4f acc[T::MT];
+    for (int j = 0; j < T::TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+  constexpr int P = T::STAGES - 1;  // slices issued ahead of the one multiplied
 #pragma unroll
-  for (int i = 0; i < T::MT; ++i) acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
-  uint8_t* const buf0 = lds;
-  uint8_t* const buf1 = lds + T::R * T::STAGE;
-  auto round = [&](DecSlot<T>(&ring)[T::R], float& sa, uint8_t* buf, int refill_kb) {
+  for (int u = 0; u < P; ++u)
+    if (u < nk) dma(stages + u * T::STAGE_BYTES, kb0 + u);
+  int cur = 0;
+  for (int i = 0; i < nk; ++i) {
+    wait_slice_and_barrier<T>(nk - 1 - i);  // slice i + 1 may stay in flight
+    const int nxt = cur == 0 ? P : cur - 1;  // (i + P) % STAGES: freed by slice i - 1
+    if (i + P < nk) dma(stages + nxt * T::STAGE_BYTES, kb0 + i + P);
+    const uint8_t* st = stages + cur * T::STAGE_BYTES;
+    const float swv = reinterpret_cast<const float*>(st + T::SW_OFF)[wave];
+    mma_slice_big<T, ACC>(st, swv, 0, wave, lane, acc);
+    cur = cur == P ? 0 : cur + 1;
+  }
+
+  const int r16 = lane & 15, kq = lane >> 4;
+  float vals[T::NV];
 #pragma unroll
-    for (int u = 0; u < T::R; ++u) dec_stage<T>(buf + u * T::STAGE, ring[u], tid);
-    if (tid / T::MPA < T::R)
-      reinterpret_cast<float*>(buf + (tid / T::MPA) * T::STAGE + T::SA_OFF)[tid % T::MPA] = sa;
+  for (int i = 0; i < T::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < T::TN; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) vals[(i * T::TN + j) * 4 + v] = acc[i][j][v];
+  // The output tile goes through LDS (the stages are free once every wave is past its last
+  // slice) and leaves as 16-byte pieces of rows.
+  static_assert(T::BM * (T::BN + 4) * 4 <= T::STAGES * T::STAGE_BYTES, "output tile fits");
+  auto store_y = [&]() {
     __syncthreads();
+    if (p.out_f32) {
+      constexpr int PITCH = T::BN + 4;  // floats; rows stay 16-byte aligned
+      float* t32 = reinterpret_cast<float*>(stages);
 #pragma unroll
-    for (int u = 0; u < T::R; ++u) dec_mma<T, ACC>(buf + u * T::STAGE, ring[u], lane, acc);
-    // refill only once consumed, so each set keeps its registers across the loop
-    if (refill_kb >= 0) {
-      sa = dec_fetch_sa<T>(p, refill_kb, tid);
+      for (int i = 0; i < T::TM; ++i)
 #pragma unroll
-      for (int u = 0; u < T::R; ++u) dec_fetch<T>(ring[u], p, wrow, swrow, refill_kb + u, tid);
+        for (int j = 0; j < T::TN; ++j)
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            t32[(i * 16 + 4 * kq + v) * PITCH + wave * T::WN + j * 16 + r16] =
+                vals[(i * T::TN + j) * 4 + v];
+      __syncthreads();
+      constexpr int CH = T::BN / 4;
+      for (int q = tid; q < T::BM * CH; q += T::NT) {
+        const int r = q / CH, c = (q - r * CH) * 4;
+        if (r >= p.M) break;  // q grows with r
+        *reinterpret_cast<u32x4*>(reinterpret_cast<float*>(p.y) + r * p.ldy + n0 + c) =
+            *reinterpret_cast<const u32x4*>(t32 + r * PITCH + c);
+      }
+    } else {
+      constexpr int PITCH = T::BN + 8;  // bf16 elements; rows stay 16-byte aligned
+      uint16_t* t16 = reinterpret_cast<uint16_t*>(stages);
+#pragma unroll
+      for (int i = 0; i < T::TM; ++i)
+#pragma unroll
+        for (int j = 0; j < T::TN; ++j)
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            t16[(i * 16 + 4 * kq + v) * PITCH + wave * T::WN + j * 16 + r16] =
+                f32_to_bf16_rne(vals[(i * T::TN + j) * 4 + v]);
+      __syncthreads();
+      constexpr int CH = T::BN / 8;
+      for (int q = tid; q < T::BM * CH; q += T::NT) {
+        const int r = q / CH, c = (q - r * CH) * 8;
+        if (r >= p.M) break;
+        *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(p.y) + r * p.ldy + n0 + c) =
+            *reinterpret_cast<const u32x4*>(t16 + r * PITCH + c);
+      }
     }
   };
-  for (int k0 = 0; k0 < L - 2 * T::R; k0 += 2 * T::R) {
-    round(ring0, sa0, buf0, kb0 + k0 + 2 * T::R);
-    round(ring1, sa1, buf1, kb0 + k0 + 3 * T::R);
-  }
-  round(ring0, sa0, buf0, -1);
-  round(ring1, sa1, buf1, -1);
-
-  const int kq = lane >> 4, col = ncol + (lane & 15);
-  float vals[T::MT * 4];
-  auto store_y = [&]() {
-#pragma unroll
-    for (int i = 0; i < T::MT; ++i)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int row = i * 16 + 4 * kq + v;
-        if (row >= p.M) continue;
-        if (p.out_f32)
-          reinterpret_cast<float*>(p.y)[row * p.ldy + col] = vals[i * 4 + v];
-        else
-          reinterpret_cast<uint16_t*>(p.y)[row * p.ldy + col] = f32_to_bf16_rne(vals[i * 4 + v]);
-      }
-  };
-#pragma unroll
-  for (int i = 0; i < T::MT; ++i)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) vals[i * 4 + v] = acc[i][v];
   const int S = gridDim.y;
   if (S == 1) {
     store_y();
     return;
   }
-  float* base = p.ws + (size_t)wave * T::MT * 256 + lane;
+  // partial tile of (t, split): value q of lane l of wave w at float (w * NV + q) * 64 + l
+  float* base = p.ws + (size_t)wave * T::NV * 64 + lane;
   float* mine = base + ((size_t)t * S + split) * T::SLOT_FLOATS;
 #pragma unroll
-  for (int j = 0; j < T::MT * 4; ++j)
-    __hip_atomic_store(mine + j * 64, vals[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int q = 0; q < T::NV; ++q)
+    __hip_atomic_store(mine + q * 64, vals[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   // Ordering of the hand-off. Every access to the partials and the counter is an agent-scope
   // atomic: the partial stores are write-through stores (sc1) that complete only once they have
   // reached the level all XCDs share, and the read-back loads (sc1) are served from that level,
@@ -1115,22 +1061,22 @@ __global__ __launch_bounds__(T::NT) void gemm_decode_kernel(GemmArgs p) {
   }
   __syncthreads();
   if (!s_flag) return;
-  // last arrival: sum the partials in split order, 4 splits' loads in flight at a time
+  // last arrival: sum the partials in split order, the values of 4 splits in flight at a time
 #pragma unroll
-  for (int j = 0; j < T::MT * 4; ++j) vals[j] = 0.f;
+  for (int j = 0; j < T::NV; ++j) vals[j] = 0.f;
   for (int s0 = 0; s0 < S; s0 += 4) {
-    float v4[4][T::MT * 4];
+    float v4[4][T::NV];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const float* src = base + ((size_t)t * S + min(s0 + u, S - 1)) * T::SLOT_FLOATS;
 #pragma unroll
-      for (int j = 0; j < T::MT * 4; ++j)
+      for (int j = 0; j < T::NV; ++j)
         v4[u][j] = __hip_atomic_load(src + j * 64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int j = 0; j < T::MT * 4; ++j) vals[j] = s0 + u < S ? vals[j] + v4[u][j] : vals[j];
+      for (int j = 0; j < T::NV; ++j) vals[j] = s0 + u < S ? vals[j] + v4[u][j] : vals[j];
   }
   store_y();
   // re-arm for the next call (ordered before it by the kernel boundary)
@@ -1493,7 +1439,7 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool rowb) {
     pl.workspace_bytes = 0;
     return pl;
   }
-  if (M <= 64 && KB % 2 == 0 && !rowb) return plan_decode(M, N, K);  // the split-K decode GEMM
+  if (M <= 64 && !rowb) return plan_decode(M, N, K);  // the split-K decode GEMM
   // 64 x 64 tiles below 1024 rows: against 128 x 128 tiles split four ways over K they measured
   // 1.3-2x faster at 512-1000 rows (the split partials' round trip through memory outweighs the
   // larger tile's operand reuse); the 128 x 128 tiles stay for K beyond the DMA-fed tiles' reach
@@ -1525,28 +1471,34 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool rowb) {
 GemmPlan plan_decode(int64_t M, int64_t N, int64_t K) {
   GemmPlan pl{};
   const int64_t KB = K / 128;
-  // 1 <= M <= 64, KB even: 64-column tiles, D slices in flight per wave (the largest of 8, 4, 2
-  // dividing KB); split K into ranges of L slices (L a multiple of D dividing KB) while there
-  // are fewer than kDecWorkgroups workgroups and ranges keep at least kDecMinSlices slices
-  constexpr int64_t BN = 64;
-  const int64_t D = KB % 8 == 0 ? 8 : KB % 4 == 0 ? 4 : 2;  // two rounds of D / 2 slices
+  // 17 <= M <= 64 (rows padded to 32 or 64). Tiles of 64 columns, K split into S ranges, S the
+  // smallest power of two giving at least 256 workgroups (one per CU) while ranges keep at least
+  // 4 slices. Wide GEMMs already have 256 tiles: above 32 rows 128-column tiles without a split
+  // (half the activation bytes per weight byte, no partials), up to 32 rows a second split.
+  // Measured on the Qwen3-8B decode GEMMs (graph-replayed): q/k/v 6144x4096 and o 4096x4096 at
+  // S = 4, down 4096x12288 within 6 % of the best of (64 | 128 columns) x S, and gate/up
+  // 24576x4096 at M = 64 30.4 us against 32.5-33.7 us for 64-column tiles with S = 1 or 2 and
+  // 32.0 us for 256-column tiles with S = 2.
+  const int64_t bm = M <= 32 ? 32 : 64;
+  int64_t BN = 64, S = 1;
+  if (M > 32 && N / 128 >= 192) {
+    BN = 128;
+  } else {
+    const int64_t tiles = N / 64;
+    while (tiles * S < 256 && KB / (2 * S) >= 4) S *= 2;
+    if (tiles >= 256 && M <= 32 && KB >= 8) S = 2;
+    if (tiles > kWsCounters) S = 1;
+  }
   const int64_t tiles = N / BN;
-  int64_t S = 1;
-  if (tiles <= kWsCounters)
-    for (int64_t s = 2; s <= KB / D; ++s) {
-      if ((KB / D) % s || KB / s < kDecMinSlices) continue;
-      if (tiles * S >= kDecWorkgroups) break;
-      S = s;
-    }
+  const int64_t L = (KB + S - 1) / S;
+  S = (KB + L - 1) / L;  // no empty range
   pl.cfg = kCfgDecode;
-  pl.bm = (int)M;
+  pl.bm = (int)bm;
   pl.bn = (int)BN;
-  pl.depth = (int)D;
+  pl.depth = 3;  // LDS stages
   pl.splits = (int)S;
-  pl.kb_per_split = (int)(KB / S);
-  const int64_t mp = M <= 16 ? 16 : M <= 32 ? 32 : 64;  // rows the kernel pads M to
-  pl.workspace_bytes =
-      S > 1 ? kWsHeaderBytes + (size_t)(tiles * S) * BN * mp * sizeof(float) : 0;
+  pl.kb_per_split = (int)L;
+  pl.workspace_bytes = S > 1 ? kWsHeaderBytes + (size_t)(tiles * S) * BN * bm * sizeof(float) : 0;
   return pl;
 }
 
@@ -1629,18 +1581,11 @@ static hipError_t launch_decode_t(const GemmArgs& a, const GemmPlan& pl, hipStre
   return hipGetLastError();
 }
 
-template <int R, int ACC>
-static hipError_t launch_decode_d(const GemmArgs& a, const GemmPlan& pl, hipStream_t stream) {
-  if (a.M <= 16) return launch_decode_t<Dec<1, R>, ACC>(a, pl, stream);
-  if (a.M <= 32) return launch_decode_t<Dec<2, R>, ACC>(a, pl, stream);
-  return launch_decode_t<Dec<4, R>, ACC>(a, pl, stream);
-}
-
 template <int ACC>
 static hipError_t launch_decode(const GemmArgs& a, const GemmPlan& pl, hipStream_t stream) {
-  if (pl.depth == 8) return launch_decode_d<4, ACC>(a, pl, stream);
-  if (pl.depth == 4) return launch_decode_d<2, ACC>(a, pl, stream);
-  return launch_decode_d<1, ACC>(a, pl, stream);
+  if (pl.bn == 128) return launch_decode_t<Dec<64, 128, 32>, ACC>(a, pl, stream);  // M > 32
+  return pl.bm == 32 ? launch_decode_t<Dec<32, 64, 16>, ACC>(a, pl, stream)
+                     : launch_decode_t<Dec<64, 64, 16>, ACC>(a, pl, stream);
 }
 
 template <class T, bool PRECISE>

@@ -335,22 +335,26 @@ def test_workspace_query_is_pure_host(L):
     hdr = _lib.WORKSPACE_HEADER_BYTES
     assert hdr == 4096  # FP8RL_WORKSPACE_HEADER_BYTES
     # the blockscaled GEMM up to 16 rows splits K only inside each workgroup (no workspace); the
-    # decode GEMM above that (up to 64 rows, K/128 even) splits K over workgroups: 64-column
-    # tiles, K split into S ranges of whole rounds of D slices (D = 8, 4 or 2 dividing K/128)
-    # while fewer than 512 workgroups and ranges of >= 8 slices; workspace = header + [tiles][S]
-    # partial tiles of 64 columns x padded rows (16, 32 or 64) float32
+    # decode GEMM above that (up to 64 rows) splits K over workgroups: above 32 rows with at least
+    # 192 tiles of 128 columns, 128-column tiles and no split; otherwise 64-column tiles and K
+    # split S ways, S the smallest power of two giving >= 256 workgroups while ranges keep >= 4
+    # slices (S = 2 at <= 32 rows with >= 256 tiles and >= 8 slices; S = 1 past 1024 tiles);
+    # workspace = header + [tiles][S] partial tiles of 64 columns x padded rows (32 or 64) float32
     def dec(M, N, K):
-        tiles, kb = N // 64, K // 128
-        d = 8 if kb % 8 == 0 else 4 if kb % 4 == 0 else 2
-        S = 1
-        for s_ in range(2, kb // d + 1):
-            if (kb // d) % s_ or kb // s_ < 8:
-                continue
-            if tiles * S >= 512:
-                break
-            S = s_
-        mp = 16 if M <= 16 else 32 if M <= 32 else 64
-        return hdr + tiles * S * 64 * mp * 4 if S > 1 else 0
+        kb = K // 128
+        if M > 32 and N // 128 >= 192:
+            return 0
+        tiles, S = N // 64, 1
+        while tiles * S < 256 and kb // (2 * S) >= 4:
+            S *= 2
+        if tiles >= 256 and M <= 32 and kb >= 8:
+            S = 2
+        if tiles > 1024:
+            S = 1
+        per = -(-kb // S)
+        S = -(-kb // per)
+        bm = 32 if M <= 32 else 64
+        return hdr + tiles * S * 64 * bm * 4 if S > 1 else 0
     def a256(n):
         return (n + 255) // 256 * 256
 
@@ -362,7 +366,8 @@ def test_workspace_query_is_pure_host(L):
             return 0
         return (max(a256(L.fp8rl_workspace_bytes(0, M, N, K, 0)), hdr) + a256(M * K)
                 + M * (K // 128) * 4)
-    for shape in [(64, 4096, 4096), (20, 1024, 12288), (64, 12288, 4096)]:
+    for shape in [(64, 4096, 4096), (20, 1024, 12288), (64, 12288, 4096), (17, 6144, 4096),
+                  (32, 24576, 4096), (48, 4096, 384 * 3)]:
         assert L.fp8rl_workspace_bytes(0, *shape, 0) == dec(*shape) > 0, shape
     for shape in [(64, 4096, 4096), (20, 1024, 12288), (64, 12288, 4096), (1, 256, 2048),
                   (4, 4096, 4096), (5, 4096, 4096), (16, 4096, 4096), (17, 4096, 4096),
@@ -373,9 +378,11 @@ def test_workspace_query_is_pure_host(L):
                                                              + 64 * 4096 + 64 * 32 * 4)
     assert L.fp8rl_workspace_bytes(3, 8192, 4096, 4096, 0) == hdr + 8192 * 4096 + 8192 * 32 * 4
     assert L.fp8rl_workspace_bytes(3, 1, 256, 2048, 0) == 0
-    assert L.fp8rl_workspace_bytes(0, 64, 4096, 1024, 0) == 0  # 8 slices: one range
+    assert L.fp8rl_workspace_bytes(0, 64, 4096, 512, 0) == 0  # 4 slices: one range
+    assert L.fp8rl_workspace_bytes(0, 64, 4096, 1024, 0) == hdr + 64 * 2 * 64 * 64 * 4
     assert L.fp8rl_workspace_bytes(0, 32, 131072, 2048, 0) == 0  # more tiles than counters
-    assert L.fp8rl_workspace_bytes(0, 64, 4096, 384, 0) == 0  # odd K/128: 64x64 tiles, K unsplit
+    assert L.fp8rl_workspace_bytes(0, 64, 24576, 4096, 0) == 0  # 128-column tiles, K unsplit
+    assert L.fp8rl_workspace_bytes(0, 32, 24576, 4096, 0) == hdr + 384 * 2 * 64 * 32 * 4
     assert L.fp8rl_workspace_bytes(0, 0, 256, 256, 0) == 0
     assert L.fp8rl_workspace_bytes(0, 8192, 4096, 4096, 0) == 0  # large M: no split
     assert L.fp8rl_workspace_bytes(1, 32768, 1536, 2048, 128) == 0
