@@ -914,7 +914,7 @@ __device__ __forceinline__ v8i load_frag_global(const uint8_t* row_base, int kb,
 }
 
 // ---------------------------------------------------------------------------------------------
-// Decode-sized GEMM (17 <= M <= 64): weight streaming on DMA-fed tiles. Workgroup (t, s) of 4
+// Decode-sized GEMM (5 <= M <= 64): weight streaming on DMA-fed tiles. Workgroup (t, s) of 4
 // waves computes the BM x BN output tile t (BM = M padded to 32 or 64 rows, BN = 64 or 128
 // columns, BN / 4 per wave) over K slices [s L, s L + L). Both operands of a slice reach LDS as
 // in the large-M GEMM (global_load_lds_dwordx4, so each load instruction reads whole 128-byte
@@ -1085,7 +1085,7 @@ __global__ __launch_bounds__(T::NT) void gemm_decode_kernel(GemmArgs p) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// Decode-sized GEMM (M <= 16), weight streaming without any hand-off between workgroups.
+// Decode-sized GEMM (M <= 4), weight streaming without any hand-off between workgroups.
 // Workgroup t of 8 waves computes output columns [BN t, BN t + BN) (BN = 16 NB) for all M rows
 // over the whole K range, which its waves split among themselves: wave w takes the K slices
 // w, w + 8, w + 16, ... Each wave streams its slices' weight fragments (NB blocks of 16 rows x 128
@@ -1110,6 +1110,7 @@ struct Str {
 // instead, 8 per lane -- the 16 lanes of DPP row r hold row r's 1x128 group, so its amax is one
 // row reduction -- quantized when the slice is multiplied.
 constexpr int kStrFusedRows = 4;
+constexpr int kStrRows = 4;  // the planner's streaming-kernel range (the fused form's as well)
 
 template <class T, bool F>
 struct StrSlot;
@@ -1425,10 +1426,12 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool rowb) {
     pl.workspace_bytes = 0;
     return pl;
   }
-  if (M <= 16 && !rowb) {
+  if (M <= kStrRows && !rowb) {
     // weight streaming, K split over the waves of each workgroup (no workspace). Each
-    // workgroup reads all M activation rows for its 16 or 32 columns, so above 16 rows the
-    // activation traffic outgrows the weights' and the split-K kernel below is faster.
+    // workgroup reads all M activation rows for its 16 or 32 columns; on the Qwen3-8B decode
+    // GEMMs (graph-replayed) it beats the split-K decode GEMM below up to 4 rows (51.3 against
+    // 57.8 us for the four GEMMs at M = 1) and loses from 8 rows on (60.7 / 58.0 us at M = 8,
+    // 67.0 / 58.2 us at M = 16), as its activation reads grow with M.
     pl.cfg = kCfgStream;
     pl.bm = 16;
     pl.bn = N % 32 == 0 && N / 16 > 1024 ? 32 : 16;
@@ -1471,7 +1474,7 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool rowb) {
 GemmPlan plan_decode(int64_t M, int64_t N, int64_t K) {
   GemmPlan pl{};
   const int64_t KB = K / 128;
-  // 17 <= M <= 64 (rows padded to 32 or 64). Tiles of 64 columns, K split into S ranges, S the
+  // 5 <= M <= 64 (rows padded to 32 or 64). Tiles of 64 columns, K split into S ranges, S the
   // smallest power of two giving at least 256 workgroups (one per CU) while ranges keep at least
   // 4 slices. Wide GEMMs already have 256 tiles: above 32 rows 128-column tiles without a split
   // (half the activation bytes per weight byte, no partials), up to 32 rows a second split.
@@ -1506,8 +1509,10 @@ GemmPlan plan_fused_act(int64_t M, int64_t N, int64_t K) {
   GemmPlan pl = plan_gemm(M, N, K);
   // up to kStrFusedRows rows the streaming kernel quantizes the activations itself (one launch,
   // no workspace). Every workgroup quantizes all of X again, which pays only while that work is
-  // small against the weight stream: with 16 rows (and with 64 rows in the 64-column decode
-  // tiles) the fused kernel took 1.2x (1.4x) as long as two launches. Above, the codes and
+  // small against the weight stream: with 16 rows the fused streaming kernel took 1.2x as long as
+  // two launches, and with 64 rows a form of the decode GEMM that quantizes each slice's bf16
+  // rows in LDS took 2.1x (every activation group quantized once per 64-column tile and split,
+  // with float64 quotients). Above, the codes and
   // scales are staged in the workspace by the 1x128 quantizer and the GEMM of the same plan
   // reads them: [GEMM workspace | codes | scales], each part 256-byte aligned. The counter header
   // stays reserved even where this GEMM splits nothing, so that the workspace keeps it zero.

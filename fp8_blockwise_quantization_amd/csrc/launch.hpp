@@ -109,7 +109,7 @@ hipError_t launch_gemm(const uint8_t* xq, const float* sa, const uint8_t* wq, co
 // its counter header on the first use there (a fill kernel enqueued on `stream`).
 constexpr size_t kScratchBytes = size_t{32} << 20;
 hipError_t gemm_scratch(hipStream_t stream, void** ptr);
-// The split-K decode GEMM's plan (17 <= M <= 64).
+// The split-K decode GEMM's plan (5 <= M <= 64).
 GemmPlan plan_decode(int64_t M, int64_t N, int64_t K);
 // The GEMM with the 1x128 activation quantization fused in: bf16 X [M][ld_x] in place of xq / sa
 // (pow2: scale format of the groups). Up to 4 rows one kernel quantizes in registers; above,

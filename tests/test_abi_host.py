@@ -228,7 +228,7 @@ def test_gemm_validation(L):
     assert call(acc=-1) == EARG
     assert call(xq=A + 1) == EALIGN
     assert call(ldy=260) == EALIGN  # 520-byte bf16 pitch
-    assert L.fp8rl_workspace_bytes(0, 16, 256, 4096, 0) == 0  # up to 16 rows: none
+    assert L.fp8rl_workspace_bytes(0, 4, 256, 4096, 0) == 0  # up to 4 rows: none
     need = L.fp8rl_workspace_bytes(0, 200, 256, 4096, 0)
     assert need > 0  # a mid-M problem uses split-K partials
     assert call(M=200, K=4096, wsb=need - 1) == EWS
@@ -257,7 +257,7 @@ def test_fused_act_gemm_validation(L):
     assert call(x=A + 2) == EALIGN
     assert call(ldx=4100) == EALIGN  # 8200-byte bf16 pitch
     need = L.fp8rl_workspace_bytes(3, 64, 256, 4096, 0)
-    assert need > 0  # above 16 rows the codes and scales are staged in the workspace
+    assert need > 0  # above 4 rows the codes and scales are staged in the workspace
     assert call(wsb=need - 1) == EWS
     assert call(ws=None) == EWS
     assert call(M=65, wsb=L.fp8rl_workspace_bytes(3, 65, 256, 4096, 0) - 1) == EWS
@@ -334,7 +334,7 @@ def test_grouped_fused_act_validation(L):
 def test_workspace_query_is_pure_host(L):
     hdr = _lib.WORKSPACE_HEADER_BYTES
     assert hdr == 4096  # FP8RL_WORKSPACE_HEADER_BYTES
-    # the blockscaled GEMM up to 16 rows splits K only inside each workgroup (no workspace); the
+    # the blockscaled GEMM up to 4 rows splits K only inside each workgroup (no workspace); the
     # decode GEMM above that (up to 64 rows) splits K over workgroups: above 32 rows with at least
     # 192 tiles of 128 columns, 128-column tiles and no split; otherwise 64-column tiles and K
     # split S ways, S the smallest power of two giving >= 256 workgroups while ranges keep >= 4
@@ -367,7 +367,7 @@ def test_workspace_query_is_pure_host(L):
         return (max(a256(L.fp8rl_workspace_bytes(0, M, N, K, 0)), hdr) + a256(M * K)
                 + M * (K // 128) * 4)
     for shape in [(64, 4096, 4096), (20, 1024, 12288), (64, 12288, 4096), (17, 6144, 4096),
-                  (32, 24576, 4096), (48, 4096, 384 * 3)]:
+                  (32, 24576, 4096), (48, 4096, 384 * 3), (5, 4096, 4096), (16, 2048, 4096)]:
         assert L.fp8rl_workspace_bytes(0, *shape, 0) == dec(*shape) > 0, shape
     for shape in [(64, 4096, 4096), (20, 1024, 12288), (64, 12288, 4096), (1, 256, 2048),
                   (4, 4096, 4096), (5, 4096, 4096), (16, 4096, 4096), (17, 4096, 4096),
