@@ -77,6 +77,17 @@ def test_small_m_shapes(M, N, K):
     run_and_check(*quantized_operands(M, N, K, 1000 + M + N + K), f"small-M {M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("M,N,K", [(33, 24576, 512), (63, 32768, 384), (48, 24576, 1152),
+                                   (5, 384, 1152), (12, 4096, 640), (16, 1024, 12288),
+                                   (31, 128, 128)])
+def test_decode_tile_forms(M, N, K):
+    """The split-K decode GEMM's forms: 128-column tiles without a K split (above 32 rows with at
+    least 192 such tiles) at ragged M and odd K/128; 64-column tiles on rows padded to 32 with K
+    ranges of unequal length (K/128 = 9 and 5 split in two) and many splits (K/128 = 96); a single
+    tile and slice. Both outputs (float32 through the f16 slice sums)."""
+    run_and_check(*quantized_operands(M, N, K, 2500 + M + N + K), f"decode tiles {M}x{N}x{K}")
+
+
 @pytest.mark.parametrize("M,N,K", [(512, 512, 512), (1000, 1024, 2048), (2048 + 37, 768, 1536),
                                    (4096, 4096, 4096), (8192 + 77, 1920, 1024), (1024, 384, 256)])
 def test_large_m_shapes(M, N, K):
@@ -221,7 +232,7 @@ def test_zero_rows_noop():
     assert y.shape == (0, 256)
 
 
-@pytest.mark.parametrize("M", [16, 64, 256, 1024])
+@pytest.mark.parametrize("M", [4, 16, 64, 256, 1024])
 def test_fp8_slice_truncation_model(M):
     """The behaviour behind fp8_slice_bound, pinned on every dense kernel path (streaming, split-K
     decode, 64x64 tiles, DMA-fed 256-row tiles): in one 32-wide K block of a slice, products
