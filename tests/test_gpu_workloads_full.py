@@ -133,7 +133,7 @@ def test_qwen3_8b_decode_gemms_whole(idx):
     _check_gemm(64, N, K, 5100 + idx, what=f"qwen3-8b decode {name}")
 
 
-@pytest.mark.parametrize("idx", (2, 3))  # q_proj at M = 8192 is checked whole in test_gpu_gemm
+@pytest.mark.parametrize("idx", (0, 2, 3))  # q_proj at M = 8192 is checked whole in test_gpu_gemm
 def test_qwen3_8b_prefill_gemms_sampled_rows(idx):
     name, N, K = QWEN3_GEMMS[idx]
     _check_gemm(8192, N, K, 5200 + idx, rows=_sample_rows(8192, 48, 5250 + idx),
