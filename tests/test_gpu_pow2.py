@@ -102,7 +102,8 @@ def run_mx(xq, sa, wq, sw, what):
 
 
 @pytest.mark.parametrize("M,N,K", [(4, 256, 256), (64, 4096, 4096), (64, 1024, 12288), (17, 512, 2048),
-                                   (1, 256, 1024), (48, 2048, 1280), (200, 512, 1024),
+                                   (1, 256, 1024), (48, 2048, 1280), (40, 24576, 640),
+                                   (9, 1536, 1152), (200, 512, 1024),
                                    (1024, 1024, 2048), (2048 + 37, 768, 1536), (8192, 4096, 4096)])
 def test_mx_gemm_all_paths(M, N, K):
     run_mx(*pow2_operands(M, N, K, 7000 + M + N + K), f"{M}x{N}x{K}")
