@@ -914,10 +914,11 @@ __device__ __forceinline__ v8i load_frag_global(const uint8_t* row_base, int kb,
 }
 
 // ---------------------------------------------------------------------------------------------
-// Decode-sized GEMM (5 <= M <= 64): weight streaming on DMA-fed tiles. Workgroup (t, s) of 4
-// waves computes the BM x BN output tile t (BM = M padded to 32 or 64 rows, BN = 64 or 128
-// columns, BN / 4 per wave) over K slices [s L, s L + L). Both operands of a slice reach LDS as
-// in the large-M GEMM (global_load_lds_dwordx4, so each load instruction reads whole 128-byte
+// Decode-sized GEMM (5 <= M <= 64): weight streaming on DMA-fed tiles. Workgroup (t, s) computes
+// the BM x BN output tile t (BM = M padded to 32 or 64 rows, BN = 64 or 128 columns) over K
+// slices [s L, s L + L) with KH halves of 4 waves (BN / 4 columns per wave): each half streams
+// its own part of the range through its own stages, and the halves' partial tiles are summed
+// through LDS in half order. Both operands of a slice reach LDS as in the large-M GEMM (global_load_lds_dwordx4, so each load instruction reads whole 128-byte
 // rows; fragment loads straight into registers, where a quarter-wave touches 16 rows, stream
 // the weights more slowly), through three stages: two slices in flight while one is multiplied.
 // Each wave's weight-block scale travels with the slice (one 4-byte DMA per wave), so the K
@@ -928,9 +929,13 @@ __device__ __forceinline__ v8i load_frag_global(const uint8_t* row_base, int kb,
 // last reads the partials back, sums them in split order -- the same bits whatever the arrival
 // order -- writes Y and re-arms the counter for the next call.
 // ---------------------------------------------------------------------------------------------
-template <int BM_, int BN_, int WN_>
+template <int BM_, int BN_, int WN_, int KH_ = 1>
 struct Dec : Big<BM_, BN_, BM_, WN_, 3> {
   using Base = Big<BM_, BN_, BM_, WN_, 3>;
+  // KH halves of 4 waves per workgroup, each streaming its own part of the K range through its
+  // own stages; the halves' partial tiles are summed through LDS in half order
+  static constexpr int KH = KH_;
+  static constexpr int NT = Base::NT * KH;
   static constexpr int SW_OFF = Base::STAGE_BYTES;  // one weight-block scale per wave
   static constexpr int STAGE_BYTES = SW_OFF + 16 * ((Base::WAVES * 4 + 15) / 16);
   static constexpr int DMA_OPS = Base::DMA_OPS + 1;  // per wave and slice
@@ -941,13 +946,20 @@ struct Dec : Big<BM_, BN_, BM_, WN_, 3> {
 
 template <class T, int ACC>
 __global__ __launch_bounds__(T::NT) void gemm_decode_kernel(GemmArgs p) {
-  __shared__ __attribute__((aligned(16))) uint8_t stages[T::STAGES * T::STAGE_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[T::KH * T::STAGES * T::STAGE_BYTES];
   __shared__ int s_flag;
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = __builtin_amdgcn_readfirstlane(tid >> 8);  // 0 unless KH = 2
+  const int wave = __builtin_amdgcn_readfirstlane((tid >> 6) & 3);  // wave within the half
+  uint8_t* const stages = lds + half * (T::STAGES * T::STAGE_BYTES);
   const int t = blockIdx.x, split = blockIdx.y;
-  const int kb0 = split * p.kb_per_split;
-  const int nk = min(p.kb_per_split, p.KB - kb0);  // >= 1: the plan leaves no empty range
+  const int kbs = split * p.kb_per_split;
+  const int nks = min(p.kb_per_split, p.KB - kbs);  // >= 1: the plan leaves no empty range
+  // this half's slices: the first ceil(nks / KH) of the range, or the rest (possibly none);
+  // both halves run the same number of trips so that they meet at every barrier
+  const int trips = (nks + T::KH - 1) / T::KH;
+  const int kb0 = kbs + half * trips;
+  const int nk = half == 0 ? trips : nks - trips;
   const int n0 = t * T::BN;
   const DmaPlan<T> dp = make_dma_plan<T>(p.M, T::BN, p.K, p.KB, wave, lane);
   const uint8_t* B = p.wq + (int64_t)n0 * p.K;
@@ -968,13 +980,15 @@ __global__ __launch_bounds__(T::NT) void gemm_decode_kernel(GemmArgs p) {
   for (int u = 0; u < P; ++u)
     if (u < nk) dma(stages + u * T::STAGE_BYTES, kb0 + u);
   int cur = 0;
-  for (int i = 0; i < nk; ++i) {
+  for (int i = 0; i < trips; ++i) {
     wait_slice_and_barrier<T>(nk - 1 - i);  // slice i + 1 may stay in flight
     const int nxt = cur == 0 ? P : cur - 1;  // (i + P) % STAGES: freed by slice i - 1
     if (i + P < nk) dma(stages + nxt * T::STAGE_BYTES, kb0 + i + P);
-    const uint8_t* st = stages + cur * T::STAGE_BYTES;
-    const float swv = reinterpret_cast<const float*>(st + T::SW_OFF)[wave];
-    mma_slice_big<T, ACC>(st, swv, 0, wave, lane, acc);
+    if (i < nk) {
+      const uint8_t* st = stages + cur * T::STAGE_BYTES;
+      const float swv = reinterpret_cast<const float*>(st + T::SW_OFF)[wave];
+      mma_slice_big<T, ACC>(st, swv, 0, wave, lane, acc);
+    }
     cur = cur == P ? 0 : cur + 1;
   }
 
@@ -986,6 +1000,21 @@ __global__ __launch_bounds__(T::NT) void gemm_decode_kernel(GemmArgs p) {
     for (int j = 0; j < T::TN; ++j)
 #pragma unroll
       for (int v = 0; v < 4; ++v) vals[(i * T::TN + j) * 4 + v] = acc[i][j][v];
+  if constexpr (T::KH == 2) {
+    // half 1's partial tile through LDS (every wave is past its last slice), added to half 0's
+    float* red = reinterpret_cast<float*>(lds) + (wave * T::NV) * 64 + lane;
+    __syncthreads();
+    if (half == 1) {
+#pragma unroll
+      for (int q = 0; q < T::NV; ++q) red[q * 64] = vals[q];
+    }
+    __syncthreads();
+    if (half == 0) {
+#pragma unroll
+      for (int q = 0; q < T::NV; ++q) vals[q] += red[q * 64];
+    }
+  }
+  const bool owner = half == 0;  // holds the tile's values from here on
   // The output tile goes through LDS (the stages are free once every wave is past its last
   // slice) and leaves as 16-byte pieces of rows.
   static_assert(T::BM * (T::BN + 4) * 4 <= T::STAGES * T::STAGE_BYTES, "output tile fits");
@@ -993,15 +1022,16 @@ __global__ __launch_bounds__(T::NT) void gemm_decode_kernel(GemmArgs p) {
     __syncthreads();
     if (p.out_f32) {
       constexpr int PITCH = T::BN + 4;  // floats; rows stay 16-byte aligned
-      float* t32 = reinterpret_cast<float*>(stages);
+      float* t32 = reinterpret_cast<float*>(lds);
+      if (owner)
 #pragma unroll
-      for (int i = 0; i < T::TM; ++i)
+        for (int i = 0; i < T::TM; ++i)
 #pragma unroll
-        for (int j = 0; j < T::TN; ++j)
+          for (int j = 0; j < T::TN; ++j)
 #pragma unroll
-          for (int v = 0; v < 4; ++v)
-            t32[(i * 16 + 4 * kq + v) * PITCH + wave * T::WN + j * 16 + r16] =
-                vals[(i * T::TN + j) * 4 + v];
+            for (int v = 0; v < 4; ++v)
+              t32[(i * 16 + 4 * kq + v) * PITCH + wave * T::WN + j * 16 + r16] =
+                  vals[(i * T::TN + j) * 4 + v];
       __syncthreads();
       constexpr int CH = T::BN / 4;
       for (int q = tid; q < T::BM * CH; q += T::NT) {
@@ -1012,15 +1042,16 @@ __global__ __launch_bounds__(T::NT) void gemm_decode_kernel(GemmArgs p) {
       }
     } else {
       constexpr int PITCH = T::BN + 8;  // bf16 elements; rows stay 16-byte aligned
-      uint16_t* t16 = reinterpret_cast<uint16_t*>(stages);
+      uint16_t* t16 = reinterpret_cast<uint16_t*>(lds);
+      if (owner)
 #pragma unroll
-      for (int i = 0; i < T::TM; ++i)
+        for (int i = 0; i < T::TM; ++i)
 #pragma unroll
-        for (int j = 0; j < T::TN; ++j)
+          for (int j = 0; j < T::TN; ++j)
 #pragma unroll
-          for (int v = 0; v < 4; ++v)
-            t16[(i * 16 + 4 * kq + v) * PITCH + wave * T::WN + j * 16 + r16] =
-                f32_to_bf16_rne(vals[(i * T::TN + j) * 4 + v]);
+            for (int v = 0; v < 4; ++v)
+              t16[(i * 16 + 4 * kq + v) * PITCH + wave * T::WN + j * 16 + r16] =
+                  f32_to_bf16_rne(vals[(i * T::TN + j) * 4 + v]);
       __syncthreads();
       constexpr int CH = T::BN / 8;
       for (int q = tid; q < T::BM * CH; q += T::NT) {
@@ -1039,9 +1070,10 @@ __global__ __launch_bounds__(T::NT) void gemm_decode_kernel(GemmArgs p) {
   // partial tile of (t, split): value q of lane l of wave w at float (w * NV + q) * 64 + l
   float* base = p.ws + (size_t)wave * T::NV * 64 + lane;
   float* mine = base + ((size_t)t * S + split) * T::SLOT_FLOATS;
+  if (owner)
 #pragma unroll
-  for (int q = 0; q < T::NV; ++q)
-    __hip_atomic_store(mine + q * 64, vals[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int q = 0; q < T::NV; ++q)
+      __hip_atomic_store(mine + q * 64, vals[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   // Ordering of the hand-off. Every access to the partials and the counter is an agent-scope
   // atomic: the partial stores are write-through stores (sc1) that complete only once they have
   // reached the level all XCDs share, and the read-back loads (sc1) are served from that level,
@@ -1064,7 +1096,7 @@ __global__ __launch_bounds__(T::NT) void gemm_decode_kernel(GemmArgs p) {
   // last arrival: sum the partials in split order, the values of 4 splits in flight at a time
 #pragma unroll
   for (int j = 0; j < T::NV; ++j) vals[j] = 0.f;
-  for (int s0 = 0; s0 < S; s0 += 4) {
+  for (int s0 = 0; owner && s0 < S; s0 += 4) {
     float v4[4][T::NV];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -1474,34 +1506,41 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool rowb) {
 GemmPlan plan_decode(int64_t M, int64_t N, int64_t K) {
   GemmPlan pl{};
   const int64_t KB = K / 128;
-  // 5 <= M <= 64 (rows padded to 32 or 64). Tiles of 64 columns, K split into S ranges, S the
-  // smallest power of two giving at least 256 workgroups (one per CU) while ranges keep at least
-  // 4 slices. Wide GEMMs already have 256 tiles: above 32 rows 128-column tiles without a split
-  // (half the activation bytes per weight byte, no partials), up to 32 rows a second split.
-  // Measured on the Qwen3-8B decode GEMMs (graph-replayed): q/k/v 6144x4096 and o 4096x4096 at
-  // S = 4, down 4096x12288 within 6 % of the best of (64 | 128 columns) x S, and gate/up
-  // 24576x4096 at M = 64 30.4 us against 32.5-33.7 us for 64-column tiles with S = 1 or 2 and
-  // 32.0 us for 256-column tiles with S = 2.
+  // 5 <= M <= 64 (rows padded to 32 or 64). Tiles of 64 columns; while they number at most 256,
+  // two K halves per workgroup (8 waves, one workgroup per CU) and K split into S ranges, S the
+  // largest power of two that keeps the grid within one round of 256 workgroups and each range
+  // at least 4 slices; past 256 tiles one K half and S = 1 (2 up to 32 rows, where the
+  // partials are half as large). Wide GEMMs above 32 rows: 128-column tiles (half the
+  // activation bytes per weight byte) with two K halves and no split. Measured on the Qwen3-8B
+  // decode GEMMs at M = 64 (graph-replayed, weights rotated), two halves against one: gate/up
+  // 24576x4096 26.6 against 30.2 us (128 columns, unsplit), o 4096x4096 8.9 against 10.0 us and
+  // down 4096x12288 18.1 against 20.4 us (S = 4), q/k/v 6144x4096 10.8 us either way (S = 2
+  // against 4); with more workgroups than CUs two halves lose (q/k/v at S = 4: 13.2 us).
   const int64_t bm = M <= 32 ? 32 : 64;
-  int64_t BN = 64, S = 1;
+  int64_t BN = 64, S = 1, KH = KB >= 4 ? 2 : 1;
   if (M > 32 && N / 128 >= 192) {
     BN = 128;
+    if (N / 128 > 256) KH = 1;
   } else {
     const int64_t tiles = N / 64;
-    while (tiles * S < 256 && KB / (2 * S) >= 4) S *= 2;
-    if (tiles >= 256 && M <= 32 && KB >= 8) S = 2;
+    if (tiles <= 256) {
+      while (tiles * 2 * S <= 256 && KB / (2 * S) >= 4) S *= 2;
+    } else {
+      KH = 1;
+      if (M <= 32 && KB >= 8) S = 2;
+    }
     if (tiles > kWsCounters) S = 1;
   }
   const int64_t tiles = N / BN;
   const int64_t L = (KB + S - 1) / S;
   S = (KB + L - 1) / L;  // no empty range
   pl.cfg = kCfgDecode;
-  pl.bm = (int)bm;
+  pl.bm = BN == 128 ? 64 : (int)bm;  // the 128-column tile is built for 64 rows
   pl.bn = (int)BN;
-  pl.depth = 3;  // LDS stages
+  pl.depth = (int)KH;  // K halves per workgroup
   pl.splits = (int)S;
   pl.kb_per_split = (int)L;
-  pl.workspace_bytes = S > 1 ? kWsHeaderBytes + (size_t)(tiles * S) * BN * bm * sizeof(float) : 0;
+  pl.workspace_bytes = S > 1 ? kWsHeaderBytes + (size_t)(tiles * S) * BN * pl.bm * sizeof(float) : 0;
   return pl;
 }
 
@@ -1586,11 +1625,16 @@ static hipError_t launch_decode_t(const GemmArgs& a, const GemmPlan& pl, hipStre
   return hipGetLastError();
 }
 
+template <int ACC, int KH>
+static hipError_t launch_decode_k(const GemmArgs& a, const GemmPlan& pl, hipStream_t stream) {
+  if (pl.bn == 128) return launch_decode_t<Dec<64, 128, 32, KH>, ACC>(a, pl, stream);  // M > 32
+  return pl.bm == 32 ? launch_decode_t<Dec<32, 64, 16, KH>, ACC>(a, pl, stream)
+                     : launch_decode_t<Dec<64, 64, 16, KH>, ACC>(a, pl, stream);
+}
+
 template <int ACC>
 static hipError_t launch_decode(const GemmArgs& a, const GemmPlan& pl, hipStream_t stream) {
-  if (pl.bn == 128) return launch_decode_t<Dec<64, 128, 32>, ACC>(a, pl, stream);  // M > 32
-  return pl.bm == 32 ? launch_decode_t<Dec<32, 64, 16>, ACC>(a, pl, stream)
-                     : launch_decode_t<Dec<64, 64, 16>, ACC>(a, pl, stream);
+  return pl.depth == 2 ? launch_decode_k<ACC, 2>(a, pl, stream) : launch_decode_k<ACC, 1>(a, pl, stream);
 }
 
 template <class T, bool PRECISE>

@@ -92,7 +92,7 @@ struct GemmPlan {
   int bm, bn;  // workgroup tile
   int splits;  // K splits (1 = no split, result written directly)
   int kb_per_split;
-  int depth;   // streaming kernel: K slices in flight per wave; decode kernel: LDS stages
+  int depth;   // streaming kernel: K slices in flight per wave; decode kernel: K halves per workgroup
   size_t workspace_bytes;
   size_t stage_off;  // fused activation quantization: workspace offset of the staged codes
 };

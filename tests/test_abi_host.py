@@ -337,17 +337,18 @@ def test_workspace_query_is_pure_host(L):
     # the blockscaled GEMM up to 4 rows splits K only inside each workgroup (no workspace); the
     # decode GEMM above that (up to 64 rows) splits K over workgroups: above 32 rows with at least
     # 192 tiles of 128 columns, 128-column tiles and no split; otherwise 64-column tiles and K
-    # split S ways, S the smallest power of two giving >= 256 workgroups while ranges keep >= 4
-    # slices (S = 2 at <= 32 rows with >= 256 tiles and >= 8 slices; S = 1 past 1024 tiles);
-    # workspace = header + [tiles][S] partial tiles of 64 columns x padded rows (32 or 64) float32
+    # split S ways: up to 256 tiles S the largest power of two with tiles * 2S <= 256 and ranges
+    # of >= 4 slices, past 256 tiles S = 1 (2 at <= 32 rows with >= 8 slices), S = 1 past 1024
+    # tiles; workspace = header + [tiles][S] partial tiles of 64 columns x padded rows (32 or 64)
     def dec(M, N, K):
         kb = K // 128
         if M > 32 and N // 128 >= 192:
             return 0
         tiles, S = N // 64, 1
-        while tiles * S < 256 and kb // (2 * S) >= 4:
-            S *= 2
-        if tiles >= 256 and M <= 32 and kb >= 8:
+        if tiles <= 256:
+            while tiles * 2 * S <= 256 and kb // (2 * S) >= 4:
+                S *= 2
+        elif M <= 32 and kb >= 8:
             S = 2
         if tiles > 1024:
             S = 1
@@ -366,7 +367,7 @@ def test_workspace_query_is_pure_host(L):
             return 0
         return (max(a256(L.fp8rl_workspace_bytes(0, M, N, K, 0)), hdr) + a256(M * K)
                 + M * (K // 128) * 4)
-    for shape in [(64, 4096, 4096), (20, 1024, 12288), (64, 12288, 4096), (17, 6144, 4096),
+    for shape in [(64, 4096, 4096), (20, 1024, 12288), (64, 6144, 4096), (17, 6144, 4096),
                   (32, 24576, 4096), (48, 4096, 384 * 3), (5, 4096, 4096), (16, 2048, 4096)]:
         assert L.fp8rl_workspace_bytes(0, *shape, 0) == dec(*shape) > 0, shape
     for shape in [(64, 4096, 4096), (20, 1024, 12288), (64, 12288, 4096), (1, 256, 2048),
@@ -382,6 +383,7 @@ def test_workspace_query_is_pure_host(L):
     assert L.fp8rl_workspace_bytes(0, 64, 4096, 1024, 0) == hdr + 64 * 2 * 64 * 64 * 4
     assert L.fp8rl_workspace_bytes(0, 32, 131072, 2048, 0) == 0  # more tiles than counters
     assert L.fp8rl_workspace_bytes(0, 64, 24576, 4096, 0) == 0  # 128-column tiles, K unsplit
+    assert L.fp8rl_workspace_bytes(0, 64, 12288, 4096, 0) == 0  # 192 tiles: two K halves each
     assert L.fp8rl_workspace_bytes(0, 32, 24576, 4096, 0) == hdr + 384 * 2 * 64 * 32 * 4
     assert L.fp8rl_workspace_bytes(0, 0, 256, 256, 0) == 0
     assert L.fp8rl_workspace_bytes(0, 8192, 4096, 4096, 0) == 0  # large M: no split
