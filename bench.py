@@ -247,14 +247,28 @@ class DenseBlock:
         self.graphs[c].replay()
 
     def time_gemm(self, i, reps):
-        """Per-launch duration of GEMM i alone (its activation already quantized): `reps`
-        launches replayed from a HIP graph, timed with HIP events on the current stream."""
-        fq = self.fq
-        c = 0
-        g = lambda: fq.gemm(self.xq[i], self.sa[i], self.wq[c][i], self.sw[c][i], y=self.y[i],
-                            accum=self.accum, workspace=self.ws[i])
+        """Per-launch duration of GEMM i alone (its activation already quantized): launches
+        replayed from a HIP graph, timed with HIP events on the current stream. The launches
+        cycle through at least 1 GiB of weight codes (the quantized copies, then clones of them),
+        so that the memory-side cache never holds the next launch's weights."""
+        fq, torch = self.fq, self.torch
+        _, N, K = self.linears[i]
+        n_pool = max(self.copies, -(-ROTATE_BYTES // (N * K)))
+        pool = [(self.wq[c][i], self.sw[c][i]) for c in range(self.copies)]
+        pool += [(self.wq[c % self.copies][i].clone(), self.sw[c % self.copies][i].clone())
+                 for c in range(self.copies, n_pool)]
+        n = [0]
+
+        def g():
+            wq, sw = pool[n[0] % n_pool]
+            n[0] += 1
+            fq.gemm(self.xq[i], self.sa[i], wq, sw, y=self.y[i], accum=self.accum,
+                    workspace=self.ws[i])
+
         fq.quant_act(self.x[i], self.xq[i], self.sa[i], scale=self.scales)
-        return graph_launch_us(self.torch, g, reps)
+        us = graph_launch_us(torch, g, max(reps, n_pool))
+        del pool
+        return us
 
     def time_linears(self, reps):
         """Kernel time of the captured act-quant + GEMM part alone (graph replays)."""
